@@ -1,0 +1,296 @@
+"""Pins of the CPU oracle against values fixed outside it (no GPU needed).
+
+Each test pins one way the oracle could be wrong: a format decoder, the rounding
+used for exact comparisons, the indexing of the four transpose cases, the length
+of the accumulation, the alpha and beta terms, or the row selection.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import gemm_inputs as gi
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+TRANS = [(0, 0), (0, 1), (1, 0), (1, 1)]
+
+
+def _store(op_mat: np.ndarray, trans: int) -> np.ndarray:
+    """Storage of a logical operand: op(X) = X (trans 0) or X^T (trans 1)."""
+    return np.ascontiguousarray(op_mat.T if trans else op_mat)
+
+
+def _bf16(x):
+    return gi.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def _run(tA, tB, opA_bits, opB_bits, alpha=1.0, beta=0.0, C=None, c_fmt=oracle.C_F32,
+         in_fmt=oracle.IN_BF16, rows=None):
+    M, K = opA_bits.shape
+    N = opB_bits.shape[1]
+    A = _store(opA_bits, tA)
+    B = _store(opB_bits, tB)
+    return oracle.gemm(tA, tB, M, N, K, alpha, A, A.shape[1], B, B.shape[1], beta, C, N,
+                       in_fmt, c_fmt, rows=rows)
+
+
+# ---------------------------------------------------------------- format codecs
+
+def _frac(s: str):
+    if s == "nan":
+        return None
+    if s == "-0":
+        return Fraction(0)
+    return Fraction(s)
+
+
+def test_e4m3_golden_codes():
+    lines = [l.split("#")[0].split() for l in open(os.path.join(GOLDEN, "e4m3_codes.txt"))]
+    lines = [l for l in lines if l]
+    assert len(lines) >= 20
+    for code_s, val_s in lines:
+        code = int(code_s, 16)
+        got = oracle.load().oracle_e4m3_value(code)
+        want = _frac(val_s)
+        if want is None:
+            assert math.isnan(got), code_s
+        else:
+            assert Fraction(got) == want, (code_s, got, want)
+            if val_s == "-0":
+                assert math.copysign(1.0, got) < 0
+
+
+def test_e4m3_all_codes_closed_form_and_library():
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    mine = oracle.decode(codes, "e4m3")
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan_mine = np.isnan(mine)
+    assert nan_mine.sum() == 2 and nan_mine[0x7F] and nan_mine[0xFF]
+    assert np.array_equal(nan_mine, np.isnan(lib))
+    assert np.array_equal(mine[~nan_mine], lib[~nan_mine])
+    finite = mine[~nan_mine]
+    assert np.nanmax(finite) == 448.0 and np.nanmin(finite) == -448.0
+    # 253 distinct finite values (+0 and -0 compare equal)
+    assert len(set(finite.tolist())) == 253
+    # closed form for every code, written independently of the decoder
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            continue
+        v = Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+        assert Fraction(mine[c]) == (-v if s else v), hex(c)
+
+
+def test_bf16_decode_all_codes_against_library():
+    import torch
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = oracle.decode(codes, "bf16")
+    lib = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], lib[~nan])
+
+
+def test_bf16_round_golden():
+    for line in open(os.path.join(GOLDEN, "bf16_round.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        x_s, bits_s = line.split()
+        x = float.fromhex(x_s) if x_s.lstrip("-").startswith("0x") else float(x_s)
+        assert oracle.load().oracle_round_bf16(x) == int(bits_s, 16), line
+
+
+def test_bf16_round_matches_library_on_f32_values():
+    import torch
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal(200000).astype(np.float32) * np.float32(1e3)
+    x = np.concatenate([x, rng.random(1000).astype(np.float32) * np.float32(1e-38)])
+    mine = oracle.round_bf16(x.astype(np.float64))
+    lib = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, lib)
+
+
+# ---------------------------------------------------------------- worked example
+
+def test_worked_example():
+    rows = [l.split("#")[0].split() for l in open(os.path.join(GOLDEN, "worked_gemm.txt"))]
+    rows = [[float(v) for v in r] for r in rows if r]
+    A, B, C0 = np.array(rows[0:2]), np.array(rows[2:5]), np.array(rows[5:7])
+    alpha, beta = rows[7]
+    want = np.array(rows[8:10])
+    for tA, tB in TRANS:
+        R, S = _run(tA, tB, _bf16(A), _bf16(B), alpha=alpha, beta=beta,
+                    C=gi.f32_bits(C0), c_fmt=oracle.C_F32)
+        assert np.array_equal(R, want), (tA, tB, R)
+        assert np.array_equal(S, np.abs(A) @ np.abs(B))
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("tA,tB", TRANS)
+def test_identity_gives_op_b(tA, tB):
+    M = K = 13
+    N = 7
+    I = _bf16(np.eye(M))
+    Bv = gi.bf16_uniform((K, N), 3)
+    R, _ = _run(tA, tB, I, Bv)
+    assert np.array_equal(R, oracle.decode(Bv, "bf16"))
+    # and on the right: op(A) * I = op(A)
+    Av = gi.bf16_uniform((N, K), 4)
+    R2, _ = _run(tA, tB, Av, I)
+    assert np.array_equal(R2, oracle.decode(Av, "bf16"))
+
+
+@pytest.mark.parametrize("tA,tB", TRANS)
+def test_permutation_permutes_rows(tA, tB):
+    rng = np.random.default_rng(11)
+    M = K = 17
+    N = 9
+    perm = rng.permutation(M)
+    P = np.zeros((M, K))
+    P[np.arange(M), perm] = 1.0
+    Bv = gi.bf16_uniform((K, N), 5)
+    R, _ = _run(tA, tB, _bf16(P), Bv)
+    assert np.array_equal(R, oracle.decode(Bv, "bf16")[perm])
+
+
+@pytest.mark.parametrize("K", [1, 5, 256, 4096, 5120])
+def test_all_ones_gives_k(K):
+    M, N = 3, 4
+    R, S = _run(0, 0, _bf16(np.ones((M, K))), _bf16(np.ones((K, N))))
+    assert np.all(R == K) and np.all(S == K)
+
+
+def test_alpha_scales_and_beta_accumulates():
+    A = gi.ints((6, 5), 1, -4, 4, "bf16")
+    B = gi.ints((5, 7), 2, -4, 4, "bf16")
+    C0 = gi.ints((6, 7), 3, -4, 4, "bf16")
+    Ad, Bd, Cd = (oracle.decode(x, "bf16") for x in (A, B, C0))
+    R, _ = _run(0, 0, A, B, alpha=-2.5, beta=1.0, C=C0, c_fmt=oracle.C_BF16)
+    assert np.array_equal(R, -2.5 * (Ad @ Bd) + Cd)
+    R, _ = _run(0, 0, A, B, alpha=1.0, beta=-0.5, C=C0, c_fmt=oracle.C_BF16)
+    assert np.array_equal(R, Ad @ Bd - 0.5 * Cd)
+    # alpha = 0 and A = 0 both leave beta * C exactly
+    R, _ = _run(0, 0, A, B, alpha=0.0, beta=3.0, C=C0, c_fmt=oracle.C_BF16)
+    assert np.array_equal(R, 3.0 * Cd)
+    Z = _bf16(np.zeros((6, 5)))
+    R, _ = _run(0, 0, Z, B, alpha=1.0, beta=1.0, C=C0, c_fmt=oracle.C_BF16)
+    assert np.array_equal(R, Cd)
+
+
+def test_beta_zero_never_reads_c():
+    A = gi.bf16_uniform((4, 8), 1)
+    B = gi.bf16_uniform((8, 5), 2)
+    nan_c = gi.f32_bits(np.full((4, 5), np.nan, dtype=np.float32))
+    R, _ = _run(0, 0, A, B, beta=0.0, C=nan_c)
+    assert np.isfinite(R).all()
+    R1, _ = _run(0, 0, A, B, beta=1.0, C=nan_c)
+    assert np.isnan(R1).all()
+
+
+def test_k_zero_gives_beta_c():
+    C0 = gi.f32_bits(np.arange(6, dtype=np.float32).reshape(2, 3))
+    A = np.zeros((2, 0), dtype=np.uint16)
+    B = np.zeros((0, 3), dtype=np.uint16)
+    R, S = oracle.gemm(0, 0, 2, 3, 0, 1.0, A, 1, B, 3, 2.0, C0, 3, oracle.IN_BF16, oracle.C_F32)
+    assert np.array_equal(R, 2.0 * np.arange(6).reshape(2, 3)) and np.all(S == 0)
+
+
+# ---------------------------------------------------------------- brute force / library
+
+def test_exact_rational_brute_force():
+    """Tiny case summed in exact rationals by pure-Python loops."""
+    M, N, K = 3, 4, 5
+    for tA, tB in TRANS:
+        A = gi.bf16_uniform((M, K), 21)
+        B = gi.bf16_uniform((K, N), 22)
+        C0 = gi.bf16_uniform((M, N), 23)
+        Af = [[Fraction(float(v)) for v in row] for row in oracle.decode(A, "bf16")]
+        Bf = [[Fraction(float(v)) for v in row] for row in oracle.decode(B, "bf16")]
+        Cf = [[Fraction(float(v)) for v in row] for row in oracle.decode(C0, "bf16")]
+        alpha, beta = Fraction(3, 4), Fraction(-5, 2)
+        R, _ = _run(tA, tB, A, B, alpha=0.75, beta=-2.5, C=C0, c_fmt=oracle.C_BF16)
+        for i in range(M):
+            for j in range(N):
+                s = sum(Af[i][k] * Bf[k][j] for k in range(K))
+                want = alpha * s + beta * Cf[i][j]
+                assert R[i, j] == float(want), (tA, tB, i, j)
+
+
+@pytest.mark.parametrize("tA,tB", TRANS)
+@pytest.mark.parametrize("in_fmt", ["bf16", "e4m3"])
+def test_against_numpy_float64(tA, tB, in_fmt):
+    import torch
+    M, N, K = 37, 29, 91
+    if in_fmt == "bf16":
+        A = gi.bf16_normal((M, K), 31)
+        B = gi.bf16_normal((K, N), 32)
+        dec = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).double().numpy()
+        code = oracle.IN_BF16
+    else:
+        A = gi.e4m3_normal((M, K), 31)
+        B = gi.e4m3_normal((K, N), 32)
+        dec = lambda x: torch.from_numpy(x).view(torch.float8_e4m3fn).double().numpy()
+        code = oracle.IN_E4M3
+    R, S = _run(tA, tB, A, B, in_fmt=code)
+    ref = dec(A) @ dec(B)
+    assert np.allclose(R, ref, rtol=1e-12, atol=1e-12 * np.abs(dec(A)).max() * np.abs(dec(B)).max() * K)
+    assert np.allclose(S, np.abs(dec(A)) @ np.abs(dec(B)), rtol=1e-12)
+    assert np.all(S >= np.abs(R) - 1e-12 * S)
+
+
+def test_row_subset_equals_full():
+    g = gi.Gemm("t", 50, 40, 30, transA=1, transB=1, beta=1.0, c_dist="normal", c_std=0.5)
+    data = g.make()
+    R, S = oracle.gemm_problem(g, data)
+    rows = [49, 0, 17, 17, 3]
+    Rs, Ss = oracle.gemm_problem(g, data, rows=rows)
+    assert np.array_equal(Rs, R[rows]) and np.array_equal(Ss, S[rows])
+    with pytest.raises(ValueError):
+        oracle.gemm_problem(g, data, rows=[50])
+
+
+def test_threads_do_not_change_results():
+    g = gi.Gemm("t", 64, 48, 200, dist="normal")
+    data = g.make()
+    R1, S1 = oracle.gemm_problem(g, data, threads=1)
+    R4, S4 = oracle.gemm_problem(g, data, threads=4)
+    assert np.array_equal(R1, R4) and np.array_equal(S1, S4)
+
+
+# ---------------------------------------------------------------- input recipe
+
+def test_input_recipe_is_deterministic_and_in_range():
+    a = gi.bf16_uniform((64, 64), 0)
+    assert np.array_equal(a, gi.bf16_uniform((64, 64), 0))
+    assert not np.array_equal(a, gi.bf16_uniform((64, 64), 1))
+    v = oracle.decode(a, "bf16")
+    assert v.min() >= -1.0 and v.max() <= 1.0
+    e = oracle.decode(gi.e4m3_normal((256, 256), 0), "e4m3")
+    assert np.isfinite(e).all() and np.abs(e).max() <= 448.0
+    assert 0.9 < e.std() < 1.1
+    i4 = oracle.decode(gi.ints((100, 100), 3, -4, 4, "bf16"), "bf16")
+    assert np.array_equal(i4, np.round(i4)) and i4.min() == -4 and i4.max() == 4
+    i8 = oracle.decode(gi.ints((100, 100), 3, -8, 8, "e4m3"), "e4m3")
+    assert np.array_equal(i8, np.round(i8)) and i8.min() == -8 and i8.max() == 8
+
+
+def test_tolerance_helper_accepts_rounded_and_rejects_wrong():
+    import tolerance
+    g = gi.Gemm("t", 40, 30, 300, dist="normal")
+    data = g.make()
+    R, S = oracle.gemm_problem(g, data)
+    good = oracle.round_bf16(R)
+    assert tolerance.check(good, "bf16", R, S, g.K)["ok"]
+    bad = good.copy()
+    bad[3, 4] ^= 0x0040  # flip a mantissa bit
+    assert not tolerance.check(bad, "bf16", R, S, g.K)["ok"]
+    good32 = oracle.round_f32(R)
+    assert tolerance.check(good32, "f32", R, S, g.K)["ok"]
+    bad32 = oracle.round_f32(R * (1 + 1e-4))
+    assert not tolerance.check(bad32, "f32", R, S, g.K)["ok"]

@@ -1,0 +1,61 @@
+"""Acceptance criteria for GPU results against the fp64 oracle.
+
+bf16 output (C stored as bf16):
+    |C - R| <= 2^-8 |R| + 1e-6 + 2^-24 * sqrt(K) * S      for every element,
+  where R is the unrounded fp64 oracle value and S = sum_k |a_ik b_kj|.  The first
+  two terms are the stated bf16 bound (one bf16 unit of relative error plus 1e-6);
+  the last is the probabilistic fp32 dot-product error scale (Higham and Mary,
+  2019, lambda = 1).  It only matters where R is nearly cancelled, where a correct
+  fp32-accumulating kernel can otherwise exceed the literal bound.  The number of
+  elements outside the literal bound is reported beside the verdict.
+
+fp32 output:
+    ||C - R||_F / ||R||_F <= 1e-5, and every element within the deterministic
+  worst-case bound K * 2^-23 * S + 2^-23 |R| of any fp32 summation order.
+
+E4M3 inputs use the same criteria: the oracle decodes the identical E4M3 bits.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict
+
+import numpy as np
+
+U32 = 2.0 ** -24
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f32_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint32).view(np.float32).astype(np.float64)
+
+
+def check(C_bits: np.ndarray, c_dtype: str, R: np.ndarray, S: np.ndarray, K: int) -> Dict:
+    C = bf16_bits_to_f64(C_bits) if c_dtype == "bf16" else f32_bits_to_f64(C_bits)
+    assert C.shape == R.shape == S.shape, (C.shape, R.shape, S.shape)
+    finite = bool(np.isfinite(C).all())
+    err = np.abs(C - R)
+    rnorm = float(np.linalg.norm(R))
+    frob = float(np.linalg.norm(C - R)) / rnorm if rnorm > 0 else float(np.linalg.norm(C - R))
+    if c_dtype == "bf16":
+        literal = 2.0 ** -8 * np.abs(R) + 1e-6
+        bound = literal + U32 * math.sqrt(max(K, 1)) * S
+        ok = finite and bool((err <= bound).all())
+        n_literal = int((err > literal).sum())
+    else:
+        bound = max(K, 1) * 2.0 ** -23 * S + 2.0 ** -23 * np.abs(R)
+        ok = finite and bool((err <= bound).all()) and frob <= 1e-5
+        n_literal = int((err > bound).sum())
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bound > 0, err / bound, np.where(err > 0, np.inf, 0.0))
+    return {
+        "ok": ok,
+        "finite": finite,
+        "frob_rel": frob,
+        "max_ratio": float(ratio.max()) if ratio.size else 0.0,
+        "n_outside_literal": n_literal,
+        "n": int(C.size),
+    }
