@@ -1,0 +1,204 @@
+"""MI355X (gfx950) dense GEMM: C = alpha*op(A)*op(B) + beta*C.
+
+A thin ctypes binding over the C-ABI in ``include/gemm.h``; every step of the
+computation runs in the library's HIP kernels.  PyTorch supplies device memory and
+the current stream only.  The binding fails loudly when ``libdbgemm.so`` has not
+been built (``python -m dense_blas3_gemm_amd.build``): there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdbgemm.so")
+
+OP_N, OP_T = 0, 1
+BF16_F32, BF16_BF16, E4M3_BF16, E4M3_F32 = 0, 1, 2, 3
+STATUS = {0: "SUCCESS", 1: "INVALID_VALUE", 2: "NOT_SUPPORTED", 3: "NOT_INITIALIZED",
+          4: "LAUNCH_FAILED", 5: "INTERNAL"}
+
+# The exported C symbols, in the order include/gemm.h declares them.
+EXPORTS = ["gemm_create", "gemm_destroy", "gemm_set_stream", "gemm_run", "gemm_check_args",
+           "gemm_query_policy", "gemm_set_policy", "gemm_policy_count", "gemm_policy_name",
+           "gemm_version", "gemm_status_string"]
+
+_lib = None
+
+
+class GemmError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {STATUS.get(status, status)} ({status})")
+        self.status = status
+
+
+def _hip_runtimes():
+    """Distinct libamdhip64 files mapped into this process."""
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
+def load_library():
+    """Loads libdbgemm.so and declares the C signatures; raises if it is missing.
+
+    PyTorch is imported first so that its HIP runtime is the one already mapped when
+    the library's libamdhip64.so.7 dependency is resolved: the process then holds a
+    single HIP runtime, and torch's streams and allocations are valid in the
+    library's launches.
+    """
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m dense_blas3_gemm_amd.build`")
+    try:
+        import torch  # noqa: F401  (maps torch's HIP runtime before the library's)
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes()
+    if len(runtimes) > 1:
+        raise RuntimeError(f"two HIP runtimes are mapped into this process: {sorted(runtimes)}")
+    i32, i64, vp, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    lib.gemm_create.argtypes = [ctypes.POINTER(vp), i32]
+    lib.gemm_destroy.argtypes = [vp]
+    lib.gemm_set_stream.argtypes = [vp, vp]
+    lib.gemm_run.argtypes = [vp, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, i32]
+    lib.gemm_check_args.argtypes = [i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, i32]
+    lib.gemm_query_policy.argtypes = [vp, i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32,
+                                      ctypes.c_char_p, ctypes.c_size_t]
+    lib.gemm_set_policy.argtypes = [vp, ctypes.c_char_p]
+    lib.gemm_policy_count.argtypes = []
+    lib.gemm_policy_name.argtypes = [i32]
+    lib.gemm_policy_name.restype = ctypes.c_char_p
+    lib.gemm_version.argtypes = []
+    lib.gemm_version.restype = ctypes.c_char_p
+    lib.gemm_status_string.argtypes = [i32]
+    lib.gemm_status_string.restype = ctypes.c_char_p
+    for fn in ["gemm_create", "gemm_destroy", "gemm_set_stream", "gemm_run", "gemm_check_args",
+               "gemm_query_policy", "gemm_set_policy", "gemm_policy_count"]:
+        getattr(lib, fn).restype = i32
+    _lib = lib
+    return lib
+
+
+def version() -> str:
+    return load_library().gemm_version().decode()
+
+
+def policies():
+    lib = load_library()
+    return [lib.gemm_policy_name(i).decode() for i in range(lib.gemm_policy_count())]
+
+
+def dtype_code(in_dtype: str, c_dtype: str) -> int:
+    return {("bf16", "f32"): BF16_F32, ("bf16", "bf16"): BF16_BF16,
+            ("e4m3", "bf16"): E4M3_BF16, ("e4m3", "f32"): E4M3_F32}[(in_dtype, c_dtype)]
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _ld(t) -> int:
+    # row-major with unit column stride: the leading dimension is the row stride
+    assert t.dim() == 2 and t.stride(1) == 1, "operands must be row-major 2-D views"
+    return int(t.stride(0))
+
+
+class Gemm:
+    """A library handle on one device; calls enqueue on torch's current stream."""
+
+    def __init__(self, device: int = 0):
+        self.lib = load_library()
+        self.device = device
+        h = ctypes.c_void_p()
+        st = self.lib.gemm_create(ctypes.byref(h), int(device))
+        if st != 0:
+            raise GemmError("gemm_create", st)
+        self.handle = h
+
+    def close(self):
+        if self.handle is not None:
+            self.lib.gemm_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):  # pragma: no cover
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_policy(self, name: Optional[str]):
+        st = self.lib.gemm_set_policy(self.handle, None if name is None else name.encode())
+        if st != 0:
+            raise GemmError("gemm_set_policy", st)
+
+    def set_stream(self, stream_ptr: int):
+        st = self.lib.gemm_set_stream(self.handle, ctypes.c_void_p(stream_ptr))
+        if st != 0:
+            raise GemmError("gemm_set_stream", st)
+
+    def run_raw(self, transA, transB, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr, ldc,
+                dtype, stream_ptr: Optional[int] = None) -> int:
+        """Direct C-ABI call with raw device pointers; returns the status code."""
+        if stream_ptr is not None:
+            self.set_stream(stream_ptr)
+        return self.lib.gemm_run(self.handle, int(transA), int(transB), int(M), int(N), int(K),
+                                 float(alpha), ctypes.c_void_p(A_ptr), int(lda), ctypes.c_void_p(B_ptr),
+                                 int(ldb), float(beta), ctypes.c_void_p(C_ptr), int(ldc), int(dtype))
+
+    def __call__(self, A, B, C, transA: int = 0, transB: int = 0, alpha: float = 1.0,
+                 beta: float = 0.0, dtype: Optional[int] = None):
+        """C <- alpha*op(A)*op(B) + beta*C on torch tensors (row-major 2-D views).
+
+        A and B are bf16 or float8_e4m3fn, C bf16 or float32; op(X) = X^T when the
+        trans flag is 1, read in place from X's storage.
+        """
+        import torch
+        if dtype is None:
+            ind = "e4m3" if A.dtype == torch.float8_e4m3fn else "bf16"
+            cd = "f32" if C.dtype == torch.float32 else "bf16"
+            dtype = dtype_code(ind, cd)
+        M, N = C.shape
+        K = A.shape[0] if transA else A.shape[1]
+        stream = torch.cuda.current_stream(C.device).cuda_stream
+        st = self.run_raw(transA, transB, M, N, K, alpha, _ptr(A), _ld(A), _ptr(B), _ld(B), beta,
+                          _ptr(C), _ld(C), dtype, stream_ptr=stream)
+        if st != 0:
+            raise GemmError("gemm_run", st)
+        return C
+
+    def query_policy(self, M, N, K, transA=0, transB=0, dtype=BF16_BF16, A_ptr=0, lda=None,
+                     B_ptr=0, ldb=None, C_ptr=0, ldc=None) -> str:
+        return query_policy(M, N, K, transA, transB, dtype, A_ptr, lda, B_ptr, ldb, C_ptr, ldc,
+                            handle=self.handle)
+
+
+def query_policy(M, N, K, transA=0, transB=0, dtype=BF16_BF16, A_ptr=0, lda=None, B_ptr=0,
+                 ldb=None, C_ptr=0, ldc=None, handle=None) -> str:
+    """Name of the policy gemm_run would pick (pure host code; handle may be None)."""
+    lib = load_library()
+    lda = lda if lda is not None else (M if transA else K)
+    ldb = ldb if ldb is not None else (K if transB else N)
+    ldc = ldc if ldc is not None else N
+    buf = ctypes.create_string_buffer(128)
+    st = lib.gemm_query_policy(handle, transA, transB, M, N, K, ctypes.c_void_p(A_ptr), lda,
+                               ctypes.c_void_p(B_ptr), ldb, ctypes.c_void_p(C_ptr), ldc, dtype, buf, 128)
+    if st != 0:
+        raise GemmError("gemm_query_policy", st)
+    return buf.value.decode()
+
+
+def check_args(transA, transB, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr, ldc, dtype) -> int:
+    lib = load_library()
+    return lib.gemm_check_args(transA, transB, M, N, K, alpha, ctypes.c_void_p(A_ptr), lda,
+                               ctypes.c_void_p(B_ptr), ldb, beta, ctypes.c_void_p(C_ptr), ldc, dtype)

@@ -1,0 +1,257 @@
+// C-ABI of the GEMM library: handles, argument checks, policy choice and launch.
+// The operation and its conventions are documented in include/gemm.h.
+#include "gemm.h"
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <unordered_set>
+
+#include "gemm_internal.h"
+
+using namespace dbgemm;
+
+namespace {
+
+constexpr const char* kVersion = "dbgemm 0.1.0 policy-table 1";
+
+struct Handle {
+  int device = 0;
+  int cu_count = 256;
+  hipStream_t stream = nullptr;
+  int forced = -1;  // policy index, -1 = shape-driven
+};
+
+// Live handles; a destroyed (or never created) handle is rejected instead of used.
+std::mutex g_mu;
+std::unordered_set<const void*> g_live;
+
+bool live(gemm_handle_t h) {
+  if (!h) return false;
+  std::lock_guard<std::mutex> lk(g_mu);
+  return g_live.count(h) != 0;
+}
+
+bool valid_op(int op) { return op == GEMM_OP_N || op == GEMM_OP_T; }
+bool valid_dtype(int d) { return d >= GEMM_BF16_F32 && d <= GEMM_E4M3_F32; }
+int in_bytes(int d) { return (d == GEMM_E4M3_BF16 || d == GEMM_E4M3_F32) ? 1 : 2; }
+int out_bytes(int d) { return (d == GEMM_BF16_F32 || d == GEMM_E4M3_F32) ? 4 : 2; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+Problem make_problem(int transA, int transB, int64_t M, int64_t N, int64_t K, const void* A,
+                     int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc,
+                     int dtype) {
+  Problem pr;
+  pr.transA = transA;
+  pr.transB = transB;
+  pr.M = M;
+  pr.N = N;
+  pr.K = K;
+  pr.in_fp8 = in_bytes(dtype) == 1;
+  pr.c_f32 = out_bytes(dtype) == 4;
+  const int ie = in_bytes(dtype), oe = out_bytes(dtype);
+  const int vec = 16 / ie;
+  bool ok = aligned16(A) && aligned16(B) && aligned16(C);
+  ok = ok && (lda * ie) % 16 == 0 && (ldb * ie) % 16 == 0 && (ldc * oe) % 16 == 0;
+  // contiguous extent of each operand in whole 16-byte chunks
+  ok = ok && (transA ? M % vec == 0 : K % vec == 0);
+  ok = ok && (transB ? K % vec == 0 : N % vec == 0);
+  // 32-bit buffer offsets: every operand span, plus one tile of rows of slack for
+  // the out-of-range marker, stays below 2^31 bytes
+  const double lim = 2147483647.0;
+  const double a_rows = (double)(transA ? K : M) + 256.0;
+  const double b_rows = (double)(transB ? N : K) + 256.0;
+  ok = ok && a_rows * (double)lda * ie < lim && b_rows * (double)ldb * ie < lim;
+  pr.fast_ok = ok;
+  return pr;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gemm_version(void) { return kVersion; }
+
+const char* gemm_status_string(int status) {
+  switch (status) {
+    case GEMM_STATUS_SUCCESS: return "GEMM_STATUS_SUCCESS";
+    case GEMM_STATUS_INVALID_VALUE: return "GEMM_STATUS_INVALID_VALUE";
+    case GEMM_STATUS_NOT_SUPPORTED: return "GEMM_STATUS_NOT_SUPPORTED";
+    case GEMM_STATUS_NOT_INITIALIZED: return "GEMM_STATUS_NOT_INITIALIZED";
+    case GEMM_STATUS_LAUNCH_FAILED: return "GEMM_STATUS_LAUNCH_FAILED";
+    case GEMM_STATUS_INTERNAL: return "GEMM_STATUS_INTERNAL";
+    default: return "GEMM_STATUS_UNKNOWN";
+  }
+}
+
+int gemm_policy_count(void) { return policy_count(); }
+
+const char* gemm_policy_name(int index) {
+  if (index < 0 || index >= policy_count()) return nullptr;
+  return policy_at(index).name;
+}
+
+gemm_status_t gemm_check_args(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+                              const void* A, int64_t lda, const void* B, int64_t ldb, float beta,
+                              const void* C, int64_t ldc, int dtype) {
+  if (!valid_op(transA) || !valid_op(transB) || !valid_dtype(dtype)) return GEMM_STATUS_INVALID_VALUE;
+  if (M < 0 || N < 0 || K < 0) return GEMM_STATUS_INVALID_VALUE;
+  const int64_t imax = 0x7FFFFFFF;
+  if (M > imax || N > imax || K > imax) return GEMM_STATUS_INVALID_VALUE;
+  // leading dimensions: at least the stored row length, and at least 1
+  const int64_t a_cols = transA ? M : K, b_cols = transB ? K : N;
+  if (lda < (a_cols > 1 ? a_cols : 1) || ldb < (b_cols > 1 ? b_cols : 1) || ldc < (N > 1 ? N : 1))
+    return GEMM_STATUS_INVALID_VALUE;
+  if (!std::isfinite(alpha) || !std::isfinite(beta)) return GEMM_STATUS_NOT_SUPPORTED;
+  if (M == 0 || N == 0) return GEMM_STATUS_SUCCESS;
+  if (!C) return GEMM_STATUS_INVALID_VALUE;
+  if (K > 0 && alpha != 0.f && (!A || !B)) return GEMM_STATUS_INVALID_VALUE;
+  return GEMM_STATUS_SUCCESS;
+}
+
+gemm_status_t gemm_create(gemm_handle_t* h, int device) {
+  if (!h) return GEMM_STATUS_INVALID_VALUE;
+  *h = nullptr;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return GEMM_STATUS_NOT_INITIALIZED;
+  }
+  if (device < 0 || device >= n) return GEMM_STATUS_INVALID_VALUE;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) {
+    (void)hipGetLastError();
+    return GEMM_STATUS_INTERNAL;
+  }
+  Handle* p = new Handle();
+  p->device = device;
+  p->cu_count = cus > 0 ? cus : 256;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_live.insert(p);
+  }
+  *h = reinterpret_cast<gemm_handle_t>(p);
+  return GEMM_STATUS_SUCCESS;
+}
+
+gemm_status_t gemm_destroy(gemm_handle_t h) {
+  if (!h) return GEMM_STATUS_SUCCESS;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_live.erase(h) == 0) return GEMM_STATUS_NOT_INITIALIZED;
+  }
+  delete reinterpret_cast<Handle*>(h);
+  return GEMM_STATUS_SUCCESS;
+}
+
+gemm_status_t gemm_set_stream(gemm_handle_t h, void* stream) {
+  if (!live(h)) return GEMM_STATUS_NOT_INITIALIZED;
+  reinterpret_cast<Handle*>(h)->stream = reinterpret_cast<hipStream_t>(stream);
+  return GEMM_STATUS_SUCCESS;
+}
+
+gemm_status_t gemm_set_policy(gemm_handle_t h, const char* name) {
+  if (!live(h)) return GEMM_STATUS_NOT_INITIALIZED;
+  Handle* p = reinterpret_cast<Handle*>(h);
+  if (!name || std::strcmp(name, "auto") == 0) {
+    p->forced = -1;
+    return GEMM_STATUS_SUCCESS;
+  }
+  const int i = policy_find(name);
+  if (i < 0) return GEMM_STATUS_INVALID_VALUE;
+  p->forced = i;
+  return GEMM_STATUS_SUCCESS;
+}
+
+gemm_status_t gemm_query_policy(gemm_handle_t h, int transA, int transB, int64_t M, int64_t N,
+                                int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                                const void* C, int64_t ldc, int dtype, char* name, size_t len) {
+  if (!name || len == 0) return GEMM_STATUS_INVALID_VALUE;
+  name[0] = 0;
+  if (h && !live(h)) return GEMM_STATUS_NOT_INITIALIZED;
+  if (!valid_op(transA) || !valid_op(transB) || !valid_dtype(dtype)) return GEMM_STATUS_INVALID_VALUE;
+  if (M < 0 || N < 0 || K < 0) return GEMM_STATUS_INVALID_VALUE;
+  const Handle* p = reinterpret_cast<const Handle*>(h);
+  const Problem pr = make_problem(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, dtype);
+  int idx;
+  if (p && p->forced >= 0) {
+    idx = p->forced;
+    if (!policy_serves(policy_at(idx), pr)) return GEMM_STATUS_NOT_SUPPORTED;
+  } else {
+    idx = policy_select(pr, p ? p->cu_count : 256);
+  }
+  std::snprintf(name, len, "%s", policy_at(idx).name);
+  return GEMM_STATUS_SUCCESS;
+}
+
+gemm_status_t gemm_run(gemm_handle_t h, int transA, int transB, int64_t M, int64_t N, int64_t K,
+                       float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+                       float beta, void* C, int64_t ldc, int dtype) {
+  if (!live(h)) return GEMM_STATUS_NOT_INITIALIZED;
+  const gemm_status_t st = gemm_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                           ldc, dtype);
+  if (st != GEMM_STATUS_SUCCESS) return st;
+  if (M == 0 || N == 0) return GEMM_STATUS_SUCCESS;
+  const Handle* p = reinterpret_cast<const Handle*>(h);
+
+  GemmArgs a{};
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldc = ldc;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.c_f32 = out_bytes(dtype) == 4;
+  a.in_fp8 = in_bytes(dtype) == 1;
+  a.transA = transA;
+  a.transB = transB;
+
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return GEMM_STATUS_INTERNAL;
+  if (cur != p->device && hipSetDevice(p->device) != hipSuccess) return GEMM_STATUS_INTERNAL;
+
+  hipError_t err;
+  if (K == 0 || alpha == 0.f) {
+    err = launch_scale(a, p->stream);
+  } else {
+    const Problem pr = make_problem(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, dtype);
+    int idx;
+    if (p->forced >= 0) {
+      idx = p->forced;
+      if (!policy_serves(policy_at(idx), pr)) {
+        if (cur != p->device) (void)hipSetDevice(cur);
+        return GEMM_STATUS_NOT_SUPPORTED;
+      }
+    } else {
+      idx = policy_select(pr, p->cu_count);
+    }
+    const Policy& pol = policy_at(idx);
+    if (pol.kind == KIND_SIMT) {
+      if ((M + 63) / 64 > 65535) {
+        if (cur != p->device) (void)hipSetDevice(cur);
+        return GEMM_STATUS_NOT_SUPPORTED;
+      }
+      err = launch_simt(a, p->stream);
+    } else {
+      a.tiles_m = (int)((M + pol.BM - 1) / pol.BM);
+      a.tiles_n = (int)((N + pol.BN - 1) / pol.BN);
+      a.group = pol.group;
+      a.raster_n = pol.raster_n;
+      a.xcd = pol.xcd;
+      a.swizzle = pol.swizzle;
+      err = launch_mfma(pol, a, p->stream);
+    }
+  }
+  if (cur != p->device) (void)hipSetDevice(cur);
+  if (err != hipSuccess) return GEMM_STATUS_LAUNCH_FAILED;
+  return GEMM_STATUS_SUCCESS;
+}
+
+}  // extern "C"

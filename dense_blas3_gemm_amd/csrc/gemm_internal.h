@@ -1,0 +1,66 @@
+// Internal interfaces between the C-ABI layer, the policy table and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace dbgemm {
+
+// Everything a kernel needs for one call.  Sizes are validated on the host before a
+// launch: the fast kernels additionally require every operand span to stay below
+// 2^31 bytes so that 32-bit buffer offsets cover it.
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  void* C;
+  int64_t lda, ldb, ldc;
+  int M, N, K;
+  float alpha, beta;
+  int c_f32;      // 1: C is fp32, 0: C is bf16
+  int in_fp8;     // 1: A, B are E4M3, 0: bf16
+  int transA, transB;
+  int tiles_m, tiles_n;
+  int group;      // raster group width (tiles) along the grouped dimension
+  int raster_n;   // 0: groups of `group` tile-rows walked along N; 1: the transpose
+  int xcd;        // number of XCDs to remap across (1 disables the remap)
+  int swizzle;    // 1: XOR-swizzled LDS layout, 0: plain row-major LDS tiles
+};
+
+enum PolicyKind { KIND_SIMT = 0, KIND_MFMA = 1, KIND_SCALE = 2 };
+
+struct Policy {
+  const char* name;
+  int kind;
+  int in_mode;     // 0: bf16 in, bf16 MFMA; 1: E4M3 in, widened to bf16 in LDS (exact
+                   // fp32 accumulation); 2: E4M3 in, native f8f6f4 MFMA; -1: any (generic)
+  int BM, BN, BK;  // workgroup tile
+  int WM, WN;      // waves along M and N
+  int MT;          // MFMA block edge (32 or 16)
+  int stages;      // LDS stages
+  int group, raster_n, xcd, swizzle;
+  int threads;
+  float efficiency;  // relative per-CU throughput used by the wave-time model
+};
+
+// Launchers (one per kernel family).  They return hipSuccess or the launch error.
+hipError_t launch_simt(const GemmArgs& a, hipStream_t s);
+hipError_t launch_scale(const GemmArgs& a, hipStream_t s);  // C <- beta*C (K == 0 or alpha == 0)
+hipError_t launch_mfma(const Policy& p, const GemmArgs& a, hipStream_t s);
+
+// Tile-policy table.
+int policy_count();
+const Policy& policy_at(int i);
+int policy_find(const char* name);
+
+struct Problem {
+  int transA, transB;
+  int64_t M, N, K;
+  int in_fp8, c_f32;
+  bool fast_ok;  // alignment / divisibility allow the MFMA kernels
+};
+// Shape-driven selection; returns an index into the table.
+int policy_select(const Problem& pr, int cu_count);
+bool policy_serves(const Policy& p, const Problem& pr);
+
+}  // namespace dbgemm

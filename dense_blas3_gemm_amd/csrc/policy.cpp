@@ -1,0 +1,85 @@
+// Shape-driven tile-policy table and its wave-time model.
+//
+// The fused profile protocol's GEMM policies (sections "fixed sampling flow" and the
+// QKV command: tile policies named by BM x BN, a `wave_time_model` auto policy, raster
+// m/n and swizzle 1/2/4/8 knobs, environment overrides used only to pin a policy for
+// ablation) are the model here.  On MI355X a "wave" is one round of workgroups over
+// the 256 CUs: a grid of T tiles with `occ` resident workgroups per CU takes
+// ceil(T / (CUs * occ)) rounds, each as long as one CU needs for `occ` tiles.
+#include <cstring>
+
+#include "gemm_internal.h"
+
+namespace dbgemm {
+namespace {
+
+const Policy kTable[] = {
+#define DBGEMM_SIMT(name_, eff_) {name_, KIND_SIMT, -1, 64, 64, 16, 1, 1, 0, 1, 1, 0, 1, 0, 256, eff_},
+#define DBGEMM_MFMA(name_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_, eff_) \
+  {name_, KIND_MFMA, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_, (wm_) * (wn_) * 64, eff_},
+#include "policies.inc"
+#undef DBGEMM_SIMT
+#undef DBGEMM_MFMA
+};
+constexpr int kCount = sizeof(kTable) / sizeof(kTable[0]);
+
+// Resident workgroups per CU: bounded by LDS (160 KiB) and by the unified register
+// file (512 registers per lane per SIMD shared by the waves on that SIMD).
+int occupancy(const Policy& p) {
+  const int es = p.in_mode == 2 ? 1 : 2;  // bytes per element in LDS
+  const int lds = p.stages * (p.BM + p.BN) * p.BK * es;
+  int occ_lds = (160 * 1024) / lds;
+  const int acc = (p.BM / p.WM) * (p.BN / p.WN) / 64;  // fp32 accumulators per lane
+  const int regs = acc + 128;                            // + fragments, staging, addresses
+  const int waves_per_simd = 512 / regs;
+  const int wg_waves_per_simd = (p.WM * p.WN + 3) / 4;
+  int occ_reg = waves_per_simd / wg_waves_per_simd;
+  int occ = occ_lds < occ_reg ? occ_lds : occ_reg;
+  if (occ < 1) occ = 1;
+  if (occ > 8) occ = 8;
+  return occ;
+}
+
+}  // namespace
+
+int policy_count() { return kCount; }
+const Policy& policy_at(int i) { return kTable[i]; }
+
+int policy_find(const char* name) {
+  if (!name) return -1;
+  for (int i = 0; i < kCount; ++i)
+    if (std::strcmp(kTable[i].name, name) == 0) return i;
+  return -1;
+}
+
+bool policy_serves(const Policy& p, const Problem& pr) {
+  if (p.kind == KIND_SIMT) return true;
+  if (p.kind != KIND_MFMA) return false;
+  return pr.fast_ok && (p.in_mode != 0) == (pr.in_fp8 != 0);
+}
+
+int policy_select(const Problem& pr, int cu_count) {
+  if (cu_count <= 0) cu_count = 256;
+  int best = policy_find("simt_generic");
+  if (!pr.fast_ok) return best;
+  double best_t = 0.0;
+  bool have = false;
+  const double K0 = 256.0;  // prologue + epilogue cost of a tile, in K-equivalents
+  for (int i = 0; i < kCount; ++i) {
+    const Policy& p = kTable[i];
+    if (p.kind != KIND_MFMA || p.efficiency <= 0.f || !policy_serves(p, pr)) continue;
+    const int occ = occupancy(p);
+    const double tiles = (double)((pr.M + p.BM - 1) / p.BM) * (double)((pr.N + p.BN - 1) / p.BN);
+    const double slots = (double)cu_count * occ;
+    const double rounds = (double)(int64_t)((tiles + slots - 1) / slots);
+    const double t = rounds * occ * (double)p.BM * p.BN * ((double)pr.K + K0) / p.efficiency;
+    if (!have || t < best_t * 0.999) {
+      best = i;
+      best_t = t;
+      have = true;
+    }
+  }
+  return best;
+}
+
+}  // namespace dbgemm

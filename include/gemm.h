@@ -1,0 +1,131 @@
+/*
+ * gemm.h -- C-ABI of the MI355X (gfx950) dense GEMM library.
+ *
+ * Operation.  Every entry point that computes evaluates the BLAS level-3 GEMM
+ *
+ *     C <- alpha * op(A) * op(B) + beta * C,      op(X) = X or X^T,
+ *
+ * the local compute that the pages are built on: the GEMM under the distributed
+ * BLAS3 operators of "BLASMp development notes" (section 1), the bf16 hgemm of the
+ * "cp.async / ldmatrix ablation" plan (section 2, fixed baseline M = N = K = 4096),
+ * and the projection-backward and FP8 GEMMs of the fused communication/compute
+ * profile protocol (sections "formal launch and timing rules": weight gradient with
+ * beta = 1 accumulating into bf16, plain mode beta = 0; "v10 backward operators":
+ * dW = dY^T X read in place; "v12 FP8 boundary": E4M3 operands, fp32 accumulation,
+ * no scales inside the operator).
+ *
+ * Layout.  Row-major only; the leading dimension is the row stride in elements.
+ *   op(A) is M x K: A is stored [M][lda >= K] (transA = 0) or [K][lda >= M] (transA = 1).
+ *   op(B) is K x N: B is stored [K][ldb >= N] (transB = 0) or [N][ldb >= K] (transB = 1).
+ *   C is stored [M][ldc >= N].
+ * A column-major caller uses C^T = op(B)^T op(A)^T.  A transposed operand is read in
+ * place; the library never makes a transposed copy.
+ *
+ * Types.  Inputs are bf16 or OCP E4M3 ("FN": bias 7, no infinities, max 448);
+ * products are accumulated in fp32; C is bf16 (round to nearest even) or fp32.
+ * E4M3 runs with unit scale: any scaling is the caller's (alpha may carry it).
+ *
+ * Memory and ownership.  A, B and C are device pointers owned by the caller.  The
+ * handle owns only host-side state.  gemm_run never allocates, never synchronises
+ * and returns once the kernel is enqueued on the handle's stream; faults during
+ * execution surface at the caller's next synchronisation.  A handle must be used
+ * from one host thread at a time.
+ *
+ * Errors.  Arguments are checked before anything is launched; on any error status
+ * nothing is launched and nothing is written.
+ *
+ * Special cases (BLAS convention):  M == 0 or N == 0: nothing to do, SUCCESS.
+ * K == 0 or alpha == 0: C <- beta * C.  beta == 0: C is written without being
+ * read, so NaN or Inf already in C does not propagate.
+ *
+ * Fast path.  The MFMA kernels need 16-byte aligned A, B and C, leading dimensions
+ * whose byte size is a multiple of 16, and the contiguous extent of each operand
+ * (K for a K-contiguous operand, M or N otherwise) a multiple of 8 elements (bf16)
+ * or 16 (E4M3).  Anything else runs on a generic kernel: slower, never an error.
+ */
+#ifndef DENSE_BLAS3_GEMM_AMD_GEMM_H
+#define DENSE_BLAS3_GEMM_AMD_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gemm_handle_s* gemm_handle_t;
+
+typedef enum { GEMM_OP_N = 0, GEMM_OP_T = 1 } gemm_op_t;
+
+/* input dtype -> C dtype; accumulation is always fp32 */
+typedef enum {
+  GEMM_BF16_F32 = 0,  /* bf16 A, B; fp32 C */
+  GEMM_BF16_BF16 = 1, /* bf16 A, B; bf16 C */
+  GEMM_E4M3_BF16 = 2, /* E4M3 A, B; bf16 C */
+  GEMM_E4M3_F32 = 3   /* E4M3 A, B; fp32 C */
+} gemm_dtype_t;
+
+typedef enum {
+  GEMM_STATUS_SUCCESS = 0,
+  GEMM_STATUS_INVALID_VALUE = 1,   /* bad size, leading dimension, pointer, op or dtype */
+  GEMM_STATUS_NOT_SUPPORTED = 2,   /* well-formed but unsupported (non-finite alpha/beta, policy) */
+  GEMM_STATUS_NOT_INITIALIZED = 3, /* NULL or destroyed handle; no usable HIP device */
+  GEMM_STATUS_LAUNCH_FAILED = 4,   /* the HIP runtime refused the launch */
+  GEMM_STATUS_INTERNAL = 5
+} gemm_status_t;
+
+/* Creates a handle bound to HIP device `device`; reads its CU count and builds the
+ * tile-policy table.  The handle starts on the default stream (NULL).  On error
+ * *h is set to NULL.  Allocates host memory only. */
+gemm_status_t gemm_create(gemm_handle_t* h, int device);
+
+/* Releases the handle.  Work already enqueued is unaffected.  NULL is accepted. */
+gemm_status_t gemm_destroy(gemm_handle_t h);
+
+/* Binds the hipStream_t (passed as void*) that later gemm_run calls enqueue on.
+ * NULL selects the default stream.  The caller keeps ownership of the stream. */
+gemm_status_t gemm_set_stream(gemm_handle_t h, void* stream);
+
+/* C <- alpha*op(A)*op(B) + beta*C on the handle's device and stream.  transA and
+ * transB take gemm_op_t values, dtype a gemm_dtype_t value.  Device pointers; A and B
+ * may be NULL only when the product is empty (M, N or K is 0), C only when M or N
+ * is 0. */
+gemm_status_t gemm_run(gemm_handle_t h, int transA, int transB, int64_t M, int64_t N,
+                       int64_t K, float alpha, const void* A, int64_t lda, const void* B,
+                       int64_t ldb, float beta, void* C, int64_t ldc, int dtype);
+
+/* Validates gemm_run's arguments on the host only (no handle, no device). */
+gemm_status_t gemm_check_args(int transA, int transB, int64_t M, int64_t N, int64_t K,
+                              float alpha, const void* A, int64_t lda, const void* B,
+                              int64_t ldb, float beta, const void* C, int64_t ldc, int dtype);
+
+/* Writes the name of the policy gemm_run would use for these arguments into
+ * name[len] (NUL-terminated, truncated to fit).  The pointers are only inspected
+ * for alignment.  h may be NULL: then a 256-CU device and no forced policy are
+ * assumed.  Pure host code. */
+gemm_status_t gemm_query_policy(gemm_handle_t h, int transA, int transB, int64_t M, int64_t N,
+                                int64_t K, const void* A, int64_t lda, const void* B,
+                                int64_t ldb, const void* C, int64_t ldc, int dtype, char* name,
+                                size_t len);
+
+/* Forces the named policy for later gemm_run calls on this handle (for ablations and
+ * invariance checks); NULL or "auto" restores the shape-driven choice.  A forced
+ * policy that cannot serve a call (dtype, alignment) returns NOT_SUPPORTED from
+ * gemm_run.  Unknown names return INVALID_VALUE. */
+gemm_status_t gemm_set_policy(gemm_handle_t h, const char* name);
+
+/* The policy table: count and names (index 0 .. count-1).  Out-of-range -> NULL. */
+int gemm_policy_count(void);
+const char* gemm_policy_name(int index);
+
+/* Library and policy-table version string, e.g. "dbgemm 0.1.0 policy-table 1". */
+const char* gemm_version(void);
+
+/* Human-readable name of a status code. */
+const char* gemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DENSE_BLAS3_GEMM_AMD_GEMM_H */

@@ -1,0 +1,333 @@
+"""GPU parity: the HIP path against the fp64 oracle, through the C-ABI.
+
+Small and ragged cases are compared element by element over the whole output;
+full-size workloads are compared on rows sampled across every M tile (the oracle
+computes each sampled row exactly), plus properties checked on every element.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import gemm_inputs as gi
+import oracle
+import tolerance
+from gpu_util import compare, empty_c, run_gpu, sample_rows, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+TRANS = [(0, 0), (0, 1), (1, 0), (1, 1)]
+BF16_POLICIES = ["bf16_m256n256k64_w2x2_mt32_s2", "bf16_m256n256k64_w2x4_mt32_s2",
+                 "bf16_m256n128k64_w2x2_mt32_s2", "bf16_m128n256k64_w2x2_mt32_s2",
+                 "bf16_m128n128k64_w2x2_mt32_s2", "bf16_m128n128k64_w2x2_mt16_s2",
+                 "bf16_m64n64k64_w2x2_mt16_s2", "bf16_m256n256k64_w2x2_mt32_s2_noswz",
+                 "bf16_m256n256k64_w2x2_mt32_s2_noxcd"]
+FP8_POLICIES = ["e4m3_m256n256k64_w2x2_mt32_s2", "e4m3_m256n256k64_w2x4_mt32_s2",
+                "e4m3_m128n128k64_w2x2_mt32_s2", "e4m3_m64n64k64_w2x2_mt16_s2"]
+FP8_NATIVE_POLICIES = ["e4m3native_m256n256k128_w2x2_mt32_s2", "e4m3native_m256n256k128_w2x4_mt32_s2",
+                       "e4m3native_m128n128k128_w2x2_mt32_s2", "e4m3native_m64n64k128_w2x2_mt16_s2"]
+
+
+def _assert_ok(res, what):
+    assert res["ok"], f"{what}: {res}"
+
+
+# ---------------------------------------------------------------- small, every element
+
+def test_library_loaded_from_tree(gpu):
+    import dense_blas3_gemm_amd as d
+    assert d._lib is not None and d.LIB_PATH.endswith("libdbgemm.so")
+
+
+def test_gemm_256_fp32_output(gpu):
+    """256^3 bf16 -> fp32 C, alpha 1, beta 0: every element."""
+    p = gi.SMALL_256
+    data = p.make()
+    C = run_gpu(gpu, p, data)
+    _assert_ok(compare(p, data, C), p.name)
+
+
+@pytest.mark.parametrize("tA,tB", TRANS)
+@pytest.mark.parametrize("policy", BF16_POLICIES + ["simt_generic", None])
+def test_bf16_policies_transposes(gpu, policy, tA, tB):
+    """Every bf16 policy on every transpose case, over several tiles and a ragged edge."""
+    p = gi.Gemm("t", 328, 296, 200, transA=tA, transB=tB, dist="normal")
+    data = p.make()
+    C = run_gpu(gpu, p, data, policy=policy)
+    _assert_ok(compare(p, data, C), f"{policy} {tA}{tB}")
+
+
+@pytest.mark.parametrize("tA,tB", TRANS)
+@pytest.mark.parametrize("policy", FP8_POLICIES + ["simt_generic", None])
+def test_e4m3_policies_transposes(gpu, policy, tA, tB):
+    for c_dtype in ("bf16", "f32"):
+        p = gi.Gemm("t", 320, 288, 384, transA=tA, transB=tB, in_dtype="e4m3", c_dtype=c_dtype,
+                    dist="e4m3")
+        data = p.make()
+        C = run_gpu(gpu, p, data, policy=policy)
+        _assert_ok(compare(p, data, C), f"{policy} {tA}{tB} {c_dtype}")
+
+
+@pytest.mark.parametrize("tA,tB", TRANS)
+@pytest.mark.parametrize("policy", FP8_NATIVE_POLICIES)
+def test_e4m3_native_policies(gpu, policy, tA, tB):
+    """The opt-in native f8f6f4 path, against its hardware-model bound."""
+    for c_dtype in ("bf16", "f32"):
+        p = gi.Gemm("t", 320, 288, 384, transA=tA, transB=tB, in_dtype="e4m3", c_dtype=c_dtype,
+                    dist="e4m3")
+        data = p.make()
+        C = run_gpu(gpu, p, data, policy=policy)
+        _assert_ok(compare(p, data, C, accumulate="e4m3_native"), f"{policy} {tA}{tB} {c_dtype}")
+
+
+def test_e4m3_widening_is_exact_for_every_code(gpu):
+    """C = A * e0 with fp32 C returns every E4M3 code's value exactly (NaN codes excluded)."""
+    codes = np.arange(256, dtype=np.uint8)
+    codes[[0x7F, 0xFF]] = 0
+    M, N, K = 256, 16, 32
+    A = np.zeros((M, K), dtype=np.uint8)
+    A[:, 0] = codes
+    A[:, 17] = codes[::-1]
+    B = np.zeros((K, N), dtype=np.uint8)
+    B[0, 0] = 0x38  # 1.0
+    B[17, 1] = 0x38
+    for policy in ["e4m3_m64n64k64_w2x2_mt16_s2", "e4m3_m256n256k64_w2x2_mt32_s2", "simt_generic"]:
+        p = gi.Gemm("t", M, N, K, in_dtype="e4m3", c_dtype="f32")
+        C = tolerance.f32_bits_to_f64(run_gpu(gpu, p, {"A": A, "B": B}, policy=policy))
+        assert np.array_equal(C[:, 0], oracle.decode(codes, "e4m3")), policy
+        assert np.array_equal(C[:, 1], oracle.decode(codes[::-1].copy(), "e4m3")), policy
+        assert np.all(C[:, 2:] == 0)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (7, 5, 3), (33, 17, 9), (255, 257, 129),
+                                   (257, 255, 64), (64, 8, 8), (8, 64, 16), (1, 300, 520),
+                                   (300, 1, 520), (513, 520, 8)])
+@pytest.mark.parametrize("tA,tB", TRANS)
+def test_odd_shapes_auto(gpu, M, N, K, tA, tB):
+    for c_dtype in ("bf16", "f32"):
+        p = gi.Gemm("t", M, N, K, transA=tA, transB=tB, c_dtype=c_dtype, dist="uniform")
+        data = p.make(seeds=(M, N, K))
+        C = run_gpu(gpu, p, data)
+        _assert_ok(compare(p, data, C), f"{M}x{N}x{K} {tA}{tB} {c_dtype}")
+
+
+def test_padded_leading_dimensions(gpu):
+    """Row strides larger than the row length (aligned and unaligned)."""
+    import torch
+    for lda_pad, ldc_pad in ((8, 8), (3, 5), (0, 0)):
+        M, N, K = 200, 136, 264
+        A_full = gi.bf16_uniform((M, K + lda_pad), 1)
+        B = gi.bf16_uniform((K, N), 2)
+        A = to_device(A_full, "bf16")[:, :K]
+        Bt = to_device(B, "bf16")
+        C = empty_c(M, N, "bf16", ldc=N + ldc_pad)
+        gpu(A, Bt, C)
+        torch.cuda.synchronize()
+        got = to_host(C)
+        R, S = oracle.gemm(0, 0, M, N, K, 1.0, A_full, K + lda_pad, B, N, 0.0, None, N,
+                           oracle.IN_BF16, oracle.C_BF16)
+        _assert_ok(tolerance.check(got, "bf16", R, S, K), f"pads {lda_pad},{ldc_pad}")
+
+
+# ---------------------------------------------------------------- alpha / beta
+
+@pytest.mark.parametrize("alpha,beta", [(1.0, 1.0), (2.5, -0.5), (0.0, 1.5), (0.0, 0.0),
+                                        (-1.0, 0.0), (1.0, 2.0)])
+@pytest.mark.parametrize("c_dtype", ["bf16", "f32"])
+def test_alpha_beta(gpu, alpha, beta, c_dtype):
+    p = gi.Gemm("t", 300, 264, 136, alpha=alpha, beta=beta, c_dtype=c_dtype, dist="normal",
+                c_dist="normal" if beta != 0 else None)
+    data = p.make()
+    if beta == 0.0:  # the old C is poisoned and must never be read
+        Cinit = np.full((p.M, p.N), np.nan, dtype=np.float32)
+        Cbits = gi.f32_bits(Cinit) if c_dtype == "f32" else gi.f32_to_bf16_bits(Cinit)
+    else:
+        Cbits = data["C"]
+    C = run_gpu(gpu, p, data, C_init=Cbits)
+    _assert_ok(compare(p, data, C), f"alpha={alpha} beta={beta}")
+
+
+def test_k_zero_scales_c(gpu):
+    """K = 0: C = beta*C_old; beta = 0 writes zeros without reading C."""
+    import torch
+    for beta in (0.0, 2.0, -0.5):
+        C0 = gi.bf16_normal((40, 24), 5)
+        C = to_device(C0, "bf16")
+        A = torch.empty((40, 0), dtype=torch.bfloat16, device="cuda:0")
+        B = torch.empty((0, 24), dtype=torch.bfloat16, device="cuda:0")
+        st = gpu.run_raw(0, 0, 40, 24, 0, 1.0, A.data_ptr(), 1, B.data_ptr(), 24, beta, C.data_ptr(),
+                         24, gi.DTYPE_CODES[("bf16", "bf16")])
+        assert st == 0
+        torch.cuda.synchronize()
+        R, _ = oracle.gemm(0, 0, 40, 24, 0, 1.0, np.zeros((40, 0), np.uint16), 1,
+                           np.zeros((0, 24), np.uint16), 24, beta, C0, 24, oracle.IN_BF16, oracle.C_BF16)
+        assert np.array_equal(to_host(C), oracle.round_bf16(R))
+
+
+# ---------------------------------------------------------------- exactness (bitwise)
+
+@pytest.mark.parametrize("tA,tB", TRANS)
+@pytest.mark.parametrize("in_dtype,c_dtype", [("bf16", "bf16"), ("bf16", "f32"), ("e4m3", "bf16"),
+                                              ("e4m3", "f32")])
+def test_integer_inputs_bitwise(gpu, tA, tB, in_dtype, c_dtype):
+    """Integer-valued inputs make every partial sum exact in fp32: C == RNE(R) bit for bit."""
+    kind = "int4" if in_dtype == "bf16" else "int8"
+    p = gi.Gemm("t", 520, 392, 1040, transA=tA, transB=tB, in_dtype=in_dtype, c_dtype=c_dtype, dist=kind)
+    data = p.make()
+    C = run_gpu(gpu, p, data)
+    R, _ = oracle.gemm_problem(p, data, with_abs=False)
+    want = oracle.round_bf16(R) if c_dtype == "bf16" else oracle.round_f32(R)
+    assert np.array_equal(C, want)
+
+
+@pytest.mark.parametrize("tA,tB", TRANS)
+def test_identity_and_permutation(gpu, tA, tB):
+    """op(A) = permutation matrix: C = rows of op(B) permuted, exactly."""
+    import torch
+    M = K = 384
+    N = 264
+    perm = np.random.default_rng(3).permutation(M)
+    P = np.zeros((M, K), dtype=np.float32)
+    P[np.arange(M), perm] = 1.0
+    Pb = gi.f32_to_bf16_bits(P)
+    opB = gi.bf16_normal((K, N), 4)
+    A = Pb.T.copy() if tA else Pb
+    B = opB.T.copy() if tB else opB
+    p = gi.Gemm("t", M, N, K, transA=tA, transB=tB)
+    C = run_gpu(gpu, p, {"A": A, "B": B})
+    assert np.array_equal(C, opB[perm])
+
+
+def test_all_ones_gives_k(gpu):
+    for K in (256, 4096, 5120, 8192):
+        p = gi.Gemm("t", 512, 512, K)
+        ones = gi.f32_to_bf16_bits(np.ones((512, K), dtype=np.float32))
+        onesB = gi.f32_to_bf16_bits(np.ones((K, 512), dtype=np.float32))
+        C = run_gpu(gpu, p, {"A": ones, "B": onesB})
+        assert np.all(tolerance.bf16_bits_to_f64(C) == K)
+
+
+# ---------------------------------------------------------------- invariance
+
+def test_data_movement_variants_bitwise_equal(gpu):
+    """Swizzle, XCD remap and raster only move data: identical bits (same BK and MFMA)."""
+    p = gi.Gemm("t", 1024, 768, 1000, dist="normal")
+    data = p.make()
+    outs = [run_gpu(gpu, p, data, policy=pol) for pol in
+            ["bf16_m256n256k64_w2x2_mt32_s2", "bf16_m256n256k64_w2x2_mt32_s2_noswz",
+             "bf16_m256n256k64_w2x2_mt32_s2_noxcd", "bf16_m256n256k64_w2x4_mt32_s2",
+             "bf16_m128n128k64_w2x2_mt32_s2"]]
+    for o in outs[1:]:
+        assert np.array_equal(outs[0], o)
+
+
+def test_run_to_run_deterministic_and_seed_sensitive(gpu):
+    p = gi.Gemm("t", 512, 512, 512, dist="normal")
+    d0 = p.make()
+    c1 = run_gpu(gpu, p, d0)
+    c2 = run_gpu(gpu, p, d0)
+    assert np.array_equal(c1, c2)
+    d1 = p.make(seeds=(10, 11, 12))
+    c3 = run_gpu(gpu, p, d1)
+    assert (c3 != c1).mean() > 0.99
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+@pytest.mark.slow
+def test_square_4096(gpu):
+    p = gi.SQUARE_4096
+    data = p.make()
+    C = run_gpu(gpu, p, data)
+    assert np.isfinite(tolerance.bf16_bits_to_f64(C)).all()
+    rows = sample_rows(p.M, per_tile=1, cap=40)
+    _assert_ok(compare(p, data, C, rows=rows), p.name)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", [g.name for g in gi.SWEEP])
+def test_sweep(gpu, name):
+    p = gi.BY_NAME[name]
+    data = p.make()
+    C = run_gpu(gpu, p, data)
+    assert np.isfinite(tolerance.bf16_bits_to_f64(C)).all()
+    rows = sample_rows(p.M, per_tile=1, cap=24)
+    _assert_ok(compare(p, data, C, rows=rows), name)
+
+
+@pytest.mark.slow
+def test_projection_backward_pair(gpu):
+    """dX = dY W (NN, beta 0); dW += dY^T X (TN, beta 1, bf16 grad), dY read in place."""
+    import torch
+    d = gi.proj_backward_inputs()
+    dY = to_device(d["dY"], "bf16")
+    W = to_device(d["W"], "bf16")
+    X = to_device(d["X"], "bf16")
+    dX = empty_c(2048, 5120, "bf16")
+    dW = to_device(d["dW0"], "bf16")
+    gpu(dY, W, dX)
+    gpu(dY, X, dW, transA=1, beta=1.0)
+    torch.cuda.synchronize()
+    dX_h, dW_h = to_host(dX), to_host(dW)
+    rows = sample_rows(2048, per_tile=1, cap=16)
+    _assert_ok(compare(gi.PROJ_DX, {"A": d["dY"], "B": d["W"]}, dX_h, rows=rows), "dX")
+    rows = sample_rows(5120, per_tile=1, cap=24)
+    _assert_ok(compare(gi.PROJ_DW, {"A": d["dY"], "B": d["X"], "C": d["dW0"]}, dW_h, rows=rows), "dW")
+
+
+@pytest.mark.slow
+def test_projection_backward_beta_visible(gpu):
+    """X scaled by 2^-8 (exact in bf16) so dY^T X is ~0.18 while beta*C_old ~ 0.02: a
+    dropped beta term fails the bound."""
+    import torch
+    d = gi.proj_backward_inputs()
+    Xs = gi.f32_to_bf16_bits(tolerance.bf16_bits_to_f64(d["X"]).astype(np.float32) * np.float32(2 ** -8))
+    dY = to_device(d["dY"], "bf16")
+    dW = to_device(d["dW0"], "bf16")
+    gpu(dY, to_device(Xs, "bf16"), dW, transA=1, beta=1.0)
+    torch.cuda.synchronize()
+    rows = sample_rows(5120, per_tile=1, cap=24)
+    p = gi.PROJ_DW
+    data = {"A": d["dY"], "B": Xs, "C": d["dW0"]}
+    res = compare(p, data, to_host(dW), rows=rows)
+    _assert_ok(res, "dW scaled")
+    # the same output checked against an oracle without the beta term must fail
+    p0 = dataclasses.replace(p, beta=0.0)
+    assert not compare(p0, data, to_host(dW), rows=rows)["ok"]
+
+
+@pytest.mark.slow
+def test_fp8_16384(gpu):
+    p = gi.FP8_FWD
+    data = p.make()
+    C = run_gpu(gpu, p, data)
+    assert np.isfinite(tolerance.bf16_bits_to_f64(C)).all()
+    rows = sample_rows(p.M, tile=256, per_tile=0, cap=24)
+    _assert_ok(compare(p, data, C, rows=rows), p.name)
+    # the fp32 bound applies to the accumulation: same inputs with fp32 C
+    p32 = dataclasses.replace(p, c_dtype="f32")
+    C32 = run_gpu(gpu, p32, data)
+    res = compare(p32, data, C32, rows=rows)
+    _assert_ok(res, "fp8 -> fp32")
+    assert res["frob_rel"] <= 1e-5
+
+
+@pytest.mark.slow
+def test_fp8_16384_native(gpu):
+    """The opt-in native f8f6f4 path at the full forward shape, hardware-model bound."""
+    p = gi.FP8_FWD
+    data = p.make()
+    C = run_gpu(gpu, p, data, policy="e4m3native_m256n256k128_w2x2_mt32_s2")
+    rows = sample_rows(p.M, tile=256, per_tile=0, cap=16)
+    _assert_ok(compare(p, data, C, rows=rows, accumulate="e4m3_native"), "native")
+
+
+@pytest.mark.slow
+def test_full_size_integer_bitwise(gpu):
+    """4096^3 with integer inputs: sampled rows equal RNE(R) bit for bit; all-ones elsewhere."""
+    p = dataclasses.replace(gi.SQUARE_4096, dist="int4")
+    data = p.make()
+    C = run_gpu(gpu, p, data)
+    rows = sample_rows(p.M, per_tile=1, cap=24)
+    R, _ = oracle.gemm_problem(p, data, rows=rows, with_abs=False)
+    assert np.array_equal(C[rows], oracle.round_bf16(R))
