@@ -1,6 +1,7 @@
 """Benchmark of the dense GEMM hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--sweep]
+                    [--ablation] [--policy NAME] [--workload NAME] [--copy-calibration MiB]
 
 A step is one call C = alpha*A*B + beta*C of the headline workload, 4096^3 bf16
 row-major NN with bf16 C (alpha 1, beta 0), on inputs already resident in HBM.
@@ -10,6 +11,11 @@ recorded on the stream the kernel runs on.  Prints one JSON line.
 
 --sweep additionally times every other workload (10 warmup + 50 event-timed calls
 each, p50/p95) and prints a Markdown table to stderr; the JSON line is unchanged.
+--ablation times every applicable policy on the headline and the E4M3 workloads.
+--policy / --workload pin the policy or pick another workload for the timed steps
+(used for profiling single kernels); the JSON line then names them in `config`.
+--copy-calibration N runs only a plain device-to-device copy of N MiB (the known-size
+reference that scales the rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exits.
 """
 from __future__ import annotations
 
@@ -31,7 +37,8 @@ HBM_GBS = 8000.0
 METRIC = "TFLOP/s and % of MI355X dense MFMA peak, 4096³ bf16 GEMM (1 GPU)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_4096_bf16.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "dense_blas3_gemm_amd", "csrc", f)
-                  for f in ("kernel_mfma.hip", "policies.inc", "policy.cpp")]
+                  for f in ("kernel_mfma.hip", "kernel_mfma_dma.hip", "mfma_common.h", "policies.inc",
+                            "policy.cpp")]
 
 
 def _dev(bits, kind):
@@ -178,6 +185,9 @@ def main():
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--ablation", action="store_true",
                     help="time every applicable policy on the 4096^3 bf16 and the E4M3 workloads")
+    ap.add_argument("--policy", default=None, help="force a named policy for the timed steps")
+    ap.add_argument("--workload", default=gi.SQUARE_4096.name, choices=sorted(gi.BY_NAME))
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this GEMM engine runs on a single MI355X "
@@ -190,17 +200,29 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": args.warmup + args.steps}))
+        return
     g = d.Gemm(0)
-    p = gi.SQUARE_4096
+    p = gi.BY_NAME[args.workload]
+    if args.policy:
+        g.set_policy(args.policy)
     r = time_problem(g, p, args.warmup, args.steps)
+    g.set_policy(None)
     ms = r["wall_ms"]
     value = p.flops / (ms * 1e-3) / 1e12
     ev = r["event_ms"]
     avg_launch_ms = float(ev.mean())
     achieved = p.flops / (avg_launch_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS["bf16"]
+    peak = PEAK_TFLOPS[p.in_dtype]
     out = {
-        "metric": METRIC,
+        "metric": METRIC if p is gi.SQUARE_4096 else f"TFLOP/s and % of MI355X dense MFMA peak, {p.name} (1 GPU)",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -210,14 +232,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": p.in_dtype,
         "data": "synthetic",
         "pct_of_peak": round(100.0 * value / peak, 2),
-        "config": {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "layout": "row-major NN",
-                   "inputs": "bf16 U[-1,1) seeds 0/1", "c_dtype": "bf16", "accumulate": "f32",
-                   "alpha": p.alpha, "beta": p.beta, "policy": r["policy"]},
+        "config": {"workload": p.name, "M": p.M, "N": p.N, "K": p.K,
+                   "layout": "row-major " + "NT"[p.transA] + "NT"[p.transB],
+                   "inputs": f"{p.in_dtype} {p.dist} seeds {p.seeds[0]}/{p.seeds[1]}", "c_dtype": p.c_dtype,
+                   "accumulate": "f32", "alpha": p.alpha, "beta": p.beta, "policy": r["policy"]},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": measured_traffic(),
+                     "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic() if p is gi.SQUARE_4096 and not args.policy else None,
                      "launch_us_p50": round(float(np.percentile(ev, 50)) * 1e3, 2),
                      "launch_us_p95": round(float(np.percentile(ev, 95)) * 1e3, 2),
                      "launch_us_mean": round(avg_launch_ms * 1e3, 2)},

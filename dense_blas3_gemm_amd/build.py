@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libdbgemm.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["api.cpp", "policy.cpp", "kernel_simt.hip", "kernel_mfma.hip"]
+SOURCES = ["api.cpp", "policy.cpp", "kernel_simt.hip", "kernel_mfma.hip", "kernel_mfma_dma.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",

@@ -246,7 +246,7 @@ gemm_status_t gemm_run(gemm_handle_t h, int transA, int transB, int64_t M, int64
       a.raster_n = pol.raster_n;
       a.xcd = pol.xcd;
       a.swizzle = pol.swizzle;
-      err = launch_mfma(pol, a, p->stream);
+      err = pol.pipe == 1 ? launch_mfma_dma(pol, a, p->stream) : launch_mfma_staged(pol, a, p->stream);
     }
   }
   if (cur != p->device) (void)hipSetDevice(cur);

@@ -32,6 +32,7 @@ enum PolicyKind { KIND_SIMT = 0, KIND_MFMA = 1, KIND_SCALE = 2 };
 struct Policy {
   const char* name;
   int kind;
+  int pipe;        // 0: global -> registers -> LDS (two stages); 1: direct-to-LDS loads
   int in_mode;     // 0: bf16 in, bf16 MFMA; 1: E4M3 in, widened to bf16 in LDS (exact
                    // fp32 accumulation); 2: E4M3 in, native f8f6f4 MFMA; -1: any (generic)
   int BM, BN, BK;  // workgroup tile
@@ -46,7 +47,8 @@ struct Policy {
 // Launchers (one per kernel family).  They return hipSuccess or the launch error.
 hipError_t launch_simt(const GemmArgs& a, hipStream_t s);
 hipError_t launch_scale(const GemmArgs& a, hipStream_t s);  // C <- beta*C (K == 0 or alpha == 0)
-hipError_t launch_mfma(const Policy& p, const GemmArgs& a, hipStream_t s);
+hipError_t launch_mfma_staged(const Policy& p, const GemmArgs& a, hipStream_t s);  // pipe 0
+hipError_t launch_mfma_dma(const Policy& p, const GemmArgs& a, hipStream_t s);     // pipe 1
 
 // Tile-policy table.
 int policy_count();

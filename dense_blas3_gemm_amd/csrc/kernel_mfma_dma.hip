@@ -1,0 +1,283 @@
+// MFMA GEMM kernels for gfx950 with direct-to-LDS operand staging.
+//
+// Same operation, LDS layout, fragment reads, MFMA and epilogue as the register-
+// staged kernels (mfma_common.h), but the global -> LDS copy goes through the
+// gfx950 buffer-load-to-LDS path: one `buffer_load_dwordx4 ... lds` moves 64 x 16
+// bytes from 64 independently addressed global chunks into 1 KiB of contiguous LDS
+// (lane i -> M0 + 16*i), without passing through vector registers.  This is the
+// CDNA4 counterpart of the pages' asynchronous global->shared copies (the
+// "cp.async / ldmatrix ablation" plan, sections 0.2 and 1: copy groups, per-stage
+// completion tracking, multi-stage buffering), re-designed around what gfx950 has:
+//
+//   * a ring of STAGES LDS buffers; stage t+STAGES is loaded while stage t is
+//     consumed, so loads run STAGES-1 K tiles ahead of the matrix cores;
+//   * the LDS XOR swizzle is applied on the load side: the lane that fills LDS
+//     chunk p fetches the global chunk that the swizzle maps to p;
+//   * completion is tracked per wave with `s_waitcnt vmcnt(N)` counting the
+//     loads still in flight, followed by one workgroup barrier per K tile;
+//   * the barrier of tile t+1 is taken before the last K step of tile t, so the
+//     first fragments of tile t+1 are read while tile t's last MFMAs execute.
+//
+// The cross-wave wait is explicit (`s_waitcnt vmcnt` + `s_barrier`); within a wave the
+// compiler also orders each LDS read after the loads into the same ring slot.
+#include "mfma_common.h"
+
+namespace dbgemm {
+namespace {
+
+// 64 lanes x 16 bytes from buffer `rsrc` at per-lane byte offset `voff` into LDS
+// bytes [lds_base, lds_base + 1024) (lane i -> lds_base + 16*i); an offset past the
+// buffer's size reads zeros.  Issued as assembly: the compiler neither sees nor waits
+// for these loads (it could not tell them apart from the LDS reads of other ring
+// slots), so every wait on them below is explicit.
+__device__ __forceinline__ void load_to_lds(uint32_t lds_base, uint32_t voff, __amdgpu_buffer_rsrc_t rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
+// Waits until at most N of this wave's buffer loads are in flight and all its LDS
+// reads have returned, then joins the workgroup barrier.
+template <int N>
+__device__ __forceinline__ void wait_loads_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+template <class C>
+struct Dma {
+  static_assert(C::IN != IN_E4M3, "widening needs the register-staged pipeline");
+  static_assert(C::GES == C::ES, "LDS holds the global format");
+  static constexpr int NW = C::THREADS / 64;
+  static_assert(C::A_BYTES % (1024 * NW) == 0 && C::B_BYTES % (1024 * NW) == 0,
+                "each wave loads whole 1 KiB blocks of both tiles");
+  static constexpr int A_IPW = C::A_BYTES / 1024 / NW;  // load instructions per wave per tile
+  static constexpr int B_IPW = C::B_BYTES / 1024 / NW;
+  static constexpr int IPW = A_IPW + B_IPW;
+  static_assert(C::STAGES >= 2 && C::STAGES <= 4, "two to four LDS stages");
+  static_assert((C::STAGES - 1) * IPW <= 63, "vmcnt range");
+  static_assert(C::KSTEPS >= 2 && C::KSTEPS % 2 == 0,
+                "an even number (>= 2) of K steps per tile: loads ride on the first steps");
+  // the loads of one tile are spread over the first KSTEPS-1 steps of the tile before
+  static constexpr int LOAD_STEPS = C::KSTEPS - 1;
+  static constexpr int loads_before(int kk) { return IPW * kk / LOAD_STEPS; }
+};
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(GemmArgs a) {
+  using D = Dma<C>;
+  // One LDS object per ring slot: the compiler tracks the loads into each slot on
+  // its own, so its automatic waits before LDS reads wait for that slot only.
+  __shared__ __attribute__((aligned(1024))) char lds_s0[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds_s1[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds_s2[C::STAGES > 2 ? C::STAGE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char lds_s3[C::STAGES > 3 ? C::STAGE_BYTES : 16];
+  auto slot = [&](auto sc) -> lds_char* {
+    constexpr int s = decltype(sc)::value;
+    if constexpr (s == 0) return (lds_char*)lds_s0;
+    else if constexpr (s == 1) return (lds_char*)lds_s1;
+    else if constexpr (s == 2) return (lds_char*)lds_s2;
+    else return (lds_char*)lds_s3;
+  };
+  using Frag = typename FragOf<C::FP8>::T;
+  using Acc = typename AccOf<C::MT>::T;
+
+  int tm, tn;
+  tile_of(blockIdx.x, a, tm, tn);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int sw_on = a.swizzle;
+
+  const uint32_t a_rows = C::A_KC ? a.M : a.K;
+  const uint32_t b_rows = C::B_KC ? a.N : a.K;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, (uint32_t)(a_rows * a.lda * C::ES));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.B, (uint32_t)(b_rows * a.ldb * C::ES));
+
+  // ---- per-lane sources of the load instructions (fixed over the K loop).
+  // Instruction i of this wave fills LDS block blk = wave*IPW + i of the tile; this
+  // lane fills chunk p = blk*64 + lane, i.e. row p / CPR and physical chunk p % CPR,
+  // which holds logical chunk (p % CPR) ^ swizzle(row).
+  uint32_t a_goff[D::A_IPW], b_goff[D::B_IPW];
+  int a_kc[D::A_IPW], b_kc[D::B_IPW];  // K index of this lane's chunk within a tile
+  bool a_ok[D::A_IPW], b_ok[D::B_IPW];
+#pragma unroll
+  for (int i = 0; i < D::A_IPW; ++i) {
+    const int p = (wave * D::A_IPW + i) * 64 + lane;
+    const int r = p / C::A_CPR;
+    const int c = (p % C::A_CPR) ^ (sw_on ? swz<C::A_KC, C::FP8, C::A_CPR>(r) : 0);
+    if constexpr (C::A_KC) {  // rows = m, chunks along k
+      a_goff[i] = (uint32_t)((m0 + r) * a.lda + c * C::VEC) * C::ES;
+      a_ok[i] = (m0 + r) < a.M;
+      a_kc[i] = c * C::VEC;
+    } else {  // rows = k, chunks along m
+      a_goff[i] = (uint32_t)(r * a.lda + m0 + c * C::VEC) * C::ES;
+      a_ok[i] = (m0 + c * C::VEC) < a.M;
+      a_kc[i] = r;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < D::B_IPW; ++i) {
+    const int p = (wave * D::B_IPW + i) * 64 + lane;
+    const int r = p / C::B_CPR;
+    const int c = (p % C::B_CPR) ^ (sw_on ? swz<C::B_KC, C::FP8, C::B_CPR>(r) : 0);
+    if constexpr (C::B_KC) {  // rows = n, chunks along k
+      b_goff[i] = (uint32_t)((n0 + r) * a.ldb + c * C::VEC) * C::ES;
+      b_ok[i] = (n0 + r) < a.N;
+      b_kc[i] = c * C::VEC;
+    } else {  // rows = k, chunks along n
+      b_goff[i] = (uint32_t)(r * a.ldb + n0 + c * C::VEC) * C::ES;
+      b_ok[i] = (n0 + c * C::VEC) < a.N;
+      b_kc[i] = r;
+    }
+  }
+  const uint32_t a_kstep = C::A_KC ? C::BK * C::ES : (uint32_t)(C::BK * a.lda * C::ES);
+  const uint32_t b_kstep = C::B_KC ? C::BK * C::ES : (uint32_t)(C::BK * a.ldb * C::ES);
+
+  // Loads instructions [lo, hi) of K tile kt (A blocks first, then B) into slot sb.
+  // Past the end of K every offset is out of range: the loads read zeros and touch no
+  // memory.
+  const uint32_t a_blk = (uint32_t)(wave * D::A_IPW) * 1024u;
+  const uint32_t b_blk = C::A_BYTES + (uint32_t)(wave * D::B_IPW) * 1024u;
+  // Load instruction q (A blocks first, then B) of K tile kt into slot sb.
+  auto issue_one = [&](const lds_char* sb, int kt, auto qc) {
+    constexpr int q = decltype(qc)::value;
+    const int k0 = kt * C::BK;
+    const uint32_t base = (uint32_t)(uintptr_t)sb;
+    if constexpr (q < D::A_IPW) {
+      const bool ok = a_ok[q] & (k0 + a_kc[q] < a.K);
+      load_to_lds(__builtin_amdgcn_readfirstlane(base + a_blk + q * 1024u),
+                  ok ? a_goff[q] + (uint32_t)kt * a_kstep : kOOB, ra);
+    } else {
+      constexpr int i = q - D::A_IPW;
+      const bool ok = b_ok[i] & (k0 + b_kc[i] < a.K);
+      load_to_lds(__builtin_amdgcn_readfirstlane(base + b_blk + i * 1024u),
+                  ok ? b_goff[i] + (uint32_t)kt * b_kstep : kOOB, rb);
+    }
+  };
+
+  Acc acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = Acc{};
+
+  const int nk = (a.K + C::BK - 1) / C::BK;
+  const int xa0 = wm * C::WTM, xb0 = wn * C::WTN;
+
+  Frag fa[2][C::FM], fb[2][C::FN];
+  // Fragment r of K step kk, in the order the MFMAs first use them (the MFMAs run
+  // A-fragment-major): A0, B0 .. B(FN-1), then A1 .. A(FM-1).
+  auto read_one = [&](const lds_char* sb, int kk, Frag* xa, Frag* xb, auto rc) {
+    constexpr int r = decltype(rc)::value;
+    constexpr bool is_b = r >= 1 && r <= C::FN;
+    constexpr int idx = r == 0 ? 0 : (is_b ? r - 1 : r - C::FN);
+    if constexpr (!is_b)
+      xa[idx] = load_frag<C, C::A_KC, C::A_RB>(sb, xa0 + idx * C::MT, kk * C::KT, lane, sw_on);
+    else
+      xb[idx] = load_frag<C, C::B_KC, C::B_RB>(sb + C::A_BYTES, xb0 + idx * C::MT, kk * C::KT, lane, sw_on);
+  };
+  auto read_step = [&](const lds_char* sb, int kk, Frag* xa, Frag* xb) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+      xa[i] = load_frag<C, C::A_KC, C::A_RB>(sb, xa0 + i * C::MT, kk * C::KT, lane, sw_on);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+      xb[j] = load_frag<C, C::B_KC, C::B_RB>(sb + C::A_BYTES, xb0 + j * C::MT, kk * C::KT, lane, sw_on);
+  };
+
+  // ---- prologue: tiles 0 .. STAGES-2 into slots 0 .. STAGES-2; wait for tile 0
+  static_for<C::STAGES - 1>([&](auto sc) {
+    static_for<D::IPW>([&](auto qc) { issue_one(slot(sc), decltype(sc)::value, qc); });
+  });
+  wait_loads_and_barrier<(C::STAGES - 2) * D::IPW>();
+  read_step(slot(std::integral_constant<int, 0>{}), 0, fa[0], fb[0]);
+
+  // ---- main loop.  Tile u lives in slot u % STAGES.  During tile u's first K steps
+  // the loads of tile u+STAGES-1 go into slot (u-1) % STAGES, which every wave left at
+  // the barrier of tile u-1.  In tile u's last step each wave waits for its loads of
+  // tile u+1, the barrier makes all of them visible, and the first fragments of tile
+  // u+1 are read while tile u's last MFMAs run.  The loop runs over whole rings;
+  // tiles past the end of K are all zeros and add nothing.
+  for (int kt0 = 0; kt0 < nk; kt0 += C::STAGES) {
+    static_for<C::STAGES>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      const int u = kt0 + s;
+      const lds_char* cur = slot(sc);
+      const lds_char* nxt = slot(std::integral_constant<int, (s + 1) % C::STAGES>{});
+      lds_char* fill = slot(std::integral_constant<int, (s + C::STAGES - 1) % C::STAGES>{});
+      static_for<C::KSTEPS>([&](auto kkc) {
+        constexpr int kk = decltype(kkc)::value;
+        constexpr bool last = kk + 1 == C::KSTEPS;
+        constexpr int NMF = C::FM * C::FN;
+        constexpr int NRF = C::FM + C::FN;
+        // the barrier of the last step comes after its first quarter of MFMAs, which
+        // keep the matrix core busy while the workgroup gathers
+        constexpr int BAR_AT = last ? (NMF + 3) / 4 : -1;
+        constexpr int RD0 = last ? BAR_AT : 0;  // reads start after the barrier
+        constexpr int LD0 = kk < D::LOAD_STEPS ? D::loads_before(kk) : 0;
+        constexpr int NLD = kk < D::LOAD_STEPS ? D::loads_before(kk + 1) - LD0 : 0;
+        Frag* ra_next = fa[(kk + 1) & 1];
+        Frag* rb_next = fb[(kk + 1) & 1];
+        const lds_char* rsrc_slot = last ? nxt : cur;
+        const int rkk = last ? 0 : kk + 1;
+        // Explicit order: MFMA i, then its share of the fragment reads for the next
+        // step and of the loads for tile u+STAGES-1; nothing is moved across a group.
+        static_for<NMF>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          if constexpr (i == BAR_AT) wait_loads_and_barrier<(C::STAGES - 2) * D::IPW>();
+          mma(acc[i / C::FN][i % C::FN], fb[kk & 1][i % C::FN], fa[kk & 1][i / C::FN]);
+          if constexpr (i >= RD0) {
+            constexpr int r0 = NRF * (i - RD0) / (NMF - RD0), r1 = NRF * (i + 1 - RD0) / (NMF - RD0);
+            static_for<r1 - r0>([&](auto jc) {
+              read_one(rsrc_slot, rkk, ra_next, rb_next, std::integral_constant<int, r0 + decltype(jc)::value>{});
+            });
+          }
+          constexpr int l0 = LD0 + NLD * i / NMF, l1 = LD0 + NLD * (i + 1) / NMF;
+          static_for<l1 - l0>([&](auto qc) {
+            issue_one(fill, u + C::STAGES - 1, std::integral_constant<int, l0 + decltype(qc)::value>{});
+          });
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      });
+    });
+  }
+  // drain the loads of the tiles past the end before the workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  store_tile<C>(a, acc, m0 + xa0, n0 + xb0, lane);
+}
+
+template <class C>
+hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
+  const int ntiles = a.tiles_m * a.tiles_n;
+  hipLaunchKernelGGL(gemm_dma_kernel<C>, dim3(ntiles), dim3(C::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int MT, int ST, int IN>
+hipError_t launch_trans(const GemmArgs& a, hipStream_t s) {
+  switch (a.transA * 2 + a.transB) {
+    case 0: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, false, false>>(a, s);
+    case 1: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, false, true>>(a, s);
+    case 2: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, true, false>>(a, s);
+    default: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, true, true>>(a, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mfma_dma(const Policy& p, const GemmArgs& a, hipStream_t s) {
+#define DBGEMM_SIMT(name, eff)
+#define DBGEMM_MFMA(name_, pipe_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_, eff_)       \
+  if constexpr (pipe_ == 1)                                                                               \
+    if (p.BM == bm_ && p.BN == bn_ && p.BK == bk_ && p.WM == wm_ && p.WN == wn_ && p.MT == mt_ &&         \
+        p.stages == st_ && p.in_mode == in_)                                                              \
+      return launch_trans<bm_, bn_, bk_, wm_, wn_, mt_, st_, in_>(a, s);
+#include "policies.inc"
+#undef DBGEMM_SIMT
+#undef DBGEMM_MFMA
+  return hipErrorInvalidConfiguration;
+}
+
+}  // namespace dbgemm

@@ -1,0 +1,337 @@
+// Device-side building blocks shared by the MFMA GEMM kernels for gfx950:
+// vector types, buffer resources, the tile raster, the LDS XOR swizzle, MFMA
+// fragment reads (direct and transposing), scheduling hints, E4M3 widening and the
+// alpha/beta epilogue.  Included by the kernel translation units only.
+#pragma once
+
+#include <type_traits>
+
+#include "gemm_internal.h"
+
+namespace dbgemm {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) char lds_char;
+#define LDS_PTR(T, base, off) ((__attribute__((address_space(3))) T*)((base) + (off)))
+
+constexpr uint32_t kOOB = 0x80000000u;  // offset past every buffer's num_records
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Workgroup id -> output tile.  First an XCD-aware remap: the hardware hands
+// consecutive workgroup ids to the XCDs round-robin, so id b runs on XCD b % xcd;
+// the remap gives each XCD one contiguous run of the raster order, which keeps the
+// A and B panels that neighbouring tiles share inside one XCD's L2.  Then a grouped
+// raster: `group` tile-rows are walked column by column (or the transpose).  Both
+// maps are bijections, so every tile is computed exactly once.
+__device__ inline void tile_of(int bid, const GemmArgs& a, int& tm, int& tn) {
+  const int ntiles = a.tiles_m * a.tiles_n;
+  int L = bid;
+  if (a.xcd > 1) {
+    const int q = ntiles / a.xcd;
+    if (bid < q * a.xcd) L = (bid % a.xcd) * q + bid / a.xcd;
+  }
+  const int major = a.raster_n ? a.tiles_m : a.tiles_n;  // tiles along the walk
+  const int minor = a.raster_n ? a.tiles_n : a.tiles_m;  // grouped dimension
+  const int width = a.group * major;
+  const int g = L / width;
+  const int first = g * a.group;
+  const int gs = min(minor - first, a.group);
+  const int r = L - g * width;
+  const int i_minor = first + r % gs;
+  const int i_major = r / gs;
+  tm = a.raster_n ? i_major : i_minor;
+  tn = a.raster_n ? i_minor : i_major;
+}
+
+// Input modes: IN_BF16 (bf16 operands, bf16 MFMA); IN_E4M3 (E4M3 operands widened
+// exactly to bf16 on their way into LDS, bf16 MFMA: full fp32 accumulation);
+// IN_E4M3_NATIVE (E4M3 operands fed to the f8f6f4 MFMA as they are).
+enum { IN_BF16 = 0, IN_E4M3 = 1, IN_E4M3_NATIVE = 2 };
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int MT_, int STAGES_, int IN_, bool TA_, bool TB_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, MT = MT_, STAGES = STAGES_;
+  static constexpr int IN = IN_;
+  static constexpr bool TA = TA_, TB = TB_;
+  static constexpr bool FP8 = IN == IN_E4M3_NATIVE;  // fragments and MFMA are E4M3
+  static constexpr int THREADS = WM * WN * 64;
+  static constexpr int GES = IN == IN_BF16 ? 2 : 1;  // bytes per element in global memory
+  static constexpr int ES = FP8 ? 1 : 2;             // bytes per element in LDS and fragments
+  static constexpr int WIDEN = ES / GES;             // LDS chunks per global 16-byte chunk
+  static constexpr int VEC = 16 / GES;               // elements per global 16-byte chunk
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int KT = FP8 ? (MT == 32 ? 64 : 128) : (MT == 32 ? 16 : 32);  // K per MFMA
+  static constexpr int KPL = FP8 ? 32 : 8;                                        // K per lane
+  static constexpr int FM = WTM / MT, FN = WTN / MT;
+  static constexpr int KSTEPS = BK / KT;
+  static constexpr int ACC = MT * MT / 64;  // accumulator floats per lane per block
+  // operand tiles in LDS: rows x cols elements, cols contiguous
+  static constexpr bool A_KC = !TA, B_KC = TB;
+  static constexpr int A_ROWS = A_KC ? BM : BK, A_COLS = A_KC ? BK : BM;
+  static constexpr int B_ROWS = B_KC ? BN : BK, B_COLS = B_KC ? BK : BN;
+  static constexpr int A_RB = A_COLS * ES, B_RB = B_COLS * ES;  // LDS row bytes
+  static constexpr int A_CPR = A_RB / 16, B_CPR = B_RB / 16;    // LDS chunks per row
+  static constexpr int A_GCPR = A_COLS * GES / 16, B_GCPR = B_COLS * GES / 16;  // global chunks per row
+  static constexpr int A_BYTES = A_ROWS * A_RB, B_BYTES = B_ROWS * B_RB;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int A_CH = A_ROWS * A_GCPR / THREADS, B_CH = B_ROWS * B_GCPR / THREADS;
+
+  // LDS read instructions per fragment and per K step of one wave
+  static constexpr int A_FRAG_READS = A_KC ? (FP8 ? 2 : 1) : (FP8 ? 4 : 2);
+  static constexpr int B_FRAG_READS = B_KC ? (FP8 ? 2 : 1) : (FP8 ? 4 : 2);
+  static constexpr int DS_READS_PER_STEP = FM * A_FRAG_READS + FN * B_FRAG_READS;
+
+  static_assert(WTM % MT == 0 && WTN % MT == 0, "wave tile must hold whole MFMA blocks");
+  static_assert(BK % KT == 0, "BK must hold whole MFMA K steps");
+  static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
+};
+
+// XOR swizzle of the 16-byte chunk index of LDS row r.
+//  * K-contiguous tiles (row = 64, 128 or 256 bytes) are read by ds_read_b128 with
+//    16 consecutive lanes on 16 consecutive rows at one chunk column: the xor makes
+//    those 16 reads land on distinct 16-byte slots of the 256-byte bank line, and any
+//    8 consecutive rows on distinct slots of a 128-byte line.
+//  * M/N-contiguous bf16 tiles are read by ds_read_b64_tr_b16: each group of 16
+//    lanes reads 4 consecutive rows of one 32-byte column pair; a half wave reads
+//    either two neighbouring pairs of the same rows (32x32 MFMA) or one pair of rows
+//    r..r+3 and r+8..r+11 (16x16).  The xor moves the pair by ((r&3)<<1)|((r>>3)&1).
+//  * M/N-contiguous E4M3 tiles are read by ds_read_b64_tr_b8: 16 lanes read 8
+//    consecutive rows of one 16-byte chunk; a half wave reads two neighbouring
+//    chunks of the same rows (32x32) or rows r..r+7 and r+32..r+39 (16x16).
+// The result is masked to the row's chunk count, so a swizzled chunk never leaves
+// its row whatever the tile width.
+template <bool KC, bool FP8, int CPR>
+__device__ inline int swz(int r) {
+  int x;
+  if constexpr (KC) {
+    if constexpr (CPR == 4) x = ((r >> 1) ^ (r >> 3)) & 3;
+    else if constexpr (CPR == 8) x = (r & 7) ^ ((r >> 3) & 1);
+    else x = r & 15;
+  } else if constexpr (!FP8) {
+    x = (((r & 3) << 1) | ((r >> 3) & 1)) << 1;
+  } else {
+    x = ((r & 7) << 1) | ((r >> 5) & 1);
+  }
+  return x & (CPR - 1);
+}
+
+__device__ inline void mma(f32x16& acc, const bf16x8& b, const bf16x8& a) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc, 0, 0, 0);
+}
+__device__ inline void mma(f32x4& acc, const bf16x8& b, const bf16x8& a) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a, acc, 0, 0, 0);
+}
+__device__ inline void mma(f32x16& acc, const i32x8& b, const i32x8& a) {
+  // cbsz = blgp = 0: both operands OCP E4M3; zero scale operands give the unscaled op
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc, 0, 0, 0, 0, 0, 0);
+}
+__device__ inline void mma(f32x4& acc, const i32x8& b, const i32x8& a) {
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, acc, 0, 0, 0, 0, 0, 0);
+}
+
+template <bool FP8> struct FragOf { using T = bf16x8; };
+template <> struct FragOf<true> { using T = i32x8; };
+template <int MT> struct AccOf { using T = f32x16; };
+template <> struct AccOf<16> { using T = f32x4; };
+
+// Fragment of one MFMA operand for lane `lane`: MT rows (M or N index, x0..x0+MT)
+// times KPL consecutive K values starting at kbase + (lane / MT) * KPL.
+//  K-contiguous tile (rows = x, cols = k): one or two ds_read_b128.
+//  M/N-contiguous tile (rows = k, cols = x): transposing reads; within each group of
+//  16 lanes, lane s supplies the address of row (s / (16/E)) and column chunk
+//  (s % (16/E)) * E of an E-row by 16-column block, and lane i receives column i of
+//  all E rows (E = 4 for bf16, 8 for E4M3).
+template <class C, bool KC, int RB>
+__device__ inline typename FragOf<C::FP8>::T load_frag(const lds_char* base, int x0, int kbase,
+                                                        int lane, int sw_on) {
+  using Frag = typename FragOf<C::FP8>::T;
+  constexpr int CPR = RB / 16;
+  Frag f;
+  if constexpr (KC) {
+    const int r = x0 + lane % C::MT;
+    const int k = kbase + (lane / C::MT) * C::KPL;
+    const int c = k * C::ES / 16;
+    const int s = sw_on ? swz<true, C::FP8, CPR>(r) : 0;
+    if constexpr (!C::FP8) {
+      const uint32_t off = r * RB + ((c ^ s) << 4);
+      f = *LDS_PTR(bf16x8, base, off);
+    } else {
+      const uint32_t off0 = r * RB + ((c ^ s) << 4);
+      const uint32_t off1 = r * RB + (((c + 1) ^ s) << 4);
+      i32x4 lo = *LDS_PTR(i32x4, base, off0);
+      i32x4 hi = *LDS_PTR(i32x4, base, off1);
+      f = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  } else {
+    constexpr int E = C::FP8 ? 8 : 4;
+    constexpr int LPR = 16 / E;  // lanes per row inside a 16-lane group
+    const int g = lane >> 4, s = lane & 15;
+    const int coloff = (C::MT == 32) ? 16 * (g & 1) : 0;
+    const int kgrp = (C::MT == 32) ? (g >> 1) : g;
+    const int x = x0 + coloff + (s % LPR) * E;  // first column of this lane's 8 bytes
+    const int xb = x * C::ES;                   // byte column
+    if constexpr (!C::FP8) {
+      u16x4 part[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = kbase + kgrp * C::KPL + h * E + s / LPR;
+        const int sw = sw_on ? swz<false, false, CPR>(k) : 0;
+        const uint32_t off = k * RB + ((((xb >> 4) ^ sw) << 4) | (xb & 15));
+        s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, base, off));
+        part[h] = __builtin_bit_cast(u16x4, v);
+      }
+      u16x4 lo = part[0], hi = part[1];
+      typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+      u16x8 all = (u16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      f = __builtin_bit_cast(bf16x8, all);
+    } else {
+      i32x2 part[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int k = kbase + kgrp * C::KPL + h * E + s / LPR;
+        const int sw = sw_on ? swz<false, true, CPR>(k) : 0;
+        const uint32_t off = k * RB + ((((xb >> 4) ^ sw) << 4) | (xb & 15));
+        part[h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, base, off));
+      }
+      f = (i32x8){part[0][0], part[0][1], part[1][0], part[1][1],
+                  part[2][0], part[2][1], part[3][0], part[3][1]};
+    }
+  }
+  return f;
+}
+
+__device__ inline uint16_t f32_to_bf16_bits(float v) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+}
+__device__ inline float bf16_bits_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+// Compile-time loop: f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>).
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// Instruction-scheduling hints for one K step: NMF MFMAs, each followed by its even
+// share of NDS LDS reads, NVM global loads and NDW LDS writes (the groups are
+// matched in order by the scheduler within the current basic block).
+template <int NMF, int NDS, int NVM, int NDW, int I = 0>
+__device__ __forceinline__ void interleave() {
+  if constexpr (I < NMF) {
+    constexpr int ds = NDS * (I + 1) / NMF - NDS * I / NMF;
+    constexpr int vm = NVM * (I + 1) / NMF - NVM * I / NMF;
+    constexpr int dw = NDW * (I + 1) / NMF - NDW * I / NMF;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);  // DS read
+    if constexpr (vm > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm, 0);  // VMEM read
+    if constexpr (dw > 0) __builtin_amdgcn_sched_group_barrier(0x200, dw, 0);  // DS write
+    interleave<NMF, NDS, NVM, NDW, I + 1>();
+  }
+}
+
+// 16 E4M3 values -> 16 bf16 values (exact: every E4M3 number, subnormals included, is
+// a bf16 number) with the gfx950 packed conversion at unit scale.
+__device__ inline void widen_e4m3(const i32x4& v, i32x4& lo, i32x4& hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  int w[8];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    w[2 * d] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[d], 1.0f, false));
+    w[2 * d + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[d], 1.0f, true));
+  }
+  lo = (i32x4){w[0], w[1], w[2], w[3]};
+  hi = (i32x4){w[4], w[5], w[6], w[7]};
+}
+
+// Stores one global chunk into LDS at byte offset `off` (its first LDS chunk).  A
+// widened chunk fills two logically adjacent LDS chunks; under the XOR swizzle their
+// physical positions differ only in bit 4 of the offset.
+template <class C>
+__device__ inline void put_chunk(lds_char* sbase, uint32_t off, const i32x4& v) {
+  if constexpr (C::WIDEN == 1) {
+    *LDS_PTR(i32x4, sbase, off) = v;
+  } else {
+    i32x4 lo, hi;
+    widen_e4m3(v, lo, hi);
+    *LDS_PTR(i32x4, sbase, off) = lo;
+    *LDS_PTR(i32x4, sbase, off ^ 16u) = hi;
+  }
+}
+
+// alpha*acc + beta*C_old -> C for one wave's accumulator tile whose first row is
+// row0 and first column col0.  The MFMA ran with the B fragment as first operand, so
+// a lane holds, for row row0 + i*MT + lane%MT, groups of four consecutive columns.
+template <class C>
+__device__ inline void store_tile(const GemmArgs& a, const typename AccOf<C::MT>::T (&acc)[C::FM][C::FN],
+                                  int row0, int col0, int lane) {
+  // ---- epilogue: lane holds rows m = .. + lane % MT, four consecutive columns per group
+  const bool c_f32 = a.c_f32;
+  const float alpha = a.alpha, beta = a.beta;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    const int m = row0 + i * C::MT + lane % C::MT;
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+#pragma unroll
+      for (int q = 0; q < C::ACC / 4; ++q) {
+        const int n = col0 + j * C::MT + (C::MT == 32 ? 8 * q + 4 * (lane / 32) : 4 * (lane / 16));
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = alpha * acc[i][j][4 * q + e];
+        const int64_t base = (int64_t)m * a.ldc + n;
+        if (n + 3 < a.N) {
+          if (c_f32) {
+            float* cp = (float*)a.C + base;
+            if (beta != 0.f) {
+              f32x4 old = *(const f32x4*)cp;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] += beta * old[e];
+            }
+            *(f32x4*)cp = (f32x4){v[0], v[1], v[2], v[3]};
+          } else {
+            uint16_t* cp = (uint16_t*)a.C + base;
+            if (beta != 0.f) {
+              u16x4 old = *(const u16x4*)cp;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] += beta * bf16_bits_to_f32(old[e]);
+            }
+            *(u16x4*)cp = (u16x4){f32_to_bf16_bits(v[0]), f32_to_bf16_bits(v[1]),
+                                  f32_to_bf16_bits(v[2]), f32_to_bf16_bits(v[3])};
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (n + e >= a.N) break;
+            if (c_f32) {
+              float* cp = (float*)a.C + base + e;
+              *cp = v[e] + (beta != 0.f ? beta * *cp : 0.f);
+            } else {
+              uint16_t* cp = (uint16_t*)a.C + base + e;
+              *cp = f32_to_bf16_bits(v[e] + (beta != 0.f ? beta * bf16_bits_to_f32(*cp) : 0.f));
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+}  // namespace dbgemm

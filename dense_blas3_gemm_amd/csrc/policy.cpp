@@ -14,9 +14,9 @@ namespace dbgemm {
 namespace {
 
 const Policy kTable[] = {
-#define DBGEMM_SIMT(name_, eff_) {name_, KIND_SIMT, -1, 64, 64, 16, 1, 1, 0, 1, 1, 0, 1, 0, 256, eff_},
-#define DBGEMM_MFMA(name_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_, eff_) \
-  {name_, KIND_MFMA, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_, (wm_) * (wn_) * 64, eff_},
+#define DBGEMM_SIMT(name_, eff_) {name_, KIND_SIMT, 0, -1, 64, 64, 16, 1, 1, 0, 1, 1, 0, 1, 0, 256, eff_},
+#define DBGEMM_MFMA(name_, pipe_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_, eff_) \
+  {name_, KIND_MFMA, pipe_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_, (wm_) * (wn_) * 64, eff_},
 #include "policies.inc"
 #undef DBGEMM_SIMT
 #undef DBGEMM_MFMA
@@ -28,9 +28,10 @@ constexpr int kCount = sizeof(kTable) / sizeof(kTable[0]);
 int occupancy(const Policy& p) {
   const int es = p.in_mode == 2 ? 1 : 2;  // bytes per element in LDS
   const int lds = p.stages * (p.BM + p.BN) * p.BK * es;
+  const int staging = p.pipe == 0 ? (p.BM + p.BN) * p.BK * (p.in_mode == 0 ? 2 : 1) / (p.WM * p.WN * 64) / 4 : 0;
   int occ_lds = (160 * 1024) / lds;
   const int acc = (p.BM / p.WM) * (p.BN / p.WN) / 64;  // fp32 accumulators per lane
-  const int regs = acc + 128;                            // + fragments, staging, addresses
+  const int regs = acc + 96 + staging;                   // + fragments, addresses, load staging
   const int waves_per_simd = 512 / regs;
   const int wg_waves_per_simd = (p.WM * p.WN + 3) / 4;
   int occ_reg = waves_per_simd / wg_waves_per_simd;

@@ -103,7 +103,7 @@ def test_create_without_device_or_with_one():
 def test_policy_selection_is_shape_driven_and_deterministic():
     q = lambda *a, **k: d.query_policy(*a, A_ptr=A, B_ptr=B, C_ptr=C, **k)
     big = q(4096, 4096, 4096)
-    assert big.startswith("bf16_m256n256") and big == q(4096, 4096, 4096)
+    assert big.startswith("bf16_") and "m256n256" in big and big == q(4096, 4096, 4096)
     assert q(4096, 4096, 4096, dtype=d.E4M3_BF16).startswith("e4m3_")
     # misaligned pointers or strides fall back to the generic kernel
     assert d.query_policy(4096, 4096, 4096, A_ptr=A + 2, B_ptr=B, C_ptr=C) == "simt_generic"
