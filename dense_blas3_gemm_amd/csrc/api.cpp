@@ -246,6 +246,7 @@ gemm_status_t gemm_run(gemm_handle_t h, int transA, int transB, int64_t M, int64
       a.raster_n = pol.raster_n;
       a.xcd = pol.xcd;
       a.swizzle = pol.swizzle;
+      a.krot = pol.krot;
       err = pol.pipe == 1 ? launch_mfma_dma(pol, a, p->stream) : launch_mfma_staged(pol, a, p->stream);
     }
   }

@@ -25,6 +25,7 @@ struct GemmArgs {
   int raster_n;   // 0: groups of `group` tile-rows walked along N; 1: the transpose
   int xcd;        // number of XCDs to remap across (1 disables the remap)
   int swizzle;    // 1: XOR-swizzled LDS layout, 0: plain row-major LDS tiles
+  int krot;       // 1: each XCD starts its K loop at its own eighth of K (see the DMA kernel)
 };
 
 enum PolicyKind { KIND_SIMT = 0, KIND_MFMA = 1, KIND_SCALE = 2 };
@@ -40,6 +41,7 @@ struct Policy {
   int MT;          // MFMA block edge (32 or 16)
   int stages;      // LDS stages
   int group, raster_n, xcd, swizzle;
+  int krot;        // K-loop rotation per XCD (direct-to-LDS kernels only)
   int threads;
   float efficiency;  // relative per-CU throughput used by the wave-time model
 };

@@ -139,9 +139,19 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(GemmArgs a) {
   // memory.
   const uint32_t a_blk = (uint32_t)(wave * D::A_IPW) * 1024u;
   const uint32_t b_blk = C::A_BYTES + (uint32_t)(wave * D::B_IPW) * 1024u;
-  // Load instruction q (A blocks first, then B) of K tile kt into slot sb.
-  auto issue_one = [&](const lds_char* sb, int kt, auto qc) {
+  const int nk = (a.K + C::BK - 1) / C::BK;
+  // K-loop rotation: with krot set, the workgroups of XCD x (ids x, x+8, ...) walk K
+  // starting at tile x*nk/8 and wrap around, so the eight XCDs stream different parts
+  // of A and B at any moment instead of the same power-of-two-strided addresses.  The
+  // workgroups of one XCD stay in step and keep sharing its L2.  (This changes only
+  // the order of the K tiles in each sum.)
+  const int krot = a.krot ? (int)((blockIdx.x % 8) * nk / 8) : 0;
+  // Load instruction q (A blocks first, then B) of logical K tile u into slot sb;
+  // logical tiles past the end stay past the end (zeros).
+  auto issue_one = [&](const lds_char* sb, int u, auto qc) {
     constexpr int q = decltype(qc)::value;
+    int kt = u;
+    if (krot != 0 && u < nk) kt = u + krot < nk ? u + krot : u + krot - nk;
     const int k0 = kt * C::BK;
     const uint32_t base = (uint32_t)(uintptr_t)sb;
     if constexpr (q < D::A_IPW) {
@@ -162,7 +172,6 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = Acc{};
 
-  const int nk = (a.K + C::BK - 1) / C::BK;
   const int xa0 = wm * C::WTM, xb0 = wn * C::WTN;
 
   Frag fa[2][C::FM], fb[2][C::FN];

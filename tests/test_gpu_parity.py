@@ -19,13 +19,19 @@ pytestmark = pytest.mark.gpu
 TRANS = [(0, 0), (0, 1), (1, 0), (1, 1)]
 BF16_DMA_POLICIES = ["bf16_dma_m256n256k32_w2x4_mt32_s4", "bf16_dma_m256n256k32_w2x2_mt32_s4",
                      "bf16_dma_m256n256k64_w2x4_mt32_s2", "bf16_dma_m128n128k64_w2x2_mt32_s3",
-                     "bf16_dma_m256n128k32_w2x2_mt32_s4", "bf16_dma_m128n256k32_w2x2_mt32_s4"]
+                     "bf16_dma_m256n128k32_w2x2_mt32_s4", "bf16_dma_m128n256k32_w2x2_mt32_s4",
+                     "bf16_dma_m256n256k64_w2x4_mt32_s2_krot", "bf16_dma_m256n256k64_w2x2_mt32_s2",
+                     "bf16_dma_m256n256k64_w2x2_mt32_s2_krot", "bf16_dma_m256n256k32_w2x2_mt32_s4_krot",
+                     "bf16_dma_m256n256k64_w2x4_mt16_s2", "bf16_dma_m128n256k64_w2x4_mt16_s3",
+                     "bf16_dma_m256n128k64_w4x2_mt16_s3", "bf16_dma_m128n128k64_w2x2_mt16_s4",
+                     "bf16_dma_m128n128k64_w2x4_mt16_s4", "bf16_dma_m64n64k64_w2x2_mt16_s4"]
 BF16_POLICIES = BF16_DMA_POLICIES + ["bf16_m256n256k64_w2x2_mt32_s2", "bf16_m256n256k64_w2x4_mt32_s2",
                  "bf16_m256n128k64_w2x2_mt32_s2", "bf16_m128n256k64_w2x2_mt32_s2",
                  "bf16_m128n128k64_w2x2_mt32_s2", "bf16_m128n128k64_w2x2_mt16_s2",
                  "bf16_m64n64k64_w2x2_mt16_s2", "bf16_m256n256k64_w2x2_mt32_s2_noswz",
                  "bf16_m256n256k64_w2x2_mt32_s2_noxcd"]
 FP8_POLICIES = ["e4m3_m256n256k64_w2x2_mt32_s2", "e4m3_m256n256k64_w2x4_mt32_s2",
+                "e4m3_m256n256k64_w2x4_mt16_s2", "e4m3_m128n128k64_w2x4_mt16_s2",
                 "e4m3_m128n128k64_w2x2_mt32_s2", "e4m3_m64n64k64_w2x2_mt16_s2"]
 FP8_NATIVE_POLICIES = ["e4m3native_dma_m256n256k128_w2x4_mt32_s2", "e4m3native_m256n256k128_w2x2_mt32_s2", "e4m3native_m256n256k128_w2x4_mt32_s2",
                        "e4m3native_m128n128k128_w2x2_mt32_s2", "e4m3native_m64n64k128_w2x2_mt16_s2"]
@@ -219,7 +225,7 @@ def test_data_movement_variants_bitwise_equal(gpu):
     outs = [run_gpu(gpu, p, data, policy=pol) for pol in
             ["bf16_m256n256k64_w2x2_mt32_s2", "bf16_m256n256k64_w2x2_mt32_s2_noswz",
              "bf16_m256n256k64_w2x2_mt32_s2_noxcd", "bf16_m256n256k64_w2x4_mt32_s2",
-             "bf16_m128n128k64_w2x2_mt32_s2"] + BF16_DMA_POLICIES]
+             "bf16_m128n128k64_w2x2_mt32_s2"] + [p for p in BF16_DMA_POLICIES if "krot" not in p and "mt16" not in p]]
     for o in outs[1:]:
         assert np.array_equal(outs[0], o)
 
