@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <unordered_set>
@@ -16,11 +17,17 @@ namespace {
 
 constexpr const char* kVersion = "dbgemm 0.1.0 policy-table 1";
 
+// Split-K workspace for the fp32 partial tiles, allocated once per handle at creation.
+constexpr size_t kWorkspaceBytes = (size_t)64 << 20;
+
 struct Handle {
   int device = 0;
   int cu_count = 256;
   hipStream_t stream = nullptr;
-  int forced = -1;  // policy index, -1 = shape-driven
+  int forced = -1;         // policy index, -1 = shape-driven
+  int forced_splits = 1;   // split-K factor of a forced policy
+  void* ws = nullptr;      // kWorkspaceBytes on `device`, or null (split-K off)
+  int64_t ws_floats() const { return ws ? (int64_t)(kWorkspaceBytes / sizeof(float)) : 0; }
 };
 
 // Live handles; a destroyed (or never created) handle is rejected instead of used.
@@ -128,6 +135,14 @@ gemm_status_t gemm_create(gemm_handle_t* h, int device) {
   Handle* p = new Handle();
   p->device = device;
   p->cu_count = cus > 0 ? cus : 256;
+  // The workspace is optional: without it every call runs unsplit.
+  int prev = -1;
+  if (hipGetDevice(&prev) == hipSuccess && hipSetDevice(device) == hipSuccess) {
+    void* ws = nullptr;
+    if (hipMalloc(&ws, kWorkspaceBytes) == hipSuccess) p->ws = ws;
+    (void)hipSetDevice(prev);
+  }
+  (void)hipGetLastError();
   {
     std::lock_guard<std::mutex> lk(g_mu);
     g_live.insert(p);
@@ -142,7 +157,16 @@ gemm_status_t gemm_destroy(gemm_handle_t h) {
     std::lock_guard<std::mutex> lk(g_mu);
     if (g_live.erase(h) == 0) return GEMM_STATUS_NOT_INITIALIZED;
   }
-  delete reinterpret_cast<Handle*>(h);
+  Handle* p = reinterpret_cast<Handle*>(h);
+  if (p->ws) {
+    int prev = -1;
+    if (hipGetDevice(&prev) == hipSuccess && hipSetDevice(p->device) == hipSuccess) {
+      (void)hipFree(p->ws);  // waits for the device's work in flight
+      (void)hipSetDevice(prev);
+    }
+    (void)hipGetLastError();
+  }
+  delete p;
   return GEMM_STATUS_SUCCESS;
 }
 
@@ -157,11 +181,28 @@ gemm_status_t gemm_set_policy(gemm_handle_t h, const char* name) {
   Handle* p = reinterpret_cast<Handle*>(h);
   if (!name || std::strcmp(name, "auto") == 0) {
     p->forced = -1;
+    p->forced_splits = 1;
     return GEMM_STATUS_SUCCESS;
   }
-  const int i = policy_find(name);
+  // "<policy>" or "<policy>+sk<S>" with S in {2, 4, 8, 16}
+  char base[128];
+  int sp = 1;
+  const char* plus = std::strstr(name, "+sk");
+  const size_t n = plus ? (size_t)(plus - name) : std::strlen(name);
+  if (n == 0 || n >= sizeof(base)) return GEMM_STATUS_INVALID_VALUE;
+  std::memcpy(base, name, n);
+  base[n] = 0;
+  if (plus) {
+    char* end = nullptr;
+    const long v = std::strtol(plus + 3, &end, 10);
+    if (!end || *end != 0 || (v != 2 && v != 4 && v != 8 && v != 16)) return GEMM_STATUS_INVALID_VALUE;
+    sp = (int)v;
+  }
+  const int i = policy_find(base);
   if (i < 0) return GEMM_STATUS_INVALID_VALUE;
+  if (sp > 1 && policy_at(i).pipe != 1) return GEMM_STATUS_INVALID_VALUE;  // direct-to-LDS only
   p->forced = i;
+  p->forced_splits = sp;
   return GEMM_STATUS_SUCCESS;
 }
 
@@ -175,14 +216,21 @@ gemm_status_t gemm_query_policy(gemm_handle_t h, int transA, int transB, int64_t
   if (M < 0 || N < 0 || K < 0) return GEMM_STATUS_INVALID_VALUE;
   const Handle* p = reinterpret_cast<const Handle*>(h);
   const Problem pr = make_problem(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, dtype);
-  int idx;
+  int idx, sp = 1;
   if (p && p->forced >= 0) {
     idx = p->forced;
-    if (!policy_serves(policy_at(idx), pr)) return GEMM_STATUS_NOT_SUPPORTED;
+    sp = p->forced_splits;
+    if (!policy_serves(policy_at(idx), pr) || !split_allowed(policy_at(idx), pr, sp, p->ws_floats()))
+      return GEMM_STATUS_NOT_SUPPORTED;
   } else {
-    idx = policy_select(pr, p ? p->cu_count : 256);
+    // without a handle, the workspace a new handle would have
+    const int64_t wsf = p ? p->ws_floats() : (int64_t)(kWorkspaceBytes / sizeof(float));
+    idx = policy_select(pr, p ? p->cu_count : 256, wsf, &sp);
   }
-  std::snprintf(name, len, "%s", policy_at(idx).name);
+  if (sp > 1)
+    std::snprintf(name, len, "%s+sk%d", policy_at(idx).name, sp);
+  else
+    std::snprintf(name, len, "%s", policy_at(idx).name);
   return GEMM_STATUS_SUCCESS;
 }
 
@@ -212,6 +260,7 @@ gemm_status_t gemm_run(gemm_handle_t h, int transA, int transB, int64_t M, int64
   a.in_fp8 = in_bytes(dtype) == 1;
   a.transA = transA;
   a.transB = transB;
+  a.splits = 1;
 
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess) return GEMM_STATUS_INTERNAL;
@@ -222,15 +271,16 @@ gemm_status_t gemm_run(gemm_handle_t h, int transA, int transB, int64_t M, int64
     err = launch_scale(a, p->stream);
   } else {
     const Problem pr = make_problem(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, dtype);
-    int idx;
+    int idx, sp = 1;
     if (p->forced >= 0) {
       idx = p->forced;
-      if (!policy_serves(policy_at(idx), pr)) {
+      sp = p->forced_splits;
+      if (!policy_serves(policy_at(idx), pr) || !split_allowed(policy_at(idx), pr, sp, p->ws_floats())) {
         if (cur != p->device) (void)hipSetDevice(cur);
         return GEMM_STATUS_NOT_SUPPORTED;
       }
     } else {
-      idx = policy_select(pr, p->cu_count);
+      idx = policy_select(pr, p->cu_count, p->ws_floats(), &sp);
     }
     const Policy& pol = policy_at(idx);
     if (pol.kind == KIND_SIMT) {
@@ -247,6 +297,9 @@ gemm_status_t gemm_run(gemm_handle_t h, int transA, int transB, int64_t M, int64
       a.xcd = pol.xcd;
       a.swizzle = pol.swizzle;
       a.krot = pol.krot;
+      a.splits = sp;
+      a.kt_per_split = (int)split_kt(pol, K, sp);
+      if (sp > 1) a.ws = (float*)p->ws;
       err = pol.pipe == 1 ? launch_mfma_dma(pol, a, p->stream) : launch_mfma_staged(pol, a, p->stream);
     }
   }

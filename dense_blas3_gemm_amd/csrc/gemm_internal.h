@@ -26,6 +26,14 @@ struct GemmArgs {
   int xcd;        // number of XCDs to remap across (1 disables the remap)
   int swizzle;    // 1: XOR-swizzled LDS layout, 0: plain row-major LDS tiles
   int krot;       // 1: each XCD starts its K loop at its own eighth of K (see the DMA kernel)
+  // Split-K (direct-to-LDS kernels): `splits` workgroups share each output tile, split
+  // s summing K tiles [s*kt_per_split, (s+1)*kt_per_split).  Each writes its fp32
+  // partial tile to `ws` (slot tile*splits + s, tile = tm*tiles_n + tn); a second
+  // kernel adds the partials in split order and runs the epilogue.  splits == 1: no
+  // workspace use.
+  int splits;
+  int kt_per_split;
+  float* ws;
 };
 
 enum PolicyKind { KIND_SIMT = 0, KIND_MFMA = 1, KIND_SCALE = 2 };
@@ -63,8 +71,14 @@ struct Problem {
   int in_fp8, c_f32;
   bool fast_ok;  // alignment / divisibility allow the MFMA kernels
 };
-// Shape-driven selection; returns an index into the table.
-int policy_select(const Problem& pr, int cu_count);
+// Shape-driven selection; returns an index into the table and, in *splits, the
+// split-K factor (1 unless a workspace of ws_floats fp32 values allows more).
+int policy_select(const Problem& pr, int cu_count, int64_t ws_floats, int* splits);
+// fp32 partials a split-K call of policy p with `splits` needs, K tiles per split
+// (0: that split is not allowed), and whether the split fits a workspace.
+int64_t split_ws_floats(const Policy& p, const Problem& pr, int splits);
+int64_t split_kt(const Policy& p, int64_t K, int splits);
+bool split_allowed(const Policy& p, const Problem& pr, int splits, int64_t ws_floats);
 bool policy_serves(const Policy& p, const Problem& pr);
 
 }  // namespace dbgemm

@@ -45,7 +45,8 @@ __global__ __launch_bounds__(C::THREADS) void gemm_mfma_kernel(GemmArgs a) {
   using Acc = typename AccOf<C::MT>::T;
 
   int tm, tn;
-  tile_of(blockIdx.x, a, tm, tn);
+  int split_unused;  // the register-staged kernels run with splits == 1
+  tile_of(blockIdx.x, a, tm, tn, split_unused);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;

@@ -82,8 +82,8 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(GemmArgs a) {
   using Frag = typename FragOf<C::FP8>::T;
   using Acc = typename AccOf<C::MT>::T;
 
-  int tm, tn;
-  tile_of(blockIdx.x, a, tm, tn);
+  int tm, tn, split;
+  tile_of(blockIdx.x, a, tm, tn, split);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
@@ -139,18 +139,21 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(GemmArgs a) {
   // memory.
   const uint32_t a_blk = (uint32_t)(wave * D::A_IPW) * 1024u;
   const uint32_t b_blk = C::A_BYTES + (uint32_t)(wave * D::B_IPW) * 1024u;
-  const int nk = (a.K + C::BK - 1) / C::BK;
+  // K tiles of this workgroup: [kbeg, kbeg + nk) of the nk_all tiles of K
+  const int nk_all = (a.K + C::BK - 1) / C::BK;
+  const int kbeg = split * a.kt_per_split;
+  const int nk = a.splits > 1 ? min(nk_all - kbeg, a.kt_per_split) : nk_all;
   // K-loop rotation: with krot set, the workgroups of XCD x (ids x, x+8, ...) walk K
   // starting at tile x*nk/8 and wrap around, so the eight XCDs stream different parts
   // of A and B at any moment instead of the same power-of-two-strided addresses.  The
   // workgroups of one XCD stay in step and keep sharing its L2.  (This changes only
   // the order of the K tiles in each sum.)
-  const int krot = a.krot ? (int)((blockIdx.x % 8) * nk / 8) : 0;
+  const int krot = a.krot && a.splits == 1 ? (int)((blockIdx.x % 8) * nk / 8) : 0;
   // Load instruction q (A blocks first, then B) of logical K tile u into slot sb;
   // logical tiles past the end stay past the end (zeros).
   auto issue_one = [&](const lds_char* sb, int u, auto qc) {
     constexpr int q = decltype(qc)::value;
-    int kt = u;
+    int kt = u < nk ? kbeg + u : nk_all;  // past this workgroup's range: past K (zeros)
     if (krot != 0 && u < nk) kt = u + krot < nk ? u + krot : u + krot - nk;
     const int k0 = kt * C::BK;
     const uint32_t base = (uint32_t)(uintptr_t)sb;
@@ -254,13 +257,57 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(GemmArgs a) {
   // drain the loads of the tiles past the end before the workgroup's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+  if (a.splits > 1) {  // split-K: this split's fp32 partial, summed by split_reduce_kernel
+    const int tile = tm * a.tiles_n + tn;
+    store_partial<C>(a.ws + ((size_t)tile * a.splits + split) * (C::BM * C::BN), acc, t);
+    return;
+  }
   store_tile<C>(a, acc, m0 + xa0, n0 + xb0, lane);
+}
+
+// Split-K, second launch on the same stream: C <- alpha * (P_0 + ... + P_{S-1}) +
+// beta * C with the partials added in split order, so the result does not depend on
+// which split finished first.  Workgroup (tile, c) handles float4 groups
+// [c*CH, (c+1)*CH) of every thread of the tile's partials; the kernel boundary
+// makes the first launch's partials visible, whichever XCD wrote them.
+template <class C>
+struct Reduce {
+  static constexpr int NP = C::FM * C::FN * C::ACC / 4;  // float4 groups per thread
+  static constexpr int CH = NP < 2 ? NP : 2;
+  static constexpr int CHUNKS = NP / CH;
+  static_assert(NP % CH == 0, "whole chunks");
+};
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void split_reduce_kernel(GemmArgs a) {
+  using Rd = Reduce<C>;
+  const int tile = blockIdx.x / Rd::CHUNKS, c0 = (blockIdx.x % Rd::CHUNKS) * Rd::CH;
+  const int tm = tile / a.tiles_n, tn = tile % a.tiles_n;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const f32x4* src = (const f32x4*)(a.ws + (size_t)tile * a.splits * (C::BM * C::BN));
+  const size_t stride = (size_t)Rd::NP * C::THREADS;  // float4s per partial
+  f32x4 v[Rd::CH];
+#pragma unroll
+  for (int c = 0; c < Rd::CH; ++c) v[c] = src[(c0 + c) * C::THREADS + t];
+  for (int s = 1; s < a.splits; ++s) {
+#pragma unroll
+    for (int c = 0; c < Rd::CH; ++c) v[c] += src[s * stride + (c0 + c) * C::THREADS + t];
+  }
+#pragma unroll
+  for (int c = 0; c < Rd::CH; ++c)
+    store_group<C>(a, v[c], c0 + c, tm * C::BM + wm * C::WTM, tn * C::BN + wn * C::WTN, lane);
 }
 
 template <class C>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   const int ntiles = a.tiles_m * a.tiles_n;
-  hipLaunchKernelGGL(gemm_dma_kernel<C>, dim3(ntiles), dim3(C::THREADS), 0, s, a);
+  hipLaunchKernelGGL(gemm_dma_kernel<C>, dim3(ntiles * a.splits), dim3(C::THREADS), 0, s, a);
+  if (a.splits > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(split_reduce_kernel<C>, dim3(ntiles * Reduce<C>::CHUNKS), dim3(C::THREADS), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -34,14 +34,18 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 // the remap gives each XCD one contiguous run of the raster order, which keeps the
 // A and B panels that neighbouring tiles share inside one XCD's L2.  Then a grouped
 // raster: `group` tile-rows are walked column by column (or the transpose).  Both
-// maps are bijections, so every tile is computed exactly once.
-__device__ inline void tile_of(int bid, const GemmArgs& a, int& tm, int& tn) {
-  const int ntiles = a.tiles_m * a.tiles_n;
+// maps are bijections, so every tile is computed exactly once.  With split-K the ids
+// cover tiles x splits; the splits of one tile are neighbours in the remapped order
+// (so they run on one XCD) and `split` is the id's position among them.
+__device__ inline void tile_of(int bid, const GemmArgs& a, int& tm, int& tn, int& split) {
+  const int total = a.tiles_m * a.tiles_n * a.splits;
   int L = bid;
   if (a.xcd > 1) {
-    const int q = ntiles / a.xcd;
+    const int q = total / a.xcd;
     if (bid < q * a.xcd) L = (bid % a.xcd) * q + bid / a.xcd;
   }
+  split = L % a.splits;
+  L /= a.splits;
   const int major = a.raster_n ? a.tiles_m : a.tiles_n;  // tiles along the walk
   const int minor = a.raster_n ? a.tiles_n : a.tiles_m;  // grouped dimension
   const int width = a.group * major;
@@ -274,63 +278,85 @@ __device__ inline void put_chunk(lds_char* sbase, uint32_t off, const i32x4& v) 
   }
 }
 
+// Epilogue of one group of four accumulator values: acc float4 number p of this lane
+// (block (i, j), quarter q) holds C[m][n .. n+3]; C <- alpha*v + beta*C_old, rounded
+// to C's type.  store_tile applies it to every group.
+template <class C>
+__device__ inline void store_group(const GemmArgs& a, f32x4 v, int p, int row0, int col0, int lane) {
+  const int q = p % (C::ACC / 4), j = (p / (C::ACC / 4)) % C::FN, i = p / (C::ACC / 4) / C::FN;
+  const int m = row0 + i * C::MT + lane % C::MT;
+  const int n = col0 + j * C::MT + (C::MT == 32 ? 8 * q + 4 * (lane / 32) : 4 * (lane / 16));
+  if (m >= a.M) return;
+  const float alpha = a.alpha, beta = a.beta;
+  float w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = alpha * v[e];
+  const int64_t base = (int64_t)m * a.ldc + n;
+  if (n + 3 < a.N) {
+    if (a.c_f32) {
+      float* cp = (float*)a.C + base;
+      if (beta != 0.f) {
+        f32x4 old = *(const f32x4*)cp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] += beta * old[e];
+      }
+      *(f32x4*)cp = (f32x4){w[0], w[1], w[2], w[3]};
+    } else {
+      uint16_t* cp = (uint16_t*)a.C + base;
+      if (beta != 0.f) {
+        u16x4 old = *(const u16x4*)cp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] += beta * bf16_bits_to_f32(old[e]);
+      }
+      *(u16x4*)cp = (u16x4){f32_to_bf16_bits(w[0]), f32_to_bf16_bits(w[1]), f32_to_bf16_bits(w[2]),
+                            f32_to_bf16_bits(w[3])};
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (n + e >= a.N) break;
+      if (a.c_f32) {
+        float* cp = (float*)a.C + base + e;
+        *cp = w[e] + (beta != 0.f ? beta * *cp : 0.f);
+      } else {
+        uint16_t* cp = (uint16_t*)a.C + base + e;
+        *cp = f32_to_bf16_bits(w[e] + (beta != 0.f ? beta * bf16_bits_to_f32(*cp) : 0.f));
+      }
+    }
+  }
+}
+
 // alpha*acc + beta*C_old -> C for one wave's accumulator tile whose first row is
 // row0 and first column col0.  The MFMA ran with the B fragment as first operand, so
 // a lane holds, for row row0 + i*MT + lane%MT, groups of four consecutive columns.
 template <class C>
 __device__ inline void store_tile(const GemmArgs& a, const typename AccOf<C::MT>::T (&acc)[C::FM][C::FN],
                                   int row0, int col0, int lane) {
-  // ---- epilogue: lane holds rows m = .. + lane % MT, four consecutive columns per group
-  const bool c_f32 = a.c_f32;
-  const float alpha = a.alpha, beta = a.beta;
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-    const int m = row0 + i * C::MT + lane % C::MT;
-    if (m >= a.M) continue;
+  for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
+    for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-      for (int q = 0; q < C::ACC / 4; ++q) {
-        const int n = col0 + j * C::MT + (C::MT == 32 ? 8 * q + 4 * (lane / 32) : 4 * (lane / 16));
-        float v[4];
+      for (int q = 0; q < C::ACC / 4; ++q)
+        store_group<C>(a,
+                       (f32x4){acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]},
+                       (i * C::FN + j) * (C::ACC / 4) + q, row0, col0, lane);
+}
+
+// Split-K partial tiles.  A partial is kept in register order: float4 number p of
+// thread t sits at p * THREADS + t, so both the write and the read-back are fully
+// coalesced and need no index math beyond the thread id.
+template <class C>
+__device__ inline void store_partial(float* blk, const typename AccOf<C::MT>::T (&acc)[C::FM][C::FN], int t) {
+  f32x4* dst = (f32x4*)blk;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = alpha * acc[i][j][4 * q + e];
-        const int64_t base = (int64_t)m * a.ldc + n;
-        if (n + 3 < a.N) {
-          if (c_f32) {
-            float* cp = (float*)a.C + base;
-            if (beta != 0.f) {
-              f32x4 old = *(const f32x4*)cp;
+  for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] += beta * old[e];
-            }
-            *(f32x4*)cp = (f32x4){v[0], v[1], v[2], v[3]};
-          } else {
-            uint16_t* cp = (uint16_t*)a.C + base;
-            if (beta != 0.f) {
-              u16x4 old = *(const u16x4*)cp;
+    for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] += beta * bf16_bits_to_f32(old[e]);
-            }
-            *(u16x4*)cp = (u16x4){f32_to_bf16_bits(v[0]), f32_to_bf16_bits(v[1]),
-                                  f32_to_bf16_bits(v[2]), f32_to_bf16_bits(v[3])};
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (n + e >= a.N) break;
-            if (c_f32) {
-              float* cp = (float*)a.C + base + e;
-              *cp = v[e] + (beta != 0.f ? beta * *cp : 0.f);
-            } else {
-              uint16_t* cp = (uint16_t*)a.C + base + e;
-              *cp = f32_to_bf16_bits(v[e] + (beta != 0.f ? beta * bf16_bits_to_f32(*cp) : 0.f));
-            }
-          }
-        }
-      }
-    }
-  }
+      for (int q = 0; q < C::ACC / 4; ++q)
+        dst[((i * C::FN + j) * (C::ACC / 4) + q) * C::THREADS + t] =
+            (f32x4){acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
 }
 
 }  // namespace

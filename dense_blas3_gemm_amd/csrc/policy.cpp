@@ -60,25 +60,61 @@ bool policy_serves(const Policy& p, const Problem& pr) {
   return pr.fast_ok && (p.in_mode != 0) == (pr.in_fp8 != 0);
 }
 
-int policy_select(const Problem& pr, int cu_count) {
+int64_t split_ws_floats(const Policy& p, const Problem& pr, int splits) {
+  const int64_t tiles = ((pr.M + p.BM - 1) / p.BM) * ((pr.N + p.BN - 1) / p.BN);
+  return tiles * splits * p.BM * p.BN;
+}
+
+// K tiles per split for `splits` ways, or 0 when that split is not a distinct,
+// useful one (every split gets at least two K tiles and the last is not empty).
+int64_t split_kt(const Policy& p, int64_t K, int splits) {
+  const int64_t nk = (K + p.BK - 1) / p.BK;
+  if (splits == 1) return nk;
+  const int64_t per = (nk + splits - 1) / splits;
+  if (per < 2 || (nk + per - 1) / per != splits) return 0;
+  return per;
+}
+
+bool split_allowed(const Policy& p, const Problem& pr, int splits, int64_t ws_floats) {
+  if (splits == 1) return true;
+  if (p.pipe != 1 || split_kt(p, pr.K, splits) == 0) return false;  // direct-to-LDS kernels
+  return split_ws_floats(p, pr, splits) <= ws_floats;
+}
+
+int policy_select(const Problem& pr, int cu_count, int64_t ws_floats, int* splits) {
   if (cu_count <= 0) cu_count = 256;
   int best = policy_find("simt_generic");
+  *splits = 1;
   if (!pr.fast_ok) return best;
   double best_t = 0.0;
   bool have = false;
   const double K0 = 256.0;  // prologue + epilogue cost of a tile, in K-equivalents
+  // Split-K adds a reduction launch: about 1.5 us plus 0.75 us per split on MI355X.
+  // The model's unit is BM*BN*K/efficiency per CU; one us is about 2e6 of them (a
+  // 64 x 64 tile at efficiency 0.5 advances about 265 K per us).
+  const double kUnitsPerUs = 2.0e6;
   for (int i = 0; i < kCount; ++i) {
     const Policy& p = kTable[i];
     if (p.kind != KIND_MFMA || p.efficiency <= 0.f || !policy_serves(p, pr)) continue;
     const int occ = occupancy(p);
     const double tiles = (double)((pr.M + p.BM - 1) / p.BM) * (double)((pr.N + p.BN - 1) / p.BN);
     const double slots = (double)cu_count * occ;
-    const double rounds = (double)(int64_t)((tiles + slots - 1) / slots);
-    const double t = rounds * occ * (double)p.BM * p.BN * ((double)pr.K + K0) / p.efficiency;
-    if (!have || t < best_t * 0.999) {
-      best = i;
-      best_t = t;
-      have = true;
+    for (int sp = 1; sp <= 16; sp *= 2) {
+      if (!split_allowed(p, pr, sp, ws_floats)) continue;
+      const double wgs = tiles * sp;
+      const double k_eff = (double)split_kt(p, pr.K, sp) * p.BK;
+      const double rounds = (double)(int64_t)((wgs + slots - 1) / slots);
+      // workgroups sharing a CU at a time: the occupancy, or fewer on a small grid
+      const double per_cu = (double)(int64_t)((wgs + cu_count - 1) / cu_count);
+      const double conc = per_cu < occ ? per_cu : occ;
+      double t = rounds * conc * (double)p.BM * p.BN * (k_eff + K0) / p.efficiency;
+      if (sp > 1) t += (1.5 + 0.75 * sp) * kUnitsPerUs;
+      if (!have || t < best_t * 0.999) {
+        best = i;
+        best_t = t;
+        *splits = sp;
+        have = true;
+      }
     }
   }
   return best;

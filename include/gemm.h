@@ -26,10 +26,19 @@
  * E4M3 runs with unit scale: any scaling is the caller's (alpha may carry it).
  *
  * Memory and ownership.  A, B and C are device pointers owned by the caller.  The
- * handle owns only host-side state.  gemm_run never allocates, never synchronises
- * and returns once the kernel is enqueued on the handle's stream; faults during
- * execution surface at the caller's next synchronisation.  A handle must be used
- * from one host thread at a time.
+ * handle owns its host-side state and one 64 MiB device workspace for split-K
+ * (allocated by gemm_create, freed by gemm_destroy).  gemm_run never allocates,
+ * never synchronises and returns once the kernel is enqueued on the handle's stream;
+ * faults during execution surface at the caller's next synchronisation.  A handle
+ * must be used from one host thread at a time, and its calls must not overlap on
+ * the device: calls on one stream are ordered, but two streams must not run calls
+ * of the same handle concurrently (they would share the workspace).
+ *
+ * Split-K.  When the output tiles alone would leave CUs idle (small M x N, long K),
+ * the policy may split each tile's K range over 2 to 16 workgroups.  Each writes its
+ * fp32 partial to the workspace and a second kernel on the same stream adds the
+ * partials in split order and applies alpha and beta, so results are deterministic
+ * (bitwise the same run to run) but rounded differently from the unsplit sum.
  *
  * Errors.  Arguments are checked before anything is launched; on any error status
  * nothing is launched and nothing is written.
@@ -74,12 +83,14 @@ typedef enum {
   GEMM_STATUS_INTERNAL = 5
 } gemm_status_t;
 
-/* Creates a handle bound to HIP device `device`; reads its CU count and builds the
- * tile-policy table.  The handle starts on the default stream (NULL).  On error
- * *h is set to NULL.  Allocates host memory only. */
+/* Creates a handle bound to HIP device `device`; reads its CU count, builds the
+ * tile-policy table and allocates the split-K workspace on that device (if that
+ * allocation fails the handle still works, without split-K).  The handle starts on
+ * the default stream (NULL).  On error *h is set to NULL. */
 gemm_status_t gemm_create(gemm_handle_t* h, int device);
 
-/* Releases the handle.  Work already enqueued is unaffected.  NULL is accepted. */
+/* Releases the handle and its workspace (hipFree waits for the device's work in
+ * flight, so enqueued calls finish first).  NULL is accepted. */
 gemm_status_t gemm_destroy(gemm_handle_t h);
 
 /* Binds the hipStream_t (passed as void*) that later gemm_run calls enqueue on.
@@ -100,18 +111,22 @@ gemm_status_t gemm_check_args(int transA, int transB, int64_t M, int64_t N, int6
                               int64_t ldb, float beta, const void* C, int64_t ldc, int dtype);
 
 /* Writes the name of the policy gemm_run would use for these arguments into
- * name[len] (NUL-terminated, truncated to fit).  The pointers are only inspected
- * for alignment.  h may be NULL: then a 256-CU device and no forced policy are
- * assumed.  Pure host code. */
+ * name[len] (NUL-terminated, truncated to fit), with "+sk<S>" appended when the call
+ * is split S ways along K.  The pointers are only inspected for alignment.  h may be
+ * NULL: then a 256-CU device with a workspace and no forced policy are assumed.
+ * Pure host code. */
 gemm_status_t gemm_query_policy(gemm_handle_t h, int transA, int transB, int64_t M, int64_t N,
                                 int64_t K, const void* A, int64_t lda, const void* B,
                                 int64_t ldb, const void* C, int64_t ldc, int dtype, char* name,
                                 size_t len);
 
 /* Forces the named policy for later gemm_run calls on this handle (for ablations and
- * invariance checks); NULL or "auto" restores the shape-driven choice.  A forced
- * policy that cannot serve a call (dtype, alignment) returns NOT_SUPPORTED from
- * gemm_run.  Unknown names return INVALID_VALUE. */
+ * invariance checks); NULL or "auto" restores the shape-driven choice.  The name is a
+ * table entry, optionally followed by "+sk<S>" (S = 2, 4, 8 or 16; direct-to-LDS
+ * policies only) to force split-K.  A forced policy that cannot serve a call (dtype,
+ * alignment, a split that leaves a split fewer than two K tiles or does not fit the
+ * workspace) returns NOT_SUPPORTED from gemm_run.  Unknown names return
+ * INVALID_VALUE. */
 gemm_status_t gemm_set_policy(gemm_handle_t h, const char* name);
 
 /* The policy table: count and names (index 0 .. count-1).  Out-of-range -> NULL. */

@@ -112,6 +112,9 @@ def test_policy_selection_is_shape_driven_and_deterministic():
     assert q(5120, 5120, 2048, transA=1).startswith("bf16_")
     small = q(256, 256, 256, dtype=d.BF16_F32)
     assert small.startswith("bf16_") and "m256n256" not in small  # more than one tile for 256^3
+    # split-K only where the tiles alone leave most CUs idle
+    assert "+sk" in q(512, 512, 8192) and "+sk" not in q(4096, 4096, 4096)
+    assert "+sk" not in q(512, 512, 256)  # too few K tiles to share
 
 
 def test_query_policy_rejects_bad_arguments():
