@@ -36,9 +36,9 @@ PEAK_TFLOPS = {"bf16": 2516.6, "e4m3": 5033.2}  # 256 CU x 2.4 GHz x 4096 (8192 
 HBM_GBS = 8000.0
 METRIC = "TFLOP/s and % of MI355X dense MFMA peak, 4096³ bf16 GEMM (1 GPU)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_4096_bf16.md")
+# the device code of the direct-to-LDS kernels (the headline policy's kernel)
 KERNEL_SOURCES = [os.path.join(ROOT, "dense_blas3_gemm_amd", "csrc", f)
-                  for f in ("kernel_mfma.hip", "kernel_mfma_dma.hip", "mfma_common.h", "policies.inc",
-                            "policy.cpp")]
+                  for f in ("kernel_mfma_dma.hip", "mfma_common.h", "gemm_internal.h")]
 
 
 def _dev(bits, kind):
@@ -59,9 +59,9 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(policy: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel sources (else None)."""
+    taken on the current kernel sources and the same policy (else None)."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
@@ -70,7 +70,7 @@ def measured_traffic():
             for kv in line[len("traffic:"):].split():
                 k, v = kv.split("=")
                 vals[k] = v
-    if vals.get("kernel_hash") != kernel_hash():
+    if vals.get("kernel_hash") != kernel_hash() or vals.get("policy") != policy:
         return None
     try:
         return float(vals["fetch_bytes"]) + float(vals["write_bytes"])
@@ -241,7 +241,7 @@ def main():
                    "accumulate": "f32", "alpha": p.alpha, "beta": p.beta, "policy": r["policy"]},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic() if p is gi.SQUARE_4096 and not args.policy else None,
+                     "traffic": measured_traffic(r["policy"]) if p is gi.SQUARE_4096 and not args.policy else None,
                      "launch_us_p50": round(float(np.percentile(ev, 50)) * 1e3, 2),
                      "launch_us_p95": round(float(np.percentile(ev, 95)) * 1e3, 2),
                      "launch_us_mean": round(avg_launch_ms * 1e3, 2)},

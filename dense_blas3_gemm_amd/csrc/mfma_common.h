@@ -102,15 +102,21 @@ struct Cfg {
   static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
 };
 
-// XOR swizzle of the 16-byte chunk index of LDS row r.
-//  * K-contiguous tiles (row = 64, 128 or 256 bytes) are read by ds_read_b128 with
-//    16 consecutive lanes on 16 consecutive rows at one chunk column: the xor makes
-//    those 16 reads land on distinct 16-byte slots of the 256-byte bank line, and any
-//    8 consecutive rows on distinct slots of a 128-byte line.
+// XOR swizzle of the 16-byte chunk index of LDS row r.  The LDS serves 256 bytes per
+// clock (64 banks); a 128-byte row puts even and odd rows on the two bank halves.
+//  * K-contiguous tiles (row = 64, 128 or 256 bytes) are read by ds_read_b128.  On
+//    gfx950 the lanes served together are 0-7 with 24-31 and 8-15 with 16-23 (and the
+//    same in the upper half wave), as measured with the LDS bank-conflict counter.  A
+//    32x32 fragment puts lanes 0-31 on rows r..r+31 at one chunk column; a 16x16 one
+//    puts lanes 0-15 on rows r..r+15 at chunk c and lanes 16-31 on the same rows at
+//    c+1.  For 128-byte bf16 rows the xor (r>>1)&7 keeps both shapes conflict-free:
+//    every serving group then covers each bank slot once.
 //  * M/N-contiguous bf16 tiles are read by ds_read_b64_tr_b16: each group of 16
 //    lanes reads 4 consecutive rows of one 32-byte column pair; a half wave reads
 //    either two neighbouring pairs of the same rows (32x32 MFMA) or one pair of rows
-//    r..r+3 and r+8..r+11 (16x16).  The xor moves the pair by ((r&3)<<1)|((r>>3)&1).
+//    r..r+3 and r+8..r+11 (16x16).  Rows of 256 bytes or more all start on bank 0, so
+//    the pair moves by ((r&3)<<1)|((r>>3)&1); 128-byte rows alternate bank halves, so
+//    only the rows of one parity must separate: by 4 chunks for r&2 and 2 for r&8.
 //  * M/N-contiguous E4M3 tiles are read by ds_read_b64_tr_b8: 16 lanes read 8
 //    consecutive rows of one 16-byte chunk; a half wave reads two neighbouring
 //    chunks of the same rows (32x32) or rows r..r+7 and r+32..r+39 (16x16).
@@ -120,11 +126,21 @@ template <bool KC, bool FP8, int CPR>
 __device__ inline int swz(int r) {
   int x;
   if constexpr (KC) {
-    if constexpr (CPR == 4) x = ((r >> 1) ^ (r >> 3)) & 3;
-    else if constexpr (CPR == 8) x = (r & 7) ^ ((r >> 3) & 1);
-    else x = r & 15;
+    if constexpr (CPR == 4) {
+      x = ((r >> 1) ^ (r >> 3)) & 3;
+    } else if constexpr (CPR == 8) {
+      if constexpr (FP8)
+        x = (r & 7) ^ ((r >> 3) & 1);
+      else
+        x = (r >> 1) & 7;
+    } else {
+      x = r & 15;
+    }
   } else if constexpr (!FP8) {
-    x = (((r & 3) << 1) | ((r >> 3) & 1)) << 1;
+    if constexpr (CPR == 8)
+      x = (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 1);
+    else
+      x = (((r & 3) << 1) | ((r >> 3) & 1)) << 1;
   } else {
     x = ((r & 7) << 1) | ((r >> 5) & 1);
   }
