@@ -104,6 +104,16 @@ def dtype_code(in_dtype: str, c_dtype: str) -> int:
             ("e4m3", "bf16"): E4M3_BF16, ("e4m3", "f32"): E4M3_F32}[(in_dtype, c_dtype)]
 
 
+def _current_stream(device) -> int:
+    """Raw hipStream_t of torch's current stream on `device` (the cheap accessor when
+    this torch has it)."""
+    import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return int(raw(device.index if device.index is not None else torch.cuda.current_device()))
+    return torch.cuda.current_stream(device).cuda_stream
+
+
 def _ptr(t) -> int:
     return 0 if t is None else int(t.data_ptr())
 
@@ -125,6 +135,7 @@ class Gemm:
         if st != 0:
             raise GemmError("gemm_create", st)
         self.handle = h
+        self._stream = 0  # the stream the handle is bound to (gemm_create starts on NULL)
 
     def close(self):
         if self.handle is not None:
@@ -146,11 +157,12 @@ class Gemm:
         st = self.lib.gemm_set_stream(self.handle, ctypes.c_void_p(stream_ptr))
         if st != 0:
             raise GemmError("gemm_set_stream", st)
+        self._stream = stream_ptr
 
     def run_raw(self, transA, transB, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr, ldc,
                 dtype, stream_ptr: Optional[int] = None) -> int:
         """Direct C-ABI call with raw device pointers; returns the status code."""
-        if stream_ptr is not None:
+        if stream_ptr is not None and stream_ptr != self._stream:
             self.set_stream(stream_ptr)
         return self.lib.gemm_run(self.handle, int(transA), int(transB), int(M), int(N), int(K),
                                  float(alpha), ctypes.c_void_p(A_ptr), int(lda), ctypes.c_void_p(B_ptr),
@@ -170,7 +182,7 @@ class Gemm:
             dtype = dtype_code(ind, cd)
         M, N = C.shape
         K = A.shape[0] if transA else A.shape[1]
-        stream = torch.cuda.current_stream(C.device).cuda_stream
+        stream = _current_stream(C.device)
         st = self.run_raw(transA, transB, M, N, K, alpha, _ptr(A), _ld(A), _ptr(B), _ld(B), beta,
                           _ptr(C), _ld(C), dtype, stream_ptr=stream)
         if st != 0:
