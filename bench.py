@@ -1,7 +1,8 @@
 """Benchmark of the dense GEMM hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--sweep]
-                    [--ablation] [--policy NAME] [--workload NAME] [--copy-calibration MiB]
+                    [--ablation] [--ladder] [--lds-probe] [--policy NAME] [--workload NAME]
+                    [--copy-calibration MiB]
 
 A step is one call C = alpha*A*B + beta*C of the headline workload, 4096^3 bf16
 row-major NN with bf16 C (alpha 1, beta 0), on inputs already resident in HBM.
@@ -12,6 +13,10 @@ recorded on the stream the kernel runs on.  Prints one JSON line.
 --sweep additionally times every other workload (10 warmup + 50 event-timed calls
 each, p50/p95) and prints a Markdown table to stderr; the JSON line is unchanged.
 --ablation times every applicable policy on the headline and the E4M3 workloads.
+--ladder runs the ablation ladder (one variable per rung: global->LDS path and LDS stages,
+LDS->register reads, B layout, swizzle) on three K values and a K x M/N heat map, and
+--lds-probe the load-only LDS read microbenchmark; both print Markdown to stderr and
+exit without the JSON line.
 --policy / --workload pin the policy or pick another workload for the timed steps
 (used for profiling single kernels); the JSON line then names them in `config`.
 --copy-calibration N runs only a plain device-to-device copy of N MiB (the known-size
@@ -176,6 +181,158 @@ def ablation(g, p: gi.Gemm, warmup: int = 10, steps: int = 50):
     return rows
 
 
+# The ablation ladder ("cp.async / ldmatrix ablation -- initial plan", sections 2-4) at a
+# fixed 128x128x64 tile, 8 waves, 16x16x32 MFMA.  Global -> LDS rungs in the corrected
+# order (section 2.3, first pitfall: a second buffer before the asynchronous path):
+# register-staged loads with two LDS stages, then direct-to-LDS loads with two, three and
+# four stages.  LDS -> register rungs on the last of them: element-wise reads, the
+# layout most favourable to plain reads (B stored K-contiguous), transposing reads.
+LADDER = [
+    ("B0", "global -> VGPR -> ds_write, 2 LDS stages", "bf16_m128n128k64_w2x4_mt16_s2", 0),
+    ("B1", "direct-to-LDS loads, 2 stages", "bf16_dma_m128n128k64_w2x4_mt16_s2", 0),
+    ("B2", "direct-to-LDS loads, 3 stages", "bf16_dma_m128n128k64_w2x4_mt16_s3", 0),
+    ("B3", "direct-to-LDS loads, 4 stages", "bf16_dma_m128n128k64_w2x4_mt16_s4", 0),
+    ("A1", "B3, B read one element at a time (ds_read_u16)", "bf16_dma_m128n128k64_w2x4_mt16_s4_rd0", 0),
+    ("A2", "B3, B stored K-contiguous (NT): plain ds_read_b128", "bf16_dma_m128n128k64_w2x4_mt16_s4", 1),
+    ("A3", "B3, B read with ds_read_b64_tr_b16 (NN)", "bf16_dma_m128n128k64_w2x4_mt16_s4", 0),
+    ("S0", "B3 without the LDS xor swizzle", "bf16_dma_m128n128k64_w2x4_mt16_s4_noswz", 0),
+    ("S1", "B3 with the swizzle", "bf16_dma_m128n128k64_w2x4_mt16_s4", 0),
+    ("P0", "256x256 tile, global -> VGPR -> ds_write", "bf16_m256n256k64_w2x4_mt16_s2", 0),
+    ("P1", "256x256 tile, direct-to-LDS (the 4096^3 default)", "bf16_dma_m256n256k64_w2x4_mt16_s2", 0),
+]
+
+
+def ladder(g, rounds: int = 3, warmup: int = 3, steps: int = 20, heatmap: bool = True, quick: bool = False):
+    """Each rung on K = 256, 4096, 8192 at M = N = 4096 (section 2.3, third pitfall: a
+    single shape misleads), rounds interleaved; Markdown to stderr.  quick: 4096^3 only,
+    one round, in LADDER order (for counter passes: 23 GEMM dispatches per rung)."""
+    import dataclasses
+    shapes = [gi.BY_NAME["sweep_mn4096_k256"], gi.SQUARE_4096, gi.BY_NAME["sweep_mn4096_k8192"]]
+    if quick:
+        shapes, rounds, heatmap = [gi.SQUARE_4096], 1, False
+    res = {}
+    for p in shapes:
+        datas = {tb: dataclasses.replace(p, transB=tb).make() for tb in (0, 1)}
+        times = {r[0]: [] for r in LADDER}
+        for _ in range(rounds):
+            for rung, _desc, pol, tb in LADDER:
+                q = dataclasses.replace(p, transB=tb)
+                g.set_policy(pol)
+                try:
+                    t = time_problem(g, q, warmup, steps, data=datas[tb])
+                finally:
+                    g.set_policy(None)
+                times[rung].append(float(np.percentile(t["event_ms"], 50)))
+        for rung in times:
+            ms = float(np.median(times[rung]))
+            res[(rung, p.name)] = (ms * 1e3, p.flops / (ms * 1e-3) / 1e12)
+    out = sys.stderr
+    print("ablation ladder (p50 of event-timed calls, median over rounds; delta vs the rung above)", file=out)
+    hdr = "| rung | change | policy | " + " | ".join(f"{p.name} TFLOP/s | delta" for p in shapes) + " |"
+    print(hdr, file=out)
+    print("|" + "---|" * (3 + 2 * len(shapes)), file=out)
+    prev = None
+    for rung, desc, pol, tb in LADDER:
+        cells = []
+        for p in shapes:
+            tf = res[(rung, p.name)][1]
+            base = None
+            if prev is not None and rung[0] == prev[0]:
+                base = res[(prev, p.name)][1]
+            cells.append(f"{tf:.1f} | " + (f"{100 * (tf / base - 1):+.1f}%" if base else ""))
+        print(f"| {rung} | {desc} | {pol}{' (NT)' if tb else ''} | " + " | ".join(cells) + " |", file=out)
+        prev = rung
+    if heatmap:
+        print("heat map (TFLOP/s, p50 of 20 event-timed calls): rows K, columns M = N", file=out)
+        ks = sorted({w.K for w in gi.SWEEP})
+        mns = sorted({w.M for w in gi.SWEEP})
+        for label, pol in [("B0", LADDER[0][2]), ("B3", LADDER[3][2]), ("P1", LADDER[-1][2]), ("auto", None)]:
+            print(f"{label} ({pol or 'shape-driven policy'})", file=out)
+            print("| K | " + " | ".join(f"M=N={m}" for m in mns) + " |", file=out)
+            print("|---|" + "---|" * len(mns), file=out)
+            for k in ks:
+                row = []
+                for m in mns:
+                    w = next(x for x in gi.SWEEP if x.K == k and x.M == m)
+                    g.set_policy(pol)
+                    try:
+                        t = time_problem(g, w, warmup, steps)
+                    finally:
+                        g.set_policy(None)
+                    row.append(f"{w.flops / (float(np.percentile(t['event_ms'], 50)) * 1e-3) / 1e12:.1f}")
+                print(f"| {k} | " + " | ".join(row) + " |", file=out)
+    return res
+
+
+def lds_probe_patterns():
+    """Per-lane LDS byte offsets of the kernels' 16x16x32 fragment reads (8 read slots).
+    K-contiguous A fragments of a 128-byte-row tile (ds_read_b128, one read per fragment);
+    M/N-contiguous B fragments of a 256-byte-row tile (128 wide): transposing reads (two
+    per fragment) or one element per read (eight per fragment); with and without the row
+    xor."""
+    def kc(r, swz):
+        return ((r >> 1) & 7) if swz else 0
+
+    def mn(k, swz):
+        return ((((k & 3) << 1) | ((k >> 3) & 1)) << 1) & 15 if swz else 0
+    pats = []
+    for swz in (1, 0):
+        b128 = [[(16 * j + l % 16) * 128 + (((l // 16) ^ kc(16 * j + l % 16, swz)) & 7) * 16 for l in range(64)]
+                for j in range(8)]
+        tr = []
+        for j in range(8):
+            x0, h = 16 * (j // 2), j % 2
+            row = []
+            for l in range(64):
+                g_, s_ = l >> 4, l & 15
+                x, k = x0 + (s_ % 4) * 4, g_ * 8 + h * 4 + s_ // 4
+                xb = 2 * x
+                row.append(k * 256 + ((((xb >> 4) ^ mn(k, swz)) << 4) | (xb & 15)))
+            tr.append(row)
+        u16 = []
+        for e in range(8):
+            row = []
+            for l in range(64):
+                x, k = l % 16, (l // 16) * 8 + e
+                xb = 2 * x
+                row.append(k * 256 + ((((xb >> 4) ^ mn(k, swz)) << 4) | (xb & 15)))
+            u16.append(row)
+        tag = "swizzled" if swz else "plain"
+        pats += [(f"A fragment, ds_read_b128, {tag}", 0, b128, 8),
+                 (f"B fragment, ds_read_b64_tr_b16, {tag}", 1, tr, 4),
+                 (f"B fragment, ds_read_u16 x8, {tag}", 2, u16, 1)]
+    return pats
+
+
+def lds_probe(g, iters: int = 512, workgroups: int = 1024, reps: int = 5):
+    """The load-only LDS microbenchmark (section 2.3, second pitfall): ns per 16x16x32
+    fragment per CU for each read form, Markdown to stderr."""
+    import torch
+    stream = torch.cuda.current_stream()
+    out = sys.stderr
+    print("LDS read microbenchmark: 1024 workgroups x 4 waves, 512 iterations x 8 reads per lane", file=out)
+    print("| read | reads per fragment | us per launch (p50) | ns per fragment per CU | fragment bytes per CU per ns |",
+          file=out)
+    print("|---|---|---|---|---|", file=out)
+    rows = []
+    for name, kind, offs, frags in lds_probe_patterns():
+        ev = []
+        for _ in range(reps + 1):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.lds_probe(kind, offs, iters, workgroups, stream_ptr=stream.cuda_stream)
+            b.record(stream)
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) for a, b in ev[1:]])) * 1e3
+        total_frags = workgroups * 4 * iters * frags
+        ns_per_frag_cu = us * 1e3 * 256 / total_frags
+        rows.append((name, 8 // frags, us, ns_per_frag_cu))
+        print(f"| {name} | {8 // frags} | {us:.1f} | {ns_per_frag_cu:.2f} | {1024 / ns_per_frag_cu:.1f} |",
+              file=out)
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +342,11 @@ def main():
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--ablation", action="store_true",
                     help="time every applicable policy on the 4096^3 bf16 and the E4M3 workloads")
+    ap.add_argument("--ladder", action="store_true", help="run the ablation ladder and exit")
+    ap.add_argument("--no-heatmap", action="store_true", help="with --ladder: skip the K x M/N heat map")
+    ap.add_argument("--ladder-quick", action="store_true",
+                    help="with --ladder: 4096^3 only, one round (3 + 20 calls per rung, in order)")
+    ap.add_argument("--lds-probe", action="store_true", help="run the LDS read microbenchmark and exit")
     ap.add_argument("--policy", default=None, help="force a named policy for the timed steps")
     ap.add_argument("--workload", default=gi.SQUARE_4096.name, choices=sorted(gi.BY_NAME))
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
@@ -210,6 +372,13 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": args.warmup + args.steps}))
         return
     g = d.Gemm(0)
+    if args.ladder or args.lds_probe:
+        if args.lds_probe:
+            lds_probe(g)
+        if args.ladder:
+            ladder(g, heatmap=not args.no_heatmap, quick=args.ladder_quick)
+        g.close()
+        return
     p = gi.BY_NAME[args.workload]
     if args.policy:
         g.set_policy(args.policy)

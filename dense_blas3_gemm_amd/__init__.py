@@ -21,8 +21,8 @@ STATUS = {0: "SUCCESS", 1: "INVALID_VALUE", 2: "NOT_SUPPORTED", 3: "NOT_INITIALI
 
 # The exported C symbols, in the order include/gemm.h declares them.
 EXPORTS = ["gemm_create", "gemm_destroy", "gemm_set_stream", "gemm_run", "gemm_check_args",
-           "gemm_query_policy", "gemm_set_policy", "gemm_policy_count", "gemm_policy_name",
-           "gemm_version", "gemm_status_string"]
+           "gemm_query_policy", "gemm_set_policy", "gemm_lds_probe", "gemm_policy_count",
+           "gemm_policy_name", "gemm_version", "gemm_status_string"]
 
 _lib = None
 
@@ -76,6 +76,7 @@ def load_library():
     lib.gemm_query_policy.argtypes = [vp, i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32,
                                       ctypes.c_char_p, ctypes.c_size_t]
     lib.gemm_set_policy.argtypes = [vp, ctypes.c_char_p]
+    lib.gemm_lds_probe.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_uint32), i32, i32]
     lib.gemm_policy_count.argtypes = []
     lib.gemm_policy_name.argtypes = [i32]
     lib.gemm_policy_name.restype = ctypes.c_char_p
@@ -84,7 +85,7 @@ def load_library():
     lib.gemm_status_string.argtypes = [i32]
     lib.gemm_status_string.restype = ctypes.c_char_p
     for fn in ["gemm_create", "gemm_destroy", "gemm_set_stream", "gemm_run", "gemm_check_args",
-               "gemm_query_policy", "gemm_set_policy", "gemm_policy_count"]:
+               "gemm_query_policy", "gemm_set_policy", "gemm_lds_probe", "gemm_policy_count"]:
         getattr(lib, fn).restype = i32
     _lib = lib
     return lib
@@ -188,6 +189,18 @@ class Gemm:
         if st != 0:
             raise GemmError("gemm_run", st)
         return C
+
+    def lds_probe(self, kind: int, offsets, iters: int, workgroups: int, stream_ptr: Optional[int] = None):
+        """Enqueues the LDS read microbenchmark (gemm_lds_probe); offsets: 8 x 64 byte offsets."""
+        flat = [int(v) for row in offsets for v in row]
+        if len(flat) != 512:
+            raise ValueError("offsets must be 8 rows of 64 lanes")
+        if stream_ptr is not None and stream_ptr != self._stream:
+            self.set_stream(stream_ptr)
+        arr = (ctypes.c_uint32 * 512)(*flat)
+        st = self.lib.gemm_lds_probe(self.handle, int(kind), arr, int(iters), int(workgroups))
+        if st != 0:
+            raise GemmError("gemm_lds_probe", st)
 
     def query_policy(self, M, N, K, transA=0, transB=0, dtype=BF16_BF16, A_ptr=0, lda=None,
                      B_ptr=0, ldb=None, C_ptr=0, ldc=None) -> str:

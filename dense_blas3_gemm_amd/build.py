@@ -19,17 +19,23 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libdbgemm.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["api.cpp", "policy.cpp", "kernel_simt.hip", "kernel_mfma.hip", "kernel_mfma_dma.hip"]
+# (source, object name, extra flags): the direct-to-LDS kernels are compiled once per
+# transpose case so that the four groups of instantiations build in parallel
+SOURCES = [("api.cpp", "api", []), ("policy.cpp", "policy", []), ("kernel_simt.hip", "kernel_simt", []),
+           ("kernel_mfma.hip", "kernel_mfma", []), ("lds_probe.hip", "lds_probe", [])] + [
+    ("kernel_mfma_dma.hip", f"kernel_mfma_dma_{ta}{tb}", [f"-DDBGEMM_DMA_TA={ta}", f"-DDBGEMM_DMA_TB={tb}"])
+    for ta in (0, 1) for tb in (0, 1)]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
          "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(entry) -> str:
+    src, name, extra = entry
+    obj = os.path.join(BUILD, name + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -77,6 +77,17 @@ Problem make_problem(int transA, int transB, int64_t M, int64_t N, int64_t K, co
 
 }  // namespace
 
+namespace dbgemm {
+hipError_t launch_mfma_dma(const Policy& p, const GemmArgs& a, hipStream_t s) {
+  switch (a.transA * 2 + a.transB) {
+    case 0: return launch_mfma_dma_00(p, a, s);
+    case 1: return launch_mfma_dma_01(p, a, s);
+    case 2: return launch_mfma_dma_10(p, a, s);
+    default: return launch_mfma_dma_11(p, a, s);
+  }
+}
+}  // namespace dbgemm
+
 extern "C" {
 
 const char* gemm_version(void) { return kVersion; }
@@ -232,6 +243,28 @@ gemm_status_t gemm_query_policy(gemm_handle_t h, int transA, int transB, int64_t
   else
     std::snprintf(name, len, "%s", policy_at(idx).name);
   return GEMM_STATUS_SUCCESS;
+}
+
+gemm_status_t gemm_lds_probe(gemm_handle_t h, int kind, const uint32_t* offsets, int iters,
+                             int workgroups) {
+  if (!live(h)) return GEMM_STATUS_NOT_INITIALIZED;
+  const int w = lds_probe_width(kind);
+  if (w == 0 || !offsets || iters < 1 || iters > (1 << 20) || workgroups < 1 || workgroups > 65536)
+    return GEMM_STATUS_INVALID_VALUE;
+  LdsProbeOffsets o;
+  for (int j = 0; j < 8; ++j)
+    for (int l = 0; l < 64; ++l) {
+      const uint32_t v = offsets[j * 64 + l];
+      if (v % (uint32_t)w != 0 || v > (uint32_t)(kLdsProbeBytes - w)) return GEMM_STATUS_INVALID_VALUE;
+      o.off[j][l] = v;
+    }
+  const Handle* p = reinterpret_cast<const Handle*>(h);
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return GEMM_STATUS_INTERNAL;
+  if (cur != p->device && hipSetDevice(p->device) != hipSuccess) return GEMM_STATUS_INTERNAL;
+  const hipError_t err = launch_lds_probe(kind, o, iters, workgroups, p->stream);
+  if (cur != p->device) (void)hipSetDevice(cur);
+  return err == hipSuccess ? GEMM_STATUS_SUCCESS : GEMM_STATUS_LAUNCH_FAILED;
 }
 
 gemm_status_t gemm_run(gemm_handle_t h, int transA, int transB, int64_t M, int64_t N, int64_t K,

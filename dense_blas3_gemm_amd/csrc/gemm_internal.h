@@ -50,6 +50,7 @@ struct Policy {
   int stages;      // LDS stages
   int group, raster_n, xcd, swizzle;
   int krot;        // K-loop rotation per XCD (direct-to-LDS kernels only)
+  int read_mode;   // 1: transposing LDS reads for M/N-contiguous operands; 0: one element per read
   int threads;
   float efficiency;  // relative per-CU throughput used by the wave-time model
 };
@@ -59,6 +60,20 @@ hipError_t launch_simt(const GemmArgs& a, hipStream_t s);
 hipError_t launch_scale(const GemmArgs& a, hipStream_t s);  // C <- beta*C (K == 0 or alpha == 0)
 hipError_t launch_mfma_staged(const Policy& p, const GemmArgs& a, hipStream_t s);  // pipe 0
 hipError_t launch_mfma_dma(const Policy& p, const GemmArgs& a, hipStream_t s);     // pipe 1
+// pipe 1, one per (transA, transB) case, each in its own object
+hipError_t launch_mfma_dma_00(const Policy& p, const GemmArgs& a, hipStream_t s);
+hipError_t launch_mfma_dma_01(const Policy& p, const GemmArgs& a, hipStream_t s);
+hipError_t launch_mfma_dma_10(const Policy& p, const GemmArgs& a, hipStream_t s);
+hipError_t launch_mfma_dma_11(const Policy& p, const GemmArgs& a, hipStream_t s);
+
+// LDS read microbenchmark: 8 reads per lane per iteration, offsets in bytes from the
+// start of a 64 KiB LDS array, each a multiple of the read width and inside the array.
+struct LdsProbeOffsets {
+  uint32_t off[8][64];
+};
+constexpr int kLdsProbeBytes = 65536;
+int lds_probe_width(int kind);  // bytes per lane of read kind 0..3, 0 for an unknown kind
+hipError_t launch_lds_probe(int kind, const LdsProbeOffsets& offs, int iters, int workgroups, hipStream_t s);
 
 // Tile-policy table.
 int policy_count();

@@ -210,7 +210,7 @@ hipError_t launch_mfma_staged(const Policy& p, const GemmArgs& a, hipStream_t s)
 #define DBGEMM_MFMA(name_, pipe_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_, eff_)       \
   if constexpr (pipe_ == 0)                                                                               \
     if (p.BM == bm_ && p.BN == bn_ && p.BK == bk_ && p.WM == wm_ && p.WN == wn_ && p.MT == mt_ &&         \
-        p.stages == st_ && p.in_mode == in_)                                                              \
+        p.stages == st_ && p.in_mode == in_ && p.read_mode == 1)                                          \
       return launch_trans<bm_, bn_, bk_, wm_, wn_, mt_, st_, in_>(a, s);
 #include "policies.inc"
 #undef DBGEMM_SIMT

@@ -311,25 +311,25 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int MT, int ST, int IN>
-hipError_t launch_trans(const GemmArgs& a, hipStream_t s) {
-  switch (a.transA * 2 + a.transB) {
-    case 0: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, false, false>>(a, s);
-    case 1: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, false, true>>(a, s);
-    case 2: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, true, false>>(a, s);
-    default: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, true, true>>(a, s);
-  }
-}
+// This file is compiled once per transpose case (DBGEMM_DMA_TA, DBGEMM_DMA_TB), so the
+// four groups of kernel instantiations build in parallel.
+#if !defined(DBGEMM_DMA_TA) || !defined(DBGEMM_DMA_TB)
+#error "compile with -DDBGEMM_DMA_TA=0|1 -DDBGEMM_DMA_TB=0|1"
+#endif
 
 }  // namespace
 
-hipError_t launch_mfma_dma(const Policy& p, const GemmArgs& a, hipStream_t s) {
+#define DBGEMM_DMA_CAT2(a, b) launch_mfma_dma_##a##b
+#define DBGEMM_DMA_CAT(a, b) DBGEMM_DMA_CAT2(a, b)
+
+hipError_t DBGEMM_DMA_CAT(DBGEMM_DMA_TA, DBGEMM_DMA_TB)(const Policy& p, const GemmArgs& a, hipStream_t s) {
 #define DBGEMM_SIMT(name, eff)
 #define DBGEMM_MFMA(name_, pipe_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_, eff_)       \
   if constexpr (pipe_ == 1)                                                                               \
     if (p.BM == bm_ && p.BN == bn_ && p.BK == bk_ && p.WM == wm_ && p.WN == wn_ && p.MT == mt_ &&         \
-        p.stages == st_ && p.in_mode == in_)                                                              \
-      return launch_trans<bm_, bn_, bk_, wm_, wn_, mt_, st_, in_>(a, s);
+        p.stages == st_ && p.in_mode == in_ && p.read_mode == ((((sw_) >> 2) & 1) ? 0 : 1))               \
+      return launch_cfg<Cfg<bm_, bn_, bk_, wm_, wn_, mt_, st_, in_, DBGEMM_DMA_TA != 0, DBGEMM_DMA_TB != 0,  \
+                            (((sw_) >> 2) & 1) ? 0 : 1>>(a, s);
 #include "policies.inc"
 #undef DBGEMM_SIMT
 #undef DBGEMM_MFMA

@@ -64,10 +64,15 @@ __device__ inline void tile_of(int bid, const GemmArgs& a, int& tm, int& tn, int
 // IN_E4M3_NATIVE (E4M3 operands fed to the f8f6f4 MFMA as they are).
 enum { IN_BF16 = 0, IN_E4M3 = 1, IN_E4M3_NATIVE = 2 };
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int MT_, int STAGES_, int IN_, bool TA_, bool TB_>
+// READ_: 1 reads M/N-contiguous fragments with the transposing ds_read_b64_tr_*; 0 reads
+// them one element at a time (ds_read_u16), the plain-load rung of the read ablation.
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int MT_, int STAGES_, int IN_, bool TA_, bool TB_,
+          int READ_ = 1>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, MT = MT_, STAGES = STAGES_;
   static constexpr int IN = IN_;
+  static constexpr int READ = READ_;
+  static_assert(READ == 1 || IN != IN_E4M3_NATIVE, "element-wise reads are for bf16 fragments");
   static constexpr bool TA = TA_, TB = TB_;
   static constexpr bool FP8 = IN == IN_E4M3_NATIVE;  // fragments and MFMA are E4M3
   static constexpr int THREADS = WM * WN * 64;
@@ -194,6 +199,22 @@ __device__ inline typename FragOf<C::FP8>::T load_frag(const lds_char* base, int
       i32x4 hi = *LDS_PTR(i32x4, base, off1);
       f = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
+  } else if constexpr (C::READ == 0) {
+    // one ds_read_u16 per element: lane holds column x (its M or N index) of rows
+    // k .. k+7 (its K values)
+    const int x = x0 + lane % C::MT;
+    const int k0 = kbase + (lane / C::MT) * C::KPL;
+    const int xb = x * C::ES;
+    typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+    u16x8 all;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = k0 + e;
+      const int sw = sw_on ? swz<false, false, CPR>(k) : 0;
+      const uint32_t off = k * RB + ((((xb >> 4) ^ sw) << 4) | (xb & 15));
+      all[e] = *LDS_PTR(uint16_t, base, off);
+    }
+    f = __builtin_bit_cast(bf16x8, all);
   } else {
     constexpr int E = C::FP8 ? 8 : 4;
     constexpr int LPR = 16 / E;  // lanes per row inside a 16-lane group

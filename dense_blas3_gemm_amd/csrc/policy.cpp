@@ -14,10 +14,10 @@ namespace dbgemm {
 namespace {
 
 const Policy kTable[] = {
-#define DBGEMM_SIMT(name_, eff_) {name_, KIND_SIMT, 0, -1, 64, 64, 16, 1, 1, 0, 1, 1, 0, 1, 0, 0, 256, eff_},
+#define DBGEMM_SIMT(name_, eff_) {name_, KIND_SIMT, 0, -1, 64, 64, 16, 1, 1, 0, 1, 1, 0, 1, 0, 0, 1, 256, eff_},
 #define DBGEMM_MFMA(name_, pipe_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_, eff_) \
-  {name_, KIND_MFMA, pipe_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_ & 1, (sw_) >> 1, \
-   (wm_) * (wn_) * 64, eff_},
+  {name_, KIND_MFMA, pipe_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, (sw_) & 1,        \
+   ((sw_) >> 1) & 1, ((sw_) >> 2) & 1 ? 0 : 1, (wm_) * (wn_) * 64, eff_},
 #include "policies.inc"
 #undef DBGEMM_SIMT
 #undef DBGEMM_MFMA

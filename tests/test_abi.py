@@ -117,6 +117,13 @@ def test_policy_selection_is_shape_driven_and_deterministic():
     assert "+sk" not in q(512, 512, 256)  # too few K tiles to share
 
 
+def test_lds_probe_rejects_bad_arguments():
+    lib = d.load_library()
+    ok = (ctypes.c_uint32 * 512)(*([0] * 512))
+    assert lib.gemm_lds_probe(None, 0, ok, 1, 1) == NOT_INIT
+    assert lib.gemm_lds_probe(ctypes.c_void_p(0x1234), 0, ok, 1, 1) == NOT_INIT
+
+
 def test_query_policy_rejects_bad_arguments():
     lib = d.load_library()
     buf = ctypes.create_string_buffer(64)

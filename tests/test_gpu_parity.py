@@ -24,11 +24,15 @@ BF16_DMA_POLICIES = ["bf16_dma_m256n256k32_w2x4_mt32_s4", "bf16_dma_m256n256k32_
                      "bf16_dma_m256n256k64_w2x2_mt32_s2_krot", "bf16_dma_m256n256k32_w2x2_mt32_s4_krot",
                      "bf16_dma_m256n256k64_w2x4_mt16_s2", "bf16_dma_m128n256k64_w2x4_mt16_s3",
                      "bf16_dma_m256n128k64_w4x2_mt16_s3", "bf16_dma_m128n128k64_w2x2_mt16_s4",
-                     "bf16_dma_m128n128k64_w2x4_mt16_s4", "bf16_dma_m64n64k64_w2x2_mt16_s4"]
+                     "bf16_dma_m128n128k64_w2x4_mt16_s4", "bf16_dma_m64n64k64_w2x2_mt16_s4",
+                     "bf16_dma_m128n128k64_w2x4_mt16_s2", "bf16_dma_m128n128k64_w2x4_mt16_s3",
+                     "bf16_dma_m128n128k64_w2x4_mt16_s4_rd0", "bf16_dma_m128n128k64_w2x4_mt16_s4_noswz",
+                     "bf16_dma_m256n256k64_w2x4_mt16_s2_rd0", "bf16_dma_m256n256k64_w2x4_mt16_s2_noswz"]
 BF16_POLICIES = BF16_DMA_POLICIES + ["bf16_m256n256k64_w2x2_mt32_s2", "bf16_m256n256k64_w2x4_mt32_s2",
                  "bf16_m256n128k64_w2x2_mt32_s2", "bf16_m128n256k64_w2x2_mt32_s2",
                  "bf16_m128n128k64_w2x2_mt32_s2", "bf16_m128n128k64_w2x2_mt16_s2",
                  "bf16_m64n64k64_w2x2_mt16_s2", "bf16_m256n256k64_w2x2_mt32_s2_noswz",
+                 "bf16_m128n128k64_w2x4_mt16_s2", "bf16_m256n256k64_w2x4_mt16_s2",
                  "bf16_m256n256k64_w2x2_mt32_s2_noxcd"]
 FP8_POLICIES = ["e4m3_m256n256k64_w2x2_mt32_s2", "e4m3_m256n256k64_w2x4_mt32_s2",
                 "e4m3_m256n256k64_w2x4_mt16_s2", "e4m3_m128n128k64_w2x4_mt16_s2",
@@ -228,6 +232,40 @@ def test_data_movement_variants_bitwise_equal(gpu):
              "bf16_m128n128k64_w2x2_mt32_s2"] + [p for p in BF16_DMA_POLICIES if "krot" not in p and "mt16" not in p]]
     for o in outs[1:]:
         assert np.array_equal(outs[0], o)
+
+
+def test_data_movement_variants_bitwise_equal_16x16(gpu):
+    """With 16x16x32 MFMA and BK = 64, every tile size, load path, stage count, read form
+    and swizzle sums each output in the same order: identical bits."""
+    p = gi.Gemm("t", 1024, 768, 1000, dist="normal")
+    data = p.make()
+    pols = ["bf16_dma_m256n256k64_w2x4_mt16_s2", "bf16_dma_m256n256k64_w2x4_mt16_s2_rd0",
+            "bf16_dma_m256n256k64_w2x4_mt16_s2_noswz", "bf16_m256n256k64_w2x4_mt16_s2",
+            "bf16_dma_m128n128k64_w2x4_mt16_s2", "bf16_dma_m128n128k64_w2x4_mt16_s3",
+            "bf16_dma_m128n128k64_w2x4_mt16_s4", "bf16_dma_m128n128k64_w2x4_mt16_s4_rd0",
+            "bf16_dma_m128n128k64_w2x4_mt16_s4_noswz", "bf16_m128n128k64_w2x4_mt16_s2",
+            "bf16_dma_m64n64k64_w2x2_mt16_s4", "bf16_m64n64k64_w2x2_mt16_s2"]
+    outs = [run_gpu(gpu, p, data, policy=pol) for pol in pols]
+    for pol, o in zip(pols[1:], outs[1:]):
+        assert np.array_equal(outs[0], o), pol
+    _assert_ok(compare(p, data, outs[0]), "16x16 family")
+
+
+def test_lds_probe_runs(gpu):
+    """The LDS read microbenchmark launches for every read form and rejects bad offsets."""
+    import torch
+    import bench
+    import dense_blas3_gemm_amd as d
+    for _name, kind, offs, _f in bench.lds_probe_patterns():
+        gpu.lds_probe(kind, offs, 4, 8)
+    torch.cuda.synchronize()
+    bad = [[0] * 64 for _ in range(8)]
+    bad[3][5] = 8  # not a multiple of 16 for ds_read_b128
+    with pytest.raises(d.GemmError, match="INVALID"):
+        gpu.lds_probe(0, bad, 4, 8)
+    bad[3][5] = 65536 - 8  # past the end for 16-byte reads
+    with pytest.raises(d.GemmError, match="INVALID"):
+        gpu.lds_probe(0, bad, 4, 8)
 
 
 def test_run_to_run_deterministic_and_seed_sensitive(gpu):
