@@ -64,6 +64,9 @@ def load():
     lib.oracle_bf16_value.restype = ctypes.c_double
     lib.oracle_round_bf16.argtypes = [ctypes.c_double]
     lib.oracle_round_bf16.restype = ctypes.c_uint16
+    lib.oracle_gemm_mx.restype = ctypes.c_int
+    lib.oracle_gemm_mx.argtypes = [i64, i64, i64, ctypes.c_double, vp, i64, vp, i64, vp, i64, vp, i64,
+                                   ctypes.c_double, vp, i64, ctypes.c_int, vp, i64, vp, vp, ctypes.c_int]
     _lib = lib
     return lib
 
@@ -145,3 +148,86 @@ def gemm_problem(g, data, rows=None, with_abs=True, threads=None):
     C = data.get("C")
     return gemm(g.transA, g.transB, g.M, g.N, g.K, g.alpha, A, A.shape[1], B, B.shape[1],
                 g.beta, C, g.N, in_fmt, c_fmt, rows=rows, with_abs=with_abs, threads=threads)
+
+
+def gemm_mx(M: int, N: int, K: int, alpha: float, A: np.ndarray, lda: int, SA: np.ndarray, ldsa: int,
+            B: np.ndarray, ldb: int, SB: np.ndarray, ldsb: int, beta: float, C: Optional[np.ndarray],
+            ldc: int, c_fmt: int, rows: Optional[Sequence[int]] = None, with_abs: bool = True,
+            threads: Optional[int] = None) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+    """Block-scaled E4M3 GEMM (see oracle_gemm_mx): A [M][lda], B [N][ldb] E4M3 codes, SA
+    [M][ldsa], SB [N][ldsb] UE8M0 bytes, one per row and 32-element K block."""
+    lib = load()
+    A, B = np.ascontiguousarray(A, dtype=np.uint8), np.ascontiguousarray(B, dtype=np.uint8)
+    SA, SB = np.ascontiguousarray(SA, dtype=np.uint8), np.ascontiguousarray(SB, dtype=np.uint8)
+    if C is not None:
+        C = np.ascontiguousarray(C)
+    if rows is None:
+        nrows, rows_arr = M, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = int(rows_arr.size)
+    R = np.empty((nrows, N), dtype=np.float64)
+    S = np.empty((nrows, N), dtype=np.float64) if with_abs else None
+    rc = lib.oracle_gemm_mx(int(M), int(N), int(K), float(alpha), _ptr(A), int(lda), _ptr(SA), int(ldsa),
+                            _ptr(B), int(ldb), _ptr(SB), int(ldsb), float(beta), _ptr(C), int(ldc),
+                            int(c_fmt), _ptr(rows_arr), int(nrows), _ptr(R), _ptr(S),
+                            int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_gemm_mx rejected its arguments")
+    return R, S
+
+
+# The 127 non-negative finite E4M3 values in code order (0x00 .. 0x7E), for quantisation.
+def _e4m3_grid():
+    codes = np.arange(0x7F, dtype=np.uint8)
+    return decode(codes, "e4m3"), codes
+
+
+def quantize_mx(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Quantises each row of x (float64 values, rows x cols) to E4M3 codes with one UE8M0
+    scale per 32 consecutive elements of the row (the last block may be shorter).
+
+    The MXFP8 quantisation the fused profile protocol describes (section "SM103 MXFP8
+    QKV weight-quantization diagnostics": read, amax of the 32-element group, UE8M0
+    scale, E4M3 conversion) with the rule of the OCP microscaling format, which the page
+    does not spell out: the scale exponent is floor(log2(amax)) minus 8, the largest
+    E4M3 exponent, clamped to the UE8M0 range (stored as that plus 127, 0 .. 254; an
+    all-zero block gets 0); each element is x / 2^(e-127) rounded to the nearest E4M3
+    value, ties to the even code, saturating at +-448, keeping the sign of x.
+    Plain loops over blocks; the nearest value is found on the sorted grid.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    rows, cols = x.shape
+    nb = (cols + 31) // 32
+    grid, gcodes = _e4m3_grid()
+    codes = np.zeros((rows, cols), dtype=np.uint8)
+    scales = np.zeros((rows, nb), dtype=np.uint8)
+    for i in range(rows):
+        for b in range(nb):
+            blk = x[i, 32 * b:32 * b + 32]
+            amax = float(np.max(np.abs(blk)))
+            if amax == 0.0:
+                e = 0
+            else:
+                _f, ex = np.frexp(amax)  # amax = f * 2^ex, f in [0.5, 1)
+                e = int(min(254, max(0, (int(ex) - 1) - 8 + 127)))
+            scales[i, b] = e
+            for t, v in enumerate(blk):
+                q = abs(float(v)) / 2.0 ** (e - 127)
+                if q >= 448.0:
+                    c = 0x7E
+                else:
+                    hi = int(np.searchsorted(grid, q))  # grid[hi-1] < q <= grid[hi]
+                    if grid[hi] == q:
+                        c = int(gcodes[hi])
+                    else:
+                        lo = hi - 1
+                        dlo, dhi = q - grid[lo], grid[hi] - q
+                        if dlo < dhi or (dlo == dhi and gcodes[lo] % 2 == 0):
+                            c = int(gcodes[lo])
+                        else:
+                            c = int(gcodes[hi])
+                if np.signbit(v):
+                    c |= 0x80
+                codes[i, 32 * b + t] = c
+    return codes, scales

@@ -178,6 +178,61 @@ int oracle_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, double 
   return bad ? -1 : 0;
 }
 
+/*
+ * Block-scaled E4M3 GEMM ("MXFP8").  The fused profile protocol's MXFP8 paths (section
+ * "SM103 MXFP8 QKV weight-quantization diagnostics": E4M3 elements, one UE8M0 scale
+ * per group of 32 along K, obtained from the group's amax) multiply such operands.
+ * A UE8M0 byte e stands for 2^(e-127); e = 255 is NaN.  The plain reading of a
+ * block-scaled product, with both operands K-contiguous (A stored [M][lda], B stored
+ * [N][ldb], one scale byte per row and 32-element K block in SA [M][ldsa] and
+ * SB [N][ldsb]):
+ *
+ *   R[i][j] = alpha * sum_k (A(i,k) * 2^(SA[i][k/32]-127)) * (B(j,k) * 2^(SB[j][k/32]-127))
+ *             + beta * Cold[i][j]
+ *
+ * summed in binary64 in k order like oracle_gemm; every scaled value and every
+ * product is exact in binary64.  S receives sum_k |product|.
+ */
+static inline double mx_scale(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
+int oracle_gemm_mx(int64_t M, int64_t N, int64_t K, double alpha, const uint8_t* A, int64_t lda,
+                   const uint8_t* SA, int64_t ldsa, const uint8_t* B, int64_t ldb,
+                   const uint8_t* SB, int64_t ldsb, double beta, const void* C, int64_t ldc,
+                   int c_fmt, const int64_t* rows, int64_t nrows, double* R, double* S,
+                   int nthreads) {
+  if (M < 0 || N < 0 || K < 0) return -1;
+  if (c_fmt != ORACLE_C_F32 && c_fmt != ORACLE_C_BF16) return -1;
+  if (rows == NULL) nrows = M;
+  if (nrows == 0 || N == 0) return 0;
+  init_tables();
+  if (nthreads <= 0) nthreads = 1;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t i = rows ? rows[r] : r;
+    if (i < 0 || i >= M) {
+      bad = 1;
+      continue;
+    }
+    double* acc = R + r * N;
+    double* sab = S ? S + r * N : NULL;
+    for (int64_t j = 0; j < N; ++j) {
+      double sum = 0.0, sabs = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const double a = e4m3_table[A[i * lda + k]] * mx_scale(SA[i * ldsa + k / 32]);
+        const double b = e4m3_table[B[j * ldb + k]] * mx_scale(SB[j * ldsb + k / 32]);
+        sum += a * b;
+        sabs += fabs(a * b);
+      }
+      double v = alpha * sum;
+      if (beta != 0.0) v += beta * c_value(C, i * ldc + j, c_fmt);
+      acc[j] = v;
+      if (sab) sab[j] = sabs;
+    }
+  }
+  return bad ? -1 : 0;
+}
+
 /* Bulk helpers for the Python wrapper. */
 void oracle_decode(int fmt, const void* bits, int64_t n, double* out) {
   init_tables();

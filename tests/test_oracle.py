@@ -294,3 +294,134 @@ def test_tolerance_helper_accepts_rounded_and_rejects_wrong():
     assert tolerance.check(good32, "f32", R, S, g.K)["ok"]
     bad32 = oracle.round_f32(R * (1 + 1e-4))
     assert not tolerance.check(bad32, "f32", R, S, g.K)["ok"]
+
+
+# ---------------------------------------------------------------- block-scaled E4M3 (MXFP8)
+
+def _golden_mx():
+    vals = {}
+    for line in open(os.path.join(GOLDEN, "worked_mx.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            k, *rest = line.split()
+            vals[k] = rest
+    return vals
+
+
+def _expand(spec):
+    out = []
+    for item in spec:
+        n, code = item.split("x")
+        out += [int(code, 16)] * int(n)
+    return np.array(out, dtype=np.uint8)
+
+
+def test_mx_worked_example():
+    v = _golden_mx()
+    K = int(v["K"][0])
+    A, B = _expand(v["A"])[None, :], _expand(v["B"])[None, :]
+    SA = np.array([int(x) for x in v["SA"]], np.uint8)[None, :]
+    SB = np.array([int(x) for x in v["SB"]], np.uint8)[None, :]
+    R, S = oracle.gemm_mx(1, 1, K, 1.0, A, K, SA, 2, B, K, SB, 2, 0.0, None, 1, oracle.C_F32)
+    assert R[0, 0] == float(v["R"][0]) and S[0, 0] == float(v["R"][0])
+
+
+def _finite_e4m3_codes(rng, shape):
+    c = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x38  # no NaN codes
+    return c
+
+
+def test_mx_unit_scales_equal_plain_e4m3():
+    """Scale byte 127 is x1: the block-scaled product equals the (pinned) plain E4M3 GEMM
+    with B stored [N][K] (transB = 1), bit for bit, R and S."""
+    rng = np.random.default_rng(11)
+    M, N, K = 9, 7, 100
+    A, B = _finite_e4m3_codes(rng, (M, K)), _finite_e4m3_codes(rng, (N, K))
+    one = lambda r: np.full((r, 4), 127, np.uint8)
+    C = gi.f32_to_bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    R1, S1 = oracle.gemm_mx(M, N, K, 0.75, A, K, one(M), 4, B, K, one(N), 4, -2.0, C, N, oracle.C_BF16)
+    R2, S2 = oracle.gemm(0, 1, M, N, K, 0.75, A, K, B, K, -2.0, C, N, oracle.IN_E4M3, oracle.C_BF16)
+    assert np.array_equal(R1, R2) and np.array_equal(S1, S2)
+
+
+def test_mx_exact_rational_brute_force():
+    """Random codes and scales, summed in Fractions: R within the fp64 summation bound."""
+    rng = np.random.default_rng(12)
+    M, N, K = 3, 4, 70  # three K blocks, the last one partial
+    A, B = _finite_e4m3_codes(rng, (M, K)), _finite_e4m3_codes(rng, (N, K))
+    SA = rng.integers(110, 145, size=(M, 3), dtype=np.uint8)
+    SB = rng.integers(110, 145, size=(N, 3), dtype=np.uint8)
+    R, S = oracle.gemm_mx(M, N, K, 1.0, A, K, SA, 3, B, K, SB, 3, 0.0, None, N, oracle.C_F32)
+    tab = oracle.decode(np.arange(256, dtype=np.uint8), "e4m3")
+    for i in range(M):
+        for j in range(N):
+            ex = sum(Fraction(tab[A[i, k]]) * Fraction(2) ** (int(SA[i, k // 32]) - 127) *
+                     Fraction(tab[B[j, k]]) * Fraction(2) ** (int(SB[j, k // 32]) - 127) for k in range(K))
+            assert abs(R[i, j] - float(ex)) <= K * 2.0 ** -53 * S[i, j]
+
+
+def test_mx_scale_255_is_nan_and_beta_zero_never_reads_c():
+    A = np.full((2, 32), 0x38, np.uint8)
+    B = np.full((2, 32), 0x38, np.uint8)
+    SA = np.array([[127], [255]], np.uint8)
+    SB = np.array([[127], [127]], np.uint8)
+    Cnan = np.full((2, 2), 0x7FC00000, np.uint32)
+    R, _ = oracle.gemm_mx(2, 2, 32, 1.0, A, 32, SA, 1, B, 32, SB, 1, 0.0, Cnan, 2, oracle.C_F32)
+    assert np.all(R[0] == 32.0) and np.all(np.isnan(R[1]))
+
+
+def test_mx_quantize_golden():
+    for line in open(os.path.join(GOLDEN, "mx_quantize.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        xs, e, cs = [part.split() for part in line.split("|")]
+        x = np.array([[float(v) for v in xs]])
+        codes, scales = oracle.quantize_mx(x)
+        assert int(scales[0, 0]) == int(e[0]), line
+        assert [int(c) for c in codes[0]] == [int(c, 16) for c in cs], line
+
+
+def test_mx_quantize_grid_round_trip_and_partial_block():
+    """Every finite E4M3 value times 2^s, in blocks whose amax is in [256, 448), comes back
+    as its own code with scale byte s + 127; a 70-wide row has a 6-element last block."""
+    rng = np.random.default_rng(13)
+    tab = oracle.decode(np.arange(256, dtype=np.uint8), "e4m3")
+    finite = [c for c in range(256) if (c & 0x7F) != 0x7F]
+    for s in (-20, 0, 7):
+        codes = np.array(rng.choice(finite, size=(4, 70)), dtype=np.uint8)
+        codes[:, 0] = 0x7E  # 448 in every block's first slot: amax 448 -> e = 127 + s
+        codes[:, 32] = 0x7E
+        codes[:, 64] = 0x7E
+        x = tab[codes] * 2.0 ** s
+        got, scales = oracle.quantize_mx(x)
+        assert np.all(scales == 127 + s)
+        same = (got == codes) | ((got & 0x7F) == 0) & ((codes & 0x7F) == 0)
+        assert same.all()
+
+
+def test_mx_quantize_matches_library_cast_and_error_bound():
+    """For in-range values the element rounding equals torch's float8_e4m3fn cast (round to
+    nearest even, a library routine) of x / 2^(e-127); the decoded block then lies within
+    half an E4M3 step of x."""
+    import torch
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((6, 96)) * np.exp(rng.uniform(-6, 6, size=(6, 1)))
+    codes, scales = oracle.quantize_mx(x)
+    tab = oracle.decode(np.arange(256, dtype=np.uint8), "e4m3")
+    for i in range(6):
+        for b in range(3):
+            sc = 2.0 ** (int(scales[i, b]) - 127)
+            q = x[i, 32 * b:32 * b + 32] / sc
+            lib = torch.from_numpy(q.astype(np.float64)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            got = codes[i, 32 * b:32 * b + 32]
+            inr = np.abs(q) <= 448.0  # the library cast does not saturate (it gives NaN)
+            assert np.array_equal(lib[inr], got[inr])
+            assert np.all((got[~inr] & 0x7F) == 0x7E)
+            back = tab[got] * sc
+            xb = x[i, 32 * b:32 * b + 32]
+            err = np.abs(back - xb)
+            assert np.all(err[inr] <= np.abs(xb[inr]) * 2.0 ** -4 + sc * 2.0 ** -10)
+            # saturated elements (|q| in (448, 512) by the scale rule) come back as 448
+            assert np.all(np.abs(back[~inr]) == 448.0 * sc) and np.all(np.abs(xb[~inr]) < 512.0 * sc)
