@@ -15,14 +15,15 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdbgemm.so")
 
 OP_N, OP_T = 0, 1
-BF16_F32, BF16_BF16, E4M3_BF16, E4M3_F32 = 0, 1, 2, 3
+BF16_F32, BF16_BF16, E4M3_BF16, E4M3_F32, MXE4M3_BF16, MXE4M3_F32 = 0, 1, 2, 3, 4, 5
 STATUS = {0: "SUCCESS", 1: "INVALID_VALUE", 2: "NOT_SUPPORTED", 3: "NOT_INITIALIZED",
           4: "LAUNCH_FAILED", 5: "INTERNAL"}
 
 # The exported C symbols, in the order include/gemm.h declares them.
-EXPORTS = ["gemm_create", "gemm_destroy", "gemm_set_stream", "gemm_run", "gemm_check_args",
-           "gemm_query_policy", "gemm_set_policy", "gemm_lds_probe", "gemm_policy_count",
-           "gemm_policy_name", "gemm_version", "gemm_status_string"]
+EXPORTS = ["gemm_create", "gemm_destroy", "gemm_set_stream", "gemm_run", "gemm_run_mx",
+           "gemm_quantize_mx", "gemm_check_args", "gemm_query_policy", "gemm_set_policy",
+           "gemm_lds_probe", "gemm_policy_count", "gemm_policy_name", "gemm_version",
+           "gemm_status_string"]
 
 _lib = None
 
@@ -77,6 +78,8 @@ def load_library():
                                       ctypes.c_char_p, ctypes.c_size_t]
     lib.gemm_set_policy.argtypes = [vp, ctypes.c_char_p]
     lib.gemm_lds_probe.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_uint32), i32, i32]
+    lib.gemm_run_mx.argtypes = [vp, i64, i64, i64, f32, vp, i64, vp, i64, vp, i64, vp, i64, f32, vp, i64, i32]
+    lib.gemm_quantize_mx.argtypes = [vp, i64, i64, vp, i64, vp, i64, vp, i64]
     lib.gemm_policy_count.argtypes = []
     lib.gemm_policy_name.argtypes = [i32]
     lib.gemm_policy_name.restype = ctypes.c_char_p
@@ -85,7 +88,8 @@ def load_library():
     lib.gemm_status_string.argtypes = [i32]
     lib.gemm_status_string.restype = ctypes.c_char_p
     for fn in ["gemm_create", "gemm_destroy", "gemm_set_stream", "gemm_run", "gemm_check_args",
-               "gemm_query_policy", "gemm_set_policy", "gemm_lds_probe", "gemm_policy_count"]:
+               "gemm_query_policy", "gemm_set_policy", "gemm_lds_probe", "gemm_policy_count",
+               "gemm_run_mx", "gemm_quantize_mx"]:
         getattr(lib, fn).restype = i32
     _lib = lib
     return lib
@@ -189,6 +193,39 @@ class Gemm:
         if st != 0:
             raise GemmError("gemm_run", st)
         return C
+
+    def run_mx(self, A, SA, B, SB, C, alpha: float = 1.0, beta: float = 0.0):
+        """Block-scaled E4M3 GEMM (gemm_run_mx) on torch tensors: A [M][K] and B [N][K] as
+        float8_e4m3fn (or uint8 codes), SA [M][ceil(K/32)] and SB [N][ceil(K/32)] uint8
+        UE8M0 scales, C bf16 or float32 [M][N]; C <- alpha*A*B^T(scaled) + beta*C."""
+        import torch
+        M, N = C.shape
+        K = A.shape[1]
+        dtype = MXE4M3_F32 if C.dtype == torch.float32 else MXE4M3_BF16
+        stream = _current_stream(C.device)
+        if stream != self._stream:
+            self.set_stream(stream)
+        st = self.lib.gemm_run_mx(self.handle, int(M), int(N), int(K), float(alpha), ctypes.c_void_p(_ptr(A)),
+                                  _ld(A), ctypes.c_void_p(_ptr(SA)), _ld(SA), ctypes.c_void_p(_ptr(B)), _ld(B),
+                                  ctypes.c_void_p(_ptr(SB)), _ld(SB), float(beta), ctypes.c_void_p(_ptr(C)),
+                                  _ld(C), int(dtype))
+        if st != 0:
+            raise GemmError("gemm_run_mx", st)
+        return C
+
+    def quantize_mx(self, src, dst, scales):
+        """bf16 [rows][cols] -> E4M3 codes in dst [rows][cols] (uint8 or float8_e4m3fn) and
+        UE8M0 scales [rows][ceil(cols/32)] (uint8), along rows (gemm_quantize_mx)."""
+        rows, cols = src.shape
+        stream = _current_stream(src.device)
+        if stream != self._stream:
+            self.set_stream(stream)
+        st = self.lib.gemm_quantize_mx(self.handle, int(rows), int(cols), ctypes.c_void_p(_ptr(src)), _ld(src),
+                                       ctypes.c_void_p(_ptr(dst)), _ld(dst), ctypes.c_void_p(_ptr(scales)),
+                                       _ld(scales))
+        if st != 0:
+            raise GemmError("gemm_quantize_mx", st)
+        return dst, scales
 
     def lds_probe(self, kind: int, offsets, iters: int, workgroups: int, stream_ptr: Optional[int] = None):
         """Enqueues the LDS read microbenchmark (gemm_lds_probe); offsets: 8 x 64 byte offsets."""

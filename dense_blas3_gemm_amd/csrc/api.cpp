@@ -41,9 +41,11 @@ bool live(gemm_handle_t h) {
 }
 
 bool valid_op(int op) { return op == GEMM_OP_N || op == GEMM_OP_T; }
-bool valid_dtype(int d) { return d >= GEMM_BF16_F32 && d <= GEMM_E4M3_F32; }
-int in_bytes(int d) { return (d == GEMM_E4M3_BF16 || d == GEMM_E4M3_F32) ? 1 : 2; }
-int out_bytes(int d) { return (d == GEMM_BF16_F32 || d == GEMM_E4M3_F32) ? 4 : 2; }
+bool valid_dtype(int d) { return d >= GEMM_BF16_F32 && d <= GEMM_E4M3_F32; }        // gemm_run
+bool valid_query_dtype(int d) { return d >= GEMM_BF16_F32 && d <= GEMM_MXE4M3_F32; }  // + block-scaled
+bool is_mx(int d) { return d == GEMM_MXE4M3_BF16 || d == GEMM_MXE4M3_F32; }
+int in_bytes(int d) { return (d == GEMM_BF16_F32 || d == GEMM_BF16_BF16) ? 2 : 1; }
+int out_bytes(int d) { return (d == GEMM_BF16_F32 || d == GEMM_E4M3_F32 || d == GEMM_MXE4M3_F32) ? 4 : 2; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -58,6 +60,7 @@ Problem make_problem(int transA, int transB, int64_t M, int64_t N, int64_t K, co
   pr.K = K;
   pr.in_fp8 = in_bytes(dtype) == 1;
   pr.c_f32 = out_bytes(dtype) == 4;
+  pr.mx = is_mx(dtype);
   const int ie = in_bytes(dtype), oe = out_bytes(dtype);
   const int vec = 16 / ie;
   bool ok = aligned16(A) && aligned16(B) && aligned16(C);
@@ -71,6 +74,8 @@ Problem make_problem(int transA, int transB, int64_t M, int64_t N, int64_t K, co
   const double a_rows = (double)(transA ? K : M) + 256.0;
   const double b_rows = (double)(transB ? N : K) + 256.0;
   ok = ok && a_rows * (double)lda * ie < lim && b_rows * (double)ldb * ie < lim;
+  // block-scaled operands: the MFMA kernels take A [M][K] and B [N][K] only
+  if (pr.mx) ok = ok && transA == 0 && transB == 1;
   pr.fast_ok = ok;
   return pr;
 }
@@ -223,7 +228,7 @@ gemm_status_t gemm_query_policy(gemm_handle_t h, int transA, int transB, int64_t
   if (!name || len == 0) return GEMM_STATUS_INVALID_VALUE;
   name[0] = 0;
   if (h && !live(h)) return GEMM_STATUS_NOT_INITIALIZED;
-  if (!valid_op(transA) || !valid_op(transB) || !valid_dtype(dtype)) return GEMM_STATUS_INVALID_VALUE;
+  if (!valid_op(transA) || !valid_op(transB) || !valid_query_dtype(dtype)) return GEMM_STATUS_INVALID_VALUE;
   if (M < 0 || N < 0 || K < 0) return GEMM_STATUS_INVALID_VALUE;
   const Handle* p = reinterpret_cast<const Handle*>(h);
   const Problem pr = make_problem(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, dtype);
@@ -267,16 +272,12 @@ gemm_status_t gemm_lds_probe(gemm_handle_t h, int kind, const uint32_t* offsets,
   return err == hipSuccess ? GEMM_STATUS_SUCCESS : GEMM_STATUS_LAUNCH_FAILED;
 }
 
-gemm_status_t gemm_run(gemm_handle_t h, int transA, int transB, int64_t M, int64_t N, int64_t K,
-                       float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
-                       float beta, void* C, int64_t ldc, int dtype) {
-  if (!live(h)) return GEMM_STATUS_NOT_INITIALIZED;
-  const gemm_status_t st = gemm_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
-                                           ldc, dtype);
-  if (st != GEMM_STATUS_SUCCESS) return st;
+// Shared by gemm_run and gemm_run_mx once the arguments are checked.
+static gemm_status_t run_checked(const Handle* p, int transA, int transB, int64_t M, int64_t N, int64_t K,
+                                 float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+                                 float beta, void* C, int64_t ldc, int dtype, const uint8_t* sa,
+                                 int64_t ldsa, const uint8_t* sb, int64_t ldsb) {
   if (M == 0 || N == 0) return GEMM_STATUS_SUCCESS;
-  const Handle* p = reinterpret_cast<const Handle*>(h);
-
   GemmArgs a{};
   a.A = A;
   a.B = B;
@@ -294,6 +295,11 @@ gemm_status_t gemm_run(gemm_handle_t h, int transA, int transB, int64_t M, int64
   a.transA = transA;
   a.transB = transB;
   a.splits = 1;
+  a.mx = is_mx(dtype);
+  a.sa = sa;
+  a.sb = sb;
+  a.ldsa = ldsa;
+  a.ldsb = ldsb;
 
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess) return GEMM_STATUS_INTERNAL;
@@ -339,6 +345,56 @@ gemm_status_t gemm_run(gemm_handle_t h, int transA, int transB, int64_t M, int64
   if (cur != p->device) (void)hipSetDevice(cur);
   if (err != hipSuccess) return GEMM_STATUS_LAUNCH_FAILED;
   return GEMM_STATUS_SUCCESS;
+}
+
+gemm_status_t gemm_run(gemm_handle_t h, int transA, int transB, int64_t M, int64_t N, int64_t K,
+                       float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+                       float beta, void* C, int64_t ldc, int dtype) {
+  if (!live(h)) return GEMM_STATUS_NOT_INITIALIZED;
+  const gemm_status_t st = gemm_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                           ldc, dtype);
+  if (st != GEMM_STATUS_SUCCESS) return st;
+  return run_checked(reinterpret_cast<const Handle*>(h), transA, transB, M, N, K, alpha, A, lda, B, ldb,
+                     beta, C, ldc, dtype, nullptr, 0, nullptr, 0);
+}
+
+gemm_status_t gemm_run_mx(gemm_handle_t h, int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+                          int64_t lda, const uint8_t* scale_a, int64_t ld_scale_a, const void* B,
+                          int64_t ldb, const uint8_t* scale_b, int64_t ld_scale_b, float beta, void* C,
+                          int64_t ldc, int dtype) {
+  if (!live(h)) return GEMM_STATUS_NOT_INITIALIZED;
+  if (!is_mx(dtype)) return GEMM_STATUS_INVALID_VALUE;
+  // the operand checks of gemm_run with the E4M3 dtype of the same C type
+  const int plain = dtype == GEMM_MXE4M3_F32 ? GEMM_E4M3_F32 : GEMM_E4M3_BF16;
+  const gemm_status_t st = gemm_check_args(GEMM_OP_N, GEMM_OP_T, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                           ldc, plain);
+  if (st != GEMM_STATUS_SUCCESS) return st;
+  const int64_t nb = (K + 31) / 32;
+  if (ld_scale_a < (nb > 1 ? nb : 1) || ld_scale_b < (nb > 1 ? nb : 1)) return GEMM_STATUS_INVALID_VALUE;
+  if (M > 0 && N > 0 && K > 0 && alpha != 0.f && (!scale_a || !scale_b)) return GEMM_STATUS_INVALID_VALUE;
+  // 32-bit offsets into the scale arrays
+  if ((double)M * (double)ld_scale_a >= 2147483647.0 || (double)N * (double)ld_scale_b >= 2147483647.0)
+    return GEMM_STATUS_NOT_SUPPORTED;
+  return run_checked(reinterpret_cast<const Handle*>(h), GEMM_OP_N, GEMM_OP_T, M, N, K, alpha, A, lda, B,
+                     ldb, beta, C, ldc, dtype, scale_a, ld_scale_a, scale_b, ld_scale_b);
+}
+
+gemm_status_t gemm_quantize_mx(gemm_handle_t h, int64_t rows, int64_t cols, const void* src, int64_t ld_src,
+                               void* dst, int64_t ld_dst, uint8_t* scales, int64_t ld_scales) {
+  if (!live(h)) return GEMM_STATUS_NOT_INITIALIZED;
+  if (rows < 0 || cols < 0) return GEMM_STATUS_INVALID_VALUE;
+  const int64_t nb = (cols + 31) / 32;
+  if (ld_src < (cols > 1 ? cols : 1) || ld_dst < (cols > 1 ? cols : 1) || ld_scales < (nb > 1 ? nb : 1))
+    return GEMM_STATUS_INVALID_VALUE;
+  if (rows == 0 || cols == 0) return GEMM_STATUS_SUCCESS;
+  if (!src || !dst || !scales) return GEMM_STATUS_INVALID_VALUE;
+  const Handle* p = reinterpret_cast<const Handle*>(h);
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return GEMM_STATUS_INTERNAL;
+  if (cur != p->device && hipSetDevice(p->device) != hipSuccess) return GEMM_STATUS_INTERNAL;
+  const hipError_t err = launch_quantize_mx(rows, cols, src, ld_src, dst, ld_dst, scales, ld_scales, p->stream);
+  if (cur != p->device) (void)hipSetDevice(cur);
+  return err == hipSuccess ? GEMM_STATUS_SUCCESS : GEMM_STATUS_LAUNCH_FAILED;
 }
 
 }  // extern "C"

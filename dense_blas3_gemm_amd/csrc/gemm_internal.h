@@ -34,6 +34,12 @@ struct GemmArgs {
   int splits;
   int kt_per_split;
   float* ws;
+  // Block-scaled E4M3 (mx = 1): one UE8M0 byte per row and 32-element K block, for A
+  // (rows m) in sa[m * ldsa + k / 32] and for B (rows n) in sb[n * ldsb + k / 32].
+  int mx;
+  const uint8_t* sa;
+  const uint8_t* sb;
+  int64_t ldsa, ldsb;
 };
 
 enum PolicyKind { KIND_SIMT = 0, KIND_MFMA = 1, KIND_SCALE = 2 };
@@ -43,7 +49,8 @@ struct Policy {
   int kind;
   int pipe;        // 0: global -> registers -> LDS (two stages); 1: direct-to-LDS loads
   int in_mode;     // 0: bf16 in, bf16 MFMA; 1: E4M3 in, widened to bf16 in LDS (exact
-                   // fp32 accumulation); 2: E4M3 in, native f8f6f4 MFMA; -1: any (generic)
+                   // fp32 accumulation); 2: E4M3 in, native f8f6f4 MFMA; 3: block-scaled
+                   // E4M3 (MXFP8), widened with its scale; -1: any (generic)
   int BM, BN, BK;  // workgroup tile
   int WM, WN;      // waves along M and N
   int MT;          // MFMA block edge (32 or 16)
@@ -75,6 +82,11 @@ constexpr int kLdsProbeBytes = 65536;
 int lds_probe_width(int kind);  // bytes per lane of read kind 0..3, 0 for an unknown kind
 hipError_t launch_lds_probe(int kind, const LdsProbeOffsets& offs, int iters, int workgroups, hipStream_t s);
 
+// bf16 [rows][ld_src] -> E4M3 [rows][ld_dst] plus one UE8M0 byte per 32 elements of a row
+// in scales [rows][ld_scales] (the MXFP8 quantisation; see gemm_quantize_mx).
+hipError_t launch_quantize_mx(int64_t rows, int64_t cols, const void* src, int64_t ld_src, void* dst,
+                              int64_t ld_dst, uint8_t* scales, int64_t ld_scales, hipStream_t s);
+
 // Tile-policy table.
 int policy_count();
 const Policy& policy_at(int i);
@@ -84,6 +96,7 @@ struct Problem {
   int transA, transB;
   int64_t M, N, K;
   int in_fp8, c_f32;
+  int mx;        // block-scaled E4M3 operands (gemm_run_mx)
   bool fast_ok;  // alignment / divisibility allow the MFMA kernels
 };
 // Shape-driven selection; returns an index into the table and, in *splits, the

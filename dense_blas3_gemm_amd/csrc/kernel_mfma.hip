@@ -99,6 +99,13 @@ __global__ __launch_bounds__(C::THREADS) void gemm_mfma_kernel(GemmArgs a) {
   const uint32_t b_kstep = C::B_KC ? C::BK * C::GES : (uint32_t)(C::BK * a.ldb * C::GES);
 
   i32x4 a_reg[C::A_CH], b_reg[C::B_CH];
+  // block-scaled E4M3: the UE8M0 byte of each chunk (a 16-element chunk of a row lies in
+  // one 32-element block); both operands are K-contiguous here
+  constexpr bool MX = C::IN == IN_MX;
+  static_assert(!MX || (C::A_KC && C::B_KC && C::VEC == 16), "block-scaled operands are K-contiguous E4M3");
+  uint32_t a_sc[MX ? C::A_CH : 1], b_sc[MX ? C::B_CH : 1];
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(MX ? a.sa : nullptr, MX ? (uint32_t)(a.M * a.ldsa) : 0u);
+  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(MX ? a.sb : nullptr, MX ? (uint32_t)(a.N * a.ldsb) : 0u);
 
   auto global_load = [&](int kt) {
     const int k0 = kt * C::BK;
@@ -108,6 +115,10 @@ __global__ __launch_bounds__(C::THREADS) void gemm_mfma_kernel(GemmArgs a) {
       const bool ok = a_fixed_ok[i] & (C::A_KC ? (k0 + a_c * C::VEC < a.K) : (k0 + r < a.K));
       const uint32_t off = ok ? a_goff[i] + (uint32_t)kt * a_kstep : kOOB;
       a_reg[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
+      if constexpr (MX) {
+        const uint32_t so = ok ? (uint32_t)((m0 + r) * a.ldsa + (k0 + a_c * C::VEC) / 32) : kOOB;
+        a_sc[i] = __builtin_amdgcn_raw_buffer_load_b8(rsa, so, 0, 0);
+      }
     }
 #pragma unroll
     for (int i = 0; i < C::B_CH; ++i) {
@@ -115,14 +126,18 @@ __global__ __launch_bounds__(C::THREADS) void gemm_mfma_kernel(GemmArgs a) {
       const bool ok = b_fixed_ok[i] & (C::B_KC ? (k0 + b_c * C::VEC < a.K) : (k0 + r < a.K));
       const uint32_t off = ok ? b_goff[i] + (uint32_t)kt * b_kstep : kOOB;
       b_reg[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+      if constexpr (MX) {
+        const uint32_t so = ok ? (uint32_t)((n0 + r) * a.ldsb + (k0 + b_c * C::VEC) / 32) : kOOB;
+        b_sc[i] = __builtin_amdgcn_raw_buffer_load_b8(rsb, so, 0, 0);
+      }
     }
   };
   lds_char* const sm = (lds_char*)smem;
   auto lds_store_to = [&](lds_char* sbase) {
 #pragma unroll
-    for (int i = 0; i < C::A_CH; ++i) put_chunk<C>(sbase, a_soff[i], a_reg[i]);
+    for (int i = 0; i < C::A_CH; ++i) put_chunk<C>(sbase, a_soff[i], a_reg[i], MX ? ue8m0_value(a_sc[i]) : 1.0f);
 #pragma unroll
-    for (int i = 0; i < C::B_CH; ++i) put_chunk<C>(sbase, b_soff[i], b_reg[i]);
+    for (int i = 0; i < C::B_CH; ++i) put_chunk<C>(sbase, b_soff[i], b_reg[i], MX ? ue8m0_value(b_sc[i]) : 1.0f);
   };
   auto lds_store = [&](int stage) { lds_store_to(sm + stage * C::STAGE_BYTES); };
 
@@ -195,11 +210,16 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 template <int BM, int BN, int BK, int WM, int WN, int MT, int ST, int IN>
 hipError_t launch_trans(const GemmArgs& a, hipStream_t s) {
   const int code = a.transA * 2 + a.transB;
-  switch (code) {
-    case 0: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, false, false>>(a, s);
-    case 1: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, false, true>>(a, s);
-    case 2: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, true, false>>(a, s);
-    default: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, true, true>>(a, s);
+  if constexpr (IN == IN_MX) {  // block-scaled operands: A [M][K] and B [N][K] only
+    if (code != 1) return hipErrorInvalidConfiguration;
+    return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, false, true>>(a, s);
+  } else {
+    switch (code) {
+      case 0: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, false, false>>(a, s);
+      case 1: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, false, true>>(a, s);
+      case 2: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, true, false>>(a, s);
+      default: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, true, true>>(a, s);
+    }
   }
 }
 

@@ -22,6 +22,11 @@ __device__ inline float load_in(const void* p, int64_t idx, int fp8) {
   return fp8 ? e4m3_to_f32(((const uint8_t*)p)[idx]) : bf16_to_f32(((const uint16_t*)p)[idx]);
 }
 
+// UE8M0 byte -> 2^(e-127) in fp32 (255 is NaN, 0 is the subnormal 2^-127).
+__device__ inline float ue8m0_to_f32(uint8_t e) {
+  return e == 255 ? __builtin_nanf("") : __builtin_bit_cast(float, e == 0 ? 0x00400000u : (uint32_t)e << 23);
+}
+
 __device__ inline float load_c(const void* p, int64_t idx, int f32) {
   return f32 ? ((const float*)p)[idx] : bf16_to_f32(((const uint16_t*)p)[idx]);
 }
@@ -49,10 +54,14 @@ __global__ __launch_bounds__(256) void gemm_simt_kernel(GemmArgs a) {
       const int kk = e / TS, x = e % TS;
       const int k = k0 + kk, m = m0 + x, n = n0 + x;
       float av = 0.f, bv = 0.f;
-      if (k < a.K && m < a.M)
+      if (k < a.K && m < a.M) {
         av = load_in(a.A, a.transA ? (int64_t)k * a.lda + m : (int64_t)m * a.lda + k, a.in_fp8);
-      if (k < a.K && n < a.N)
+        if (a.mx) av *= ue8m0_to_f32(a.sa[(int64_t)m * a.ldsa + k / 32]);
+      }
+      if (k < a.K && n < a.N) {
         bv = load_in(a.B, a.transB ? (int64_t)n * a.ldb + k : (int64_t)k * a.ldb + n, a.in_fp8);
+        if (a.mx) bv *= ue8m0_to_f32(a.sb[(int64_t)n * a.ldsb + k / 32]);
+      }
       As[kk][x] = av;
       Bs[kk][x] = bv;
     }

@@ -61,8 +61,9 @@ __device__ inline void tile_of(int bid, const GemmArgs& a, int& tm, int& tn, int
 
 // Input modes: IN_BF16 (bf16 operands, bf16 MFMA); IN_E4M3 (E4M3 operands widened
 // exactly to bf16 on their way into LDS, bf16 MFMA: full fp32 accumulation);
-// IN_E4M3_NATIVE (E4M3 operands fed to the f8f6f4 MFMA as they are).
-enum { IN_BF16 = 0, IN_E4M3 = 1, IN_E4M3_NATIVE = 2 };
+// IN_E4M3_NATIVE (E4M3 operands fed to the f8f6f4 MFMA as they are); IN_MX (E4M3
+// operands with a UE8M0 scale per 32 along K, widened to bf16 times their scale).
+enum { IN_BF16 = 0, IN_E4M3 = 1, IN_E4M3_NATIVE = 2, IN_MX = 3 };
 
 // READ_: 1 reads M/N-contiguous fragments with the transposing ds_read_b64_tr_*; 0 reads
 // them one element at a time (ds_read_u16), the plain-load rung of the read ablation.
@@ -288,13 +289,13 @@ __device__ __forceinline__ void interleave() {
 
 // 16 E4M3 values -> 16 bf16 values (exact: every E4M3 number, subnormals included, is
 // a bf16 number) with the gfx950 packed conversion at unit scale.
-__device__ inline void widen_e4m3(const i32x4& v, i32x4& lo, i32x4& hi) {
+__device__ inline void widen_e4m3(const i32x4& v, i32x4& lo, i32x4& hi, float scale = 1.0f) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   int w[8];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    w[2 * d] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[d], 1.0f, false));
-    w[2 * d + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[d], 1.0f, true));
+    w[2 * d] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[d], scale, false));
+    w[2 * d + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[d], scale, true));
   }
   lo = (i32x4){w[0], w[1], w[2], w[3]};
   hi = (i32x4){w[4], w[5], w[6], w[7]};
@@ -303,13 +304,18 @@ __device__ inline void widen_e4m3(const i32x4& v, i32x4& lo, i32x4& hi) {
 // Stores one global chunk into LDS at byte offset `off` (its first LDS chunk).  A
 // widened chunk fills two logically adjacent LDS chunks; under the XOR swizzle their
 // physical positions differ only in bit 4 of the offset.
+// UE8M0 byte -> the fp32 power of two it stands for (255 is NaN; 0 is 2^-127).
+__device__ inline float ue8m0_value(uint32_t e) {
+  return e == 255u ? __builtin_nanf("") : __builtin_bit_cast(float, e == 0u ? 0x00400000u : e << 23);
+}
+
 template <class C>
-__device__ inline void put_chunk(lds_char* sbase, uint32_t off, const i32x4& v) {
+__device__ inline void put_chunk(lds_char* sbase, uint32_t off, const i32x4& v, float scale = 1.0f) {
   if constexpr (C::WIDEN == 1) {
     *LDS_PTR(i32x4, sbase, off) = v;
   } else {
     i32x4 lo, hi;
-    widen_e4m3(v, lo, hi);
+    widen_e4m3(v, lo, hi, scale);
     *LDS_PTR(i32x4, sbase, off) = lo;
     *LDS_PTR(i32x4, sbase, off ^ 16u) = hi;
   }

@@ -192,3 +192,28 @@ def proj_backward_inputs(seed_offset: int = 0) -> Dict[str, np.ndarray]:
         "X": bf16_normal((2048, 5120), 2 + s),
         "dW0": bf16_normal((5120, 5120), 3 + s, std=0.02),
     }
+
+
+# ---------------------------------------------------------------- block-scaled E4M3 operands
+
+def ue8m0_bytes(shape, seed: int, lo: int = 120, hi: int = 134) -> np.ndarray:
+    """Seeded UE8M0 scale bytes, uniform integers in [lo, hi] (2^-7 .. 2^7 around 1)."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(lo, hi + 1, size=shape, dtype=np.int64).astype(np.uint8)
+
+
+def mx_operands(M: int, N: int, K: int, seeds=(0, 1, 2, 3), kind: str = "e4m3"):
+    """Synthetic block-scaled operands: A [M][K] and B [N][K] E4M3 codes (N(0,1) clamped to
+    +-448, or integers in [-8, 8] for kind "int8"), with one scale byte per row and 32
+    elements of K (SA [M][ceil(K/32)], SB [N][ceil(K/32)]) drawn by ue8m0_bytes."""
+    nb = (K + 31) // 32
+    if kind == "int8":
+        A, B = ints((M, K), seeds[0], -8, 8, E4M3), ints((N, K), seeds[1], -8, 8, E4M3)
+    else:
+        A, B = e4m3_normal((M, K), seeds[0]), e4m3_normal((N, K), seeds[1])
+    return {"A": A, "B": B, "SA": ue8m0_bytes((M, nb), seeds[2]), "SB": ue8m0_bytes((N, nb), seeds[3])}
+
+
+# The MXFP8 forward at the E4M3 forward shape (one CP8 rank of S = 128K): A [16384][5120],
+# B stored [N][K] = [5120][5120], C bf16.
+MX_FWD_SHAPE = (16384, 5120, 5120)

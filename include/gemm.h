@@ -68,10 +68,12 @@ typedef enum { GEMM_OP_N = 0, GEMM_OP_T = 1 } gemm_op_t;
 
 /* input dtype -> C dtype; accumulation is always fp32 */
 typedef enum {
-  GEMM_BF16_F32 = 0,  /* bf16 A, B; fp32 C */
-  GEMM_BF16_BF16 = 1, /* bf16 A, B; bf16 C */
-  GEMM_E4M3_BF16 = 2, /* E4M3 A, B; bf16 C */
-  GEMM_E4M3_F32 = 3   /* E4M3 A, B; fp32 C */
+  GEMM_BF16_F32 = 0,    /* bf16 A, B; fp32 C */
+  GEMM_BF16_BF16 = 1,   /* bf16 A, B; bf16 C */
+  GEMM_E4M3_BF16 = 2,   /* E4M3 A, B; bf16 C */
+  GEMM_E4M3_F32 = 3,    /* E4M3 A, B; fp32 C */
+  GEMM_MXE4M3_BF16 = 4, /* block-scaled E4M3 A, B (gemm_run_mx only); bf16 C */
+  GEMM_MXE4M3_F32 = 5   /* block-scaled E4M3 A, B (gemm_run_mx only); fp32 C */
 } gemm_dtype_t;
 
 typedef enum {
@@ -105,12 +107,45 @@ gemm_status_t gemm_run(gemm_handle_t h, int transA, int transB, int64_t M, int64
                        int64_t K, float alpha, const void* A, int64_t lda, const void* B,
                        int64_t ldb, float beta, void* C, int64_t ldc, int dtype);
 
+/* Block-scaled E4M3 ("MXFP8") GEMM: the MXFP8 operands of the fused profile protocol
+ * (section "SM103 MXFP8 QKV weight-quantization diagnostics": E4M3 elements with one
+ * UE8M0 scale per 32 elements along K).  Computes
+ *
+ *   C <- alpha * sum_k (A[m][k] * 2^(sa[m][k/32]-127)) * (B[n][k] * 2^(sb[n][k/32]-127)) + beta*C
+ *
+ * Layout (both operands K-contiguous, the layout whose 32-element blocks are
+ * contiguous): A is E4M3 [M][lda >= K]; B is E4M3 [N][ldb >= K] (op(B) = B^T);
+ * scale_a is one byte per row and block, [M][ld_scale_a >= ceil(K/32)]; scale_b
+ * [N][ld_scale_b >= ceil(K/32)]; C as in gemm_run.  A scale byte e stands for 2^(e-127)
+ * (255 is NaN).  dtype is GEMM_MXE4M3_BF16 or GEMM_MXE4M3_F32 (C's type).  Every scaled
+ * element is widened exactly to bf16 and accumulated in fp32 (scaled values below the
+ * bf16 range lose precision).  Device pointers; errors and special cases as gemm_run;
+ * NOT_SUPPORTED when a scale array spans 2^31 bytes or more. */
+gemm_status_t gemm_run_mx(gemm_handle_t h, int64_t M, int64_t N, int64_t K, float alpha,
+                          const void* A, int64_t lda, const uint8_t* scale_a, int64_t ld_scale_a,
+                          const void* B, int64_t ldb, const uint8_t* scale_b, int64_t ld_scale_b,
+                          float beta, void* C, int64_t ldc, int dtype);
+
+/* Quantises a bf16 matrix to block-scaled E4M3 along its rows (the quantisation step
+ * before the MXFP8 GEMMs in the same section of the profile protocol: amax of each
+ * 32-element group, a UE8M0 scale, E4M3 conversion).  src is bf16 [rows][ld_src >=
+ * cols]; dst receives E4M3 [rows][ld_dst >= cols] and scales one byte per row and
+ * 32-element group [rows][ld_scales >= ceil(cols/32)] (the last group of a row may be
+ * shorter).  Rule (OCP microscaling): e = clamp(floor(log2(amax)) - 8 + 127, 0, 254),
+ * 0 for an all-zero group; element = x / 2^(e-127) rounded to the nearest E4M3 value,
+ * ties to the even code, saturating at +-448; NaN stays NaN and does not set the scale.
+ * Device pointers, enqueued on the handle's stream; writes nothing on an error. */
+gemm_status_t gemm_quantize_mx(gemm_handle_t h, int64_t rows, int64_t cols, const void* src,
+                               int64_t ld_src, void* dst, int64_t ld_dst, uint8_t* scales,
+                               int64_t ld_scales);
+
 /* Validates gemm_run's arguments on the host only (no handle, no device). */
 gemm_status_t gemm_check_args(int transA, int transB, int64_t M, int64_t N, int64_t K,
                               float alpha, const void* A, int64_t lda, const void* B,
                               int64_t ldb, float beta, const void* C, int64_t ldc, int dtype);
 
-/* Writes the name of the policy gemm_run would use for these arguments into
+/* Writes the name of the policy gemm_run (gemm_run_mx for the block-scaled dtypes,
+ * with transA = 0, transB = 1) would use for these arguments into
  * name[len] (NUL-terminated, truncated to fit), with "+sk<S>" appended when the call
  * is split S ways along K.  The pointers are only inspected for alignment.  h may be
  * NULL: then a 256-CU device with a workspace and no forced policy are assumed.

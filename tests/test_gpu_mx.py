@@ -1,0 +1,179 @@
+"""Block-scaled E4M3 (MXFP8) through the C-ABI: the quantiser bit for bit and the GEMM
+against the fp64 oracle (oracle.quantize_mx / oracle.gemm_mx)."""
+import numpy as np
+import pytest
+
+import gemm_inputs as gi
+import oracle
+import tolerance
+from gpu_util import sample_rows
+
+pytestmark = pytest.mark.gpu
+
+MX_POLICIES = ["mxe4m3_m256n256k64_w2x4_mt16_s2", "mxe4m3_m128n128k64_w2x4_mt16_s2",
+               "mxe4m3_m64n64k64_w2x2_mt16_s2", "simt_generic", None]
+
+
+def _dev(bits, dtype=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits))
+    return t.cuda() if dtype is None else t.view(dtype).cuda()
+
+
+def _bf16_input(rows, cols, seed):
+    """bf16 N(0,1) scaled per row by exp(U(-6, 6)), with a few all-zero 32-groups."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols)).astype(np.float32) * np.exp(rng.uniform(-6, 6, (rows, 1))).astype(np.float32)
+    if cols >= 64:
+        x[::3, 32:64] = 0.0
+    return gi.f32_to_bf16_bits(x)
+
+
+def _quantize_gpu(gpu, bits):
+    import torch
+    rows, cols = bits.shape
+    src = _dev(bits.view(np.int16), torch.bfloat16)
+    dst = torch.zeros((rows, cols), dtype=torch.uint8, device="cuda:0")
+    sc = torch.zeros((rows, (cols + 31) // 32), dtype=torch.uint8, device="cuda:0")
+    gpu.quantize_mx(src, dst, sc)
+    torch.cuda.synchronize()
+    return dst.cpu().numpy(), sc.cpu().numpy()
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 1), (3, 31), (7, 33), (64, 70), (129, 256), (40, 1000)])
+def test_quantize_mx_bit_exact(gpu, rows, cols):
+    bits = _bf16_input(rows, cols, rows * 1000 + cols)
+    codes, scales = _quantize_gpu(gpu, bits)
+    want_c, want_s = oracle.quantize_mx(oracle.decode(bits, "bf16"))
+    assert np.array_equal(scales, want_s)
+    assert np.array_equal(codes, want_c)
+
+
+def test_quantize_mx_extremes(gpu):
+    """Saturation (|x| / scale in (448, 512)), ties, bf16 subnormals and huge values."""
+    vals = np.array([[480.0, 1.0, 1.0625, 1.1875, -3.0e38, 2.0 ** -133, 0.0, -0.0] * 4,
+                     [2.0 ** -130, 2.0 ** -133, 0.0, 0.0] * 8,
+                     [300.0, 288.0, 320.0, 304.0, -304.0, 0.5, 2.0 ** -12, 7.0] * 4], dtype=np.float32)
+    bits = gi.f32_to_bf16_bits(vals)
+    codes, scales = _quantize_gpu(gpu, bits)
+    want_c, want_s = oracle.quantize_mx(oracle.decode(bits, "bf16"))
+    assert np.array_equal(scales, want_s)
+    assert np.array_equal(codes, want_c)
+
+
+def _run_mx(gpu, data, M, N, K, alpha=1.0, beta=0.0, c_dtype="bf16", C0=None, policy=None):
+    import torch
+    A = _dev(data["A"], torch.float8_e4m3fn)
+    B = _dev(data["B"], torch.float8_e4m3fn)
+    SA, SB = _dev(data["SA"]), _dev(data["SB"])
+    dt = torch.float32 if c_dtype == "f32" else torch.bfloat16
+    if C0 is not None:
+        C = _dev(C0.view(np.int16) if c_dtype == "bf16" else C0.view(np.float32), dt if c_dtype == "bf16" else None)
+    else:
+        C = torch.full((M, N), float("nan"), dtype=dt, device="cuda:0")
+    gpu.set_policy(policy)
+    try:
+        gpu.run_mx(A, SA, B, SB, C, alpha=alpha, beta=beta)
+    finally:
+        gpu.set_policy(None)
+    torch.cuda.synchronize()
+    out = C.cpu()
+    return out.view(torch.int16).numpy().view(np.uint16) if c_dtype == "bf16" else out.numpy().view(np.uint32)
+
+
+def _oracle_mx(data, M, N, K, alpha, beta, c_dtype, C0, rows=None):
+    nb = (K + 31) // 32
+    return oracle.gemm_mx(M, N, K, alpha, data["A"], K, data["SA"], nb, data["B"], K, data["SB"], nb, beta,
+                          C0, N, oracle.C_F32 if c_dtype == "f32" else oracle.C_BF16, rows=rows)
+
+
+@pytest.mark.parametrize("policy", MX_POLICIES)
+@pytest.mark.parametrize("c_dtype", ["bf16", "f32"])
+def test_run_mx_parity(gpu, policy, c_dtype):
+    """K = 1008: 32 scale blocks, the last one half full; alpha and beta both visible."""
+    M, N, K = 328, 296, 1008
+    data = gi.mx_operands(M, N, K, seeds=(5, 6, 7, 8))
+    rng = np.random.default_rng(9)
+    c = rng.standard_normal((M, N)).astype(np.float32)
+    C0 = gi.f32_to_bf16_bits(c) if c_dtype == "bf16" else gi.f32_bits(c)
+    got = _run_mx(gpu, data, M, N, K, 1.5, -0.5, c_dtype, C0, policy)
+    R, S = _oracle_mx(data, M, N, K, 1.5, -0.5, c_dtype, C0)
+    res = tolerance.check(got, c_dtype, R, S, K)
+    assert res["ok"], res
+
+
+@pytest.mark.parametrize("c_dtype", ["bf16", "f32"])
+def test_run_mx_integer_bitwise(gpu, c_dtype):
+    """Integer elements with scales 2^-2 .. 2^2 keep every product and partial sum exact."""
+    M, N, K = 264, 200, 520
+    d = gi.mx_operands(M, N, K, seeds=(1, 2, 3, 4), kind="int8")
+    d["SA"] = gi.ue8m0_bytes(d["SA"].shape, 3, 125, 129)
+    d["SB"] = gi.ue8m0_bytes(d["SB"].shape, 4, 125, 129)
+    got = _run_mx(gpu, d, M, N, K, c_dtype=c_dtype)
+    R, _ = _oracle_mx(d, M, N, K, 1.0, 0.0, c_dtype, None)
+    want = oracle.round_bf16(R) if c_dtype == "bf16" else oracle.round_f32(R)
+    assert np.array_equal(got, want)
+
+
+def test_run_mx_unit_scales_match_plain_e4m3(gpu):
+    """Scale bytes 127 everywhere: the block-scaled call gives the plain E4M3 GEMM's bits."""
+    import torch
+    M, N, K = 256, 192, 384
+    d = gi.mx_operands(M, N, K, seeds=(3, 4, 5, 6))
+    d["SA"][:] = 127
+    d["SB"][:] = 127
+    got = _run_mx(gpu, d, M, N, K, c_dtype="f32", policy="mxe4m3_m128n128k64_w2x4_mt16_s2")
+    A = _dev(d["A"], torch.float8_e4m3fn)
+    B = _dev(d["B"], torch.float8_e4m3fn)
+    C = torch.zeros((M, N), dtype=torch.float32, device="cuda:0")
+    gpu.set_policy("e4m3_m128n128k64_w2x4_mt16_s2")  # the same tile and MFMA, unit scale
+    try:
+        gpu(A, B, C, transB=1)
+    finally:
+        gpu.set_policy(None)
+    torch.cuda.synchronize()
+    assert np.array_equal(got, C.cpu().numpy().view(np.uint32))
+
+
+def test_run_mx_odd_k_runs_generic(gpu):
+    """K not a multiple of 16 (E4M3 chunks): the shape-driven choice is the generic kernel."""
+    M, N, K = 70, 50, 1000
+    d = gi.mx_operands(M, N, K, seeds=(9, 8, 7, 6))
+    assert gpu.query_policy(M, N, K, transB=1, dtype=4) == "simt_generic"
+    got = _run_mx(gpu, d, M, N, K)
+    R, S = _oracle_mx(d, M, N, K, 1.0, 0.0, "bf16", None)
+    res = tolerance.check(got, "bf16", R, S, K)
+    assert res["ok"], res
+
+
+def test_run_mx_argument_errors(gpu):
+    import ctypes
+    import dense_blas3_gemm_amd as d
+    lib = d.load_library()
+    p = ctypes.c_void_p(0x1000)
+    # ld of the scales below ceil(K/32), a missing scale array, a non-MX dtype
+    assert lib.gemm_run_mx(gpu.handle, 64, 64, 64, 1.0, p, 64, p, 1, p, 64, p, 2, 0.0, p, 64, 4) == 1
+    assert lib.gemm_run_mx(gpu.handle, 64, 64, 64, 1.0, p, 64, None, 2, p, 64, p, 2, 0.0, p, 64, 4) == 1
+    assert lib.gemm_run_mx(gpu.handle, 64, 64, 64, 1.0, p, 64, p, 2, p, 64, p, 2, 0.0, p, 64, 2) == 1
+    assert lib.gemm_run(gpu.handle, 0, 1, 64, 64, 64, 1.0, p, 64, p, 64, 0.0, p, 64, 4) == 1
+    assert lib.gemm_quantize_mx(gpu.handle, 4, 64, p, 32, p, 64, p, 2) == 1  # ld_src < cols
+
+
+@pytest.mark.slow
+def test_mx_forward_full_size(gpu):
+    """16384 x 5120 x 5120 with bf16 C: sampled rows of every M tile against the oracle,
+    and the quantiser on sampled rows of a bf16 matrix of the same size."""
+    import torch
+    M, N, K = gi.MX_FWD_SHAPE
+    d = gi.mx_operands(M, N, K, seeds=(0, 1, 2, 3))
+    got = _run_mx(gpu, d, M, N, K)
+    assert np.isfinite(tolerance.bf16_bits_to_f64(got)).all()
+    rows = sample_rows(M, per_tile=0, cap=16)
+    R, S = _oracle_mx(d, M, N, K, 1.0, 0.0, "bf16", None, rows=rows)
+    res = tolerance.check(got[rows], "bf16", R, S, K)
+    assert res["ok"], res
+    bits = gi.bf16_normal((M, K), 0)
+    codes, scales = _quantize_gpu(gpu, bits)
+    qr = sample_rows(M, per_tile=0, cap=8)
+    want_c, want_s = oracle.quantize_mx(oracle.decode(bits[qr], "bf16"))
+    assert np.array_equal(scales[qr], want_s) and np.array_equal(codes[qr], want_c)
