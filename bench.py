@@ -15,8 +15,8 @@ each, p50/p95) and prints a Markdown table to stderr; the JSON line is unchanged
 --ablation times every applicable policy on the headline and the E4M3 workloads.
 --ladder runs the ablation ladder (one variable per rung: global->LDS path and LDS stages,
 LDS->register reads, B layout, swizzle) on three K values and a K x M/N heat map, and
---lds-probe the load-only LDS read microbenchmark; both print Markdown to stderr and
-exit without the JSON line.
+--lds-probe the load-only LDS read microbenchmark, --mx the MXFP8 quantiser and GEMM at
+the E4M3 forward shape; these print to stderr and exit without the JSON line.
 --policy / --workload pin the policy or pick another workload for the timed steps
 (used for profiling single kernels); the JSON line then names them in `config`.
 --copy-calibration N runs only a plain device-to-device copy of N MiB (the known-size
@@ -333,6 +333,46 @@ def lds_probe(g, iters: int = 512, workgroups: int = 1024, reps: int = 5):
     return rows
 
 
+def mx_bench(g, warmup: int = 5, steps: int = 30):
+    """Block-scaled E4M3 at the E4M3 forward shape: the quantiser on a bf16 [16384][5120]
+    matrix (HBM bytes/s) and gemm_run_mx 16384 x 5120 x 5120 (TFLOP/s).  Returns a dict."""
+    import torch
+    M, N, K = gi.MX_FWD_SHAPE
+    stream = torch.cuda.current_stream()
+    src = _dev(gi.bf16_normal((M, K), 0), "bf16")
+    dst = torch.empty((M, K), dtype=torch.uint8, device="cuda:0")
+    sc = torch.empty((M, (K + 31) // 32), dtype=torch.uint8, device="cuda:0")
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ev])
+    q_ms = timed(lambda: g.quantize_mx(src, dst, sc))
+    q_bytes = M * K * 2 + M * K + M * ((K + 31) // 32)
+    d = gi.mx_operands(M, N, K, seeds=(0, 1, 2, 3))
+    A, B = _dev(d["A"], "e4m3"), _dev(d["B"], "e4m3")
+    SA = torch.from_numpy(d["SA"]).cuda()
+    SB = torch.from_numpy(d["SB"]).cuda()
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    g_ms = timed(lambda: g.run_mx(A, SA, B, SB, C))
+    flops = 2.0 * M * N * K
+    qp50, gp50 = float(np.percentile(q_ms, 50)), float(np.percentile(g_ms, 50))
+    out = {"quantize_us_p50": round(qp50 * 1e3, 1), "quantize_GBps": round(q_bytes / (qp50 * 1e-3) / 1e9, 1),
+           "quantize_frac_hbm": round(q_bytes / (qp50 * 1e-3) / 1e9 / HBM_GBS, 3),
+           "gemm_us_p50": round(gp50 * 1e3, 1), "gemm_tflops": round(flops / (gp50 * 1e-3) / 1e12, 1),
+           "gemm_frac_bf16_peak": round(flops / (gp50 * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+           "policy": g.query_policy(M, N, K, 0, 1, 4)}
+    print("MXFP8 at 16384 x 5120 x 5120: " + json.dumps(out), file=sys.stderr)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -347,6 +387,7 @@ def main():
     ap.add_argument("--ladder-quick", action="store_true",
                     help="with --ladder: 4096^3 only, one round (3 + 20 calls per rung, in order)")
     ap.add_argument("--lds-probe", action="store_true", help="run the LDS read microbenchmark and exit")
+    ap.add_argument("--mx", action="store_true", help="time the MXFP8 quantiser and GEMM and exit")
     ap.add_argument("--policy", default=None, help="force a named policy for the timed steps")
     ap.add_argument("--workload", default=gi.SQUARE_4096.name, choices=sorted(gi.BY_NAME))
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
@@ -372,7 +413,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": args.warmup + args.steps}))
         return
     g = d.Gemm(0)
-    if args.ladder or args.lds_probe:
+    if args.ladder or args.lds_probe or args.mx:
+        if args.mx:
+            mx_bench(g)
         if args.lds_probe:
             lds_probe(g)
         if args.ladder:

@@ -103,7 +103,20 @@ __global__ __launch_bounds__(C::THREADS) void gemm_mfma_kernel(GemmArgs a) {
   // one 32-element block); both operands are K-contiguous here
   constexpr bool MX = C::IN == IN_MX;
   static_assert(!MX || (C::A_KC && C::B_KC && C::VEC == 16), "block-scaled operands are K-contiguous E4M3");
-  uint32_t a_sc[MX ? C::A_CH : 1], b_sc[MX ? C::B_CH : 1];
+  static_assert(!MX || C::A_CH + C::B_CH <= 4, "scale bytes of a tile fit one register");
+  static_assert(!MX || C::BK % 32 == 0, "whole scale blocks per K tile");
+  uint32_t sc_packed = 0;  // byte i: scale of A chunk i, then of B chunk i - A_CH
+  // byte offsets of this thread's scale bytes in K tile 0 (32-bit: the host keeps each
+  // scale array below 2^31 bytes); K tile kt adds kt * BK / 32
+  uint32_t a_sco[MX ? C::A_CH : 1], b_sco[MX ? C::B_CH : 1];
+  if constexpr (MX) {
+#pragma unroll
+    for (int i = 0; i < C::A_CH; ++i)
+      a_sco[i] = (uint32_t)(m0 + a_r0 + i * A_RSTEP) * (uint32_t)a.ldsa + (uint32_t)(a_c * C::VEC / 32);
+#pragma unroll
+    for (int i = 0; i < C::B_CH; ++i)
+      b_sco[i] = (uint32_t)(n0 + b_r0 + i * B_RSTEP) * (uint32_t)a.ldsb + (uint32_t)(b_c * C::VEC / 32);
+  }
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc(MX ? a.sa : nullptr, MX ? (uint32_t)(a.M * a.ldsa) : 0u);
   const __amdgpu_buffer_rsrc_t rsb = make_rsrc(MX ? a.sb : nullptr, MX ? (uint32_t)(a.N * a.ldsb) : 0u);
 
@@ -116,8 +129,9 @@ __global__ __launch_bounds__(C::THREADS) void gemm_mfma_kernel(GemmArgs a) {
       const uint32_t off = ok ? a_goff[i] + (uint32_t)kt * a_kstep : kOOB;
       a_reg[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
       if constexpr (MX) {
-        const uint32_t so = ok ? (uint32_t)((m0 + r) * a.ldsa + (k0 + a_c * C::VEC) / 32) : kOOB;
-        a_sc[i] = __builtin_amdgcn_raw_buffer_load_b8(rsa, so, 0, 0);
+        const uint32_t so = ok ? a_sco[i] + (uint32_t)(kt * (C::BK / 32)) : kOOB;
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b8(rsa, so, 0, 0);
+        sc_packed = i == 0 ? v : (sc_packed | (v << (8 * i)));
       }
     }
 #pragma unroll
@@ -127,17 +141,20 @@ __global__ __launch_bounds__(C::THREADS) void gemm_mfma_kernel(GemmArgs a) {
       const uint32_t off = ok ? b_goff[i] + (uint32_t)kt * b_kstep : kOOB;
       b_reg[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
       if constexpr (MX) {
-        const uint32_t so = ok ? (uint32_t)((n0 + r) * a.ldsb + (k0 + b_c * C::VEC) / 32) : kOOB;
-        b_sc[i] = __builtin_amdgcn_raw_buffer_load_b8(rsb, so, 0, 0);
+        const uint32_t so = ok ? b_sco[i] + (uint32_t)(kt * (C::BK / 32)) : kOOB;
+        sc_packed |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rsb, so, 0, 0) << (8 * (C::A_CH + i));
       }
     }
   };
   lds_char* const sm = (lds_char*)smem;
   auto lds_store_to = [&](lds_char* sbase) {
 #pragma unroll
-    for (int i = 0; i < C::A_CH; ++i) put_chunk<C>(sbase, a_soff[i], a_reg[i], MX ? ue8m0_value(a_sc[i]) : 1.0f);
+    for (int i = 0; i < C::A_CH; ++i)
+      put_chunk<C>(sbase, a_soff[i], a_reg[i], MX ? ue8m0_value((sc_packed >> (8 * i)) & 0xFFu) : 1.0f);
 #pragma unroll
-    for (int i = 0; i < C::B_CH; ++i) put_chunk<C>(sbase, b_soff[i], b_reg[i], MX ? ue8m0_value(b_sc[i]) : 1.0f);
+    for (int i = 0; i < C::B_CH; ++i)
+      put_chunk<C>(sbase, b_soff[i], b_reg[i],
+                   MX ? ue8m0_value((sc_packed >> (8 * (C::A_CH + i))) & 0xFFu) : 1.0f);
   };
   auto lds_store = [&](int stage) { lds_store_to(sm + stage * C::STAGE_BYTES); };
 
@@ -188,7 +205,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_mfma_kernel(GemmArgs a) {
         for (int j = 0; j < C::FN; ++j) mma(acc[i][j], fb[kk & 1][j], fa[kk & 1][i]);
       constexpr int nmf = C::FM * C::FN;
       constexpr int nds = kk + 1 < C::KSTEPS ? C::DS_READS_PER_STEP : 0;
-      constexpr int nvm = kk == 0 ? C::A_CH + C::B_CH : 0;
+      constexpr int nvm = kk == 0 ? (C::A_CH + C::B_CH) * (MX ? 2 : 1) : 0;  // + the scale bytes
       constexpr int ndw = kk + 1 < C::KSTEPS ? 0 : (C::A_CH + C::B_CH) * C::WIDEN;
       interleave<nmf, nds, nvm, ndw>();
       __builtin_amdgcn_sched_barrier(0);  // nothing crosses a K-step boundary

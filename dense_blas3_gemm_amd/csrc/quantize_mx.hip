@@ -45,11 +45,23 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(int64_t rows, int64_t 
     const uint16_t* s = src + r * ld_src + c0;
     float v[32];
     float amax = 0.0f;
+    if (n == 32 && ((uintptr_t)s & 15u) == 0) {  // a whole aligned group: four 16-byte loads
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      v[j] = j < n ? bf16f(s[j]) : 0.0f;
-      amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));  // NaN elements do not set the scale
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 w = *(const u32x4*)(s + 8 * q);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          v[8 * q + 2 * h] = __builtin_bit_cast(float, w[h] << 16);
+          v[8 * q + 2 * h + 1] = __builtin_bit_cast(float, w[h] & 0xFFFF0000u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) v[j] = j < n ? bf16f(s[j]) : 0.0f;
     }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));  // NaN does not set it
     int e = 0;
     if (amax > 0.0f) {
       int ex;  // floor(log2(amax)); amax is a bf16 value, normal or subnormal in fp32
@@ -65,9 +77,24 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(int64_t rows, int64_t 
     // x / 2^(e-127) = x * 2^(127-e): exact (the results stay below 512 in magnitude)
     const float inv = e == 254 ? 0x1p-127f : __builtin_bit_cast(float, (uint32_t)(254 - e) << 23);
     uint8_t* d = dst + r * ld_dst + c0;
+    if (n == 32 && ((uintptr_t)d & 15u) == 0) {  // two 16-byte stores of packed codes
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int j = 0; j < 32; ++j)
-      if (j < n) d[j] = (uint8_t)to_e4m3(v[j] * inv);
+      for (int q = 0; q < 2; ++q) {
+        u32x4 w;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const int j = 16 * q + 4 * h;
+          w[h] = to_e4m3(v[j] * inv) | (to_e4m3(v[j + 1] * inv) << 8) | (to_e4m3(v[j + 2] * inv) << 16) |
+                 (to_e4m3(v[j + 3] * inv) << 24);
+        }
+        *(u32x4*)(d + 16 * q) = w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        if (j < n) d[j] = (uint8_t)to_e4m3(v[j] * inv);
+    }
   }
 }
 

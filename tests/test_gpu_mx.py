@@ -40,7 +40,8 @@ def _quantize_gpu(gpu, bits):
     return dst.cpu().numpy(), sc.cpu().numpy()
 
 
-@pytest.mark.parametrize("rows,cols", [(1, 1), (3, 31), (7, 33), (64, 70), (129, 256), (40, 1000)])
+@pytest.mark.parametrize("rows,cols", [(1, 1), (3, 31), (7, 33), (64, 70), (129, 256), (40, 1000),
+                                       (3, 96), (17, 512), (5, 5120)])
 def test_quantize_mx_bit_exact(gpu, rows, cols):
     bits = _bf16_input(rows, cols, rows * 1000 + cols)
     codes, scales = _quantize_gpu(gpu, bits)
