@@ -362,13 +362,21 @@ def mx_bench(g, warmup: int = 5, steps: int = 30):
     SB = torch.from_numpy(d["SB"]).cuda()
     C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
     g_ms = timed(lambda: g.run_mx(A, SA, B, SB, C))
+    g.set_policy("mxe4m3native_dma_m256n256k128_w2x4_mt32_s2")  # the scaled f8f6f4 MFMA
+    try:
+        n_ms = timed(lambda: g.run_mx(A, SA, B, SB, C))
+    finally:
+        g.set_policy(None)
     flops = 2.0 * M * N * K
     qp50, gp50 = float(np.percentile(q_ms, 50)), float(np.percentile(g_ms, 50))
+    np50 = float(np.percentile(n_ms, 50))
     out = {"quantize_us_p50": round(qp50 * 1e3, 1), "quantize_GBps": round(q_bytes / (qp50 * 1e-3) / 1e9, 1),
            "quantize_frac_hbm": round(q_bytes / (qp50 * 1e-3) / 1e9 / HBM_GBS, 3),
            "gemm_us_p50": round(gp50 * 1e3, 1), "gemm_tflops": round(flops / (gp50 * 1e-3) / 1e12, 1),
            "gemm_frac_bf16_peak": round(flops / (gp50 * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
-           "policy": g.query_policy(M, N, K, 0, 1, 4)}
+           "policy": g.query_policy(M, N, K, 0, 1, 4),
+           "native_us_p50": round(np50 * 1e3, 1), "native_tflops": round(flops / (np50 * 1e-3) / 1e12, 1),
+           "native_frac_fp8_peak": round(flops / (np50 * 1e-3) / 1e12 / PEAK_TFLOPS["e4m3"], 4)}
     print("MXFP8 at 16384 x 5120 x 5120: " + json.dumps(out), file=sys.stderr)
     return out
 

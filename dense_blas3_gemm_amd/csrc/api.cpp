@@ -51,7 +51,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 Problem make_problem(int transA, int transB, int64_t M, int64_t N, int64_t K, const void* A,
                      int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc,
-                     int dtype) {
+                     int dtype, const void* sa = nullptr, int64_t ldsa = 4, const void* sb = nullptr,
+                     int64_t ldsb = 4) {
   Problem pr;
   pr.transA = transA;
   pr.transB = transB;
@@ -61,6 +62,7 @@ Problem make_problem(int transA, int transB, int64_t M, int64_t N, int64_t K, co
   pr.in_fp8 = in_bytes(dtype) == 1;
   pr.c_f32 = out_bytes(dtype) == 4;
   pr.mx = is_mx(dtype);
+  pr.mx_words = ((uintptr_t)sa & 3u) == 0 && ((uintptr_t)sb & 3u) == 0 && ldsa % 4 == 0 && ldsb % 4 == 0;
   const int ie = in_bytes(dtype), oe = out_bytes(dtype);
   const int vec = 16 / ie;
   bool ok = aligned16(A) && aligned16(B) && aligned16(C);
@@ -309,7 +311,7 @@ static gemm_status_t run_checked(const Handle* p, int transA, int transB, int64_
   if (K == 0 || alpha == 0.f) {
     err = launch_scale(a, p->stream);
   } else {
-    const Problem pr = make_problem(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, dtype);
+    const Problem pr = make_problem(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, dtype, sa, ldsa, sb, ldsb);
     int idx, sp = 1;
     if (p->forced >= 0) {
       idx = p->forced;

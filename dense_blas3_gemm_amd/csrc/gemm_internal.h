@@ -50,7 +50,8 @@ struct Policy {
   int pipe;        // 0: global -> registers -> LDS (two stages); 1: direct-to-LDS loads
   int in_mode;     // 0: bf16 in, bf16 MFMA; 1: E4M3 in, widened to bf16 in LDS (exact
                    // fp32 accumulation); 2: E4M3 in, native f8f6f4 MFMA; 3: block-scaled
-                   // E4M3 (MXFP8), widened with its scale; -1: any (generic)
+                   // E4M3 (MXFP8), widened with its scale; 4: block-scaled E4M3 on the
+                   // scaled f8f6f4 MFMA; -1: any (generic)
   int BM, BN, BK;  // workgroup tile
   int WM, WN;      // waves along M and N
   int MT;          // MFMA block edge (32 or 16)
@@ -97,6 +98,7 @@ struct Problem {
   int64_t M, N, K;
   int in_fp8, c_f32;
   int mx;        // block-scaled E4M3 operands (gemm_run_mx)
+  bool mx_words;  // scale rows 4-byte aligned (the scaled native MFMA reads 32-bit words)
   bool fast_ok;  // alignment / divisibility allow the MFMA kernels
 };
 // Shape-driven selection; returns an index into the table and, in *splits, the

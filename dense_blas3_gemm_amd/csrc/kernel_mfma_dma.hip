@@ -37,6 +37,15 @@ __device__ __forceinline__ void load_to_lds(uint32_t lds_base, uint32_t voff, __
                : "memory");
 }
 
+// 64 lanes x 4 bytes from buffer `rsrc` at per-lane byte offset `voff` into LDS bytes
+// [lds_base, lds_base + 256) (lane i -> lds_base + 4*i); an offset past the buffer reads 0.
+__device__ __forceinline__ void load_to_lds_dword(uint32_t lds_base, uint32_t voff, __amdgpu_buffer_rsrc_t rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
 // Waits until at most N of this wave's buffer loads are in flight and all its LDS
 // reads have returned, then joins the workgroup barrier.
 template <int N>
@@ -53,7 +62,10 @@ struct Dma {
                 "each wave loads whole 1 KiB blocks of both tiles");
   static constexpr int A_IPW = C::A_BYTES / 1024 / NW;  // load instructions per wave per tile
   static constexpr int B_IPW = C::B_BYTES / 1024 / NW;
-  static constexpr int IPW = A_IPW + B_IPW;
+  // scaled native E4M3: each wave also loads the scale words of 64 tile rows
+  static_assert(!C::MXN || (C::BM + C::BN) / 64 == NW, "one 64-row block of scale words per wave");
+  static constexpr int SC_IPW = C::MXN ? 1 : 0;
+  static constexpr int IPW = A_IPW + B_IPW + SC_IPW;
   static_assert(C::STAGES >= 2 && C::STAGES <= 4, "two to four LDS stages");
   static_assert((C::STAGES - 1) * IPW <= 63, "vmcnt range");
   static_assert(C::KSTEPS >= 2 && C::KSTEPS % 2 == 0,
@@ -134,6 +146,20 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(GemmArgs a) {
   const uint32_t a_kstep = C::A_KC ? C::BK * C::ES : (uint32_t)(C::BK * a.lda * C::ES);
   const uint32_t b_kstep = C::B_KC ? C::BK * C::ES : (uint32_t)(C::BK * a.ldb * C::ES);
 
+  // ---- scaled native E4M3: this wave's scale words (rows wave*64 + lane of A's tile, or
+  // of B's for the upper waves); K tile kt reads the word at byte kt*4 of the row.  Rows
+  // past M or N read zeros; tiles past K read whatever follows, all of it masked below.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const bool sc_is_a = wave_u < C::BM / 64;
+  const int sc_w = sc_is_a ? wave_u : wave_u - C::BM / 64;
+  const int sc_r = (sc_is_a ? m0 : n0) + sc_w * 64 + lane;
+  const uint32_t sc_goff =
+      !C::MXN || sc_r >= (sc_is_a ? a.M : a.N) ? kOOB : (uint32_t)(sc_r * (sc_is_a ? a.ldsa : a.ldsb));
+  const uint32_t sc_lds = (uint32_t)C::SC_OFF + (uint32_t)((sc_is_a ? 0 : C::A_SC_BYTES) + sc_w * 256);
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(C::MXN ? a.sa : nullptr, C::MXN ? (uint32_t)(a.M * a.ldsa) : 0u);
+  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(C::MXN ? a.sb : nullptr, C::MXN ? (uint32_t)(a.N * a.ldsb) : 0u);
+  const int nb = (a.K + 31) / 32;  // scale blocks along K
+
   // Loads instructions [lo, hi) of K tile kt (A blocks first, then B) into slot sb.
   // Past the end of K every offset is out of range: the loads read zeros and touch no
   // memory.
@@ -157,7 +183,9 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(GemmArgs a) {
     if (krot != 0 && u < nk) kt = u + krot < nk ? u + krot : u + krot - nk;
     const int k0 = kt * C::BK;
     const uint32_t base = (uint32_t)(uintptr_t)sb;
-    if constexpr (q < D::A_IPW) {
+    if constexpr (C::MXN && q == D::IPW - 1) {
+      load_to_lds_dword(base + sc_lds, sc_goff + (uint32_t)kt * 4u, sc_is_a ? rsa : rsb);
+    } else if constexpr (q < D::A_IPW) {
       const bool ok = a_ok[q] & (k0 + a_kc[q] < a.K);
       load_to_lds(__builtin_amdgcn_readfirstlane(base + a_blk + q * 1024u),
                   ok ? a_goff[q] + (uint32_t)kt * a_kstep : kOOB, ra);
@@ -198,12 +226,44 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(GemmArgs a) {
       xb[j] = load_frag<C, C::B_KC, C::B_RB>(sb + C::A_BYTES, xb0 + j * C::MT, kk * C::KT, lane, sw_on);
   };
 
+  // Scaled native E4M3: the scale bytes this lane's MFMAs take, one register per two
+  // fragments and one set per tile parity (two LDS stages).  A tile row's LDS word holds
+  // its four 32-wide K blocks; the lane's K half h takes blocks h (step 0) and 2 + h
+  // (step 1), so fragment f of a pair sits at bytes 2f (step 0) and 2f + 1 (step 1).
+  // Blocks past K, which meet zero-filled elements, read as 127 (x1), so that whatever
+  // the caller left in the scale rows' padding cannot bring a NaN or an overflow.
+  static_assert(!C::MXN || (C::FM % 2 == 0 && C::FN % 2 == 0), "fragments pair up for the scales");
+  constexpr int SCA = C::MXN ? C::FM / 2 : 1, SCB = C::MXN ? C::FN / 2 : 1;
+  int scA[2][SCA], scB[2][SCB];
+  auto read_scales = [&](const lds_char* sb, int u, auto bc) {
+    if constexpr (C::MXN) {
+      constexpr int b = decltype(bc)::value;
+      int kt = u < nk ? kbeg + u : nk_all;  // the K tile issue_one loaded for u
+      if (krot != 0 && u < nk) kt = u + krot < nk ? u + krot : u + krot - nk;
+      const int blk = kt * 4 + (lane >> 5);
+      const uint32_t m = (blk >= nb ? 0x00FF00FFu : 0u) | (blk + 2 >= nb ? 0xFF00FF00u : 0u);
+      const uint32_t sh = 8u * (uint32_t)(lane >> 5);
+      auto pair = [&](int off) {
+        const uint32_t w0 = *LDS_PTR(uint32_t, sb, off) >> sh;
+        const uint32_t w1 = *LDS_PTR(uint32_t, sb, off + C::MT * 4) >> sh;
+        const uint32_t v = __builtin_amdgcn_perm(w1, w0, 0x06040200u);  // w0.b0 w0.b2 w1.b0 w1.b2
+        return (int)((v & ~m) | (0x7F7F7F7Fu & m));
+      };
+#pragma unroll
+      for (int i = 0; i < SCA; ++i) scA[b][i] = pair(C::SC_OFF + (xa0 + 2 * i * C::MT + (lane & 31)) * 4);
+#pragma unroll
+      for (int j = 0; j < SCB; ++j)
+        scB[b][j] = pair(C::SC_OFF + C::A_SC_BYTES + (xb0 + 2 * j * C::MT + (lane & 31)) * 4);
+    }
+  };
+
   // ---- prologue: tiles 0 .. STAGES-2 into slots 0 .. STAGES-2; wait for tile 0
   static_for<C::STAGES - 1>([&](auto sc) {
     static_for<D::IPW>([&](auto qc) { issue_one(slot(sc), decltype(sc)::value, qc); });
   });
   wait_loads_and_barrier<(C::STAGES - 2) * D::IPW>();
   read_step(slot(std::integral_constant<int, 0>{}), 0, fa[0], fb[0]);
+  read_scales(slot(std::integral_constant<int, 0>{}), 0, std::integral_constant<int, 0>{});
 
   // ---- main loop.  Tile u lives in slot u % STAGES.  During tile u's first K steps
   // the loads of tile u+STAGES-1 go into slot (u-1) % STAGES, which every wave left at
@@ -237,8 +297,16 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(GemmArgs a) {
         // step and of the loads for tile u+STAGES-1; nothing is moved across a group.
         static_for<NMF>([&](auto ic) {
           constexpr int i = decltype(ic)::value;
-          if constexpr (i == BAR_AT) wait_loads_and_barrier<(C::STAGES - 2) * D::IPW>();
-          mma(acc[i / C::FN][i % C::FN], fb[kk & 1][i % C::FN], fa[kk & 1][i / C::FN]);
+          if constexpr (i == BAR_AT) {
+            wait_loads_and_barrier<(C::STAGES - 2) * D::IPW>();
+            read_scales(nxt, u + 1, std::integral_constant<int, (s + 1) & 1>{});
+          }
+          if constexpr (C::MXN)
+            mma_mx<2 * (i % C::FN % 2) + kk, 2 * (i / C::FN % 2) + kk>(
+                acc[i / C::FN][i % C::FN], fb[kk & 1][i % C::FN], fa[kk & 1][i / C::FN],
+                scB[s & 1][i % C::FN / 2], scA[s & 1][i / C::FN / 2]);
+          else
+            mma(acc[i / C::FN][i % C::FN], fb[kk & 1][i % C::FN], fa[kk & 1][i / C::FN]);
           if constexpr (i >= RD0) {
             constexpr int r0 = NRF * (i - RD0) / (NMF - RD0), r1 = NRF * (i + 1 - RD0) / (NMF - RD0);
             static_for<r1 - r0>([&](auto jc) {
@@ -325,7 +393,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 hipError_t DBGEMM_DMA_CAT(DBGEMM_DMA_TA, DBGEMM_DMA_TB)(const Policy& p, const GemmArgs& a, hipStream_t s) {
 #define DBGEMM_SIMT(name, eff)
 #define DBGEMM_MFMA(name_, pipe_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_, eff_)       \
-  if constexpr (pipe_ == 1)                                                                               \
+  if constexpr (pipe_ == 1 && (in_ != 4 || (DBGEMM_DMA_TA == 0 && DBGEMM_DMA_TB == 1)))                  \
     if (p.BM == bm_ && p.BN == bn_ && p.BK == bk_ && p.WM == wm_ && p.WN == wn_ && p.MT == mt_ &&         \
         p.stages == st_ && p.in_mode == in_ && p.read_mode == ((((sw_) >> 2) & 1) ? 0 : 1))               \
       return launch_cfg<Cfg<bm_, bn_, bk_, wm_, wn_, mt_, st_, in_, DBGEMM_DMA_TA != 0, DBGEMM_DMA_TB != 0,  \

@@ -62,8 +62,9 @@ __device__ inline void tile_of(int bid, const GemmArgs& a, int& tm, int& tn, int
 // Input modes: IN_BF16 (bf16 operands, bf16 MFMA); IN_E4M3 (E4M3 operands widened
 // exactly to bf16 on their way into LDS, bf16 MFMA: full fp32 accumulation);
 // IN_E4M3_NATIVE (E4M3 operands fed to the f8f6f4 MFMA as they are); IN_MX (E4M3
-// operands with a UE8M0 scale per 32 along K, widened to bf16 times their scale).
-enum { IN_BF16 = 0, IN_E4M3 = 1, IN_E4M3_NATIVE = 2, IN_MX = 3 };
+// operands with a UE8M0 scale per 32 along K, widened to bf16 times their scale);
+// IN_MX_NATIVE (the same operands on the scaled f8f6f4 MFMA, which applies the scales).
+enum { IN_BF16 = 0, IN_E4M3 = 1, IN_E4M3_NATIVE = 2, IN_MX = 3, IN_MX_NATIVE = 4 };
 
 // READ_: 1 reads M/N-contiguous fragments with the transposing ds_read_b64_tr_*; 0 reads
 // them one element at a time (ds_read_u16), the plain-load rung of the read ablation.
@@ -73,9 +74,10 @@ struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, MT = MT_, STAGES = STAGES_;
   static constexpr int IN = IN_;
   static constexpr int READ = READ_;
-  static_assert(READ == 1 || IN != IN_E4M3_NATIVE, "element-wise reads are for bf16 fragments");
+  static_assert(READ == 1 || (IN != IN_E4M3_NATIVE && IN != IN_MX_NATIVE), "element-wise reads are for bf16");
   static constexpr bool TA = TA_, TB = TB_;
-  static constexpr bool FP8 = IN == IN_E4M3_NATIVE;  // fragments and MFMA are E4M3
+  static constexpr bool MXN = IN == IN_MX_NATIVE;  // block scales ride in LDS next to the tiles
+  static constexpr bool FP8 = IN == IN_E4M3_NATIVE || MXN;  // fragments and MFMA are E4M3
   static constexpr int THREADS = WM * WN * 64;
   static constexpr int GES = IN == IN_BF16 ? 2 : 1;  // bytes per element in global memory
   static constexpr int ES = FP8 ? 1 : 2;             // bytes per element in LDS and fragments
@@ -95,7 +97,11 @@ struct Cfg {
   static constexpr int A_CPR = A_RB / 16, B_CPR = B_RB / 16;    // LDS chunks per row
   static constexpr int A_GCPR = A_COLS * GES / 16, B_GCPR = B_COLS * GES / 16;  // global chunks per row
   static constexpr int A_BYTES = A_ROWS * A_RB, B_BYTES = B_ROWS * B_RB;
-  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  // scaled native E4M3: one 32-bit word per tile row holding the UE8M0 bytes of the tile's
+  // four 32-element K blocks, A rows then B rows
+  static constexpr int A_SC_BYTES = MXN ? BM * 4 : 0, B_SC_BYTES = MXN ? BN * 4 : 0;
+  static constexpr int SC_OFF = A_BYTES + B_BYTES;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + A_SC_BYTES + B_SC_BYTES;
   static constexpr int A_CH = A_ROWS * A_GCPR / THREADS, B_CH = B_ROWS * B_GCPR / THREADS;
 
   // LDS read instructions per fragment and per K step of one wave
@@ -106,6 +112,8 @@ struct Cfg {
   static_assert(WTM % MT == 0 && WTN % MT == 0, "wave tile must hold whole MFMA blocks");
   static_assert(BK % KT == 0, "BK must hold whole MFMA K steps");
   static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(!MXN || (BK == 128 && MT == 32 && STAGES == 2 && !TA && TB),
+                "scaled native E4M3: K tiles of four scale blocks, 32x32x64 MFMA, A [M][K], B [N][K]");
 };
 
 // XOR swizzle of the 16-byte chunk index of LDS row r.  The LDS serves 256 bytes per
@@ -167,6 +175,14 @@ __device__ inline void mma(f32x4& acc, const i32x8& b, const i32x8& a) {
   acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, acc, 0, 0, 0, 0, 0, 0);
 }
 
+// Scaled f8f6f4 MFMA: the first operand (the B fragment, rows n) is scaled by byte SELB
+// of sb, the second (the A fragment, rows m) by byte SELA of sa, each byte a UE8M0
+// exponent (127 = 1); each lane's 32 K values form one scale block.
+template <int SELB, int SELA>
+__device__ inline void mma_mx(f32x16& acc, const i32x8& b, const i32x8& a, int sb, int sa) {
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc, 0, 0, SELB, sb, SELA, sa);
+}
+
 template <bool FP8> struct FragOf { using T = bf16x8; };
 template <> struct FragOf<true> { using T = i32x8; };
 template <int MT> struct AccOf { using T = f32x16; };
@@ -194,8 +210,15 @@ __device__ inline typename FragOf<C::FP8>::T load_frag(const lds_char* base, int
       const uint32_t off = r * RB + ((c ^ s) << 4);
       f = *LDS_PTR(bf16x8, base, off);
     } else {
-      const uint32_t off0 = r * RB + ((c ^ s) << 4);
-      const uint32_t off1 = r * RB + (((c + 1) ^ s) << 4);
+      // The scaled MFMA reads the first 16 bytes of every lane as scale block 0 of the
+      // step (its scale from lanes 0-31) and the last 16 as block 1 (lanes 32-63), as
+      // measured on gfx950; so with scales lane half h holds the 16-byte K chunks h
+      // and h + 2 of the step, and 32-wide block b is chunks 2b and 2b + 1.  Without
+      // scales only the K order of A and B must agree: consecutive chunks.
+      const int c0 = C::MXN ? kbase * C::ES / 16 + lane / C::MT : c;
+      const int c1 = C::MXN ? c0 + 2 : c + 1;
+      const uint32_t off0 = r * RB + ((c0 ^ s) << 4);
+      const uint32_t off1 = r * RB + ((c1 ^ s) << 4);
       i32x4 lo = *LDS_PTR(i32x4, base, off0);
       i32x4 hi = *LDS_PTR(i32x4, base, off1);
       f = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};

@@ -27,7 +27,7 @@ constexpr int kCount = sizeof(kTable) / sizeof(kTable[0]);
 // Resident workgroups per CU: bounded by LDS (160 KiB) and by the unified register
 // file (512 registers per lane per SIMD shared by the waves on that SIMD).
 int occupancy(const Policy& p) {
-  const int es = p.in_mode == 2 ? 1 : 2;  // bytes per element in LDS (E4M3 widens to bf16)
+  const int es = (p.in_mode == 2 || p.in_mode == 4) ? 1 : 2;  // bytes per element in LDS
   const int lds = p.stages * (p.BM + p.BN) * p.BK * es;
   const int staging = p.pipe == 0 ? (p.BM + p.BN) * p.BK * (p.in_mode == 0 ? 2 : 1) / (p.WM * p.WN * 64) / 4 : 0;
   int occ_lds = (160 * 1024) / lds;
@@ -57,8 +57,8 @@ int policy_find(const char* name) {
 bool policy_serves(const Policy& p, const Problem& pr) {
   if (p.kind == KIND_SIMT) return true;
   if (p.kind != KIND_MFMA || !pr.fast_ok) return false;
-  if (pr.mx) return p.in_mode == 3;
-  return p.in_mode != 3 && (p.in_mode != 0) == (pr.in_fp8 != 0);
+  if (pr.mx) return p.in_mode == 3 || (p.in_mode == 4 && pr.mx_words);
+  return p.in_mode < 3 && (p.in_mode != 0) == (pr.in_fp8 != 0);
 }
 
 int64_t split_ws_floats(const Policy& p, const Problem& pr, int splits) {
