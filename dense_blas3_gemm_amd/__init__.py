@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdbgemm.so")
 
 OP_N, OP_T = 0, 1
-BF16_F32, BF16_BF16, E4M3_BF16, E4M3_F32, MXE4M3_BF16, MXE4M3_F32 = 0, 1, 2, 3, 4, 5
+BF16_F32, BF16_BF16, E4M3_BF16, E4M3_F32, MXE4M3_BF16, MXE4M3_F32, E4M3_E4M3, MXE4M3_E4M3 = range(8)
 STATUS = {0: "SUCCESS", 1: "INVALID_VALUE", 2: "NOT_SUPPORTED", 3: "NOT_INITIALIZED",
           4: "LAUNCH_FAILED", 5: "INTERNAL"}
 
@@ -106,7 +106,17 @@ def policies():
 
 def dtype_code(in_dtype: str, c_dtype: str) -> int:
     return {("bf16", "f32"): BF16_F32, ("bf16", "bf16"): BF16_BF16,
-            ("e4m3", "bf16"): E4M3_BF16, ("e4m3", "f32"): E4M3_F32}[(in_dtype, c_dtype)]
+            ("e4m3", "bf16"): E4M3_BF16, ("e4m3", "f32"): E4M3_F32,
+            ("e4m3", "e4m3"): E4M3_E4M3}[(in_dtype, c_dtype)]
+
+
+def _c_kind(C) -> str:
+    import torch
+    if C.dtype == torch.float32:
+        return "f32"
+    if C.dtype == torch.float8_e4m3fn:
+        return "e4m3"
+    return "bf16"
 
 
 def _current_stream(device) -> int:
@@ -177,14 +187,13 @@ class Gemm:
                  beta: float = 0.0, dtype: Optional[int] = None):
         """C <- alpha*op(A)*op(B) + beta*C on torch tensors (row-major 2-D views).
 
-        A and B are bf16 or float8_e4m3fn, C bf16 or float32; op(X) = X^T when the
-        trans flag is 1, read in place from X's storage.
+        A and B are bf16 or float8_e4m3fn, C bf16 or float32 (or float8_e4m3fn for E4M3
+        inputs); op(X) = X^T when the trans flag is 1, read in place from X's storage.
         """
         import torch
         if dtype is None:
             ind = "e4m3" if A.dtype == torch.float8_e4m3fn else "bf16"
-            cd = "f32" if C.dtype == torch.float32 else "bf16"
-            dtype = dtype_code(ind, cd)
+            dtype = dtype_code(ind, _c_kind(C))
         M, N = C.shape
         K = A.shape[0] if transA else A.shape[1]
         stream = _current_stream(C.device)
@@ -197,11 +206,12 @@ class Gemm:
     def run_mx(self, A, SA, B, SB, C, alpha: float = 1.0, beta: float = 0.0):
         """Block-scaled E4M3 GEMM (gemm_run_mx) on torch tensors: A [M][K] and B [N][K] as
         float8_e4m3fn (or uint8 codes), SA [M][ceil(K/32)] and SB [N][ceil(K/32)] uint8
-        UE8M0 scales, C bf16 or float32 [M][N]; C <- alpha*A*B^T(scaled) + beta*C."""
+        UE8M0 scales, C bf16, float32 or float8_e4m3fn [M][N];
+        C <- alpha*A*B^T(scaled) + beta*C."""
         import torch
         M, N = C.shape
         K = A.shape[1]
-        dtype = MXE4M3_F32 if C.dtype == torch.float32 else MXE4M3_BF16
+        dtype = {"f32": MXE4M3_F32, "e4m3": MXE4M3_E4M3, "bf16": MXE4M3_BF16}[_c_kind(C)]
         stream = _current_stream(C.device)
         if stream != self._stream:
             self.set_stream(stream)

@@ -41,11 +41,16 @@ bool live(gemm_handle_t h) {
 }
 
 bool valid_op(int op) { return op == GEMM_OP_N || op == GEMM_OP_T; }
-bool valid_dtype(int d) { return d >= GEMM_BF16_F32 && d <= GEMM_E4M3_F32; }        // gemm_run
-bool valid_query_dtype(int d) { return d >= GEMM_BF16_F32 && d <= GEMM_MXE4M3_F32; }  // + block-scaled
-bool is_mx(int d) { return d == GEMM_MXE4M3_BF16 || d == GEMM_MXE4M3_F32; }
+bool is_mx(int d) { return d == GEMM_MXE4M3_BF16 || d == GEMM_MXE4M3_F32 || d == GEMM_MXE4M3_E4M3; }
+bool valid_query_dtype(int d) { return d >= GEMM_BF16_F32 && d <= GEMM_MXE4M3_E4M3; }
+bool valid_dtype(int d) { return valid_query_dtype(d) && !is_mx(d); }  // gemm_run
 int in_bytes(int d) { return (d == GEMM_BF16_F32 || d == GEMM_BF16_BF16) ? 2 : 1; }
-int out_bytes(int d) { return (d == GEMM_BF16_F32 || d == GEMM_E4M3_F32 || d == GEMM_MXE4M3_F32) ? 4 : 2; }
+int c_kind(int d) {
+  if (d == GEMM_BF16_F32 || d == GEMM_E4M3_F32 || d == GEMM_MXE4M3_F32) return C_F32;
+  if (d == GEMM_E4M3_E4M3 || d == GEMM_MXE4M3_E4M3) return C_E4M3;
+  return C_BF16;
+}
+int out_bytes(int d) { return c_kind(d) == C_F32 ? 4 : c_kind(d) == C_E4M3 ? 1 : 2; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -60,7 +65,7 @@ Problem make_problem(int transA, int transB, int64_t M, int64_t N, int64_t K, co
   pr.N = N;
   pr.K = K;
   pr.in_fp8 = in_bytes(dtype) == 1;
-  pr.c_f32 = out_bytes(dtype) == 4;
+  pr.c_kind = c_kind(dtype);
   pr.mx = is_mx(dtype);
   pr.mx_words = ((uintptr_t)sa & 3u) == 0 && ((uintptr_t)sb & 3u) == 0 && ldsa % 4 == 0 && ldsb % 4 == 0;
   const int ie = in_bytes(dtype), oe = out_bytes(dtype);
@@ -292,7 +297,7 @@ static gemm_status_t run_checked(const Handle* p, int transA, int transB, int64_
   a.K = (int)K;
   a.alpha = alpha;
   a.beta = beta;
-  a.c_f32 = out_bytes(dtype) == 4;
+  a.c_kind = c_kind(dtype);
   a.in_fp8 = in_bytes(dtype) == 1;
   a.transA = transA;
   a.transB = transB;
@@ -367,7 +372,9 @@ gemm_status_t gemm_run_mx(gemm_handle_t h, int64_t M, int64_t N, int64_t K, floa
   if (!live(h)) return GEMM_STATUS_NOT_INITIALIZED;
   if (!is_mx(dtype)) return GEMM_STATUS_INVALID_VALUE;
   // the operand checks of gemm_run with the E4M3 dtype of the same C type
-  const int plain = dtype == GEMM_MXE4M3_F32 ? GEMM_E4M3_F32 : GEMM_E4M3_BF16;
+  const int plain = dtype == GEMM_MXE4M3_F32    ? GEMM_E4M3_F32
+                    : dtype == GEMM_MXE4M3_E4M3 ? GEMM_E4M3_E4M3
+                                                : GEMM_E4M3_BF16;
   const gemm_status_t st = gemm_check_args(GEMM_OP_N, GEMM_OP_T, M, N, K, alpha, A, lda, B, ldb, beta, C,
                                            ldc, plain);
   if (st != GEMM_STATUS_SUCCESS) return st;

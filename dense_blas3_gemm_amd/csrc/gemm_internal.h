@@ -10,6 +10,9 @@ namespace dbgemm {
 // Everything a kernel needs for one call.  Sizes are validated on the host before a
 // launch: the fast kernels additionally require every operand span to stay below
 // 2^31 bytes so that 32-bit buffer offsets cover it.
+// C element types (GemmArgs::c_kind)
+enum { C_BF16 = 0, C_F32 = 1, C_E4M3 = 2 };
+
 struct GemmArgs {
   const void* A;
   const void* B;
@@ -17,7 +20,7 @@ struct GemmArgs {
   int64_t lda, ldb, ldc;
   int M, N, K;
   float alpha, beta;
-  int c_f32;      // 1: C is fp32, 0: C is bf16
+  int c_kind;     // C's element type: C_BF16, C_F32 or C_E4M3
   int in_fp8;     // 1: A, B are E4M3, 0: bf16
   int transA, transB;
   int tiles_m, tiles_n;
@@ -96,7 +99,7 @@ int policy_find(const char* name);
 struct Problem {
   int transA, transB;
   int64_t M, N, K;
-  int in_fp8, c_f32;
+  int in_fp8, c_kind;
   int mx;        // block-scaled E4M3 operands (gemm_run_mx)
   bool mx_words;  // scale rows 4-byte aligned (the scaled native MFMA reads 32-bit words)
   bool fast_ok;  // alignment / divisibility allow the MFMA kernels

@@ -1,6 +1,7 @@
 // Generic GEMM kernels for gfx950: shapes, strides or alignments the MFMA kernels do
 // not take, and the beta-only update.  Same operation and conventions as the MFMA
 // path (row-major, op(X) = X or X^T, fp32 accumulation, bf16 RNE or fp32 C).
+#include "e4m3_codec.h"
 #include "gemm_internal.h"
 
 namespace dbgemm {
@@ -27,13 +28,17 @@ __device__ inline float ue8m0_to_f32(uint8_t e) {
   return e == 255 ? __builtin_nanf("") : __builtin_bit_cast(float, e == 0 ? 0x00400000u : (uint32_t)e << 23);
 }
 
-__device__ inline float load_c(const void* p, int64_t idx, int f32) {
-  return f32 ? ((const float*)p)[idx] : bf16_to_f32(((const uint16_t*)p)[idx]);
+__device__ inline float load_c(const void* p, int64_t idx, int kind) {
+  if (kind == C_F32) return ((const float*)p)[idx];
+  if (kind == C_E4M3) return e4m3_to_f32(((const uint8_t*)p)[idx]);
+  return bf16_to_f32(((const uint16_t*)p)[idx]);
 }
 
-__device__ inline void store_c(void* p, int64_t idx, int f32, float v) {
-  if (f32)
+__device__ inline void store_c(void* p, int64_t idx, int kind, float v) {
+  if (kind == C_F32)
     ((float*)p)[idx] = v;
+  else if (kind == C_E4M3)
+    ((uint8_t*)p)[idx] = (uint8_t)e4m3_from_f32(v);
   else
     ((uint16_t*)p)[idx] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
 }
@@ -90,8 +95,8 @@ __global__ __launch_bounds__(256) void gemm_simt_kernel(GemmArgs a) {
       if (n >= a.N) continue;
       const int64_t idx = (int64_t)m * a.ldc + n;
       float v = a.alpha * acc[i][j];
-      if (a.beta != 0.f) v += a.beta * load_c(a.C, idx, a.c_f32);
-      store_c(a.C, idx, a.c_f32, v);
+      if (a.beta != 0.f) v += a.beta * load_c(a.C, idx, a.c_kind);
+      store_c(a.C, idx, a.c_kind, v);
     }
   }
 }
@@ -102,8 +107,8 @@ __global__ __launch_bounds__(256) void scale_kernel(GemmArgs a) {
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
     const int m = (int)(e / a.N), n = (int)(e % a.N);
     const int64_t idx = (int64_t)m * a.ldc + n;
-    const float v = a.beta != 0.f ? a.beta * load_c(a.C, idx, a.c_f32) : 0.f;
-    store_c(a.C, idx, a.c_f32, v);
+    const float v = a.beta != 0.f ? a.beta * load_c(a.C, idx, a.c_kind) : 0.f;
+    store_c(a.C, idx, a.c_kind, v);
   }
 }
 

@@ -6,6 +6,7 @@
 
 #include <type_traits>
 
+#include "e4m3_codec.h"
 #include "gemm_internal.h"
 
 namespace dbgemm {
@@ -346,9 +347,10 @@ __device__ inline void put_chunk(lds_char* sbase, uint32_t off, const i32x4& v, 
 
 // Epilogue of one group of four accumulator values: acc float4 number p of this lane
 // (block (i, j), quarter q) holds C[m][n .. n+3]; C <- alpha*v + beta*C_old, rounded
-// to C's type.  store_tile applies it to every group.
+// to C's type (bf16 and E4M3 to nearest even, E4M3 saturating at +-448).  store_tile
+// applies it to every group.
 template <class C>
-__device__ inline void store_group(const GemmArgs& a, f32x4 v, int p, int row0, int col0, int lane) {
+__device__ __forceinline__ void store_group(const GemmArgs& a, f32x4 v, int p, int row0, int col0, int lane) {
   const int q = p % (C::ACC / 4), j = (p / (C::ACC / 4)) % C::FN, i = p / (C::ACC / 4) / C::FN;
   const int m = row0 + i * C::MT + lane % C::MT;
   const int n = col0 + j * C::MT + (C::MT == 32 ? 8 * q + 4 * (lane / 32) : 4 * (lane / 16));
@@ -359,7 +361,7 @@ __device__ inline void store_group(const GemmArgs& a, f32x4 v, int p, int row0, 
   for (int e = 0; e < 4; ++e) w[e] = alpha * v[e];
   const int64_t base = (int64_t)m * a.ldc + n;
   if (n + 3 < a.N) {
-    if (a.c_f32) {
+    if (a.c_kind == C_F32) {
       float* cp = (float*)a.C + base;
       if (beta != 0.f) {
         f32x4 old = *(const f32x4*)cp;
@@ -367,6 +369,16 @@ __device__ inline void store_group(const GemmArgs& a, f32x4 v, int p, int row0, 
         for (int e = 0; e < 4; ++e) w[e] += beta * old[e];
       }
       *(f32x4*)cp = (f32x4){w[0], w[1], w[2], w[3]};
+    } else if (a.c_kind == C_E4M3) {  // four codes in one 32-bit word (n is a multiple of 4)
+      uint32_t* cp = (uint32_t*)((uint8_t*)a.C + base);
+      if (beta != 0.f) {
+        const uint32_t old = *cp;
+        w[0] += beta * __builtin_amdgcn_cvt_f32_fp8((int)old, 0);
+        w[1] += beta * __builtin_amdgcn_cvt_f32_fp8((int)old, 1);
+        w[2] += beta * __builtin_amdgcn_cvt_f32_fp8((int)old, 2);
+        w[3] += beta * __builtin_amdgcn_cvt_f32_fp8((int)old, 3);
+      }
+      *cp = e4m3x4_from_f32(w[0], w[1], w[2], w[3]);
     } else {
       uint16_t* cp = (uint16_t*)a.C + base;
       if (beta != 0.f) {
@@ -381,9 +393,13 @@ __device__ inline void store_group(const GemmArgs& a, f32x4 v, int p, int row0, 
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (n + e >= a.N) break;
-      if (a.c_f32) {
+      if (a.c_kind == C_F32) {
         float* cp = (float*)a.C + base + e;
         *cp = w[e] + (beta != 0.f ? beta * *cp : 0.f);
+      } else if (a.c_kind == C_E4M3) {
+        uint8_t* cp = (uint8_t*)a.C + base + e;
+        *cp = (uint8_t)e4m3x4_from_f32(w[e] + (beta != 0.f ? beta * __builtin_amdgcn_cvt_f32_fp8(*cp, 0) : 0.f),
+                                       0.f, 0.f, 0.f);
       } else {
         uint16_t* cp = (uint16_t*)a.C + base + e;
         *cp = f32_to_bf16_bits(w[e] + (beta != 0.f ? beta * bf16_bits_to_f32(*cp) : 0.f));
@@ -396,17 +412,15 @@ __device__ inline void store_group(const GemmArgs& a, f32x4 v, int p, int row0, 
 // row0 and first column col0.  The MFMA ran with the B fragment as first operand, so
 // a lane holds, for row row0 + i*MT + lane%MT, groups of four consecutive columns.
 template <class C>
-__device__ inline void store_tile(const GemmArgs& a, const typename AccOf<C::MT>::T (&acc)[C::FM][C::FN],
+__device__ __forceinline__ void store_tile(const GemmArgs& a, const typename AccOf<C::MT>::T (&acc)[C::FM][C::FN],
                                   int row0, int col0, int lane) {
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-      for (int q = 0; q < C::ACC / 4; ++q)
-        store_group<C>(a,
-                       (f32x4){acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]},
-                       (i * C::FN + j) * (C::ACC / 4) + q, row0, col0, lane);
+  // compile-time indices (not a loop left to the unroller), so acc stays in registers
+  static_for<C::FM * C::FN * (C::ACC / 4)>([&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    constexpr int q = p % (C::ACC / 4), j = (p / (C::ACC / 4)) % C::FN, i = p / (C::ACC / 4) / C::FN;
+    store_group<C>(a, (f32x4){acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]},
+                   p, row0, col0, lane);
+  });
 }
 
 // Split-K partial tiles.  A partial is kept in register order: float4 number p of

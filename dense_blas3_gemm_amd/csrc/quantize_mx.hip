@@ -7,31 +7,12 @@
 // rounded to the nearest E4M3 value, ties to the even code, saturating at +-448.
 // One thread per 32-element group; the conversion is integer/RNE arithmetic, exact.
 #include "gemm_internal.h"
+#include "e4m3_codec.h"
 
 namespace dbgemm {
 namespace {
 
 __device__ inline float bf16f(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
-
-// |q| < 448 or NaN handled by the caller's saturation; returns the E4M3 code of q
-// rounded to nearest even (sign included), saturating at +-448.
-__device__ inline uint32_t to_e4m3(float q) {
-  const uint32_t sign = (__builtin_bit_cast(uint32_t, q) >> 24) & 0x80u;
-  const float a = __builtin_fabsf(q);
-  if (!(a == a)) return sign | 0x7Fu;  // NaN stays NaN
-  if (a >= 448.0f) return sign | 0x7Eu;
-  if (a < 0x1p-6f) {  // subnormal range: multiples of 2^-9 (8 rounds up to 2^-6, code 8)
-    return sign | (uint32_t)__builtin_rintf(a * 512.0f);
-  }
-  int ex = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFFu) - 127;  // -6 .. 8
-  // mantissa on the 3-bit grid: m in [8, 16) before rounding (exact scaling by 2^(3-ex))
-  uint32_t m = (uint32_t)__builtin_rintf(a * __builtin_bit_cast(float, (uint32_t)(127 + 3 - ex) << 23));
-  if (m == 16u) {
-    m = 8u;
-    ++ex;
-  }
-  return sign | ((uint32_t)(ex + 7) << 3) | (m - 8u);
-}
 
 __global__ __launch_bounds__(256) void quantize_mx_kernel(int64_t rows, int64_t cols, const uint16_t* src,
                                                           int64_t ld_src, uint8_t* dst, int64_t ld_dst,
@@ -85,15 +66,15 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(int64_t rows, int64_t 
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
           const int j = 16 * q + 4 * h;
-          w[h] = to_e4m3(v[j] * inv) | (to_e4m3(v[j + 1] * inv) << 8) | (to_e4m3(v[j + 2] * inv) << 16) |
-                 (to_e4m3(v[j + 3] * inv) << 24);
+          w[h] = e4m3_from_f32(v[j] * inv) | (e4m3_from_f32(v[j + 1] * inv) << 8) | (e4m3_from_f32(v[j + 2] * inv) << 16) |
+                 (e4m3_from_f32(v[j + 3] * inv) << 24);
         }
         *(u32x4*)(d + 16 * q) = w;
       }
     } else {
 #pragma unroll
       for (int j = 0; j < 32; ++j)
-        if (j < n) d[j] = (uint8_t)to_e4m3(v[j] * inv);
+        if (j < n) d[j] = (uint8_t)e4m3_from_f32(v[j] * inv);
     }
   }
 }

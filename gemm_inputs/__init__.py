@@ -36,6 +36,7 @@ DTYPE_CODES = {
     (BF16, BF16): 1,
     (E4M3, BF16): 2,
     (E4M3, F32): 3,
+    (E4M3, E4M3): 6,
 }
 
 

@@ -73,8 +73,15 @@ typedef enum {
   GEMM_E4M3_BF16 = 2,   /* E4M3 A, B; bf16 C */
   GEMM_E4M3_F32 = 3,    /* E4M3 A, B; fp32 C */
   GEMM_MXE4M3_BF16 = 4, /* block-scaled E4M3 A, B (gemm_run_mx only); bf16 C */
-  GEMM_MXE4M3_F32 = 5   /* block-scaled E4M3 A, B (gemm_run_mx only); fp32 C */
+  GEMM_MXE4M3_F32 = 5,  /* block-scaled E4M3 A, B (gemm_run_mx only); fp32 C */
+  GEMM_E4M3_E4M3 = 6,   /* E4M3 A, B; E4M3 C (see below) */
+  GEMM_MXE4M3_E4M3 = 7  /* block-scaled E4M3 A, B (gemm_run_mx only); E4M3 C */
 } gemm_dtype_t;
+/* E4M3 C (the fp8 data path of the fused-protocol page, "v12 FP8 boundary": inputs and
+ * outputs are already E4M3, the scales are the caller's): C <- E4M3(alpha * acc + beta *
+ * C_old), with C_old decoded from its E4M3 codes.  The caller folds its output scale into
+ * alpha.  Rounding is to the nearest E4M3 value, ties to the even code; magnitudes at or
+ * above 448 (and values that round past it) saturate to +-448; NaN stays NaN. */
 
 typedef enum {
   GEMM_STATUS_SUCCESS = 0,
@@ -117,10 +124,15 @@ gemm_status_t gemm_run(gemm_handle_t h, int transA, int transB, int64_t M, int64
  * contiguous): A is E4M3 [M][lda >= K]; B is E4M3 [N][ldb >= K] (op(B) = B^T);
  * scale_a is one byte per row and block, [M][ld_scale_a >= ceil(K/32)]; scale_b
  * [N][ld_scale_b >= ceil(K/32)]; C as in gemm_run.  A scale byte e stands for 2^(e-127)
- * (255 is NaN).  dtype is GEMM_MXE4M3_BF16 or GEMM_MXE4M3_F32 (C's type).  Every scaled
- * element is widened exactly to bf16 and accumulated in fp32 (scaled values below the
- * bf16 range lose precision).  Device pointers; errors and special cases as gemm_run;
- * NOT_SUPPORTED when a scale array spans 2^31 bytes or more. */
+ * (255 is NaN).  dtype is GEMM_MXE4M3_BF16, GEMM_MXE4M3_F32 or GEMM_MXE4M3_E4M3 (C's
+ * type).  By default every scaled element is widened exactly to bf16 and accumulated in
+ * fp32 (scaled values below the bf16 range lose precision).  The policy
+ * "mxe4m3native_dma_m256n256k128_w2x4_mt32_s2" (gemm_set_policy) runs the scaled f8f6f4
+ * MFMA instead, which sums each group of products at reduced precision (bits below
+ * 2^-13 of the group's largest product are dropped); it needs 4-byte aligned scale
+ * arrays with ld_scale_a and ld_scale_b multiples of 4 (else NOT_SUPPORTED) and never
+ * uses the scale bytes of blocks past K.  Device pointers; errors and special cases as
+ * gemm_run; NOT_SUPPORTED when a scale array spans 2^31 bytes or more. */
 gemm_status_t gemm_run_mx(gemm_handle_t h, int64_t M, int64_t N, int64_t K, float alpha,
                           const void* A, int64_t lda, const uint8_t* scale_a, int64_t ld_scale_a,
                           const void* B, int64_t ldb, const uint8_t* scale_b, int64_t ld_scale_b,

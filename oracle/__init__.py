@@ -25,6 +25,7 @@ IN_BF16 = 0
 IN_E4M3 = 1
 C_F32 = 0
 C_BF16 = 1
+C_E4M3 = 2
 
 _lib = None
 
@@ -177,10 +178,40 @@ def gemm_mx(M: int, N: int, K: int, alpha: float, A: np.ndarray, lda: int, SA: n
     return R, S
 
 
-# The 127 non-negative finite E4M3 values in code order (0x00 .. 0x7E), for quantisation.
+# The 127 non-negative finite E4M3 values in code order (0x00 .. 0x7E).
 def _e4m3_grid():
     codes = np.arange(0x7F, dtype=np.uint8)
     return decode(codes, "e4m3"), codes
+
+
+def _e4m3_code(q: float, grid, gcodes) -> int:
+    """E4M3 code of |q| (q >= 0, not NaN): the nearest grid value, ties to the even code,
+    448 for everything at or above 448."""
+    if q >= 448.0:
+        return 0x7E
+    hi = int(np.searchsorted(grid, q))  # grid[hi-1] < q <= grid[hi]
+    if grid[hi] == q:
+        return int(gcodes[hi])
+    lo = hi - 1
+    dlo, dhi = q - grid[lo], grid[hi] - q
+    if dlo < dhi or (dlo == dhi and gcodes[lo] % 2 == 0):
+        return int(gcodes[lo])
+    return int(gcodes[hi])
+
+
+def round_e4m3(x: np.ndarray) -> np.ndarray:
+    """float64 values -> OCP E4M3 codes: the nearest E4M3 value, ties to the even code,
+    saturating at +-448 (an output format with a caller scale has no infinity to go to),
+    NaN to the NaN code, sign kept (also for zero).  Element by element on the sorted grid
+    of the format's values."""
+    x = np.asarray(x, dtype=np.float64)
+    grid, gcodes = _e4m3_grid()
+    out = np.empty(x.shape, dtype=np.uint8)
+    flat, dst = x.reshape(-1), out.reshape(-1)
+    for t, v in enumerate(flat):
+        c = 0x7F if np.isnan(v) else _e4m3_code(abs(float(v)), grid, gcodes)
+        dst[t] = c | (0x80 if np.signbit(v) else 0)
+    return out
 
 
 def quantize_mx(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
@@ -213,20 +244,7 @@ def quantize_mx(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
                 e = int(min(254, max(0, (int(ex) - 1) - 8 + 127)))
             scales[i, b] = e
             for t, v in enumerate(blk):
-                q = abs(float(v)) / 2.0 ** (e - 127)
-                if q >= 448.0:
-                    c = 0x7E
-                else:
-                    hi = int(np.searchsorted(grid, q))  # grid[hi-1] < q <= grid[hi]
-                    if grid[hi] == q:
-                        c = int(gcodes[hi])
-                    else:
-                        lo = hi - 1
-                        dlo, dhi = q - grid[lo], grid[hi] - q
-                        if dlo < dhi or (dlo == dhi and gcodes[lo] % 2 == 0):
-                            c = int(gcodes[lo])
-                        else:
-                            c = int(gcodes[hi])
+                c = _e4m3_code(abs(float(v)) / 2.0 ** (e - 127), grid, gcodes)
                 if np.signbit(v):
                     c |= 0x80
                 codes[i, 32 * b + t] = c

@@ -40,7 +40,7 @@
 #endif
 
 enum { ORACLE_IN_BF16 = 0, ORACLE_IN_E4M3 = 1 };
-enum { ORACLE_C_F32 = 0, ORACLE_C_BF16 = 1 };
+enum { ORACLE_C_F32 = 0, ORACLE_C_BF16 = 1, ORACLE_C_E4M3 = 2 };
 
 /* bf16 storage: the upper 16 bits of an IEEE-754 binary32. */
 double oracle_bf16_value(uint16_t bits) {
@@ -122,8 +122,10 @@ static inline double in_value(const void* p, int64_t idx, int fmt) {
   return e4m3_table[((const uint8_t*)p)[idx]];
 }
 
+/* The old value of C for the beta term, decoded from C's storage format. */
 static inline double c_value(const void* p, int64_t idx, int fmt) {
   if (fmt == ORACLE_C_BF16) return oracle_bf16_value(((const uint16_t*)p)[idx]);
+  if (fmt == ORACLE_C_E4M3) return oracle_e4m3_value(((const uint8_t*)p)[idx]);
   return oracle_f32_value(((const uint32_t*)p)[idx]);
 }
 
@@ -137,7 +139,7 @@ int oracle_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, double 
                 int64_t nrows, double* R, double* S, int nthreads) {
   if (M < 0 || N < 0 || K < 0) return -1;
   if (in_fmt != ORACLE_IN_BF16 && in_fmt != ORACLE_IN_E4M3) return -1;
-  if (c_fmt != ORACLE_C_F32 && c_fmt != ORACLE_C_BF16) return -1;
+  if (c_fmt != ORACLE_C_F32 && c_fmt != ORACLE_C_BF16 && c_fmt != ORACLE_C_E4M3) return -1;
   if (rows == NULL) nrows = M;
   if (nrows == 0 || N == 0) return 0;
   init_tables();
@@ -201,7 +203,7 @@ int oracle_gemm_mx(int64_t M, int64_t N, int64_t K, double alpha, const uint8_t*
                    int c_fmt, const int64_t* rows, int64_t nrows, double* R, double* S,
                    int nthreads) {
   if (M < 0 || N < 0 || K < 0) return -1;
-  if (c_fmt != ORACLE_C_F32 && c_fmt != ORACLE_C_BF16) return -1;
+  if (c_fmt != ORACLE_C_F32 && c_fmt != ORACLE_C_BF16 && c_fmt != ORACLE_C_E4M3) return -1;
   if (rows == NULL) nrows = M;
   if (nrows == 0 || N == 0) return 0;
   init_tables();

@@ -425,3 +425,46 @@ def test_mx_quantize_matches_library_cast_and_error_bound():
             assert np.all(err[inr] <= np.abs(xb[inr]) * 2.0 ** -4 + sc * 2.0 ** -10)
             # saturated elements (|q| in (448, 512) by the scale rule) come back as 448
             assert np.all(np.abs(back[~inr]) == 448.0 * sc) and np.all(np.abs(xb[~inr]) < 512.0 * sc)
+
+
+def test_e4m3_round_golden():
+    for line in open(os.path.join(GOLDEN, "e4m3_round.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        x_s, code_s = line.split()
+        x = float.fromhex(x_s) if x_s.lstrip("-").startswith("0x") else float(x_s)
+        assert int(oracle.round_e4m3(np.array([x]))[0]) == int(code_s, 16), line
+
+
+def test_e4m3_round_grid_and_special_values():
+    """Every finite E4M3 value rounds to its own code (both zeros keep their sign); NaN
+    gives the NaN code; +-inf and everything at or past 448 saturate."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = oracle.decode(codes, "e4m3")
+    assert np.array_equal(oracle.round_e4m3(vals), codes)
+    got = oracle.round_e4m3(np.array([np.nan, np.inf, -np.inf, 448.0, 449.0, -1e300]))
+    assert list(got) == [0x7F, 0x7E, 0xFE, 0x7E, 0x7E, 0xFE]
+
+
+def test_e4m3_round_matches_library_cast_in_range():
+    """In range (|x| <= 448) the rounding equals torch's float8_e4m3fn cast (round to
+    nearest even, a library routine) on fp32-representable values, normal and subnormal."""
+    import torch
+    rng = np.random.default_rng(21)
+    x = np.concatenate([rng.standard_normal(20000) * 60.0, rng.uniform(-2.0 ** -5, 2.0 ** -5, 20000),
+                        rng.uniform(-448.0, 448.0, 20000)]).astype(np.float32)
+    mine = oracle.round_e4m3(x.astype(np.float64))
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    inr = np.abs(x) <= 448.0
+    assert inr.sum() > 55000
+    assert np.array_equal(mine[inr], lib[inr])
+
+
+def test_e4m3_output_beta_reads_e4m3():
+    """With an E4M3 C the beta term reads C's old codes as E4M3 values."""
+    A = np.ones((1, 2), dtype=np.uint16) * 0x3F80  # bf16 1.0
+    B = np.ones((2, 1), dtype=np.uint16) * 0x3F80
+    C = np.array([[0x48]], dtype=np.uint8)  # E4M3 4.0
+    R, _ = oracle.gemm(0, 0, 1, 1, 2, 1.0, A, 2, B, 1, 0.5, C, 1, oracle.IN_BF16, oracle.C_E4M3)
+    assert R[0, 0] == 2.0 + 0.5 * 4.0

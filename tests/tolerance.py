@@ -20,6 +20,12 @@ hardware-model bound instead: that instruction sums each group of 8 products aft
 aligning them to the group's largest exponent E and dropping the bits below 2^(E-13)
 (measured on gfx950).  Each group then loses less than 7 * 2^-13 of its largest
 product, at most 7 * 2^-13 * S over the whole sum; that term is added to the bound.
+
+E4M3 output (check_e4m3): the code must be the E4M3 rounding (nearest, ties to even,
+saturating) of some value within the accumulation bound B of R, i.e. lie between the
+codes of R - B and R + B (the rounding is monotone), with
+  B = |alpha| * S * (K * 2^-23 [+ 7 * 2^-13 on the native path]) + 2^-21 * (|R| + 1e-30)
+(the last term: the fp32 roundings of alpha * acc and of the beta term).
 """
 from __future__ import annotations
 
@@ -72,3 +78,22 @@ def check(C_bits: np.ndarray, c_dtype: str, R: np.ndarray, S: np.ndarray, K: int
         "n_outside_literal": n_literal,
         "n": int(C.size),
     }
+
+
+def check_e4m3(codes: np.ndarray, R: np.ndarray, S: np.ndarray, K: int, alpha: float = 1.0,
+               accumulate: str = "fp32") -> Dict:
+    import oracle
+    codes = np.asarray(codes, dtype=np.uint8)
+    assert codes.shape == R.shape == S.shape, (codes.shape, R.shape, S.shape)
+    per = max(K, 1) * 2.0 ** -23 + (7.0 * 2.0 ** -13 if accumulate == "e4m3_native" else 0.0)
+    B = abs(alpha) * S * per + 2.0 ** -21 * (np.abs(R) + 1e-30)
+    tab = oracle.decode(np.arange(256, dtype=np.uint8), "e4m3")
+    lo = tab[oracle.round_e4m3(R - B)]
+    hi = tab[oracle.round_e4m3(R + B)]
+    got = tab[codes]
+    finite = bool(np.isfinite(got).all())
+    inside = (got >= lo) & (got <= hi)
+    exact = oracle.round_e4m3(R)
+    return {"ok": finite and bool(inside.all()), "finite": finite, "n_outside": int((~inside).sum()),
+            "n_differ_from_rounded_R": int((codes != exact).sum()), "n": int(codes.size),
+            "n_saturated": int((np.abs(got) == 448.0).sum())}
