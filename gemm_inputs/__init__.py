@@ -218,3 +218,72 @@ def mx_operands(M: int, N: int, K: int, seeds=(0, 1, 2, 3), kind: str = "e4m3"):
 # The MXFP8 forward at the E4M3 forward shape (one CP8 rank of S = 128K): A [16384][5120],
 # B stored [N][K] = [5120][5120], C bf16.
 MX_FWD_SHAPE = (16384, 5120, 5120)
+
+
+# ---------------------------------------------------------------- BLAS3 family operands
+# Triangular and symmetric operands are stored as full n x n row-major arrays; only the
+# referenced triangle (lower: i >= j, upper: i <= j) carries the matrix.  The other
+# triangle -- and the diagonal, for a unit-diagonal operand -- is filled with NaN, so a
+# kernel that reads what it must not read produces NaN.
+
+LOWER, UPPER = 0, 1
+BF16_NAN = np.uint16(0x7FC0)
+
+
+def _referenced(n: int, uplo: int, strict: bool = False) -> np.ndarray:
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    if uplo == LOWER:
+        return (i > j) if strict else (i >= j)
+    return (i < j) if strict else (i <= j)
+
+
+def bf16_triangular(n: int, uplo: int, seed: int, unit: bool = False) -> np.ndarray:
+    """A well-conditioned triangular operand: off-diagonal entries U[-1,1)/sqrt(n), the
+    diagonal 1 + U[0,1) (condition number about 3 at every n, measured; the off-diagonal
+    part carries about a quarter of op(T) x).  Unreferenced entries are NaN; with unit
+    set the diagonal is NaN too (it must be taken as ones, never read)."""
+    rng = np.random.default_rng(seed)
+    off = (rng.random((n, n), dtype=np.float32) * np.float32(2.0) - np.float32(1.0)) / np.float32(np.sqrt(n))
+    diag = np.float32(1.0) + rng.random(n, dtype=np.float32)
+    bits = f32_to_bf16_bits(off)
+    dbits = f32_to_bf16_bits(diag)
+    out = np.full((n, n), BF16_NAN, dtype=np.uint16)
+    strict = _referenced(n, uplo, strict=True)
+    out[strict] = bits[strict]
+    if not unit:
+        out[np.arange(n), np.arange(n)] = dbits
+    return out
+
+
+def bf16_symmetric_stored(n: int, uplo: int, seed: int, kind: str = "uniform") -> np.ndarray:
+    """The uplo triangle (diagonal included) of a random matrix, U[-1,1) or N(0,1) in
+    bf16; the other triangle NaN."""
+    full = draw(kind, (n, n), seed, BF16)
+    out = np.full((n, n), BF16_NAN, dtype=np.uint16)
+    keep = _referenced(n, uplo)
+    out[keep] = full[keep]
+    return out
+
+
+def int_triangular(n: int, uplo: int, seed: int, unit: bool = True, nnz_per_row: int = 4) -> np.ndarray:
+    """An integer triangular operand whose inverse and every partial substitution stay
+    small exact binary numbers: off-diagonal entries in {-1, +1} only at (odd row, even
+    column) positions of the referenced triangle, about nnz_per_row per odd row, so the
+    strictly triangular part squares to zero; the diagonal is all ones (unit; stored as
+    NaN) or a power of two in {+-1, +-2, +-4}.  The unreferenced triangle is NaN."""
+    rng = np.random.default_rng(seed)
+    vals = np.zeros((n, n), dtype=np.float32)
+    for i in range(1, n, 2):
+        cols = np.arange(0, i, 2) if uplo == LOWER else np.arange(i + 1, n, 2)
+        if cols.size == 0:
+            continue
+        pick = rng.choice(cols, size=min(nnz_per_row, cols.size), replace=False)
+        vals[i, pick] = rng.choice(np.array([-1.0, 1.0], dtype=np.float32), size=pick.size)
+    out = np.full((n, n), BF16_NAN, dtype=np.uint16)
+    strict = _referenced(n, uplo, strict=True)
+    out[strict] = f32_to_bf16_bits(vals)[strict]
+    if not unit:
+        d = rng.choice(np.array([-4.0, -2.0, -1.0, 1.0, 2.0, 4.0], dtype=np.float32), size=n)
+        out[np.arange(n), np.arange(n)] = f32_to_bf16_bits(d)
+    return out
