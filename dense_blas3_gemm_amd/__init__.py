@@ -23,7 +23,11 @@ STATUS = {0: "SUCCESS", 1: "INVALID_VALUE", 2: "NOT_SUPPORTED", 3: "NOT_INITIALI
 EXPORTS = ["gemm_create", "gemm_destroy", "gemm_set_stream", "gemm_run", "gemm_run_mx",
            "gemm_quantize_mx", "gemm_check_args", "gemm_query_policy", "gemm_set_policy",
            "gemm_lds_probe", "gemm_policy_count", "gemm_policy_name", "gemm_version",
-           "gemm_status_string"]
+           "gemm_status_string", "gemm_syrk", "gemm_syr2k", "gemm_symm", "gemm_trmm", "gemm_trsm"]
+
+LOWER, UPPER = 0, 1
+LEFT, RIGHT = 0, 1
+NON_UNIT, UNIT = 0, 1
 
 _lib = None
 
@@ -87,9 +91,15 @@ def load_library():
     lib.gemm_version.restype = ctypes.c_char_p
     lib.gemm_status_string.argtypes = [i32]
     lib.gemm_status_string.restype = ctypes.c_char_p
+    lib.gemm_syrk.argtypes = [vp, i32, i32, i64, i64, f32, vp, i64, f32, vp, i64, i32]
+    lib.gemm_syr2k.argtypes = [vp, i32, i32, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, i32]
+    lib.gemm_symm.argtypes = [vp, i32, i32, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, i32]
+    lib.gemm_trmm.argtypes = [vp, i32, i32, i32, i32, i64, i64, f32, vp, i64, vp, i64, vp, i64, i32]
+    lib.gemm_trsm.argtypes = [vp, i32, i32, i32, i32, i64, i64, f32, vp, i64, vp, i64, i32]
     for fn in ["gemm_create", "gemm_destroy", "gemm_set_stream", "gemm_run", "gemm_check_args",
                "gemm_query_policy", "gemm_set_policy", "gemm_lds_probe", "gemm_policy_count",
-               "gemm_run_mx", "gemm_quantize_mx"]:
+               "gemm_run_mx", "gemm_quantize_mx", "gemm_syrk", "gemm_syr2k", "gemm_symm", "gemm_trmm",
+               "gemm_trsm"]:
         getattr(lib, fn).restype = i32
     _lib = lib
     return lib
@@ -248,6 +258,91 @@ class Gemm:
         st = self.lib.gemm_lds_probe(self.handle, int(kind), arr, int(iters), int(workgroups))
         if st != 0:
             raise GemmError("gemm_lds_probe", st)
+
+    # ---------------------------------------------------------------- BLAS3 family
+    # Raw C-ABI calls (device pointers; the handle's current stream) return the status;
+    # the tensor forms below bind torch's current stream and raise on an error.
+
+    def _bind(self, t):
+        stream = _current_stream(t.device)
+        if stream != self._stream:
+            self.set_stream(stream)
+
+    def syrk_raw(self, uplo, trans, N, K, alpha, A_ptr, lda, beta, C_ptr, ldc, dtype) -> int:
+        return self.lib.gemm_syrk(self.handle, int(uplo), int(trans), int(N), int(K), float(alpha),
+                                  ctypes.c_void_p(A_ptr), int(lda), float(beta), ctypes.c_void_p(C_ptr), int(ldc),
+                                  int(dtype))
+
+    def syr2k_raw(self, uplo, trans, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr, ldc, dtype) -> int:
+        return self.lib.gemm_syr2k(self.handle, int(uplo), int(trans), int(N), int(K), float(alpha),
+                                   ctypes.c_void_p(A_ptr), int(lda), ctypes.c_void_p(B_ptr), int(ldb), float(beta),
+                                   ctypes.c_void_p(C_ptr), int(ldc), int(dtype))
+
+    def symm_raw(self, side, uplo, M, N, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr, ldc, dtype) -> int:
+        return self.lib.gemm_symm(self.handle, int(side), int(uplo), int(M), int(N), float(alpha),
+                                  ctypes.c_void_p(A_ptr), int(lda), ctypes.c_void_p(B_ptr), int(ldb), float(beta),
+                                  ctypes.c_void_p(C_ptr), int(ldc), int(dtype))
+
+    def trmm_raw(self, side, uplo, transA, diag, M, N, alpha, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, dtype) -> int:
+        return self.lib.gemm_trmm(self.handle, int(side), int(uplo), int(transA), int(diag), int(M), int(N),
+                                  float(alpha), ctypes.c_void_p(A_ptr), int(lda), ctypes.c_void_p(B_ptr), int(ldb),
+                                  ctypes.c_void_p(C_ptr), int(ldc), int(dtype))
+
+    def trsm_raw(self, side, uplo, transA, diag, M, N, alpha, A_ptr, lda, B_ptr, ldb, dtype=BF16_BF16) -> int:
+        return self.lib.gemm_trsm(self.handle, int(side), int(uplo), int(transA), int(diag), int(M), int(N),
+                                  float(alpha), ctypes.c_void_p(A_ptr), int(lda), ctypes.c_void_p(B_ptr), int(ldb),
+                                  int(dtype))
+
+    def syrk(self, A, C, uplo=LOWER, trans=0, alpha=1.0, beta=0.0):
+        """C <- alpha*op(A)op(A)^T + beta*C on the uplo triangle (bf16 A; bf16 or fp32 C)."""
+        self._bind(C)
+        N = C.shape[0]
+        K = A.shape[0] if trans else A.shape[1]
+        st = self.syrk_raw(uplo, trans, N, K, alpha, _ptr(A), _ld(A), beta, _ptr(C), _ld(C),
+                           dtype_code("bf16", _c_kind(C)))
+        if st != 0:
+            raise GemmError("gemm_syrk", st)
+        return C
+
+    def syr2k(self, A, B, C, uplo=LOWER, trans=0, alpha=1.0, beta=0.0):
+        """C <- alpha*(op(A)op(B)^T + op(B)op(A)^T) + beta*C on the uplo triangle."""
+        self._bind(C)
+        N = C.shape[0]
+        K = A.shape[0] if trans else A.shape[1]
+        st = self.syr2k_raw(uplo, trans, N, K, alpha, _ptr(A), _ld(A), _ptr(B), _ld(B), beta, _ptr(C), _ld(C),
+                            dtype_code("bf16", _c_kind(C)))
+        if st != 0:
+            raise GemmError("gemm_syr2k", st)
+        return C
+
+    def symm(self, A, B, C, side=LEFT, uplo=LOWER, alpha=1.0, beta=0.0):
+        """C <- alpha*S*B (side LEFT) or alpha*B*S (RIGHT) + beta*C, S from A's uplo triangle."""
+        self._bind(C)
+        M, N = C.shape
+        st = self.symm_raw(side, uplo, M, N, alpha, _ptr(A), _ld(A), _ptr(B), _ld(B), beta, _ptr(C), _ld(C),
+                           dtype_code("bf16", _c_kind(C)))
+        if st != 0:
+            raise GemmError("gemm_symm", st)
+        return C
+
+    def trmm(self, A, B, C, side=LEFT, uplo=LOWER, transA=0, diag=NON_UNIT, alpha=1.0):
+        """C <- alpha*op(T)*B (side LEFT) or alpha*B*op(T) (RIGHT), T from A's uplo triangle."""
+        self._bind(C)
+        M, N = C.shape
+        st = self.trmm_raw(side, uplo, transA, diag, M, N, alpha, _ptr(A), _ld(A), _ptr(B), _ld(B), _ptr(C),
+                           _ld(C), dtype_code("bf16", _c_kind(C)))
+        if st != 0:
+            raise GemmError("gemm_trmm", st)
+        return C
+
+    def trsm(self, A, B, side=LEFT, uplo=LOWER, transA=0, diag=NON_UNIT, alpha=1.0):
+        """B <- X with op(T) X = alpha*B (side LEFT) or X op(T) = alpha*B (RIGHT), in place; bf16."""
+        self._bind(B)
+        M, N = B.shape
+        st = self.trsm_raw(side, uplo, transA, diag, M, N, alpha, _ptr(A), _ld(A), _ptr(B), _ld(B))
+        if st != 0:
+            raise GemmError("gemm_trsm", st)
+        return B
 
     def query_policy(self, M, N, K, transA=0, transB=0, dtype=BF16_BF16, A_ptr=0, lda=None,
                      B_ptr=0, ldb=None, C_ptr=0, ldc=None) -> str:

@@ -23,7 +23,8 @@ BUILD = os.path.join(PKG, "_build")
 # transpose case so that the four groups of instantiations build in parallel
 SOURCES = [("api.cpp", "api", []), ("policy.cpp", "policy", []), ("kernel_simt.hip", "kernel_simt", []),
            ("kernel_mfma.hip", "kernel_mfma", []), ("lds_probe.hip", "lds_probe", []),
-           ("quantize_mx.hip", "quantize_mx", [])] + [
+           ("quantize_mx.hip", "quantize_mx", []),
+           ("blas3.cpp", "blas3", []), ("blas3_kernels.hip", "blas3_kernels", [])] + [
     ("kernel_mfma_dma.hip", f"kernel_mfma_dma_{ta}{tb}", [f"-DDBGEMM_DMA_TA={ta}", f"-DDBGEMM_DMA_TB={tb}"])
     for ta in (0, 1) for tb in (0, 1)]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -9,7 +9,7 @@
 #include <mutex>
 #include <unordered_set>
 
-#include "gemm_internal.h"
+#include "blas3_internal.h"
 
 using namespace dbgemm;
 
@@ -279,12 +279,15 @@ gemm_status_t gemm_lds_probe(gemm_handle_t h, int kind, const uint32_t* offsets,
   return err == hipSuccess ? GEMM_STATUS_SUCCESS : GEMM_STATUS_LAUNCH_FAILED;
 }
 
-// Shared by gemm_run and gemm_run_mx once the arguments are checked.
-static gemm_status_t run_checked(const Handle* p, int transA, int transB, int64_t M, int64_t N, int64_t K,
-                                 float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
-                                 float beta, void* C, int64_t ldc, int dtype, const uint8_t* sa,
-                                 int64_t ldsa, const uint8_t* sb, int64_t ldsb) {
-  if (M == 0 || N == 0) return GEMM_STATUS_SUCCESS;
+// Enqueues one checked GEMM on `stream` (the device is current).  `forced` >= 0 pins a
+// policy with `forced_splits`; *unsupported is set when that policy cannot serve the call.
+static hipError_t enqueue_impl(int cu_count, hipStream_t stream, void* ws, int64_t ws_floats, int transA, int transB,
+                               int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                               const void* B, int64_t ldb, float beta, void* C, int64_t ldc, int dtype,
+                               const uint8_t* sa, int64_t ldsa, const uint8_t* sb, int64_t ldsb,
+                               const GemmExtras& x, int forced, int forced_splits, bool* unsupported) {
+  *unsupported = false;
+  if (M == 0 || N == 0) return hipSuccess;
   GemmArgs a{};
   a.A = A;
   a.B = B;
@@ -307,52 +310,110 @@ static gemm_status_t run_checked(const Handle* p, int transA, int transB, int64_
   a.sb = sb;
   a.ldsa = ldsa;
   a.ldsb = ldsb;
+  a.tri = x.tri;
+  a.kband = x.kband;
+  a.band_off = x.band_off;
+  a.dual = x.dual;
+  a.A2 = x.A2;
+  a.B2 = x.B2;
+  a.lda2 = x.lda2;
+  a.ldb2 = x.ldb2;
+  const bool extras = x.tri != TRI_NONE || x.kband != KBAND_NONE || x.dual;
 
+  if (K == 0 || alpha == 0.f) return launch_scale(a, stream);
+  Problem pr = make_problem(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, dtype, sa, ldsa, sb, ldsb);
+  if (extras) {
+    pr.blas3 = true;
+    pr.square_tiles = x.tri != TRI_NONE;
+    if (x.dual) {  // the second product must fit the same buffer descriptors' strides
+      const Problem p2 = make_problem(transA, transB, M, N, K, x.A2, x.lda2, x.B2, x.ldb2, C, ldc, dtype);
+      pr.fast_ok = pr.fast_ok && p2.fast_ok && x.lda2 == lda && x.ldb2 == ldb;
+    }
+  }
+  int idx, sp = 1;
+  if (forced >= 0) {
+    idx = forced;
+    sp = forced_splits;
+    if (!policy_serves(policy_at(idx), pr) || !split_allowed(policy_at(idx), pr, sp, ws_floats) ||
+        (extras && sp != 1)) {
+      *unsupported = true;
+      return hipSuccess;
+    }
+  } else {
+    idx = policy_select(pr, cu_count, extras ? 0 : ws_floats, &sp);
+  }
+  const Policy& pol = policy_at(idx);
+  if (pol.kind == KIND_SIMT) {
+    if ((M + 63) / 64 > 65535) {
+      *unsupported = true;
+      return hipSuccess;
+    }
+    return launch_simt(a, stream);
+  }
+  a.tiles_m = (int)((M + pol.BM - 1) / pol.BM);
+  a.tiles_n = (int)((N + pol.BN - 1) / pol.BN);
+  a.group = pol.group;
+  a.raster_n = pol.raster_n;
+  a.xcd = pol.xcd;
+  a.swizzle = pol.swizzle;
+  a.krot = extras ? 0 : pol.krot;
+  a.splits = sp;
+  a.kt_per_split = (int)split_kt(pol, K, sp);
+  if (sp > 1) a.ws = (float*)ws;
+  return pol.pipe == 1 ? launch_mfma_dma(pol, a, stream) : launch_mfma_staged(pol, a, stream);
+}
+
+// Shared by gemm_run and gemm_run_mx once the arguments are checked.
+static gemm_status_t run_checked(const Handle* p, int transA, int transB, int64_t M, int64_t N, int64_t K,
+                                 float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+                                 float beta, void* C, int64_t ldc, int dtype, const uint8_t* sa,
+                                 int64_t ldsa, const uint8_t* sb, int64_t ldsb) {
+  if (M == 0 || N == 0) return GEMM_STATUS_SUCCESS;
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess) return GEMM_STATUS_INTERNAL;
   if (cur != p->device && hipSetDevice(p->device) != hipSuccess) return GEMM_STATUS_INTERNAL;
-
-  hipError_t err;
-  if (K == 0 || alpha == 0.f) {
-    err = launch_scale(a, p->stream);
-  } else {
-    const Problem pr = make_problem(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, dtype, sa, ldsa, sb, ldsb);
-    int idx, sp = 1;
-    if (p->forced >= 0) {
-      idx = p->forced;
-      sp = p->forced_splits;
-      if (!policy_serves(policy_at(idx), pr) || !split_allowed(policy_at(idx), pr, sp, p->ws_floats())) {
-        if (cur != p->device) (void)hipSetDevice(cur);
-        return GEMM_STATUS_NOT_SUPPORTED;
-      }
-    } else {
-      idx = policy_select(pr, p->cu_count, p->ws_floats(), &sp);
-    }
-    const Policy& pol = policy_at(idx);
-    if (pol.kind == KIND_SIMT) {
-      if ((M + 63) / 64 > 65535) {
-        if (cur != p->device) (void)hipSetDevice(cur);
-        return GEMM_STATUS_NOT_SUPPORTED;
-      }
-      err = launch_simt(a, p->stream);
-    } else {
-      a.tiles_m = (int)((M + pol.BM - 1) / pol.BM);
-      a.tiles_n = (int)((N + pol.BN - 1) / pol.BN);
-      a.group = pol.group;
-      a.raster_n = pol.raster_n;
-      a.xcd = pol.xcd;
-      a.swizzle = pol.swizzle;
-      a.krot = pol.krot;
-      a.splits = sp;
-      a.kt_per_split = (int)split_kt(pol, K, sp);
-      if (sp > 1) a.ws = (float*)p->ws;
-      err = pol.pipe == 1 ? launch_mfma_dma(pol, a, p->stream) : launch_mfma_staged(pol, a, p->stream);
-    }
-  }
+  bool unsupported = false;
+  const hipError_t err = enqueue_impl(p->cu_count, p->stream, p->ws, p->ws_floats(), transA, transB, M, N, K, alpha,
+                                      A, lda, B, ldb, beta, C, ldc, dtype, sa, ldsa, sb, ldsb, GemmExtras{},
+                                      p->forced, p->forced_splits, &unsupported);
   if (cur != p->device) (void)hipSetDevice(cur);
+  if (unsupported) return GEMM_STATUS_NOT_SUPPORTED;
   if (err != hipSuccess) return GEMM_STATUS_LAUNCH_FAILED;
   return GEMM_STATUS_SUCCESS;
 }
+
+}  // extern "C"
+
+namespace dbgemm {
+bool handle_view(gemm_handle_t h, HandleView* v) {
+  if (!live(h)) return false;
+  const Handle* p = reinterpret_cast<const Handle*>(h);
+  v->device = p->device;
+  v->cu_count = p->cu_count;
+  v->stream = p->stream;
+  v->ws = p->ws;
+  v->ws_bytes = p->ws ? kWorkspaceBytes : 0;
+  return true;
+}
+
+hipError_t gemm_enqueue(const HandleView& hv, int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+                        const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C, int64_t ldc,
+                        int dtype, const GemmExtras& x) {
+  bool unsupported = false;
+  // never split: the BLAS3 operations keep their operands in the workspace
+  const hipError_t e = enqueue_impl(hv.cu_count, hv.stream, nullptr, 0, transA,
+                                    transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, nullptr, 0, nullptr,
+                                    0, x, x.policy, 1, &unsupported);
+  return unsupported ? hipErrorInvalidConfiguration : e;
+}
+
+bool gemm_fast_ok(int transA, int transB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                  int64_t ldb, const void* C, int64_t ldc, int dtype) {
+  return make_problem(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, dtype).fast_ok;
+}
+}  // namespace dbgemm
+
+extern "C" {
 
 gemm_status_t gemm_run(gemm_handle_t h, int transA, int transB, int64_t M, int64_t N, int64_t K,
                        float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,

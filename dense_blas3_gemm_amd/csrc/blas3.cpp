@@ -1,0 +1,336 @@
+// Host side of the single-GPU BLAS3 family (declared and documented in include/gemm.h):
+// argument checks, then the GEMM launches, and the operand preparation each operation
+// is built from ("BLASMp development notes", section 2: every operator of the library
+// runs its local compute on a GEMM).
+//
+//   SYRK   one GEMM (A and A, the second read transposed) over a triangle of tiles;
+//   SYR2K  one GEMM whose K loop runs over both products, over a triangle of tiles;
+//   SYMM   the symmetric matrix expanded into the workspace (row panels), then GEMMs;
+//   TRMM   the triangle expanded with zeros into the workspace (panels), then GEMMs whose
+//          tiles skip the K tiles that meet only zeros;
+//   TRSM   the diagonal blocks inverted in one launch, then a recursive split: solve one
+//          half, update the other half with a GEMM (alpha*B - T21*X1), solve it; a leaf
+//          block is the product of its inverted diagonal block with its rows of B.
+#include <climits>
+#include <cmath>
+
+#include "blas3_internal.h"
+
+using namespace dbgemm;
+
+namespace {
+
+bool bf16_dtype(int d) { return d == GEMM_BF16_BF16 || d == GEMM_BF16_F32; }
+int c_bytes(int d) { return d == GEMM_BF16_F32 ? 4 : 2; }
+int64_t at_least_1(int64_t v) { return v > 1 ? v : 1; }
+int64_t pad8(int64_t v) { return (v + 7) / 8 * 8; }
+bool valid_flag(int f) { return f == 0 || f == 1; }
+bool size_ok(int64_t v) { return v >= 0 && v <= INT_MAX; }
+
+const void* off(const void* p, int64_t row, int64_t col, int64_t ld, int es) {
+  return (const char*)p + (row * ld + col) * es;
+}
+void* off(void* p, int64_t row, int64_t col, int64_t ld, int es) { return (char*)p + (row * ld + col) * es; }
+
+// Makes the handle's device current for the lifetime of the object.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false, switched = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) return;
+    if (prev != dev) {
+      if (hipSetDevice(dev) != hipSuccess) return;
+      switched = true;
+    }
+    ok = true;
+  }
+  ~DeviceGuard() {
+    if (switched) (void)hipSetDevice(prev);
+  }
+};
+
+gemm_status_t status_of(hipError_t e) {
+  if (e == hipSuccess) return GEMM_STATUS_SUCCESS;
+  return e == hipErrorInvalidConfiguration ? GEMM_STATUS_NOT_SUPPORTED : GEMM_STATUS_LAUNCH_FAILED;
+}
+
+// Rows of an n-wide (padded) bf16 panel that fit the workspace, in whole 256-row tiles;
+// 0 when not even one tile row fits.
+int64_t panel_rows(const HandleView& hv, int64_t n) {
+  if (!hv.ws) return 0;
+  const int64_t per_row = pad8(n) * 2;
+  int64_t p = (int64_t)(hv.ws_bytes / (size_t)per_row) / 256 * 256;
+  return p;
+}
+
+// The policy a TRSM leaf runs with when it updates its block of B in place: one
+// 128-row (128-column) tile spans the whole leaf, so each workgroup reads the part of B
+// it overwrites, all of it before its epilogue, and no other workgroup reads it.
+int leaf_policy() {
+  static const int idx = policy_find("bf16_dma_m128n128k64_w2x4_mt16_s4");
+  return idx;
+}
+
+struct Trsm {
+  HandleView hv;
+  int side, transA;
+  bool opT_lower;
+  int64_t M, N;
+  const void* A;
+  int64_t lda;
+  void* B;
+  int64_t ldb;
+  uint16_t* inv;      // inverted diagonal blocks, [blocks][NB][NB]
+  uint16_t* scratch;  // one block row (column) of B, for leaves that cannot run in place
+  hipError_t err = hipSuccess;
+
+  void keep(hipError_t e) {
+    if (err == hipSuccess && e != hipSuccess) err = e;
+  }
+  // op(T)[r0 .. , c0 .. ] as a GEMM operand: the stored block and the transpose flag
+  const void* opT_block(int64_t r0, int64_t c0) const {
+    return transA ? off(A, c0, r0, lda, 2) : off(A, r0, c0, lda, 2);
+  }
+
+  void leaf(int64_t o, int64_t nb, float alpha) {
+    const uint16_t* ib = inv + (o / kTrsmNB) * kTrsmNB * kTrsmNB;
+    GemmExtras x;
+    if (side == GEMM_SIDE_LEFT) {  // X rows [o, o+nb) = alpha * op(inv) * B rows
+      void* Bb = off(B, o, 0, ldb, 2);
+      if (gemm_fast_ok(transA, 0, nb, N, nb, ib, kTrsmNB, Bb, ldb, Bb, ldb, GEMM_BF16_BF16) && leaf_policy() >= 0) {
+        x.policy = leaf_policy();
+        keep(gemm_enqueue(hv, transA, 0, nb, N, nb, alpha, ib, kTrsmNB, Bb, ldb, 0.f, Bb, ldb, GEMM_BF16_BF16, x));
+      } else {
+        const int64_t lds = pad8(N);
+        keep(gemm_enqueue(hv, transA, 0, nb, N, nb, alpha, ib, kTrsmNB, Bb, ldb, 0.f, scratch, lds, GEMM_BF16_BF16,
+                          x));
+        keep(launch_copy2d(scratch, lds, Bb, ldb, (int)nb, (int)N, hv.stream));
+      }
+    } else {  // X columns [o, o+nb) = alpha * B columns * op(inv)
+      void* Bb = off(B, 0, o, ldb, 2);
+      if (gemm_fast_ok(0, transA, M, nb, nb, Bb, ldb, ib, kTrsmNB, Bb, ldb, GEMM_BF16_BF16) && leaf_policy() >= 0) {
+        x.policy = leaf_policy();
+        keep(gemm_enqueue(hv, 0, transA, M, nb, nb, alpha, Bb, ldb, ib, kTrsmNB, 0.f, Bb, ldb, GEMM_BF16_BF16, x));
+      } else {
+        keep(gemm_enqueue(hv, 0, transA, M, nb, nb, alpha, Bb, ldb, ib, kTrsmNB, 0.f, scratch, kTrsmNB,
+                          GEMM_BF16_BF16, x));
+        keep(launch_copy2d(scratch, kTrsmNB, Bb, ldb, (int)M, (int)nb, hv.stream));
+      }
+    }
+  }
+
+  // Rows [r0, r0+m) of op(T) X = alpha * B (left side).
+  void left(int64_t r0, int64_t m, float alpha) {
+    if (m <= kTrsmNB) return leaf(r0, m, alpha);
+    const int64_t m1 = ((m + 1) / 2 + kTrsmNB - 1) / kTrsmNB * kTrsmNB;
+    const GemmExtras x;
+    if (opT_lower) {
+      left(r0, m1, alpha);
+      keep(gemm_enqueue(hv, transA, 0, m - m1, N, m1, -1.f, opT_block(r0 + m1, r0), lda, off(B, r0, 0, ldb, 2), ldb,
+                        alpha, off(B, r0 + m1, 0, ldb, 2), ldb, GEMM_BF16_BF16, x));
+      left(r0 + m1, m - m1, 1.f);
+    } else {
+      left(r0 + m1, m - m1, alpha);
+      keep(gemm_enqueue(hv, transA, 0, m1, N, m - m1, -1.f, opT_block(r0, r0 + m1), lda,
+                        off(B, r0 + m1, 0, ldb, 2), ldb, alpha, off(B, r0, 0, ldb, 2), ldb, GEMM_BF16_BF16, x));
+      left(r0, m1, 1.f);
+    }
+  }
+
+  // Columns [c0, c0+n) of X op(T) = alpha * B (right side).
+  void right(int64_t c0, int64_t n, float alpha) {
+    if (n <= kTrsmNB) return leaf(c0, n, alpha);
+    const int64_t n1 = ((n + 1) / 2 + kTrsmNB - 1) / kTrsmNB * kTrsmNB;
+    const GemmExtras x;
+    if (!opT_lower) {  // X1 first: X2 op(T)22 = alpha*B2 - X1 op(T)12
+      right(c0, n1, alpha);
+      keep(gemm_enqueue(hv, 0, transA, M, n - n1, n1, -1.f, off(B, 0, c0, ldb, 2), ldb, opT_block(c0, c0 + n1), lda,
+                        alpha, off(B, 0, c0 + n1, ldb, 2), ldb, GEMM_BF16_BF16, x));
+      right(c0 + n1, n - n1, 1.f);
+    } else {  // X2 first: X1 op(T)11 = alpha*B1 - X2 op(T)21
+      right(c0 + n1, n - n1, alpha);
+      keep(gemm_enqueue(hv, 0, transA, M, n1, n - n1, -1.f, off(B, 0, c0 + n1, ldb, 2), ldb, opT_block(c0 + n1, c0),
+                        lda, alpha, off(B, 0, c0, ldb, 2), ldb, GEMM_BF16_BF16, x));
+      right(c0, n1, 1.f);
+    }
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+gemm_status_t gemm_syrk(gemm_handle_t h, int uplo, int trans, int64_t N, int64_t K, float alpha, const void* A,
+                        int64_t lda, float beta, void* C, int64_t ldc, int dtype) {
+  HandleView hv;
+  if (!handle_view(h, &hv)) return GEMM_STATUS_NOT_INITIALIZED;
+  if (!valid_flag(uplo) || !valid_flag(trans) || !bf16_dtype(dtype)) return GEMM_STATUS_INVALID_VALUE;
+  if (!size_ok(N) || !size_ok(K)) return GEMM_STATUS_INVALID_VALUE;
+  if (lda < at_least_1(trans ? N : K) || ldc < at_least_1(N)) return GEMM_STATUS_INVALID_VALUE;
+  if (!std::isfinite(alpha) || !std::isfinite(beta)) return GEMM_STATUS_NOT_SUPPORTED;
+  if (N == 0) return GEMM_STATUS_SUCCESS;
+  if (!C || (K > 0 && alpha != 0.f && !A)) return GEMM_STATUS_INVALID_VALUE;
+  DeviceGuard g(hv.device);
+  if (!g.ok) return GEMM_STATUS_INTERNAL;
+  GemmExtras x;
+  x.tri = uplo == GEMM_LOWER ? TRI_LOWER : TRI_UPPER;
+  return status_of(gemm_enqueue(hv, trans, 1 - trans, N, N, K, alpha, A, lda, A, lda, beta, C, ldc, dtype, x));
+}
+
+gemm_status_t gemm_syr2k(gemm_handle_t h, int uplo, int trans, int64_t N, int64_t K, float alpha, const void* A,
+                         int64_t lda, const void* B, int64_t ldb, float beta, void* C, int64_t ldc, int dtype) {
+  HandleView hv;
+  if (!handle_view(h, &hv)) return GEMM_STATUS_NOT_INITIALIZED;
+  if (!valid_flag(uplo) || !valid_flag(trans) || !bf16_dtype(dtype)) return GEMM_STATUS_INVALID_VALUE;
+  if (!size_ok(N) || !size_ok(K)) return GEMM_STATUS_INVALID_VALUE;
+  const int64_t row = at_least_1(trans ? N : K);
+  if (lda < row || ldb < row || ldc < at_least_1(N)) return GEMM_STATUS_INVALID_VALUE;
+  if (!std::isfinite(alpha) || !std::isfinite(beta)) return GEMM_STATUS_NOT_SUPPORTED;
+  if (N == 0) return GEMM_STATUS_SUCCESS;
+  if (!C || (K > 0 && alpha != 0.f && (!A || !B))) return GEMM_STATUS_INVALID_VALUE;
+  DeviceGuard g(hv.device);
+  if (!g.ok) return GEMM_STATUS_INTERNAL;
+  GemmExtras x;
+  x.tri = uplo == GEMM_LOWER ? TRI_LOWER : TRI_UPPER;
+  x.dual = 1;  // op(A) op(B)^T, then op(B) op(A)^T
+  x.A2 = B;
+  x.lda2 = ldb;
+  x.B2 = A;
+  x.ldb2 = lda;
+  return status_of(gemm_enqueue(hv, trans, 1 - trans, N, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, x));
+}
+
+gemm_status_t gemm_symm(gemm_handle_t h, int side, int uplo, int64_t M, int64_t N, float alpha, const void* A,
+                        int64_t lda, const void* B, int64_t ldb, float beta, void* C, int64_t ldc, int dtype) {
+  HandleView hv;
+  if (!handle_view(h, &hv)) return GEMM_STATUS_NOT_INITIALIZED;
+  if (!valid_flag(side) || !valid_flag(uplo) || !bf16_dtype(dtype)) return GEMM_STATUS_INVALID_VALUE;
+  if (!size_ok(M) || !size_ok(N)) return GEMM_STATUS_INVALID_VALUE;
+  const int64_t n = side == GEMM_SIDE_LEFT ? M : N;
+  if (lda < at_least_1(n) || ldb < at_least_1(N) || ldc < at_least_1(N)) return GEMM_STATUS_INVALID_VALUE;
+  if (!std::isfinite(alpha) || !std::isfinite(beta)) return GEMM_STATUS_NOT_SUPPORTED;
+  if (M == 0 || N == 0) return GEMM_STATUS_SUCCESS;
+  if (!C || (alpha != 0.f && (!A || !B))) return GEMM_STATUS_INVALID_VALUE;
+  DeviceGuard g(hv.device);
+  if (!g.ok) return GEMM_STATUS_INTERNAL;
+  const int es = c_bytes(dtype);
+  const GemmExtras x;
+  if (alpha == 0.f)  // C <- beta*C
+    return status_of(gemm_enqueue(hv, 0, 0, M, N, 0, 0.f, nullptr, 1, nullptr, 1, beta, C, ldc, dtype, x));
+  const int64_t P = panel_rows(hv, n);
+  if (P <= 0) return GEMM_STATUS_NOT_SUPPORTED;
+  const int64_t npad = pad8(n);
+  hipError_t err = hipSuccess;
+  // Left: C rows [p0, p0+rows) = alpha * S[p0 .., :] B + beta * C.  Right: C columns
+  // [p0, p0+rows) = alpha * B S[:, p0 ..] + beta * C, with S[:, p0 ..] = S[p0 .., :]^T.
+  const int64_t outer = side == GEMM_SIDE_LEFT ? M : N;
+  for (int64_t p0 = 0; p0 < outer && err == hipSuccess; p0 += P) {
+    const int64_t rows = outer - p0 < P ? outer - p0 : P;
+    err = launch_expand_sym(A, lda, hv.ws, npad, (int)p0, 0, (int)rows, (int)n, (int)npad, (int)n, uplo, hv.stream);
+    if (err != hipSuccess) break;
+    if (side == GEMM_SIDE_LEFT)
+      err = gemm_enqueue(hv, 0, 0, rows, N, n, alpha, hv.ws, npad, B, ldb, beta, off(C, p0, 0, ldc, es), ldc, dtype,
+                         x);
+    else
+      err = gemm_enqueue(hv, 0, 1, M, rows, n, alpha, B, ldb, hv.ws, npad, beta, off(C, 0, p0, ldc, es), ldc, dtype,
+                         x);
+  }
+  return status_of(err);
+}
+
+gemm_status_t gemm_trmm(gemm_handle_t h, int side, int uplo, int transA, int diag, int64_t M, int64_t N, float alpha,
+                        const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int dtype) {
+  HandleView hv;
+  if (!handle_view(h, &hv)) return GEMM_STATUS_NOT_INITIALIZED;
+  if (!valid_flag(side) || !valid_flag(uplo) || !valid_flag(transA) || !valid_flag(diag) || !bf16_dtype(dtype))
+    return GEMM_STATUS_INVALID_VALUE;
+  if (!size_ok(M) || !size_ok(N)) return GEMM_STATUS_INVALID_VALUE;
+  const int64_t n = side == GEMM_SIDE_LEFT ? M : N;
+  if (lda < at_least_1(n) || ldb < at_least_1(N) || ldc < at_least_1(N)) return GEMM_STATUS_INVALID_VALUE;
+  if (!std::isfinite(alpha)) return GEMM_STATUS_NOT_SUPPORTED;
+  if (M == 0 || N == 0) return GEMM_STATUS_SUCCESS;
+  if (!C || (alpha != 0.f && (!A || !B))) return GEMM_STATUS_INVALID_VALUE;
+  DeviceGuard g(hv.device);
+  if (!g.ok) return GEMM_STATUS_INTERNAL;
+  const int es = c_bytes(dtype);
+  if (alpha == 0.f)  // C <- 0
+    return status_of(gemm_enqueue(hv, 0, 0, M, N, 0, 0.f, nullptr, 1, nullptr, 1, 0.f, C, ldc, dtype, GemmExtras{}));
+  const int64_t P = panel_rows(hv, n);
+  if (P <= 0) return GEMM_STATUS_NOT_SUPPORTED;
+  const bool opT_lower = (uplo == GEMM_LOWER) != (transA != 0);
+  hipError_t err = hipSuccess;
+  const int64_t outer = side == GEMM_SIDE_LEFT ? M : N;
+  for (int64_t p0 = 0; p0 < outer && err == hipSuccess; p0 += P) {
+    const int64_t w = outer - p0 < P ? outer - p0 : P;  // rows (left) / columns (right) of C
+    GemmExtras x;
+    x.band_off = (int)p0;
+    // The panel of op(T) this part of C needs -- rows [p0, p0+w) of op(T) (left) or its
+    // columns (right) -- expanded from T's rows or columns as the transpose dictates.
+    const bool panel_is_rows = (side == GEMM_SIDE_LEFT) == (transA == 0);
+    int64_t ldw;
+    if (panel_is_rows) {  // T rows [p0, p0+w) x all n columns
+      ldw = pad8(n);
+      err = launch_expand_tri(A, lda, hv.ws, ldw, (int)p0, 0, (int)w, (int)n, (int)ldw, uplo, diag, hv.stream);
+    } else {  // T all n rows x columns [p0, p0+w)
+      ldw = pad8(w);
+      err = launch_expand_tri(A, lda, hv.ws, ldw, 0, (int)p0, (int)n, (int)w, (int)ldw, uplo, diag, hv.stream);
+    }
+    if (err != hipSuccess) break;
+    if (side == GEMM_SIDE_LEFT) {  // C rows = alpha * op(T)[p0.., :] B
+      x.kband = opT_lower ? KBAND_A_LOWER : KBAND_A_UPPER;
+      err = gemm_enqueue(hv, transA, 0, w, N, M, alpha, hv.ws, ldw, B, ldb, 0.f, off(C, p0, 0, ldc, es), ldc, dtype,
+                         x);
+    } else {  // C columns = alpha * B op(T)[:, p0..]
+      x.kband = opT_lower ? KBAND_B_LOWER : KBAND_B_UPPER;
+      err = gemm_enqueue(hv, 0, transA, M, w, N, alpha, B, ldb, hv.ws, ldw, 0.f, off(C, 0, p0, ldc, es), ldc, dtype,
+                         x);
+    }
+  }
+  return status_of(err);
+}
+
+gemm_status_t gemm_trsm(gemm_handle_t h, int side, int uplo, int transA, int diag, int64_t M, int64_t N, float alpha,
+                        const void* A, int64_t lda, void* B, int64_t ldb, int dtype) {
+  HandleView hv;
+  if (!handle_view(h, &hv)) return GEMM_STATUS_NOT_INITIALIZED;
+  if (!valid_flag(side) || !valid_flag(uplo) || !valid_flag(transA) || !valid_flag(diag) || dtype != GEMM_BF16_BF16)
+    return GEMM_STATUS_INVALID_VALUE;
+  if (!size_ok(M) || !size_ok(N)) return GEMM_STATUS_INVALID_VALUE;
+  const int64_t n = side == GEMM_SIDE_LEFT ? M : N;
+  if (lda < at_least_1(n) || ldb < at_least_1(N)) return GEMM_STATUS_INVALID_VALUE;
+  if (!std::isfinite(alpha)) return GEMM_STATUS_NOT_SUPPORTED;
+  if (M == 0 || N == 0) return GEMM_STATUS_SUCCESS;
+  if (!B || (alpha != 0.f && !A)) return GEMM_STATUS_INVALID_VALUE;
+  DeviceGuard g(hv.device);
+  if (!g.ok) return GEMM_STATUS_INTERNAL;
+  if (alpha == 0.f)  // X = 0
+    return status_of(gemm_enqueue(hv, 0, 0, M, N, 0, 0.f, nullptr, 1, nullptr, 1, 0.f, B, ldb, dtype, GemmExtras{}));
+  const int64_t blocks = (n + kTrsmNB - 1) / kTrsmNB;
+  const size_t inv_bytes = (size_t)blocks * kTrsmNB * kTrsmNB * 2;
+  const size_t scratch_bytes = side == GEMM_SIDE_LEFT ? (size_t)kTrsmNB * pad8(N) * 2 : (size_t)M * kTrsmNB * 2;
+  if (!hv.ws || inv_bytes + scratch_bytes > hv.ws_bytes) return GEMM_STATUS_NOT_SUPPORTED;
+  Trsm t;
+  t.hv = hv;
+  t.side = side;
+  t.transA = transA;
+  t.opT_lower = (uplo == GEMM_LOWER) != (transA != 0);
+  t.M = M;
+  t.N = N;
+  t.A = A;
+  t.lda = lda;
+  t.B = B;
+  t.ldb = ldb;
+  t.inv = (uint16_t*)hv.ws;
+  t.scratch = (uint16_t*)((char*)hv.ws + (inv_bytes + 255) / 256 * 256);
+  if ((size_t)((char*)t.scratch - (char*)hv.ws) + scratch_bytes > hv.ws_bytes) return GEMM_STATUS_NOT_SUPPORTED;
+  t.keep(launch_invert_diag(A, lda, (int)n, uplo, diag, t.inv, hv.stream));
+  if (t.err == hipSuccess) {
+    if (side == GEMM_SIDE_LEFT)
+      t.left(0, M, alpha);
+    else
+      t.right(0, N, alpha);
+  }
+  return status_of(t.err);
+}
+
+}  // extern "C"

@@ -1,0 +1,181 @@
+// Device kernels of the single-GPU BLAS3 family that are not GEMMs ("BLASMp development
+// notes", section 2: SYMM, TRMM and TRSM built on a GEMM core).  The products themselves
+// run on the GEMM kernels; these kernels prepare their operands:
+//
+//   * expand_tri_kernel: a rectangle of the dense matrix a triangular operand stands for
+//     (its stored triangle, zeros elsewhere, ones on a unit diagonal), so that TRMM is a
+//     GEMM whose tiles skip the zero K band;
+//   * expand_sym_kernel: a rectangle of the dense symmetric matrix a stored triangle
+//     stands for, mirrored through LDS so that both the reads and the writes are
+//     row-contiguous;
+//   * invert_diag_kernel: the inverses of the diagonal blocks of a triangular operand, in
+//     fp32, stored as bf16: TRSM then applies each diagonal block as a product.
+//
+// Every kernel reads the stored triangle only: the other triangle (and a unit diagonal)
+// may hold anything, NaN included.
+#include "blas3_internal.h"
+
+namespace dbgemm {
+namespace {
+
+__device__ inline float bf16f(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+__device__ inline uint16_t f2bf(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
+
+__device__ inline bool referenced(int i, int j, int uplo) { return uplo == 0 ? i >= j : i <= j; }
+
+// dst[r][c] (r < rows, c < cols, leading dimension ldd) = T[r0 + r][c0 + c] of the n x n
+// triangular matrix T.  One thread per 8 consecutive columns of one row; columns past
+// `cols` up to the padded width are written as zeros.
+__global__ __launch_bounds__(256) void expand_tri_kernel(const uint16_t* __restrict__ src, int64_t lds,
+                                                         uint16_t* __restrict__ dst, int64_t ldd, int r0, int c0,
+                                                         int rows, int cols, int cols_pad, int uplo, int unit) {
+  const int groups = cols_pad / 8;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (int64_t)rows * groups) return;
+  const int r = (int)(t / groups), c8 = (int)(t % groups) * 8;
+  const int i = r0 + r;
+  uint16_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = c8 + e, j = c0 + c;
+    float x = 0.f;
+    if (c < cols) {
+      if (i == j && unit) x = 1.f;
+      else if (referenced(i, j, uplo)) x = bf16f(src[(int64_t)i * lds + j]);
+    }
+    v[e] = f2bf(x);
+  }
+  uint4 w;
+  w.x = v[0] | ((uint32_t)v[1] << 16);
+  w.y = v[2] | ((uint32_t)v[3] << 16);
+  w.z = v[4] | ((uint32_t)v[5] << 16);
+  w.w = v[6] | ((uint32_t)v[7] << 16);
+  *(uint4*)(dst + (int64_t)r * ldd + c8) = w;
+}
+
+// dst[r][c] = S[r0 + r][c0 + c] of the symmetric matrix S whose uplo triangle is stored
+// in src.  Workgroup (bx, by) writes the 64 x 64 output block at rows 64*by, columns
+// 64*bx; its elements come from src directly where (i, j) is referenced and from the
+// mirrored block (read row-wise, transposed in LDS) elsewhere.  Columns past `cols` up to
+// the padded width are zeros.
+constexpr int SB = 64;
+__global__ __launch_bounds__(256) void expand_sym_kernel(const uint16_t* __restrict__ src, int64_t lds,
+                                                         uint16_t* __restrict__ dst, int64_t ldd, int r0, int c0,
+                                                         int rows, int cols, int cols_pad, int n, int uplo) {
+  __shared__ uint16_t mir[SB][SB + 2];
+  const int br = blockIdx.y * SB, bc = blockIdx.x * SB;  // output block origin
+  const int gi0 = r0 + br, gj0 = c0 + bc;                  // in S
+  // does the block need the mirror (any element outside the stored triangle)?
+  const bool need_mirror = uplo == 0 ? (gi0 < gj0 + SB - 1) : (gi0 + SB - 1 > gj0);
+  if (need_mirror) {
+    // mir[x][y] = src[gj0 + y][gi0 + x] (row gj0 + y of src, read along its columns)
+    for (int e = threadIdx.x; e < SB * SB; e += 256) {
+      const int y = e / SB, x = e % SB;
+      const int si = gj0 + y, sj = gi0 + x;
+      uint16_t v = 0;
+      if (si < n && sj < n && referenced(si, sj, uplo)) v = src[(int64_t)si * lds + sj];
+      mir[x][y] = v;
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < SB * SB; e += 256) {
+    const int y = e / SB, x = e % SB;
+    const int r = br + y, c = bc + x;
+    if (r >= rows || c >= cols_pad) continue;
+    const int i = r0 + r, j = c0 + c;
+    uint16_t v = 0;
+    if (c < cols && i < n && j < n) v = referenced(i, j, uplo) ? src[(int64_t)i * lds + j] : mir[y][x];
+    dst[(int64_t)r * ldd + c] = v;
+  }
+}
+
+// Inverse of each diagonal block T_bb (rows and columns [b*NB, b*NB + nb), nb = NB except
+// for a shorter last block) of the n x n triangular T.  Workgroup b, thread c computes
+// column c of inv(T_bb) by substitution in fp32: lower blocks forward from row c, upper
+// blocks backward from row c.  The block is padded to NB x NB with the identity.  The
+// result, zeros outside the triangle, is stored as bf16 at dst + b*NB*NB, [NB][NB].
+__global__ __launch_bounds__(kTrsmNB) void invert_diag_kernel(const uint16_t* __restrict__ src, int64_t lds, int n,
+                                                              int uplo, int unit, uint16_t* __restrict__ dst) {
+  constexpr int NB = kTrsmNB;
+  __shared__ float T[NB][NB + 1];
+  __shared__ float X[NB][NB + 1];
+  const int b = blockIdx.x, o = b * NB;
+  const int nb = n - o < NB ? n - o : NB;
+  const int c = threadIdx.x;
+  for (int e = c; e < NB * NB; e += NB) {
+    const int i = e / NB, j = e % NB;
+    float v = 0.f;
+    if (i == j && (unit || i >= nb)) v = 1.f;
+    else if (i < nb && j < nb && referenced(i, j, uplo)) v = bf16f(src[(int64_t)(o + i) * lds + o + j]);
+    T[i][j] = v;
+  }
+  __syncthreads();
+  if (uplo == 0) {
+    for (int r = 0; r < NB; ++r) {
+      float s = r == c ? 1.f : 0.f;
+      for (int k = c; k < r; ++k) s -= T[r][k] * X[k][c];
+      X[r][c] = r < c ? 0.f : s / T[r][r];
+    }
+  } else {
+    for (int r = NB - 1; r >= 0; --r) {
+      float s = r == c ? 1.f : 0.f;
+      for (int k = r + 1; k <= c; ++k) s -= T[r][k] * X[k][c];
+      X[r][c] = r > c ? 0.f : s / T[r][r];
+    }
+  }
+  __syncthreads();
+  uint16_t* out = dst + (int64_t)b * NB * NB;
+  for (int e = c; e < NB * NB; e += NB) out[e] = f2bf(X[e / NB][e % NB]);
+}
+
+// dst[r][c] = src[r][c] for an rows x cols bf16 block (both row-major with their own
+// leading dimensions).
+__global__ __launch_bounds__(256) void copy2d_kernel(const uint16_t* __restrict__ src, int64_t lds,
+                                                     uint16_t* __restrict__ dst, int64_t ldd, int rows, int cols) {
+  const int64_t total = (int64_t)rows * cols;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int r = (int)(e / cols), c = (int)(e % cols);
+    dst[(int64_t)r * ldd + c] = src[(int64_t)r * lds + c];
+  }
+}
+
+unsigned blocks_for(int64_t work) {
+  int64_t b = (work + 255) / 256;
+  if (b < 1) b = 1;
+  return (unsigned)b;
+}
+
+}  // namespace
+
+hipError_t launch_expand_tri(const void* src, int64_t lds, void* dst, int64_t ldd, int r0, int c0, int rows, int cols,
+                             int cols_pad, int uplo, int unit, hipStream_t s) {
+  hipLaunchKernelGGL(expand_tri_kernel, dim3(blocks_for((int64_t)rows * (cols_pad / 8))), dim3(256), 0, s,
+                     (const uint16_t*)src, lds, (uint16_t*)dst, ldd, r0, c0, rows, cols, cols_pad, uplo, unit);
+  return hipGetLastError();
+}
+
+hipError_t launch_expand_sym(const void* src, int64_t lds, void* dst, int64_t ldd, int r0, int c0, int rows, int cols,
+                             int cols_pad, int n, int uplo, hipStream_t s) {
+  dim3 grid((unsigned)((cols_pad + SB - 1) / SB), (unsigned)((rows + SB - 1) / SB));
+  hipLaunchKernelGGL(expand_sym_kernel, grid, dim3(256), 0, s, (const uint16_t*)src, lds, (uint16_t*)dst, ldd, r0, c0,
+                     rows, cols, cols_pad, n, uplo);
+  return hipGetLastError();
+}
+
+hipError_t launch_invert_diag(const void* src, int64_t lds, int n, int uplo, int unit, void* dst, hipStream_t s) {
+  const int blocks = (n + kTrsmNB - 1) / kTrsmNB;
+  hipLaunchKernelGGL(invert_diag_kernel, dim3((unsigned)blocks), dim3(kTrsmNB), 0, s, (const uint16_t*)src, lds, n,
+                     uplo, unit, (uint16_t*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy2d(const void* src, int64_t lds, void* dst, int64_t ldd, int rows, int cols, hipStream_t s) {
+  int64_t b = ((int64_t)rows * cols + 255) / 256;
+  if (b > 8192) b = 8192;
+  if (b < 1) b = 1;
+  hipLaunchKernelGGL(copy2d_kernel, dim3((unsigned)b), dim3(256), 0, s, (const uint16_t*)src, lds, (uint16_t*)dst, ldd,
+                     rows, cols);
+  return hipGetLastError();
+}
+
+}  // namespace dbgemm

@@ -43,7 +43,35 @@ struct GemmArgs {
   const uint8_t* sa;
   const uint8_t* sb;
   int64_t ldsa, ldsb;
+  // Triangle of C (the symmetric rank-K updates): TRI_LOWER writes only elements with
+  // row >= column, TRI_UPPER only row <= column, and the grid holds only the tiles that
+  // meet that triangle (square tiles, M == N; see tile_of).  TRI_NONE: all of C.
+  int tri;
+  // K band of each tile (a triangular operand expanded with zeros outside its triangle):
+  // the tile skips the K tiles that meet only zeros.  KBAND_A_LOWER: op(A) is lower, tile
+  // row tm reads k < (tm+1)*BM; KBAND_A_UPPER: k >= tm*BM; KBAND_B_LOWER: op(B) is lower
+  // (zero for k < n), tile column tn reads k >= tn*BN; KBAND_B_UPPER: k < (tn+1)*BN.
+  // band_off is added to the tile's first row (A bands) or column (B bands): the index,
+  // in the triangular operand, of this call's first row or column of C.
+  int kband;
+  int band_off;
+  // Two products in one sum (the rank-2K update): with dual set, the K loop runs over
+  // op(A)*op(B) and then over op(A2)*op(B2), same M, N, K and transposes; A2 has leading
+  // dimension lda2, B2 ldb2 (the direct-to-LDS kernels need lda2 == lda, ldb2 == ldb).
+  int dual;
+  const void* A2;
+  const void* B2;
+  int64_t lda2, ldb2;
 };
+enum { TRI_NONE = 0, TRI_LOWER = 1, TRI_UPPER = 2 };
+enum { KBAND_NONE = 0, KBAND_A_LOWER = 1, KBAND_A_UPPER = 2, KBAND_B_LOWER = 3, KBAND_B_UPPER = 4 };
+
+// Workgroups of a tile grid: every tile, or with a triangle the T(T+1)/2 tiles on and
+// below (or above) the diagonal of the T x T tile grid; times the split-K factor.
+__host__ __device__ inline int grid_tiles(const GemmArgs& a) {
+  const int t = a.tri ? a.tiles_m * (a.tiles_m + 1) / 2 : a.tiles_m * a.tiles_n;
+  return t * a.splits;
+}
 
 enum PolicyKind { KIND_SIMT = 0, KIND_MFMA = 1, KIND_SCALE = 2 };
 
@@ -103,6 +131,10 @@ struct Problem {
   int mx;        // block-scaled E4M3 operands (gemm_run_mx)
   bool mx_words;  // scale rows 4-byte aligned (the scaled native MFMA reads 32-bit words)
   bool fast_ok;  // alignment / divisibility allow the MFMA kernels
+  // BLAS3 calls with a triangle, K band or second product: direct-to-LDS bf16 kernels
+  // only, unsplit, and square tiles for a triangle
+  bool blas3 = false;
+  bool square_tiles = false;
 };
 // Shape-driven selection; returns an index into the table and, in *splits, the
 // split-K factor (1 unless a workspace of ws_floats fp32 values allows more).

@@ -219,8 +219,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_mfma_kernel(GemmArgs a) {
 
 template <class C>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
-  const int ntiles = a.tiles_m * a.tiles_n;
-  hipLaunchKernelGGL(gemm_mfma_kernel<C>, dim3(ntiles), dim3(C::THREADS), 0, s, a);
+  hipLaunchKernelGGL(gemm_mfma_kernel<C>, dim3(grid_tiles(a)), dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

@@ -52,19 +52,33 @@ __global__ __launch_bounds__(256) void gemm_simt_kernel(GemmArgs a) {
   __shared__ float Bs[TK][TS + 1];
   const int tn = blockIdx.x, tm = blockIdx.y;
   const int m0 = tm * TS, n0 = tn * TS;
+  // a triangle of C: tiles that do not meet it have nothing to write
+  if (a.tri == TRI_LOWER && m0 + TS - 1 < n0) return;
+  if (a.tri == TRI_UPPER && m0 > n0 + TS - 1) return;
   const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
   float acc[4][4] = {};
-  for (int k0 = 0; k0 < a.K; k0 += TK) {
+  // K band (zeros of an expanded triangular operand outside it are skipped)
+  int klo = 0, khi = a.K;
+  if (a.kband == KBAND_A_LOWER) khi = min(a.K, a.band_off + m0 + TS);
+  if (a.kband == KBAND_A_UPPER) klo = min(a.K, a.band_off + m0);
+  if (a.kband == KBAND_B_LOWER) klo = min(a.K, a.band_off + n0);
+  if (a.kband == KBAND_B_UPPER) khi = min(a.K, a.band_off + n0 + TS);
+  // one pass over K, or two for a dual call (the second on A2, B2)
+  for (int pass = 0; pass < (a.dual ? 2 : 1); ++pass) {
+  const void* pa = pass ? a.A2 : a.A;
+  const void* pb = pass ? a.B2 : a.B;
+  const int64_t lda = pass ? a.lda2 : a.lda, ldb = pass ? a.ldb2 : a.ldb;
+  for (int k0 = klo; k0 < khi; k0 += TK) {
     for (int e = threadIdx.x; e < TK * TS; e += 256) {
       const int kk = e / TS, x = e % TS;
       const int k = k0 + kk, m = m0 + x, n = n0 + x;
       float av = 0.f, bv = 0.f;
-      if (k < a.K && m < a.M) {
-        av = load_in(a.A, a.transA ? (int64_t)k * a.lda + m : (int64_t)m * a.lda + k, a.in_fp8);
+      if (k < khi && m < a.M) {
+        av = load_in(pa, a.transA ? (int64_t)k * lda + m : (int64_t)m * lda + k, a.in_fp8);
         if (a.mx) av *= ue8m0_to_f32(a.sa[(int64_t)m * a.ldsa + k / 32]);
       }
-      if (k < a.K && n < a.N) {
-        bv = load_in(a.B, a.transB ? (int64_t)n * a.ldb + k : (int64_t)k * a.ldb + n, a.in_fp8);
+      if (k < khi && n < a.N) {
+        bv = load_in(pb, a.transB ? (int64_t)n * ldb + k : (int64_t)k * ldb + n, a.in_fp8);
         if (a.mx) bv *= ue8m0_to_f32(a.sb[(int64_t)n * a.ldsb + k / 32]);
       }
       As[kk][x] = av;
@@ -85,6 +99,7 @@ __global__ __launch_bounds__(256) void gemm_simt_kernel(GemmArgs a) {
     }
     __syncthreads();
   }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + ty * 4 + i;
@@ -93,6 +108,7 @@ __global__ __launch_bounds__(256) void gemm_simt_kernel(GemmArgs a) {
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + tx * 4 + j;
       if (n >= a.N) continue;
+      if ((a.tri == TRI_LOWER && n > m) || (a.tri == TRI_UPPER && n < m)) continue;
       const int64_t idx = (int64_t)m * a.ldc + n;
       float v = a.alpha * acc[i][j];
       if (a.beta != 0.f) v += a.beta * load_c(a.C, idx, a.c_kind);
@@ -106,6 +122,7 @@ __global__ __launch_bounds__(256) void scale_kernel(GemmArgs a) {
   const int64_t total = (int64_t)a.M * a.N;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
     const int m = (int)(e / a.N), n = (int)(e % a.N);
+    if ((a.tri == TRI_LOWER && n > m) || (a.tri == TRI_UPPER && n < m)) continue;
     const int64_t idx = (int64_t)m * a.ldc + n;
     const float v = a.beta != 0.f ? a.beta * load_c(a.C, idx, a.c_kind) : 0.f;
     store_c(a.C, idx, a.c_kind, v);

@@ -39,7 +39,7 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 // cover tiles x splits; the splits of one tile are neighbours in the remapped order
 // (so they run on one XCD) and `split` is the id's position among them.
 __device__ inline void tile_of(int bid, const GemmArgs& a, int& tm, int& tn, int& split) {
-  const int total = a.tiles_m * a.tiles_n * a.splits;
+  const int total = grid_tiles(a);
   int L = bid;
   if (a.xcd > 1) {
     const int q = total / a.xcd;
@@ -47,6 +47,17 @@ __device__ inline void tile_of(int bid, const GemmArgs& a, int& tm, int& tn, int
   }
   split = L % a.splits;
   L /= a.splits;
+  if (a.tri) {
+    // triangle of the tile grid, row by row: tile row r holds tiles (r, 0 .. r), which
+    // start at L = r(r+1)/2.  r from the square root, then corrected to be exact.
+    int r = (int)((__builtin_sqrtf(8.f * (float)L + 1.f) - 1.f) * 0.5f);
+    while (r > 0 && r * (r + 1) / 2 > L) --r;
+    while ((r + 1) * (r + 2) / 2 <= L) ++r;
+    const int c = L - r * (r + 1) / 2;
+    tm = a.tri == TRI_LOWER ? r : c;  // the upper triangle is the transposed walk
+    tn = a.tri == TRI_LOWER ? c : r;
+    return;
+  }
   const int major = a.raster_n ? a.tiles_m : a.tiles_n;  // tiles along the walk
   const int minor = a.raster_n ? a.tiles_n : a.tiles_m;  // grouped dimension
   const int width = a.group * major;
@@ -355,12 +366,18 @@ __device__ __forceinline__ void store_group(const GemmArgs& a, f32x4 v, int p, i
   const int m = row0 + i * C::MT + lane % C::MT;
   const int n = col0 + j * C::MT + (C::MT == 32 ? 8 * q + 4 * (lane / 32) : 4 * (lane / 16));
   if (m >= a.M) return;
+  // elements [e0, e1) of the four columns are written: the last columns stop at N, and a
+  // triangle keeps n + e <= m (lower) or n + e >= m (upper)
+  int e0 = 0, e1 = a.N - n < 4 ? a.N - n : 4;
+  if (a.tri == TRI_LOWER) e1 = m - n + 1 < e1 ? m - n + 1 : e1;
+  if (a.tri == TRI_UPPER) e0 = m - n > 0 ? m - n : 0;
+  if (e1 <= e0) return;
   const float alpha = a.alpha, beta = a.beta;
   float w[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) w[e] = alpha * v[e];
   const int64_t base = (int64_t)m * a.ldc + n;
-  if (n + 3 < a.N) {
+  if (e0 == 0 && e1 == 4) {
     if (a.c_kind == C_F32) {
       float* cp = (float*)a.C + base;
       if (beta != 0.f) {
@@ -392,7 +409,7 @@ __device__ __forceinline__ void store_group(const GemmArgs& a, f32x4 v, int p, i
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (n + e >= a.N) break;
+      if (e < e0 || e >= e1) continue;
       if (a.c_kind == C_F32) {
         float* cp = (float*)a.C + base + e;
         *cp = w[e] + (beta != 0.f ? beta * *cp : 0.f);

@@ -58,6 +58,8 @@ bool policy_serves(const Policy& p, const Problem& pr) {
   if (p.kind == KIND_SIMT) return true;
   if (p.kind != KIND_MFMA || !pr.fast_ok) return false;
   if (pr.mx) return p.in_mode == 3 || (p.in_mode == 4 && pr.mx_words);
+  if (pr.blas3)  // triangle, K band or dual product: the bf16 direct-to-LDS kernels
+    return p.pipe == 1 && p.in_mode == 0 && !pr.in_fp8 && (!pr.square_tiles || p.BM == p.BN);
   return p.in_mode < 3 && (p.in_mode != 0) == (pr.in_fp8 != 0);
 }
 
@@ -98,7 +100,11 @@ int policy_select(const Problem& pr, int cu_count, int64_t ws_floats, int* split
     const Policy& p = kTable[i];
     if (p.kind != KIND_MFMA || p.efficiency <= 0.f || !policy_serves(p, pr)) continue;
     const int occ = occupancy(p);
-    const double tiles = (double)((pr.M + p.BM - 1) / p.BM) * (double)((pr.N + p.BN - 1) / p.BN);
+    double tiles = (double)((pr.M + p.BM - 1) / p.BM) * (double)((pr.N + p.BN - 1) / p.BN);
+    if (pr.square_tiles) {  // a triangle of the T x T tile grid
+      const double t = (double)((pr.M + p.BM - 1) / p.BM);
+      tiles = t * (t + 1) / 2;
+    }
     const double slots = (double)cu_count * occ;
     for (int sp = 1; sp <= 16; sp *= 2) {
       if (!split_allowed(p, pr, sp, ws_floats)) continue;

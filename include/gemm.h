@@ -198,6 +198,89 @@ const char* gemm_version(void);
 /* Human-readable name of a status code. */
 const char* gemm_status_string(int status);
 
+/* ---------------------------------------------------------------------------------
+ * The single-GPU BLAS level-3 family on the GEMM core: the operator set of "BLASMp
+ * development notes" (section 1: a BLAS3 library; section 2: SYRK built on the GEMM,
+ * then TRSM, SYR2K, SYMM and TRMM), on one GPU, without the 2D block-cyclic
+ * distribution.  The operations are the textbook BLAS ones, in the row-major
+ * convention of gemm_run: element (i, j) is row i, column j, and the leading
+ * dimension is the row stride.
+ *
+ *   uplo  GEMM_LOWER: the lower triangle (i >= j) is referenced (written, for SYRK and
+ *         SYR2K); GEMM_UPPER: the upper triangle (i <= j).  The other triangle of a
+ *         triangular or symmetric operand is never read (it may hold anything, NaN
+ *         included); the other triangle of a SYRK / SYR2K result is never written.
+ *   side  GEMM_SIDE_LEFT: the triangular / symmetric matrix multiplies from the left;
+ *         GEMM_SIDE_RIGHT: from the right.
+ *   diag  GEMM_DIAG_UNIT: the triangular matrix has ones on its diagonal, which is not
+ *         read; GEMM_DIAG_NON_UNIT: the diagonal is read.
+ *
+ * Types: bf16 operands, fp32 accumulation; dtype GEMM_BF16_BF16 (bf16 C) or
+ * GEMM_BF16_F32 (fp32 C) where a C is produced, GEMM_BF16_BF16 only for gemm_trsm.
+ * Memory: device pointers owned by the caller; the calls use the handle's workspace
+ * (SYMM and TRMM expand the triangle into it, TRSM keeps the inverted diagonal blocks
+ * there), so, like split-K GEMMs, calls of one handle must not overlap on the device.
+ * Nothing is allocated; the calls return once everything is enqueued on the handle's
+ * stream.  Errors: arguments are checked before anything is launched (INVALID_VALUE
+ * for a bad size, leading dimension, flag, pointer or dtype; NOT_SUPPORTED for
+ * non-finite alpha / beta or an operand larger than the workspace handles, see each
+ * call); on an error nothing is written.  Fast path: the MFMA kernels need the GEMM
+ * fast-path alignment of gemm.h; anything else runs on the generic kernel.
+ * --------------------------------------------------------------------------------- */
+typedef enum { GEMM_LOWER = 0, GEMM_UPPER = 1 } gemm_uplo_t;
+typedef enum { GEMM_SIDE_LEFT = 0, GEMM_SIDE_RIGHT = 1 } gemm_side_t;
+typedef enum { GEMM_DIAG_NON_UNIT = 0, GEMM_DIAG_UNIT = 1 } gemm_diag_t;
+
+/* Symmetric rank-K update of one triangle:
+ *   C <- alpha * op(A) op(A)^T + beta * C   on the uplo triangle of the N x N C,
+ * op(A) N x K: A is [N][lda >= K] (trans = GEMM_OP_N) or [K][lda >= N] (GEMM_OP_T).
+ * The GEMM kernels run over the tiles on one side of the diagonal only, and the
+ * epilogue masks the diagonal tiles.  K == 0 or alpha == 0: C <- beta*C on the
+ * triangle; beta == 0: C is not read. */
+gemm_status_t gemm_syrk(gemm_handle_t h, int uplo, int trans, int64_t N, int64_t K, float alpha,
+                        const void* A, int64_t lda, float beta, void* C, int64_t ldc, int dtype);
+
+/* Symmetric rank-2K update of one triangle:
+ *   C <- alpha * (op(A) op(B)^T + op(B) op(A)^T) + beta * C   on the uplo triangle,
+ * op(A), op(B) N x K stored like syrk's A.  Both products accumulate in one fp32 sum
+ * (one rounding of C); the MFMA kernels need lda == ldb. */
+gemm_status_t gemm_syr2k(gemm_handle_t h, int uplo, int trans, int64_t N, int64_t K, float alpha,
+                         const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+                         int64_t ldc, int dtype);
+
+/* Symmetric matrix product: C <- alpha * S B + beta * C (side LEFT, S M x M) or
+ * alpha * B S + beta * C (side RIGHT, S N x N); B and C are M x N ([M][ldb], [M][ldc]).
+ * S is given by the uplo triangle of A ([n][lda >= n], n = M or N).  S is expanded
+ * into the workspace in row panels, so NOT_SUPPORTED when 256 rows of it exceed the
+ * workspace (n > 131072). */
+gemm_status_t gemm_symm(gemm_handle_t h, int side, int uplo, int64_t M, int64_t N, float alpha,
+                        const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+                        int64_t ldc, int dtype);
+
+/* Triangular matrix product, out of place: C <- alpha * op(T) B (side LEFT, T M x M) or
+ * alpha * B op(T) (side RIGHT, T N x N); T is the uplo triangle of A ([n][lda >= n])
+ * with the diagonal per diag; B and C are M x N and must not overlap.  T is expanded
+ * with zeros into the workspace in panels and each output tile skips the K tiles that
+ * meet only zeros of op(T).  NOT_SUPPORTED when n > 131072. */
+gemm_status_t gemm_trmm(gemm_handle_t h, int side, int uplo, int transA, int diag, int64_t M,
+                        int64_t N, float alpha, const void* A, int64_t lda, const void* B,
+                        int64_t ldb, void* C, int64_t ldc, int dtype);
+
+/* Triangular solve, in place: B <- X with op(T) X = alpha * B (side LEFT, T M x M) or
+ * X op(T) = alpha * B (side RIGHT, T N x N); T as in gemm_trmm, B is bf16 M x N
+ * ([M][ldb]); dtype must be GEMM_BF16_BF16.  The method is the blocked recursive one:
+ * the 128 x 128 diagonal blocks of T are inverted in fp32 (stored as bf16 in the
+ * workspace), each block row (or column) of X is a product with its inverted block,
+ * and the rest of B is updated with GEMMs (alpha*B - T_21 X_1), each rounded to bf16.
+ * T must be non-singular (a zero on a non-unit diagonal gives Inf / NaN).  The result
+ * is checked, as the pages' own TRSM checks were, by residual and forward / backward
+ * error rather than element by element against an exact solution.  NOT_SUPPORTED when
+ * the inverted blocks plus one block row (column) of B exceed the workspace.
+ * alpha == 0: B <- 0. */
+gemm_status_t gemm_trsm(gemm_handle_t h, int side, int uplo, int transA, int diag, int64_t M,
+                        int64_t N, float alpha, const void* A, int64_t lda, void* B, int64_t ldb,
+                        int dtype);
+
 #ifdef __cplusplus
 }
 #endif

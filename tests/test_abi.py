@@ -19,7 +19,7 @@ A, B, C = 0x1000, 0x2000, 0x3000  # host-side stand-ins; never dereferenced by t
 def header_symbols():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"\b(gemm_[a-z_]+)\s*\(", text)
+    return re.findall(r"\b(gemm_[a-z0-9_]+)\s*\(", text)
 
 
 def test_library_exports_every_declared_symbol():
@@ -130,3 +130,15 @@ def test_query_policy_rejects_bad_arguments():
     assert lib.gemm_query_policy(None, 3, 0, 8, 8, 8, None, 8, None, 8, None, 8, 1, buf, 64) == INVALID
     assert lib.gemm_query_policy(None, 0, 0, -8, 8, 8, None, 8, None, 8, None, 8, 1, buf, 64) == INVALID
     assert lib.gemm_query_policy(None, 0, 0, 8, 8, 8, None, 8, None, 8, None, 8, 1, None, 0) == INVALID
+
+
+def test_blas3_calls_reject_a_missing_handle():
+    """Every BLAS3 entry point checks the handle before anything else (no device needed)."""
+    lib = d.load_library()
+    vp = ctypes.c_void_p
+    for h in (None, vp(0x1234)):
+        assert lib.gemm_syrk(h, 0, 0, 8, 8, 1.0, vp(A), 8, 0.0, vp(C), 8, BF16_BF16) == NOT_INIT
+        assert lib.gemm_syr2k(h, 0, 0, 8, 8, 1.0, vp(A), 8, vp(B), 8, 0.0, vp(C), 8, BF16_BF16) == NOT_INIT
+        assert lib.gemm_symm(h, 0, 0, 8, 8, 1.0, vp(A), 8, vp(B), 8, 0.0, vp(C), 8, BF16_BF16) == NOT_INIT
+        assert lib.gemm_trmm(h, 0, 0, 0, 0, 8, 8, 1.0, vp(A), 8, vp(B), 8, vp(C), 8, BF16_BF16) == NOT_INIT
+        assert lib.gemm_trsm(h, 0, 0, 0, 0, 8, 8, 1.0, vp(A), 8, vp(B), 8, BF16_BF16) == NOT_INIT

@@ -1,0 +1,298 @@
+"""GPU parity of the BLAS3 family (gemm_syrk, gemm_syr2k, gemm_symm, gemm_trmm, gemm_trsm)
+against the float64 oracle (oracle/blas3.py), through the C-ABI.
+
+Ragged sizes run on the generic kernel, sizes in whole 16-byte chunks on the MFMA kernels;
+both are compared element by element.  Unreferenced triangles of the operands hold NaN
+(a read of them shows), and the triangle of C that SYRK / SYR2K must not write starts as
+NaN or as known values that must come back bit for bit.
+"""
+import numpy as np
+import pytest
+
+import gemm_inputs as gi
+import oracle
+import tolerance
+from gpu_util import to_device, to_host
+from oracle import blas3
+
+pytestmark = pytest.mark.gpu
+
+LOWER, UPPER, LEFT, RIGHT = 0, 1, 0, 1
+C_FMT = {"bf16": oracle.C_BF16, "f32": oracle.C_F32}
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def c_bits(shape, c_dtype, seed, std=1.0):
+    return gi.draw("normal", shape, seed, gi.BF16 if c_dtype == "bf16" else gi.F32, std)
+
+
+def tri_mask(N, uplo):
+    i, j = np.arange(N)[:, None], np.arange(N)[None, :]
+    return (i >= j) if uplo == LOWER else (i <= j)
+
+
+def check_c(got_bits, c_dtype, R, S, K, mask=None):
+    got = got_bits if mask is None else got_bits[mask]
+    Rm = R if mask is None else R[mask]
+    Sm = S if mask is None else S[mask]
+    res = tolerance.check(got.reshape(1, -1), c_dtype, Rm.reshape(1, -1), Sm.reshape(1, -1), K)
+    assert res["ok"], res
+
+
+# ------------------------------------------------------------------------------ SYRK
+
+SYRK_SHAPES = [(264, 200), (512, 136), (301, 203), (1024, 512)]
+
+
+@pytest.mark.parametrize("N,K", SYRK_SHAPES)
+@pytest.mark.parametrize("uplo", [LOWER, UPPER])
+@pytest.mark.parametrize("trans", [0, 1])
+@pytest.mark.parametrize("c_dtype", ["bf16", "f32"])
+def test_syrk(gpu, N, K, uplo, trans, c_dtype):
+    A = gi.bf16_uniform((K, N) if trans else (N, K), 0)
+    C0 = c_bits((N, N), c_dtype, 2)
+    C = to_device(C0, c_dtype)
+    gpu.syrk(to_device(A, "bf16"), C, uplo=uplo, trans=trans, alpha=-1.5, beta=0.5)
+    sync()
+    got = to_host(C)
+    R, S = blas3.syrk(uplo, trans, N, K, -1.5, A, 0.5, C0, C_FMT[c_dtype])
+    m = tri_mask(N, uplo)
+    check_c(got, c_dtype, R, S, K, m)
+    assert np.array_equal(got[~m], C0[~m]), "the other triangle was written"
+
+
+@pytest.mark.parametrize("N,K", [(256, 64), (520, 72), (77, 33)])
+@pytest.mark.parametrize("uplo", [LOWER, UPPER])
+def test_syrk_beta0_nan_c_and_exact(gpu, N, K, uplo):
+    """Integer inputs: every product and sum is exact in fp32, so the triangle must equal the
+    rounded exact result bit for bit; beta = 0 never reads the NaN-filled C, and the other
+    triangle keeps its NaN."""
+    import torch
+    A = gi.ints((N, K), 5, -4, 4, gi.BF16)
+    C = torch.full((N, N), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    gpu.syrk(to_device(A, "bf16"), C, uplo=uplo, trans=0, alpha=1.0, beta=0.0)
+    sync()
+    got = to_host(C)
+    R, _ = blas3.syrk(uplo, 0, N, K, 1.0, A, 0.0, None, oracle.C_BF16)
+    m = tri_mask(N, uplo)
+    assert np.array_equal(got[m], oracle.round_bf16(R[m]))
+    assert np.isnan(tolerance.bf16_bits_to_f64(got[~m])).all()
+
+
+def test_syrk_k0_scales_triangle_only(gpu):
+    N = 64
+    C0 = c_bits((N, N), "f32", 3)
+    C = to_device(C0, "f32")
+    A = to_device(gi.bf16_uniform((N, 8), 1), "bf16")
+    assert gpu.syrk_raw(LOWER, 0, N, 0, 1.0, A.data_ptr(), 8, 2.0, C.data_ptr(), N, 0) == 0
+    sync()
+    got = tolerance.f32_bits_to_f64(to_host(C))
+    old = tolerance.f32_bits_to_f64(C0)
+    m = tri_mask(N, LOWER)
+    assert np.array_equal(got[m], 2.0 * old[m]) and np.array_equal(got[~m], old[~m])
+
+
+def test_syrk_4096_sampled_rows(gpu):
+    """The measured SYRK workload (N = K = 4096, lower, bf16 C): rows sampled over every tile
+    row against the GEMM oracle restricted to them, the rest of the triangle checked for
+    finiteness and the upper triangle for being untouched."""
+    import torch
+    N = K = 4096
+    A = gi.bf16_uniform((N, K), 0)
+    C = torch.full((N, N), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    gpu.syrk(to_device(A, "bf16"), C, uplo=LOWER, trans=0)
+    sync()
+    got = to_host(C)
+    rows = sorted(set([0, 1, 255, 256, 2047, 2048, 4095] + list(range(37, N, 331))))
+    R, S = oracle.gemm(0, 1, N, N, K, 1.0, A, K, A, K, 0.0, None, N, oracle.IN_BF16, oracle.C_BF16, rows=rows)
+    for t, r in enumerate(rows):
+        res = tolerance.check(got[r, : r + 1].reshape(1, -1), "bf16", R[t, : r + 1].reshape(1, -1),
+                              S[t, : r + 1].reshape(1, -1), K)
+        assert res["ok"], (r, res)
+    v = tolerance.bf16_bits_to_f64(got)
+    m = tri_mask(N, LOWER)
+    assert np.isfinite(v[m]).all() and np.isnan(v[~m]).all()
+
+
+# ------------------------------------------------------------------------------ SYR2K
+
+@pytest.mark.parametrize("N,K", [(264, 200), (301, 203), (512, 264)])
+@pytest.mark.parametrize("uplo", [LOWER, UPPER])
+@pytest.mark.parametrize("trans", [0, 1])
+@pytest.mark.parametrize("c_dtype", ["bf16", "f32"])
+def test_syr2k(gpu, N, K, uplo, trans, c_dtype):
+    shape = (K, N) if trans else (N, K)
+    A, B = gi.bf16_uniform(shape, 0), gi.bf16_uniform(shape, 1)
+    C0 = c_bits((N, N), c_dtype, 2)
+    C = to_device(C0, c_dtype)
+    gpu.syr2k(to_device(A, "bf16"), to_device(B, "bf16"), C, uplo=uplo, trans=trans, alpha=0.75, beta=-1.0)
+    sync()
+    got = to_host(C)
+    R, S = blas3.syr2k(uplo, trans, N, K, 0.75, A, B, -1.0, C0, C_FMT[c_dtype])
+    m = tri_mask(N, uplo)
+    check_c(got, c_dtype, R, S, 2 * K, m)
+    assert np.array_equal(got[~m], C0[~m])
+
+
+def test_syr2k_different_leading_dimensions(gpu):
+    """lda != ldb: the generic kernel (two K passes with their own strides)."""
+    import torch
+    N, K = 136, 72
+    A = gi.bf16_uniform((N, K), 3)
+    Bw = gi.bf16_uniform((N, K + 24), 4)
+    C = torch.zeros((N, N), dtype=torch.float32, device="cuda:0")
+    Bd = to_device(Bw, "bf16")[:, :K]
+    gpu.syr2k(to_device(A, "bf16"), Bd, C, uplo=UPPER, trans=0, alpha=1.0, beta=0.0)
+    sync()
+    R, S = blas3.syr2k(UPPER, 0, N, K, 1.0, A, np.ascontiguousarray(Bw[:, :K]), 0.0, None, oracle.C_F32)
+    m = tri_mask(N, UPPER)
+    check_c(to_host(C), "f32", R, S, 2 * K, m)
+
+
+def test_syr2k_exact_integers(gpu):
+    import torch
+    N, K = 384, 128
+    A, B = gi.ints((N, K), 6, -4, 4, gi.BF16), gi.ints((N, K), 7, -4, 4, gi.BF16)
+    C = torch.full((N, N), float("nan"), dtype=torch.float32, device="cuda:0")
+    gpu.syr2k(to_device(A, "bf16"), to_device(B, "bf16"), C, uplo=LOWER, trans=0, alpha=1.0, beta=0.0)
+    sync()
+    R, _ = blas3.syr2k(LOWER, 0, N, K, 1.0, A, B, 0.0, None, oracle.C_F32)
+    m = tri_mask(N, LOWER)
+    assert np.array_equal(tolerance.f32_bits_to_f64(to_host(C))[m], R[m])
+
+
+# ------------------------------------------------------------------------------ SYMM
+
+@pytest.mark.parametrize("M,N", [(264, 136), (301, 203), (512, 384)])
+@pytest.mark.parametrize("side", [LEFT, RIGHT])
+@pytest.mark.parametrize("uplo", [LOWER, UPPER])
+@pytest.mark.parametrize("c_dtype", ["bf16", "f32"])
+def test_symm(gpu, M, N, side, uplo, c_dtype):
+    n = M if side == LEFT else N
+    A = gi.bf16_symmetric_stored(n, uplo, 0)
+    B = gi.bf16_uniform((M, N), 1)
+    C0 = c_bits((M, N), c_dtype, 2)
+    C = to_device(C0, c_dtype)
+    gpu.symm(to_device(A, "bf16"), to_device(B, "bf16"), C, side=side, uplo=uplo, alpha=1.25, beta=-0.5)
+    sync()
+    R, S = blas3.symm(side, uplo, M, N, 1.25, A, B, -0.5, C0, C_FMT[c_dtype])
+    check_c(to_host(C), c_dtype, R, S, n)
+
+
+# ------------------------------------------------------------------------------ TRMM
+
+@pytest.mark.parametrize("M,N", [(264, 200), (301, 203)])
+@pytest.mark.parametrize("side", [LEFT, RIGHT])
+@pytest.mark.parametrize("uplo", [LOWER, UPPER])
+@pytest.mark.parametrize("transA", [0, 1])
+@pytest.mark.parametrize("unit", [0, 1])
+def test_trmm(gpu, M, N, side, uplo, transA, unit):
+    import torch
+    n = M if side == LEFT else N
+    A = gi.bf16_triangular(n, uplo, 0, unit=bool(unit))
+    B = gi.bf16_uniform((M, N), 1)
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    gpu.trmm(to_device(A, "bf16"), to_device(B, "bf16"), C, side=side, uplo=uplo, transA=transA, diag=unit,
+             alpha=-2.0)
+    sync()
+    R, S = blas3.trmm(side, uplo, transA, unit, M, N, -2.0, A, B)
+    check_c(to_host(C), "bf16", R, S, n)
+
+
+@pytest.mark.parametrize("side", [LEFT, RIGHT])
+@pytest.mark.parametrize("uplo", [LOWER, UPPER])
+@pytest.mark.parametrize("transA", [0, 1])
+def test_trmm_larger_fp32(gpu, side, uplo, transA):
+    import torch
+    M, N = 1024, 768
+    n = M if side == LEFT else N
+    A = gi.bf16_triangular(n, uplo, 2)
+    B = gi.bf16_uniform((M, N), 3)
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda:0")
+    gpu.trmm(to_device(A, "bf16"), to_device(B, "bf16"), C, side=side, uplo=uplo, transA=transA)
+    sync()
+    R, S = blas3.trmm(side, uplo, transA, 0, M, N, 1.0, A, B)
+    check_c(to_host(C), "f32", R, S, n)
+
+
+# ------------------------------------------------------------------------------ TRSM
+
+def _int_system(n, M, N, side, uplo, transA, unit, seed):
+    A = gi.int_triangular(n, uplo, seed, unit=bool(unit))
+    Xt = gi.ints((M, N), seed + 1, -2, 2, gi.BF16)
+    # B = op(T) X (or X op(T)) from the oracle's product: exact integers here
+    Bv, _ = blas3.trmm(side, uplo, transA, unit, M, N, 1.0, A, Xt)
+    assert np.abs(Bv).max() < 256
+    return A, Xt, gi.f32_to_bf16_bits(Bv.astype(np.float32))
+
+
+@pytest.mark.parametrize("M,N", [(512, 264), (300, 136), (136, 300)])
+@pytest.mark.parametrize("side", [LEFT, RIGHT])
+@pytest.mark.parametrize("uplo", [LOWER, UPPER])
+@pytest.mark.parametrize("transA", [0, 1])
+@pytest.mark.parametrize("unit", [1, 0])
+def test_trsm_exact_integer_system(gpu, M, N, side, uplo, transA, unit):
+    """op(T) X = B with T integer, its strictly triangular part squaring to zero, and X
+    integer: every block inverse, leaf product and update is exact in bf16 and fp32, so the
+    solution must come back bit for bit (this pins indexing, sides, transposes, the
+    recursion's splits and the partial last block)."""
+    n = M if side == LEFT else N
+    A, Xt, Bb = _int_system(n, M, N, side, uplo, transA, unit, 10)
+    Bd = to_device(Bb, "bf16")
+    gpu.trsm(to_device(A, "bf16"), Bd, side=side, uplo=uplo, transA=transA, diag=unit, alpha=1.0)
+    sync()
+    assert np.array_equal(to_host(Bd), Xt)
+
+
+@pytest.mark.parametrize("M,N", [(512, 264), (301, 203), (264, 520)])
+@pytest.mark.parametrize("side", [LEFT, RIGHT])
+@pytest.mark.parametrize("uplo", [LOWER, UPPER])
+@pytest.mark.parametrize("transA", [0, 1])
+@pytest.mark.parametrize("unit", [0, 1])
+def test_trsm_real(gpu, M, N, side, uplo, transA, unit):
+    n = M if side == LEFT else N
+    A = gi.bf16_triangular(n, uplo, 20, unit=bool(unit))
+    B = gi.bf16_uniform((M, N), 21)
+    Bd = to_device(B, "bf16")
+    alpha = 0.5
+    gpu.trsm(to_device(A, "bf16"), Bd, side=side, uplo=uplo, transA=transA, diag=unit, alpha=alpha)
+    sync()
+    X = tolerance.bf16_bits_to_f64(to_host(Bd))
+    X_ref = blas3.trsm(side, uplo, transA, unit, M, N, alpha, A, B)
+    T = blas3.triangular(A, n, uplo, unit)
+    opT = T.T if transA else T
+    res = tolerance.trsm_check(X, X_ref, opT, alpha * tolerance.bf16_bits_to_f64(B), side, n)
+    assert res["ok"], res
+
+
+def test_trsm_alpha0_zeroes_b(gpu):
+    import torch
+    B = torch.full((64, 48), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    A = to_device(gi.bf16_triangular(64, LOWER, 1), "bf16")
+    gpu.trsm(A, B, alpha=0.0)
+    sync()
+    assert (B.float() == 0).all().item()
+
+
+def test_trsm_4096_sampled_columns(gpu):
+    """The measured TRSM workload (M = N = 4096, left, lower, no transpose, non-unit): the
+    columns of X are independent systems, so sampled columns are checked against the oracle
+    solved for those columns only."""
+    M = N = 4096
+    A = gi.bf16_triangular(M, LOWER, 30)
+    B = gi.bf16_uniform((M, N), 31)
+    Bd = to_device(B, "bf16")
+    gpu.trsm(to_device(A, "bf16"), Bd, side=LEFT, uplo=LOWER)
+    sync()
+    X = tolerance.bf16_bits_to_f64(to_host(Bd))
+    cols = [0, 1, 127, 128, 2047, 4095] + list(range(300, N, 517))
+    Bs = np.ascontiguousarray(B[:, cols])
+    X_ref = blas3.trsm(LEFT, LOWER, 0, 0, M, len(cols), 1.0, A, Bs)
+    T = blas3.triangular(A, M, LOWER, 0)
+    res = tolerance.trsm_check(X[:, cols], X_ref, T, tolerance.bf16_bits_to_f64(Bs), LEFT, M)
+    assert res["ok"], res
+    assert np.isfinite(X).all()

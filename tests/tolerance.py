@@ -97,3 +97,31 @@ def check_e4m3(codes: np.ndarray, R: np.ndarray, S: np.ndarray, K: int, alpha: f
     return {"ok": finite and bool(inside.all()), "finite": finite, "n_outside": int((~inside).sum()),
             "n_differ_from_rounded_R": int((codes != exact).sum()), "n": int(codes.size),
             "n_saturated": int((np.abs(got) == 448.0).sum())}
+
+
+def trsm_check(X: np.ndarray, X_ref: np.ndarray, opT: np.ndarray, rhs: np.ndarray, side: int, n: int,
+               leaf: int = 128) -> Dict:
+    """Acceptance of a bf16 triangular solve op(T) X = rhs (side 0) or X op(T) = rhs (side 1),
+    rhs = alpha * B, checked the way a solver is checked (residual and forward error, not
+    element by element against the exact X).
+
+    Error model of the blocked method: the inverted diagonal blocks, each leaf product and
+    each GEMM update of B are rounded to bf16 once (relative error <= 2^-9 each); a row of
+    X passes through at most L = ceil(log2(n / leaf)) updates, one inverted block and one
+    leaf rounding.  With u = 2^-9 and g = L + 3 roundings, the normwise backward error
+        eta = ||op(T) X - rhs||_F / (||op(T)||_F ||X||_F + ||rhs||_F)
+    is bounded by g * u times a modest growth factor (4 is used), and the forward error
+        ||X - X_ref||_F / ||X_ref||_F <= kappa_2(op(T)) * 4 g u,
+    X_ref being the exact (float64) solution.  Every element must also be finite.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    L = max(0, math.ceil(math.log2(max(n, 1) / leaf))) if n > leaf else 0
+    g = L + 3
+    u = 2.0 ** -9
+    prod = opT @ X if side == 0 else X @ opT
+    eta = float(np.linalg.norm(prod - rhs) / (np.linalg.norm(opT) * np.linalg.norm(X) + np.linalg.norm(rhs)))
+    kappa = float(np.linalg.cond(opT))
+    fwd = float(np.linalg.norm(X - X_ref) / max(np.linalg.norm(X_ref), 1e-300))
+    ok = bool(np.isfinite(X).all()) and eta <= 4 * g * u and fwd <= kappa * 4 * g * u
+    return {"ok": ok, "eta": eta, "eta_bound": 4 * g * u, "forward": fwd, "forward_bound": kappa * 4 * g * u,
+            "kappa": kappa}
