@@ -16,7 +16,8 @@ each, p50/p95) and prints a Markdown table to stderr; the JSON line is unchanged
 --ladder runs the ablation ladder (one variable per rung: global->LDS path and LDS stages,
 LDS->register reads, B layout, swizzle) on three K values and a K x M/N heat map, and
 --lds-probe the load-only LDS read microbenchmark, --mx the MXFP8 quantiser and GEMM at
-the E4M3 forward shape; these print to stderr and exit without the JSON line.
+the E4M3 forward shape, --blas3 the BLAS3 family (SYRK, SYR2K, SYMM, TRMM, TRSM) at 4096;
+these print to stderr and exit without the JSON line.
 --policy / --workload pin the policy or pick another workload for the timed steps
 (used for profiling single kernels); the JSON line then names them in `config`.
 --copy-calibration N runs only a plain device-to-device copy of N MiB (the known-size
@@ -381,6 +382,70 @@ def mx_bench(g, warmup: int = 5, steps: int = 30):
     return out
 
 
+# The BLAS3 family at 4096 (bf16 operands, fp32 accumulation, bf16 results): the
+# operator set of "BLASMp development notes" on one GPU.  FLOP counts are the standard
+# ones of each operation's useful work (the triangle only for SYRK / SYR2K, the
+# triangular half for TRMM / TRSM): SYRK N(N+1)K, SYR2K 2N(N+1)K, SYMM 2M^2N (left),
+# TRMM M^2N, TRSM M^2N (left).
+BLAS3_N = 4096
+
+
+def blas3_bench(g, warmup: int = 5, steps: int = 30, n: int = BLAS3_N):
+    """Event-timed p50 of each BLAS3 call at n x n (left side, lower, no transpose,
+    non-unit diagonal); returns a list of dicts and prints a Markdown table to stderr."""
+    import torch
+    stream = torch.cuda.current_stream()
+    A = _dev(gi.bf16_uniform((n, n), 0), "bf16")
+    B = _dev(gi.bf16_uniform((n, n), 1), "bf16")
+    Tm = _dev(gi.bf16_triangular(n, gi.LOWER, 2), "bf16")
+    Sm = _dev(gi.bf16_symmetric_stored(n, gi.LOWER, 3), "bf16")
+    C = torch.zeros((n, n), dtype=torch.bfloat16, device="cuda:0")
+    X = torch.empty_like(B)
+
+    def timed(fn, pre=None):
+        for _ in range(warmup):
+            if pre:
+                pre()
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            if pre:
+                pre()
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ev])
+    nn = float(n)
+    ops = [
+        ("gemm (context)", 2 * nn ** 3, lambda: g(A, B, C), None),
+        ("syrk lower, N", nn * (nn + 1) * nn, lambda: g.syrk(A, C, uplo=0, trans=0), None),
+        ("syr2k lower, N", 2 * nn * (nn + 1) * nn, lambda: g.syr2k(A, B, C, uplo=0, trans=0), None),
+        ("symm left lower", 2 * nn ** 3, lambda: g.symm(Sm, B, C, side=0, uplo=0), None),
+        ("trmm left lower N", nn ** 3, lambda: g.trmm(Tm, B, C, side=0, uplo=0, transA=0), None),
+        # the solve overwrites its right-hand side: a fresh copy goes in before each call,
+        # outside the event pair
+        ("trsm left lower N", nn ** 3, lambda: g.trsm(Tm, X, side=0, uplo=0, transA=0), lambda: X.copy_(B)),
+    ]
+    rows = []
+    for name, flops, fn, pre in ops:
+        ms = timed(fn, pre)
+        p50, p95 = float(np.percentile(ms, 50)), float(np.percentile(ms, 95))
+        tf = flops / (p50 * 1e-3) / 1e12
+        rows.append({"op": name, "n": n, "us_p50": round(p50 * 1e3, 1), "us_p95": round(p95 * 1e3, 1),
+                     "tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_TFLOPS["bf16"], 4)})
+    print(f"BLAS3 family at {n} (bf16 in, fp32 accumulate, bf16 out; p50 of {steps} event-timed calls)",
+          file=sys.stderr)
+    print("| op | us p50 | us p95 | TFLOP/s | frac of bf16 peak |", file=sys.stderr)
+    print("|---|---|---|---|---|", file=sys.stderr)
+    for r in rows:
+        print(f"| {r['op']} | {r['us_p50']} | {r['us_p95']} | {r['tflops']} | {r['frac_bf16_peak']} |",
+              file=sys.stderr)
+    print("blas3: " + json.dumps(rows), file=sys.stderr)
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -396,6 +461,7 @@ def main():
                     help="with --ladder: 4096^3 only, one round (3 + 20 calls per rung, in order)")
     ap.add_argument("--lds-probe", action="store_true", help="run the LDS read microbenchmark and exit")
     ap.add_argument("--mx", action="store_true", help="time the MXFP8 quantiser and GEMM and exit")
+    ap.add_argument("--blas3", action="store_true", help="time the BLAS3 family at 4096 and exit")
     ap.add_argument("--policy", default=None, help="force a named policy for the timed steps")
     ap.add_argument("--workload", default=gi.SQUARE_4096.name, choices=sorted(gi.BY_NAME))
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
@@ -421,7 +487,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": args.warmup + args.steps}))
         return
     g = d.Gemm(0)
-    if args.ladder or args.lds_probe or args.mx:
+    if args.ladder or args.lds_probe or args.mx or args.blas3:
+        if args.blas3:
+            blas3_bench(g)
         if args.mx:
             mx_bench(g)
         if args.lds_probe:

@@ -13,6 +13,8 @@
 //
 // Every kernel reads the stored triangle only: the other triangle (and a unit diagonal)
 // may hold anything, NaN included.
+#include <type_traits>
+
 #include "blas3_internal.h"
 
 namespace dbgemm {
@@ -22,6 +24,15 @@ __device__ inline float bf16f(uint16_t b) { return __builtin_bit_cast(float, (ui
 __device__ inline uint16_t f2bf(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
 
 __device__ inline bool referenced(int i, int j, int uplo) { return uplo == 0 ? i >= j : i <= j; }
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), expanded at compile time
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void cfor(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    cfor<N, I + 1>(f);
+  }
+}
 
 // dst[r][c] (r < rows, c < cols, leading dimension ldd) = T[r0 + r][c0 + c] of the n x n
 // triangular matrix T.  One thread per 8 consecutive columns of one row; columns past
@@ -90,42 +101,55 @@ __global__ __launch_bounds__(256) void expand_sym_kernel(const uint16_t* __restr
 }
 
 // Inverse of each diagonal block T_bb (rows and columns [b*NB, b*NB + nb), nb = NB except
-// for a shorter last block) of the n x n triangular T.  Workgroup b, thread c computes
-// column c of inv(T_bb) by substitution in fp32: lower blocks forward from row c, upper
-// blocks backward from row c.  The block is padded to NB x NB with the identity.  The
-// result, zeros outside the triangle, is stored as bf16 at dst + b*NB*NB, [NB][NB].
+// for a shorter last block) of the n x n triangular T, padded to NB x NB with the
+// identity.  Workgroup b, thread c computes column c of inv(T_bb) by column-oriented
+// substitution in fp32 with the whole column in registers: for each k in order
+// (ascending for a lower block, descending for an upper one), x_k = b_k / T_kk, then
+// b_r -= T_rk * x_k for the rows r still to come.  The updates of one step are
+// independent, so the loop is bound by FMA issue, not by latency; T is kept transposed in
+// LDS so that column k is one broadcast row.  The result, zeros outside the triangle, is
+// stored as bf16 at dst + b*NB*NB, [NB][NB].
+template <bool UPPER>
 __global__ __launch_bounds__(kTrsmNB) void invert_diag_kernel(const uint16_t* __restrict__ src, int64_t lds, int n,
-                                                              int uplo, int unit, uint16_t* __restrict__ dst) {
+                                                              int unit, uint16_t* __restrict__ dst) {
   constexpr int NB = kTrsmNB;
-  __shared__ float T[NB][NB + 1];
-  __shared__ float X[NB][NB + 1];
+  constexpr int LD = NB + 4;  // row stride of Tt: float4-aligned, 4-way bank spread on the transposing writes
+  __shared__ __attribute__((aligned(16))) float Tt[NB * LD];  // Tt[k * LD + r] = T[r][k]
   const int b = blockIdx.x, o = b * NB;
   const int nb = n - o < NB ? n - o : NB;
   const int c = threadIdx.x;
-  for (int e = c; e < NB * NB; e += NB) {
+  for (int e = c; e < NB * NB; e += NB) {  // thread c reads column c of row e / NB
     const int i = e / NB, j = e % NB;
     float v = 0.f;
     if (i == j && (unit || i >= nb)) v = 1.f;
-    else if (i < nb && j < nb && referenced(i, j, uplo)) v = bf16f(src[(int64_t)(o + i) * lds + o + j]);
-    T[i][j] = v;
+    else if (i < nb && j < nb && (UPPER ? i <= j : i >= j)) v = bf16f(src[(int64_t)(o + i) * lds + o + j]);
+    Tt[j * LD + i] = v;
   }
   __syncthreads();
-  if (uplo == 0) {
-    for (int r = 0; r < NB; ++r) {
-      float s = r == c ? 1.f : 0.f;
-      for (int k = c; k < r; ++k) s -= T[r][k] * X[k][c];
-      X[r][c] = r < c ? 0.f : s / T[r][r];
-    }
-  } else {
-    for (int r = NB - 1; r >= 0; --r) {
-      float s = r == c ? 1.f : 0.f;
-      for (int k = r + 1; k <= c; ++k) s -= T[r][k] * X[k][c];
-      X[r][c] = r > c ? 0.f : s / T[r][r];
-    }
-  }
-  __syncthreads();
+  float x[NB];
+#pragma unroll
+  for (int r = 0; r < NB; ++r) x[r] = r == c ? 1.f : 0.f;
+  // every index below is a compile-time constant, so x stays in registers
+  cfor<NB>([&](auto sc) {
+    constexpr int k = UPPER ? NB - 1 - decltype(sc)::value : decltype(sc)::value;
+    const float* col = Tt + k * LD;
+    const float xk = x[k] / col[k];
+    x[k] = xk;
+    // rows still to come: (k, NB) for a lower block, [0, k) for an upper one, in groups of
+    // 32 so that at most one group of T's column is live in registers beside x
+    constexpr int lo = UPPER ? 0 : k + 1, hi = UPPER ? k : NB, G = 32;
+    cfor<(hi - lo + G - 1) / G>([&](auto gc) {
+      constexpr int r0 = lo + G * decltype(gc)::value;
+      cfor<(hi - r0 < G ? hi - r0 : G)>([&](auto jc) {
+        constexpr int r = r0 + decltype(jc)::value;
+        x[r] -= col[r] * xk;
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  });
   uint16_t* out = dst + (int64_t)b * NB * NB;
-  for (int e = c; e < NB * NB; e += NB) out[e] = f2bf(X[e / NB][e % NB]);
+#pragma unroll
+  for (int r = 0; r < NB; ++r) out[r * NB + c] = f2bf(x[r]);
 }
 
 // dst[r][c] = src[r][c] for an rows x cols bf16 block (both row-major with their own
@@ -164,8 +188,12 @@ hipError_t launch_expand_sym(const void* src, int64_t lds, void* dst, int64_t ld
 
 hipError_t launch_invert_diag(const void* src, int64_t lds, int n, int uplo, int unit, void* dst, hipStream_t s) {
   const int blocks = (n + kTrsmNB - 1) / kTrsmNB;
-  hipLaunchKernelGGL(invert_diag_kernel, dim3((unsigned)blocks), dim3(kTrsmNB), 0, s, (const uint16_t*)src, lds, n,
-                     uplo, unit, (uint16_t*)dst);
+  if (uplo == 0)
+    hipLaunchKernelGGL(invert_diag_kernel<false>, dim3((unsigned)blocks), dim3(kTrsmNB), 0, s, (const uint16_t*)src,
+                       lds, n, unit, (uint16_t*)dst);
+  else
+    hipLaunchKernelGGL(invert_diag_kernel<true>, dim3((unsigned)blocks), dim3(kTrsmNB), 0, s, (const uint16_t*)src,
+                       lds, n, unit, (uint16_t*)dst);
   return hipGetLastError();
 }
 
