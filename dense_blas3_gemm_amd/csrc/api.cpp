@@ -325,6 +325,7 @@ static hipError_t enqueue_impl(int cu_count, hipStream_t stream, void* ws, int64
   if (extras) {
     pr.blas3 = true;
     pr.square_tiles = x.tri != TRI_NONE;
+    pr.kband = x.kband != KBAND_NONE;
     if (x.dual) {  // the second product must fit the same buffer descriptors' strides
       const Problem p2 = make_problem(transA, transB, M, N, K, x.A2, x.lda2, x.B2, x.ldb2, C, ldc, dtype);
       pr.fast_ok = pr.fast_ok && p2.fast_ok && x.lda2 == lda && x.ldb2 == ldb;
@@ -355,6 +356,12 @@ static hipError_t enqueue_impl(int cu_count, hipStream_t stream, void* ws, int64
   a.group = pol.group;
   a.raster_n = pol.raster_n;
   a.xcd = pol.xcd;
+  if (x.kband != KBAND_NONE) {
+    // longest tiles first in dispatch order (tile_of): no per-XCD split of the order, and
+    // groups of tile rows (A bands) or columns (B bands) walked from the long end
+    a.xcd = 1;
+    a.raster_n = (x.kband == KBAND_B_LOWER || x.kband == KBAND_B_UPPER) ? 1 : 0;
+  }
   a.swizzle = pol.swizzle;
   a.krot = extras ? 0 : pol.krot;
   a.splits = sp;

@@ -92,6 +92,7 @@ struct Policy {
   int read_mode;   // 1: transposing LDS reads for M/N-contiguous operands; 0: one element per read
   int threads;
   float efficiency;  // relative per-CU throughput used by the wave-time model
+  int k_contig_only;  // serves only A [M][K] with B [N][K] (transA = 0, transB = 1)
 };
 
 // Launchers (one per kernel family).  They return hipSuccess or the launch error.
@@ -135,6 +136,7 @@ struct Problem {
   // only, unsplit, and square tiles for a triangle
   bool blas3 = false;
   bool square_tiles = false;
+  bool kband = false;  // per-tile K band (wave model: longest tiles first)
 };
 // Shape-driven selection; returns an index into the table and, in *splits, the
 // split-K factor (1 unless a workspace of ws_floats fp32 values allows more).

@@ -412,7 +412,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 hipError_t DBGEMM_DMA_CAT(DBGEMM_DMA_TA, DBGEMM_DMA_TB)(const Policy& p, const GemmArgs& a, hipStream_t s) {
 #define DBGEMM_SIMT(name, eff)
 #define DBGEMM_MFMA(name_, pipe_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_, eff_)       \
-  if constexpr (pipe_ == 1 && (in_ != 4 || (DBGEMM_DMA_TA == 0 && DBGEMM_DMA_TB == 1)))                  \
+  if constexpr (pipe_ == 1 && ((in_ != 4 && !(((sw_) >> 3) & 1)) || (DBGEMM_DMA_TA == 0 && DBGEMM_DMA_TB == 1))) \
     if (p.BM == bm_ && p.BN == bn_ && p.BK == bk_ && p.WM == wm_ && p.WN == wn_ && p.MT == mt_ &&         \
         p.stages == st_ && p.in_mode == in_ && p.read_mode == ((((sw_) >> 2) & 1) ? 0 : 1))               \
       return launch_cfg<Cfg<bm_, bn_, bk_, wm_, wn_, mt_, st_, in_, DBGEMM_DMA_TA != 0, DBGEMM_DMA_TB != 0,  \

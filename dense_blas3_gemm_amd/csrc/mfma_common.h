@@ -69,6 +69,10 @@ __device__ inline void tile_of(int bid, const GemmArgs& a, int& tm, int& tn, int
   const int i_major = r / gs;
   tm = a.raster_n ? i_major : i_minor;
   tn = a.raster_n ? i_minor : i_major;
+  // K bands: walk the tiles with the longest K range first (the host groups the raster
+  // along the banded dimension), so that later, shorter tiles fill the last round
+  if (a.kband == KBAND_A_LOWER) tm = a.tiles_m - 1 - tm;
+  if (a.kband == KBAND_B_UPPER) tn = a.tiles_n - 1 - tn;
 }
 
 // Input modes: IN_BF16 (bf16 operands, bf16 MFMA); IN_E4M3 (E4M3 operands widened

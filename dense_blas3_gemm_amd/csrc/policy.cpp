@@ -14,10 +14,10 @@ namespace dbgemm {
 namespace {
 
 const Policy kTable[] = {
-#define DBGEMM_SIMT(name_, eff_) {name_, KIND_SIMT, 0, -1, 64, 64, 16, 1, 1, 0, 1, 1, 0, 1, 0, 0, 1, 256, eff_},
+#define DBGEMM_SIMT(name_, eff_) {name_, KIND_SIMT, 0, -1, 64, 64, 16, 1, 1, 0, 1, 1, 0, 1, 0, 0, 1, 256, eff_, 0},
 #define DBGEMM_MFMA(name_, pipe_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_, eff_) \
   {name_, KIND_MFMA, pipe_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, (sw_) & 1,        \
-   ((sw_) >> 1) & 1, ((sw_) >> 2) & 1 ? 0 : 1, (wm_) * (wn_) * 64, eff_},
+   ((sw_) >> 1) & 1, ((sw_) >> 2) & 1 ? 0 : 1, (wm_) * (wn_) * 64, eff_, ((sw_) >> 3) & 1},
 #include "policies.inc"
 #undef DBGEMM_SIMT
 #undef DBGEMM_MFMA
@@ -57,6 +57,7 @@ int policy_find(const char* name) {
 bool policy_serves(const Policy& p, const Problem& pr) {
   if (p.kind == KIND_SIMT) return true;
   if (p.kind != KIND_MFMA || !pr.fast_ok) return false;
+  if (p.k_contig_only && (pr.transA != 0 || pr.transB != 1)) return false;
   if (pr.mx) return p.in_mode == 3 || (p.in_mode == 4 && pr.mx_words);
   if (pr.blas3)  // triangle, K band or dual product: the bf16 direct-to-LDS kernels
     return p.pipe == 1 && p.in_mode == 0 && !pr.in_fp8 && (!pr.square_tiles || p.BM == p.BN);
@@ -115,6 +116,9 @@ int policy_select(const Problem& pr, int cu_count, int64_t ws_floats, int* split
       const double per_cu = (double)(int64_t)((wgs + cu_count - 1) / cu_count);
       const double conc = per_cu < occ ? per_cu : occ;
       double t = rounds * conc * (double)p.BM * p.BN * (k_eff + K0) / p.efficiency;
+      // a K band, tiles walked from the longest K to the shortest: round r of R holds
+      // tiles of about K (1 - r/R), so the rounds add up to (R + 1) / 2 full-K rounds
+      if (pr.kband) t *= (rounds + 1.0) / (2.0 * rounds);
       if (sp > 1) t += (1.5 + 0.75 * sp) * kUnitsPerUs;
       if (!have || t < best_t * 0.999) {
         best = i;

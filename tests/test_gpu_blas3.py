@@ -296,3 +296,27 @@ def test_trsm_4096_sampled_columns(gpu):
     res = tolerance.trsm_check(X[:, cols], X_ref, T, tolerance.bf16_bits_to_f64(Bs), LEFT, M)
     assert res["ok"], res
     assert np.isfinite(X).all()
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 256), (600, 328, 200), (192, 192, 64)])
+def test_gemm_192_tile_nt(gpu, M, N, K):
+    """The 192 x 192 tile (chosen for the symmetric updates) as a plain GEMM by name: A [M][K],
+    B [N][K], ragged edges, every element against the oracle; other layouts are refused."""
+    import dataclasses
+    from gpu_util import compare, run_gpu
+    p = gi.Gemm("nt192", M, N, K, transA=0, transB=1, c_dtype="f32", alpha=0.5, beta=0.0)
+    data = p.make()
+    C = run_gpu(gpu, p, data, policy="bf16_dma_m192n192k64_w2x4_mt16_s2_nt")
+    res = compare(p, data, C)
+    assert res["ok"], res
+    q = dataclasses.replace(p, transB=0)
+    dq = q.make()
+    A, B = to_device(dq["A"], "bf16"), to_device(dq["B"], "bf16")
+    import torch
+    Cq = torch.zeros((M, N), dtype=torch.float32, device="cuda:0")
+    gpu.set_policy("bf16_dma_m192n192k64_w2x4_mt16_s2_nt")
+    try:
+        st = gpu.run_raw(0, 0, M, N, K, 1.0, A.data_ptr(), K, B.data_ptr(), N, 0.0, Cq.data_ptr(), N, 0)
+    finally:
+        gpu.set_policy(None)
+    assert st == 2  # NOT_SUPPORTED
