@@ -8,9 +8,10 @@
 //   SYMM   the symmetric matrix expanded into the workspace (row panels), then GEMMs;
 //   TRMM   the triangle expanded with zeros into the workspace (panels), then GEMMs whose
 //          tiles skip the K tiles that meet only zeros;
-//   TRSM   the diagonal blocks inverted in one launch, then a recursive split: solve one
-//          half, update the other half with a GEMM (alpha*B - T21*X1), solve it; a leaf
-//          block is the product of its inverted diagonal block with its rows of B.
+//   TRSM   the 256 x 256 diagonal blocks inverted in two launches (fp32 128-block
+//          inverses, then their 2 x 2 combination), then a recursive split: solve one half,
+//          update the other half with a GEMM (alpha*B - T21*X1), solve it; a leaf block is the
+//          product of its inverted diagonal block with its rows (columns) of B.
 #include <climits>
 #include <cmath>
 
@@ -63,12 +64,13 @@ int64_t panel_rows(const HandleView& hv, int64_t n) {
   return p;
 }
 
-// The policy a TRSM leaf runs with when it updates its block of B in place: one
-// 128-row (128-column) tile spans the whole leaf, so each workgroup reads the part of B
-// it overwrites, all of it before its epilogue, and no other workgroup reads it.
-int leaf_policy() {
-  static const int idx = policy_find("bf16_dma_m128n128k64_w2x4_mt16_s4");
-  return idx;
+// The policies a TRSM leaf runs with when it updates its block of B in place: one 256-row
+// (left) or 256-column (right) tile spans the whole leaf, so each workgroup reads the part
+// of B it overwrites, all of it before its epilogue, and no other workgroup reads it.
+int leaf_policy(int side) {
+  static const int left = policy_find("bf16_dma_m256n128k64_w4x2_mt16_s3");
+  static const int right = policy_find("bf16_dma_m128n256k64_w2x4_mt16_s3");
+  return side == GEMM_SIDE_LEFT ? left : right;
 }
 
 struct Trsm {
@@ -80,7 +82,7 @@ struct Trsm {
   int64_t lda;
   void* B;
   int64_t ldb;
-  uint16_t* inv;      // inverted diagonal blocks, [blocks][NB][NB]
+  uint16_t* inv;      // inverted 256 x 256 diagonal blocks, [blocks][256][256]
   uint16_t* scratch;  // one block row (column) of B, for leaves that cannot run in place
   hipError_t err = hipSuccess;
 
@@ -93,36 +95,36 @@ struct Trsm {
   }
 
   void leaf(int64_t o, int64_t nb, float alpha) {
-    const uint16_t* ib = inv + (o / kTrsmNB) * kTrsmNB * kTrsmNB;
+    constexpr int L = kTrsmLeaf;
+    const uint16_t* ib = inv + (o / L) * L * L;
     GemmExtras x;
+    const int pol = leaf_policy(side);
     if (side == GEMM_SIDE_LEFT) {  // X rows [o, o+nb) = alpha * op(inv) * B rows
       void* Bb = off(B, o, 0, ldb, 2);
-      if (gemm_fast_ok(transA, 0, nb, N, nb, ib, kTrsmNB, Bb, ldb, Bb, ldb, GEMM_BF16_BF16) && leaf_policy() >= 0) {
-        x.policy = leaf_policy();
-        keep(gemm_enqueue(hv, transA, 0, nb, N, nb, alpha, ib, kTrsmNB, Bb, ldb, 0.f, Bb, ldb, GEMM_BF16_BF16, x));
+      if (gemm_fast_ok(transA, 0, nb, N, nb, ib, L, Bb, ldb, Bb, ldb, GEMM_BF16_BF16) && pol >= 0) {
+        x.policy = pol;
+        keep(gemm_enqueue(hv, transA, 0, nb, N, nb, alpha, ib, L, Bb, ldb, 0.f, Bb, ldb, GEMM_BF16_BF16, x));
       } else {
         const int64_t lds = pad8(N);
-        keep(gemm_enqueue(hv, transA, 0, nb, N, nb, alpha, ib, kTrsmNB, Bb, ldb, 0.f, scratch, lds, GEMM_BF16_BF16,
-                          x));
+        keep(gemm_enqueue(hv, transA, 0, nb, N, nb, alpha, ib, L, Bb, ldb, 0.f, scratch, lds, GEMM_BF16_BF16, x));
         keep(launch_copy2d(scratch, lds, Bb, ldb, (int)nb, (int)N, hv.stream));
       }
     } else {  // X columns [o, o+nb) = alpha * B columns * op(inv)
       void* Bb = off(B, 0, o, ldb, 2);
-      if (gemm_fast_ok(0, transA, M, nb, nb, Bb, ldb, ib, kTrsmNB, Bb, ldb, GEMM_BF16_BF16) && leaf_policy() >= 0) {
-        x.policy = leaf_policy();
-        keep(gemm_enqueue(hv, 0, transA, M, nb, nb, alpha, Bb, ldb, ib, kTrsmNB, 0.f, Bb, ldb, GEMM_BF16_BF16, x));
+      if (gemm_fast_ok(0, transA, M, nb, nb, Bb, ldb, ib, L, Bb, ldb, GEMM_BF16_BF16) && pol >= 0) {
+        x.policy = pol;
+        keep(gemm_enqueue(hv, 0, transA, M, nb, nb, alpha, Bb, ldb, ib, L, 0.f, Bb, ldb, GEMM_BF16_BF16, x));
       } else {
-        keep(gemm_enqueue(hv, 0, transA, M, nb, nb, alpha, Bb, ldb, ib, kTrsmNB, 0.f, scratch, kTrsmNB,
-                          GEMM_BF16_BF16, x));
-        keep(launch_copy2d(scratch, kTrsmNB, Bb, ldb, (int)M, (int)nb, hv.stream));
+        keep(gemm_enqueue(hv, 0, transA, M, nb, nb, alpha, Bb, ldb, ib, L, 0.f, scratch, L, GEMM_BF16_BF16, x));
+        keep(launch_copy2d(scratch, L, Bb, ldb, (int)M, (int)nb, hv.stream));
       }
     }
   }
 
   // Rows [r0, r0+m) of op(T) X = alpha * B (left side).
   void left(int64_t r0, int64_t m, float alpha) {
-    if (m <= kTrsmNB) return leaf(r0, m, alpha);
-    const int64_t m1 = ((m + 1) / 2 + kTrsmNB - 1) / kTrsmNB * kTrsmNB;
+    if (m <= kTrsmLeaf) return leaf(r0, m, alpha);
+    const int64_t m1 = ((m + 1) / 2 + kTrsmLeaf - 1) / kTrsmLeaf * kTrsmLeaf;
     const GemmExtras x;
     if (opT_lower) {
       left(r0, m1, alpha);
@@ -139,8 +141,8 @@ struct Trsm {
 
   // Columns [c0, c0+n) of X op(T) = alpha * B (right side).
   void right(int64_t c0, int64_t n, float alpha) {
-    if (n <= kTrsmNB) return leaf(c0, n, alpha);
-    const int64_t n1 = ((n + 1) / 2 + kTrsmNB - 1) / kTrsmNB * kTrsmNB;
+    if (n <= kTrsmLeaf) return leaf(c0, n, alpha);
+    const int64_t n1 = ((n + 1) / 2 + kTrsmLeaf - 1) / kTrsmLeaf * kTrsmLeaf;
     const GemmExtras x;
     if (!opT_lower) {  // X1 first: X2 op(T)22 = alpha*B2 - X1 op(T)12
       right(c0, n1, alpha);
@@ -305,10 +307,14 @@ gemm_status_t gemm_trsm(gemm_handle_t h, int side, int uplo, int transA, int dia
   if (!g.ok) return GEMM_STATUS_INTERNAL;
   if (alpha == 0.f)  // X = 0
     return status_of(gemm_enqueue(hv, 0, 0, M, N, 0, 0.f, nullptr, 1, nullptr, 1, 0.f, B, ldb, dtype, GemmExtras{}));
-  const int64_t blocks = (n + kTrsmNB - 1) / kTrsmNB;
-  const size_t inv_bytes = (size_t)blocks * kTrsmNB * kTrsmNB * 2;
-  const size_t scratch_bytes = side == GEMM_SIDE_LEFT ? (size_t)kTrsmNB * pad8(N) * 2 : (size_t)M * kTrsmNB * 2;
-  if (!hv.ws || inv_bytes + scratch_bytes > hv.ws_bytes) return GEMM_STATUS_NOT_SUPPORTED;
+  // workspace: the 256-block inverses (bf16), the fp32 128-block inverses they are made
+  // from, and one leaf's rows (columns) of B for leaves that cannot run in place
+  auto up256 = [](size_t v) { return (v + 255) / 256 * 256; };
+  const int64_t blocks = (n + kTrsmLeaf - 1) / kTrsmLeaf;
+  const size_t inv_bytes = up256((size_t)blocks * kTrsmLeaf * kTrsmLeaf * 2);
+  const size_t inv128_bytes = up256((size_t)2 * blocks * kTrsmNB * kTrsmNB * 4);
+  const size_t scratch_bytes = side == GEMM_SIDE_LEFT ? (size_t)kTrsmLeaf * pad8(N) * 2 : (size_t)M * kTrsmLeaf * 2;
+  if (!hv.ws || inv_bytes + inv128_bytes + scratch_bytes > hv.ws_bytes) return GEMM_STATUS_NOT_SUPPORTED;
   Trsm t;
   t.hv = hv;
   t.side = side;
@@ -321,9 +327,9 @@ gemm_status_t gemm_trsm(gemm_handle_t h, int side, int uplo, int transA, int dia
   t.B = B;
   t.ldb = ldb;
   t.inv = (uint16_t*)hv.ws;
-  t.scratch = (uint16_t*)((char*)hv.ws + (inv_bytes + 255) / 256 * 256);
-  if ((size_t)((char*)t.scratch - (char*)hv.ws) + scratch_bytes > hv.ws_bytes) return GEMM_STATUS_NOT_SUPPORTED;
-  t.keep(launch_invert_diag(A, lda, (int)n, uplo, diag, t.inv, hv.stream));
+  float* inv128 = (float*)((char*)hv.ws + inv_bytes);
+  t.scratch = (uint16_t*)((char*)hv.ws + inv_bytes + inv128_bytes);
+  t.keep(launch_invert_diag(A, lda, (int)n, uplo, diag, inv128, t.inv, hv.stream));
   if (t.err == hipSuccess) {
     if (side == GEMM_SIDE_LEFT)
       t.left(0, M, alpha);

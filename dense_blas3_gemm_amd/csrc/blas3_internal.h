@@ -7,9 +7,11 @@
 
 namespace dbgemm {
 
-// Rows and columns of the diagonal blocks a triangular solve inverts (one workgroup of
-// kTrsmNB threads per block).
+// A triangular solve inverts its 128 x 128 diagonal blocks (one workgroup of kTrsmNB
+// threads each, fp32), combines pairs of them into the inverses of the 256 x 256 diagonal
+// blocks (bf16), and solves kTrsmLeaf rows (columns) at a time with them.
 constexpr int kTrsmNB = 128;
+constexpr int kTrsmLeaf = 2 * kTrsmNB;
 
 // What the BLAS3 code needs of a live handle.
 struct HandleView {
@@ -49,7 +51,10 @@ hipError_t launch_expand_tri(const void* src, int64_t lds, void* dst, int64_t ld
                              int cols_pad, int uplo, int unit, hipStream_t s);
 hipError_t launch_expand_sym(const void* src, int64_t lds, void* dst, int64_t ldd, int r0, int c0, int rows, int cols,
                              int cols_pad, int n, int uplo, hipStream_t s);
-hipError_t launch_invert_diag(const void* src, int64_t lds, int n, int uplo, int unit, void* dst, hipStream_t s);
+// inv128: 2 * ceil(n / 256) fp32 [128][128] blocks (scratch); dst: ceil(n / 256) bf16
+// [256][256] blocks, the inverses of T's 256 x 256 diagonal blocks (identity past n).
+hipError_t launch_invert_diag(const void* src, int64_t lds, int n, int uplo, int unit, float* inv128, void* dst,
+                              hipStream_t s);
 hipError_t launch_copy2d(const void* src, int64_t lds, void* dst, int64_t ldd, int rows, int cols, hipStream_t s);
 
 }  // namespace dbgemm

@@ -269,8 +269,9 @@ gemm_status_t gemm_trmm(gemm_handle_t h, int side, int uplo, int transA, int dia
 /* Triangular solve, in place: B <- X with op(T) X = alpha * B (side LEFT, T M x M) or
  * X op(T) = alpha * B (side RIGHT, T N x N); T as in gemm_trmm, B is bf16 M x N
  * ([M][ldb]); dtype must be GEMM_BF16_BF16.  The method is the blocked recursive one:
- * the 128 x 128 diagonal blocks of T are inverted in fp32 (stored as bf16 in the
- * workspace), each block row (or column) of X is a product with its inverted block,
+ * the 256 x 256 diagonal blocks of T are inverted in fp32 (from the inverses of their
+ * 128 x 128 halves; stored as bf16 in the workspace), each 256-row (or column) block of X
+ * is a product with its inverted block,
  * and the rest of B is updated with GEMMs (alpha*B - T_21 X_1), each rounded to bf16.
  * T must be non-singular (a zero on a non-unit diagonal gives Inf / NaN).  The result
  * is checked, as the pages' own TRSM checks were, by residual and forward / backward
