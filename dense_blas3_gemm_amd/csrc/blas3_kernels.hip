@@ -56,68 +56,107 @@ __device__ __forceinline__ void cfor(F&& f) {
 }
 
 // dst[r][c] (r < rows, c < cols, leading dimension ldd) = T[r0 + r][c0 + c] of the n x n
-// triangular matrix T.  One thread per 8 consecutive columns of one row; columns past
-// `cols` up to the padded width are written as zeros.
+// triangular matrix T.  One thread per 8 consecutive columns of one row, written with one
+// 16-byte store; a group inside the stored triangle (and off a unit diagonal) is read with
+// one 16-byte load when `vec` (src 16-byte aligned, lds and c0 multiples of 8), the rest
+// element by element, and groups outside it are not read.  Columns past `cols` up to the
+// padded width are zeros.
 __global__ __launch_bounds__(256) void expand_tri_kernel(const uint16_t* __restrict__ src, int64_t lds,
                                                          uint16_t* __restrict__ dst, int64_t ldd, int r0, int c0,
-                                                         int rows, int cols, int cols_pad, int uplo, int unit) {
+                                                         int rows, int cols, int cols_pad, int uplo, int unit,
+                                                         int vec) {
   const int groups = cols_pad / 8;
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= (int64_t)rows * groups) return;
   const int r = (int)(t / groups), c8 = (int)(t % groups) * 8;
-  const int i = r0 + r;
-  uint16_t v[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int c = c8 + e, j = c0 + c;
-    float x = 0.f;
-    if (c < cols) {
-      if (i == j && unit) x = 1.f;
-      else if (referenced(i, j, uplo)) x = bf16f(src[(int64_t)i * lds + j]);
-    }
-    v[e] = f2bf(x);
-  }
+  const int i = r0 + r, j0 = c0 + c8;
   uint4 w;
-  w.x = v[0] | ((uint32_t)v[1] << 16);
-  w.y = v[2] | ((uint32_t)v[3] << 16);
-  w.z = v[4] | ((uint32_t)v[5] << 16);
-  w.w = v[6] | ((uint32_t)v[7] << 16);
+  // the whole group strictly inside the triangle: i > j0 + 7 (lower) or i < j0 (upper)
+  const bool inside = c8 + 8 <= cols && (uplo == 0 ? i > j0 + 7 : i < j0);
+  const bool outside = uplo == 0 ? i < j0 : i > j0 + 7;
+  if (vec && inside) {
+    w = *(const uint4*)(src + (int64_t)i * lds + j0);
+  } else if (outside) {
+    w = make_uint4(0, 0, 0, 0);
+  } else {
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = c8 + e, j = c0 + c;
+      float x = 0.f;
+      if (c < cols) {
+        if (i == j && unit) x = 1.f;
+        else if (referenced(i, j, uplo)) x = bf16f(src[(int64_t)i * lds + j]);
+      }
+      v[e] = f2bf(x);
+    }
+    w.x = v[0] | ((uint32_t)v[1] << 16);
+    w.y = v[2] | ((uint32_t)v[3] << 16);
+    w.z = v[4] | ((uint32_t)v[5] << 16);
+    w.w = v[6] | ((uint32_t)v[7] << 16);
+  }
   *(uint4*)(dst + (int64_t)r * ldd + c8) = w;
 }
 
 // dst[r][c] = S[r0 + r][c0 + c] of the symmetric matrix S whose uplo triangle is stored
 // in src.  Workgroup (bx, by) writes the 64 x 64 output block at rows 64*by, columns
-// 64*bx; its elements come from src directly where (i, j) is referenced and from the
-// mirrored block (read row-wise, transposed in LDS) elsewhere.  Columns past `cols` up to
-// the padded width are zeros.
+// 64*bx, 8 columns (16 bytes) per thread and store; its elements come from src directly
+// where (i, j) is referenced and from the mirrored block elsewhere, which is read row-wise
+// into LDS and read back transposed.  With `vec` (src 16-byte aligned, lds, r0 and c0
+// multiples of 8) groups of 8 stored elements are read with one 16-byte load.  Columns
+// past `cols` up to the padded width are zeros.
 constexpr int SB = 64;
 __global__ __launch_bounds__(256) void expand_sym_kernel(const uint16_t* __restrict__ src, int64_t lds,
                                                          uint16_t* __restrict__ dst, int64_t ldd, int r0, int c0,
-                                                         int rows, int cols, int cols_pad, int n, int uplo) {
-  __shared__ uint16_t mir[SB][SB + 2];
+                                                         int rows, int cols, int cols_pad, int n, int uplo, int vec) {
+  __shared__ __attribute__((aligned(16))) uint16_t mir[SB][SB + 8];  // mir[y][x] = src[gj0 + y][gi0 + x]
   const int br = blockIdx.y * SB, bc = blockIdx.x * SB;  // output block origin
   const int gi0 = r0 + br, gj0 = c0 + bc;                  // in S
+  // 8 stored elements of src row si from column sj, or fewer / none at the edges
+  auto read8 = [&](int si, int sj, uint16_t* v) {
+    const bool all = si < n && sj + 7 < n && (uplo == 0 ? si >= sj + 7 : si <= sj);
+    if (vec && all) {
+      const uint4 w = *(const uint4*)(src + (int64_t)si * lds + sj);
+      v[0] = (uint16_t)w.x; v[1] = (uint16_t)(w.x >> 16); v[2] = (uint16_t)w.y; v[3] = (uint16_t)(w.y >> 16);
+      v[4] = (uint16_t)w.z; v[5] = (uint16_t)(w.z >> 16); v[6] = (uint16_t)w.w; v[7] = (uint16_t)(w.w >> 16);
+      return;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sje = sj + e;
+      v[e] = si < n && sje < n && referenced(si, sje, uplo) ? src[(int64_t)si * lds + sje] : (uint16_t)0;
+    }
+  };
   // does the block need the mirror (any element outside the stored triangle)?
   const bool need_mirror = uplo == 0 ? (gi0 < gj0 + SB - 1) : (gi0 + SB - 1 > gj0);
   if (need_mirror) {
-    // mir[x][y] = src[gj0 + y][gi0 + x] (row gj0 + y of src, read along its columns)
-    for (int e = threadIdx.x; e < SB * SB; e += 256) {
-      const int y = e / SB, x = e % SB;
-      const int si = gj0 + y, sj = gi0 + x;
-      uint16_t v = 0;
-      if (si < n && sj < n && referenced(si, sj, uplo)) v = src[(int64_t)si * lds + sj];
-      mir[x][y] = v;
+    for (int e = threadIdx.x; e < SB * SB / 8; e += 256) {
+      const int y = e / (SB / 8), x8 = (e % (SB / 8)) * 8;
+      uint16_t v[8];
+      read8(gj0 + y, gi0 + x8, v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) mir[y][x8 + k] = v[k];
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < SB * SB; e += 256) {
-    const int y = e / SB, x = e % SB;
-    const int r = br + y, c = bc + x;
+  for (int e = threadIdx.x; e < SB * SB / 8; e += 256) {
+    const int y = e / (SB / 8), x8 = (e % (SB / 8)) * 8;
+    const int r = br + y, c = bc + x8;
     if (r >= rows || c >= cols_pad) continue;
     const int i = r0 + r, j = c0 + c;
-    uint16_t v = 0;
-    if (c < cols && i < n && j < n) v = referenced(i, j, uplo) ? src[(int64_t)i * lds + j] : mir[y][x];
-    dst[(int64_t)r * ldd + c] = v;
+    uint16_t v[8];
+    read8(i, j, v);  // the referenced ones (zeros elsewhere)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (c + k >= cols || i >= n || j + k >= n) v[k] = 0;
+      else if (!referenced(i, j + k, uplo)) v[k] = mir[x8 + k][y];  // S[i][j+k] = src[j+k][i]
+    }
+    uint4 w;
+    w.x = v[0] | ((uint32_t)v[1] << 16);
+    w.y = v[2] | ((uint32_t)v[3] << 16);
+    w.z = v[4] | ((uint32_t)v[5] << 16);
+    w.w = v[6] | ((uint32_t)v[7] << 16);
+    *(uint4*)(dst + (int64_t)r * ldd + c) = w;
   }
 }
 
@@ -132,19 +171,45 @@ __global__ __launch_bounds__(256) void expand_sym_kernel(const uint16_t* __restr
 // stored in fp32 at dst + b*NB*NB, [NB][NB]; blocks past n are the identity.
 template <bool UPPER>
 __global__ __launch_bounds__(kTrsmNB) void invert_diag_kernel(const uint16_t* __restrict__ src, int64_t lds, int n,
-                                                              int unit, float* __restrict__ dst) {
+                                                              int unit, int vec, float* __restrict__ dst) {
   constexpr int NB = kTrsmNB;
   constexpr int LD = NB + 4;  // row stride of Tt: float4-aligned, 4-way bank spread on the transposing writes
   __shared__ __attribute__((aligned(16))) float Tt[NB * LD];  // Tt[k * LD + r] = T[r][k]
+  __shared__ float dinv[NB];                                  // 1 / T[k][k]
   const int b = blockIdx.x, o = b * NB;
   const int nb = n - o < NB ? n - o : NB;
   const int c = threadIdx.x;
-  for (int e = c; e < NB * NB; e += NB) {  // thread c reads column c of row e / NB
-    const int i = e / NB, j = e % NB;
+  // Thread c reads row c of the block: with `vec` (a full block, 16-byte aligned rows) as
+  // 16 independent 16-byte loads issued together, else element by element; it writes
+  // column c of Tt (consecutive threads, consecutive LDS words).
+  const int i = c;
+  uint16_t row[NB];
+  if (vec && nb == NB) {
+    const uint4* rp = (const uint4*)(src + (int64_t)(o + i) * lds + o);
+    uint4 w[NB / 8];
+#pragma unroll
+    for (int q = 0; q < NB / 8; ++q) w[q] = rp[q];
+#pragma unroll
+    for (int q = 0; q < NB / 8; ++q) {
+      const uint32_t u[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        row[8 * q + 2 * h] = (uint16_t)u[h];
+        row[8 * q + 2 * h + 1] = (uint16_t)(u[h] >> 16);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      row[j] = i < nb && j < nb && (UPPER ? i <= j : i >= j) ? src[(int64_t)(o + i) * lds + o + j] : (uint16_t)0;
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
     float v = 0.f;
     if (i == j && (unit || i >= nb)) v = 1.f;
-    else if (i < nb && j < nb && (UPPER ? i <= j : i >= j)) v = bf16f(src[(int64_t)(o + i) * lds + o + j]);
+    else if (i < nb && j < nb && (UPPER ? i <= j : i >= j)) v = bf16f(row[j]);
     Tt[j * LD + i] = v;
+    if (i == j) dinv[i] = 1.f / v;
   }
   __syncthreads();
   float x[NB];
@@ -153,8 +218,10 @@ __global__ __launch_bounds__(kTrsmNB) void invert_diag_kernel(const uint16_t* __
   // The updates of step s (k = s, or NB-1-s for an upper block) touch rows in 32-row
   // groups; item (s, g) needs the 32 values T[32g .. 32g+31][k].  T never changes, so the
   // values of the next item that has rows to update are read from LDS one item ahead (two
-  // register buffers) and the read latency hides behind the current item's FMAs.  Every
-  // index is a compile-time constant, so x stays in registers.
+  // register buffers) and the read latency hides behind the current item's FMAs.  Step s
+  // starts with x_k = b_k * (1 / T_kk): one multiply on the dependent chain instead of a
+  // division, with the reciprocal read one step ahead.  Every index is a compile-time
+  // constant, so x stays in registers.
   constexpr int G = 32, NG = NB / G;
   float4 buf[2][G / 4];
   auto load = [&](auto item, float4* dstb) {
@@ -166,10 +233,12 @@ __global__ __launch_bounds__(kTrsmNB) void invert_diag_kernel(const uint16_t* __
   };
   constexpr int first = next_item<UPPER, NB, G>(-1);
   load(std::integral_constant<int, first>{}, buf[0]);
+  float dk = dinv[UPPER ? NB - 1 : 0];
   cfor<NB>([&](auto sc) {
     constexpr int s = decltype(sc)::value;
     constexpr int k = UPPER ? NB - 1 - s : s;
-    x[k] = x[k] / Tt[k * LD + k];  // x_k, before the updates of its step
+    x[k] = x[k] * dk;  // x_k, before the updates of its step
+    if constexpr (s + 1 < NB) dk = dinv[UPPER ? k - 1 : k + 1];
     cfor<NG>([&](auto gc) {
       constexpr int g = decltype(gc)::value, it = s * NG + g;
       if constexpr (item_has_work<UPPER, NB, G>(it)) {
@@ -201,7 +270,7 @@ __global__ __launch_bounds__(kTrsmNB) void invert_diag_kernel(const uint16_t* __
 constexpr int CB = 2 * kTrsmNB;  // the combined block edge
 template <bool UPPER>
 __global__ __launch_bounds__(256) void combine_inverse_kernel(const uint16_t* __restrict__ src, int64_t lds, int n,
-                                                              const float* __restrict__ inv,
+                                                              int vec, const float* __restrict__ inv,
                                                               uint16_t* __restrict__ dst) {
   constexpr int NB = kTrsmNB, SW = 32, LD = NB + 4;
   __shared__ __attribute__((aligned(16))) float Xt[NB * LD];  // C^T, then P^T: Xt[k*LD + i] = X[i][k]
@@ -215,12 +284,44 @@ __global__ __launch_bounds__(256) void combine_inverse_kernel(const uint16_t* __
   const float* R = UPPER ? Di : Ai;
   // C: rows o+128.., columns o.. (lower) or rows o.., columns o+128.. (upper) of T
   const int cr = UPPER ? o : o + NB, cc = UPPER ? o + NB : o;
-  for (int e = t; e < NB * NB; e += 256) {
-    const int i = e / NB, k = e % NB;
-    const int gi = cr + i, gk = cc + k;
-    Xt[k * LD + i] = gi < n && gk < n ? bf16f(src[(int64_t)gi * lds + gk]) : 0.f;
+  // C: thread t reads half t % 2 of row t / 2 (64 elements), as 8 independent 16-byte
+  // loads when `vec` and the block is inside T, else element by element
+  {
+    const int i = t / 2, k0 = (t % 2) * (NB / 2);
+    const int gi = cr + i;
+    uint16_t row[NB / 2];
+    if (vec && cr + NB <= n && cc + NB <= n) {
+      const uint4* rp = (const uint4*)(src + (int64_t)gi * lds + cc + k0);
+      uint4 w[NB / 16];
+#pragma unroll
+      for (int q = 0; q < NB / 16; ++q) w[q] = rp[q];
+#pragma unroll
+      for (int q = 0; q < NB / 16; ++q) {
+        const uint32_t u[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          row[8 * q + 2 * h] = (uint16_t)u[h];
+          row[8 * q + 2 * h + 1] = (uint16_t)(u[h] >> 16);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NB / 2; ++k)
+        row[k] = gi < n && cc + k0 + k < n ? src[(int64_t)gi * lds + cc + k0 + k] : (uint16_t)0;
+    }
+#pragma unroll
+    for (int k = 0; k < NB / 2; ++k) Xt[(k0 + k) * LD + i] = bf16f(row[k]);
   }
-  for (int e = t; e < NB * SW; e += 256) Rs[e] = R[(e / SW) * NB + s0 + e % SW];
+  {  // R[:, s0 .. s0 + 32): 1024 float4, four per thread
+    float4 w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = (t + 256 * q) * 4;
+      w[q] = *(const float4*)(R + (e / SW) * NB + s0 + e % SW);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *(float4*)(Rs + (t + 256 * q) * 4) = w[q];
+  }
   __syncthreads();
   const int i0 = (t / 8) * 4, j0 = (t % 8) * 4;
   float acc[4][4] = {};
@@ -238,9 +339,19 @@ __global__ __launch_bounds__(256) void combine_inverse_kernel(const uint16_t* __
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) Ws[(i0 + ii) * SW + j0 + jj] = acc[ii][jj];
   __syncthreads();  // W complete; C^T no longer needed
-  for (int e = t; e < NB * NB; e += 256) {
-    const int i = e / NB, k = e % NB;
-    Xt[k * LD + i] = P[e];
+  {  // P: thread t reads half t % 2 of row t / 2 as 16 independent float4 loads
+    const int i = t / 2, k0 = (t % 2) * (NB / 2);
+    const float4* rp = (const float4*)(P + i * NB + k0);
+    float4 w[NB / 8];
+#pragma unroll
+    for (int q = 0; q < NB / 8; ++q) w[q] = rp[q];
+#pragma unroll
+    for (int q = 0; q < NB / 8; ++q) {
+      Xt[(k0 + 4 * q) * LD + i] = w[q].x;
+      Xt[(k0 + 4 * q + 1) * LD + i] = w[q].y;
+      Xt[(k0 + 4 * q + 2) * LD + i] = w[q].z;
+      Xt[(k0 + 4 * q + 3) * LD + i] = w[q].w;
+    }
   }
   __syncthreads();
   float q[4][4] = {};
@@ -291,36 +402,40 @@ unsigned blocks_for(int64_t work) {
 
 hipError_t launch_expand_tri(const void* src, int64_t lds, void* dst, int64_t ldd, int r0, int c0, int rows, int cols,
                              int cols_pad, int uplo, int unit, hipStream_t s) {
+  const int vec = ((uintptr_t)src % 16 == 0) && lds % 8 == 0 && c0 % 8 == 0;
   hipLaunchKernelGGL(expand_tri_kernel, dim3(blocks_for((int64_t)rows * (cols_pad / 8))), dim3(256), 0, s,
-                     (const uint16_t*)src, lds, (uint16_t*)dst, ldd, r0, c0, rows, cols, cols_pad, uplo, unit);
+                     (const uint16_t*)src, lds, (uint16_t*)dst, ldd, r0, c0, rows, cols, cols_pad, uplo, unit, vec);
   return hipGetLastError();
 }
 
 hipError_t launch_expand_sym(const void* src, int64_t lds, void* dst, int64_t ldd, int r0, int c0, int rows, int cols,
                              int cols_pad, int n, int uplo, hipStream_t s) {
+  const int vec = ((uintptr_t)src % 16 == 0) && lds % 8 == 0 && r0 % 8 == 0 && c0 % 8 == 0;
   dim3 grid((unsigned)((cols_pad + SB - 1) / SB), (unsigned)((rows + SB - 1) / SB));
   hipLaunchKernelGGL(expand_sym_kernel, grid, dim3(256), 0, s, (const uint16_t*)src, lds, (uint16_t*)dst, ldd, r0, c0,
-                     rows, cols, cols_pad, n, uplo);
+                     rows, cols, cols_pad, n, uplo, vec);
   return hipGetLastError();
 }
 
 hipError_t launch_invert_diag(const void* src, int64_t lds, int n, int uplo, int unit, float* inv128, void* dst,
                               hipStream_t s) {
   const int blocks = (n + kTrsmLeaf - 1) / kTrsmLeaf;  // 256-blocks; two 128-blocks each
+  // rows of T readable as 16-byte vectors
+  const int vec = ((uintptr_t)src % 16 == 0) && lds % 8 == 0;
   if (uplo == 0)
     hipLaunchKernelGGL(invert_diag_kernel<false>, dim3((unsigned)(2 * blocks)), dim3(kTrsmNB), 0, s,
-                       (const uint16_t*)src, lds, n, unit, inv128);
+                       (const uint16_t*)src, lds, n, unit, vec, inv128);
   else
     hipLaunchKernelGGL(invert_diag_kernel<true>, dim3((unsigned)(2 * blocks)), dim3(kTrsmNB), 0, s,
-                       (const uint16_t*)src, lds, n, unit, inv128);
+                       (const uint16_t*)src, lds, n, unit, vec, inv128);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)blocks, kTrsmNB / 32);
   if (uplo == 0)
-    hipLaunchKernelGGL(combine_inverse_kernel<false>, grid, dim3(256), 0, s, (const uint16_t*)src, lds, n,
+    hipLaunchKernelGGL(combine_inverse_kernel<false>, grid, dim3(256), 0, s, (const uint16_t*)src, lds, n, vec,
                        (const float*)inv128, (uint16_t*)dst);
   else
-    hipLaunchKernelGGL(combine_inverse_kernel<true>, grid, dim3(256), 0, s, (const uint16_t*)src, lds, n,
+    hipLaunchKernelGGL(combine_inverse_kernel<true>, grid, dim3(256), 0, s, (const uint16_t*)src, lds, n, vec,
                        (const float*)inv128, (uint16_t*)dst);
   return hipGetLastError();
 }
