@@ -84,6 +84,11 @@ struct Trsm {
   int64_t ldb;
   uint16_t* inv;      // inverted 256 x 256 diagonal blocks, [blocks][256][256]
   uint16_t* scratch;  // one block row (column) of B, for leaves that cannot run in place
+  // Out of place: every leaf writes its rows (columns) of X to X [M][ldx] in the workspace,
+  // the updates read X from there, and one copy moves X into B at the end.  The leaves then
+  // take any tile shape (more workgroups than the one-tile-per-leaf in-place form).
+  uint16_t* X = nullptr;
+  int64_t ldx = 0;
   hipError_t err = hipSuccess;
 
   void keep(hipError_t e) {
@@ -94,10 +99,23 @@ struct Trsm {
     return transA ? off(A, c0, r0, lda, 2) : off(A, r0, c0, lda, 2);
   }
 
+  // where the solved rows (columns) of X live: X in the workspace, or B itself
+  const void* xsrc(int64_t row, int64_t col) const { return X ? off(X, row, col, ldx, 2) : off(B, row, col, ldb, 2); }
+  int64_t xld() const { return X ? ldx : ldb; }
+
   void leaf(int64_t o, int64_t nb, float alpha) {
     constexpr int L = kTrsmLeaf;
     const uint16_t* ib = inv + (o / L) * L * L;
     GemmExtras x;
+    if (X) {  // out of place: any policy
+      if (side == GEMM_SIDE_LEFT)
+        keep(gemm_enqueue(hv, transA, 0, nb, N, nb, alpha, ib, L, off(B, o, 0, ldb, 2), ldb, 0.f, off(X, o, 0, ldx, 2),
+                          ldx, GEMM_BF16_BF16, x));
+      else
+        keep(gemm_enqueue(hv, 0, transA, M, nb, nb, alpha, off(B, 0, o, ldb, 2), ldb, ib, L, 0.f, off(X, 0, o, ldx, 2),
+                          ldx, GEMM_BF16_BF16, x));
+      return;
+    }
     const int pol = leaf_policy(side);
     if (side == GEMM_SIDE_LEFT) {  // X rows [o, o+nb) = alpha * op(inv) * B rows
       void* Bb = off(B, o, 0, ldb, 2);
@@ -128,13 +146,13 @@ struct Trsm {
     const GemmExtras x;
     if (opT_lower) {
       left(r0, m1, alpha);
-      keep(gemm_enqueue(hv, transA, 0, m - m1, N, m1, -1.f, opT_block(r0 + m1, r0), lda, off(B, r0, 0, ldb, 2), ldb,
-                        alpha, off(B, r0 + m1, 0, ldb, 2), ldb, GEMM_BF16_BF16, x));
+      keep(gemm_enqueue(hv, transA, 0, m - m1, N, m1, -1.f, opT_block(r0 + m1, r0), lda, xsrc(r0, 0), xld(), alpha,
+                        off(B, r0 + m1, 0, ldb, 2), ldb, GEMM_BF16_BF16, x));
       left(r0 + m1, m - m1, 1.f);
     } else {
       left(r0 + m1, m - m1, alpha);
-      keep(gemm_enqueue(hv, transA, 0, m1, N, m - m1, -1.f, opT_block(r0, r0 + m1), lda,
-                        off(B, r0 + m1, 0, ldb, 2), ldb, alpha, off(B, r0, 0, ldb, 2), ldb, GEMM_BF16_BF16, x));
+      keep(gemm_enqueue(hv, transA, 0, m1, N, m - m1, -1.f, opT_block(r0, r0 + m1), lda, xsrc(r0 + m1, 0), xld(),
+                        alpha, off(B, r0, 0, ldb, 2), ldb, GEMM_BF16_BF16, x));
       left(r0, m1, 1.f);
     }
   }
@@ -146,13 +164,13 @@ struct Trsm {
     const GemmExtras x;
     if (!opT_lower) {  // X1 first: X2 op(T)22 = alpha*B2 - X1 op(T)12
       right(c0, n1, alpha);
-      keep(gemm_enqueue(hv, 0, transA, M, n - n1, n1, -1.f, off(B, 0, c0, ldb, 2), ldb, opT_block(c0, c0 + n1), lda,
-                        alpha, off(B, 0, c0 + n1, ldb, 2), ldb, GEMM_BF16_BF16, x));
+      keep(gemm_enqueue(hv, 0, transA, M, n - n1, n1, -1.f, xsrc(0, c0), xld(), opT_block(c0, c0 + n1), lda, alpha,
+                        off(B, 0, c0 + n1, ldb, 2), ldb, GEMM_BF16_BF16, x));
       right(c0 + n1, n - n1, 1.f);
     } else {  // X2 first: X1 op(T)11 = alpha*B1 - X2 op(T)21
       right(c0 + n1, n - n1, alpha);
-      keep(gemm_enqueue(hv, 0, transA, M, n1, n - n1, -1.f, off(B, 0, c0 + n1, ldb, 2), ldb, opT_block(c0 + n1, c0),
-                        lda, alpha, off(B, 0, c0, ldb, 2), ldb, GEMM_BF16_BF16, x));
+      keep(gemm_enqueue(hv, 0, transA, M, n1, n - n1, -1.f, xsrc(0, c0 + n1), xld(), opT_block(c0 + n1, c0), lda,
+                        alpha, off(B, 0, c0, ldb, 2), ldb, GEMM_BF16_BF16, x));
       right(c0, n1, 1.f);
     }
   }
@@ -329,6 +347,14 @@ gemm_status_t gemm_trsm(gemm_handle_t h, int side, int uplo, int transA, int dia
   t.inv = (uint16_t*)hv.ws;
   float* inv128 = (float*)((char*)hv.ws + inv_bytes);
   t.scratch = (uint16_t*)((char*)hv.ws + inv_bytes + inv128_bytes);
+  // Out of place for large right-hand sides (from 2^20 elements of B), when X fits beside
+  // the inverses: its one copy back is cheaper than leaves limited to one tile per leaf.
+  const int64_t ldx = pad8(N);
+  const size_t x_bytes = (size_t)M * ldx * 2;
+  if (M * N >= ((int64_t)1 << 20) && inv_bytes + inv128_bytes + x_bytes <= hv.ws_bytes) {
+    t.X = t.scratch;
+    t.ldx = ldx;
+  }
   t.keep(launch_invert_diag(A, lda, (int)n, uplo, diag, inv128, t.inv, hv.stream));
   if (t.err == hipSuccess) {
     if (side == GEMM_SIDE_LEFT)
@@ -336,6 +362,7 @@ gemm_status_t gemm_trsm(gemm_handle_t h, int side, int uplo, int transA, int dia
     else
       t.right(0, N, alpha);
   }
+  if (t.err == hipSuccess && t.X) t.keep(launch_copy2d(t.X, ldx, B, ldb, (int)M, (int)N, hv.stream));
   return status_of(t.err);
 }
 

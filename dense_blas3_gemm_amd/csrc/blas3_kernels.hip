@@ -382,9 +382,20 @@ __global__ __launch_bounds__(256) void combine_inverse_kernel(const uint16_t* __
 }
 
 // dst[r][c] = src[r][c] for an rows x cols bf16 block (both row-major with their own
-// leading dimensions).
+// leading dimensions); with `vec` (both 16-byte aligned, leading dimensions and cols
+// multiples of 8) 8 elements per 16-byte load and store.
 __global__ __launch_bounds__(256) void copy2d_kernel(const uint16_t* __restrict__ src, int64_t lds,
-                                                     uint16_t* __restrict__ dst, int64_t ldd, int rows, int cols) {
+                                                     uint16_t* __restrict__ dst, int64_t ldd, int rows, int cols,
+                                                     int vec) {
+  if (vec) {
+    const int g = cols / 8;
+    const int64_t total = (int64_t)rows * g;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+      const int r = (int)(e / g), c = (int)(e % g) * 8;
+      *(uint4*)(dst + (int64_t)r * ldd + c) = *(const uint4*)(src + (int64_t)r * lds + c);
+    }
+    return;
+  }
   const int64_t total = (int64_t)rows * cols;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
     const int r = (int)(e / cols), c = (int)(e % cols);
@@ -444,8 +455,9 @@ hipError_t launch_copy2d(const void* src, int64_t lds, void* dst, int64_t ldd, i
   int64_t b = ((int64_t)rows * cols + 255) / 256;
   if (b > 8192) b = 8192;
   if (b < 1) b = 1;
+  const int vec = (uintptr_t)src % 16 == 0 && (uintptr_t)dst % 16 == 0 && lds % 8 == 0 && ldd % 8 == 0 && cols % 8 == 0;
   hipLaunchKernelGGL(copy2d_kernel, dim3((unsigned)b), dim3(256), 0, s, (const uint16_t*)src, lds, (uint16_t*)dst, ldd,
-                     rows, cols);
+                     rows, cols, vec);
   return hipGetLastError();
 }
 

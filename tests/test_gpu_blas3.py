@@ -320,3 +320,19 @@ def test_gemm_192_tile_nt(gpu, M, N, K):
     finally:
         gpu.set_policy(None)
     assert st == 2  # NOT_SUPPORTED
+
+
+@pytest.mark.parametrize("side", [LEFT, RIGHT])
+@pytest.mark.parametrize("uplo", [LOWER, UPPER])
+@pytest.mark.parametrize("transA", [0, 1])
+def test_trsm_exact_integer_out_of_place(gpu, side, uplo, transA):
+    """From 2^20 elements of B the solve keeps X in the workspace and copies it back at the
+    end (the leaves then run on any tile shape): the exact integer system at 1024 x 1024
+    pins that form bit for bit, as the smaller cases pin the in-place one."""
+    M = N = 1024
+    n = M if side == LEFT else N
+    A, Xt, Bb = _int_system(n, M, N, side, uplo, transA, 0, 40)
+    Bd = to_device(Bb, "bf16")
+    gpu.trsm(to_device(A, "bf16"), Bd, side=side, uplo=uplo, transA=transA, diag=0, alpha=1.0)
+    sync()
+    assert np.array_equal(to_host(Bd), Xt)
