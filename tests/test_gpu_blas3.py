@@ -336,3 +336,89 @@ def test_trsm_exact_integer_out_of_place(gpu, side, uplo, transA):
     gpu.trsm(to_device(A, "bf16"), Bd, side=side, uplo=uplo, transA=transA, diag=0, alpha=1.0)
     sync()
     assert np.array_equal(to_host(Bd), Xt)
+
+
+# ------------------------------------------------------------------ panels and strides
+
+@pytest.mark.parametrize("side", [LEFT, RIGHT])
+def test_symm_two_panels(gpu, side):
+    """n = 6144: the expanded symmetric matrix (6144 x 6144 bf16) exceeds the 64 MiB workspace,
+    so it is expanded and multiplied in two row panels (5376 + 768 rows)."""
+    n, other = 6144, 40
+    M, N = (n, other) if side == LEFT else (other, n)
+    A = gi.bf16_symmetric_stored(n, UPPER, 5)
+    B = gi.bf16_uniform((M, N), 6)
+    C0 = c_bits((M, N), "f32", 7)
+    C = to_device(C0, "f32")
+    gpu.symm(to_device(A, "bf16"), to_device(B, "bf16"), C, side=side, uplo=UPPER, alpha=0.5, beta=2.0)
+    sync()
+    R, S = blas3.symm(side, UPPER, M, N, 0.5, A, B, 2.0, C0, oracle.C_F32)
+    check_c(to_host(C), "f32", R, S, n)
+
+
+@pytest.mark.parametrize("side", [LEFT, RIGHT])
+@pytest.mark.parametrize("transA", [0, 1])
+def test_trmm_two_panels(gpu, side, transA):
+    """n = 6144 in two panels, each with its own K-band offset."""
+    import torch
+    n, other = 6144, 48
+    M, N = (n, other) if side == LEFT else (other, n)
+    A = gi.bf16_triangular(n, LOWER, 8)
+    B = gi.bf16_uniform((M, N), 9)
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda:0")
+    gpu.trmm(to_device(A, "bf16"), to_device(B, "bf16"), C, side=side, uplo=LOWER, transA=transA, alpha=1.0)
+    sync()
+    R, S = blas3.trmm(side, LOWER, transA, 0, M, N, 1.0, A, B)
+    check_c(to_host(C), "f32", R, S, n)
+
+
+def _strided(bits, extra):
+    """A device view of `bits` inside a wider buffer (leading dimension + extra), the padding
+    NaN so that a read past the row shows."""
+    import torch
+    rows, cols = bits.shape
+    wide = np.full((rows, cols + extra), 0x7FC0, dtype=np.uint16)
+    wide[:, :cols] = bits
+    return to_device(wide, "bf16")[:, :cols]
+
+
+def test_blas3_strided_operands(gpu):
+    """Every operand with a leading dimension larger than its row (views of wider buffers
+    with NaN padding): SYRK, SYR2K (lda == ldb), SYMM, TRMM and TRSM against the oracle."""
+    import torch
+    N, K = 136, 72
+    A = gi.bf16_uniform((N, K), 1)
+    B = gi.bf16_uniform((N, K), 2)
+    C = torch.zeros((N, N + 16), dtype=torch.float32, device="cuda:0")[:, :N]
+    gpu.syrk(_strided(A, 8), C, uplo=LOWER, trans=0)
+    sync()
+    R, S = blas3.syrk(LOWER, 0, N, K, 1.0, A, 0.0, None, oracle.C_F32)
+    m = tri_mask(N, LOWER)
+    check_c(to_host(C), "f32", R, S, K, m)
+    C.zero_()
+    gpu.syr2k(_strided(A, 8), _strided(B, 8), C, uplo=UPPER, trans=0)
+    sync()
+    R, S = blas3.syr2k(UPPER, 0, N, K, 1.0, A, B, 0.0, None, oracle.C_F32)
+    check_c(to_host(C), "f32", R, S, 2 * K, tri_mask(N, UPPER))
+    M2, N2 = 136, 200
+    Sm = gi.bf16_symmetric_stored(M2, LOWER, 3)
+    B2 = gi.bf16_uniform((M2, N2), 4)
+    C2 = torch.zeros((M2, N2 + 8), dtype=torch.float32, device="cuda:0")[:, :N2]
+    gpu.symm(_strided(Sm, 16), _strided(B2, 8), C2, side=LEFT, uplo=LOWER)
+    sync()
+    R, S = blas3.symm(LEFT, LOWER, M2, N2, 1.0, Sm, B2, 0.0, None, oracle.C_F32)
+    check_c(to_host(C2), "f32", R, S, M2)
+    T = gi.bf16_triangular(M2, UPPER, 5)
+    C2.zero_()
+    gpu.trmm(_strided(T, 24), _strided(B2, 8), C2, side=LEFT, uplo=UPPER, transA=1)
+    sync()
+    R, S = blas3.trmm(LEFT, UPPER, 1, 0, M2, N2, 1.0, T, B2)
+    check_c(to_host(C2), "f32", R, S, M2)
+    Bd = _strided(B2, 8)
+    gpu.trsm(_strided(T, 24), Bd, side=LEFT, uplo=UPPER, transA=1, alpha=1.0)
+    sync()
+    X = tolerance.bf16_bits_to_f64(to_host(Bd))
+    X_ref = blas3.trsm(LEFT, UPPER, 1, 0, M2, N2, 1.0, T, B2)
+    opT = blas3.triangular(T, M2, UPPER, 0).T
+    res = tolerance.trsm_check(X, X_ref, opT, tolerance.bf16_bits_to_f64(B2), LEFT, M2)
+    assert res["ok"], res
