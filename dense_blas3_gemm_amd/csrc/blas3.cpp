@@ -27,6 +27,11 @@ int64_t at_least_1(int64_t v) { return v > 1 ? v : 1; }
 int64_t pad8(int64_t v) { return (v + 7) / 8 * 8; }
 bool valid_flag(int f) { return f == 0 || f == 1; }
 bool size_ok(int64_t v) { return v >= 0 && v <= INT_MAX; }
+// Rows the generic kernel's grid can cover (65535 workgroups of 64 rows).  The operations
+// below launch several kernels; checking this bound before the first launch keeps an
+// unsupported size from failing half way through, with part of the output written.
+constexpr int64_t kMaxRows = (int64_t)65535 * 64;
+bool rows_ok(int64_t a, int64_t b) { return a <= kMaxRows && b <= kMaxRows; }
 
 const void* off(const void* p, int64_t row, int64_t col, int64_t ld, int es) {
   return (const char*)p + (row * ld + col) * es;
@@ -187,7 +192,7 @@ gemm_status_t gemm_syrk(gemm_handle_t h, int uplo, int trans, int64_t N, int64_t
   if (!valid_flag(uplo) || !valid_flag(trans) || !bf16_dtype(dtype)) return GEMM_STATUS_INVALID_VALUE;
   if (!size_ok(N) || !size_ok(K)) return GEMM_STATUS_INVALID_VALUE;
   if (lda < at_least_1(trans ? N : K) || ldc < at_least_1(N)) return GEMM_STATUS_INVALID_VALUE;
-  if (!std::isfinite(alpha) || !std::isfinite(beta)) return GEMM_STATUS_NOT_SUPPORTED;
+  if (!std::isfinite(alpha) || !std::isfinite(beta) || !rows_ok(N, N)) return GEMM_STATUS_NOT_SUPPORTED;
   if (N == 0) return GEMM_STATUS_SUCCESS;
   if (!C || (K > 0 && alpha != 0.f && !A)) return GEMM_STATUS_INVALID_VALUE;
   DeviceGuard g(hv.device);
@@ -205,7 +210,7 @@ gemm_status_t gemm_syr2k(gemm_handle_t h, int uplo, int trans, int64_t N, int64_
   if (!size_ok(N) || !size_ok(K)) return GEMM_STATUS_INVALID_VALUE;
   const int64_t row = at_least_1(trans ? N : K);
   if (lda < row || ldb < row || ldc < at_least_1(N)) return GEMM_STATUS_INVALID_VALUE;
-  if (!std::isfinite(alpha) || !std::isfinite(beta)) return GEMM_STATUS_NOT_SUPPORTED;
+  if (!std::isfinite(alpha) || !std::isfinite(beta) || !rows_ok(N, N)) return GEMM_STATUS_NOT_SUPPORTED;
   if (N == 0) return GEMM_STATUS_SUCCESS;
   if (!C || (K > 0 && alpha != 0.f && (!A || !B))) return GEMM_STATUS_INVALID_VALUE;
   DeviceGuard g(hv.device);
@@ -228,7 +233,7 @@ gemm_status_t gemm_symm(gemm_handle_t h, int side, int uplo, int64_t M, int64_t 
   if (!size_ok(M) || !size_ok(N)) return GEMM_STATUS_INVALID_VALUE;
   const int64_t n = side == GEMM_SIDE_LEFT ? M : N;
   if (lda < at_least_1(n) || ldb < at_least_1(N) || ldc < at_least_1(N)) return GEMM_STATUS_INVALID_VALUE;
-  if (!std::isfinite(alpha) || !std::isfinite(beta)) return GEMM_STATUS_NOT_SUPPORTED;
+  if (!std::isfinite(alpha) || !std::isfinite(beta) || !rows_ok(M, N)) return GEMM_STATUS_NOT_SUPPORTED;
   if (M == 0 || N == 0) return GEMM_STATUS_SUCCESS;
   if (!C || (alpha != 0.f && (!A || !B))) return GEMM_STATUS_INVALID_VALUE;
   DeviceGuard g(hv.device);
@@ -267,7 +272,7 @@ gemm_status_t gemm_trmm(gemm_handle_t h, int side, int uplo, int transA, int dia
   if (!size_ok(M) || !size_ok(N)) return GEMM_STATUS_INVALID_VALUE;
   const int64_t n = side == GEMM_SIDE_LEFT ? M : N;
   if (lda < at_least_1(n) || ldb < at_least_1(N) || ldc < at_least_1(N)) return GEMM_STATUS_INVALID_VALUE;
-  if (!std::isfinite(alpha)) return GEMM_STATUS_NOT_SUPPORTED;
+  if (!std::isfinite(alpha) || !rows_ok(M, N)) return GEMM_STATUS_NOT_SUPPORTED;
   if (M == 0 || N == 0) return GEMM_STATUS_SUCCESS;
   if (!C || (alpha != 0.f && (!A || !B))) return GEMM_STATUS_INVALID_VALUE;
   DeviceGuard g(hv.device);
@@ -318,7 +323,7 @@ gemm_status_t gemm_trsm(gemm_handle_t h, int side, int uplo, int transA, int dia
   if (!size_ok(M) || !size_ok(N)) return GEMM_STATUS_INVALID_VALUE;
   const int64_t n = side == GEMM_SIDE_LEFT ? M : N;
   if (lda < at_least_1(n) || ldb < at_least_1(N)) return GEMM_STATUS_INVALID_VALUE;
-  if (!std::isfinite(alpha)) return GEMM_STATUS_NOT_SUPPORTED;
+  if (!std::isfinite(alpha) || !rows_ok(M, N)) return GEMM_STATUS_NOT_SUPPORTED;
   if (M == 0 || N == 0) return GEMM_STATUS_SUCCESS;
   if (!B || (alpha != 0.f && !A)) return GEMM_STATUS_INVALID_VALUE;
   DeviceGuard g(hv.device);

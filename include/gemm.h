@@ -223,8 +223,8 @@ const char* gemm_status_string(int status);
  * Nothing is allocated; the calls return once everything is enqueued on the handle's
  * stream.  Errors: arguments are checked before anything is launched (INVALID_VALUE
  * for a bad size, leading dimension, flag, pointer or dtype; NOT_SUPPORTED for
- * non-finite alpha / beta or an operand larger than the workspace handles, see each
- * call); on an error nothing is written.  Fast path: the MFMA kernels need the GEMM
+ * non-finite alpha / beta, M or N above 65535 * 64, or an operand larger than the
+ * workspace handles, see each call); on an error nothing is written.  Fast path: the MFMA kernels need the GEMM
  * fast-path alignment of gemm.h; anything else runs on the generic kernel.
  * --------------------------------------------------------------------------------- */
 typedef enum { GEMM_LOWER = 0, GEMM_UPPER = 1 } gemm_uplo_t;
