@@ -390,7 +390,7 @@ def mx_bench(g, warmup: int = 5, steps: int = 30):
 BLAS3_N = 4096
 
 
-def blas3_bench(g, warmup: int = 5, steps: int = 30, n: int = BLAS3_N):
+def blas3_bench(g, warmup: int = 5, steps: int = 30, n: int = BLAS3_N, cpu: bool = True):
     """Event-timed p50 of each BLAS3 call at n x n (left side, lower, no transpose,
     non-unit diagonal); returns a list of dicts and prints a Markdown table to stderr."""
     import torch
@@ -435,15 +435,47 @@ def blas3_bench(g, warmup: int = 5, steps: int = 30, n: int = BLAS3_N):
         tf = flops / (p50 * 1e-3) / 1e12
         rows.append({"op": name, "n": n, "us_p50": round(p50 * 1e3, 1), "us_p95": round(p95 * 1e3, 1),
                      "tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_TFLOPS["bf16"], 4)})
+    if cpu:
+        for r, c in zip(rows, blas3_cpu_baseline()):
+            r["cpu_oracle_gflops"] = c
     print(f"BLAS3 family at {n} (bf16 in, fp32 accumulate, bf16 out; p50 of {steps} event-timed calls)",
           file=sys.stderr)
-    print("| op | us p50 | us p95 | TFLOP/s | frac of bf16 peak |", file=sys.stderr)
-    print("|---|---|---|---|---|", file=sys.stderr)
+    import oracle
+    print(f"| op | us p50 | us p95 | TFLOP/s | frac of bf16 peak | oracle GFLOP/s (host, n = 1024, "
+          f"{oracle.default_threads()} threads) |", file=sys.stderr)
+    print("|---|---|---|---|---|---|", file=sys.stderr)
     for r in rows:
-        print(f"| {r['op']} | {r['us_p50']} | {r['us_p95']} | {r['tflops']} | {r['frac_bf16_peak']} |",
-              file=sys.stderr)
+        print(f"| {r['op']} | {r['us_p50']} | {r['us_p95']} | {r['tflops']} | {r['frac_bf16_peak']} | "
+              f"{r.get('cpu_oracle_gflops', '-')} |", file=sys.stderr)
     print("blas3: " + json.dumps(rows), file=sys.stderr)
     return rows
+
+
+def blas3_cpu_baseline(n: int = 1024):
+    """The oracle as it stands (float64 numpy, oracle/blas3.py; the C oracle for the plain
+    GEMM), timed on the host for each operation of blas3_bench at n = 1024 instead of 4096
+    (a bounded sample of the same workload: each takes under a few seconds).  Returns
+    GFLOP/s in blas3_bench's order, counting the same useful FLOPs."""
+    import oracle
+    from oracle import blas3 as ob
+    A, B = gi.bf16_uniform((n, n), 0), gi.bf16_uniform((n, n), 1)
+    Tm, Sm = gi.bf16_triangular(n, gi.LOWER, 2), gi.bf16_symmetric_stored(n, gi.LOWER, 3)
+    nn = float(n)
+    calls = [
+        (2 * nn ** 3, lambda: oracle.gemm(0, 0, n, n, n, 1.0, A, n, B, n, 0.0, None, n, oracle.IN_BF16,
+                                          oracle.C_BF16, with_abs=False)),
+        (nn * (nn + 1) * nn, lambda: ob.syrk(0, 0, n, n, 1.0, A, 0.0, None, oracle.C_BF16)),
+        (2 * nn * (nn + 1) * nn, lambda: ob.syr2k(0, 0, n, n, 1.0, A, B, 0.0, None, oracle.C_BF16)),
+        (2 * nn ** 3, lambda: ob.symm(0, 0, n, n, 1.0, Sm, B, 0.0, None, oracle.C_BF16)),
+        (nn ** 3, lambda: ob.trmm(0, 0, 0, 0, n, n, 1.0, Tm, B)),
+        (nn ** 3, lambda: ob.trsm(0, 0, 0, 0, n, n, 1.0, Tm, B)),
+    ]
+    out = []
+    for flops, fn in calls:
+        t0 = time.perf_counter()
+        fn()
+        out.append(round(flops / (time.perf_counter() - t0) / 1e9, 2))
+    return out
 
 
 def main():
@@ -489,7 +521,7 @@ def main():
     g = d.Gemm(0)
     if args.ladder or args.lds_probe or args.mx or args.blas3:
         if args.blas3:
-            blas3_bench(g)
+            blas3_bench(g, cpu=not args.no_cpu_baseline)
         if args.mx:
             mx_bench(g)
         if args.lds_probe:
