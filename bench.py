@@ -398,6 +398,7 @@ def blas3_bench(g, warmup: int = 5, steps: int = 30, n: int = BLAS3_N, cpu: bool
     A = _dev(gi.bf16_uniform((n, n), 0), "bf16")
     B = _dev(gi.bf16_uniform((n, n), 1), "bf16")
     Tm = _dev(gi.bf16_triangular(n, gi.LOWER, 2), "bf16")
+    Tu = _dev(gi.bf16_triangular(n, gi.UPPER, 4), "bf16")
     Sm = _dev(gi.bf16_symmetric_stored(n, gi.LOWER, 3), "bf16")
     C = torch.zeros((n, n), dtype=torch.bfloat16, device="cuda:0")
     X = torch.empty_like(B)
@@ -427,6 +428,10 @@ def blas3_bench(g, warmup: int = 5, steps: int = 30, n: int = BLAS3_N, cpu: bool
         # the solve overwrites its right-hand side: a fresh copy goes in before each call,
         # outside the event pair
         ("trsm left lower N", nn ** 3, lambda: g.trsm(Tm, X, side=0, uplo=0, transA=0), lambda: X.copy_(B)),
+        # the other layouts: A read transposed (TN), the triangle on the right, upper, transposed
+        ("syrk lower, T", nn * (nn + 1) * nn, lambda: g.syrk(A, C, uplo=0, trans=1), None),
+        ("trmm right upper T", nn ** 3, lambda: g.trmm(Tu, B, C, side=1, uplo=1, transA=1), None),
+        ("trsm right upper T", nn ** 3, lambda: g.trsm(Tu, X, side=1, uplo=1, transA=1), lambda: X.copy_(B)),
     ]
     rows = []
     for name, flops, fn, pre in ops:
@@ -460,6 +465,7 @@ def blas3_cpu_baseline(n: int = 1024):
     from oracle import blas3 as ob
     A, B = gi.bf16_uniform((n, n), 0), gi.bf16_uniform((n, n), 1)
     Tm, Sm = gi.bf16_triangular(n, gi.LOWER, 2), gi.bf16_symmetric_stored(n, gi.LOWER, 3)
+    Tu = gi.bf16_triangular(n, gi.UPPER, 4)
     nn = float(n)
     calls = [
         (2 * nn ** 3, lambda: oracle.gemm(0, 0, n, n, n, 1.0, A, n, B, n, 0.0, None, n, oracle.IN_BF16,
@@ -469,6 +475,9 @@ def blas3_cpu_baseline(n: int = 1024):
         (2 * nn ** 3, lambda: ob.symm(0, 0, n, n, 1.0, Sm, B, 0.0, None, oracle.C_BF16)),
         (nn ** 3, lambda: ob.trmm(0, 0, 0, 0, n, n, 1.0, Tm, B)),
         (nn ** 3, lambda: ob.trsm(0, 0, 0, 0, n, n, 1.0, Tm, B)),
+        (nn * (nn + 1) * nn, lambda: ob.syrk(0, 1, n, n, 1.0, A, 0.0, None, oracle.C_BF16)),
+        (nn ** 3, lambda: ob.trmm(1, 1, 1, 0, n, n, 1.0, Tu, B)),
+        (nn ** 3, lambda: ob.trsm(1, 1, 1, 0, n, n, 1.0, Tu, B)),
     ]
     out = []
     for flops, fn in calls:
