@@ -69,6 +69,17 @@ int64_t panel_rows(const HandleView& hv, int64_t n) {
   return p;
 }
 
+// Whether a symmetric update with A (and B) stored [K][N] should first copy its `count`
+// operands transposed into the workspace: from 2^20 elements per operand (where the copy,
+// HBM-bound, costs much less than running the product with both operands M/N-contiguous),
+// when the copies fit and the product would then take the fast kernels.
+bool transpose_pays(const HandleView& hv, int64_t N, int64_t K, int count) {
+  const int64_t ldt = pad8(K);
+  if (!hv.ws || N * K < ((int64_t)1 << 20)) return false;
+  if ((size_t)count * (size_t)N * ldt * 2 > hv.ws_bytes) return false;
+  return gemm_fast_ok(0, 1, N, N, K, hv.ws, ldt, hv.ws, ldt, hv.ws, N, GEMM_BF16_BF16);
+}
+
 // The policies a TRSM leaf runs with when it updates its block of B in place: one 256-row
 // (left) or 256-column (right) tile spans the whole leaf, so each workgroup reads the part
 // of B it overwrites, all of it before its epilogue, and no other workgroup reads it.
@@ -199,6 +210,14 @@ gemm_status_t gemm_syrk(gemm_handle_t h, int uplo, int trans, int64_t N, int64_t
   if (!g.ok) return GEMM_STATUS_INTERNAL;
   GemmExtras x;
   x.tri = uplo == GEMM_LOWER ? TRI_LOWER : TRI_UPPER;
+  if (trans && K > 0 && alpha != 0.f && transpose_pays(hv, N, K, 1)) {
+    // A [K][N] is copied once as A^T [N][K] into the workspace, so the product runs with both
+    // operands K-contiguous (the 192-wide tile, plain LDS reads)
+    const int64_t ldt = pad8(K);
+    hipError_t e = launch_transpose(A, lda, hv.ws, ldt, (int)K, (int)N, hv.stream);
+    if (e == hipSuccess) e = gemm_enqueue(hv, 0, 1, N, N, K, alpha, hv.ws, ldt, hv.ws, ldt, beta, C, ldc, dtype, x);
+    return status_of(e);
+  }
   return status_of(gemm_enqueue(hv, trans, 1 - trans, N, N, K, alpha, A, lda, A, lda, beta, C, ldc, dtype, x));
 }
 
@@ -218,6 +237,20 @@ gemm_status_t gemm_syr2k(gemm_handle_t h, int uplo, int trans, int64_t N, int64_
   GemmExtras x;
   x.tri = uplo == GEMM_LOWER ? TRI_LOWER : TRI_UPPER;
   x.dual = 1;  // op(A) op(B)^T, then op(B) op(A)^T
+  if (trans && K > 0 && alpha != 0.f && transpose_pays(hv, N, K, 2)) {
+    // A and B [K][N] copied once as A^T, B^T [N][K] into the workspace (see gemm_syrk)
+    const int64_t ldt = pad8(K);
+    void* At = hv.ws;
+    void* Bt = (char*)hv.ws + (size_t)N * ldt * 2;
+    hipError_t e = launch_transpose(A, lda, At, ldt, (int)K, (int)N, hv.stream);
+    if (e == hipSuccess) e = launch_transpose(B, ldb, Bt, ldt, (int)K, (int)N, hv.stream);
+    x.A2 = Bt;
+    x.lda2 = ldt;
+    x.B2 = At;
+    x.ldb2 = ldt;
+    if (e == hipSuccess) e = gemm_enqueue(hv, 0, 1, N, N, K, alpha, At, ldt, Bt, ldt, beta, C, ldc, dtype, x);
+    return status_of(e);
+  }
   x.A2 = B;
   x.lda2 = ldb;
   x.B2 = A;

@@ -55,6 +55,9 @@ hipError_t launch_expand_sym(const void* src, int64_t lds, void* dst, int64_t ld
 // [256][256] blocks, the inverses of T's 256 x 256 diagonal blocks (identity past n).
 hipError_t launch_invert_diag(const void* src, int64_t lds, int n, int uplo, int unit, float* inv128, void* dst,
                               hipStream_t s);
+// dst [cols][ldd] = src [rows][lds] transposed (bf16); dst rows zero-padded to a multiple of
+// 8 columns (ldd >= round_up(rows, 8)).
+hipError_t launch_transpose(const void* src, int64_t lds, void* dst, int64_t ldd, int rows, int cols, hipStream_t s);
 hipError_t launch_copy2d(const void* src, int64_t lds, void* dst, int64_t ldd, int rows, int cols, hipStream_t s);
 
 }  // namespace dbgemm

@@ -403,6 +403,53 @@ __global__ __launch_bounds__(256) void copy2d_kernel(const uint16_t* __restrict_
   }
 }
 
+// dst[c][r] = src[r][c] for an rows x cols bf16 matrix: 64 x 64 blocks through LDS, rows
+// read and written as 16-byte vectors when `vec` (both 16-byte aligned, leading dimensions
+// multiples of 8), else element by element.  dst rows are padded with zeros up to a
+// multiple of 8 columns (dst columns rows .. round_up(rows, 8) - 1).
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ src, int64_t lds,
+                                                       uint16_t* __restrict__ dst, int64_t ldd, int rows, int cols,
+                                                       int vec) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[SB][SB + 8];  // tile[y][x] = src[r0 + y][c0 + x]
+  const int r0 = blockIdx.y * SB, c0 = blockIdx.x * SB;
+  for (int e = threadIdx.x; e < SB * SB / 8; e += 256) {
+    const int y = e / (SB / 8), x8 = (e % (SB / 8)) * 8;
+    const int r = r0 + y, c = c0 + x8;
+    uint16_t v[8];
+    if (vec && r < rows && c + 7 < cols) {
+      const uint4 w = *(const uint4*)(src + (int64_t)r * lds + c);
+      v[0] = (uint16_t)w.x; v[1] = (uint16_t)(w.x >> 16); v[2] = (uint16_t)w.y; v[3] = (uint16_t)(w.y >> 16);
+      v[4] = (uint16_t)w.z; v[5] = (uint16_t)(w.z >> 16); v[6] = (uint16_t)w.w; v[7] = (uint16_t)(w.w >> 16);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = r < rows && c + k < cols ? src[(int64_t)r * lds + c + k] : (uint16_t)0;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) tile[y][x8 + k] = v[k];
+  }
+  __syncthreads();
+  const int rows_pad = (rows + 7) / 8 * 8;
+  for (int e = threadIdx.x; e < SB * SB / 8; e += 256) {
+    const int x = e / (SB / 8), y8 = (e % (SB / 8)) * 8;  // dst row c0 + x, columns r0 + y8 ..
+    const int dr = c0 + x, dc = r0 + y8;
+    if (dr >= cols || dc >= rows_pad) continue;
+    uint16_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = tile[y8 + k][x];  // zero past `rows` (filled above)
+    if (vec) {
+      uint4 w;
+      w.x = v[0] | ((uint32_t)v[1] << 16);
+      w.y = v[2] | ((uint32_t)v[3] << 16);
+      w.z = v[4] | ((uint32_t)v[5] << 16);
+      w.w = v[6] | ((uint32_t)v[7] << 16);
+      *(uint4*)(dst + (int64_t)dr * ldd + dc) = w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) dst[(int64_t)dr * ldd + dc + k] = v[k];
+    }
+  }
+}
+
 unsigned blocks_for(int64_t work) {
   int64_t b = (work + 255) / 256;
   if (b < 1) b = 1;
@@ -448,6 +495,14 @@ hipError_t launch_invert_diag(const void* src, int64_t lds, int n, int uplo, int
   else
     hipLaunchKernelGGL(combine_inverse_kernel<true>, grid, dim3(256), 0, s, (const uint16_t*)src, lds, n, vec,
                        (const float*)inv128, (uint16_t*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const void* src, int64_t lds, void* dst, int64_t ldd, int rows, int cols, hipStream_t s) {
+  const int vec = (uintptr_t)src % 16 == 0 && (uintptr_t)dst % 16 == 0 && lds % 8 == 0 && ldd % 8 == 0;
+  dim3 grid((unsigned)((cols + SB - 1) / SB), (unsigned)((rows + SB - 1) / SB));
+  hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, s, (const uint16_t*)src, lds, (uint16_t*)dst, ldd, rows,
+                     cols, vec);
   return hipGetLastError();
 }
 

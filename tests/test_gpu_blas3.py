@@ -422,3 +422,36 @@ def test_blas3_strided_operands(gpu):
     opT = blas3.triangular(T, M2, UPPER, 0).T
     res = tolerance.trsm_check(X, X_ref, opT, tolerance.bf16_bits_to_f64(B2), LEFT, M2)
     assert res["ok"], res
+
+
+@pytest.mark.parametrize("N,K", [(1536, 768), (1100, 1024)])
+@pytest.mark.parametrize("uplo", [LOWER, UPPER])
+@pytest.mark.parametrize("c_dtype", ["bf16", "f32"])
+def test_syrk_transposed_copy(gpu, N, K, uplo, c_dtype):
+    """A stored [K][N] with N*K >= 2^20: A is first copied transposed into the workspace and
+    the triangle runs with both operands K-contiguous."""
+    A = gi.bf16_uniform((K, N), 11)
+    C0 = c_bits((N, N), c_dtype, 12)
+    C = to_device(C0, c_dtype)
+    gpu.syrk(to_device(A, "bf16"), C, uplo=uplo, trans=1, alpha=0.5, beta=1.0)
+    sync()
+    got = to_host(C)
+    R, S = blas3.syrk(uplo, 1, N, K, 0.5, A, 1.0, C0, C_FMT[c_dtype])
+    m = tri_mask(N, uplo)
+    check_c(got, c_dtype, R, S, K, m)
+    assert np.array_equal(got[~m], C0[~m])
+
+
+@pytest.mark.parametrize("uplo", [LOWER, UPPER])
+def test_syr2k_transposed_copy(gpu, uplo):
+    N, K = 1024, 1024
+    A, B = gi.bf16_uniform((K, N), 13), gi.bf16_uniform((K, N), 14)
+    C0 = c_bits((N, N), "f32", 15)
+    C = to_device(C0, "f32")
+    gpu.syr2k(to_device(A, "bf16"), to_device(B, "bf16"), C, uplo=uplo, trans=1, alpha=1.0, beta=-1.0)
+    sync()
+    got = to_host(C)
+    R, S = blas3.syr2k(uplo, 1, N, K, 1.0, A, B, -1.0, C0, oracle.C_F32)
+    m = tri_mask(N, uplo)
+    check_c(got, "f32", R, S, 2 * K, m)
+    assert np.array_equal(got[~m], C0[~m])
