@@ -323,25 +323,27 @@ gemm_status_t gemm_trmm(gemm_handle_t h, int side, int uplo, int transA, int dia
     GemmExtras x;
     x.band_off = (int)p0;
     // The panel of op(T) this part of C needs -- rows [p0, p0+w) of op(T) (left) or its
-    // columns (right) -- expanded from T's rows or columns as the transpose dictates.
-    const bool panel_is_rows = (side == GEMM_SIDE_LEFT) == (transA == 0);
+    // columns (right) -- expanded as op(T) itself (transposed from T when transA is set), so
+    // that the product is always NN (the fastest layout of the kernels).
     int64_t ldw;
-    if (panel_is_rows) {  // T rows [p0, p0+w) x all n columns
+    if (side == GEMM_SIDE_LEFT) {  // op(T) rows [p0, p0+w) x all n columns
       ldw = pad8(n);
-      err = launch_expand_tri(A, lda, hv.ws, ldw, (int)p0, 0, (int)w, (int)n, (int)ldw, uplo, diag, hv.stream);
-    } else {  // T all n rows x columns [p0, p0+w)
+      err = transA ? launch_expand_tri_trans(A, lda, hv.ws, ldw, (int)p0, 0, (int)w, (int)n, (int)ldw, (int)n, uplo,
+                                             diag, hv.stream)
+                   : launch_expand_tri(A, lda, hv.ws, ldw, (int)p0, 0, (int)w, (int)n, (int)ldw, uplo, diag, hv.stream);
+    } else {  // op(T) all n rows x columns [p0, p0+w)
       ldw = pad8(w);
-      err = launch_expand_tri(A, lda, hv.ws, ldw, 0, (int)p0, (int)n, (int)w, (int)ldw, uplo, diag, hv.stream);
+      err = transA ? launch_expand_tri_trans(A, lda, hv.ws, ldw, 0, (int)p0, (int)n, (int)w, (int)ldw, (int)n, uplo,
+                                             diag, hv.stream)
+                   : launch_expand_tri(A, lda, hv.ws, ldw, 0, (int)p0, (int)n, (int)w, (int)ldw, uplo, diag, hv.stream);
     }
     if (err != hipSuccess) break;
     if (side == GEMM_SIDE_LEFT) {  // C rows = alpha * op(T)[p0.., :] B
       x.kband = opT_lower ? KBAND_A_LOWER : KBAND_A_UPPER;
-      err = gemm_enqueue(hv, transA, 0, w, N, M, alpha, hv.ws, ldw, B, ldb, 0.f, off(C, p0, 0, ldc, es), ldc, dtype,
-                         x);
+      err = gemm_enqueue(hv, 0, 0, w, N, M, alpha, hv.ws, ldw, B, ldb, 0.f, off(C, p0, 0, ldc, es), ldc, dtype, x);
     } else {  // C columns = alpha * B op(T)[:, p0..]
       x.kband = opT_lower ? KBAND_B_LOWER : KBAND_B_UPPER;
-      err = gemm_enqueue(hv, 0, transA, M, w, N, alpha, B, ldb, hv.ws, ldw, 0.f, off(C, 0, p0, ldc, es), ldc, dtype,
-                         x);
+      err = gemm_enqueue(hv, 0, 0, M, w, N, alpha, B, ldb, hv.ws, ldw, 0.f, off(C, 0, p0, ldc, es), ldc, dtype, x);
     }
   }
   return status_of(err);

@@ -49,6 +49,10 @@ bool gemm_fast_ok(int transA, int transB, int64_t M, int64_t N, int64_t K, const
 // Operand preparation kernels (blas3_kernels.hip); bf16 throughout.
 hipError_t launch_expand_tri(const void* src, int64_t lds, void* dst, int64_t ldd, int r0, int c0, int rows, int cols,
                              int cols_pad, int uplo, int unit, hipStream_t s);
+// dst[r][c] = T^T[r0 + r][c0 + c] for r < rows, c < cols (zeros up to cols_pad): the
+// transposed triangular operand, expanded.
+hipError_t launch_expand_tri_trans(const void* src, int64_t lds, void* dst, int64_t ldd, int r0, int c0, int rows,
+                                   int cols, int cols_pad, int n, int uplo, int unit, hipStream_t s);
 hipError_t launch_expand_sym(const void* src, int64_t lds, void* dst, int64_t ldd, int r0, int c0, int rows, int cols,
                              int cols_pad, int n, int uplo, hipStream_t s);
 // inv128: 2 * ceil(n / 256) fp32 [128][128] blocks (scratch); dst: ceil(n / 256) bf16

@@ -98,6 +98,64 @@ __global__ __launch_bounds__(256) void expand_tri_kernel(const uint16_t* __restr
   *(uint4*)(dst + (int64_t)r * ldd + c8) = w;
 }
 
+constexpr int SB = 64;  // block edge of the kernels that go through an LDS block
+
+// dst[r][c] = T^T[r0 + r][c0 + c] = T[c0 + c][r0 + r] of the n x n triangular T (stored
+// triangle, zeros elsewhere, ones on a unit diagonal): the transposed operand written out, so
+// that the product that follows reads it in the layout of an untransposed one.  Workgroup
+// (bx, by) writes the 64 x 64 block at rows 64*by, columns 64*bx: the source block (rows
+// c0 + 64*bx .., columns r0 + 64*by ..) is read row-wise into LDS (16-byte loads when `vec`)
+// and written transposed, 8 columns per 16-byte store.  Columns past `cols` up to the padded
+// width are zeros.
+__global__ __launch_bounds__(256) void expand_tri_trans_kernel(const uint16_t* __restrict__ src, int64_t lds,
+                                                               uint16_t* __restrict__ dst, int64_t ldd, int r0,
+                                                               int c0, int rows, int cols, int cols_pad, int n,
+                                                               int uplo, int unit, int vec) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[SB][SB + 8];  // tile[y][x] = src[sr0 + y][sc0 + x]
+  const int br = blockIdx.y * SB, bc = blockIdx.x * SB;
+  const int sr0 = c0 + bc, sc0 = r0 + br;  // the source block
+  for (int e = threadIdx.x; e < SB * SB / 8; e += 256) {
+    const int y = e / (SB / 8), x8 = (e % (SB / 8)) * 8;
+    const int si = sr0 + y, sj = sc0 + x8;
+    uint16_t v[8];
+    if (vec && si < n && sj + 7 < n) {
+      const uint4 w = *(const uint4*)(src + (int64_t)si * lds + sj);
+      v[0] = (uint16_t)w.x; v[1] = (uint16_t)(w.x >> 16); v[2] = (uint16_t)w.y; v[3] = (uint16_t)(w.y >> 16);
+      v[4] = (uint16_t)w.z; v[5] = (uint16_t)(w.z >> 16); v[6] = (uint16_t)w.w; v[7] = (uint16_t)(w.w >> 16);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = si < n && sj + k < n ? src[(int64_t)si * lds + sj + k] : (uint16_t)0;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) tile[y][x8 + k] = v[k];
+  }
+  __syncthreads();
+  const uint16_t one = f2bf(1.f);
+  for (int e = threadIdx.x; e < SB * SB / 8; e += 256) {
+    const int y = e / (SB / 8), x8 = (e % (SB / 8)) * 8;
+    const int r = br + y, c = bc + x8;
+    if (r >= rows || c >= cols_pad) continue;
+    const int i = r0 + r;  // row of T^T = column of T
+    uint16_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int j = c0 + c + k;  // column of T^T = row of T: element T[j][i]
+      uint16_t x = 0;
+      if (c + k < cols && i < n && j < n) {
+        if (i == j && unit) x = one;
+        else if (referenced(j, i, uplo)) x = tile[x8 + k][y];
+      }
+      v[k] = x;
+    }
+    uint4 w;
+    w.x = v[0] | ((uint32_t)v[1] << 16);
+    w.y = v[2] | ((uint32_t)v[3] << 16);
+    w.z = v[4] | ((uint32_t)v[5] << 16);
+    w.w = v[6] | ((uint32_t)v[7] << 16);
+    *(uint4*)(dst + (int64_t)r * ldd + c) = w;
+  }
+}
+
 // dst[r][c] = S[r0 + r][c0 + c] of the symmetric matrix S whose uplo triangle is stored
 // in src.  Workgroup (bx, by) writes the 64 x 64 output block at rows 64*by, columns
 // 64*bx, 8 columns (16 bytes) per thread and store; its elements come from src directly
@@ -105,7 +163,6 @@ __global__ __launch_bounds__(256) void expand_tri_kernel(const uint16_t* __restr
 // into LDS and read back transposed.  With `vec` (src 16-byte aligned, lds, r0 and c0
 // multiples of 8) groups of 8 stored elements are read with one 16-byte load.  Columns
 // past `cols` up to the padded width are zeros.
-constexpr int SB = 64;
 __global__ __launch_bounds__(256) void expand_sym_kernel(const uint16_t* __restrict__ src, int64_t lds,
                                                          uint16_t* __restrict__ dst, int64_t ldd, int r0, int c0,
                                                          int rows, int cols, int cols_pad, int n, int uplo, int vec) {
@@ -463,6 +520,15 @@ hipError_t launch_expand_tri(const void* src, int64_t lds, void* dst, int64_t ld
   const int vec = ((uintptr_t)src % 16 == 0) && lds % 8 == 0 && c0 % 8 == 0;
   hipLaunchKernelGGL(expand_tri_kernel, dim3(blocks_for((int64_t)rows * (cols_pad / 8))), dim3(256), 0, s,
                      (const uint16_t*)src, lds, (uint16_t*)dst, ldd, r0, c0, rows, cols, cols_pad, uplo, unit, vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_expand_tri_trans(const void* src, int64_t lds, void* dst, int64_t ldd, int r0, int c0, int rows,
+                                   int cols, int cols_pad, int n, int uplo, int unit, hipStream_t s) {
+  const int vec = ((uintptr_t)src % 16 == 0) && lds % 8 == 0 && r0 % 8 == 0;
+  dim3 grid((unsigned)((cols_pad + SB - 1) / SB), (unsigned)((rows + SB - 1) / SB));
+  hipLaunchKernelGGL(expand_tri_trans_kernel, grid, dim3(256), 0, s, (const uint16_t*)src, lds, (uint16_t*)dst, ldd,
+                     r0, c0, rows, cols, cols_pad, n, uplo, unit, vec);
   return hipGetLastError();
 }
 
