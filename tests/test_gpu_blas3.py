@@ -455,3 +455,60 @@ def test_syr2k_transposed_copy(gpu, uplo):
     m = tri_mask(N, uplo)
     check_c(got, "f32", R, S, 2 * K, m)
     assert np.array_equal(got[~m], C0[~m])
+
+
+# ------------------------------------------------------------------ degenerate sizes
+
+@pytest.mark.parametrize("M,N", [(1, 1), (1, 7), (9, 1), (3, 2)])
+def test_blas3_tiny(gpu, M, N):
+    """One row, one column, 1 x 1: every operation of the family against the oracle."""
+    import torch
+    A = gi.bf16_uniform((M, M), 1)
+    Bm = gi.bf16_uniform((M, N), 2)
+    C = torch.zeros((M, M), dtype=torch.float32, device="cuda:0")
+    gpu.syrk(to_device(gi.bf16_uniform((M, N), 3), "bf16"), C, uplo=LOWER, trans=0)
+    sync()
+    R, S = blas3.syrk(LOWER, 0, M, N, 1.0, gi.bf16_uniform((M, N), 3), 0.0, None, oracle.C_F32)
+    check_c(to_host(C), "f32", R, S, N, tri_mask(M, LOWER))
+    Sm = gi.bf16_symmetric_stored(M, UPPER, 4)
+    C2 = torch.zeros((M, N), dtype=torch.float32, device="cuda:0")
+    gpu.symm(to_device(Sm, "bf16"), to_device(Bm, "bf16"), C2, side=LEFT, uplo=UPPER)
+    sync()
+    R, S = blas3.symm(LEFT, UPPER, M, N, 1.0, Sm, Bm, 0.0, None, oracle.C_F32)
+    check_c(to_host(C2), "f32", R, S, M)
+    T = gi.bf16_triangular(M, LOWER, 5)
+    gpu.trmm(to_device(T, "bf16"), to_device(Bm, "bf16"), C2, side=LEFT, uplo=LOWER, transA=1)
+    sync()
+    R, S = blas3.trmm(LEFT, LOWER, 1, 0, M, N, 1.0, T, Bm)
+    check_c(to_host(C2), "f32", R, S, M)
+    Bd = to_device(Bm, "bf16")
+    gpu.trsm(to_device(T, "bf16"), Bd, side=LEFT, uplo=LOWER, transA=0, alpha=2.0)
+    sync()
+    X = tolerance.bf16_bits_to_f64(to_host(Bd))
+    X_ref = blas3.trsm(LEFT, LOWER, 0, 0, M, N, 2.0, T, Bm)
+    res = tolerance.trsm_check(X, X_ref, blas3.triangular(T, M, LOWER, 0), 2.0 * tolerance.bf16_bits_to_f64(Bm),
+                               LEFT, M)
+    assert res["ok"], res
+
+
+def test_blas3_empty_calls_write_nothing(gpu):
+    """M, N or K = 0: success, nothing launched or written (C keeps its NaN); K = 0 SYRK
+    scales the triangle only (covered above); invalid flags and dtypes are refused."""
+    import torch
+    C = torch.full((8, 8), float("nan"), dtype=torch.float32, device="cuda:0")
+    p = C.data_ptr()
+    assert gpu.syrk_raw(LOWER, 0, 0, 4, 1.0, p, 4, 0.0, p, 8, 0) == 0
+    assert gpu.syr2k_raw(UPPER, 1, 0, 4, 1.0, p, 1, p, 1, 0.0, p, 8, 0) == 0
+    assert gpu.symm_raw(LEFT, LOWER, 0, 8, 1.0, p, 1, p, 8, 0.0, p, 8, 0) == 0
+    assert gpu.trmm_raw(RIGHT, UPPER, 0, 0, 8, 0, 1.0, p, 1, p, 1, p, 8, 0) == 0
+    assert gpu.trsm_raw(LEFT, LOWER, 0, 0, 0, 8, 1.0, p, 1, p, 8) == 0
+    sync()
+    assert torch.isnan(C).all().item()
+    # bad flags / dtypes: INVALID_VALUE, nothing written
+    assert gpu.syrk_raw(2, 0, 8, 8, 1.0, p, 8, 0.0, p, 8, 0) == 1
+    assert gpu.symm_raw(LEFT, LOWER, 8, 8, 1.0, p, 8, p, 8, 0.0, p, 8, 2) == 1   # E4M3 not in the family
+    assert gpu.trsm_raw(LEFT, LOWER, 0, 0, 8, 8, 1.0, p, 8, p, 8, 0) == 1       # TRSM is bf16 in and out
+    assert gpu.trmm_raw(LEFT, LOWER, 0, 3, 8, 8, 1.0, p, 8, p, 8, p, 8, 0) == 1  # diag flag
+    assert gpu.trsm_raw(LEFT, LOWER, 0, 0, 8, 8, float("inf"), p, 8, p, 8) == 2  # non-finite alpha
+    sync()
+    assert torch.isnan(C).all().item()
