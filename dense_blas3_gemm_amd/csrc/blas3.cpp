@@ -4,7 +4,8 @@
 // runs its local compute on a GEMM).
 //
 //   SYRK   one GEMM (A and A, the second read transposed) over a triangle of tiles;
-//   SYR2K  one GEMM whose K loop runs over both products, over a triangle of tiles;
+//   SYR2K  one GEMM over a triangle of tiles on the operands packed as [A | B | A] (the second
+//          factor is the same buffer shifted by one part: both products in one sum);
 //   SYMM   the symmetric matrix expanded into the workspace (row panels), then GEMMs;
 //   TRMM   the triangle expanded with zeros into the workspace (panels), then GEMMs whose
 //          tiles skip the K tiles that meet only zeros;
@@ -236,21 +237,26 @@ gemm_status_t gemm_syr2k(gemm_handle_t h, int uplo, int trans, int64_t N, int64_
   if (!g.ok) return GEMM_STATUS_INTERNAL;
   GemmExtras x;
   x.tri = uplo == GEMM_LOWER ? TRI_LOWER : TRI_UPPER;
-  x.dual = 1;  // op(A) op(B)^T, then op(B) op(A)^T
-  if (trans && K > 0 && alpha != 0.f && transpose_pays(hv, N, K, 2)) {
-    // A and B [K][N] copied once as A^T, B^T [N][K] into the workspace (see gemm_syrk)
-    const int64_t ldt = pad8(K);
-    void* At = hv.ws;
-    void* Bt = (char*)hv.ws + (size_t)N * ldt * 2;
-    hipError_t e = launch_transpose(A, lda, At, ldt, (int)K, (int)N, hv.stream);
-    if (e == hipSuccess) e = launch_transpose(B, ldb, Bt, ldt, (int)K, (int)N, hv.stream);
-    x.A2 = Bt;
-    x.lda2 = ldt;
-    x.B2 = At;
-    x.ldb2 = ldt;
-    if (e == hipSuccess) e = gemm_enqueue(hv, 0, 1, N, N, K, alpha, At, ldt, Bt, ldt, beta, C, ldc, dtype, x);
-    return status_of(e);
+  if (K > 0 && alpha != 0.f && N * K >= ((int64_t)1 << 16)) {
+    // W = [op(A) | op(B) | op(A)] (N x 3Kp, each part Kp = K rounded up to 8, zero-padded) in the
+    // workspace: W[:, 0:2Kp] W[:, Kp:3Kp]^T = op(A) op(B)^T + op(B) op(A)^T, one K-contiguous
+    // product over 2Kp with a single fp32 sum and one rounding of C
+    const int64_t Kp = pad8(K), ldw = 3 * Kp;
+    if (hv.ws && (size_t)N * ldw * 2 <= hv.ws_bytes) {
+      uint16_t* W = (uint16_t*)hv.ws;
+      auto pack = [&](const void* X, int64_t ldx_, int64_t col) {
+        return trans ? launch_transpose(X, ldx_, W + col, ldw, (int)K, (int)N, hv.stream)
+                     : launch_copy2d(X, ldx_, W + col, ldw, (int)N, (int)K, hv.stream, (int)Kp);
+      };
+      hipError_t e = pack(A, lda, 0);
+      if (e == hipSuccess) e = pack(B, ldb, Kp);
+      if (e == hipSuccess) e = pack(A, lda, 2 * Kp);
+      if (e == hipSuccess) e = gemm_enqueue(hv, 0, 1, N, N, 2 * Kp, alpha, W, ldw, W + Kp, ldw, beta, C, ldc, dtype, x);
+      return status_of(e);
+    }
   }
+  // small, or no room to pack: both products in one K loop of the generic kernel
+  x.dual = 1;
   x.A2 = B;
   x.lda2 = ldb;
   x.B2 = A;

@@ -62,6 +62,8 @@ hipError_t launch_invert_diag(const void* src, int64_t lds, int n, int uplo, int
 // dst [cols][ldd] = src [rows][lds] transposed (bf16); dst rows zero-padded to a multiple of
 // 8 columns (ldd >= round_up(rows, 8)).
 hipError_t launch_transpose(const void* src, int64_t lds, void* dst, int64_t ldd, int rows, int cols, hipStream_t s);
-hipError_t launch_copy2d(const void* src, int64_t lds, void* dst, int64_t ldd, int rows, int cols, hipStream_t s);
+// dst [rows][ldd] = src [rows][lds] for cols columns, zeros in columns cols .. cols_pad - 1.
+hipError_t launch_copy2d(const void* src, int64_t lds, void* dst, int64_t ldd, int rows, int cols, hipStream_t s,
+                         int cols_pad = 0);
 
 }  // namespace dbgemm

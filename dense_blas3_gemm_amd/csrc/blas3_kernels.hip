@@ -439,11 +439,12 @@ __global__ __launch_bounds__(256) void combine_inverse_kernel(const uint16_t* __
 }
 
 // dst[r][c] = src[r][c] for an rows x cols bf16 block (both row-major with their own
-// leading dimensions); with `vec` (both 16-byte aligned, leading dimensions and cols
-// multiples of 8) 8 elements per 16-byte load and store.
+// leading dimensions), and zeros in dst columns cols .. cols_pad - 1; with `vec` (both
+// 16-byte aligned, leading dimensions and cols multiples of 8, no padding) 8 elements per
+// 16-byte load and store.
 __global__ __launch_bounds__(256) void copy2d_kernel(const uint16_t* __restrict__ src, int64_t lds,
                                                      uint16_t* __restrict__ dst, int64_t ldd, int rows, int cols,
-                                                     int vec) {
+                                                     int cols_pad, int vec) {
   if (vec) {
     const int g = cols / 8;
     const int64_t total = (int64_t)rows * g;
@@ -453,10 +454,10 @@ __global__ __launch_bounds__(256) void copy2d_kernel(const uint16_t* __restrict_
     }
     return;
   }
-  const int64_t total = (int64_t)rows * cols;
+  const int64_t total = (int64_t)rows * cols_pad;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    const int r = (int)(e / cols), c = (int)(e % cols);
-    dst[(int64_t)r * ldd + c] = src[(int64_t)r * lds + c];
+    const int r = (int)(e / cols_pad), c = (int)(e % cols_pad);
+    dst[(int64_t)r * ldd + c] = c < cols ? src[(int64_t)r * lds + c] : (uint16_t)0;
   }
 }
 
@@ -572,13 +573,16 @@ hipError_t launch_transpose(const void* src, int64_t lds, void* dst, int64_t ldd
   return hipGetLastError();
 }
 
-hipError_t launch_copy2d(const void* src, int64_t lds, void* dst, int64_t ldd, int rows, int cols, hipStream_t s) {
-  int64_t b = ((int64_t)rows * cols + 255) / 256;
+hipError_t launch_copy2d(const void* src, int64_t lds, void* dst, int64_t ldd, int rows, int cols, hipStream_t s,
+                         int cols_pad) {
+  if (cols_pad < cols) cols_pad = cols;
+  int64_t b = ((int64_t)rows * cols_pad + 255) / 256;
   if (b > 8192) b = 8192;
   if (b < 1) b = 1;
-  const int vec = (uintptr_t)src % 16 == 0 && (uintptr_t)dst % 16 == 0 && lds % 8 == 0 && ldd % 8 == 0 && cols % 8 == 0;
+  const int vec = (uintptr_t)src % 16 == 0 && (uintptr_t)dst % 16 == 0 && lds % 8 == 0 && ldd % 8 == 0 &&
+                  cols % 8 == 0 && cols_pad == cols;
   hipLaunchKernelGGL(copy2d_kernel, dim3((unsigned)b), dim3(256), 0, s, (const uint16_t*)src, lds, (uint16_t*)dst, ldd,
-                     rows, cols, vec);
+                     rows, cols, cols_pad, vec);
   return hipGetLastError();
 }
 

@@ -55,9 +55,9 @@ struct GemmArgs {
   // in the triangular operand, of this call's first row or column of C.
   int kband;
   int band_off;
-  // Two products in one sum (the rank-2K update): with dual set, the K loop runs over
-  // op(A)*op(B) and then over op(A2)*op(B2), same M, N, K and transposes; A2 has leading
-  // dimension lda2, B2 ldb2 (the direct-to-LDS kernels need lda2 == lda, ldb2 == ldb).
+  // Two products in one sum (the rank-2K update when its operands cannot be packed): with
+  // dual set, the K loop runs over op(A)*op(B) and then over op(A2)*op(B2), same M, N, K and
+  // transposes; A2 has leading dimension lda2, B2 ldb2.  Generic kernel only.
   int dual;
   const void* A2;
   const void* B2;

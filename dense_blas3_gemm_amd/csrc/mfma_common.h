@@ -365,7 +365,7 @@ __device__ inline void put_chunk(lds_char* sbase, uint32_t off, const i32x4& v, 
 // to C's type (bf16 and E4M3 to nearest even, E4M3 saturating at +-448).  store_tile
 // applies it to every group.
 template <class C>
-__device__ __forceinline__ void store_group(const GemmArgs& a, f32x4 v, int p, int row0, int col0, int lane) {
+__device__ __forceinline__ void store_group_tri(const GemmArgs& a, f32x4 v, int p, int row0, int col0, int lane) {
   const int q = p % (C::ACC / 4), j = (p / (C::ACC / 4)) % C::FN, i = p / (C::ACC / 4) / C::FN;
   const int m = row0 + i * C::MT + lane % C::MT;
   const int n = col0 + j * C::MT + (C::MT == 32 ? 8 * q + 4 * (lane / 32) : 4 * (lane / 16));
@@ -414,6 +414,67 @@ __device__ __forceinline__ void store_group(const GemmArgs& a, f32x4 v, int p, i
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (e < e0 || e >= e1) continue;
+      if (a.c_kind == C_F32) {
+        float* cp = (float*)a.C + base + e;
+        *cp = w[e] + (beta != 0.f ? beta * *cp : 0.f);
+      } else if (a.c_kind == C_E4M3) {
+        uint8_t* cp = (uint8_t*)a.C + base + e;
+        *cp = (uint8_t)e4m3x4_from_f32(w[e] + (beta != 0.f ? beta * __builtin_amdgcn_cvt_f32_fp8(*cp, 0) : 0.f),
+                                       0.f, 0.f, 0.f);
+      } else {
+        uint16_t* cp = (uint16_t*)a.C + base + e;
+        *cp = f32_to_bf16_bits(w[e] + (beta != 0.f ? beta * bf16_bits_to_f32(*cp) : 0.f));
+      }
+    }
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void store_group(const GemmArgs& a, f32x4 v, int p, int row0, int col0, int lane) {
+  // a triangle of C takes its own path, so that the common one keeps its register budget
+  if (a.tri != TRI_NONE) return store_group_tri<C>(a, v, p, row0, col0, lane);
+  const int q = p % (C::ACC / 4), j = (p / (C::ACC / 4)) % C::FN, i = p / (C::ACC / 4) / C::FN;
+  const int m = row0 + i * C::MT + lane % C::MT;
+  const int n = col0 + j * C::MT + (C::MT == 32 ? 8 * q + 4 * (lane / 32) : 4 * (lane / 16));
+  if (m >= a.M) return;
+  const float alpha = a.alpha, beta = a.beta;
+  float w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = alpha * v[e];
+  const int64_t base = (int64_t)m * a.ldc + n;
+  if (n + 3 < a.N) {
+    if (a.c_kind == C_F32) {
+      float* cp = (float*)a.C + base;
+      if (beta != 0.f) {
+        f32x4 old = *(const f32x4*)cp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] += beta * old[e];
+      }
+      *(f32x4*)cp = (f32x4){w[0], w[1], w[2], w[3]};
+    } else if (a.c_kind == C_E4M3) {  // four codes in one 32-bit word (n is a multiple of 4)
+      uint32_t* cp = (uint32_t*)((uint8_t*)a.C + base);
+      if (beta != 0.f) {
+        const uint32_t old = *cp;
+        w[0] += beta * __builtin_amdgcn_cvt_f32_fp8((int)old, 0);
+        w[1] += beta * __builtin_amdgcn_cvt_f32_fp8((int)old, 1);
+        w[2] += beta * __builtin_amdgcn_cvt_f32_fp8((int)old, 2);
+        w[3] += beta * __builtin_amdgcn_cvt_f32_fp8((int)old, 3);
+      }
+      *cp = e4m3x4_from_f32(w[0], w[1], w[2], w[3]);
+    } else {
+      uint16_t* cp = (uint16_t*)a.C + base;
+      if (beta != 0.f) {
+        u16x4 old = *(const u16x4*)cp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] += beta * bf16_bits_to_f32(old[e]);
+      }
+      *(u16x4*)cp = (u16x4){f32_to_bf16_bits(w[0]), f32_to_bf16_bits(w[1]), f32_to_bf16_bits(w[2]),
+                            f32_to_bf16_bits(w[3])};
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (n + e >= a.N) break;
       if (a.c_kind == C_F32) {
         float* cp = (float*)a.C + base + e;
         *cp = w[e] + (beta != 0.f ? beta * *cp : 0.f);

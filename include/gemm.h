@@ -26,8 +26,8 @@
  * E4M3 runs with unit scale: any scaling is the caller's (alpha may carry it).
  *
  * Memory and ownership.  A, B and C are device pointers owned by the caller.  The
- * handle owns its host-side state and one 64 MiB device workspace for split-K
- * (allocated by gemm_create, freed by gemm_destroy).  gemm_run never allocates,
+ * handle owns its host-side state and one 256 MiB device workspace for split-K and the
+ * BLAS3 calls (allocated by gemm_create, freed by gemm_destroy).  gemm_run never allocates,
  * never synchronises and returns once the kernel is enqueued on the handle's stream;
  * faults during execution surface at the caller's next synchronisation.  A handle
  * must be used from one host thread at a time, and its calls must not overlap on
@@ -243,7 +243,9 @@ gemm_status_t gemm_syrk(gemm_handle_t h, int uplo, int trans, int64_t N, int64_t
 /* Symmetric rank-2K update of one triangle:
  *   C <- alpha * (op(A) op(B)^T + op(B) op(A)^T) + beta * C   on the uplo triangle,
  * op(A), op(B) N x K stored like syrk's A.  Both products accumulate in one fp32 sum
- * (one rounding of C); the MFMA kernels need lda == ldb. */
+ * (one rounding of C): from N*K = 2^16 the operands are packed into the workspace as
+ * [op(A) | op(B) | op(A)] (N x 3K, when it fits) and one K-contiguous product over 2K runs on
+ * the MFMA kernels; smaller calls run both products in one K loop of the generic kernel. */
 gemm_status_t gemm_syr2k(gemm_handle_t h, int uplo, int trans, int64_t N, int64_t K, float alpha,
                          const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
                          int64_t ldc, int dtype);
