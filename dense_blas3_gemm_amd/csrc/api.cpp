@@ -330,7 +330,10 @@ static hipError_t enqueue_impl(int cu_count, hipStream_t stream, void* ws, int64
     pr.blas3 = true;
     pr.square_tiles = x.tri != TRI_NONE;
     pr.kband = x.kband != KBAND_NONE;
-    if (x.dual) pr.fast_ok = false;  // two products in one sum: the generic kernel
+    if (x.dual) {  // two products in one sum: the bf16 A [M][K], B [N][K] kernels, equal strides
+      const Problem p2 = make_problem(transA, transB, M, N, K, x.A2, x.lda2, x.B2, x.ldb2, C, ldc, dtype);
+      pr.fast_ok = pr.fast_ok && p2.fast_ok && x.lda2 == lda && x.ldb2 == ldb && transA == 0 && transB == 1;
+    }
   }
   int idx, sp = 1;
   if (forced >= 0) {

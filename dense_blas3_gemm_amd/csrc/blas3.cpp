@@ -4,8 +4,9 @@
 // runs its local compute on a GEMM).
 //
 //   SYRK   one GEMM (A and A, the second read transposed) over a triangle of tiles;
-//   SYR2K  one GEMM over a triangle of tiles on the operands packed as [A | B | A] (the second
-//          factor is the same buffer shifted by one part: both products in one sum);
+//   SYR2K  one GEMM over a triangle of tiles whose K loop runs over both products (the second
+//          half of the K tiles reads the other operand pair), on copies of the operands
+//          when they are not both K-contiguous with one stride;
 //   SYMM   the symmetric matrix expanded into the workspace (row panels), then GEMMs;
 //   TRMM   the triangle expanded with zeros into the workspace (panels), then GEMMs whose
 //          tiles skip the K tiles that meet only zeros;
@@ -237,26 +238,37 @@ gemm_status_t gemm_syr2k(gemm_handle_t h, int uplo, int trans, int64_t N, int64_
   if (!g.ok) return GEMM_STATUS_INTERNAL;
   GemmExtras x;
   x.tri = uplo == GEMM_LOWER ? TRI_LOWER : TRI_UPPER;
-  if (K > 0 && alpha != 0.f && N * K >= ((int64_t)1 << 16)) {
-    // W = [op(A) | op(B) | op(A)] (N x 3Kp, each part Kp = K rounded up to 8, zero-padded) in the
-    // workspace: W[:, 0:2Kp] W[:, Kp:3Kp]^T = op(A) op(B)^T + op(B) op(A)^T, one K-contiguous
-    // product over 2Kp with a single fp32 sum and one rounding of C
-    const int64_t Kp = pad8(K), ldw = 3 * Kp;
-    if (hv.ws && (size_t)N * ldw * 2 <= hv.ws_bytes) {
-      uint16_t* W = (uint16_t*)hv.ws;
-      auto pack = [&](const void* X, int64_t ldx_, int64_t col) {
-        return trans ? launch_transpose(X, ldx_, W + col, ldw, (int)K, (int)N, hv.stream)
-                     : launch_copy2d(X, ldx_, W + col, ldw, (int)N, (int)K, hv.stream, (int)Kp);
+  x.dual = 1;  // op(A) op(B)^T, then op(B) op(A)^T, in one K loop and one fp32 sum
+  if (K > 0 && alpha != 0.f) {
+    // A [N][K], B [N][K] with one stride: straight onto the direct-to-LDS kernels
+    if (!trans && lda == ldb && gemm_fast_ok(0, 1, N, N, K, A, lda, B, ldb, C, ldc, dtype)) {
+      x.A2 = B;
+      x.lda2 = ldb;
+      x.B2 = A;
+      x.ldb2 = lda;
+      return status_of(gemm_enqueue(hv, 0, 1, N, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, x));
+    }
+    // Otherwise, from 2^16 elements and when both fit the workspace: op(A) and op(B) copied
+    // K-contiguous with a common stride (transposed when trans is set), then the same product.
+    const int64_t Kp = pad8(K);
+    if (N * K >= ((int64_t)1 << 16) && hv.ws && (size_t)2 * N * Kp * 2 <= hv.ws_bytes) {
+      uint16_t* At = (uint16_t*)hv.ws;
+      uint16_t* Bt = At + N * Kp;
+      auto pack = [&](const void* X, int64_t ldx_, uint16_t* dst) {
+        return trans ? launch_transpose(X, ldx_, dst, Kp, (int)K, (int)N, hv.stream)
+                     : launch_copy2d(X, ldx_, dst, Kp, (int)N, (int)K, hv.stream, (int)Kp);
       };
-      hipError_t e = pack(A, lda, 0);
-      if (e == hipSuccess) e = pack(B, ldb, Kp);
-      if (e == hipSuccess) e = pack(A, lda, 2 * Kp);
-      if (e == hipSuccess) e = gemm_enqueue(hv, 0, 1, N, N, 2 * Kp, alpha, W, ldw, W + Kp, ldw, beta, C, ldc, dtype, x);
+      hipError_t e = pack(A, lda, At);
+      if (e == hipSuccess) e = pack(B, ldb, Bt);
+      x.A2 = Bt;
+      x.lda2 = Kp;
+      x.B2 = At;
+      x.ldb2 = Kp;
+      if (e == hipSuccess) e = gemm_enqueue(hv, 0, 1, N, N, K, alpha, At, Kp, Bt, Kp, beta, C, ldc, dtype, x);
       return status_of(e);
     }
   }
-  // small, or no room to pack: both products in one K loop of the generic kernel
-  x.dual = 1;
+  // small, or no room to copy: both products in one K loop of the generic kernel
   x.A2 = B;
   x.lda2 = ldb;
   x.B2 = A;

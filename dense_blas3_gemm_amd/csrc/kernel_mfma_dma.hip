@@ -105,6 +105,13 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(GemmArgs a) {
   const uint32_t b_rows = C::B_KC ? a.N : a.K;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, (uint32_t)(a_rows * a.lda * C::ES));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.B, (uint32_t)(b_rows * a.ldb * C::ES));
+  // Two products in one sum (the rank-2K update), in the bf16 A [M][K], B [N][K]
+  // instantiations only: their register budget has room for the second pair of buffer
+  // descriptors, which pushed the transposed-A 256 x 256 tile (and the scaled-E4M3 one) into
+  // scratch.  Same strides as (A, B).
+  constexpr bool kDual = !C::TA && C::TB && C::IN == IN_BF16;
+  const __amdgpu_buffer_rsrc_t ra2 = kDual ? make_rsrc(a.dual ? a.A2 : a.A, (uint32_t)(a_rows * a.lda * C::ES)) : ra;
+  const __amdgpu_buffer_rsrc_t rb2 = kDual ? make_rsrc(a.dual ? a.B2 : a.B, (uint32_t)(b_rows * a.ldb * C::ES)) : rb;
 
   // ---- per-lane sources of the load instructions (fixed over the K loop).
   // Instruction i of this wave fills LDS block blk = wave*IPW + i of the tile; this
@@ -165,13 +172,14 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(GemmArgs a) {
   // memory.
   const uint32_t a_blk = (uint32_t)(wave * D::A_IPW) * 1024u;
   const uint32_t b_blk = C::A_BYTES + (uint32_t)(wave * D::B_IPW) * 1024u;
-  // K tiles of this workgroup: [kbeg, kbeg + nk) of the nk_all tiles of K.  A K band keeps
-  // only the tiles that meet the band (the rest multiply zeros).  (Two products in one sum,
-  // GemmArgs::dual, are not taken here: the host routes them to the generic kernel.)
-  const int nk_all = (a.K + C::BK - 1) / C::BK;
+  // K tiles of this workgroup: [kbeg, kbeg + nk) of the nk_all tiles of K.  A dual call
+  // walks 2 * nk_k tiles, the second nk_k on (A2, B2).  A K band keeps only the tiles that
+  // meet the band (the rest multiply zeros).
+  const int nk_k = (a.K + C::BK - 1) / C::BK;
+  const int nk_all = kDual && a.dual ? 2 * nk_k : nk_k;
   int kbeg = split * a.kt_per_split;
   int nk = a.splits > 1 ? min(nk_all - kbeg, a.kt_per_split) : nk_all;
-  if (a.kband != KBAND_NONE) {
+  if (C::IN == IN_BF16 && a.kband != KBAND_NONE) {  // K bands: bf16 calls only
     int lo = 0, hi = a.K;  // elements of K
     if (a.kband == KBAND_A_LOWER) hi = min(a.K, a.band_off + (tm + 1) * C::BM);
     if (a.kband == KBAND_A_UPPER) lo = min(a.K, a.band_off + tm * C::BM);
@@ -192,6 +200,10 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(GemmArgs a) {
     constexpr int q = decltype(qc)::value;
     int kt = u < nk ? kbeg + u : nk_all;  // past this workgroup's range: past K (zeros)
     if (krot != 0 && u < nk) kt = u + krot < nk ? u + krot : u + krot - nk;
+    // a dual call's second product: tiles nk_k .. 2*nk_k - 1 are K tiles of (A2, B2); the
+    // past-the-end marker 2*nk_k becomes K tile nk_k, past K as well
+    const bool second = kDual && a.dual && kt >= nk_k;
+    if (second) kt -= nk_k;
     const int k0 = kt * C::BK;
     const uint32_t base = (uint32_t)(uintptr_t)sb;
     if constexpr (C::MXN && q == D::IPW - 1) {
@@ -199,12 +211,12 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(GemmArgs a) {
     } else if constexpr (q < D::A_IPW) {
       const bool ok = a_ok[q] & (k0 + a_kc[q] < a.K);
       load_to_lds(__builtin_amdgcn_readfirstlane(base + a_blk + q * 1024u),
-                  ok ? a_goff[q] + (uint32_t)kt * a_kstep : kOOB, ra);
+                  ok ? a_goff[q] + (uint32_t)kt * a_kstep : kOOB, second ? ra2 : ra);
     } else {
       constexpr int i = q - D::A_IPW;
       const bool ok = b_ok[i] & (k0 + b_kc[i] < a.K);
       load_to_lds(__builtin_amdgcn_readfirstlane(base + b_blk + i * 1024u),
-                  ok ? b_goff[i] + (uint32_t)kt * b_kstep : kOOB, rb);
+                  ok ? b_goff[i] + (uint32_t)kt * b_kstep : kOOB, second ? rb2 : rb);
     }
   };
 

@@ -431,8 +431,10 @@ __device__ __forceinline__ void store_group_tri(const GemmArgs& a, f32x4 v, int 
 
 template <class C>
 __device__ __forceinline__ void store_group(const GemmArgs& a, f32x4 v, int p, int row0, int col0, int lane) {
-  // a triangle of C takes its own path, so that the common one keeps its register budget
-  if (a.tri != TRI_NONE) return store_group_tri<C>(a, v, p, row0, col0, lane);
+  // a triangle of C takes its own path, so that the common one keeps its register budget;
+  // only bf16 square tiles serve triangles (the host picks no other), the rest compile it out
+  if constexpr (C::IN == IN_BF16 && C::BM == C::BN)
+    if (a.tri != TRI_NONE) return store_group_tri<C>(a, v, p, row0, col0, lane);
   const int q = p % (C::ACC / 4), j = (p / (C::ACC / 4)) % C::FN, i = p / (C::ACC / 4) / C::FN;
   const int m = row0 + i * C::MT + lane % C::MT;
   const int n = col0 + j * C::MT + (C::MT == 32 ? 8 * q + 4 * (lane / 32) : 4 * (lane / 16));

@@ -243,9 +243,9 @@ gemm_status_t gemm_syrk(gemm_handle_t h, int uplo, int trans, int64_t N, int64_t
 /* Symmetric rank-2K update of one triangle:
  *   C <- alpha * (op(A) op(B)^T + op(B) op(A)^T) + beta * C   on the uplo triangle,
  * op(A), op(B) N x K stored like syrk's A.  Both products accumulate in one fp32 sum
- * (one rounding of C): from N*K = 2^16 the operands are packed into the workspace as
- * [op(A) | op(B) | op(A)] (N x 3K, when it fits) and one K-contiguous product over 2K runs on
- * the MFMA kernels; smaller calls run both products in one K loop of the generic kernel. */
+ * (one rounding of C), in one K loop: on the caller's buffers for trans = GEMM_OP_N with
+ * lda == ldb, else (from N*K = 2^16, when they fit) on copies of op(A), op(B) made
+ * K-contiguous in the workspace; smaller calls run on the generic kernel. */
 gemm_status_t gemm_syr2k(gemm_handle_t h, int uplo, int trans, int64_t N, int64_t K, float alpha,
                          const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
                          int64_t ldc, int dtype);
