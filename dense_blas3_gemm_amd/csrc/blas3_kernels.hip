@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void expand_tri_trans_kernel(const uint16_t* _
                                                                uint16_t* __restrict__ dst, int64_t ldd, int r0,
                                                                int c0, int rows, int cols, int cols_pad, int n,
                                                                int uplo, int unit, int vec) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[SB][SB + 8];  // tile[y][x] = src[sr0 + y][sc0 + x]
+  __shared__ uint16_t tile[SB][SB + 2];  // tile[y][x] = src[sr0 + y][sc0 + x]; 33-word rows: column reads spread over the banks
   const int br = blockIdx.y * SB, bc = blockIdx.x * SB;
   const int sr0 = c0 + bc, sc0 = r0 + br;  // the source block
   for (int e = threadIdx.x; e < SB * SB / 8; e += 256) {
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void expand_tri_trans_kernel(const uint16_t* _
 __global__ __launch_bounds__(256) void expand_sym_kernel(const uint16_t* __restrict__ src, int64_t lds,
                                                          uint16_t* __restrict__ dst, int64_t ldd, int r0, int c0,
                                                          int rows, int cols, int cols_pad, int n, int uplo, int vec) {
-  __shared__ __attribute__((aligned(16))) uint16_t mir[SB][SB + 8];  // mir[y][x] = src[gj0 + y][gi0 + x]
+  __shared__ uint16_t mir[SB][SB + 2];  // mir[y][x] = src[gj0 + y][gi0 + x]; 33-word rows: column reads spread over the banks
   const int br = blockIdx.y * SB, bc = blockIdx.x * SB;  // output block origin
   const int gi0 = r0 + br, gj0 = c0 + bc;                  // in S
   // 8 stored elements of src row si from column sj, or fewer / none at the edges
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(256) void copy2d_kernel(const uint16_t* __restrict_
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ src, int64_t lds,
                                                        uint16_t* __restrict__ dst, int64_t ldd, int rows, int cols,
                                                        int vec) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[SB][SB + 8];  // tile[y][x] = src[r0 + y][c0 + x]
+  __shared__ uint16_t tile[SB][SB + 2];  // tile[y][x] = src[r0 + y][c0 + x]; 33-word rows: column reads spread over the banks
   const int r0 = blockIdx.y * SB, c0 = blockIdx.x * SB;
   for (int e = threadIdx.x; e < SB * SB / 8; e += 256) {
     const int y = e / (SB / 8), x8 = (e % (SB / 8)) * 8;
