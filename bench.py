@@ -6,9 +6,13 @@
 
 A step is one call C = alpha*A*B + beta*C of the headline workload, 4096^3 bf16
 row-major NN with bf16 C (alpha 1, beta 0), on inputs already resident in HBM.
-W untimed warmup steps run first; then K steps are timed between two device
-synchronisations, and each launch also sits between its own pair of HIP events
-recorded on the stream the kernel runs on.  Prints one JSON line.
+W untimed warmup steps run first; then K steps run back to back between two device
+synchronisations, with one pair of HIP events on the kernels' stream around them:
+`value` is 2MNK*K over the host wall time of that region, `roofline.achieved` 2MNK over
+the event time per step.  A separate pass afterwards times each launch between its own
+pair of events (p50/p95).  Prints one JSON line, with the shader clock sampled from a host
+thread during the timed region, the device, and (with the CPU baseline) the timed
+output's rows checked against the fp64 oracle.
 
 --sweep additionally times every other workload (10 warmup + 50 event-timed calls
 each, p50/p95) and prints a Markdown table to stderr; the JSON line is unchanged.
@@ -42,9 +46,9 @@ PEAK_TFLOPS = {"bf16": 2516.6, "e4m3": 5033.2}  # 256 CU x 2.4 GHz x 4096 (8192 
 HBM_GBS = 8000.0
 METRIC = "TFLOP/s and % of MI355X dense MFMA peak, 4096³ bf16 GEMM (1 GPU)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_4096_bf16.md")
-# the device code of the direct-to-LDS kernels (the headline policy's kernel)
+# the device code of the headline policy's kernel (the ping-pong kernel and its shared parts)
 KERNEL_SOURCES = [os.path.join(ROOT, "dense_blas3_gemm_amd", "csrc", f)
-                  for f in ("kernel_mfma_dma.hip", "mfma_common.h", "gemm_internal.h")]
+                  for f in ("kernel_pingpong.hip", "mfma_common.h", "gemm_internal.h")]
 
 
 def _dev(bits, kind):
@@ -84,10 +88,8 @@ def measured_traffic(policy: str):
         return None
 
 
-def time_problem(g, p: gi.Gemm, warmup: int, steps: int, data=None):
-    """Returns dict with wall ms/step, event durations (ms) and the policy name."""
+def _operands(p: gi.Gemm, data):
     import torch
-    data = data if data is not None else p.make()
     A = _dev(data["A"], p.in_dtype)
     B = _dev(data["B"], p.in_dtype)
     if "C" in data:
@@ -95,6 +97,15 @@ def time_problem(g, p: gi.Gemm, warmup: int, steps: int, data=None):
     else:
         C = torch.zeros((p.M, p.N), dtype=torch.float32 if p.c_dtype == "f32" else torch.bfloat16,
                         device="cuda:0")
+    return A, B, C
+
+
+def time_problem(g, p: gi.Gemm, warmup: int, steps: int, data=None):
+    """Event-timed launches: returns dict with wall ms/step, per-launch event durations (ms)
+    and the policy name.  Each launch sits between its own pair of HIP events."""
+    import torch
+    data = data if data is not None else p.make()
+    A, B, C = _operands(p, data)
     policy = g.query_policy(p.M, p.N, p.K, p.transA, p.transB, p.dtype_code, A.data_ptr(),
                             A.stride(0), B.data_ptr(), B.stride(0), C.data_ptr(), C.stride(0))
     stream = torch.cuda.current_stream()
@@ -116,6 +127,96 @@ def time_problem(g, p: gi.Gemm, warmup: int, steps: int, data=None):
     return {"wall_ms": wall * 1e3 / steps, "event_ms": durs, "policy": policy}
 
 
+def time_headline(g, p: gi.Gemm, warmup: int, steps: int, data):
+    """The bench step loop: W warmup launches, then K launches back to back between two
+    device synchronisations, with one pair of HIP events on the kernels' stream around
+    the whole timed region (no event between launches).  Returns wall and event ms per
+    step, the policy, the output C and the operands (for the per-launch pass)."""
+    import torch
+    A, B, C = _operands(p, data)
+    policy = g.query_policy(p.M, p.N, p.K, p.transA, p.transB, p.dtype_code, A.data_ptr(),
+                            A.stride(0), B.data_ptr(), B.stride(0), C.data_ptr(), C.stride(0))
+    stream = torch.cuda.current_stream()
+    call = lambda: g(A, B, C, transA=p.transA, transB=p.transB, alpha=p.alpha, beta=p.beta,
+                     dtype=p.dtype_code)
+    for _ in range(warmup):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return {"wall_ms": wall * 1e3 / steps, "event_ms_per_step": e0.elapsed_time(e1) / steps, "policy": policy,
+            "C": C}
+
+
+def _sclk_files():
+    import glob
+    return sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+
+
+def gpu_clock_mhz(files=None):
+    """Current shader clock (MHz) of the first GPU the kernel driver lists, from sysfs
+    pp_dpm_sclk (the level marked '*'); None where it cannot be read."""
+    for f in files if files is not None else _sclk_files():
+        try:
+            for line in open(f):
+                if line.rstrip().endswith("*"):
+                    return int(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
+class ClockSampler:
+    """Samples the shader clock from a host thread while the timed region runs (the clock
+    read after a synchronisation is the idle one)."""
+
+    def __init__(self, period_s: float = 0.0005):
+        import threading
+        self.files = _sclk_files()[:1]
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = gpu_clock_mhz(self.files)
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.files:
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.files:
+            self._t.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = np.array(self.samples)
+        return {"samples": int(v.size), "median": int(np.median(v)), "min": int(v.min()), "max": int(v.max())}
+
+
+def build_info():
+    """The build stamp written next to the library (git state at build time), if present."""
+    f = os.path.join(ROOT, "dense_blas3_gemm_amd", "build_info.json")
+    try:
+        return json.load(open(f))
+    except (OSError, ValueError):
+        return {}
+
+
 def cpu_baseline(p: gi.Gemm, target_s: float = 8.0):
     """The fp64 oracle on a bounded sample of output rows of the same workload."""
     import oracle
@@ -134,6 +235,27 @@ def cpu_baseline(p: gi.Gemm, target_s: float = 8.0):
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} of {p.M} output rows of {p.name} (fp64 triple loop, "
                       f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s)"}
+
+
+def parity_sample(p: gi.Gemm, data, C_dev, nrows: int = 32):
+    """The timed output on rows spread over every 256-row tile against the fp64 oracle (the
+    CPU-baseline leg): elements past the stated bf16 bound (2^-8 |R| + 1e-6), past the bound
+    with the probabilistic fp32 accumulation term (2^-24 sqrt(K) sum|a b|), the largest
+    error / bound and the relative Frobenius error of those rows."""
+    import oracle
+    import torch
+    rows = np.unique(np.linspace(0, p.M - 1, nrows).round().astype(np.int64))
+    R, S = oracle.gemm_problem(p, data, rows=rows, with_abs=True, threads=oracle.default_threads())
+    C = C_dev.detach()[torch.as_tensor(rows, device=C_dev.device)].float().cpu().numpy().astype(np.float64)
+    err = np.abs(C - R)
+    literal = 2.0 ** -8 * np.abs(R) + 1e-6 if p.c_dtype == "bf16" else 2.0 ** -23 * np.abs(R) + 1e-6
+    bound = literal + 2.0 ** -24 * np.sqrt(p.K) * S
+    return {"rows": int(len(rows)), "elements": int(err.size),
+            "n_outside_literal_bound": int((err > literal).sum()),
+            "n_outside_bound": int((err > bound).sum()),
+            "max_err_over_bound": float((err / bound).max()),
+            "frob_rel": float(np.linalg.norm(C - R) / np.linalg.norm(R)),
+            "finite": bool(np.isfinite(C).all())}
 
 
 def sweep(g, warmup: int = 10, steps: int = 50):
@@ -540,16 +662,22 @@ def main():
         g.close()
         return
     p = gi.BY_NAME[args.workload]
+    data = p.make()
     if args.policy:
         g.set_policy(args.policy)
-    r = time_problem(g, p, args.warmup, args.steps)
+    with ClockSampler() as clk:
+        r = time_headline(g, p, args.warmup, args.steps, data)
+    # per-launch distribution: a separate pass after the timed region, each launch between
+    # its own pair of events
+    dist = time_problem(g, p, 0, args.steps, data=data)["event_ms"]
     g.set_policy(None)
     ms = r["wall_ms"]
     value = p.flops / (ms * 1e-3) / 1e12
-    ev = r["event_ms"]
-    avg_launch_ms = float(ev.mean())
-    achieved = p.flops / (avg_launch_ms * 1e-3) / 1e12
+    ev_ms = r["event_ms_per_step"]
+    achieved = p.flops / (ev_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[p.in_dtype]
+    import torch
+    props = torch.cuda.get_device_properties(0)
     out = {
         "metric": METRIC if p is gi.SQUARE_4096 else f"TFLOP/s and % of MI355X dense MFMA peak, {p.name} (1 GPU)",
         "value": round(value, 2),
@@ -571,10 +699,13 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(r["policy"]) if p is gi.SQUARE_4096 and not args.policy else None,
-                     "launch_us_p50": round(float(np.percentile(ev, 50)) * 1e3, 2),
-                     "launch_us_p95": round(float(np.percentile(ev, 95)) * 1e3, 2),
-                     "launch_us_mean": round(avg_launch_ms * 1e3, 2)},
+                     "kernel_us_timed_region": round(ev_ms * 1e3, 2),
+                     "launch_us_p50": round(float(np.percentile(dist, 50)) * 1e3, 2),
+                     "launch_us_p95": round(float(np.percentile(dist, 95)) * 1e3, 2)},
+        "device": {"name": props.name, "cus": props.multi_processor_count, "hip": torch.version.hip,
+                   "sclk_mhz_during_timed_region": clk.summary(), "build": build_info()},
     }
+    C_out = r["C"]
     if args.sweep:
         sweep(g)
     if args.ablation:
@@ -583,6 +714,7 @@ def main():
     g.close()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p)
+        out["parity"] = parity_sample(p, data, C_out)
     print(json.dumps(out))
 
 

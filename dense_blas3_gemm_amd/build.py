@@ -1,6 +1,7 @@
 """Builds libdbgemm.so (HIP kernels for gfx950 + the C-ABI) in the package folder.
 
-    python -m dense_blas3_gemm_amd.build        # or dense_blas3_gemm_amd.build.build()
+    python -m dense_blas3_gemm_amd.build                 # or dense_blas3_gemm_amd.build.build()
+    python -m dense_blas3_gemm_amd.build --incremental   # recompile only stale objects
 
 Every translation unit is compiled by hipcc for gfx950 only.  Packed-fp32 VALU
 instructions are disabled for all device code.
@@ -19,13 +20,17 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libdbgemm.so")
 BUILD = os.path.join(PKG, "_build")
 
-# (source, object name, extra flags): the direct-to-LDS kernels are compiled once per
-# transpose case so that the four groups of instantiations build in parallel
+# (source, object name, extra flags): the direct-to-LDS ring kernels are compiled once per
+# transpose case and half of the policy table, the ping-pong kernels once per transpose
+# case, so that the groups of instantiations build in parallel
 SOURCES = [("api.cpp", "api", []), ("policy.cpp", "policy", []), ("kernel_simt.hip", "kernel_simt", []),
            ("kernel_mfma.hip", "kernel_mfma", []), ("lds_probe.hip", "lds_probe", []),
            ("quantize_mx.hip", "quantize_mx", []),
            ("blas3.cpp", "blas3", []), ("blas3_kernels.hip", "blas3_kernels", [])] + [
-    ("kernel_mfma_dma.hip", f"kernel_mfma_dma_{ta}{tb}", [f"-DDBGEMM_DMA_TA={ta}", f"-DDBGEMM_DMA_TB={tb}"])
+    ("kernel_mfma_dma.hip", f"kernel_mfma_dma_{ta}{tb}_p{part}",
+     [f"-DDBGEMM_DMA_TA={ta}", f"-DDBGEMM_DMA_TB={tb}", f"-DDBGEMM_DMA_PART={part}"])
+    for ta in (0, 1) for tb in (0, 1) for part in (0, 1)] + [
+    ("kernel_pingpong.hip", f"kernel_pingpong_{ta}{tb}", [f"-DDBGEMM_DMA_TA={ta}", f"-DDBGEMM_DMA_TB={tb}"])
     for ta in (0, 1) for tb in (0, 1)]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -33,9 +38,21 @@ FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-ta
          "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC]
 
 
-def _compile(entry) -> str:
+def _stale(src: str, obj: str) -> bool:
+    """An object is stale when it is older than its source or any header of csrc/ and include/."""
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    deps = [os.path.join(CSRC, src)] + [os.path.join(d, f) for d in (CSRC, INCLUDE) for f in os.listdir(d)
+                                        if f.endswith((".h", ".inc"))]
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def _compile(entry, incremental: bool = False) -> str:
     src, name, extra = entry
     obj = os.path.join(BUILD, name + ".o")
+    if incremental and not _stale(src, obj):
+        return obj
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
     cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -44,21 +61,39 @@ def _compile(entry) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def _write_build_info() -> None:
+    """Records the source state the library was built from (git describe, when the tree is
+    a git checkout) beside it; bench.py reports it."""
+    import json
+    import time
+    try:
+        desc = subprocess.run(["git", "-C", ROOT, "describe", "--always", "--dirty", "--abbrev=12"],
+                              capture_output=True, text=True, timeout=20).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        desc = None
+    with open(os.path.join(PKG, "build_info.json"), "w") as f:
+        json.dump({"git": desc, "built": time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime()), "arch": ARCH}, f)
+
+
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compiles every translation unit (only the stale ones with `incremental`) and links."""
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    # the slowest translation units first, so that they start at once
+    order = sorted(SOURCES, key=lambda e: not e[0].startswith("kernel_mfma_dma"))
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 8)) as ex:
+        objs = list(ex.map(lambda e: _compile(e, incremental), order))
     tmp = OUT + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, OUT)
+    _write_build_info()
     if verbose:
         print(f"built {OUT}")
     return OUT
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, incremental="--incremental" in sys.argv[1:])
     sys.exit(0)

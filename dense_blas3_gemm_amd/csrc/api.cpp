@@ -95,11 +95,21 @@ Problem make_problem(int transA, int transB, int64_t M, int64_t N, int64_t K, co
 
 namespace dbgemm {
 hipError_t launch_mfma_dma(const Policy& p, const GemmArgs& a, hipStream_t s) {
+  hipError_t e = hipErrorInvalidConfiguration;
   switch (a.transA * 2 + a.transB) {
-    case 0: return launch_mfma_dma_00(p, a, s);
-    case 1: return launch_mfma_dma_01(p, a, s);
-    case 2: return launch_mfma_dma_10(p, a, s);
-    default: return launch_mfma_dma_11(p, a, s);
+    case 0: (void)(launch_mfma_dma_00_p0(p, a, s, &e) || launch_mfma_dma_00_p1(p, a, s, &e)); break;
+    case 1: (void)(launch_mfma_dma_01_p0(p, a, s, &e) || launch_mfma_dma_01_p1(p, a, s, &e)); break;
+    case 2: (void)(launch_mfma_dma_10_p0(p, a, s, &e) || launch_mfma_dma_10_p1(p, a, s, &e)); break;
+    default: (void)(launch_mfma_dma_11_p0(p, a, s, &e) || launch_mfma_dma_11_p1(p, a, s, &e)); break;
+  }
+  return e;
+}
+hipError_t launch_mfma_pp(const Policy& p, const GemmArgs& a, hipStream_t s) {
+  switch (a.transA * 2 + a.transB) {
+    case 0: return launch_mfma_pp_00(p, a, s);
+    case 1: return launch_mfma_pp_01(p, a, s);
+    case 2: return launch_mfma_pp_10(p, a, s);
+    default: return launch_mfma_pp_11(p, a, s);
   }
 }
 }  // namespace dbgemm
@@ -371,6 +381,7 @@ static hipError_t enqueue_impl(int cu_count, hipStream_t stream, void* ws, int64
   a.splits = sp;
   a.kt_per_split = (int)split_kt(pol, K, sp);
   if (sp > 1) a.ws = (float*)ws;
+  if (pol.pipe == 2) return launch_mfma_pp(pol, a, stream);
   return pol.pipe == 1 ? launch_mfma_dma(pol, a, stream) : launch_mfma_staged(pol, a, stream);
 }
 

@@ -78,7 +78,8 @@ enum PolicyKind { KIND_SIMT = 0, KIND_MFMA = 1, KIND_SCALE = 2 };
 struct Policy {
   const char* name;
   int kind;
-  int pipe;        // 0: global -> registers -> LDS (two stages); 1: direct-to-LDS loads
+  int pipe;        // 0: global -> registers -> LDS (two stages); 1: direct-to-LDS loads into a
+                   // ring; 2: direct-to-LDS loads, two wave groups taking turns (ping-pong)
   int in_mode;     // 0: bf16 in, bf16 MFMA; 1: E4M3 in, widened to bf16 in LDS (exact
                    // fp32 accumulation); 2: E4M3 in, native f8f6f4 MFMA; 3: block-scaled
                    // E4M3 (MXFP8), widened with its scale; 4: block-scaled E4M3 on the
@@ -100,11 +101,22 @@ hipError_t launch_simt(const GemmArgs& a, hipStream_t s);
 hipError_t launch_scale(const GemmArgs& a, hipStream_t s);  // C <- beta*C (K == 0 or alpha == 0)
 hipError_t launch_mfma_staged(const Policy& p, const GemmArgs& a, hipStream_t s);  // pipe 0
 hipError_t launch_mfma_dma(const Policy& p, const GemmArgs& a, hipStream_t s);     // pipe 1
-// pipe 1, one per (transA, transB) case, each in its own object
-hipError_t launch_mfma_dma_00(const Policy& p, const GemmArgs& a, hipStream_t s);
-hipError_t launch_mfma_dma_01(const Policy& p, const GemmArgs& a, hipStream_t s);
-hipError_t launch_mfma_dma_10(const Policy& p, const GemmArgs& a, hipStream_t s);
-hipError_t launch_mfma_dma_11(const Policy& p, const GemmArgs& a, hipStream_t s);
+// pipe 1, one per (transA, transB) case and half of the policy table, each in its own
+// object: true when that part launched p (*err = the launch status)
+#define DBGEMM_DMA_DECL(ab)                                                                           \
+  bool launch_mfma_dma_##ab##_p0(const Policy& p, const GemmArgs& a, hipStream_t s, hipError_t* err); \
+  bool launch_mfma_dma_##ab##_p1(const Policy& p, const GemmArgs& a, hipStream_t s, hipError_t* err);
+DBGEMM_DMA_DECL(00)
+DBGEMM_DMA_DECL(01)
+DBGEMM_DMA_DECL(10)
+DBGEMM_DMA_DECL(11)
+#undef DBGEMM_DMA_DECL
+// pipe 2 (ping-pong), one per (transA, transB) case
+hipError_t launch_mfma_pp(const Policy& p, const GemmArgs& a, hipStream_t s);
+hipError_t launch_mfma_pp_00(const Policy& p, const GemmArgs& a, hipStream_t s);
+hipError_t launch_mfma_pp_01(const Policy& p, const GemmArgs& a, hipStream_t s);
+hipError_t launch_mfma_pp_10(const Policy& p, const GemmArgs& a, hipStream_t s);
+hipError_t launch_mfma_pp_11(const Policy& p, const GemmArgs& a, hipStream_t s);
 
 // LDS read microbenchmark: 8 reads per lane per iteration, offsets in bytes from the
 // start of a 64 KiB LDS array, each a multiple of the read width and inside the array.

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_mfma_kernel(GemmArgs a) {
       a_goff[i] = (uint32_t)(r * a.lda + m0 + a_c * C::VEC) * C::GES;
       a_fixed_ok[i] = (m0 + a_c * C::VEC) < a.M;
     }
-    const int s = sw_on ? swz<C::A_KC, C::FP8, C::A_CPR>(r) : 0;
+    const int s = sw_on ? swz<C::A_KC, C::FP8, C::A_CPR, C::MT>(r) : 0;
     a_soff[i] = r * C::A_RB + (((a_c * C::WIDEN) ^ s) << 4);
   }
 #pragma unroll
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_mfma_kernel(GemmArgs a) {
       b_goff[i] = (uint32_t)(r * a.ldb + n0 + b_c * C::VEC) * C::GES;
       b_fixed_ok[i] = (n0 + b_c * C::VEC) < a.N;
     }
-    const int s = sw_on ? swz<C::B_KC, C::FP8, C::B_CPR>(r) : 0;
+    const int s = sw_on ? swz<C::B_KC, C::FP8, C::B_CPR, C::MT>(r) : 0;
     b_soff[i] = C::A_BYTES + r * C::B_RB + (((b_c * C::WIDEN) ^ s) << 4);
   }
   // byte advance of one K tile

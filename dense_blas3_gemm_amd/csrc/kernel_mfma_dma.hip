@@ -29,21 +29,36 @@ namespace {
 // bytes [lds_base, lds_base + 1024) (lane i -> lds_base + 16*i); an offset past the
 // buffer's size reads zeros.  Issued as assembly: the compiler neither sees nor waits
 // for these loads (it could not tell them apart from the LDS reads of other ring
-// slots), so every wait on them below is explicit.
+// slots), so every wait on them below is explicit.  M0 carries the LDS address: the
+// statement saves and restores it (the compiler reserves M0 and does not honour it as
+// a clobber), and one wait state separates its write from the load that reads it.
 __device__ __forceinline__ void load_to_lds(uint32_t lds_base, uint32_t voff, __amdgpu_buffer_rsrc_t rsrc) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds_base), "v"(voff), "s"(rsrc)
-               : "memory");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(voff), "s"(rsrc)
+      : "memory");
 }
 
 // 64 lanes x 4 bytes from buffer `rsrc` at per-lane byte offset `voff` into LDS bytes
 // [lds_base, lds_base + 256) (lane i -> lds_base + 4*i); an offset past the buffer reads 0.
+// M0 as in load_to_lds.
 __device__ __forceinline__ void load_to_lds_dword(uint32_t lds_base, uint32_t voff, __amdgpu_buffer_rsrc_t rsrc) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :
-               : "s"(lds_base), "v"(voff), "s"(rsrc)
-               : "memory");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(voff), "s"(rsrc)
+      : "memory");
 }
 
 // Waits until at most N of this wave's buffer loads are in flight and all its LDS
@@ -124,7 +139,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(GemmArgs a) {
   for (int i = 0; i < D::A_IPW; ++i) {
     const int p = (wave * D::A_IPW + i) * 64 + lane;
     const int r = p / C::A_CPR;
-    const int c = (p % C::A_CPR) ^ (sw_on ? swz<C::A_KC, C::FP8, C::A_CPR>(r) : 0);
+    const int c = (p % C::A_CPR) ^ (sw_on ? swz<C::A_KC, C::FP8, C::A_CPR, C::MT>(r) : 0);
     if constexpr (C::A_KC) {  // rows = m, chunks along k
       a_goff[i] = (uint32_t)((m0 + r) * a.lda + c * C::VEC) * C::ES;
       a_ok[i] = (m0 + r) < a.M;
@@ -139,7 +154,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(GemmArgs a) {
   for (int i = 0; i < D::B_IPW; ++i) {
     const int p = (wave * D::B_IPW + i) * 64 + lane;
     const int r = p / C::B_CPR;
-    const int c = (p % C::B_CPR) ^ (sw_on ? swz<C::B_KC, C::FP8, C::B_CPR>(r) : 0);
+    const int c = (p % C::B_CPR) ^ (sw_on ? swz<C::B_KC, C::FP8, C::B_CPR, C::MT>(r) : 0);
     if constexpr (C::B_KC) {  // rows = n, chunks along k
       b_goff[i] = (uint32_t)((n0 + r) * a.ldb + c * C::VEC) * C::ES;
       b_ok[i] = (n0 + r) < a.N;
@@ -402,29 +417,36 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// This file is compiled once per transpose case (DBGEMM_DMA_TA, DBGEMM_DMA_TB), so the
-// four groups of kernel instantiations build in parallel.
-#if !defined(DBGEMM_DMA_TA) || !defined(DBGEMM_DMA_TB)
-#error "compile with -DDBGEMM_DMA_TA=0|1 -DDBGEMM_DMA_TB=0|1"
+// This file is compiled once per transpose case (DBGEMM_DMA_TA, DBGEMM_DMA_TB) and half of
+// the policy table (DBGEMM_DMA_PART: the entries on even or odd lines of policies.inc), so
+// the eight groups of kernel instantiations build in parallel.
+#if !defined(DBGEMM_DMA_TA) || !defined(DBGEMM_DMA_TB) || !defined(DBGEMM_DMA_PART)
+#error "compile with -DDBGEMM_DMA_TA=0|1 -DDBGEMM_DMA_TB=0|1 -DDBGEMM_DMA_PART=0|1"
 #endif
 
 }  // namespace
 
-#define DBGEMM_DMA_CAT2(a, b) launch_mfma_dma_##a##b
-#define DBGEMM_DMA_CAT(a, b) DBGEMM_DMA_CAT2(a, b)
+#define DBGEMM_DMA_CAT2(a, b, c) launch_mfma_dma_##a##b##_p##c
+#define DBGEMM_DMA_CAT(a, b, c) DBGEMM_DMA_CAT2(a, b, c)
 
-hipError_t DBGEMM_DMA_CAT(DBGEMM_DMA_TA, DBGEMM_DMA_TB)(const Policy& p, const GemmArgs& a, hipStream_t s) {
+// Launches policy p if this part of the table instantiates its geometry (*err is the launch
+// status); returns false, with nothing enqueued, otherwise.
+bool DBGEMM_DMA_CAT(DBGEMM_DMA_TA, DBGEMM_DMA_TB, DBGEMM_DMA_PART)(const Policy& p, const GemmArgs& a, hipStream_t s,
+                                                                   hipError_t* err) {
 #define DBGEMM_SIMT(name, eff)
 #define DBGEMM_MFMA(name_, pipe_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_, eff_)       \
-  if constexpr (pipe_ == 1 && ((in_ != 4 && !(((sw_) >> 3) & 1)) || (DBGEMM_DMA_TA == 0 && DBGEMM_DMA_TB == 1))) \
+  if constexpr (pipe_ == 1 && __LINE__ % 2 == DBGEMM_DMA_PART &&                                          \
+                ((in_ != 4 && !(((sw_) >> 3) & 1)) || (DBGEMM_DMA_TA == 0 && DBGEMM_DMA_TB == 1)))        \
     if (p.BM == bm_ && p.BN == bn_ && p.BK == bk_ && p.WM == wm_ && p.WN == wn_ && p.MT == mt_ &&         \
-        p.stages == st_ && p.in_mode == in_ && p.read_mode == ((((sw_) >> 2) & 1) ? 0 : 1))               \
-      return launch_cfg<Cfg<bm_, bn_, bk_, wm_, wn_, mt_, st_, in_, DBGEMM_DMA_TA != 0, DBGEMM_DMA_TB != 0,  \
-                            (((sw_) >> 2) & 1) ? 0 : 1>>(a, s);
+        p.stages == st_ && p.in_mode == in_ && p.read_mode == ((((sw_) >> 2) & 1) ? 0 : 1)) {             \
+      *err = launch_cfg<Cfg<bm_, bn_, bk_, wm_, wn_, mt_, st_, in_, DBGEMM_DMA_TA != 0, DBGEMM_DMA_TB != 0,  \
+                            (((sw_) >> 2) & 1) ? 0 : 1>>(a, s);                                           \
+      return true;                                                                                        \
+    }
 #include "policies.inc"
 #undef DBGEMM_SIMT
 #undef DBGEMM_MFMA
-  return hipErrorInvalidConfiguration;
+  return false;
 }
 
 }  // namespace dbgemm

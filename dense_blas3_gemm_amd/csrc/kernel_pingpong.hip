@@ -1,0 +1,378 @@
+// Ping-pong MFMA GEMM kernel for gfx950 (large tiles, bf16 operands).
+//
+// Same operation, LDS layout (XOR-swizzled 16-byte chunks), fragment reads, MFMA and
+// epilogue as the other MFMA kernels (mfma_common.h), and the same direct-to-LDS
+// operand staging as the ring kernel; what differs is how the eight waves of a
+// workgroup share each SIMD's matrix core.
+//
+// A CU has four SIMDs and a 256x256 workgroup tile keeps two waves on each.  In the
+// ring kernel both waves of a SIMD run the same instruction mix at the same time:
+// MFMAs with their share of fragment reads between them, and all eight waves meet at
+// one barrier per K tile, where the matrix cores drain.  Here the waves form two
+// groups of four, one wave of each group per SIMD, and the groups take turns:
+//
+//   * while group 0 runs one K tile's MFMAs (one uninterrupted cluster of 64
+//     16x16x32 MFMAs per wave, at raised wave priority) group 1 reads its fragments
+//     of the same K tile from LDS, and the other way round in the next phase;
+//   * every phase ends at a workgroup barrier, and a group that arrives from its
+//     memory phase has its fragments in registers, so the matrix core of each SIMD
+//     passes from one wave's cluster straight to the other's;
+//   * the operand tiles sit in two LDS slots.  K tile t + 2 is loaded into the slot of
+//     tile t as soon as both groups have read tile t (the barrier after group 1's read
+//     of it): group 0 issues its share of the copies in its memory phase, group 1
+//     between its MFMAs; every wave waits for its own copies (vmcnt) before the
+//     barrier after which they are read, two phases after they were issued.
+//
+// Barrier schedule (B_i is the i-th barrier of the main loop; C(t) = MFMAs of tile t,
+// M(t) = fragment reads of tile t):
+//
+//   group 0:  M(0) | C(0) B1 M(1) B2 | C(1) B3 M(2) B4 | ... | C(n-1) B(2n-1)
+//   group 1:       | M(0) B1 C(0) B2 | M(1) B3 C(1) B4 | ... | M(n-1) B(2n-1) C(n-1)
+//
+// Both groups execute the same number of barriers.  This is the gfx950 form of the
+// pages' producer/consumer split of a CTA ("cp.async / ldmatrix ablation", sections 0.2
+// and 1: asynchronous copies running ahead of the matrix instructions, per-stage
+// completion tracking), with the roles taken by two groups of waves that alternate
+// rather than by dedicated producer warps.
+#include "mfma_common.h"
+
+namespace dbgemm {
+namespace {
+
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+// 64 lanes x 16 bytes from buffer `rsrc` at per-lane byte offset `voff` into LDS bytes
+// [lds_base, lds_base + 1024) (lane i -> lds_base + 16*i); an offset past the buffer's
+// size reads zeros.  M0 carries the LDS address: it is saved and restored inside the
+// statement (the compiler reserves M0 and does not honour it as a clobber), and one
+// wait state separates its write from the load that reads it.  The compiler neither
+// sees nor waits for these loads; every wait on them is explicit.
+__device__ __forceinline__ void pp_load_to_lds(uint32_t lds_base, uint32_t voff, __amdgpu_buffer_rsrc_t rsrc) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
+// Waits for this wave's LDS reads only (its copies stay in flight), then the barrier.
+__device__ __forceinline__ void pp_wait_lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void pp_wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+template <class C>
+struct PingPong {
+  static_assert(C::THREADS == 512 && C::WM == 2 && C::WN == 4, "two groups of four waves");
+  static_assert(C::STAGES >= 2 && C::STAGES <= 5, "two to five LDS slots");
+  static_assert(C::IN == IN_BF16 && C::GES == C::ES, "bf16 operands, LDS holds the global format");
+  static constexpr int NW = 8, S = C::STAGES;
+  static_assert(C::A_BYTES % (1024 * NW) == 0 && C::B_BYTES % (1024 * NW) == 0,
+                "each wave copies whole 1 KiB blocks of both tiles");
+  static constexpr int A_IPW = C::A_BYTES / 1024 / NW;  // copy instructions per wave per K tile
+  static constexpr int B_IPW = C::B_BYTES / 1024 / NW;
+  static constexpr int IPW = A_IPW + B_IPW;
+  static_assert((S - 1) * IPW <= 63, "vmcnt range");
+  static constexpr int NMF = C::FM * C::FN * C::KSTEPS;  // MFMAs per wave per K tile
+  static_assert(NMF >= IPW, "one copy per MFMA at most");
+  // LDS: the A tiles of the S slots, then the B tiles
+  static constexpr int A_OFF = 0, B_OFF = S * C::A_BYTES;
+  static constexpr int LDS_BYTES = S * (C::A_BYTES + C::B_BYTES);
+  // LDS reads per fragment (transposing reads take two 8-byte reads per bf16 fragment)
+  static constexpr int A_RD = C::A_KC ? 1 : 2, B_RD = C::B_KC ? 1 : 2;
+};
+
+// Byte offset, inside one operand tile in LDS, of this lane's part of fragment read h of
+// the MT-row block starting at x0 (M or N index) and K step starting at kbase: the
+// addresses that load_frag computes, for bf16 tiles in the XOR-swizzled layout.
+template <class C, bool KC, int RB>
+__device__ __forceinline__ uint32_t pp_frag_off(int x0, int kbase, int lane, int h) {
+  constexpr int CPR = RB / 16;
+  if constexpr (KC) {
+    const int r = x0 + lane % C::MT;
+    const int c = (kbase + (lane / C::MT) * C::KPL) * 2 / 16;
+    return (uint32_t)(r * RB + ((c ^ swz<true, false, CPR, C::MT>(r)) << 4));
+  } else {
+    const int g = lane >> 4, s = lane & 15;
+    const int coloff = (C::MT == 32) ? 16 * (g & 1) : 0;
+    const int kgrp = (C::MT == 32) ? (g >> 1) : g;
+    const int xb = (x0 + coloff + (s % 4) * 4) * 2;
+    const int k = kbase + kgrp * C::KPL + h * 4 + s / 4;
+    return (uint32_t)(k * RB + ((((xb >> 4) ^ swz<false, false, CPR, C::MT>(k)) << 4) | (xb & 15)));
+  }
+}
+
+template <class C>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
+  using P = PingPong<C>;
+  constexpr int S = P::S;
+  __shared__ __attribute__((aligned(1024))) char lds[P::LDS_BYTES];
+  using Acc = typename AccOf<C::MT>::T;
+
+  int tm, tn, split_unused;  // unsplit
+  tile_of(blockIdx.x, a, tm, tn, split_unused);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  // waves are dealt to the four SIMDs in turn: waves w and w + 4 share a SIMD
+  const int grp = wave >> 2;
+  const int wn = wave & 3;
+  const int wm = grp;
+
+  const uint32_t a_rows = C::A_KC ? a.M : a.K;
+  const uint32_t b_rows = C::B_KC ? a.N : a.K;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, (uint32_t)(a_rows * a.lda * C::ES));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.B, (uint32_t)(b_rows * a.ldb * C::ES));
+
+  // ---- this wave's copy instructions: instruction i fills LDS block wave*IPW + i of the
+  // tile (A blocks, then B); this lane fills chunk p = blk*64 + lane of its operand, row
+  // p / CPR, physical chunk p % CPR, which holds logical chunk (p % CPR) ^ swizzle(row).
+  // A chunk in a row or column past M or N gets an offset past every buffer (adding K
+  // tiles keeps it there: each operand spans less than 2^31 bytes).  For a K-contiguous
+  // operand the chunk's K index within the tile is kept: chunks past K read zeros.
+  uint32_t a_goff[P::A_IPW], b_goff[P::B_IPW];
+  int a_kc[P::A_IPW], b_kc[P::B_IPW];
+#pragma unroll
+  for (int i = 0; i < P::A_IPW; ++i) {
+    const int p = (wave * P::A_IPW + i) * 64 + lane;
+    const int r = p / C::A_CPR;
+    const int c = (p % C::A_CPR) ^ swz<C::A_KC, false, C::A_CPR, C::MT>(r);
+    if constexpr (C::A_KC)
+      a_goff[i] = (m0 + r) < a.M ? (uint32_t)((m0 + r) * a.lda + c * C::VEC) * C::ES : kOOB;
+    else
+      a_goff[i] = (m0 + c * C::VEC) < a.M ? (uint32_t)(r * a.lda + m0 + c * C::VEC) * C::ES : kOOB;
+    a_kc[i] = c * C::VEC;
+  }
+#pragma unroll
+  for (int i = 0; i < P::B_IPW; ++i) {
+    const int p = (wave * P::B_IPW + i) * 64 + lane;
+    const int r = p / C::B_CPR;
+    const int c = (p % C::B_CPR) ^ swz<C::B_KC, false, C::B_CPR, C::MT>(r);
+    if constexpr (C::B_KC)
+      b_goff[i] = (n0 + r) < a.N ? (uint32_t)((n0 + r) * a.ldb + c * C::VEC) * C::ES : kOOB;
+    else
+      b_goff[i] = (n0 + c * C::VEC) < a.N ? (uint32_t)(r * a.ldb + n0 + c * C::VEC) * C::ES : kOOB;
+    b_kc[i] = c * C::VEC;
+  }
+  const uint32_t a_kstep = C::A_KC ? C::BK * C::ES : (uint32_t)(C::BK * a.lda * C::ES);
+  const uint32_t b_kstep = C::B_KC ? C::BK * C::ES : (uint32_t)(C::BK * a.ldb * C::ES);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)lds;
+  const int nk = (a.K + C::BK - 1) / C::BK;
+
+  // Copy instruction q (A blocks first, then B) of K tile kt into slot u.  Rows past K of
+  // an M/N-contiguous operand lie past its buffer and read zeros; a K-contiguous
+  // operand's chunks past K (the last tile's tail, or a tile past the end) are sent past
+  // the buffer here.  Tiles past the end are still issued, so that every wave has the
+  // same number of copies in flight at every barrier and the waits can count them.
+  auto copy_one = [&](int u, int kt, auto qc) {
+    constexpr int q = decltype(qc)::value;
+    const int kleft = a.K - kt * C::BK;  // K elements left from this tile's start
+    if constexpr (q < P::A_IPW) {
+      uint32_t off = a_goff[q] + (uint32_t)kt * a_kstep;
+      if constexpr (C::A_KC) off = a_kc[q] < kleft ? off : kOOB;
+      pp_load_to_lds(__builtin_amdgcn_readfirstlane(lds0 + P::A_OFF + u * C::A_BYTES +
+                                                     (uint32_t)(wave * P::A_IPW + q) * 1024u),
+                     off, ra);
+    } else {
+      constexpr int i = q - P::A_IPW;
+      uint32_t off = b_goff[i] + (uint32_t)kt * b_kstep;
+      if constexpr (C::B_KC) off = b_kc[i] < kleft ? off : kOOB;
+      pp_load_to_lds(__builtin_amdgcn_readfirstlane(lds0 + P::B_OFF + u * C::B_BYTES +
+                                                     (uint32_t)(wave * P::B_IPW + i) * 1024u),
+                     off, rb);
+    }
+  };
+  auto copy_tile = [&](int u, int kt) { static_for<P::IPW>([&](auto qc) { copy_one(u, kt, qc); }); };
+
+  Acc acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = Acc{};
+
+  // ---- fragment addresses of this lane, computed once for slot 0.  For a K-contiguous
+  // operand fragments MT rows apart share their swizzle, so fragment f of K step kk sits
+  // at base[kk] + f*MT rows; for an M/N-contiguous operand the K step and the second
+  // transposing read only add whole rows (the swizzle depends on bits 0, 1 and 3 of the
+  // row, which neither touches), so it sits at base[f] + (kk*KT + h*4) rows.  A slot
+  // adds its offset; all of these constants become the reads' immediate offsets.
+  const int xa0 = wm * C::WTM, xb0 = wn * C::WTN;
+  constexpr int A_NB = C::A_KC ? C::KSTEPS : C::FM, B_NB = C::B_KC ? C::KSTEPS : C::FN;
+  uint32_t a_base[A_NB], b_base[B_NB];
+#pragma unroll
+  for (int v = 0; v < A_NB; ++v)
+    a_base[v] = lds0 + P::A_OFF +
+                (C::A_KC ? pp_frag_off<C, true, C::A_RB>(xa0, v * C::KT, lane, 0)
+                         : pp_frag_off<C, false, C::A_RB>(xa0 + v * C::MT, 0, lane, 0));
+#pragma unroll
+  for (int v = 0; v < B_NB; ++v)
+    b_base[v] = lds0 + P::B_OFF +
+                (C::B_KC ? pp_frag_off<C, true, C::B_RB>(xb0, v * C::KT, lane, 0)
+                         : pp_frag_off<C, false, C::B_RB>(xb0 + v * C::MT, 0, lane, 0));
+  // LDS address of read h of fragment f (K step kk) of an operand in slot u
+  auto a_addr = [&](int u, int kk, int f, int h) -> uint32_t {
+    return C::A_KC ? a_base[kk] + (uint32_t)(u * C::A_BYTES + f * C::MT * C::A_RB)
+                   : a_base[f] + (uint32_t)(u * C::A_BYTES + (kk * C::KT + h * 4) * C::A_RB);
+  };
+  auto b_addr = [&](int u, int kk, int f, int h) -> uint32_t {
+    return C::B_KC ? b_base[kk] + (uint32_t)(u * C::B_BYTES + f * C::MT * C::B_RB)
+                   : b_base[f] + (uint32_t)(u * C::B_BYTES + (kk * C::KT + h * 4) * C::B_RB);
+  };
+
+  bf16x8 fa[C::FM], fb[C::FN];
+  auto rd = [&](uint32_t addr) -> u16x4 {
+    return __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                         (__attribute__((address_space(3))) s16x4*)(uintptr_t)addr));
+  };
+  // Memory phase: the fragments of K step kk of the tile in slot u.
+  auto read_step = [&](auto uc, auto kc) {
+    constexpr int u = decltype(uc)::value, kk = decltype(kc)::value;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+      if constexpr (C::A_KC) {
+        fa[i] = *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)a_addr(u, kk, i, 0);
+      } else {
+        const u16x4 lo = rd(a_addr(u, kk, i, 0)), hi = rd(a_addr(u, kk, i, 1));
+        fa[i] = __builtin_bit_cast(bf16x8, (u16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      if constexpr (C::B_KC) {
+        fb[j] = *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)b_addr(u, kk, j, 0);
+      } else {
+        const u16x4 lo = rd(b_addr(u, kk, j, 0)), hi = rd(b_addr(u, kk, j, 1));
+        fb[j] = __builtin_bit_cast(bf16x8, (u16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      }
+    }
+  };
+  // Compute phase: the MFMA cluster of one K step, at raised wave priority.
+  auto compute_step = [&]() {
+    __builtin_amdgcn_s_setprio(1);
+    static_for<C::FM * C::FN>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      mma(acc[i / C::FN][i % C::FN], fb[i % C::FN], fa[i / C::FN]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // copies allowed in flight at the barrier before a tile's first K step is read: those
+  // of the S - 2 tiles issued after it
+  constexpr int VM = (S - 2) * P::IPW;
+  constexpr int KS = C::KSTEPS;
+
+  // ---- prologue: K tiles 0 .. S-1 into slots 0 .. S-1; wait for tile 0
+  static_for<S>([&](auto uc) { copy_tile(decltype(uc)::value, decltype(uc)::value); });
+  pp_wait_vm_barrier<(S - 1) * P::IPW>();
+
+  // ---- main loop over K steps h = (tile t, step kk), S tiles per iteration so that slots
+  // are compile-time constants: tile t sits in slot t % S.  Group 0 computes step h while
+  // group 1 reads it, then group 1 computes h while group 0 reads h + 1; barriers B(2h+1)
+  // and B(2h+2) separate the phases.  Once both groups have read the last step of tile t
+  // (B(2h+1) of that step) tile t + S replaces it: group 0 issues its copies right after
+  // that barrier, group 1 at the start of its next memory phase.  Before the barrier
+  // after which the first step of tile t + 1 is read, every wave waits for its copies of
+  // tile t + 1.  Both groups run 2 nk KS barriers in all.
+  if (grp == 0) {
+    read_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    pp_wait_lds_barrier();  // B0
+    for (int kt0 = 0; kt0 < nk; kt0 += S) {
+      static_for<S>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        const int kt = kt0 + u;
+        if (kt < nk) {
+          static_for<KS>([&](auto kc) {
+            constexpr int kk = decltype(kc)::value;
+            constexpr bool last = kk == KS - 1;
+            compute_step();
+            if constexpr (last) {
+              pp_wait_vm_barrier<VM>();  // B(2h+1): tile t + 1 complete, slot u free
+              copy_tile(u, kt + S);
+            } else {
+              pp_wait_lds_barrier();  // B(2h+1)
+            }
+            if (!last || kt + 1 < nk) {
+              read_step(std::integral_constant<int, last ? (u + 1) % S : u>{},
+                        std::integral_constant<int, last ? 0 : kk + 1>{});
+              __builtin_amdgcn_sched_barrier(0);
+              pp_wait_lds_barrier();  // B(2h+2)
+            }
+          });
+        }
+      });
+    }
+  } else {
+    pp_wait_lds_barrier();  // B0
+    for (int kt0 = 0; kt0 < nk; kt0 += S) {
+      static_for<S>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        const int kt = kt0 + u;
+        if (kt < nk) {
+          static_for<KS>([&](auto kc) {
+            constexpr int kk = decltype(kc)::value;
+            constexpr bool last = kk == KS - 1;
+            // the slot of tile t - 1, left by both groups at the last B(2h+1) of that tile
+            if (kk == 0 && kt > 0) copy_tile((u + S - 1) % S, kt - 1 + S);
+            read_step(uc, kc);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (last) {
+              pp_wait_vm_barrier<VM>();  // B(2h+1)
+            } else {
+              pp_wait_lds_barrier();
+            }
+            compute_step();
+            if (!last || kt + 1 < nk) {
+              pp_wait_lds_barrier();  // B(2h+2)
+            }
+          });
+        }
+      });
+    }
+  }
+  // the last copies (past K) land before the workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  store_tile<C>(a, acc, m0 + xa0, n0 + xb0, lane);
+}
+
+template <class C>
+hipError_t launch_pp(const GemmArgs& a, hipStream_t s) {
+  if (a.splits != 1 || a.tri != TRI_NONE || a.kband != KBAND_NONE || a.dual) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((gemm_pp_kernel<C>), dim3(grid_tiles(a)), dim3(C::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+#if !defined(DBGEMM_DMA_TA) || !defined(DBGEMM_DMA_TB)
+#error "compile with -DDBGEMM_DMA_TA=0|1 -DDBGEMM_DMA_TB=0|1"
+#endif
+
+}  // namespace
+
+#define DBGEMM_PP_CAT2(a, b) launch_mfma_pp_##a##b
+#define DBGEMM_PP_CAT(a, b) DBGEMM_PP_CAT2(a, b)
+
+// pipe 2 entries of the policy table
+hipError_t DBGEMM_PP_CAT(DBGEMM_DMA_TA, DBGEMM_DMA_TB)(const Policy& p, const GemmArgs& a, hipStream_t s) {
+#define DBGEMM_SIMT(name, eff)
+#define DBGEMM_MFMA(name_, pipe_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_, eff_)        \
+  if constexpr (pipe_ == 2)                                                                                \
+    if (p.BM == bm_ && p.BN == bn_ && p.BK == bk_ && p.WM == wm_ && p.WN == wn_ && p.MT == mt_ &&          \
+        p.stages == st_ && p.in_mode == in_)                                                               \
+      return launch_pp<Cfg<bm_, bn_, bk_, wm_, wn_, mt_, st_, in_, DBGEMM_DMA_TA != 0, DBGEMM_DMA_TB != 0>>(a, s);
+#include "policies.inc"
+#undef DBGEMM_SIMT
+#undef DBGEMM_MFMA
+  return hipErrorInvalidConfiguration;
+}
+
+}  // namespace dbgemm

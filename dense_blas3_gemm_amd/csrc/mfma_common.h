@@ -152,12 +152,20 @@ struct Cfg {
 //    chunks of the same rows (32x32) or rows r..r+7 and r+32..r+39 (16x16).
 // The result is masked to the row's chunk count, so a swizzled chunk never leaves
 // its row whatever the tile width.
-template <bool KC, bool FP8, int CPR>
+template <bool KC, bool FP8, int CPR, int MT = 16>
 __device__ inline int swz(int r) {
   int x;
   if constexpr (KC) {
     if constexpr (CPR == 4) {
-      x = ((r >> 1) ^ (r >> 3)) & 3;
+      // 64-byte rows, four to a bank line.  No xor of the row's own low bits helps every
+      // MFMA shape: measured with the LDS bank-conflict counter on gfx950, (r>>1)&3 is
+      // conflict-free for 16x16 fragments and (r>>2)&3 for 32x32 ones
+      if constexpr (FP8)
+        x = ((r >> 1) ^ (r >> 3)) & 3;
+      else if constexpr (MT == 16)
+        x = (r >> 1) & 3;
+      else
+        x = (r >> 2) & 3;
     } else if constexpr (CPR == 8) {
       if constexpr (FP8)
         x = (r & 7) ^ ((r >> 3) & 1);
@@ -221,7 +229,7 @@ __device__ inline typename FragOf<C::FP8>::T load_frag(const lds_char* base, int
     const int r = x0 + lane % C::MT;
     const int k = kbase + (lane / C::MT) * C::KPL;
     const int c = k * C::ES / 16;
-    const int s = sw_on ? swz<true, C::FP8, CPR>(r) : 0;
+    const int s = sw_on ? swz<true, C::FP8, CPR, C::MT>(r) : 0;
     if constexpr (!C::FP8) {
       const uint32_t off = r * RB + ((c ^ s) << 4);
       f = *LDS_PTR(bf16x8, base, off);
@@ -250,7 +258,7 @@ __device__ inline typename FragOf<C::FP8>::T load_frag(const lds_char* base, int
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int k = k0 + e;
-      const int sw = sw_on ? swz<false, false, CPR>(k) : 0;
+      const int sw = sw_on ? swz<false, false, CPR, C::MT>(k) : 0;
       const uint32_t off = k * RB + ((((xb >> 4) ^ sw) << 4) | (xb & 15));
       all[e] = *LDS_PTR(uint16_t, base, off);
     }
@@ -268,7 +276,7 @@ __device__ inline typename FragOf<C::FP8>::T load_frag(const lds_char* base, int
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int k = kbase + kgrp * C::KPL + h * E + s / LPR;
-        const int sw = sw_on ? swz<false, false, CPR>(k) : 0;
+        const int sw = sw_on ? swz<false, false, CPR, C::MT>(k) : 0;
         const uint32_t off = k * RB + ((((xb >> 4) ^ sw) << 4) | (xb & 15));
         s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, base, off));
         part[h] = __builtin_bit_cast(u16x4, v);
@@ -282,7 +290,7 @@ __device__ inline typename FragOf<C::FP8>::T load_frag(const lds_char* base, int
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         const int k = kbase + kgrp * C::KPL + h * E + s / LPR;
-        const int sw = sw_on ? swz<false, true, CPR>(k) : 0;
+        const int sw = sw_on ? swz<false, true, CPR, C::MT>(k) : 0;
         const uint32_t off = k * RB + ((((xb >> 4) ^ sw) << 4) | (xb & 15));
         part[h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, base, off));
       }
@@ -329,7 +337,6 @@ __device__ __forceinline__ void interleave() {
 // 16 E4M3 values -> 16 bf16 values (exact: every E4M3 number, subnormals included, is
 // a bf16 number) with the gfx950 packed conversion at unit scale.
 __device__ inline void widen_e4m3(const i32x4& v, i32x4& lo, i32x4& hi, float scale = 1.0f) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   int w[8];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {

@@ -81,7 +81,7 @@ int64_t split_kt(const Policy& p, int64_t K, int splits) {
 
 bool split_allowed(const Policy& p, const Problem& pr, int splits, int64_t ws_floats) {
   if (splits == 1) return true;
-  if (p.pipe != 1 || split_kt(p, pr.K, splits) == 0) return false;  // direct-to-LDS kernels
+  if (p.pipe != 1 || split_kt(p, pr.K, splits) == 0) return false;  // direct-to-LDS ring kernels
   return split_ws_floats(p, pr, splits) <= ws_floats;
 }
 

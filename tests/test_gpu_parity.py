@@ -28,7 +28,8 @@ BF16_DMA_POLICIES = ["bf16_dma_m256n256k32_w2x4_mt32_s4", "bf16_dma_m256n256k32_
                      "bf16_dma_m128n128k64_w2x4_mt16_s2", "bf16_dma_m128n128k64_w2x4_mt16_s3",
                      "bf16_dma_m128n128k64_w2x4_mt16_s4_rd0", "bf16_dma_m128n128k64_w2x4_mt16_s4_noswz",
                      "bf16_dma_m256n256k64_w2x4_mt16_s2_rd0", "bf16_dma_m256n256k64_w2x4_mt16_s2_noswz"]
-BF16_POLICIES = BF16_DMA_POLICIES + ["bf16_m256n256k64_w2x2_mt32_s2", "bf16_m256n256k64_w2x4_mt32_s2",
+PP_POLICIES = ["bf16_pp_m256n256k64_w2x4_mt16_s2", "bf16_pp_m256n256k32_w2x4_mt16_s4"]
+BF16_POLICIES = BF16_DMA_POLICIES + PP_POLICIES + ["bf16_m256n256k64_w2x2_mt32_s2", "bf16_m256n256k64_w2x4_mt32_s2",
                  "bf16_m256n128k64_w2x2_mt32_s2", "bf16_m128n256k64_w2x2_mt32_s2",
                  "bf16_m128n128k64_w2x2_mt32_s2", "bf16_m128n128k64_w2x2_mt16_s2",
                  "bf16_m64n64k64_w2x2_mt16_s2", "bf16_m256n256k64_w2x2_mt32_s2_noswz",
@@ -229,7 +230,8 @@ def test_data_movement_variants_bitwise_equal(gpu):
     outs = [run_gpu(gpu, p, data, policy=pol) for pol in
             ["bf16_m256n256k64_w2x2_mt32_s2", "bf16_m256n256k64_w2x2_mt32_s2_noswz",
              "bf16_m256n256k64_w2x2_mt32_s2_noxcd", "bf16_m256n256k64_w2x4_mt32_s2",
-             "bf16_m128n128k64_w2x2_mt32_s2"] + [p for p in BF16_DMA_POLICIES if "krot" not in p and "mt16" not in p]]
+             "bf16_m128n128k64_w2x2_mt32_s2"] +
+            [p for p in BF16_DMA_POLICIES if "krot" not in p and "mt16" not in p]]
     for o in outs[1:]:
         assert np.array_equal(outs[0], o)
 
@@ -244,7 +246,8 @@ def test_data_movement_variants_bitwise_equal_16x16(gpu):
             "bf16_dma_m128n128k64_w2x4_mt16_s2", "bf16_dma_m128n128k64_w2x4_mt16_s3",
             "bf16_dma_m128n128k64_w2x4_mt16_s4", "bf16_dma_m128n128k64_w2x4_mt16_s4_rd0",
             "bf16_dma_m128n128k64_w2x4_mt16_s4_noswz", "bf16_m128n128k64_w2x4_mt16_s2",
-            "bf16_dma_m64n64k64_w2x2_mt16_s4", "bf16_m64n64k64_w2x2_mt16_s2"]
+            "bf16_dma_m64n64k64_w2x2_mt16_s4", "bf16_m64n64k64_w2x2_mt16_s2",
+            "bf16_pp_m256n256k32_w2x4_mt16_s4", "bf16_pp_m256n256k64_w2x4_mt16_s2"]
     outs = [run_gpu(gpu, p, data, policy=pol) for pol in pols]
     for pol, o in zip(pols[1:], outs[1:]):
         assert np.array_equal(outs[0], o), pol
