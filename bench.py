@@ -154,14 +154,24 @@ def time_headline(g, p: gi.Gemm, warmup: int, steps: int, data):
             "C": C}
 
 
-def _sclk_files():
-    import glob
-    return sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+def _sclk_files(device: int = 0):
+    """The sysfs pp_dpm_sclk file of the GPU that HIP calls `device`, found by its PCI
+    address (the host may list other GPUs, which this process does not see, before it);
+    empty when there is none."""
+    import os
+    import torch
+    try:
+        pr = torch.cuda.get_device_properties(device)
+        addr = "%04x:%02x:%02x.0" % (pr.pci_domain_id, pr.pci_bus_id, pr.pci_device_id)
+    except (AttributeError, RuntimeError, AssertionError):
+        return []
+    f = os.path.join("/sys/bus/pci/devices", addr, "pp_dpm_sclk")
+    return [f] if os.path.exists(f) else []
 
 
 def gpu_clock_mhz(files=None):
-    """Current shader clock (MHz) of the first GPU the kernel driver lists, from sysfs
-    pp_dpm_sclk (the level marked '*'); None where it cannot be read."""
+    """Current shader clock (MHz) of the GPU, from its sysfs pp_dpm_sclk (the level marked
+    '*'); None where it cannot be read."""
     for f in files if files is not None else _sclk_files():
         try:
             for line in open(f):
@@ -178,7 +188,7 @@ class ClockSampler:
 
     def __init__(self, period_s: float = 0.0005):
         import threading
-        self.files = _sclk_files()[:1]
+        self.files = _sclk_files()
         self.period = period_s
         self.samples = []
         self._stop = threading.Event()
@@ -205,7 +215,8 @@ class ClockSampler:
         if not self.samples:
             return None
         v = np.array(self.samples)
-        return {"samples": int(v.size), "median": int(np.median(v)), "min": int(v.min()), "max": int(v.max())}
+        return {"samples": int(v.size), "median": int(np.median(v)), "min": int(v.min()), "max": int(v.max()),
+                "source": self.files[0]}
 
 
 def build_info():

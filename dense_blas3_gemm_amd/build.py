@@ -38,14 +38,29 @@ FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-ta
          "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC]
 
 
+def _deps(path: str, seen=None) -> set:
+    """The file and the local headers it includes, recursively (quoted includes found in
+    csrc/ or include/)."""
+    import re
+    seen = set() if seen is None else seen
+    if path in seen or not os.path.exists(path):
+        return seen
+    seen.add(path)
+    for inc in re.findall(r'^\s*#\s*include\s+"([^"]+)"', open(path).read(), re.M):
+        for d in (CSRC, INCLUDE):
+            cand = os.path.join(d, inc)
+            if os.path.exists(cand):
+                _deps(cand, seen)
+                break
+    return seen
+
+
 def _stale(src: str, obj: str) -> bool:
-    """An object is stale when it is older than its source or any header of csrc/ and include/."""
+    """An object is stale when it is older than its source or a header the source includes."""
     if not os.path.exists(obj):
         return True
     t = os.path.getmtime(obj)
-    deps = [os.path.join(CSRC, src)] + [os.path.join(d, f) for d in (CSRC, INCLUDE) for f in os.listdir(d)
-                                        if f.endswith((".h", ".inc"))]
-    return any(os.path.getmtime(d) > t for d in deps)
+    return any(os.path.getmtime(d) > t for d in _deps(os.path.join(CSRC, src)))
 
 
 def _compile(entry, incremental: bool = False) -> str:

@@ -83,7 +83,8 @@ struct Policy {
   int in_mode;     // 0: bf16 in, bf16 MFMA; 1: E4M3 in, widened to bf16 in LDS (exact
                    // fp32 accumulation); 2: E4M3 in, native f8f6f4 MFMA; 3: block-scaled
                    // E4M3 (MXFP8), widened with its scale; 4: block-scaled E4M3 on the
-                   // scaled f8f6f4 MFMA; -1: any (generic)
+                   // scaled f8f6f4 MFMA; 5: E4M3 in, E4M3 in LDS, widened to bf16 in
+                   // registers (ping-pong kernel); -1: any (generic)
   int BM, BN, BK;  // workgroup tile
   int WM, WN;      // waves along M and N
   int MT;          // MFMA block edge (32 or 16)
@@ -94,6 +95,7 @@ struct Policy {
   int threads;
   float efficiency;  // relative per-CU throughput used by the wave-time model
   int k_contig_only;  // serves only A [M][K] with B [N][K] (transA = 0, transB = 1)
+  int a_kc_only;      // serves only A [M][K] (transA = 0)
 };
 
 // Launchers (one per kernel family).  They return hipSuccess or the launch error.

@@ -60,6 +60,54 @@ __device__ __forceinline__ void pp_load_to_lds(uint32_t lds_base, uint32_t voff,
       : "memory");
 }
 
+// N copies of 1 KiB from one buffer into the LDS blocks at l, l + 1024, ... in one
+// statement (M0 saved once, written before each load, one wait state after each write).
+// TAIL only changes the statement's text (a ragged-K tile), so that the compiler keeps the
+// full-tile and the ragged-tile forms apart instead of merging them with per-copy selects.
+template <int N, bool TAIL>
+__device__ __forceinline__ void pp_copies(uint32_t l, const uint32_t (&o)[N], __amdgpu_buffer_rsrc_t r) {
+  uint32_t saved;
+  if constexpr (N == 1) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0 ; %4"
+        : "=&s"(saved)
+        : "s"(l), "v"(o[0]), "s"(r), "i"(TAIL ? 1 : 0)
+        : "memory");
+  } else if constexpr (N == 2) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %4, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %3, %4, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0 ; %5"
+        : "=&s"(saved)
+        : "s"(l), "v"(o[0]), "v"(o[1]), "s"(r), "i"(TAIL ? 1 : 0)
+        : "memory");
+  } else if constexpr (N == 3) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %5, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %3, %5, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %4, %5, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0 ; %6"
+        : "=&s"(saved)
+        : "s"(l), "v"(o[0]), "v"(o[1]), "v"(o[2]), "s"(r), "i"(TAIL ? 1 : 0)
+        : "memory");
+  } else {
+    static_assert(N == 4, "1 to 4 copies per statement");
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %6, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %3, %6, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %4, %6, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %5, %6, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0 ; %7"
+        : "=&s"(saved)
+        : "s"(l), "v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "s"(r), "i"(TAIL ? 1 : 0)
+        : "memory");
+  }
+}
+
 // Waits for this wave's LDS reads only (its copies stay in flight), then the barrier.
 __device__ __forceinline__ void pp_wait_lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -74,7 +122,10 @@ template <class C>
 struct PingPong {
   static_assert(C::THREADS == 512 && C::WM == 2 && C::WN == 4, "two groups of four waves");
   static_assert(C::STAGES >= 2 && C::STAGES <= 5, "two to five LDS slots");
-  static_assert(C::IN == IN_BF16 && C::GES == C::ES, "bf16 operands, LDS holds the global format");
+  static_assert((C::IN == IN_BF16 || C::IN == IN_E4M3_LDS) && C::GES == C::ES,
+                "bf16 or E4M3 operands, LDS holds the global format");
+  static_assert(C::IN != IN_E4M3_LDS || C::MT == 16, "E4M3 tiles feed the 16x16x32 fragment map");
+  static constexpr bool E8 = C::IN == IN_E4M3_LDS;  // E4M3 bytes in LDS, widened after each read
   static constexpr int NW = 8, S = C::STAGES;
   static_assert(C::A_BYTES % (1024 * NW) == 0 && C::B_BYTES % (1024 * NW) == 0,
                 "each wave copies whole 1 KiB blocks of both tiles");
@@ -82,22 +133,55 @@ struct PingPong {
   static constexpr int B_IPW = C::B_BYTES / 1024 / NW;
   static constexpr int IPW = A_IPW + B_IPW;
   static_assert((S - 1) * IPW <= 63, "vmcnt range");
+  static_assert((C::A_KC || (C::A_CPR & (C::A_CPR - 1)) == 0) && (C::B_KC || (C::B_CPR & (C::B_CPR - 1)) == 0),
+                "M/N-contiguous rows of a power of two of chunks (the XOR swizzle stays in the row)");
   static constexpr int NMF = C::FM * C::FN * C::KSTEPS;  // MFMAs per wave per K tile
   static_assert(NMF >= IPW, "one copy per MFMA at most");
   // LDS: the A tiles of the S slots, then the B tiles
   static constexpr int A_OFF = 0, B_OFF = S * C::A_BYTES;
   static constexpr int LDS_BYTES = S * (C::A_BYTES + C::B_BYTES);
-  // LDS reads per fragment (transposing reads take two 8-byte reads per bf16 fragment)
-  static constexpr int A_RD = C::A_KC ? 1 : 2, B_RD = C::B_KC ? 1 : 2;
+  // LDS reads per fragment (transposing bf16 reads take two 8-byte reads per fragment; an
+  // E4M3 fragment is 8 bytes, one read either way)
+  static constexpr int A_RD = (C::A_KC || E8) ? 1 : 2, B_RD = (C::B_KC || E8) ? 1 : 2;
 };
+
+// XOR swizzle of the 16-byte chunk index of LDS row r.  bf16 tiles use the shared layout
+// (swz).  E4M3 tiles are read 8 bytes per lane; measured conflict-free with the LDS bank
+// counter on gfx950: K-contiguous rows (ds_read_b64) xor by (r >> 2) for 64-byte rows and
+// (r >> 1) for 128-byte rows, M/N-contiguous rows (ds_read_b64_tr_b8) by the row itself.
+template <class C, bool KC, int CPR>
+__device__ __forceinline__ int pp_swz(int r) {
+  if constexpr (C::IN == IN_E4M3_LDS) {
+    if constexpr (KC)
+      return (r >> (CPR == 4 ? 2 : 1)) & (CPR - 1);
+    else
+      return r & (CPR - 1);
+  } else {
+    return swz<KC, false, CPR, C::MT>(r);
+  }
+}
 
 // Byte offset, inside one operand tile in LDS, of this lane's part of fragment read h of
 // the MT-row block starting at x0 (M or N index) and K step starting at kbase: the
-// addresses that load_frag computes, for bf16 tiles in the XOR-swizzled layout.
+// addresses that load_frag computes for bf16 tiles in the XOR-swizzled layout, and the
+// 8-byte reads of E4M3 tiles (lane l: row or column l % 16, K values 8 (l / 16) .. + 7).
 template <class C, bool KC, int RB>
 __device__ __forceinline__ uint32_t pp_frag_off(int x0, int kbase, int lane, int h) {
   constexpr int CPR = RB / 16;
-  if constexpr (KC) {
+  if constexpr (C::IN == IN_E4M3_LDS) {
+    if constexpr (KC) {
+      const int r = x0 + lane % 16;
+      const int kb = kbase + (lane / 16) * 8;  // bytes = elements
+      return (uint32_t)(r * RB + ((((kb >> 4) ^ pp_swz<C, true, CPR>(r)) << 4) | (kb & 15)));
+    } else {
+      // ds_read_b64_tr_b8: within each group of 16 lanes, lane t gives row t / 2 of eight and
+      // the 8 bytes at column (t % 2) * 8 of a 16-column block; lane i receives column i
+      const int g = lane >> 4, t = lane & 15;
+      const int k = kbase + g * 8 + t / 2;
+      const int xb = x0 + (t % 2) * 8;
+      return (uint32_t)(k * RB + ((((xb >> 4) ^ pp_swz<C, false, CPR>(k)) << 4) | (xb & 15)));
+    }
+  } else if constexpr (KC) {
     const int r = x0 + lane % C::MT;
     const int c = (kbase + (lane / C::MT) * C::KPL) * 2 / 16;
     return (uint32_t)(r * RB + ((c ^ swz<true, false, CPR, C::MT>(r)) << 4));
@@ -109,6 +193,16 @@ __device__ __forceinline__ uint32_t pp_frag_off(int x0, int kbase, int lane, int
     const int k = kbase + kgrp * C::KPL + h * 4 + s / 4;
     return (uint32_t)(k * RB + ((((xb >> 4) ^ swz<false, false, CPR, C::MT>(k)) << 4) | (xb & 15)));
   }
+}
+
+// 8 E4M3 values (bytes in K order) -> 8 bf16 values, exactly (every E4M3 number, subnormals
+// included, is a bf16 number), with the gfx950 packed conversion at unit scale.
+__device__ __forceinline__ bf16x8 pp_widen8(i32x2 v) {
+  const int w0 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, false));
+  const int w1 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, true));
+  const int w2 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, false));
+  const int w3 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, true));
+  return __builtin_bit_cast(bf16x8, (i32x4){w0, w1, w2, w3});
 }
 
 template <class C>
@@ -130,68 +224,82 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
 
   const uint32_t a_rows = C::A_KC ? a.M : a.K;
   const uint32_t b_rows = C::B_KC ? a.N : a.K;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, (uint32_t)(a_rows * a.lda * C::ES));
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.B, (uint32_t)(b_rows * a.ldb * C::ES));
 
   // ---- this wave's copy instructions: instruction i fills LDS block wave*IPW + i of the
   // tile (A blocks, then B); this lane fills chunk p = blk*64 + lane of its operand, row
   // p / CPR, physical chunk p % CPR, which holds logical chunk (p % CPR) ^ swizzle(row).
-  // A chunk in a row or column past M or N gets an offset past every buffer (adding K
-  // tiles keeps it there: each operand spans less than 2^31 bytes).  For a K-contiguous
-  // operand the chunk's K index within the tile is kept: chunks past K read zeros.
-  uint32_t a_goff[P::A_IPW], b_goff[P::B_IPW];
-  int a_kc[P::A_IPW], b_kc[P::B_IPW];
+  // The per-lane offsets are relative to the start of a K tile, and fixed: each K tile
+  // gets its own buffer descriptor (base moved to the tile, size cut by as much), built
+  // with scalar arithmetic.  A chunk in a row or column past M or N gets an offset past
+  // every buffer.  Rows past K of an M/N-contiguous operand then lie past the tile's
+  // buffer and read zeros; a K-contiguous operand's chunks past K (a ragged last tile, or
+  // a tile past the end) are sent past the buffer in copy_tile.
+  uint32_t a_off[P::A_IPW], b_off[P::B_IPW];
+  auto chunk_k = [&](int blk, int CPR, int VEC, auto swzc) {  // K index of a K-contiguous chunk
+    const int p = blk * 64 + lane;
+    return ((p % CPR) ^ swzc(p / CPR)) * VEC;
+  };
 #pragma unroll
   for (int i = 0; i < P::A_IPW; ++i) {
     const int p = (wave * P::A_IPW + i) * 64 + lane;
     const int r = p / C::A_CPR;
-    const int c = (p % C::A_CPR) ^ swz<C::A_KC, false, C::A_CPR, C::MT>(r);
+    const int c = (p % C::A_CPR) ^ pp_swz<C, C::A_KC, C::A_CPR>(r);
     if constexpr (C::A_KC)
-      a_goff[i] = (m0 + r) < a.M ? (uint32_t)((m0 + r) * a.lda + c * C::VEC) * C::ES : kOOB;
+      a_off[i] = (m0 + r) < a.M ? (uint32_t)((m0 + r) * a.lda + c * C::VEC) * C::ES : kOOB;
     else
-      a_goff[i] = (m0 + c * C::VEC) < a.M ? (uint32_t)(r * a.lda + m0 + c * C::VEC) * C::ES : kOOB;
-    a_kc[i] = c * C::VEC;
+      a_off[i] = (m0 + c * C::VEC) < a.M ? (uint32_t)(r * a.lda + m0 + c * C::VEC) * C::ES : kOOB;
   }
 #pragma unroll
   for (int i = 0; i < P::B_IPW; ++i) {
     const int p = (wave * P::B_IPW + i) * 64 + lane;
     const int r = p / C::B_CPR;
-    const int c = (p % C::B_CPR) ^ swz<C::B_KC, false, C::B_CPR, C::MT>(r);
+    const int c = (p % C::B_CPR) ^ pp_swz<C, C::B_KC, C::B_CPR>(r);
     if constexpr (C::B_KC)
-      b_goff[i] = (n0 + r) < a.N ? (uint32_t)((n0 + r) * a.ldb + c * C::VEC) * C::ES : kOOB;
+      b_off[i] = (n0 + r) < a.N ? (uint32_t)((n0 + r) * a.ldb + c * C::VEC) * C::ES : kOOB;
     else
-      b_goff[i] = (n0 + c * C::VEC) < a.N ? (uint32_t)(r * a.ldb + n0 + c * C::VEC) * C::ES : kOOB;
-    b_kc[i] = c * C::VEC;
+      b_off[i] = (n0 + c * C::VEC) < a.N ? (uint32_t)(r * a.ldb + n0 + c * C::VEC) * C::ES : kOOB;
   }
+  // 32-bit offsets: every operand spans less than 2^31 bytes with 256 rows (of K for an
+  // M/N-contiguous operand) to spare, more than the S tiles issued past the end
   const uint32_t a_kstep = C::A_KC ? C::BK * C::ES : (uint32_t)(C::BK * a.lda * C::ES);
   const uint32_t b_kstep = C::B_KC ? C::BK * C::ES : (uint32_t)(C::BK * a.ldb * C::ES);
+  const uint32_t a_total = (uint32_t)(a_rows * a.lda * C::ES), b_total = (uint32_t)(b_rows * a.ldb * C::ES);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)lds;
   const int nk = (a.K + C::BK - 1) / C::BK;
 
-  // Copy instruction q (A blocks first, then B) of K tile kt into slot u.  Rows past K of
-  // an M/N-contiguous operand lie past its buffer and read zeros; a K-contiguous
-  // operand's chunks past K (the last tile's tail, or a tile past the end) are sent past
-  // the buffer here.  Tiles past the end are still issued, so that every wave has the
-  // same number of copies in flight at every barrier and the waits can count them.
-  auto copy_one = [&](int u, int kt, auto qc) {
-    constexpr int q = decltype(qc)::value;
+  // Copies of K tile kt into slot u: A blocks first, then B.  Tiles past the end are still
+  // issued (all their chunks read zeros), so that every wave has the same number of copies
+  // in flight at every barrier and the waits can count them.
+  auto copy_tile = [&](int u, int kt) {
+    const uint32_t ao = (uint32_t)kt * a_kstep, bo = (uint32_t)kt * b_kstep;
+    // the tile's buffer: base moved to the tile, size cut by as much (none left past the
+    // end).  The sizes go through readfirstlane: the saturating subtraction is a VALU
+    // instruction, and a descriptor built from a VGPR would not be a scalar operand.
+    const uint32_t an = __builtin_amdgcn_readfirstlane(a_total - min(ao, a_total));
+    const uint32_t bn = __builtin_amdgcn_readfirstlane(b_total - min(bo, b_total));
+    const __amdgpu_buffer_rsrc_t rta = make_rsrc((const char*)a.A + ao, an);
+    const __amdgpu_buffer_rsrc_t rtb = make_rsrc((const char*)a.B + bo, bn);
+    // this wave's first LDS block of each operand tile (its blocks are consecutive)
+    const uint32_t la = lds0 + P::A_OFF + u * C::A_BYTES + (uint32_t)(wave * P::A_IPW) * 1024u;
+    const uint32_t lb = lds0 + P::B_OFF + u * C::B_BYTES + (uint32_t)(wave * P::B_IPW) * 1024u;
     const int kleft = a.K - kt * C::BK;  // K elements left from this tile's start
-    if constexpr (q < P::A_IPW) {
-      uint32_t off = a_goff[q] + (uint32_t)kt * a_kstep;
-      if constexpr (C::A_KC) off = a_kc[q] < kleft ? off : kOOB;
-      pp_load_to_lds(__builtin_amdgcn_readfirstlane(lds0 + P::A_OFF + u * C::A_BYTES +
-                                                     (uint32_t)(wave * P::A_IPW + q) * 1024u),
-                     off, ra);
-    } else {
-      constexpr int i = q - P::A_IPW;
-      uint32_t off = b_goff[i] + (uint32_t)kt * b_kstep;
-      if constexpr (C::B_KC) off = b_kc[i] < kleft ? off : kOOB;
-      pp_load_to_lds(__builtin_amdgcn_readfirstlane(lds0 + P::B_OFF + u * C::B_BYTES +
-                                                     (uint32_t)(wave * P::B_IPW + i) * 1024u),
-                     off, rb);
+    if ((!C::A_KC && !C::B_KC) || kleft >= C::BK) {
+      pp_copies<P::A_IPW, false>(la, a_off, rta);
+      pp_copies<P::B_IPW, false>(lb, b_off, rtb);
+    } else {  // a ragged last tile or a tile past the end: K-contiguous chunks past K read zeros
+      uint32_t oa[P::A_IPW], ob[P::B_IPW];
+#pragma unroll
+      for (int q = 0; q < P::A_IPW; ++q)
+        oa[q] = !C::A_KC || chunk_k(wave * P::A_IPW + q, C::A_CPR, C::VEC,
+                                    [](int r) { return pp_swz<C, true, C::A_CPR>(r); }) < kleft ? a_off[q] : kOOB;
+#pragma unroll
+      for (int q = 0; q < P::B_IPW; ++q)
+        ob[q] = !C::B_KC || chunk_k(wave * P::B_IPW + q, C::B_CPR, C::VEC,
+                                    [](int r) { return pp_swz<C, true, C::B_CPR>(r); }) < kleft ? b_off[q] : kOOB;
+      pp_copies<P::A_IPW, true>(la, oa, rta);
+      pp_copies<P::B_IPW, true>(lb, ob, rtb);
     }
   };
-  auto copy_tile = [&](int u, int kt) { static_for<P::IPW>([&](auto qc) { copy_one(u, kt, qc); }); };
 
   Acc acc[C::FM][C::FN];
 #pragma unroll
@@ -229,13 +337,34 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
   };
 
   bf16x8 fa[C::FM], fb[C::FN];
+  // E4M3: the raw 8-byte A fragments, widened by the compute phase that uses them
+  i32x2 ra8[P::E8 ? C::FM : 1];
   auto rd = [&](uint32_t addr) -> u16x4 {
     return __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                          (__attribute__((address_space(3))) s16x4*)(uintptr_t)addr));
   };
-  // Memory phase: the fragments of K step kk of the tile in slot u.
+  auto rd8 = [&](uint32_t addr, bool tr) -> i32x2 {
+    if (tr) return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(uintptr_t)addr);
+    return *(__attribute__((address_space(3))) i32x2*)(uintptr_t)addr;
+  };
+  // Memory phase: the fragments of K step kk of the tile in slot u (E4M3 tiles: all reads
+  // first, then the widening, so that the reads are in flight together).
   auto read_step = [&](auto uc, auto kc) {
     constexpr int u = decltype(uc)::value, kk = decltype(kc)::value;
+    if constexpr (P::E8) {
+      // B fragments and the first A fragment are widened here; the other A fragments in
+      // the compute phase, between the MFMAs (the conversions share the issue port with
+      // the MFMAs of the wave computing next to this one)
+      i32x2 rb8[C::FN];
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) ra8[i] = rd8(a_addr(u, kk, i, 0), !C::A_KC);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) rb8[j] = rd8(b_addr(u, kk, j, 0), !C::B_KC);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) fb[j] = pp_widen8(rb8[j]);
+      fa[0] = pp_widen8(ra8[0]);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
       if constexpr (C::A_KC) {
@@ -255,12 +384,22 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
       }
     }
   };
-  // Compute phase: the MFMA cluster of one K step, at raised wave priority.
+  // Compute phase: the MFMA cluster of one K step, at raised wave priority.  With E4M3
+  // tiles the MFMAs of A row i are followed by the four conversions of A fragment i + 1.
+  static_assert(!P::E8 || C::FN == 4, "four conversions per A fragment, one after each MFMA of a row");
+  int wpart[4];
   auto compute_step = [&]() {
     __builtin_amdgcn_s_setprio(1);
     static_for<C::FM * C::FN>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      mma(acc[i / C::FN][i % C::FN], fb[i % C::FN], fa[i / C::FN]);
+      constexpr int row = i / C::FN, col = i % C::FN;
+      mma(acc[row][col], fb[col], fa[row]);
+      if constexpr (P::E8 && row + 1 < C::FM) {
+        wpart[col] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ra8[row + 1][col >> 1], 1.0f,
+                                                                                       (col & 1) != 0));
+        if constexpr (col == 3)
+          fa[row + 1] = __builtin_bit_cast(bf16x8, (i32x4){wpart[0], wpart[1], wpart[2], wpart[3]});
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
     __builtin_amdgcn_s_setprio(0);
@@ -297,16 +436,17 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
             compute_step();
             if constexpr (last) {
               pp_wait_vm_barrier<VM>();  // B(2h+1): tile t + 1 complete, slot u free
-              copy_tile(u, kt + S);
             } else {
               pp_wait_lds_barrier();  // B(2h+1)
             }
-            if (!last || kt + 1 < nk) {
+            // the fragment reads go out first, then the copies (whose issue can wait on a
+            // full address queue)
+            if (!last || kt + 1 < nk)
               read_step(std::integral_constant<int, last ? (u + 1) % S : u>{},
                         std::integral_constant<int, last ? 0 : kk + 1>{});
-              __builtin_amdgcn_sched_barrier(0);
-              pp_wait_lds_barrier();  // B(2h+2)
-            }
+            if constexpr (last) copy_tile(u, kt + S);
+            __builtin_amdgcn_sched_barrier(0);
+            if (!last || kt + 1 < nk) pp_wait_lds_barrier();  // B(2h+2)
           });
         }
       });
@@ -321,9 +461,9 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
           static_for<KS>([&](auto kc) {
             constexpr int kk = decltype(kc)::value;
             constexpr bool last = kk == KS - 1;
+            read_step(uc, kc);
             // the slot of tile t - 1, left by both groups at the last B(2h+1) of that tile
             if (kk == 0 && kt > 0) copy_tile((u + S - 1) % S, kt - 1 + S);
-            read_step(uc, kc);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (last) {
               pp_wait_vm_barrier<VM>();  // B(2h+1)
@@ -361,15 +501,19 @@ hipError_t launch_pp(const GemmArgs& a, hipStream_t s) {
 #define DBGEMM_PP_CAT2(a, b) launch_mfma_pp_##a##b
 #define DBGEMM_PP_CAT(a, b) DBGEMM_PP_CAT2(a, b)
 
-// pipe 2 entries of the policy table
+// pipe 2 entries of the policy table; a tile edge whose M/N-contiguous rows would not be
+// a power of two of chunks is not instantiated for that transpose case (the policy code
+// does not choose it there)
+constexpr bool pp_pow2(int x) { return (x & (x - 1)) == 0; }
+
 hipError_t DBGEMM_PP_CAT(DBGEMM_DMA_TA, DBGEMM_DMA_TB)(const Policy& p, const GemmArgs& a, hipStream_t s) {
 #define DBGEMM_SIMT(name, eff)
 #define DBGEMM_MFMA(name_, pipe_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_, eff_)        \
-  if constexpr (pipe_ == 2)                                                                                \
+  if constexpr (pipe_ == 2 && pp_pow2(DBGEMM_DMA_TA ? (bm_) : 16) && pp_pow2(DBGEMM_DMA_TB ? 16 : (bn_)))  \
     if (p.BM == bm_ && p.BN == bn_ && p.BK == bk_ && p.WM == wm_ && p.WN == wn_ && p.MT == mt_ &&          \
         p.stages == st_ && p.in_mode == in_)                                                               \
       return launch_pp<Cfg<bm_, bn_, bk_, wm_, wn_, mt_, st_, in_, DBGEMM_DMA_TA != 0, DBGEMM_DMA_TB != 0>>(a, s);
-#include "policies.inc"
+#include "policies_pp.inc"
 #undef DBGEMM_SIMT
 #undef DBGEMM_MFMA
   return hipErrorInvalidConfiguration;

@@ -35,9 +35,12 @@ __global__ __launch_bounds__(256) void lds_probe_kernel(LdsProbeOffsets offs, in
       } else if constexpr (KIND == 2) {
         int v;
         asm volatile("ds_read_u16 %0, %1" : "=v"(v) : "v"(a[j]) : "memory");
-      } else {
+      } else if constexpr (KIND == 3) {
         i32x2 v;
         asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(a[j]) : "memory");
+      } else {
+        i32x2 v;
+        asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(v) : "v"(a[j]) : "memory");
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -46,14 +49,15 @@ __global__ __launch_bounds__(256) void lds_probe_kernel(LdsProbeOffsets offs, in
 
 }  // namespace
 
-int lds_probe_width(int kind) { return kind == 0 ? 16 : kind == 2 ? 2 : kind == 1 || kind == 3 ? 8 : 0; }
+int lds_probe_width(int kind) { return kind == 0 ? 16 : kind == 2 ? 2 : kind == 1 || kind == 3 || kind == 4 ? 8 : 0; }
 
 hipError_t launch_lds_probe(int kind, const LdsProbeOffsets& offs, int iters, int workgroups, hipStream_t s) {
   switch (kind) {
     case 0: hipLaunchKernelGGL(lds_probe_kernel<0>, dim3(workgroups), dim3(256), 0, s, offs, iters); break;
     case 1: hipLaunchKernelGGL(lds_probe_kernel<1>, dim3(workgroups), dim3(256), 0, s, offs, iters); break;
     case 2: hipLaunchKernelGGL(lds_probe_kernel<2>, dim3(workgroups), dim3(256), 0, s, offs, iters); break;
-    default: hipLaunchKernelGGL(lds_probe_kernel<3>, dim3(workgroups), dim3(256), 0, s, offs, iters); break;
+    case 3: hipLaunchKernelGGL(lds_probe_kernel<3>, dim3(workgroups), dim3(256), 0, s, offs, iters); break;
+    default: hipLaunchKernelGGL(lds_probe_kernel<4>, dim3(workgroups), dim3(256), 0, s, offs, iters); break;
   }
   return hipGetLastError();
 }

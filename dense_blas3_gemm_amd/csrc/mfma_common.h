@@ -79,8 +79,10 @@ __device__ inline void tile_of(int bid, const GemmArgs& a, int& tm, int& tn, int
 // exactly to bf16 on their way into LDS, bf16 MFMA: full fp32 accumulation);
 // IN_E4M3_NATIVE (E4M3 operands fed to the f8f6f4 MFMA as they are); IN_MX (E4M3
 // operands with a UE8M0 scale per 32 along K, widened to bf16 times their scale);
-// IN_MX_NATIVE (the same operands on the scaled f8f6f4 MFMA, which applies the scales).
-enum { IN_BF16 = 0, IN_E4M3 = 1, IN_E4M3_NATIVE = 2, IN_MX = 3, IN_MX_NATIVE = 4 };
+// IN_MX_NATIVE (the same operands on the scaled f8f6f4 MFMA, which applies the scales);
+// IN_E4M3_LDS (E4M3 operands kept as E4M3 bytes in LDS and widened exactly to bf16 in
+// registers after each fragment read, bf16 MFMA: the ping-pong kernel).
+enum { IN_BF16 = 0, IN_E4M3 = 1, IN_E4M3_NATIVE = 2, IN_MX = 3, IN_MX_NATIVE = 4, IN_E4M3_LDS = 5 };
 
 // READ_: 1 reads M/N-contiguous fragments with the transposing ds_read_b64_tr_*; 0 reads
 // them one element at a time (ds_read_u16), the plain-load rung of the read ablation.
@@ -96,7 +98,7 @@ struct Cfg {
   static constexpr bool FP8 = IN == IN_E4M3_NATIVE || MXN;  // fragments and MFMA are E4M3
   static constexpr int THREADS = WM * WN * 64;
   static constexpr int GES = IN == IN_BF16 ? 2 : 1;  // bytes per element in global memory
-  static constexpr int ES = FP8 ? 1 : 2;             // bytes per element in LDS and fragments
+  static constexpr int ES = (FP8 || IN == IN_E4M3_LDS) ? 1 : 2;  // bytes per element in LDS
   static constexpr int WIDEN = ES / GES;             // LDS chunks per global 16-byte chunk
   static constexpr int VEC = 16 / GES;               // elements per global 16-byte chunk
   static constexpr int WTM = BM / WM, WTN = BN / WN;

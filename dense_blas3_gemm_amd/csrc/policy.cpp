@@ -14,11 +14,12 @@ namespace dbgemm {
 namespace {
 
 const Policy kTable[] = {
-#define DBGEMM_SIMT(name_, eff_) {name_, KIND_SIMT, 0, -1, 64, 64, 16, 1, 1, 0, 1, 1, 0, 1, 0, 0, 1, 256, eff_, 0},
+#define DBGEMM_SIMT(name_, eff_) {name_, KIND_SIMT, 0, -1, 64, 64, 16, 1, 1, 0, 1, 1, 0, 1, 0, 0, 1, 256, eff_, 0, 0},
 #define DBGEMM_MFMA(name_, pipe_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_, eff_) \
   {name_, KIND_MFMA, pipe_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, (sw_) & 1,        \
-   ((sw_) >> 1) & 1, ((sw_) >> 2) & 1 ? 0 : 1, (wm_) * (wn_) * 64, eff_, ((sw_) >> 3) & 1},
+   ((sw_) >> 1) & 1, ((sw_) >> 2) & 1 ? 0 : 1, (wm_) * (wn_) * 64, eff_, ((sw_) >> 3) & 1, ((sw_) >> 4) & 1},
 #include "policies.inc"
+#include "policies_pp.inc"
 #undef DBGEMM_SIMT
 #undef DBGEMM_MFMA
 };
@@ -27,7 +28,7 @@ constexpr int kCount = sizeof(kTable) / sizeof(kTable[0]);
 // Resident workgroups per CU: bounded by LDS (160 KiB) and by the unified register
 // file (512 registers per lane per SIMD shared by the waves on that SIMD).
 int occupancy(const Policy& p) {
-  const int es = (p.in_mode == 2 || p.in_mode == 4) ? 1 : 2;  // bytes per element in LDS
+  const int es = (p.in_mode == 2 || p.in_mode == 4 || p.in_mode == 5) ? 1 : 2;  // bytes per element in LDS
   const int lds = p.stages * (p.BM + p.BN) * p.BK * es;
   const int staging = p.pipe == 0 ? (p.BM + p.BN) * p.BK * (p.in_mode == 0 ? 2 : 1) / (p.WM * p.WN * 64) / 4 : 0;
   int occ_lds = (160 * 1024) / lds;
@@ -58,10 +59,11 @@ bool policy_serves(const Policy& p, const Problem& pr) {
   if (p.kind == KIND_SIMT) return true;
   if (p.kind != KIND_MFMA || !pr.fast_ok) return false;
   if (p.k_contig_only && (pr.transA != 0 || pr.transB != 1)) return false;
+  if (p.a_kc_only && pr.transA != 0) return false;
   if (pr.mx) return p.in_mode == 3 || (p.in_mode == 4 && pr.mx_words);
   if (pr.blas3)  // triangle, K band or dual product: the bf16 direct-to-LDS kernels
     return p.pipe == 1 && p.in_mode == 0 && !pr.in_fp8 && (!pr.square_tiles || p.BM == p.BN);
-  return p.in_mode < 3 && (p.in_mode != 0) == (pr.in_fp8 != 0);
+  return (p.in_mode < 3 || p.in_mode == 5) && (p.in_mode != 0) == (pr.in_fp8 != 0);
 }
 
 int64_t split_ws_floats(const Policy& p, const Problem& pr, int splits) {

@@ -182,7 +182,8 @@ gemm_status_t gemm_set_policy(gemm_handle_t h, const char* name);
  * fills a 64 KiB LDS array, then every lane repeats `iters` times: 8 reads of one kind
  * at LDS byte offsets offsets[j*64 + (lane % 64)], j = 0..7 (a host array of 512
  * values, copied at the call), then a wait for them.  kind: 0 ds_read_b128 (16 bytes),
- * 1 ds_read_b64_tr_b16 (8), 2 ds_read_u16 (2), 3 ds_read_b64 (8).  Each offset must be a
+ * 1 ds_read_b64_tr_b16 (8), 2 ds_read_u16 (2), 3 ds_read_b64 (8), 4 ds_read_b64_tr_b8 (8).
+ * Each offset must be a
  * multiple of the width and at most 65536 - width, else INVALID_VALUE (nothing is
  * launched).  Time it with events around the call; it writes no memory. */
 gemm_status_t gemm_lds_probe(gemm_handle_t h, int kind, const uint32_t* offsets, int iters,

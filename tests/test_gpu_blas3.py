@@ -230,6 +230,15 @@ def _int_system(n, M, N, side, uplo, transA, unit, seed):
     return A, Xt, gi.f32_to_bf16_bits(Bv.astype(np.float32))
 
 
+def _report(res):
+    """Prints the achieved backward error beside the floor of one bf16 rounding of the exact
+    solution, so a run with -s shows how far the solve is from its bound."""
+    import os
+    print("trsm %s eta=%.3e eta_round=%.3e ratio=%.2f bound=%.3e forward=%.3e kappa=%.1f" % (
+        os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0], res["eta"], res["eta_round"],
+        res["eta"] / max(res["eta_round"], 1e-300), res["eta_bound"], res["forward"], res["kappa"]))
+
+
 @pytest.mark.parametrize("M,N", [(512, 264), (300, 136), (136, 300)])
 @pytest.mark.parametrize("side", [LEFT, RIGHT])
 @pytest.mark.parametrize("uplo", [LOWER, UPPER])
@@ -266,6 +275,7 @@ def test_trsm_real(gpu, M, N, side, uplo, transA, unit):
     T = blas3.triangular(A, n, uplo, unit)
     opT = T.T if transA else T
     res = tolerance.trsm_check(X, X_ref, opT, alpha * tolerance.bf16_bits_to_f64(B), side, n)
+    _report(res)
     assert res["ok"], res
 
 
@@ -294,6 +304,7 @@ def test_trsm_4096_sampled_columns(gpu):
     X_ref = blas3.trsm(LEFT, LOWER, 0, 0, M, len(cols), 1.0, A, Bs)
     T = blas3.triangular(A, M, LOWER, 0)
     res = tolerance.trsm_check(X[:, cols], X_ref, T, tolerance.bf16_bits_to_f64(Bs), LEFT, M)
+    _report(res)
     assert res["ok"], res
     assert np.isfinite(X).all()
 
@@ -421,6 +432,7 @@ def test_blas3_strided_operands(gpu):
     X_ref = blas3.trsm(LEFT, UPPER, 1, 0, M2, N2, 1.0, T, B2)
     opT = blas3.triangular(T, M2, UPPER, 0).T
     res = tolerance.trsm_check(X, X_ref, opT, tolerance.bf16_bits_to_f64(B2), LEFT, M2)
+    _report(res)
     assert res["ok"], res
 
 
@@ -488,6 +500,7 @@ def test_blas3_tiny(gpu, M, N):
     X_ref = blas3.trsm(LEFT, LOWER, 0, 0, M, N, 2.0, T, Bm)
     res = tolerance.trsm_check(X, X_ref, blas3.triangular(T, M, LOWER, 0), 2.0 * tolerance.bf16_bits_to_f64(Bm),
                                LEFT, M)
+    _report(res)
     assert res["ok"], res
 
 

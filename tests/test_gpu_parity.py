@@ -28,14 +28,18 @@ BF16_DMA_POLICIES = ["bf16_dma_m256n256k32_w2x4_mt32_s4", "bf16_dma_m256n256k32_
                      "bf16_dma_m128n128k64_w2x4_mt16_s2", "bf16_dma_m128n128k64_w2x4_mt16_s3",
                      "bf16_dma_m128n128k64_w2x4_mt16_s4_rd0", "bf16_dma_m128n128k64_w2x4_mt16_s4_noswz",
                      "bf16_dma_m256n256k64_w2x4_mt16_s2_rd0", "bf16_dma_m256n256k64_w2x4_mt16_s2_noswz"]
-PP_POLICIES = ["bf16_pp_m256n256k64_w2x4_mt16_s2", "bf16_pp_m256n256k32_w2x4_mt16_s4"]
+PP_POLICIES = ["bf16_pp_m256n256k32_w2x4_mt16_s4", "bf16_pp_m256n256k64_w2x4_mt16_s2",
+               "bf16_pp_m192n256k64_w2x4_mt16_s2"]
 BF16_POLICIES = BF16_DMA_POLICIES + PP_POLICIES + ["bf16_m256n256k64_w2x2_mt32_s2", "bf16_m256n256k64_w2x4_mt32_s2",
                  "bf16_m256n128k64_w2x2_mt32_s2", "bf16_m128n256k64_w2x2_mt32_s2",
                  "bf16_m128n128k64_w2x2_mt32_s2", "bf16_m128n128k64_w2x2_mt16_s2",
                  "bf16_m64n64k64_w2x2_mt16_s2", "bf16_m256n256k64_w2x2_mt32_s2_noswz",
                  "bf16_m128n128k64_w2x4_mt16_s2", "bf16_m256n256k64_w2x4_mt16_s2",
                  "bf16_m256n256k64_w2x2_mt32_s2_noxcd"]
-FP8_POLICIES = ["e4m3_m256n256k64_w2x2_mt32_s2", "e4m3_m256n256k64_w2x4_mt32_s2",
+# 192-row tiles: an M-contiguous A would give LDS rows of 24 chunks, not a power of two
+A_KC_ONLY = {"bf16_pp_m192n256k64_w2x4_mt16_s2"}
+FP8_PP_POLICIES = ["e4m3_pp_m256n256k128_w2x4_mt16_s2", "e4m3_pp_m256n256k64_w2x4_mt16_s4"]
+FP8_POLICIES = FP8_PP_POLICIES + ["e4m3_m256n256k64_w2x2_mt32_s2", "e4m3_m256n256k64_w2x4_mt32_s2",
                 "e4m3_m256n256k64_w2x4_mt16_s2", "e4m3_m128n128k64_w2x4_mt16_s2",
                 "e4m3_m128n128k64_w2x2_mt32_s2", "e4m3_m64n64k64_w2x2_mt16_s2"]
 FP8_NATIVE_POLICIES = ["e4m3native_dma_m256n256k128_w2x4_mt32_s2", "e4m3native_m256n256k128_w2x2_mt32_s2", "e4m3native_m256n256k128_w2x4_mt32_s2",
@@ -64,9 +68,15 @@ def test_gemm_256_fp32_output(gpu):
 @pytest.mark.parametrize("tA,tB", TRANS)
 @pytest.mark.parametrize("policy", BF16_POLICIES + ["simt_generic", None])
 def test_bf16_policies_transposes(gpu, policy, tA, tB):
-    """Every bf16 policy on every transpose case, over several tiles and a ragged edge."""
+    """Every bf16 policy on every transpose case, over several tiles and a ragged edge (a
+    policy that serves only A [M][K] refuses a transposed A)."""
+    import dense_blas3_gemm_amd as d
     p = gi.Gemm("t", 328, 296, 200, transA=tA, transB=tB, dist="normal")
     data = p.make()
+    if policy in A_KC_ONLY and tA:
+        with pytest.raises(d.GemmError, match="NOT_SUPPORTED"):
+            run_gpu(gpu, p, data, policy=policy)
+        return
     C = run_gpu(gpu, p, data, policy=policy)
     _assert_ok(compare(p, data, C), f"{policy} {tA}{tB}")
 
@@ -247,7 +257,8 @@ def test_data_movement_variants_bitwise_equal_16x16(gpu):
             "bf16_dma_m128n128k64_w2x4_mt16_s4", "bf16_dma_m128n128k64_w2x4_mt16_s4_rd0",
             "bf16_dma_m128n128k64_w2x4_mt16_s4_noswz", "bf16_m128n128k64_w2x4_mt16_s2",
             "bf16_dma_m64n64k64_w2x2_mt16_s4", "bf16_m64n64k64_w2x2_mt16_s2",
-            "bf16_pp_m256n256k32_w2x4_mt16_s4", "bf16_pp_m256n256k64_w2x4_mt16_s2"]
+            "bf16_pp_m256n256k32_w2x4_mt16_s4", "bf16_pp_m256n256k64_w2x4_mt16_s2",
+            "bf16_pp_m192n256k64_w2x4_mt16_s2"]
     outs = [run_gpu(gpu, p, data, policy=pol) for pol in pols]
     for pol, o in zip(pols[1:], outs[1:]):
         assert np.array_equal(outs[0], o), pol
@@ -286,12 +297,11 @@ def test_run_to_run_deterministic_and_seed_sensitive(gpu):
 
 @pytest.mark.slow
 def test_square_4096(gpu):
+    """Every element of the 4096^3 product against the oracle."""
     p = gi.SQUARE_4096
     data = p.make()
     C = run_gpu(gpu, p, data)
-    assert np.isfinite(tolerance.bf16_bits_to_f64(C)).all()
-    rows = sample_rows(p.M, per_tile=1, cap=40)
-    _assert_ok(compare(p, data, C, rows=rows), p.name)
+    _assert_ok(compare(p, data, C), p.name)
 
 
 @pytest.mark.slow
@@ -319,10 +329,9 @@ def test_projection_backward_pair(gpu):
     gpu(dY, X, dW, transA=1, beta=1.0)
     torch.cuda.synchronize()
     dX_h, dW_h = to_host(dX), to_host(dW)
-    rows = sample_rows(2048, per_tile=1, cap=16)
-    _assert_ok(compare(gi.PROJ_DX, {"A": d["dY"], "B": d["W"]}, dX_h, rows=rows), "dX")
-    rows = sample_rows(5120, per_tile=1, cap=24)
-    _assert_ok(compare(gi.PROJ_DW, {"A": d["dY"], "B": d["X"], "C": d["dW0"]}, dW_h, rows=rows), "dW")
+    # every element of both products
+    _assert_ok(compare(gi.PROJ_DX, {"A": d["dY"], "B": d["W"]}, dX_h), "dX")
+    _assert_ok(compare(gi.PROJ_DW, {"A": d["dY"], "B": d["X"], "C": d["dW0"]}, dW_h), "dW")
 
 
 @pytest.mark.slow
@@ -346,13 +355,25 @@ def test_projection_backward_beta_visible(gpu):
     assert not compare(p0, data, to_host(dW), rows=rows)["ok"]
 
 
+def _whole_tiles(M, tiles=(0, None, -1), tile=256):
+    """Every row of a few 256-row tiles: the first, one in the middle and the last."""
+    n = (M + tile - 1) // tile
+    rows = []
+    for t in tiles:
+        t = n // 2 if t is None else (t % n)
+        rows.extend(range(t * tile, min(M, (t + 1) * tile)))
+    return sorted(set(rows))
+
+
 @pytest.mark.slow
 def test_fp8_16384(gpu):
+    """Whole 256-row tiles (first, middle, last) of the E4M3 forward product, with bf16 and
+    with fp32 C; every other row is checked for finiteness."""
     p = gi.FP8_FWD
     data = p.make()
     C = run_gpu(gpu, p, data)
     assert np.isfinite(tolerance.bf16_bits_to_f64(C)).all()
-    rows = sample_rows(p.M, tile=256, per_tile=0, cap=24)
+    rows = _whole_tiles(p.M)
     _assert_ok(compare(p, data, C, rows=rows), p.name)
     # the fp32 bound applies to the accumulation: same inputs with fp32 C
     p32 = dataclasses.replace(p, c_dtype="f32")
@@ -364,12 +385,60 @@ def test_fp8_16384(gpu):
 
 @pytest.mark.slow
 def test_fp8_16384_native(gpu):
-    """The opt-in native f8f6f4 path at the full forward shape, hardware-model bound."""
+    """The opt-in native f8f6f4 path at the full forward shape, hardware-model bound, and its
+    measured accuracy with fp32 C beside the default (widened) path's on the same rows: the
+    native instruction's truncated group sums leave a Frobenius error above the 1e-5 fp32
+    criterion, which is why it is not the default."""
     p = gi.FP8_FWD
     data = p.make()
-    C = run_gpu(gpu, p, data, policy="e4m3native_m256n256k128_w2x2_mt32_s2")
-    rows = sample_rows(p.M, tile=256, per_tile=0, cap=16)
+    pol = "e4m3native_m256n256k128_w2x2_mt32_s2"
+    C = run_gpu(gpu, p, data, policy=pol)
+    rows = _whole_tiles(p.M, tiles=(0, -1))
     _assert_ok(compare(p, data, C, rows=rows, accumulate="e4m3_native"), "native")
+    p32 = dataclasses.replace(p, c_dtype="f32")
+    native = compare(p32, data, run_gpu(gpu, p32, data, policy=pol), rows=rows, accumulate="e4m3_native")
+    widened = compare(p32, data, run_gpu(gpu, p32, data), rows=rows)
+    print("fp8 16384x5120x5120 fp32 C: frob_rel native %.3e widened %.3e" % (native["frob_rel"],
+                                                                         widened["frob_rel"]))
+    _assert_ok(native, "native fp32")
+    _assert_ok(widened, "widened fp32")
+    assert widened["frob_rel"] <= 1e-5 < native["frob_rel"]
+
+
+def _int_problem(p):
+    """The same shape and call with integer inputs in [-4, 4] (and an integer initial C when
+    beta is non-zero): every partial sum is an integer below 2^24, exact in fp32 whatever
+    the order, so C must equal the oracle's value rounded once, bit for bit."""
+    return dataclasses.replace(p, dist="int4", c_dist="int4" if p.beta != 0.0 else None)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["proj_bwd_dx", "proj_bwd_dw", "fp8_e4m3_16384x5120x5120"])
+def test_full_size_integer_bitwise_shapes(gpu, name):
+    p = _int_problem(gi.BY_NAME[name])
+    data = p.make()
+    C = run_gpu(gpu, p, data)
+    rows = _whole_tiles(p.M) if p.M > 8192 else None
+    R, _ = oracle.gemm_problem(p, data, rows=rows, with_abs=False)
+    assert np.abs(R).max() < 2 ** 24
+    got = C if rows is None else C[rows]
+    assert np.array_equal(got, oracle.round_bf16(R)), name
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["gemm_256_bf16_f32", "gemm_4096_bf16", "proj_bwd_dx", "proj_bwd_dw",
+                                  "fp8_e4m3_16384x5120x5120"])
+def test_second_seed(gpu, name):
+    """Each workload again with other seeds: sampled rows against the oracle, and an output
+    that differs from the first seeds' almost everywhere."""
+    p = gi.BY_NAME[name]
+    seeds = tuple(s + 100 for s in p.seeds)
+    d0, d1 = p.make(), p.make(seeds=seeds)
+    C0 = run_gpu(gpu, p, d0)
+    C1 = run_gpu(gpu, p, d1)
+    rows = sample_rows(p.M, per_tile=1, cap=24, seed=1)
+    _assert_ok(compare(p, d1, C1, rows=rows), name + " second seeds")
+    assert (C0 != C1).mean() > 0.99
 
 
 @pytest.mark.slow

@@ -105,6 +105,20 @@ def test_bf16_round_golden():
         assert oracle.load().oracle_round_bf16(x) == int(bits_s, 16), line
 
 
+def test_f32_round_golden():
+    xs, want = [], []
+    for line in open(os.path.join(GOLDEN, "f32_round.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        x_s, bits_s = line.split()
+        xs.append(float.fromhex(x_s) if x_s.lstrip("-").startswith("0x") else float(x_s))
+        want.append(int(bits_s, 16))
+    got = oracle.round_f32(np.array(xs, dtype=np.float64))
+    for x, g, w in zip(xs, got.tolist(), want):
+        assert g == w, (x.hex(), hex(g), hex(w))
+
+
 def test_bf16_round_matches_library_on_f32_values():
     import torch
     rng = np.random.default_rng(7)
