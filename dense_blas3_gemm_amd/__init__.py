@@ -20,7 +20,7 @@ STATUS = {0: "SUCCESS", 1: "INVALID_VALUE", 2: "NOT_SUPPORTED", 3: "NOT_INITIALI
           4: "LAUNCH_FAILED", 5: "INTERNAL"}
 
 # The exported C symbols, in the order include/gemm.h declares them.
-EXPORTS = ["gemm_create", "gemm_destroy", "gemm_set_stream", "gemm_run", "gemm_run_mx",
+EXPORTS = ["gemm_create", "gemm_destroy", "gemm_set_stream", "gemm_run", "gemm_run_noalloc", "gemm_run_mx",
            "gemm_quantize_mx", "gemm_check_args", "gemm_query_policy", "gemm_set_policy",
            "gemm_lds_probe", "gemm_policy_count", "gemm_policy_name", "gemm_version",
            "gemm_status_string", "gemm_syrk", "gemm_syr2k", "gemm_symm", "gemm_trmm", "gemm_trsm"]
@@ -77,6 +77,8 @@ def load_library():
     lib.gemm_destroy.argtypes = [vp]
     lib.gemm_set_stream.argtypes = [vp, vp]
     lib.gemm_run.argtypes = [vp, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, i32]
+    lib.gemm_run_noalloc.argtypes = [i32, vp, ctypes.c_char_p, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32,
+                                     vp, i64, i32]
     lib.gemm_check_args.argtypes = [i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, i32]
     lib.gemm_query_policy.argtypes = [vp, i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32,
                                       ctypes.c_char_p, ctypes.c_size_t]
@@ -96,7 +98,7 @@ def load_library():
     lib.gemm_symm.argtypes = [vp, i32, i32, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, i32]
     lib.gemm_trmm.argtypes = [vp, i32, i32, i32, i32, i64, i64, f32, vp, i64, vp, i64, vp, i64, i32]
     lib.gemm_trsm.argtypes = [vp, i32, i32, i32, i32, i64, i64, f32, vp, i64, vp, i64, i32]
-    for fn in ["gemm_create", "gemm_destroy", "gemm_set_stream", "gemm_run", "gemm_check_args",
+    for fn in ["gemm_create", "gemm_destroy", "gemm_set_stream", "gemm_run", "gemm_run_noalloc", "gemm_check_args",
                "gemm_query_policy", "gemm_set_policy", "gemm_lds_probe", "gemm_policy_count",
                "gemm_run_mx", "gemm_quantize_mx", "gemm_syrk", "gemm_syr2k", "gemm_symm", "gemm_trmm",
                "gemm_trsm"]:
@@ -369,3 +371,30 @@ def check_args(transA, transB, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_p
     lib = load_library()
     return lib.gemm_check_args(transA, transB, M, N, K, alpha, ctypes.c_void_p(A_ptr), lda,
                                ctypes.c_void_p(B_ptr), ldb, beta, ctypes.c_void_p(C_ptr), ldc, dtype)
+
+
+def run_noalloc_raw(device, stream_ptr, policy, transA, transB, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta,
+                    C_ptr, ldc, dtype) -> int:
+    """gemm_run_noalloc with raw pointers (stream_ptr 0: the default stream); returns the status."""
+    lib = load_library()
+    pol = None if policy is None else policy.encode()
+    return lib.gemm_run_noalloc(int(device), ctypes.c_void_p(stream_ptr or None), pol, int(transA), int(transB),
+                                int(M), int(N), int(K), float(alpha), ctypes.c_void_p(A_ptr), int(lda),
+                                ctypes.c_void_p(B_ptr), int(ldb), float(beta), ctypes.c_void_p(C_ptr), int(ldc),
+                                int(dtype))
+
+
+def run_noalloc(A, B, C, transA: int = 0, transB: int = 0, alpha: float = 1.0, beta: float = 0.0,
+                dtype: Optional[int] = None, policy: Optional[str] = None):
+    """gemm_run_noalloc on torch tensors of one device, on torch's current stream there:
+    the handle-free call that allocates nothing (its scratch is a static device array)."""
+    import torch
+    if dtype is None:
+        ind = "e4m3" if A.dtype == torch.float8_e4m3fn else "bf16"
+        dtype = dtype_code(ind, _c_kind(C))
+    M, N = C.shape
+    K = A.shape[0] if transA else A.shape[1]
+    st = run_noalloc_raw(C.device.index or 0, _current_stream(C.device), policy, transA, transB, M, N, K, alpha,
+                         _ptr(A), _ld(A), _ptr(B), _ld(B), beta, _ptr(C), _ld(C), dtype)
+    if st != 0:
+        raise GemmError("gemm_run_noalloc", st)

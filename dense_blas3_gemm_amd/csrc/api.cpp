@@ -213,15 +213,14 @@ gemm_status_t gemm_set_stream(gemm_handle_t h, void* stream) {
   return GEMM_STATUS_SUCCESS;
 }
 
-gemm_status_t gemm_set_policy(gemm_handle_t h, const char* name) {
-  if (!live(h)) return GEMM_STATUS_NOT_INITIALIZED;
-  Handle* p = reinterpret_cast<Handle*>(h);
-  if (!name || std::strcmp(name, "auto") == 0) {
-    p->forced = -1;
-    p->forced_splits = 1;
-    return GEMM_STATUS_SUCCESS;
-  }
-  // "<policy>" or "<policy>+sk<S>" with S in {2, 4, 8, 16}
+}  // extern "C"
+
+// A policy name as gemm_set_policy takes it: NULL or "auto" (*idx = -1), "<policy>" or
+// "<policy>+sk<S>" with S in {2, 4, 8, 16}.
+static gemm_status_t parse_policy(const char* name, int* idx, int* splits) {
+  *idx = -1;
+  *splits = 1;
+  if (!name || std::strcmp(name, "auto") == 0) return GEMM_STATUS_SUCCESS;
   char base[128];
   int sp = 1;
   const char* plus = std::strstr(name, "+sk");
@@ -238,6 +237,19 @@ gemm_status_t gemm_set_policy(gemm_handle_t h, const char* name) {
   const int i = policy_find(base);
   if (i < 0) return GEMM_STATUS_INVALID_VALUE;
   if (sp > 1 && policy_at(i).pipe != 1) return GEMM_STATUS_INVALID_VALUE;  // direct-to-LDS only
+  *idx = i;
+  *splits = sp;
+  return GEMM_STATUS_SUCCESS;
+}
+
+extern "C" {
+
+gemm_status_t gemm_set_policy(gemm_handle_t h, const char* name) {
+  if (!live(h)) return GEMM_STATUS_NOT_INITIALIZED;
+  Handle* p = reinterpret_cast<Handle*>(h);
+  int i = -1, sp = 1;
+  const gemm_status_t st = parse_policy(name, &i, &sp);
+  if (st != GEMM_STATUS_SUCCESS) return st;
   p->forced = i;
   p->forced_splits = sp;
   return GEMM_STATUS_SUCCESS;
@@ -487,6 +499,69 @@ gemm_status_t gemm_quantize_mx(gemm_handle_t h, int64_t rows, int64_t cols, cons
   const hipError_t err = launch_quantize_mx(rows, cols, src, ld_src, dst, ld_dst, scales, ld_scales, p->stream);
   if (cur != p->device) (void)hipSetDevice(cur);
   return err == hipSuccess ? GEMM_STATUS_SUCCESS : GEMM_STATUS_LAUNCH_FAILED;
+}
+
+}  // extern "C"
+
+// ---- gemm_run_noalloc: the scratch memory of a handle's workspace (the split-K partials)
+// in a device array instead, so that a call allocates nothing.  The code object's loader
+// places one copy of the array on each device the library runs on; it stays there until
+// the process ends.  In host code `scratch` names a host-side stand-in, not the device
+// address: the address comes from hipGetSymbolAddress, once per device, and only that
+// pointer is ever passed to a kernel.
+static_assert(GEMM_STATIC_SCRATCH_BYTES >= kSplitBytes, "the partials of any split a handle would choose");
+static __device__ __align__(256) float scratch[GEMM_STATIC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+constexpr int kMaxStaticDevices = 64;
+struct StaticScratch {
+  std::once_flag once;
+  hipError_t err = hipErrorNotInitialized;
+  void* ptr = nullptr;  // device address of `scratch` on this device
+  int cu_count = 0;
+};
+StaticScratch g_static[kMaxStaticDevices];
+}  // namespace
+
+extern "C" {
+
+gemm_status_t gemm_run_noalloc(int device, void* stream, const char* policy, int transA, int transB, int64_t M,
+                               int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B,
+                               int64_t ldb, float beta, void* C, int64_t ldc, int dtype) {
+  gemm_status_t st = gemm_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype);
+  if (st != GEMM_STATUS_SUCCESS) return st;
+  int forced = -1, sp = 1;
+  st = parse_policy(policy, &forced, &sp);
+  if (st != GEMM_STATUS_SUCCESS) return st;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return GEMM_STATUS_NOT_INITIALIZED;
+  }
+  if (device < 0 || device >= n || device >= kMaxStaticDevices) return GEMM_STATUS_INVALID_VALUE;
+  if (M == 0 || N == 0) return GEMM_STATUS_SUCCESS;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return GEMM_STATUS_INTERNAL;
+  if (cur != device && hipSetDevice(device) != hipSuccess) return GEMM_STATUS_INTERNAL;
+  StaticScratch& s = g_static[device];
+  std::call_once(s.once, [&s, device] {  // with `device` current
+    s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch));
+    if (s.err == hipSuccess && hipDeviceGetAttribute(&s.cu_count, hipDeviceAttributeMultiprocessorCount, device) !=
+                                   hipSuccess)
+      s.err = hipErrorInvalidDevice;
+    if (s.err != hipSuccess) (void)hipGetLastError();
+  });
+  gemm_status_t out = GEMM_STATUS_INTERNAL;
+  if (s.err == hipSuccess && s.ptr) {
+    bool unsupported = false;
+    const hipError_t err =
+        enqueue_impl(s.cu_count > 0 ? s.cu_count : 256, reinterpret_cast<hipStream_t>(stream), s.ptr,
+                     (int64_t)(GEMM_STATIC_SCRATCH_BYTES / sizeof(float)), transA, transB, M, N, K, alpha, A, lda, B,
+                     ldb, beta, C, ldc, dtype, nullptr, 0, nullptr, 0, GemmExtras{}, forced, sp, &unsupported);
+    out = unsupported ? GEMM_STATUS_NOT_SUPPORTED : err == hipSuccess ? GEMM_STATUS_SUCCESS : GEMM_STATUS_LAUNCH_FAILED;
+  }
+  if (cur != device) (void)hipSetDevice(cur);
+  return out;
 }
 
 }  // extern "C"

@@ -114,6 +114,34 @@ gemm_status_t gemm_run(gemm_handle_t h, int transA, int transB, int64_t M, int64
                        int64_t K, float alpha, const void* A, int64_t lda, const void* B,
                        int64_t ldb, float beta, void* C, int64_t ldc, int dtype);
 
+/* The same call as gemm_run, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  It needs no
+ * handle and calls no allocating routine.  The split-K partials, which gemm_run keeps in
+ * its handle's workspace, go to a device array of GEMM_STATIC_SCRATCH_BYTES instead.
+ *
+ * The array: the library's code object holds one copy per device it runs on, placed by
+ * the loader and held until the process ends.  Every call on a device shares that copy,
+ * so calls that overlap on one device (two streams, two host threads) race and must not
+ * be made.  The first call on a device looks up the array's device address; make that
+ * call outside graph capture.
+ *
+ * Arguments:
+ * - device: the HIP device, made current for the call and restored after it.
+ * - stream: a hipStream_t of that device (passed as void*; NULL for the default stream).
+ * - policy: NULL or "auto" for the shape-driven choice, which is gemm_run's on a handle
+ *   of that device.  Or a policy name as gemm_set_policy takes it.
+ * - The remaining arguments, the dtypes and the special cases are gemm_run's.
+ *
+ * Errors: as gemm_run, plus these.
+ * - INVALID_VALUE: a bad device index (or one of 64 or more), or an unknown policy name.
+ * - NOT_SUPPORTED: a forced split whose partials would exceed GEMM_STATIC_SCRATCH_BYTES.
+ *   The shape-driven choice never needs more. */
+#define GEMM_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+gemm_status_t gemm_run_noalloc(int device, void* stream, const char* policy, int transA, int transB,
+                               int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+                               int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+                               int64_t ldc, int dtype);
+
 /* Block-scaled E4M3 ("MXFP8") GEMM: the MXFP8 operands of the fused profile protocol
  * (section "SM103 MXFP8 QKV weight-quantization diagnostics": E4M3 elements with one
  * UE8M0 scale per 32 elements along K).  Computes

@@ -87,6 +87,20 @@ def test_null_handle_is_not_initialized():
                         ctypes.c_void_p(B), 8, 0.0, ctypes.c_void_p(C), 8, BF16_BF16) == NOT_INIT
 
 
+def test_noalloc_checks_arguments_before_the_device():
+    """gemm_run_noalloc: argument and policy-name errors come first, before any device is
+    touched; without a GPU a valid call reports NOT_INITIALIZED."""
+    def call(policy=None, M=8, dev=0):
+        return d.run_noalloc_raw(dev, 0, policy, 0, 0, M, 8, 8, 1.0, A, 8, B, 8, 0.0, C, 8, BF16_BF16)
+    assert call(M=-1) == INVALID
+    assert call(policy="no_such_policy") == INVALID
+    assert call(policy="bf16_pp_m256n256k32_w2x4_mt16_s4+sk4") == INVALID  # split-K: ring policies only
+    st = call()
+    if st != OK:  # no GPU here
+        assert st == NOT_INIT
+        assert call(policy="auto") == NOT_INIT
+
+
 def test_create_without_device_or_with_one():
     lib = d.load_library()
     h = ctypes.c_void_p()
