@@ -12,7 +12,9 @@ import os
 from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libdbgemm.so")
+# DBGEMM_LIB selects another build of the same library (the sanitized host-only build the
+# CPU tests run under AddressSanitizer)
+LIB_PATH = os.environ.get("DBGEMM_LIB") or os.path.join(PKG, "libdbgemm.so")
 
 OP_N, OP_T = 0, 1
 BF16_F32, BF16_BF16, E4M3_BF16, E4M3_F32, MXE4M3_BF16, MXE4M3_F32, E4M3_E4M3, MXE4M3_E4M3 = range(8)

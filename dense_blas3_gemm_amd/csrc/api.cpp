@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 #include <unordered_set>
 
@@ -23,15 +24,32 @@ constexpr size_t kWorkspaceBytes = (size_t)256 << 20;
 // Split-K partials use at most this much of it: the wave-time model's split costs were fitted
 // with this bound (a larger one lets it split grids whose reduction costs more than it saves).
 constexpr size_t kSplitBytes = (size_t)64 << 20;
+// Stream-K hand-off flags, one int per stream-K workgroup; zero between calls (each owner
+// clears the flags it waited for).  Kept apart from the workspace, which the BLAS3 calls
+// overwrite with operands.
+constexpr size_t kFlagBytes = (size_t)64 << 10;
+
+// A policy pinned by name: table index (-1: shape-driven), split-K factor, and stream-K
+// (0: off, -1: one stream-K workgroup per CU, > 0: that many).
+struct Forced {
+  int idx = -1;
+  int splits = 1;
+  int sk = 0;
+};
 
 struct Handle {
   int device = 0;
   int cu_count = 256;
   hipStream_t stream = nullptr;
-  int forced = -1;         // policy index, -1 = shape-driven
-  int forced_splits = 1;   // split-K factor of a forced policy
-  void* ws = nullptr;      // kWorkspaceBytes on `device`, or null (split-K off)
+  Forced forced;
+  void* ws = nullptr;      // kWorkspaceBytes on `device`, or null (split-K and stream-K off)
+  int* flags = nullptr;    // kFlagBytes on `device`, zeroed, or null (stream-K off)
+  uint32_t epoch = 0;      // stream-K call counter (the flag value of the latest call)
   int64_t ws_floats() const { return ws ? (int64_t)(kSplitBytes / sizeof(float)) : 0; }
+  int next_epoch() {
+    if (++epoch == 0) ++epoch;
+    return (int)epoch;
+  }
 };
 
 // Live handles; a destroyed (or never created) handle is rejected instead of used.
@@ -104,6 +122,14 @@ hipError_t launch_mfma_dma(const Policy& p, const GemmArgs& a, hipStream_t s) {
   }
   return e;
 }
+hipError_t launch_mfma_staged(const Policy& p, const GemmArgs& a, hipStream_t s) {
+  switch (a.transA * 2 + a.transB) {
+    case 0: return launch_mfma_staged_00(p, a, s);
+    case 1: return launch_mfma_staged_01(p, a, s);
+    case 2: return launch_mfma_staged_10(p, a, s);
+    default: return launch_mfma_staged_11(p, a, s);
+  }
+}
 hipError_t launch_mfma_pp(const Policy& p, const GemmArgs& a, hipStream_t s) {
   switch (a.transA * 2 + a.transB) {
     case 0: return launch_mfma_pp_00(p, a, s);
@@ -172,11 +198,18 @@ gemm_status_t gemm_create(gemm_handle_t* h, int device) {
   Handle* p = new Handle();
   p->device = device;
   p->cu_count = cus > 0 ? cus : 256;
-  // The workspace is optional: without it every call runs unsplit.
+  // The workspace and the flags are optional: without them every call runs unsplit.
   int prev = -1;
   if (hipGetDevice(&prev) == hipSuccess && hipSetDevice(device) == hipSuccess) {
     void* ws = nullptr;
     if (hipMalloc(&ws, kWorkspaceBytes) == hipSuccess) p->ws = ws;
+    void* fl = nullptr;
+    if (hipMalloc(&fl, kFlagBytes) == hipSuccess) {
+      if (hipMemset(fl, 0, kFlagBytes) == hipSuccess && hipDeviceSynchronize() == hipSuccess)
+        p->flags = (int*)fl;
+      else
+        (void)hipFree(fl);
+    }
     (void)hipSetDevice(prev);
   }
   (void)hipGetLastError();
@@ -195,10 +228,11 @@ gemm_status_t gemm_destroy(gemm_handle_t h) {
     if (g_live.erase(h) == 0) return GEMM_STATUS_NOT_INITIALIZED;
   }
   Handle* p = reinterpret_cast<Handle*>(h);
-  if (p->ws) {
+  if (p->ws || p->flags) {
     int prev = -1;
     if (hipGetDevice(&prev) == hipSuccess && hipSetDevice(p->device) == hipSuccess) {
-      (void)hipFree(p->ws);  // waits for the device's work in flight
+      if (p->ws) (void)hipFree(p->ws);  // waits for the device's work in flight
+      if (p->flags) (void)hipFree(p->flags);
       (void)hipSetDevice(prev);
     }
     (void)hipGetLastError();
@@ -215,31 +249,66 @@ gemm_status_t gemm_set_stream(gemm_handle_t h, void* stream) {
 
 }  // extern "C"
 
-// A policy name as gemm_set_policy takes it: NULL or "auto" (*idx = -1), "<policy>" or
-// "<policy>+sk<S>" with S in {2, 4, 8, 16}.
-static gemm_status_t parse_policy(const char* name, int* idx, int* splits) {
-  *idx = -1;
-  *splits = 1;
+// A policy name as gemm_set_policy takes it: NULL or "auto" (shape-driven), "<policy>",
+// "<policy>+sk<S>" with S in {2, 4, 8, 16} (split-K, ring policies), "<policy>+streamk" or
+// "<policy>+streamk<G>" with 1 <= G <= 4096 (stream-K, ping-pong policies).
+static gemm_status_t parse_policy(const char* name, Forced* f) {
+  *f = Forced{};
   if (!name || std::strcmp(name, "auto") == 0) return GEMM_STATUS_SUCCESS;
   char base[128];
-  int sp = 1;
-  const char* plus = std::strstr(name, "+sk");
+  Forced out;
+  const char* plus = std::strchr(name, '+');
   const size_t n = plus ? (size_t)(plus - name) : std::strlen(name);
   if (n == 0 || n >= sizeof(base)) return GEMM_STATUS_INVALID_VALUE;
   std::memcpy(base, name, n);
   base[n] = 0;
   if (plus) {
     char* end = nullptr;
-    const long v = std::strtol(plus + 3, &end, 10);
-    if (!end || *end != 0 || (v != 2 && v != 4 && v != 8 && v != 16)) return GEMM_STATUS_INVALID_VALUE;
-    sp = (int)v;
+    if (std::strncmp(plus, "+streamk", 8) == 0) {
+      out.sk = -1;
+      if (plus[8] != 0) {
+        const long v = std::strtol(plus + 8, &end, 10);
+        if (!end || *end != 0 || v < 1 || v > 4096) return GEMM_STATUS_INVALID_VALUE;
+        out.sk = (int)v;
+      }
+    } else if (std::strncmp(plus, "+sk", 3) == 0) {
+      const long v = std::strtol(plus + 3, &end, 10);
+      if (!end || *end != 0 || (v != 2 && v != 4 && v != 8 && v != 16)) return GEMM_STATUS_INVALID_VALUE;
+      out.splits = (int)v;
+    } else {
+      return GEMM_STATUS_INVALID_VALUE;
+    }
   }
-  const int i = policy_find(base);
-  if (i < 0) return GEMM_STATUS_INVALID_VALUE;
-  if (sp > 1 && policy_at(i).pipe != 1) return GEMM_STATUS_INVALID_VALUE;  // direct-to-LDS only
-  *idx = i;
-  *splits = sp;
+  out.idx = policy_find(base);
+  if (out.idx < 0) return GEMM_STATUS_INVALID_VALUE;
+  if (out.splits > 1 && policy_at(out.idx).pipe != 1) return GEMM_STATUS_INVALID_VALUE;  // direct-to-LDS only
+  if (out.sk != 0 && policy_at(out.idx).pipe != 2) return GEMM_STATUS_INVALID_VALUE;    // ping-pong only
+  *f = out;
   return GEMM_STATUS_SUCCESS;
+}
+
+// The policy, split-K factor and stream-K plan a call runs with (`flags`: whether stream-K
+// flags are available; `extras`: a BLAS3 call, which never splits); false when a forced
+// policy cannot serve the call.  Stream-K runs only when forced by name; on a grid of
+// whole rounds it runs plain.
+static bool choose(const Problem& pr, int cu_count, int64_t ws_floats, bool flags, const Forced& f, bool extras,
+                   int* idx, int* sp, StreamK* sk) {
+  *sk = StreamK{};
+  if (f.idx >= 0) {
+    *idx = f.idx;
+    *sp = f.splits;
+    const Policy& pol = policy_at(*idx);
+    if (!policy_serves(pol, pr) || !split_allowed(pol, pr, *sp, ws_floats) || (extras && (*sp != 1 || f.sk != 0)))
+      return false;
+    if (f.sk != 0) {
+      if (!flags) return false;
+      *sk = stream_k_plan(pol, pr, cu_count, f.sk > 0 ? f.sk : 0);
+      if (sk->tiles > 0 && stream_k_ws_floats(pol, *sk) > ws_floats) return false;
+    }
+    return true;
+  }
+  *idx = policy_select(pr, cu_count, extras ? 0 : ws_floats, sp);
+  return true;
 }
 
 extern "C" {
@@ -247,11 +316,10 @@ extern "C" {
 gemm_status_t gemm_set_policy(gemm_handle_t h, const char* name) {
   if (!live(h)) return GEMM_STATUS_NOT_INITIALIZED;
   Handle* p = reinterpret_cast<Handle*>(h);
-  int i = -1, sp = 1;
-  const gemm_status_t st = parse_policy(name, &i, &sp);
+  Forced f;
+  const gemm_status_t st = parse_policy(name, &f);
   if (st != GEMM_STATUS_SUCCESS) return st;
-  p->forced = i;
-  p->forced_splits = sp;
+  p->forced = f;
   return GEMM_STATUS_SUCCESS;
 }
 
@@ -265,19 +333,19 @@ gemm_status_t gemm_query_policy(gemm_handle_t h, int transA, int transB, int64_t
   if (M < 0 || N < 0 || K < 0) return GEMM_STATUS_INVALID_VALUE;
   const Handle* p = reinterpret_cast<const Handle*>(h);
   const Problem pr = make_problem(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, dtype);
-  int idx, sp = 1;
-  if (p && p->forced >= 0) {
-    idx = p->forced;
-    sp = p->forced_splits;
-    if (!policy_serves(policy_at(idx), pr) || !split_allowed(policy_at(idx), pr, sp, p->ws_floats()))
-      return GEMM_STATUS_NOT_SUPPORTED;
-  } else {
-    // without a handle, the workspace a new handle would have
-    const int64_t wsf = p ? p->ws_floats() : (int64_t)(kSplitBytes / sizeof(float));
-    idx = policy_select(pr, p ? p->cu_count : 256, wsf, &sp);
-  }
+  // without a handle, the workspace and flags a new handle would have
+  const int64_t wsf = p ? p->ws_floats() : (int64_t)(kSplitBytes / sizeof(float));
+  const Forced f = p ? p->forced : Forced{};
+  int idx = 0, sp = 1;
+  StreamK sk;
+  if (!choose(pr, p ? p->cu_count : 256, wsf, p ? p->flags != nullptr : true, f, false, &idx, &sp, &sk))
+    return GEMM_STATUS_NOT_SUPPORTED;
   if (sp > 1)
     std::snprintf(name, len, "%s+sk%d", policy_at(idx).name, sp);
+  else if (sk.tiles > 0 && f.sk > 0)
+    std::snprintf(name, len, "%s+streamk%d", policy_at(idx).name, f.sk);
+  else if (sk.tiles > 0)
+    std::snprintf(name, len, "%s+streamk", policy_at(idx).name);
   else
     std::snprintf(name, len, "%s", policy_at(idx).name);
   return GEMM_STATUS_SUCCESS;
@@ -305,13 +373,15 @@ gemm_status_t gemm_lds_probe(gemm_handle_t h, int kind, const uint32_t* offsets,
   return err == hipSuccess ? GEMM_STATUS_SUCCESS : GEMM_STATUS_LAUNCH_FAILED;
 }
 
-// Enqueues one checked GEMM on `stream` (the device is current).  `forced` >= 0 pins a
-// policy with `forced_splits`; *unsupported is set when that policy cannot serve the call.
-static hipError_t enqueue_impl(int cu_count, hipStream_t stream, void* ws, int64_t ws_floats, int transA, int transB,
+// Enqueues one checked GEMM on `stream` (the device is current).  `f` may pin a policy;
+// *unsupported is set when that policy cannot serve the call.  `flags` (or null: no
+// stream-K) and `epoch` (non-zero, new for each call) are the stream-K hand-off state.
+static hipError_t enqueue_impl(int cu_count, hipStream_t stream, void* ws, int64_t ws_floats, int* flags, int epoch,
+                               int transA, int transB,
                                int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
                                const void* B, int64_t ldb, float beta, void* C, int64_t ldc, int dtype,
                                const uint8_t* sa, int64_t ldsa, const uint8_t* sb, int64_t ldsb,
-                               const GemmExtras& x, int forced, int forced_splits, bool* unsupported) {
+                               const GemmExtras& x, const Forced& f, bool* unsupported) {
   *unsupported = false;
   if (M == 0 || N == 0) return hipSuccess;
   GemmArgs a{};
@@ -357,17 +427,11 @@ static hipError_t enqueue_impl(int cu_count, hipStream_t stream, void* ws, int64
       pr.fast_ok = pr.fast_ok && p2.fast_ok && x.lda2 == lda && x.ldb2 == ldb && transA == 0 && transB == 1;
     }
   }
-  int idx, sp = 1;
-  if (forced >= 0) {
-    idx = forced;
-    sp = forced_splits;
-    if (!policy_serves(policy_at(idx), pr) || !split_allowed(policy_at(idx), pr, sp, ws_floats) ||
-        (extras && sp != 1)) {
-      *unsupported = true;
-      return hipSuccess;
-    }
-  } else {
-    idx = policy_select(pr, cu_count, extras ? 0 : ws_floats, &sp);
+  int idx = 0, sp = 1;
+  StreamK sk;
+  if (!choose(pr, cu_count, ws_floats, flags != nullptr, f, extras, &idx, &sp, &sk)) {
+    *unsupported = true;
+    return hipSuccess;
   }
   const Policy& pol = policy_at(idx);
   if (pol.kind == KIND_SIMT) {
@@ -393,12 +457,21 @@ static hipError_t enqueue_impl(int cu_count, hipStream_t stream, void* ws, int64
   a.splits = sp;
   a.kt_per_split = (int)split_kt(pol, K, sp);
   if (sp > 1) a.ws = (float*)ws;
+  if (sk.tiles > 0) {
+    a.sk_dp = sk.dp;
+    a.sk_tiles = sk.tiles;
+    a.sk_grid = sk.grid;
+    a.sk_iters = sk.iters;
+    a.ws = (float*)ws;
+    a.flags = flags;
+    a.epoch = epoch;
+  }
   if (pol.pipe == 2) return launch_mfma_pp(pol, a, stream);
   return pol.pipe == 1 ? launch_mfma_dma(pol, a, stream) : launch_mfma_staged(pol, a, stream);
 }
 
 // Shared by gemm_run and gemm_run_mx once the arguments are checked.
-static gemm_status_t run_checked(const Handle* p, int transA, int transB, int64_t M, int64_t N, int64_t K,
+static gemm_status_t run_checked(Handle* p, int transA, int transB, int64_t M, int64_t N, int64_t K,
                                  float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
                                  float beta, void* C, int64_t ldc, int dtype, const uint8_t* sa,
                                  int64_t ldsa, const uint8_t* sb, int64_t ldsb) {
@@ -407,9 +480,10 @@ static gemm_status_t run_checked(const Handle* p, int transA, int transB, int64_
   if (hipGetDevice(&cur) != hipSuccess) return GEMM_STATUS_INTERNAL;
   if (cur != p->device && hipSetDevice(p->device) != hipSuccess) return GEMM_STATUS_INTERNAL;
   bool unsupported = false;
-  const hipError_t err = enqueue_impl(p->cu_count, p->stream, p->ws, p->ws_floats(), transA, transB, M, N, K, alpha,
+  const hipError_t err = enqueue_impl(p->cu_count, p->stream, p->ws, p->ws_floats(), p->flags, p->next_epoch(),
+                                      transA, transB, M, N, K, alpha,
                                       A, lda, B, ldb, beta, C, ldc, dtype, sa, ldsa, sb, ldsb, GemmExtras{},
-                                      p->forced, p->forced_splits, &unsupported);
+                                      p->forced, &unsupported);
   if (cur != p->device) (void)hipSetDevice(cur);
   if (unsupported) return GEMM_STATUS_NOT_SUPPORTED;
   if (err != hipSuccess) return GEMM_STATUS_LAUNCH_FAILED;
@@ -435,9 +509,11 @@ hipError_t gemm_enqueue(const HandleView& hv, int transA, int transB, int64_t M,
                         int dtype, const GemmExtras& x) {
   bool unsupported = false;
   // never split: the BLAS3 operations keep their operands in the workspace
-  const hipError_t e = enqueue_impl(hv.cu_count, hv.stream, nullptr, 0, transA,
+  Forced f;
+  f.idx = x.policy;
+  const hipError_t e = enqueue_impl(hv.cu_count, hv.stream, nullptr, 0, nullptr, 0, transA,
                                     transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, nullptr, 0, nullptr,
-                                    0, x, x.policy, 1, &unsupported);
+                                    0, x, f, &unsupported);
   return unsupported ? hipErrorInvalidConfiguration : e;
 }
 
@@ -456,7 +532,7 @@ gemm_status_t gemm_run(gemm_handle_t h, int transA, int transB, int64_t M, int64
   const gemm_status_t st = gemm_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
                                            ldc, dtype);
   if (st != GEMM_STATUS_SUCCESS) return st;
-  return run_checked(reinterpret_cast<const Handle*>(h), transA, transB, M, N, K, alpha, A, lda, B, ldb,
+  return run_checked(reinterpret_cast<Handle*>(h), transA, transB, M, N, K, alpha, A, lda, B, ldb,
                      beta, C, ldc, dtype, nullptr, 0, nullptr, 0);
 }
 
@@ -479,7 +555,7 @@ gemm_status_t gemm_run_mx(gemm_handle_t h, int64_t M, int64_t N, int64_t K, floa
   // 32-bit offsets into the scale arrays
   if ((double)M * (double)ld_scale_a >= 2147483647.0 || (double)N * (double)ld_scale_b >= 2147483647.0)
     return GEMM_STATUS_NOT_SUPPORTED;
-  return run_checked(reinterpret_cast<const Handle*>(h), GEMM_OP_N, GEMM_OP_T, M, N, K, alpha, A, lda, B,
+  return run_checked(reinterpret_cast<Handle*>(h), GEMM_OP_N, GEMM_OP_T, M, N, K, alpha, A, lda, B,
                      ldb, beta, C, ldc, dtype, scale_a, ld_scale_a, scale_b, ld_scale_b);
 }
 
@@ -503,14 +579,14 @@ gemm_status_t gemm_quantize_mx(gemm_handle_t h, int64_t rows, int64_t cols, cons
 
 }  // extern "C"
 
-// ---- gemm_run_noalloc: the scratch memory of a handle's workspace (the split-K partials)
-// in a device array instead, so that a call allocates nothing.  The code object's loader
-// places one copy of the array on each device the library runs on; it stays there until
-// the process ends.  In host code `scratch` names a host-side stand-in, not the device
-// address: the address comes from hipGetSymbolAddress, once per device, and only that
-// pointer is ever passed to a kernel.
+// ---- gemm_run_noalloc: the scratch memory of a handle (the split-K and stream-K partials,
+// then the stream-K flags) in a device array instead, so that a call allocates nothing.
+// The code object's loader places one copy of the array on each device the library runs
+// on, zeroed; it stays there until the process ends.  In host code `scratch` names a
+// host-side stand-in, not the device address: the address comes from hipGetSymbolAddress,
+// once per device, and only that pointer is ever passed to a kernel.
 static_assert(GEMM_STATIC_SCRATCH_BYTES >= kSplitBytes, "the partials of any split a handle would choose");
-static __device__ __align__(256) float scratch[GEMM_STATIC_SCRATCH_BYTES / sizeof(float)];
+static __device__ __align__(256) float scratch[(GEMM_STATIC_SCRATCH_BYTES + kFlagBytes) / sizeof(float)];
 
 namespace {
 constexpr int kMaxStaticDevices = 64;
@@ -519,6 +595,7 @@ struct StaticScratch {
   hipError_t err = hipErrorNotInitialized;
   void* ptr = nullptr;  // device address of `scratch` on this device
   int cu_count = 0;
+  std::atomic<uint32_t> epoch{0};  // stream-K call counter
 };
 StaticScratch g_static[kMaxStaticDevices];
 }  // namespace
@@ -530,8 +607,8 @@ gemm_status_t gemm_run_noalloc(int device, void* stream, const char* policy, int
                                int64_t ldb, float beta, void* C, int64_t ldc, int dtype) {
   gemm_status_t st = gemm_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype);
   if (st != GEMM_STATUS_SUCCESS) return st;
-  int forced = -1, sp = 1;
-  st = parse_policy(policy, &forced, &sp);
+  Forced f;
+  st = parse_policy(policy, &f);
   if (st != GEMM_STATUS_SUCCESS) return st;
   int n = 0;
   if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
@@ -554,10 +631,14 @@ gemm_status_t gemm_run_noalloc(int device, void* stream, const char* policy, int
   gemm_status_t out = GEMM_STATUS_INTERNAL;
   if (s.err == hipSuccess && s.ptr) {
     bool unsupported = false;
+    uint32_t e = ++s.epoch;
+    if (e == 0) e = ++s.epoch;
+    int* flags = (int*)((char*)s.ptr + GEMM_STATIC_SCRATCH_BYTES);
     const hipError_t err =
         enqueue_impl(s.cu_count > 0 ? s.cu_count : 256, reinterpret_cast<hipStream_t>(stream), s.ptr,
-                     (int64_t)(GEMM_STATIC_SCRATCH_BYTES / sizeof(float)), transA, transB, M, N, K, alpha, A, lda, B,
-                     ldb, beta, C, ldc, dtype, nullptr, 0, nullptr, 0, GemmExtras{}, forced, sp, &unsupported);
+                     (int64_t)(GEMM_STATIC_SCRATCH_BYTES / sizeof(float)), flags, (int)e, transA, transB, M, N, K,
+                     alpha, A, lda, B, ldb, beta, C, ldc, dtype, nullptr, 0, nullptr, 0, GemmExtras{}, f,
+                     &unsupported);
     out = unsupported ? GEMM_STATUS_NOT_SUPPORTED : err == hipSuccess ? GEMM_STATUS_SUCCESS : GEMM_STATUS_LAUNCH_FAILED;
   }
   if (cur != device) (void)hipSetDevice(cur);

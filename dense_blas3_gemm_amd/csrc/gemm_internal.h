@@ -37,6 +37,17 @@ struct GemmArgs {
   int splits;
   int kt_per_split;
   float* ws;
+  // Stream-K (ping-pong kernel; sk_tiles == 0: off).  Workgroups 0 .. sk_dp-1 each run
+  // one whole tile, the first sk_dp tiles of the raster order.  The other sk_tiles tiles
+  // are shared by the next sk_grid workgroups: their K loops are laid end to end and
+  // workgroup s sums K tiles [s*sk_iters, (s+1)*sk_iters) of that sequence (the last one
+  // fewer).  A range that starts inside a tile leaves that part's sum in the workgroup's
+  // slot of `ws` (BM*BN floats per slot) and sets flags[slot] to `epoch` (non-zero); the
+  // workgroup holding the tile's first K tile waits for those flags, adds the partials in
+  // K order, sets the flags back to zero and runs the epilogue.
+  int sk_dp, sk_tiles, sk_grid, sk_iters;
+  int* flags;
+  int epoch;
   // Block-scaled E4M3 (mx = 1): one UE8M0 byte per row and 32-element K block, for A
   // (rows m) in sa[m * ldsa + k / 32] and for B (rows n) in sb[n * ldsb + k / 32].
   int mx;
@@ -102,6 +113,11 @@ struct Policy {
 hipError_t launch_simt(const GemmArgs& a, hipStream_t s);
 hipError_t launch_scale(const GemmArgs& a, hipStream_t s);  // C <- beta*C (K == 0 or alpha == 0)
 hipError_t launch_mfma_staged(const Policy& p, const GemmArgs& a, hipStream_t s);  // pipe 0
+// pipe 0, one per (transA, transB) case, each in its own object
+hipError_t launch_mfma_staged_00(const Policy& p, const GemmArgs& a, hipStream_t s);
+hipError_t launch_mfma_staged_01(const Policy& p, const GemmArgs& a, hipStream_t s);
+hipError_t launch_mfma_staged_10(const Policy& p, const GemmArgs& a, hipStream_t s);
+hipError_t launch_mfma_staged_11(const Policy& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_mfma_dma(const Policy& p, const GemmArgs& a, hipStream_t s);     // pipe 1
 // pipe 1, one per (transA, transB) case and half of the policy table, each in its own
 // object: true when that part launched p (*err = the launch status)
@@ -152,8 +168,19 @@ struct Problem {
   bool square_tiles = false;
   bool kband = false;  // per-tile K band (wave model: longest tiles first)
 };
+// Stream-K plan of a ping-pong policy on a problem (the GemmArgs fields of that name);
+// tiles == 0: none (the grid is whole rounds, or the policy has no stream-K form).
+// `grid` > 0 asks for that many stream-K workgroups; 0 takes one per CU.
+struct StreamK {
+  int dp = 0, tiles = 0, grid = 0, iters = 0;
+};
+StreamK stream_k_plan(const Policy& p, const Problem& pr, int cu_count, int grid = 0);
+int64_t stream_k_ws_floats(const Policy& p, const StreamK& s);  // partial slots
 // Shape-driven selection; returns an index into the table and, in *splits, the
-// split-K factor (1 unless a workspace of ws_floats fp32 values allows more).
+// split-K factor (1 unless a workspace of ws_floats fp32 values allows more).  Stream-K is
+// never chosen here, only by name: on the grids it was built for (dX, dW) it measured
+// slower than the plain grid, because its workgroups run at scattered K offsets and lose
+// the L2 reuse of workgroups that step through K together.
 int policy_select(const Problem& pr, int cu_count, int64_t ws_floats, int* splits);
 // fp32 partials a split-K call of policy p with `splits` needs, K tiles per split
 // (0: that split is not allowed), and whether the split fits a workspace.

@@ -223,25 +223,27 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+#if !defined(DBGEMM_DMA_TA) || !defined(DBGEMM_DMA_TB)
+#error "compile with -DDBGEMM_DMA_TA=0|1 -DDBGEMM_DMA_TB=0|1"
+#endif
+
+// This object's transpose case (the file is compiled once per case).
 template <int BM, int BN, int BK, int WM, int WN, int MT, int ST, int IN>
 hipError_t launch_trans(const GemmArgs& a, hipStream_t s) {
-  const int code = a.transA * 2 + a.transB;
-  if constexpr (IN == IN_MX) {  // block-scaled operands: A [M][K] and B [N][K] only
-    if (code != 1) return hipErrorInvalidConfiguration;
-    return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, false, true>>(a, s);
+  constexpr bool TA = DBGEMM_DMA_TA != 0, TB = DBGEMM_DMA_TB != 0;
+  if constexpr (IN == IN_MX && (TA || !TB)) {  // block-scaled operands: A [M][K] and B [N][K] only
+    return hipErrorInvalidConfiguration;
   } else {
-    switch (code) {
-      case 0: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, false, false>>(a, s);
-      case 1: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, false, true>>(a, s);
-      case 2: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, true, false>>(a, s);
-      default: return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, true, true>>(a, s);
-    }
+    return launch_cfg<Cfg<BM, BN, BK, WM, WN, MT, ST, IN, TA, TB>>(a, s);
   }
 }
 
 }  // namespace
 
-hipError_t launch_mfma_staged(const Policy& p, const GemmArgs& a, hipStream_t s) {
+#define DBGEMM_ST_CAT2(a, b) launch_mfma_staged_##a##b
+#define DBGEMM_ST_CAT(a, b) DBGEMM_ST_CAT2(a, b)
+
+hipError_t DBGEMM_ST_CAT(DBGEMM_DMA_TA, DBGEMM_DMA_TB)(const Policy& p, const GemmArgs& a, hipStream_t s) {
 #define DBGEMM_SIMT(name, eff)
 #define DBGEMM_MFMA(name_, pipe_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_, eff_)       \
   if constexpr (pipe_ == 0)                                                                               \

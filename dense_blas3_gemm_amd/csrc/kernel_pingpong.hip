@@ -40,6 +40,7 @@ namespace dbgemm {
 namespace {
 
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // 64 lanes x 16 bytes from buffer `rsrc` at per-lane byte offset `voff` into LDS bytes
 // [lds_base, lds_base + 1024) (lane i -> lds_base + 16*i); an offset past the buffer's
@@ -205,290 +206,460 @@ __device__ __forceinline__ bf16x8 pp_widen8(i32x2 v) {
   return __builtin_bit_cast(bf16x8, (i32x4){w0, w1, w2, w3});
 }
 
+// Stream-K: bound on the tries of an owner's wait for one partial (each try sleeps a few
+// hundred cycles after a device-scope load, about a microsecond, so the bound is a few
+// seconds).  Every workgroup the owner waits for is resident or next in line once the
+// grid's data-parallel part has run, so a wait only runs out if the device is held by
+// other work for that long; then the tile gets NaN instead of a hang.
+constexpr int kStreamKSpins = 1 << 22;
+
+// Stream-K partial tiles in register order (as store_partial): float4 number p of thread
+// t sits at byte (p * THREADS + t) * 16 of the slot.  Buffer instructions take the
+// thread's offset in one VGPR and each p's offset as a scalar, so no per-p address is
+// held in registers.
 template <class C>
+__device__ __forceinline__ void pp_store_partial(float* slot, const typename AccOf<C::MT>::T (&acc)[C::FM][C::FN],
+                                                 uint32_t voff) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(slot, C::BM * C::BN * 4);
+  static_for<C::FM * C::FN * (C::ACC / 4)>([&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    constexpr int q = p % (C::ACC / 4), j = (p / (C::ACC / 4)) % C::FN, i = p / (C::ACC / 4) / C::FN;
+    const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, p * C::THREADS * 16, 0);
+  });
+}
+
+// Adds such a partial into acc, half of the fragment rows at a time (the scheduling
+// barrier keeps the second half's loads from being hoisted above the first half's
+// additions, which bounds the registers in flight).
+template <class C>
+__device__ __forceinline__ void pp_add_partial(const float* slot, typename AccOf<C::MT>::T (&acc)[C::FM][C::FN],
+                                               uint32_t voff) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(slot, C::BM * C::BN * 4);
+  constexpr int NP = C::FM * C::FN * (C::ACC / 4);
+  static_assert(NP % 2 == 0, "two halves");
+  static_for<2>([&](auto hc) {
+    constexpr int h = decltype(hc)::value;
+    static_for<NP / 2>([&](auto pc) {
+      constexpr int p = h * (NP / 2) + decltype(pc)::value;
+      constexpr int q = p % (C::ACC / 4), j = (p / (C::ACC / 4)) % C::FN, i = p / (C::ACC / 4) / C::FN;
+      const f32x4 v =
+          __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, p * C::THREADS * 16, 0));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[e];
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+// SK = false: one workgroup per output tile, its whole K loop.  SK = true: the stream-K
+// grid of GemmArgs (sk_dp whole tiles, then sk_grid workgroups sharing the K loops of the
+// other sk_tiles tiles).  Each workgroup runs its segments (a tile and a range [k0, k1) of
+// its K tiles) one after the other, each through the same two-group pipeline.
+template <class C, bool SK>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
   using P = PingPong<C>;
   constexpr int S = P::S;
   __shared__ __attribute__((aligned(1024))) char lds[P::LDS_BYTES];
   using Acc = typename AccOf<C::MT>::T;
 
-  int tm, tn, split_unused;  // unsplit
-  tile_of(blockIdx.x, a, tm, tn, split_unused);
-  const int m0 = tm * C::BM, n0 = tn * C::BN;
-  const int t = threadIdx.x, lane = t & 63;
+  const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   // waves are dealt to the four SIMDs in turn: waves w and w + 4 share a SIMD
   const int grp = wave >> 2;
   const int wn = wave & 3;
   const int wm = grp;
+  const int nk = (a.K + C::BK - 1) / C::BK;
+
+  // ---- this workgroup's work: K tiles [it, it_end) of the sequence that lays the K loops
+  // of the stream-K tiles end to end (tile ts of that part holds [ts*nk, (ts+1)*nk)), or
+  // one whole tile.  `slot` is the stream-K workgroup's index: consecutive indices share
+  // tiles, and they are grouped by XCD (ids b run on XCD b % xcd) so that a tile's owner
+  // and the workgroups that hand it partials mostly share one L2.
+  int it = 0, it_end = nk, slot = 0;
+  int tm0 = 0, tn0 = 0;
+  bool whole = true;
+  if constexpr (SK) {
+    const int b = blockIdx.x;
+    if (b < a.sk_dp) {
+      raster_tile(xcd_remap(b, a.sk_dp, a.xcd), a, tm0, tn0);
+    } else {
+      const int q = b - a.sk_dp, G = a.sk_grid;
+      slot = (a.xcd > 1 && G % a.xcd == 0) ? ((q + a.sk_dp) % a.xcd) * (G / a.xcd) + q / a.xcd : q;
+      it = slot * a.sk_iters;
+      it_end = min(it + a.sk_iters, a.sk_tiles * nk);
+      whole = false;
+      if (it >= it_end) return;  // an empty range (uniform over the workgroup)
+    }
+  } else {
+    int split_unused;  // unsplit
+    tile_of(blockIdx.x, a, tm0, tn0, split_unused);
+  }
 
   const uint32_t a_rows = C::A_KC ? a.M : a.K;
   const uint32_t b_rows = C::B_KC ? a.N : a.K;
-
-  // ---- this wave's copy instructions: instruction i fills LDS block wave*IPW + i of the
-  // tile (A blocks, then B); this lane fills chunk p = blk*64 + lane of its operand, row
-  // p / CPR, physical chunk p % CPR, which holds logical chunk (p % CPR) ^ swizzle(row).
-  // The per-lane offsets are relative to the start of a K tile, and fixed: each K tile
-  // gets its own buffer descriptor (base moved to the tile, size cut by as much), built
-  // with scalar arithmetic.  A chunk in a row or column past M or N gets an offset past
-  // every buffer.  Rows past K of an M/N-contiguous operand then lie past the tile's
-  // buffer and read zeros; a K-contiguous operand's chunks past K (a ragged last tile, or
-  // a tile past the end) are sent past the buffer in copy_tile.
-  uint32_t a_off[P::A_IPW], b_off[P::B_IPW];
-  auto chunk_k = [&](int blk, int CPR, int VEC, auto swzc) {  // K index of a K-contiguous chunk
-    const int p = blk * 64 + lane;
-    return ((p % CPR) ^ swzc(p / CPR)) * VEC;
-  };
-#pragma unroll
-  for (int i = 0; i < P::A_IPW; ++i) {
-    const int p = (wave * P::A_IPW + i) * 64 + lane;
-    const int r = p / C::A_CPR;
-    const int c = (p % C::A_CPR) ^ pp_swz<C, C::A_KC, C::A_CPR>(r);
-    if constexpr (C::A_KC)
-      a_off[i] = (m0 + r) < a.M ? (uint32_t)((m0 + r) * a.lda + c * C::VEC) * C::ES : kOOB;
-    else
-      a_off[i] = (m0 + c * C::VEC) < a.M ? (uint32_t)(r * a.lda + m0 + c * C::VEC) * C::ES : kOOB;
-  }
-#pragma unroll
-  for (int i = 0; i < P::B_IPW; ++i) {
-    const int p = (wave * P::B_IPW + i) * 64 + lane;
-    const int r = p / C::B_CPR;
-    const int c = (p % C::B_CPR) ^ pp_swz<C, C::B_KC, C::B_CPR>(r);
-    if constexpr (C::B_KC)
-      b_off[i] = (n0 + r) < a.N ? (uint32_t)((n0 + r) * a.ldb + c * C::VEC) * C::ES : kOOB;
-    else
-      b_off[i] = (n0 + c * C::VEC) < a.N ? (uint32_t)(r * a.ldb + n0 + c * C::VEC) * C::ES : kOOB;
-  }
   // 32-bit offsets: every operand spans less than 2^31 bytes with 256 rows (of K for an
   // M/N-contiguous operand) to spare, more than the S tiles issued past the end
   const uint32_t a_kstep = C::A_KC ? C::BK * C::ES : (uint32_t)(C::BK * a.lda * C::ES);
   const uint32_t b_kstep = C::B_KC ? C::BK * C::ES : (uint32_t)(C::BK * a.ldb * C::ES);
   const uint32_t a_total = (uint32_t)(a_rows * a.lda * C::ES), b_total = (uint32_t)(b_rows * a.ldb * C::ES);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)lds;
-  const int nk = (a.K + C::BK - 1) / C::BK;
 
-  // Copies of K tile kt into slot u: A blocks first, then B.  Tiles past the end are still
-  // issued (all their chunks read zeros), so that every wave has the same number of copies
-  // in flight at every barrier and the waits can count them.
-  auto copy_tile = [&](int u, int kt) {
-    const uint32_t ao = (uint32_t)kt * a_kstep, bo = (uint32_t)kt * b_kstep;
-    // the tile's buffer: base moved to the tile, size cut by as much (none left past the
-    // end).  The sizes go through readfirstlane: the saturating subtraction is a VALU
-    // instruction, and a descriptor built from a VGPR would not be a scalar operand.
-    const uint32_t an = __builtin_amdgcn_readfirstlane(a_total - min(ao, a_total));
-    const uint32_t bn = __builtin_amdgcn_readfirstlane(b_total - min(bo, b_total));
-    const __amdgpu_buffer_rsrc_t rta = make_rsrc((const char*)a.A + ao, an);
-    const __amdgpu_buffer_rsrc_t rtb = make_rsrc((const char*)a.B + bo, bn);
-    // this wave's first LDS block of each operand tile (its blocks are consecutive)
-    const uint32_t la = lds0 + P::A_OFF + u * C::A_BYTES + (uint32_t)(wave * P::A_IPW) * 1024u;
-    const uint32_t lb = lds0 + P::B_OFF + u * C::B_BYTES + (uint32_t)(wave * P::B_IPW) * 1024u;
-    const int kleft = a.K - kt * C::BK;  // K elements left from this tile's start
-    if ((!C::A_KC && !C::B_KC) || kleft >= C::BK) {
-      pp_copies<P::A_IPW, false>(la, a_off, rta);
-      pp_copies<P::B_IPW, false>(lb, b_off, rtb);
-    } else {  // a ragged last tile or a tile past the end: K-contiguous chunks past K read zeros
-      uint32_t oa[P::A_IPW], ob[P::B_IPW];
-#pragma unroll
-      for (int q = 0; q < P::A_IPW; ++q)
-        oa[q] = !C::A_KC || chunk_k(wave * P::A_IPW + q, C::A_CPR, C::VEC,
-                                    [](int r) { return pp_swz<C, true, C::A_CPR>(r); }) < kleft ? a_off[q] : kOOB;
-#pragma unroll
-      for (int q = 0; q < P::B_IPW; ++q)
-        ob[q] = !C::B_KC || chunk_k(wave * P::B_IPW + q, C::B_CPR, C::VEC,
-                                    [](int r) { return pp_swz<C, true, C::B_CPR>(r); }) < kleft ? b_off[q] : kOOB;
-      pp_copies<P::A_IPW, true>(la, oa, rta);
-      pp_copies<P::B_IPW, true>(lb, ob, rtb);
+  for (;;) {
+    // ---- the segment: tile (tm, tn), K tiles [k0, k1)
+    int tm = tm0, tn = tn0, k0 = 0, k1 = nk;
+    if (!whole) {
+      const int ts = it / nk;
+      k0 = it - ts * nk;
+      k1 = min(nk, k0 + (it_end - it));
+      raster_tile(a.sk_dp + ts, a, tm, tn);
     }
-  };
+    const int m0 = tm * C::BM, n0 = tn * C::BN;
+    // The thread index through an opaque copy: everything derived from it below (fragment
+    // addresses, copy offsets, partial-tile offsets) is computed again for each segment
+    // instead of being hoisted out of the segment loop and held in registers across the
+    // K loop.
+    int lane_t = t;
+    asm volatile("" : "+v"(lane_t));
+    lane_t &= C::THREADS - 1;
+    const int lane = lane_t & 63;
 
-  Acc acc[C::FM][C::FN];
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) acc[i][j] = Acc{};
+    // ---- fragment addresses of this lane, computed once for slot 0.  For a K-contiguous
+    // operand fragments MT rows apart share their swizzle, so fragment f of K step kk sits
+    // at base[kk] + f*MT rows; for an M/N-contiguous operand the K step and the second
+    // transposing read only add whole rows (the swizzle depends on bits 0, 1 and 3 of the
+    // row, which neither touches), so it sits at base[f] + (kk*KT + h*4) rows.  A slot
+    // adds its offset; all of these constants become the reads' immediate offsets.
+    const int xa0 = wm * C::WTM, xb0 = wn * C::WTN;
+    constexpr int A_NB = C::A_KC ? C::KSTEPS : C::FM, B_NB = C::B_KC ? C::KSTEPS : C::FN;
+    uint32_t a_base[A_NB], b_base[B_NB];
+  #pragma unroll
+    for (int v = 0; v < A_NB; ++v)
+      a_base[v] = lds0 + P::A_OFF +
+                  (C::A_KC ? pp_frag_off<C, true, C::A_RB>(xa0, v * C::KT, lane, 0)
+                           : pp_frag_off<C, false, C::A_RB>(xa0 + v * C::MT, 0, lane, 0));
+  #pragma unroll
+    for (int v = 0; v < B_NB; ++v)
+      b_base[v] = lds0 + P::B_OFF +
+                  (C::B_KC ? pp_frag_off<C, true, C::B_RB>(xb0, v * C::KT, lane, 0)
+                           : pp_frag_off<C, false, C::B_RB>(xb0 + v * C::MT, 0, lane, 0));
+    // LDS address of read h of fragment f (K step kk) of an operand in slot u
+    auto a_addr = [&](int u, int kk, int f, int h) -> uint32_t {
+      return C::A_KC ? a_base[kk] + (uint32_t)(u * C::A_BYTES + f * C::MT * C::A_RB)
+                     : a_base[f] + (uint32_t)(u * C::A_BYTES + (kk * C::KT + h * 4) * C::A_RB);
+    };
+    auto b_addr = [&](int u, int kk, int f, int h) -> uint32_t {
+      return C::B_KC ? b_base[kk] + (uint32_t)(u * C::B_BYTES + f * C::MT * C::B_RB)
+                     : b_base[f] + (uint32_t)(u * C::B_BYTES + (kk * C::KT + h * 4) * C::B_RB);
+    };
 
-  // ---- fragment addresses of this lane, computed once for slot 0.  For a K-contiguous
-  // operand fragments MT rows apart share their swizzle, so fragment f of K step kk sits
-  // at base[kk] + f*MT rows; for an M/N-contiguous operand the K step and the second
-  // transposing read only add whole rows (the swizzle depends on bits 0, 1 and 3 of the
-  // row, which neither touches), so it sits at base[f] + (kk*KT + h*4) rows.  A slot
-  // adds its offset; all of these constants become the reads' immediate offsets.
-  const int xa0 = wm * C::WTM, xb0 = wn * C::WTN;
-  constexpr int A_NB = C::A_KC ? C::KSTEPS : C::FM, B_NB = C::B_KC ? C::KSTEPS : C::FN;
-  uint32_t a_base[A_NB], b_base[B_NB];
-#pragma unroll
-  for (int v = 0; v < A_NB; ++v)
-    a_base[v] = lds0 + P::A_OFF +
-                (C::A_KC ? pp_frag_off<C, true, C::A_RB>(xa0, v * C::KT, lane, 0)
-                         : pp_frag_off<C, false, C::A_RB>(xa0 + v * C::MT, 0, lane, 0));
-#pragma unroll
-  for (int v = 0; v < B_NB; ++v)
-    b_base[v] = lds0 + P::B_OFF +
-                (C::B_KC ? pp_frag_off<C, true, C::B_RB>(xb0, v * C::KT, lane, 0)
-                         : pp_frag_off<C, false, C::B_RB>(xb0 + v * C::MT, 0, lane, 0));
-  // LDS address of read h of fragment f (K step kk) of an operand in slot u
-  auto a_addr = [&](int u, int kk, int f, int h) -> uint32_t {
-    return C::A_KC ? a_base[kk] + (uint32_t)(u * C::A_BYTES + f * C::MT * C::A_RB)
-                   : a_base[f] + (uint32_t)(u * C::A_BYTES + (kk * C::KT + h * 4) * C::A_RB);
-  };
-  auto b_addr = [&](int u, int kk, int f, int h) -> uint32_t {
-    return C::B_KC ? b_base[kk] + (uint32_t)(u * C::B_BYTES + f * C::MT * C::B_RB)
-                   : b_base[f] + (uint32_t)(u * C::B_BYTES + (kk * C::KT + h * 4) * C::B_RB);
-  };
-
-  bf16x8 fa[C::FM], fb[C::FN];
-  // E4M3: the raw 8-byte A fragments, widened by the compute phase that uses them
-  i32x2 ra8[P::E8 ? C::FM : 1];
-  auto rd = [&](uint32_t addr) -> u16x4 {
-    return __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                         (__attribute__((address_space(3))) s16x4*)(uintptr_t)addr));
-  };
-  auto rd8 = [&](uint32_t addr, bool tr) -> i32x2 {
-    if (tr) return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(uintptr_t)addr);
-    return *(__attribute__((address_space(3))) i32x2*)(uintptr_t)addr;
-  };
-  // Memory phase: the fragments of K step kk of the tile in slot u (E4M3 tiles: all reads
-  // first, then the widening, so that the reads are in flight together).
-  auto read_step = [&](auto uc, auto kc) {
-    constexpr int u = decltype(uc)::value, kk = decltype(kc)::value;
-    if constexpr (P::E8) {
-      // B fragments and the first A fragment are widened here; the other A fragments in
-      // the compute phase, between the MFMAs (the conversions share the issue port with
-      // the MFMAs of the wave computing next to this one)
-      i32x2 rb8[C::FN];
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i) ra8[i] = rd8(a_addr(u, kk, i, 0), !C::A_KC);
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) rb8[j] = rd8(b_addr(u, kk, j, 0), !C::B_KC);
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) fb[j] = pp_widen8(rb8[j]);
-      fa[0] = pp_widen8(ra8[0]);
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-      if constexpr (C::A_KC) {
-        fa[i] = *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)a_addr(u, kk, i, 0);
-      } else {
-        const u16x4 lo = rd(a_addr(u, kk, i, 0)), hi = rd(a_addr(u, kk, i, 1));
-        fa[i] = __builtin_bit_cast(bf16x8, (u16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    bf16x8 fa[C::FM], fb[C::FN];
+    // E4M3: the raw 8-byte A fragments, widened by the compute phase that uses them
+    i32x2 ra8[P::E8 ? C::FM : 1];
+    auto rd = [&](uint32_t addr) -> u16x4 {
+      return __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                           (__attribute__((address_space(3))) s16x4*)(uintptr_t)addr));
+    };
+    auto rd8 = [&](uint32_t addr, bool tr) -> i32x2 {
+      if (tr) return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(uintptr_t)addr);
+      return *(__attribute__((address_space(3))) i32x2*)(uintptr_t)addr;
+    };
+    // Memory phase: the fragments of K step kk of the tile in slot u (E4M3 tiles: all reads
+    // first, then the widening, so that the reads are in flight together).
+    auto read_step = [&](auto uc, auto kc) {
+      constexpr int u = decltype(uc)::value, kk = decltype(kc)::value;
+      if constexpr (P::E8) {
+        // B fragments and the first A fragment are widened here; the other A fragments in
+        // the compute phase, between the MFMAs (the conversions share the issue port with
+        // the MFMAs of the wave computing next to this one)
+        i32x2 rb8[C::FN];
+  #pragma unroll
+        for (int i = 0; i < C::FM; ++i) ra8[i] = rd8(a_addr(u, kk, i, 0), !C::A_KC);
+  #pragma unroll
+        for (int j = 0; j < C::FN; ++j) rb8[j] = rd8(b_addr(u, kk, j, 0), !C::B_KC);
+  #pragma unroll
+        for (int j = 0; j < C::FN; ++j) fb[j] = pp_widen8(rb8[j]);
+        fa[0] = pp_widen8(ra8[0]);
+        return;
       }
+  #pragma unroll
+      for (int i = 0; i < C::FM; ++i) {
+        if constexpr (C::A_KC) {
+          fa[i] = *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)a_addr(u, kk, i, 0);
+        } else {
+          const u16x4 lo = rd(a_addr(u, kk, i, 0)), hi = rd(a_addr(u, kk, i, 1));
+          fa[i] = __builtin_bit_cast(bf16x8, (u16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        }
+      }
+  #pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        if constexpr (C::B_KC) {
+          fb[j] = *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)b_addr(u, kk, j, 0);
+        } else {
+          const u16x4 lo = rd(b_addr(u, kk, j, 0)), hi = rd(b_addr(u, kk, j, 1));
+          fb[j] = __builtin_bit_cast(bf16x8, (u16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        }
+      }
+    };
+    Acc acc[C::FM][C::FN];
+    // Compute phase: the MFMA cluster of one K step, at raised wave priority.  With E4M3
+    // tiles the MFMAs of A row i are followed by the four conversions of A fragment i + 1.
+    static_assert(!P::E8 || C::FN == 4, "four conversions per A fragment, one after each MFMA of a row");
+    int wpart[4];
+    auto compute_step = [&]() {
+      __builtin_amdgcn_s_setprio(1);
+      static_for<C::FM * C::FN>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int row = i / C::FN, col = i % C::FN;
+        mma(acc[row][col], fb[col], fa[row]);
+        if constexpr (P::E8 && row + 1 < C::FM) {
+          wpart[col] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ra8[row + 1][col >> 1], 1.0f,
+                                                                                         (col & 1) != 0));
+          if constexpr (col == 3)
+            fa[row + 1] = __builtin_bit_cast(bf16x8, (i32x4){wpart[0], wpart[1], wpart[2], wpart[3]});
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      __builtin_amdgcn_s_setprio(0);
+    };
+    // copies allowed in flight at the barrier before a tile's first K step is read: those
+    // of the S - 2 tiles issued after it
+    constexpr int VM = (S - 2) * P::IPW;
+    constexpr int KS = C::KSTEPS;
+
+
+    // ---- this wave's copy instructions: instruction i fills LDS block wave*IPW + i of the
+    // tile (A blocks, then B); this lane fills chunk p = blk*64 + lane of its operand, row
+    // p / CPR, physical chunk p % CPR, which holds logical chunk (p % CPR) ^ swizzle(row).
+    // The per-lane offsets are relative to the start of a K tile, and fixed: each K tile
+    // gets its own buffer descriptor (base moved to the tile, size cut by as much), built
+    // with scalar arithmetic.  A chunk in a row or column past M or N gets an offset past
+    // every buffer.  Rows at or past the segment's end in K of an M/N-contiguous operand
+    // then lie past the tile's buffer and read zeros; a K-contiguous operand's chunks
+    // there (a ragged last tile, or a tile past the segment) are sent past the buffer in
+    // copy_tile.
+    uint32_t a_off[P::A_IPW], b_off[P::B_IPW];
+    auto chunk_k = [&](int blk, int CPR, int VEC, auto swzc) {  // K index of a K-contiguous chunk
+      const int p = blk * 64 + lane;
+      return ((p % CPR) ^ swzc(p / CPR)) * VEC;
+    };
+#pragma unroll
+    for (int i = 0; i < P::A_IPW; ++i) {
+      const int p = (wave * P::A_IPW + i) * 64 + lane;
+      const int r = p / C::A_CPR;
+      const int c = (p % C::A_CPR) ^ pp_swz<C, C::A_KC, C::A_CPR>(r);
+      if constexpr (C::A_KC)
+        a_off[i] = (m0 + r) < a.M ? (uint32_t)((m0 + r) * a.lda + c * C::VEC) * C::ES : kOOB;
+      else
+        a_off[i] = (m0 + c * C::VEC) < a.M ? (uint32_t)(r * a.lda + m0 + c * C::VEC) * C::ES : kOOB;
     }
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      if constexpr (C::B_KC) {
-        fb[j] = *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)b_addr(u, kk, j, 0);
-      } else {
-        const u16x4 lo = rd(b_addr(u, kk, j, 0)), hi = rd(b_addr(u, kk, j, 1));
-        fb[j] = __builtin_bit_cast(bf16x8, (u16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-      }
+    for (int i = 0; i < P::B_IPW; ++i) {
+      const int p = (wave * P::B_IPW + i) * 64 + lane;
+      const int r = p / C::B_CPR;
+      const int c = (p % C::B_CPR) ^ pp_swz<C, C::B_KC, C::B_CPR>(r);
+      if constexpr (C::B_KC)
+        b_off[i] = (n0 + r) < a.N ? (uint32_t)((n0 + r) * a.ldb + c * C::VEC) * C::ES : kOOB;
+      else
+        b_off[i] = (n0 + c * C::VEC) < a.N ? (uint32_t)(r * a.ldb + n0 + c * C::VEC) * C::ES : kOOB;
     }
-  };
-  // Compute phase: the MFMA cluster of one K step, at raised wave priority.  With E4M3
-  // tiles the MFMAs of A row i are followed by the four conversions of A fragment i + 1.
-  static_assert(!P::E8 || C::FN == 4, "four conversions per A fragment, one after each MFMA of a row");
-  int wpart[4];
-  auto compute_step = [&]() {
-    __builtin_amdgcn_s_setprio(1);
-    static_for<C::FM * C::FN>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      constexpr int row = i / C::FN, col = i % C::FN;
-      mma(acc[row][col], fb[col], fa[row]);
-      if constexpr (P::E8 && row + 1 < C::FM) {
-        wpart[col] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ra8[row + 1][col >> 1], 1.0f,
-                                                                                       (col & 1) != 0));
-        if constexpr (col == 3)
-          fa[row + 1] = __builtin_bit_cast(bf16x8, (i32x4){wpart[0], wpart[1], wpart[2], wpart[3]});
+    // the segment's end in K (elements), and the bytes of each operand before it: all of
+    // a K-contiguous operand, the rows before it of an M/N-contiguous one
+    const int kend = min(a.K, k1 * C::BK);
+    const uint32_t a_lim = C::A_KC || !SK ? a_total : min(a_total, (uint32_t)(kend * a.lda * C::ES));
+    const uint32_t b_lim = C::B_KC || !SK ? b_total : min(b_total, (uint32_t)(kend * a.ldb * C::ES));
+
+    // Copies of K tile kt into slot u: A blocks first, then B.  Tiles past the segment are
+    // still issued (all their chunks read zeros), so that every wave has the same number
+    // of copies in flight at every barrier and the waits can count them.
+    auto copy_tile = [&](int u, int kt) {
+      const uint32_t ao = (uint32_t)kt * a_kstep, bo = (uint32_t)kt * b_kstep;
+      // the tile's buffer: base moved to the tile, size cut by as much (none left past the
+      // end).  The sizes go through readfirstlane: the saturating subtraction is a VALU
+      // instruction, and a descriptor built from a VGPR would not be a scalar operand.
+      const uint32_t an = __builtin_amdgcn_readfirstlane(a_lim - min(ao, a_lim));
+      const uint32_t bn = __builtin_amdgcn_readfirstlane(b_lim - min(bo, b_lim));
+      const __amdgpu_buffer_rsrc_t rta = make_rsrc((const char*)a.A + ao, an);
+      const __amdgpu_buffer_rsrc_t rtb = make_rsrc((const char*)a.B + bo, bn);
+      // this wave's first LDS block of each operand tile (its blocks are consecutive)
+      const uint32_t la = lds0 + P::A_OFF + u * C::A_BYTES + (uint32_t)(wave * P::A_IPW) * 1024u;
+      const uint32_t lb = lds0 + P::B_OFF + u * C::B_BYTES + (uint32_t)(wave * P::B_IPW) * 1024u;
+      const int kleft = kend - kt * C::BK;  // K elements left from this tile's start
+      if ((!C::A_KC && !C::B_KC) || kleft >= C::BK) {
+        pp_copies<P::A_IPW, false>(la, a_off, rta);
+        pp_copies<P::B_IPW, false>(lb, b_off, rtb);
+      } else {  // a ragged last tile or a tile past the segment: K-contiguous chunks there read zeros
+        uint32_t oa[P::A_IPW], ob[P::B_IPW];
+#pragma unroll
+        for (int q = 0; q < P::A_IPW; ++q)
+          oa[q] = !C::A_KC || chunk_k(wave * P::A_IPW + q, C::A_CPR, C::VEC,
+                                      [](int r) { return pp_swz<C, true, C::A_CPR>(r); }) < kleft ? a_off[q] : kOOB;
+#pragma unroll
+        for (int q = 0; q < P::B_IPW; ++q)
+          ob[q] = !C::B_KC || chunk_k(wave * P::B_IPW + q, C::B_CPR, C::VEC,
+                                      [](int r) { return pp_swz<C, true, C::B_CPR>(r); }) < kleft ? b_off[q] : kOOB;
+        pp_copies<P::A_IPW, true>(la, oa, rta);
+        pp_copies<P::B_IPW, true>(lb, ob, rtb);
       }
+    };
+
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) acc[i][j] = Acc{};
+
+    // ---- prologue: K tiles k0 .. k0+S-1 into slots 0 .. S-1; wait for the first
+    static_for<S>([&](auto uc) { copy_tile(decltype(uc)::value, k0 + decltype(uc)::value); });
+    pp_wait_vm_barrier<(S - 1) * P::IPW>();
+
+    // ---- main loop over K steps h = (tile t, step kk), S tiles per iteration so that slots
+    // are compile-time constants: tile t sits in slot (t - k0) % S.  Group 0 computes step h
+    // while group 1 reads it, then group 1 computes h while group 0 reads h + 1; barriers
+    // B(2h+1) and B(2h+2) separate the phases.  Once both groups have read the last step of
+    // tile t (B(2h+1) of that step) tile t + S replaces it: group 0 issues its copies right
+    // after that barrier, group 1 at the start of its next memory phase.  Before the
+    // barrier after which the first step of tile t + 1 is read, every wave waits for its
+    // copies of tile t + 1.  Both groups run 2 (k1 - k0) KS barriers in all.
+    if (grp == 0) {
+      read_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
       __builtin_amdgcn_sched_barrier(0);
-    });
-    __builtin_amdgcn_s_setprio(0);
-  };
-  // copies allowed in flight at the barrier before a tile's first K step is read: those
-  // of the S - 2 tiles issued after it
-  constexpr int VM = (S - 2) * P::IPW;
-  constexpr int KS = C::KSTEPS;
-
-  // ---- prologue: K tiles 0 .. S-1 into slots 0 .. S-1; wait for tile 0
-  static_for<S>([&](auto uc) { copy_tile(decltype(uc)::value, decltype(uc)::value); });
-  pp_wait_vm_barrier<(S - 1) * P::IPW>();
-
-  // ---- main loop over K steps h = (tile t, step kk), S tiles per iteration so that slots
-  // are compile-time constants: tile t sits in slot t % S.  Group 0 computes step h while
-  // group 1 reads it, then group 1 computes h while group 0 reads h + 1; barriers B(2h+1)
-  // and B(2h+2) separate the phases.  Once both groups have read the last step of tile t
-  // (B(2h+1) of that step) tile t + S replaces it: group 0 issues its copies right after
-  // that barrier, group 1 at the start of its next memory phase.  Before the barrier
-  // after which the first step of tile t + 1 is read, every wave waits for its copies of
-  // tile t + 1.  Both groups run 2 nk KS barriers in all.
-  if (grp == 0) {
-    read_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    __builtin_amdgcn_sched_barrier(0);
-    pp_wait_lds_barrier();  // B0
-    for (int kt0 = 0; kt0 < nk; kt0 += S) {
-      static_for<S>([&](auto uc) {
-        constexpr int u = decltype(uc)::value;
-        const int kt = kt0 + u;
-        if (kt < nk) {
-          static_for<KS>([&](auto kc) {
-            constexpr int kk = decltype(kc)::value;
-            constexpr bool last = kk == KS - 1;
-            compute_step();
-            if constexpr (last) {
-              pp_wait_vm_barrier<VM>();  // B(2h+1): tile t + 1 complete, slot u free
-            } else {
-              pp_wait_lds_barrier();  // B(2h+1)
-            }
-            // the fragment reads go out first, then the copies (whose issue can wait on a
-            // full address queue)
-            if (!last || kt + 1 < nk)
-              read_step(std::integral_constant<int, last ? (u + 1) % S : u>{},
-                        std::integral_constant<int, last ? 0 : kk + 1>{});
-            if constexpr (last) copy_tile(u, kt + S);
-            __builtin_amdgcn_sched_barrier(0);
-            if (!last || kt + 1 < nk) pp_wait_lds_barrier();  // B(2h+2)
-          });
-        }
-      });
+      pp_wait_lds_barrier();  // B0
+      for (int kt0 = k0; kt0 < k1; kt0 += S) {
+        static_for<S>([&](auto uc) {
+          constexpr int u = decltype(uc)::value;
+          const int kt = kt0 + u;
+          if (kt < k1) {
+            static_for<KS>([&](auto kc) {
+              constexpr int kk = decltype(kc)::value;
+              constexpr bool last = kk == KS - 1;
+              compute_step();
+              if constexpr (last) {
+                pp_wait_vm_barrier<VM>();  // B(2h+1): tile t + 1 complete, slot u free
+              } else {
+                pp_wait_lds_barrier();  // B(2h+1)
+              }
+              // the fragment reads go out first, then the copies (whose issue can wait on a
+              // full address queue)
+              if (!last || kt + 1 < k1)
+                read_step(std::integral_constant<int, last ? (u + 1) % S : u>{},
+                          std::integral_constant<int, last ? 0 : kk + 1>{});
+              if constexpr (last) copy_tile(u, kt + S);
+              __builtin_amdgcn_sched_barrier(0);
+              if (!last || kt + 1 < k1) pp_wait_lds_barrier();  // B(2h+2)
+            });
+          }
+        });
+      }
+    } else {
+      pp_wait_lds_barrier();  // B0
+      for (int kt0 = k0; kt0 < k1; kt0 += S) {
+        static_for<S>([&](auto uc) {
+          constexpr int u = decltype(uc)::value;
+          const int kt = kt0 + u;
+          if (kt < k1) {
+            static_for<KS>([&](auto kc) {
+              constexpr int kk = decltype(kc)::value;
+              constexpr bool last = kk == KS - 1;
+              read_step(uc, kc);
+              // the slot of tile t - 1, left by both groups at the last B(2h+1) of that tile
+              if (kk == 0 && kt > k0) copy_tile((u + S - 1) % S, kt - 1 + S);
+              __builtin_amdgcn_sched_barrier(0);
+              if constexpr (last) {
+                pp_wait_vm_barrier<VM>();  // B(2h+1)
+              } else {
+                pp_wait_lds_barrier();
+              }
+              compute_step();
+              if (!last || kt + 1 < k1) {
+                pp_wait_lds_barrier();  // B(2h+2)
+              }
+            });
+          }
+        });
+      }
     }
-  } else {
-    pp_wait_lds_barrier();  // B0
-    for (int kt0 = 0; kt0 < nk; kt0 += S) {
-      static_for<S>([&](auto uc) {
-        constexpr int u = decltype(uc)::value;
-        const int kt = kt0 + u;
-        if (kt < nk) {
-          static_for<KS>([&](auto kc) {
-            constexpr int kk = decltype(kc)::value;
-            constexpr bool last = kk == KS - 1;
-            read_step(uc, kc);
-            // the slot of tile t - 1, left by both groups at the last B(2h+1) of that tile
-            if (kk == 0 && kt > 0) copy_tile((u + S - 1) % S, kt - 1 + S);
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (last) {
-              pp_wait_vm_barrier<VM>();  // B(2h+1)
-            } else {
-              pp_wait_lds_barrier();
+    // the last copies (past the segment) land before the LDS is reused or released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    if constexpr (SK) {
+      if (k0 != 0) {
+        // Not the tile's first K tile: leave the partial sum in this workgroup's slot and
+        // raise its flag.  Every wave waits for its stores to complete (to this XCD's L2)
+        // before the workgroup barrier; then one thread raises the flag with release
+        // semantics at device scope, which first writes the L2's dirty lines back, so the
+        // owner (perhaps on another XCD, behind another L2) reads the partial from memory.
+        // This is always the workgroup's first segment.
+        pp_store_partial<C>(a.ws + (size_t)slot * (C::BM * C::BN), acc, (uint32_t)lane_t * 16u);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (t == 0) __hip_atomic_store(a.flags + slot, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        if (k1 < nk) {
+          // The tile's first K tiles: the rest of its K loop was summed by the next
+          // workgroups of the sequence, each starting inside this tile.  Wait for their
+          // flags, then add their partials in K order and clear the flags for the next call.
+          // The flag loads have acquire semantics at device scope (they invalidate this
+          // XCD's L2 and the CU's cache), and the barrier orders every wave's partial loads
+          // after them.
+          __shared__ int sk_ok;
+          const int ts = it / nk;
+          const int last_slot = ((ts + 1) * nk - 1) / a.sk_iters;
+          if (t == 0) {
+            int ok = 1;
+            for (int s2 = slot + 1; s2 <= last_slot && ok; ++s2) {
+              int n = 0;
+              while (__hip_atomic_load(a.flags + s2, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) {
+                if (++n >= kStreamKSpins) {
+                  ok = 0;
+                  break;
+                }
+                __builtin_amdgcn_s_sleep(8);
+              }
             }
-            compute_step();
-            if (!last || kt + 1 < nk) {
-              pp_wait_lds_barrier();  // B(2h+2)
-            }
-          });
+            sk_ok = ok;
+          }
+          __syncthreads();
+          if (sk_ok) {
+            for (int s2 = slot + 1; s2 <= last_slot; ++s2)
+              pp_add_partial<C>(a.ws + (size_t)s2 * (C::BM * C::BN), acc, (uint32_t)lane_t * 16u);
+          } else {
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+              for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                for (int e = 0; e < C::ACC; ++e) acc[i][j][e] = __builtin_nanf("");
+          }
+          if (t == 0)
+            for (int s2 = slot + 1; s2 <= last_slot; ++s2)
+              __hip_atomic_store(a.flags + s2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-      });
+        store_tile<C>(a, acc, m0 + xa0, n0 + xb0, lane);
+      }
+      it += k1 - k0;
+      if (whole || it >= it_end) break;
+      // the next segment's waits count its copies with vmcnt, which also counts this
+      // segment's stores, and stores may complete after later loads: drain them first
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      store_tile<C>(a, acc, m0 + xa0, n0 + xb0, lane);
+      break;
     }
   }
-  // the last copies (past K) land before the workgroup's LDS is released
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-  store_tile<C>(a, acc, m0 + xa0, n0 + xb0, lane);
 }
 
 template <class C>
 hipError_t launch_pp(const GemmArgs& a, hipStream_t s) {
   if (a.splits != 1 || a.tri != TRI_NONE || a.kband != KBAND_NONE || a.dual) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((gemm_pp_kernel<C>), dim3(grid_tiles(a)), dim3(C::THREADS), 0, s, a);
+  if (a.sk_tiles > 0) {
+    if (!a.ws || !a.flags || a.sk_grid < 1 || a.sk_iters < 1 || a.epoch == 0 ||
+        (int64_t)a.sk_grid * a.sk_iters < (int64_t)a.sk_tiles * ((a.K + C::BK - 1) / C::BK) ||
+        a.sk_dp + a.sk_tiles != a.tiles_m * a.tiles_n)
+      return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((gemm_pp_kernel<C, true>), dim3(a.sk_dp + a.sk_grid), dim3(C::THREADS), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((gemm_pp_kernel<C, false>), dim3(grid_tiles(a)), dim3(C::THREADS), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -38,15 +38,25 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 // maps are bijections, so every tile is computed exactly once.  With split-K the ids
 // cover tiles x splits; the splits of one tile are neighbours in the remapped order
 // (so they run on one XCD) and `split` is the id's position among them.
-__device__ inline void tile_of(int bid, const GemmArgs& a, int& tm, int& tn, int& split) {
-  const int total = grid_tiles(a);
-  int L = bid;
-  if (a.xcd > 1) {
-    const int q = total / a.xcd;
-    if (bid < q * a.xcd) L = (bid % a.xcd) * q + bid / a.xcd;
+__device__ inline int xcd_remap(int bid, int total, int xcd) {
+  if (xcd > 1) {
+    const int q = total / xcd;
+    if (bid < q * xcd) return (bid % xcd) * q + bid / xcd;
   }
+  return bid;
+}
+
+// Position L of the raster order -> output tile (tm, tn).
+__device__ inline void raster_tile(int L, const GemmArgs& a, int& tm, int& tn);
+
+__device__ inline void tile_of(int bid, const GemmArgs& a, int& tm, int& tn, int& split) {
+  int L = xcd_remap(bid, grid_tiles(a), a.xcd);
   split = L % a.splits;
   L /= a.splits;
+  raster_tile(L, a, tm, tn);
+}
+
+__device__ inline void raster_tile(int L, const GemmArgs& a, int& tm, int& tn) {
   if (a.tri) {
     // triangle of the tile grid, row by row: tile row r holds tiles (r, 0 .. r), which
     // start at L = r(r+1)/2.  r from the square root, then corrected to be exact.

@@ -87,6 +87,36 @@ bool split_allowed(const Policy& p, const Problem& pr, int splits, int64_t ws_fl
   return split_ws_floats(p, pr, splits) <= ws_floats;
 }
 
+// Fewest K tiles a stream-K workgroup sums: below this the partial hand-offs cost more
+// than the balance gains.
+constexpr int kStreamKMinIters = 4;
+
+StreamK stream_k_plan(const Policy& p, const Problem& pr, int cu_count, int grid) {
+  StreamK s;
+  // the ping-pong kernels on plain operands; the 128-deep E4M3 tile has no stream-K form
+  // (its registers would spill)
+  if (p.kind != KIND_MFMA || p.pipe != 2 || pr.blas3 || pr.mx || (p.in_mode == 5 && p.BK > 64)) return s;
+  if (cu_count <= 0) cu_count = 256;
+  const int64_t tiles = ((pr.M + p.BM - 1) / p.BM) * ((pr.N + p.BN - 1) / p.BN);
+  const int64_t nk = (pr.K + p.BK - 1) / p.BK;
+  // one workgroup per CU at a time (the ping-pong tiles fill the LDS), so a grid of at
+  // most one per CU is resident at once: every owner's wait ends
+  const int64_t G = grid > 0 ? (grid < cu_count ? grid : cu_count) : cu_count;
+  if (tiles == 0 || nk < 2 || (grid == 0 && tiles % G == 0)) return s;
+  const int64_t dp = (tiles / G) * G;
+  const int64_t rest = tiles - dp;
+  if (rest == 0) return s;
+  int64_t iters = (rest * nk + G - 1) / G;
+  if (iters < kStreamKMinIters) iters = nk < kStreamKMinIters ? nk : kStreamKMinIters;
+  s.dp = (int)dp;
+  s.tiles = (int)rest;
+  s.iters = (int)iters;
+  s.grid = (int)((rest * nk + iters - 1) / iters);
+  return s;
+}
+
+int64_t stream_k_ws_floats(const Policy& p, const StreamK& s) { return (int64_t)s.grid * p.BM * p.BN; }
+
 int policy_select(const Problem& pr, int cu_count, int64_t ws_floats, int* splits) {
   if (cu_count <= 0) cu_count = 256;
   int best = policy_find("simt_generic");

@@ -26,8 +26,9 @@
  * E4M3 runs with unit scale: any scaling is the caller's (alpha may carry it).
  *
  * Memory and ownership.  A, B and C are device pointers owned by the caller.  The
- * handle owns its host-side state and one 256 MiB device workspace for split-K and the
- * BLAS3 calls (allocated by gemm_create, freed by gemm_destroy).  gemm_run never allocates,
+ * handle owns its host-side state, one 256 MiB device workspace for split-K, stream-K
+ * and the BLAS3 calls, and 64 KiB of stream-K flags (allocated by gemm_create, freed by
+ * gemm_destroy).  gemm_run never allocates,
  * never synchronises and returns once the kernel is enqueued on the handle's stream;
  * faults during execution surface at the caller's next synchronisation.  A handle
  * must be used from one host thread at a time, and its calls must not overlap on
@@ -39,6 +40,19 @@
  * fp32 partial to the workspace and a second kernel on the same stream adds the
  * partials in split order and applies alpha and beta, so results are deterministic
  * (bitwise the same run to run) but rounded differently from the unsplit sum.
+ *
+ * Stream-K (by policy name only: "<ping-pong policy>+streamk", see gemm_set_policy).  The
+ * whole rounds of tiles over the CUs run one tile per workgroup, and the K loops of the
+ * remaining tiles are laid end to end and shared evenly by one further workgroup per CU
+ * (or the number the name gives).  The shape-driven choice does not use it: on 160 or 400
+ * tiles of 256 x 256 it measured slower than the plain grid (its workgroups sit at
+ * scattered K offsets, which costs the L2 reuse of workgroups stepping through K
+ * together).  A workgroup whose share starts inside a tile leaves
+ * its fp32 partial in the workspace; the workgroup holding the tile's first K steps adds
+ * those partials in K order and runs the epilogue.  Results are deterministic for a given
+ * shape and device, and rounded differently from the unsplit sum.  The hand-off waits
+ * need every workgroup of the call resident on the device in turn; with the device
+ * shared by other work for seconds a wait gives up and the tile is written as NaN.
  *
  * Errors.  Arguments are checked before anything is launched; on any error status
  * nothing is launched and nothing is written.
@@ -93,9 +107,10 @@ typedef enum {
 } gemm_status_t;
 
 /* Creates a handle bound to HIP device `device`; reads its CU count, builds the
- * tile-policy table and allocates the split-K workspace on that device (if that
- * allocation fails the handle still works, without split-K).  The handle starts on
- * the default stream (NULL).  On error *h is set to NULL. */
+ * tile-policy table and allocates the workspace and the stream-K flags on that device,
+ * zeroing the flags and waiting for that (if an allocation fails the handle still works,
+ * without split-K and stream-K).  The handle starts on the default stream (NULL).  On
+ * error *h is set to NULL. */
 gemm_status_t gemm_create(gemm_handle_t* h, int device);
 
 /* Releases the handle and its workspace (hipFree waits for the device's work in
@@ -116,8 +131,9 @@ gemm_status_t gemm_run(gemm_handle_t h, int transA, int transB, int64_t M, int64
 
 /* The same call as gemm_run, for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  It needs no
- * handle and calls no allocating routine.  The split-K partials, which gemm_run keeps in
- * its handle's workspace, go to a device array of GEMM_STATIC_SCRATCH_BYTES instead.
+ * handle and calls no allocating routine.  The split-K and stream-K partials and the
+ * stream-K flags, which gemm_run keeps in its handle's workspace, go to a device array
+ * instead: GEMM_STATIC_SCRATCH_BYTES of partials, then 64 KiB of flags.
  *
  * The array: the library's code object holds one copy per device it runs on, placed by
  * the loader and held until the process ends.  Every call on a device shares that copy,
@@ -134,8 +150,8 @@ gemm_status_t gemm_run(gemm_handle_t h, int transA, int transB, int64_t M, int64
  *
  * Errors: as gemm_run, plus these.
  * - INVALID_VALUE: a bad device index (or one of 64 or more), or an unknown policy name.
- * - NOT_SUPPORTED: a forced split whose partials would exceed GEMM_STATIC_SCRATCH_BYTES.
- *   The shape-driven choice never needs more. */
+ * - NOT_SUPPORTED: a forced split or stream-K grid whose partials would exceed
+ *   GEMM_STATIC_SCRATCH_BYTES.  The shape-driven choice never needs more. */
 #define GEMM_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
 gemm_status_t gemm_run_noalloc(int device, void* stream, const char* policy, int transA, int transB,
                                int64_t M, int64_t N, int64_t K, float alpha, const void* A,
@@ -187,7 +203,8 @@ gemm_status_t gemm_check_args(int transA, int transB, int64_t M, int64_t N, int6
 /* Writes the name of the policy gemm_run (gemm_run_mx for the block-scaled dtypes,
  * with transA = 0, transB = 1) would use for these arguments into
  * name[len] (NUL-terminated, truncated to fit), with "+sk<S>" appended when the call
- * is split S ways along K.  The pointers are only inspected for alignment.  h may be
+ * is split S ways along K, "+streamk" (or "+streamk<G>") when a forced stream-K policy
+ * runs stream-K on these arguments.  The pointers are only inspected for alignment.  h may be
  * NULL: then a 256-CU device with a workspace and no forced policy are assumed.
  * Pure host code. */
 gemm_status_t gemm_query_policy(gemm_handle_t h, int transA, int transB, int64_t M, int64_t N,
@@ -198,7 +215,9 @@ gemm_status_t gemm_query_policy(gemm_handle_t h, int transA, int transB, int64_t
 /* Forces the named policy for later gemm_run calls on this handle (for ablations and
  * invariance checks); NULL or "auto" restores the shape-driven choice.  The name is a
  * table entry, optionally followed by "+sk<S>" (S = 2, 4, 8 or 16; direct-to-LDS
- * policies only) to force split-K.  A forced policy that cannot serve a call (dtype,
+ * policies only) to force split-K, or by "+streamk" (ping-pong policies only) to force
+ * stream-K with one stream-K workgroup per CU, "+streamk<G>" with G of them (1..4096,
+ * at most the CU count is used); a forced stream-K on a grid of whole rounds runs plain.  A forced policy that cannot serve a call (dtype,
  * alignment, a split that leaves a split fewer than two K tiles or does not fit the
  * workspace) returns NOT_SUPPORTED from gemm_run.  Unknown names return
  * INVALID_VALUE. */

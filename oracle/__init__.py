@@ -27,6 +27,8 @@ C_F32 = 0
 C_BF16 = 1
 C_E4M3 = 2
 
+_SAN_LIB = os.path.join(_HERE, "liboracle_san.so")
+
 _lib = None
 
 
@@ -40,13 +42,31 @@ def build() -> str:
     return _LIB
 
 
+def build_sanitized() -> str:
+    """The same source with AddressSanitizer and UndefinedBehaviorSanitizer (clang, whose
+    runtime the sanitized GEMM library shares), for the CPU tests' sanitizer run; load it
+    with ORACLE_LIB pointing at it."""
+    if os.path.exists(_SAN_LIB) and os.path.getmtime(_SAN_LIB) >= os.path.getmtime(_SRC):
+        return _SAN_LIB
+    tmp = _SAN_LIB + ".tmp"
+    cmd = ["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+           "-ffp-contract=off", "-fno-fast-math", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=undefined", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _SAN_LIB)
+    return _SAN_LIB
+
+
 def load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB)
+    path = os.environ.get("ORACLE_LIB")
+    if not path:
+        path = _LIB
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+    lib = ctypes.CDLL(path)
     i64 = ctypes.c_int64
     vp = ctypes.c_void_p
     lib.oracle_gemm.restype = ctypes.c_int

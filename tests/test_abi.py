@@ -95,10 +95,14 @@ def test_noalloc_checks_arguments_before_the_device():
     assert call(M=-1) == INVALID
     assert call(policy="no_such_policy") == INVALID
     assert call(policy="bf16_pp_m256n256k32_w2x4_mt16_s4+sk4") == INVALID  # split-K: ring policies only
+    assert call(policy="bf16_dma_m64n64k64_w2x2_mt16_s4+streamk") == INVALID  # stream-K: ping-pong only
+    for bad in ("+streamk0", "+streamk4097", "+streamkx", "+stream", "+sk3"):
+        assert call(policy="bf16_pp_m256n256k32_w2x4_mt16_s4" + bad) == INVALID, bad
     st = call()
     if st != OK:  # no GPU here
         assert st == NOT_INIT
         assert call(policy="auto") == NOT_INIT
+        assert call(policy="bf16_pp_m256n256k32_w2x4_mt16_s4+streamk7") == NOT_INIT
 
 
 def test_create_without_device_or_with_one():
@@ -129,6 +133,19 @@ def test_policy_selection_is_shape_driven_and_deterministic():
     # split-K only where the tiles alone leave most CUs idle
     assert "+sk" in q(512, 512, 8192) and "+sk" not in q(4096, 4096, 4096)
     assert "+sk" not in q(512, 512, 256)  # too few K tiles to share
+
+
+def test_large_workload_choices():
+    """The shape-driven choice for the large workloads: a large ping-pong tile (256 x 256,
+    or 192 x 256 where 2048 rows leave a 256-row grid at 0.63 of a round), never split and
+    never stream-K (stream-K is named only)."""
+    q = lambda *a, **k: d.query_policy(*a, A_ptr=A, B_ptr=B, C_ptr=C, **k)
+    for M, N, K, tA, dt, prefix in [(4096, 4096, 4096, 0, d.BF16_BF16, "bf16_pp_m256n256k32"),
+                                    (2048, 5120, 5120, 0, d.BF16_BF16, "bf16_pp_m192n256"),
+                                    (5120, 5120, 2048, 1, d.BF16_BF16, "bf16_pp_m256n256k32"),
+                                    (16384, 5120, 5120, 0, d.E4M3_BF16, "e4m3_pp_m256n256k128")]:
+        name = q(M, N, K, transA=tA, dtype=dt)
+        assert name.startswith(prefix) and "+" not in name, (M, N, K, name)
 
 
 def test_lds_probe_rejects_bad_arguments():
