@@ -41,6 +41,7 @@ namespace {
 
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // 64 lanes x 16 bytes from buffer `rsrc` at per-lane byte offset `voff` into LDS bytes
 // [lds_base, lds_base + 1024) (lane i -> lds_base + 16*i); an offset past the buffer's
@@ -250,6 +251,107 @@ __device__ __forceinline__ void pp_add_partial(const float* slot, typename AccOf
     });
     __builtin_amdgcn_sched_barrier(0);
   });
+}
+
+// Epilogue through LDS.  Written straight from the accumulators, a 16x16 fragment store
+// puts 16 rows x 32 bytes in one instruction; here the tile goes out in whole rows instead.
+// Two passes, one per row of waves (wave group g holds tile rows [g*WTM, (g+1)*WTM)): the
+// group writes alpha*acc as fp32 into a row-major image of its rows in LDS (16-byte chunks
+// XOR-swizzled by row, so that the sixteen rows of a fragment store and the two rows of a
+// wave's chunk reads spread over all banks), then all threads take 8 consecutive columns
+// each, 32 threads per 256-column row, add beta*C_old, round to C's type once and store
+// 16 bytes (bf16), 32 (fp32) or 8 (E4M3) per thread.  The same arithmetic as store_group.
+template <class C>
+__device__ __forceinline__ void pp_store_tile_lds(const GemmArgs& a, const typename AccOf<C::MT>::T (&acc)[C::FM][C::FN],
+                                                  int m0, int n0, int grp, int xb0, int lane, int t, uint32_t lds0) {
+  static_assert(C::MT == 16 && C::BN == 256 && C::THREADS == 512, "16x16 fragments, 256 columns, 8 waves");
+  static_assert(C::WTM * C::BN * 4 <= PingPong<C>::LDS_BYTES, "one row of waves' fp32 image fits the LDS");
+  constexpr int RB = C::BN * 4;  // bytes per staged row
+  constexpr int CPR = RB / 16;   // 16-byte chunks per staged row
+  const float alpha = a.alpha, beta = a.beta;
+  // every wave's copies have landed (the last ones, past K, write zeros into LDS)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    __syncthreads();  // the LDS is free: the K loop's reads, or the previous pass's
+    if (grp == g) {
+      static_for<C::FM * C::FN>([&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        constexpr int i = p / C::FN, j = p % C::FN;
+        const int r = i * 16 + lane % 16;                 // row within the pass
+        const int c = xb0 + j * 16 + 4 * (lane / 16);     // column, a multiple of 4
+        const int chunk = (c >> 2) ^ (r & 15);
+        const f32x4 v = {alpha * acc[i][j][0], alpha * acc[i][j][1], alpha * acc[i][j][2], alpha * acc[i][j][3]};
+        *(__attribute__((address_space(3))) f32x4*)(uintptr_t)(lds0 + (uint32_t)(r * RB + chunk * 16)) = v;
+      });
+    }
+    __syncthreads();
+    constexpr int RPS = C::THREADS / 32;  // rows per step
+#pragma unroll 2
+    for (int s = 0; s < C::WTM / RPS; ++s) {
+      const int r = s * RPS + t / 32, ch = (t % 32) * 2;  // 8 columns: chunks ch, ch + 1
+      const int m = m0 + g * C::WTM + r, n = n0 + ch * 4;
+      if (m >= a.M || n >= a.N) continue;
+      const uint32_t row = lds0 + (uint32_t)(r * RB);
+      const f32x4 lo = *(__attribute__((address_space(3))) f32x4*)(uintptr_t)(row + ((ch ^ (r & 15)) * 16));
+      const f32x4 hi = *(__attribute__((address_space(3))) f32x4*)(uintptr_t)(row + (((ch + 1) ^ (r & 15)) * 16));
+      float w[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const int64_t base = (int64_t)m * a.ldc + n;
+      if (n + 8 <= a.N) {
+        if (a.c_kind == C_F32) {
+          f32x4* cp = (f32x4*)((float*)a.C + base);
+          if (beta != 0.f) {
+            const f32x4 o0 = cp[0], o1 = cp[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              w[e] += beta * o0[e];
+              w[4 + e] += beta * o1[e];
+            }
+          }
+          cp[0] = (f32x4){w[0], w[1], w[2], w[3]};
+          cp[1] = (f32x4){w[4], w[5], w[6], w[7]};
+        } else if (a.c_kind == C_E4M3) {
+          uint32_t* cp = (uint32_t*)((uint8_t*)a.C + base);
+          if (beta != 0.f) {
+            const uint32_t o0 = cp[0], o1 = cp[1];
+            static_for<4>([&](auto ec) {
+              constexpr int e = decltype(ec)::value;
+              w[e] += beta * __builtin_amdgcn_cvt_f32_fp8((int)o0, e);
+              w[4 + e] += beta * __builtin_amdgcn_cvt_f32_fp8((int)o1, e);
+            });
+          }
+          *(u32x2*)cp = (u32x2){e4m3x4_from_f32(w[0], w[1], w[2], w[3]), e4m3x4_from_f32(w[4], w[5], w[6], w[7])};
+        } else {
+          uint16_t* cp = (uint16_t*)a.C + base;
+          if (beta != 0.f) {
+            const u16x8 o = *(const u16x8*)cp;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] += beta * bf16_bits_to_f32(o[e]);
+          }
+          u16x8 v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = f32_to_bf16_bits(w[e]);
+          *(u16x8*)cp = v;
+        }
+      } else {  // the last columns of C
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (n + e >= a.N) break;
+          if (a.c_kind == C_F32) {
+            float* cp = (float*)a.C + base + e;
+            *cp = w[e] + (beta != 0.f ? beta * *cp : 0.f);
+          } else if (a.c_kind == C_E4M3) {
+            uint8_t* cp = (uint8_t*)a.C + base + e;
+            *cp = (uint8_t)e4m3x4_from_f32(w[e] + (beta != 0.f ? beta * __builtin_amdgcn_cvt_f32_fp8(*cp, 0) : 0.f),
+                                           0.f, 0.f, 0.f);
+          } else {
+            uint16_t* cp = (uint16_t*)a.C + base + e;
+            *cp = f32_to_bf16_bits(w[e] + (beta != 0.f ? beta * bf16_bits_to_f32(*cp) : 0.f));
+          }
+        }
+      }
+    }
+  }
 }
 
 // SK = false: one workgroup per output tile, its whole K loop.  SK = true: the stream-K
@@ -634,15 +736,17 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
             for (int s2 = slot + 1; s2 <= last_slot; ++s2)
               __hip_atomic_store(a.flags + s2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        store_tile<C>(a, acc, m0 + xa0, n0 + xb0, lane);
+        pp_store_tile_lds<C>(a, acc, m0, n0, grp, xb0, lane, t, lds0);
       }
       it += k1 - k0;
       if (whole || it >= it_end) break;
       // the next segment's waits count its copies with vmcnt, which also counts this
-      // segment's stores, and stores may complete after later loads: drain them first
+      // segment's stores, and stores may complete after later loads: drain them first; and
+      // its copies overwrite the LDS, which the epilogue may still be reading
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
     } else {
-      store_tile<C>(a, acc, m0 + xa0, n0 + xb0, lane);
+      pp_store_tile_lds<C>(a, acc, m0, n0, grp, xb0, lane, t, lds0);
       break;
     }
   }
@@ -652,6 +756,8 @@ template <class C>
 hipError_t launch_pp(const GemmArgs& a, hipStream_t s) {
   if (a.splits != 1 || a.tri != TRI_NONE || a.kband != KBAND_NONE || a.dual) return hipErrorInvalidConfiguration;
   if (a.sk_tiles > 0) {
+    // no stream-K form of the 128-deep E4M3 tile (the host never plans one: it would spill)
+    if constexpr (C::IN == IN_E4M3_LDS && C::BK > 64) return hipErrorInvalidConfiguration;
     if (!a.ws || !a.flags || a.sk_grid < 1 || a.sk_iters < 1 || a.epoch == 0 ||
         (int64_t)a.sk_grid * a.sk_iters < (int64_t)a.sk_tiles * ((a.K + C::BK - 1) / C::BK) ||
         a.sk_dp + a.sk_tiles != a.tiles_m * a.tiles_n)
