@@ -467,6 +467,58 @@ def lds_probe(g, iters: int = 512, workgroups: int = 1024, reps: int = 5):
     return rows
 
 
+def hw_probes(g, reps: int = 5):
+    """The hardware microbenchmarks (gemm_hw_probe): MFMA issue interval and the shader clock
+    under full-chip and light load, and the direct-to-LDS copy rate per CU, Markdown to
+    stderr.  Returns the rows."""
+    import torch
+    stream = torch.cuda.current_stream()
+    out = sys.stderr
+    src = torch.randint(-2 ** 15, 2 ** 15, ((64 << 20) // 2,), dtype=torch.int16, device="cuda:0")
+
+    def run(kind, param, iters, wgs):
+        cyc = torch.zeros(wgs, dtype=torch.int64, device="cuda:0")
+        g.hw_probe(kind, param, iters, wgs, src if kind == 2 else None, cyc)  # warm-up
+        torch.cuda.synchronize()
+        us, cycles = [], []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.hw_probe(kind, param, iters, wgs, src if kind == 2 else None, cyc)
+            b.record(stream)
+            b.synchronize()
+            us.append(a.elapsed_time(b) * 1e3)
+            cycles.append(float(cyc.double().median().item()))
+        return float(np.median(us)), float(np.median(cycles))
+
+    rows = []
+    print("MFMA issue (8 waves per workgroup, 2 per SIMD; 2048 clusters per wave):", file=out)
+    print("| MFMA | schedule | workgroups | us | shader GHz (cycles / time) | cycles per MFMA per SIMD | TFLOP/s |",
+          file=out)
+    print("|---|---|---|---|---|---|---|", file=out)
+    for kind, name, per, flop in ((0, "16x16x32 bf16", 32, 16384), (1, "32x32x16 bf16", 16, 32768)):
+        for param, sched in ((0, "all 8 waves"), (1, "two groups in turn")):
+            for wgs in (256, 32):
+                iters = 2048
+                us, cyc = run(kind, param, iters, wgs)
+                ghz = cyc / (us * 1e3)
+                per_mfma = cyc / (2 * iters * per)
+                tf = wgs * 8 * iters * per * flop / (us * 1e-6) / 1e12
+                rows.append(("mfma", name, sched, wgs, us, ghz, per_mfma, tf))
+                print(f"| {name} | {sched} | {wgs} | {us:.1f} | {ghz:.3f} | {per_mfma:.2f} | {tf:.0f} |", file=out)
+    print("Direct-to-LDS copy (256 workgroups of 8 waves, 256-row tiles, rows 8192 bytes apart):", file=out)
+    print("| row bytes | us | shader GHz | bytes per clock per CU | TB/s (chip) |", file=out)
+    print("|---|---|---|---|---|", file=out)
+    for rb in (64, 128, 256):
+        iters = 8192 * 64 // rb
+        us, cyc = run(2, rb, iters, 256)
+        per_clk = iters * 256 * rb / cyc
+        tbs = 256 * iters * 256 * rb / (us * 1e-6) / 1e12
+        rows.append(("copy", rb, us, cyc / (us * 1e3), per_clk, tbs))
+        print(f"| {rb} | {us:.1f} | {cyc / (us * 1e3):.3f} | {per_clk:.1f} | {tbs:.1f} |", file=out)
+    return rows
+
+
 def mx_bench(g, warmup: int = 5, steps: int = 30):
     """Block-scaled E4M3 at the E4M3 forward shape: the quantiser on a bf16 [16384][5120]
     matrix (HBM bytes/s) and gemm_run_mx 16384 x 5120 x 5120 (TFLOP/s).  Returns a dict."""
@@ -634,6 +686,8 @@ def main():
     ap.add_argument("--ladder-quick", action="store_true",
                     help="with --ladder: 4096^3 only, one round (3 + 20 calls per rung, in order)")
     ap.add_argument("--lds-probe", action="store_true", help="run the LDS read microbenchmark and exit")
+    ap.add_argument("--hw-probes", action="store_true",
+                    help="run the MFMA-issue and direct-to-LDS copy microbenchmarks and exit")
     ap.add_argument("--mx", action="store_true", help="time the MXFP8 quantiser and GEMM and exit")
     ap.add_argument("--blas3", action="store_true", help="time the BLAS3 family at 4096 and exit")
     ap.add_argument("--policy", default=None, help="force a named policy for the timed steps")
@@ -661,7 +715,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": args.warmup + args.steps}))
         return
     g = d.Gemm(0)
-    if args.ladder or args.lds_probe or args.mx or args.blas3:
+    if args.ladder or args.lds_probe or args.mx or args.blas3 or args.hw_probes:
+        if args.hw_probes:
+            hw_probes(g)
         if args.blas3:
             blas3_bench(g, cpu=not args.no_cpu_baseline)
         if args.mx:

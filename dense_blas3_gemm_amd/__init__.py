@@ -24,7 +24,7 @@ STATUS = {0: "SUCCESS", 1: "INVALID_VALUE", 2: "NOT_SUPPORTED", 3: "NOT_INITIALI
 # The exported C symbols, in the order include/gemm.h declares them.
 EXPORTS = ["gemm_create", "gemm_destroy", "gemm_set_stream", "gemm_run", "gemm_run_noalloc", "gemm_run_mx",
            "gemm_quantize_mx", "gemm_check_args", "gemm_query_policy", "gemm_set_policy",
-           "gemm_lds_probe", "gemm_policy_count", "gemm_policy_name", "gemm_version",
+           "gemm_lds_probe", "gemm_hw_probe", "gemm_policy_count", "gemm_policy_name", "gemm_version",
            "gemm_status_string", "gemm_syrk", "gemm_syr2k", "gemm_symm", "gemm_trmm", "gemm_trsm"]
 
 LOWER, UPPER = 0, 1
@@ -86,6 +86,7 @@ def load_library():
                                       ctypes.c_char_p, ctypes.c_size_t]
     lib.gemm_set_policy.argtypes = [vp, ctypes.c_char_p]
     lib.gemm_lds_probe.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_uint32), i32, i32]
+    lib.gemm_hw_probe.argtypes = [vp, i32, i32, i32, i32, vp, i64, vp]
     lib.gemm_run_mx.argtypes = [vp, i64, i64, i64, f32, vp, i64, vp, i64, vp, i64, vp, i64, f32, vp, i64, i32]
     lib.gemm_quantize_mx.argtypes = [vp, i64, i64, vp, i64, vp, i64, vp, i64]
     lib.gemm_policy_count.argtypes = []
@@ -101,7 +102,7 @@ def load_library():
     lib.gemm_trmm.argtypes = [vp, i32, i32, i32, i32, i64, i64, f32, vp, i64, vp, i64, vp, i64, i32]
     lib.gemm_trsm.argtypes = [vp, i32, i32, i32, i32, i64, i64, f32, vp, i64, vp, i64, i32]
     for fn in ["gemm_create", "gemm_destroy", "gemm_set_stream", "gemm_run", "gemm_run_noalloc", "gemm_check_args",
-               "gemm_query_policy", "gemm_set_policy", "gemm_lds_probe", "gemm_policy_count",
+               "gemm_query_policy", "gemm_set_policy", "gemm_lds_probe", "gemm_hw_probe", "gemm_policy_count",
                "gemm_run_mx", "gemm_quantize_mx", "gemm_syrk", "gemm_syr2k", "gemm_symm", "gemm_trmm",
                "gemm_trsm"]:
         getattr(lib, fn).restype = i32
@@ -266,6 +267,22 @@ class Gemm:
     # ---------------------------------------------------------------- BLAS3 family
     # Raw C-ABI calls (device pointers; the handle's current stream) return the status;
     # the tensor forms below bind torch's current stream and raise on an error.
+
+    def hw_probe(self, kind: int, param: int, iters: int, workgroups: int, src=None, cycles=None):
+        """Enqueues a hardware microbenchmark (gemm_hw_probe) on torch's current stream;
+        `cycles` (int64 device tensor of `workgroups` values, allocated when None) receives
+        each workgroup's shader-clock cycles.  Returns `cycles`."""
+        import torch
+        if cycles is None:
+            cycles = torch.zeros(workgroups, dtype=torch.int64, device=f"cuda:{self.device}")
+        self.set_stream(_current_stream(cycles.device))
+        src_ptr = 0 if src is None else _ptr(src)
+        src_bytes = 0 if src is None else src.numel() * src.element_size()
+        st = self.lib.gemm_hw_probe(self.handle, int(kind), int(param), int(iters), int(workgroups),
+                                    ctypes.c_void_p(src_ptr or None), int(src_bytes), ctypes.c_void_p(_ptr(cycles)))
+        if st != 0:
+            raise GemmError("gemm_hw_probe", st)
+        return cycles
 
     def _bind(self, t):
         stream = _current_stream(t.device)

@@ -24,7 +24,8 @@ BUILD = os.path.join(PKG, "_build")
 # transpose case and half of the policy table, the register-staged and ping-pong kernels
 # once per transpose case, so that the groups of instantiations build in parallel
 SOURCES = [("api.cpp", "api", []), ("policy.cpp", "policy", []), ("kernel_simt.hip", "kernel_simt", []),
-           ("lds_probe.hip", "lds_probe", []), ("quantize_mx.hip", "quantize_mx", []),
+           ("lds_probe.hip", "lds_probe", []), ("hw_probe.hip", "hw_probe", []),
+           ("quantize_mx.hip", "quantize_mx", []),
            ("blas3.cpp", "blas3", []), ("blas3_kernels.hip", "blas3_kernels", [])] + [
     ("kernel_mfma.hip", f"kernel_mfma_{ta}{tb}", [f"-DDBGEMM_DMA_TA={ta}", f"-DDBGEMM_DMA_TB={tb}"])
     for ta in (0, 1) for tb in (0, 1)] + [

@@ -373,6 +373,28 @@ gemm_status_t gemm_lds_probe(gemm_handle_t h, int kind, const uint32_t* offsets,
   return err == hipSuccess ? GEMM_STATUS_SUCCESS : GEMM_STATUS_LAUNCH_FAILED;
 }
 
+gemm_status_t gemm_hw_probe(gemm_handle_t h, int kind, int param, int iters, int workgroups, const void* src,
+                            int64_t src_bytes, unsigned long long* cycles) {
+  if (!live(h)) return GEMM_STATUS_NOT_INITIALIZED;
+  if (kind < 0 || kind > 2 || iters < 1 || iters > (1 << 20) || workgroups < 1 || workgroups > 65536 || !cycles)
+    return GEMM_STATUS_INVALID_VALUE;
+  if (kind < 2 && param != 0 && param != 1) return GEMM_STATUS_INVALID_VALUE;
+  if (kind == 2) {
+    const int64_t panel = 256 * kHwProbePitch;
+    if (param != 64 && param != 128 && param != 256) return GEMM_STATUS_INVALID_VALUE;
+    if (!src || src_bytes < panel || src_bytes % panel != 0 || src_bytes > ((int64_t)1 << 31) ||
+        ((uintptr_t)src & 15u) != 0)
+      return GEMM_STATUS_INVALID_VALUE;
+  }
+  const Handle* p = reinterpret_cast<const Handle*>(h);
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return GEMM_STATUS_INTERNAL;
+  if (cur != p->device && hipSetDevice(p->device) != hipSuccess) return GEMM_STATUS_INTERNAL;
+  const hipError_t err = launch_hw_probe(kind, param, iters, workgroups, src, src_bytes, cycles, p->stream);
+  if (cur != p->device) (void)hipSetDevice(cur);
+  return err == hipSuccess ? GEMM_STATUS_SUCCESS : GEMM_STATUS_LAUNCH_FAILED;
+}
+
 // Enqueues one checked GEMM on `stream` (the device is current).  `f` may pin a policy;
 // *unsupported is set when that policy cannot serve the call.  `flags` (or null: no
 // stream-K) and `epoch` (non-zero, new for each call) are the stream-K hand-off state.

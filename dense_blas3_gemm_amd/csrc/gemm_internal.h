@@ -145,6 +145,13 @@ constexpr int kLdsProbeBytes = 65536;
 int lds_probe_width(int kind);  // bytes per lane of read kind 0..3, 0 for an unknown kind
 hipError_t launch_lds_probe(int kind, const LdsProbeOffsets& offs, int iters, int workgroups, hipStream_t s);
 
+// Hardware microbenchmarks (gemm_hw_probe): kind 0 / 1 the 16x16x32 / 32x32x16 bf16 MFMA
+// issue (param 1: the two wave groups take turns), kind 2 the direct-to-LDS copy of 256-row
+// tiles of `param` bytes per row from a buffer of rows of kHwProbePitch bytes.
+constexpr int64_t kHwProbePitch = 8192;
+hipError_t launch_hw_probe(int kind, int param, int iters, int workgroups, const void* src, int64_t src_bytes,
+                           unsigned long long* cycles, hipStream_t s);
+
 // bf16 [rows][ld_src] -> E4M3 [rows][ld_dst] plus one UE8M0 byte per 32 elements of a row
 // in scales [rows][ld_scales] (the MXFP8 quantisation; see gemm_quantize_mx).
 hipError_t launch_quantize_mx(int64_t rows, int64_t cols, const void* src, int64_t ld_src, void* dst,

@@ -236,6 +236,29 @@ gemm_status_t gemm_set_policy(gemm_handle_t h, const char* name);
 gemm_status_t gemm_lds_probe(gemm_handle_t h, int kind, const uint32_t* offsets, int iters,
                              int workgroups);
 
+/* Diagnostic hardware microbenchmarks: one stage of the GEMM pipeline timed alone ("cp.async /
+ * ldmatrix ablation -- initial plan", section 2.3: isolate a stage with a microbenchmark), to
+ * set a kernel's time against the cost of each stage.  Enqueues on the handle's stream
+ * `workgroups` workgroups of 512 threads (8 waves); wave 0 of workgroup b writes to
+ * cycles[b] (a device array of `workgroups` values, caller-owned) the s_memtime count
+ * (shader clock cycles) from a workgroup barrier before the first iteration to one after
+ * the last wave's last iteration.
+ *   kind 0: each wave issues `iters` clusters of 32 v_mfma_f32_16x16x32_bf16 on register
+ *           operands (4 independent accumulators).  param 0: all 8 waves at once; param 1:
+ *           the two groups of 4 waves take turns, one cluster each between workgroup
+ *           barriers (the ping-pong kernel's schedule).
+ *   kind 1: the same with clusters of 16 v_mfma_f32_32x32x16_bf16.
+ *   kind 2: direct-to-LDS copies (buffer_load_dwordx4 ... lds): workgroup b copies `iters`
+ *           tiles of 256 rows x param bytes (param 64, 128 or 256) from the 256-row panel
+ *           b % (src_bytes / (256*8192)) of src, a device buffer of rows of 8192 bytes
+ *           (src_bytes a multiple of 2 MiB, at most 2 GiB, src 16-byte aligned), tile t from
+ *           byte column (t * param) % 8192, into two LDS slots in turn, one tile in flight
+ *           while the previous one lands.
+ * Arguments outside these ranges: INVALID_VALUE, nothing launched.  Time the call with
+ * events; cycles / time gives the clock under that load. */
+gemm_status_t gemm_hw_probe(gemm_handle_t h, int kind, int param, int iters, int workgroups,
+                            const void* src, int64_t src_bytes, unsigned long long* cycles);
+
 /* The policy table: count and names (index 0 .. count-1).  Out-of-range -> NULL. */
 int gemm_policy_count(void);
 const char* gemm_policy_name(int index);

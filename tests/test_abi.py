@@ -149,6 +149,7 @@ def test_large_workload_choices():
 
 def test_lds_probe_rejects_bad_arguments():
     lib = d.load_library()
+    assert lib.gemm_hw_probe(None, 0, 0, 1, 1, None, 0, ctypes.c_void_p(C)) == NOT_INIT
     ok = (ctypes.c_uint32 * 512)(*([0] * 512))
     assert lib.gemm_lds_probe(None, 0, ok, 1, 1) == NOT_INIT
     assert lib.gemm_lds_probe(ctypes.c_void_p(0x1234), 0, ok, 1, 1) == NOT_INIT

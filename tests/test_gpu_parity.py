@@ -282,6 +282,21 @@ def test_lds_probe_runs(gpu):
         gpu.lds_probe(0, bad, 4, 8)
 
 
+def test_hw_probes_run(gpu):
+    """The hardware microbenchmarks launch for every kind, report positive cycle counts,
+    and reject bad arguments before launching."""
+    import torch
+    import dense_blas3_gemm_amd as d
+    src = torch.zeros((4 << 20) // 2, dtype=torch.int16, device="cuda:0")  # two 2 MiB panels
+    for kind, param in [(0, 0), (0, 1), (1, 0), (1, 1), (2, 64), (2, 128), (2, 256)]:
+        cyc = gpu.hw_probe(kind, param, 4, 8, src if kind == 2 else None)
+        torch.cuda.synchronize()
+        assert (cyc > 0).all().item(), (kind, param)
+    for kind, param, s in [(3, 0, None), (0, 2, None), (2, 96, src), (2, 64, None), (2, 64, src[:1000])]:
+        with pytest.raises(d.GemmError, match="INVALID"):
+            gpu.hw_probe(kind, param, 4, 8, s)
+
+
 def test_run_to_run_deterministic_and_seed_sensitive(gpu):
     p = gi.Gemm("t", 512, 512, 512, dist="normal")
     d0 = p.make()
