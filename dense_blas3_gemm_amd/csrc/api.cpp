@@ -590,6 +590,7 @@ gemm_status_t gemm_quantize_mx(gemm_handle_t h, int64_t rows, int64_t cols, cons
     return GEMM_STATUS_INVALID_VALUE;
   if (rows == 0 || cols == 0) return GEMM_STATUS_SUCCESS;
   if (!src || !dst || !scales) return GEMM_STATUS_INVALID_VALUE;
+  if (cols > kQuantizeMaxCols) return GEMM_STATUS_NOT_SUPPORTED;
   const Handle* p = reinterpret_cast<const Handle*>(h);
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess) return GEMM_STATUS_INTERNAL;

@@ -154,6 +154,7 @@ hipError_t launch_hw_probe(int kind, int param, int iters, int workgroups, const
 
 // bf16 [rows][ld_src] -> E4M3 [rows][ld_dst] plus one UE8M0 byte per 32 elements of a row
 // in scales [rows][ld_scales] (the MXFP8 quantisation; see gemm_quantize_mx).
+constexpr int64_t kQuantizeMaxCols = (int64_t)65535 * 256 * 8;  // one grid row of 8-element chunks
 hipError_t launch_quantize_mx(int64_t rows, int64_t cols, const void* src, int64_t ld_src, void* dst,
                               int64_t ld_dst, uint8_t* scales, int64_t ld_scales, hipStream_t s);
 

@@ -190,7 +190,8 @@ gemm_status_t gemm_run_mx(gemm_handle_t h, int64_t M, int64_t N, int64_t K, floa
  * shorter).  Rule (OCP microscaling): e = clamp(floor(log2(amax)) - 8 + 127, 0, 254),
  * 0 for an all-zero group; element = x / 2^(e-127) rounded to the nearest E4M3 value,
  * ties to the even code, saturating at +-448; NaN stays NaN and does not set the scale.
- * Device pointers, enqueued on the handle's stream; writes nothing on an error. */
+ * Rows of more than 65535 * 2048 elements: NOT_SUPPORTED.  Device pointers, enqueued on
+ * the handle's stream; writes nothing on an error. */
 gemm_status_t gemm_quantize_mx(gemm_handle_t h, int64_t rows, int64_t cols, const void* src,
                                int64_t ld_src, void* dst, int64_t ld_dst, uint8_t* scales,
                                int64_t ld_scales);

@@ -153,6 +153,33 @@ def test_syr2k_different_leading_dimensions(gpu):
     check_c(to_host(C), "f32", R, S, 2 * K, m)
 
 
+@pytest.mark.parametrize("K,extra_a,extra_b", [(203, 0, 0), (264, 8, 24), (203, 5, 13)])
+def test_syr2k_padded_copies(gpu, K, extra_a, extra_b):
+    """N * K >= 2^16 with K not a multiple of 8 or lda != ldb: the operands are copied into the
+    workspace with zero-padded K-contiguous rows of one common stride, then the dual-product
+    kernel runs.  The unused columns of the caller's wider buffers hold NaN, so reading past K
+    in them would show."""
+    import torch
+    N = 512
+    A = gi.bf16_uniform((N, K), 21)
+    B = gi.bf16_uniform((N, K), 22)
+    nan = np.uint16(0x7FC0)
+    Aw = np.full((N, K + extra_a), nan, dtype=np.uint16)
+    Bw = np.full((N, K + extra_b), nan, dtype=np.uint16)
+    Aw[:, :K], Bw[:, :K] = A, B
+    C0 = c_bits((N, N), "f32", 23)
+    C = to_device(C0, "f32")
+    Ad = to_device(Aw, "bf16")[:, :K]
+    Bd = to_device(Bw, "bf16")[:, :K]
+    gpu.syr2k(Ad, Bd, C, uplo=LOWER, trans=0, alpha=0.5, beta=1.0)
+    sync()
+    got = to_host(C)
+    R, S = blas3.syr2k(LOWER, 0, N, K, 0.5, A, B, 1.0, C0, oracle.C_F32)
+    m = tri_mask(N, LOWER)
+    check_c(got, "f32", R, S, 2 * K, m)
+    assert np.array_equal(got[~m], C0[~m])
+
+
 def test_syr2k_exact_integers(gpu):
     import torch
     N, K = 384, 128

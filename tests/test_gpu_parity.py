@@ -47,6 +47,11 @@ FP8_NATIVE_POLICIES = ["e4m3native_dma_m256n256k128_w2x4_mt32_s2", "e4m3native_m
 
 
 def _assert_ok(res, what):
+    """Asserts the acceptance bound and prints how far the result is from it, and how many
+    elements lie outside the literal bf16 bound (2^-8 |R| + 1e-6), so that passing runs record
+    both (`pytest -s`)."""
+    print("parity %s: n=%d outside_literal=%d max_ratio=%.3f frob_rel=%.3e" % (
+        what, res["n"], res["n_outside_literal"], res["max_ratio"], res["frob_rel"]))
     assert res["ok"], f"{what}: {res}"
 
 
