@@ -95,7 +95,8 @@ struct Policy {
                    // fp32 accumulation); 2: E4M3 in, native f8f6f4 MFMA; 3: block-scaled
                    // E4M3 (MXFP8), widened with its scale; 4: block-scaled E4M3 on the
                    // scaled f8f6f4 MFMA; 5: E4M3 in, E4M3 in LDS, widened to bf16 in
-                   // registers (ping-pong kernel); -1: any (generic)
+                   // registers (ping-pong kernel); 6: block-scaled E4M3, bytes and scales in
+                   // LDS, widened with the scale in registers (ping-pong kernel); -1: any
   int BM, BN, BK;  // workgroup tile
   int WM, WN;      // waves along M and N
   int MT;          // MFMA block edge (32 or 16)

@@ -34,6 +34,12 @@
 // and 1: asynchronous copies running ahead of the matrix instructions, per-stage
 // completion tracking), with the roles taken by two groups of waves that alternate
 // rather than by dedicated producer warps.
+//
+// E4M3 operands stay E4M3 bytes in LDS and are widened exactly to bf16 in registers after
+// each fragment read.  Block-scaled E4M3 (one UE8M0 byte per row and 32 elements of K)
+// adds a third stream: the scale bytes of each K tile are copied to LDS one tile ahead of
+// their operands, turned into fp32 factors in LDS by the waves during the tile before, and
+// each fragment is widened with its block's factor.
 #include "mfma_common.h"
 
 namespace dbgemm {
@@ -43,19 +49,19 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// 64 lanes x 16 bytes from buffer `rsrc` at per-lane byte offset `voff` into LDS bytes
-// [lds_base, lds_base + 1024) (lane i -> lds_base + 16*i); an offset past the buffer's
-// size reads zeros.  M0 carries the LDS address: it is saved and restored inside the
-// statement (the compiler reserves M0 and does not honour it as a clobber), and one
-// wait state separates its write from the load that reads it.  The compiler neither
-// sees nor waits for these loads; every wait on them is explicit.
-__device__ __forceinline__ void pp_load_to_lds(uint32_t lds_base, uint32_t voff, __amdgpu_buffer_rsrc_t rsrc) {
+// 64 lanes x 4 bytes from buffer `rsrc` at per-lane byte offset `voff` into LDS bytes
+// [lds_base, lds_base + 256) (lane i -> lds_base + 4*i); an offset past the buffer's size
+// reads zeros.  M0 carries the LDS address: it is saved and restored inside the statement
+// (the compiler reserves M0 and does not honour it as a clobber), and one wait state
+// separates its write from the load that reads it.  The compiler neither sees nor waits
+// for these loads or the 16-byte copies below; every wait on them is explicit.
+__device__ __forceinline__ void pp_load_to_lds_dword(uint32_t lds_base, uint32_t voff, __amdgpu_buffer_rsrc_t rsrc) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(lds_base), "v"(voff), "s"(rsrc)
@@ -120,28 +126,53 @@ __device__ __forceinline__ void pp_wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
+// E4M3 bytes in LDS, widened to bf16 after each fragment read (with or without block scales)
+template <class C>
+constexpr bool pp_e8 = C::IN == IN_E4M3_LDS || C::IN == IN_MX_LDS;
+
 template <class C>
 struct PingPong {
   static_assert(C::THREADS == 512 && C::WM == 2 && C::WN == 4, "two groups of four waves");
   static_assert(C::STAGES >= 2 && C::STAGES <= 5, "two to five LDS slots");
-  static_assert((C::IN == IN_BF16 || C::IN == IN_E4M3_LDS) && C::GES == C::ES,
+  static_assert((C::IN == IN_BF16 || pp_e8<C>) && C::GES == C::ES,
                 "bf16 or E4M3 operands, LDS holds the global format");
-  static_assert(C::IN != IN_E4M3_LDS || C::MT == 16, "E4M3 tiles feed the 16x16x32 fragment map");
-  static constexpr bool E8 = C::IN == IN_E4M3_LDS;  // E4M3 bytes in LDS, widened after each read
+  static_assert(!pp_e8<C> || C::MT == 16, "E4M3 tiles feed the 16x16x32 fragment map");
+  static constexpr bool E8 = pp_e8<C>;
+  // block scales: per K tile, one dword per operand row (its four UE8M0 bytes) copied to
+  // LDS, then expanded there to four fp32 factors per row, one per K step
+  static constexpr bool MXS = C::IN == IN_MX_LDS;
   static constexpr int NW = 8, S = C::STAGES;
+  static_assert(!MXS || (C::A_KC && C::B_KC && C::BK == 128 && C::KT == 32 && C::BM == 256 && C::BN == 256 && S == 2),
+                "block-scaled tiles: A [M][K] and B [N][K], one 32-element scale block per K step, 512 rows "
+                "(one scale dword per thread), two slots");
   static_assert(C::A_BYTES % (1024 * NW) == 0 && C::B_BYTES % (1024 * NW) == 0,
                 "each wave copies whole 1 KiB blocks of both tiles");
   static constexpr int A_IPW = C::A_BYTES / 1024 / NW;  // copy instructions per wave per K tile
   static constexpr int B_IPW = C::B_BYTES / 1024 / NW;
-  static constexpr int IPW = A_IPW + B_IPW;
+  static constexpr int SC_IPW = MXS ? 1 : 0;            // the scale dwords: 256 bytes per wave
+  static constexpr int IPW = A_IPW + B_IPW + SC_IPW;
   static_assert((S - 1) * IPW <= 63, "vmcnt range");
   static_assert((C::A_KC || (C::A_CPR & (C::A_CPR - 1)) == 0) && (C::B_KC || (C::B_CPR & (C::B_CPR - 1)) == 0),
                 "M/N-contiguous rows of a power of two of chunks (the XOR swizzle stays in the row)");
   static constexpr int NMF = C::FM * C::FN * C::KSTEPS;  // MFMAs per wave per K tile
   static_assert(NMF >= IPW, "one copy per MFMA at most");
-  // LDS: the A tiles of the S slots, then the B tiles
+  // LDS: the A tiles of the S slots, then the B tiles; with block scales, four slots of
+  // scale bytes (a K tile's scales arrive one tile before its operands and are expanded
+  // during the tile before it) and S slots of fp32 factors.  Scale position p holds one
+  // row: bytes [p * 4, + 4) of a byte slot, and the fp32 factor of K step j at byte
+  // (j * 512 + p) * 4 of a factor slot.  Positions are ordered so that a lane's factors
+  // for one K step (its fragments' rows, 16 apart) are 16-byte runs, and the sixteen lanes
+  // of a row of a wave read sixteen consecutive runs (no bank conflicts): A rows
+  // wm * 128 + 16 i + l at p = wm * 128 + (i / 4) * 64 + 4 l + i % 4, B rows wn * 64 +
+  // 16 j + l at p = 256 + wn * 64 + 4 l + j.
   static constexpr int A_OFF = 0, B_OFF = S * C::A_BYTES;
-  static constexpr int LDS_BYTES = S * (C::A_BYTES + C::B_BYTES);
+  static constexpr int SCB_SLOTS = 4;
+  static constexpr int SCB_BYTES = MXS ? (C::BM + C::BN) * 4 : 0;
+  static constexpr int SCF_BYTES = MXS ? C::KSTEPS * (C::BM + C::BN) * 4 : 0;
+  static constexpr int SCB_OFF = S * (C::A_BYTES + C::B_BYTES);
+  static constexpr int SCF_OFF = SCB_OFF + SCB_SLOTS * SCB_BYTES;
+  static constexpr int LDS_BYTES = SCF_OFF + S * SCF_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
   // LDS reads per fragment (transposing bf16 reads take two 8-byte reads per fragment; an
   // E4M3 fragment is 8 bytes, one read either way)
   static constexpr int A_RD = (C::A_KC || E8) ? 1 : 2, B_RD = (C::B_KC || E8) ? 1 : 2;
@@ -153,7 +184,7 @@ struct PingPong {
 // (r >> 1) for 128-byte rows, M/N-contiguous rows (ds_read_b64_tr_b8) by the row itself.
 template <class C, bool KC, int CPR>
 __device__ __forceinline__ int pp_swz(int r) {
-  if constexpr (C::IN == IN_E4M3_LDS) {
+  if constexpr (pp_e8<C>) {
     if constexpr (KC)
       return (r >> (CPR == 4 ? 2 : 1)) & (CPR - 1);
     else
@@ -170,7 +201,7 @@ __device__ __forceinline__ int pp_swz(int r) {
 template <class C, bool KC, int RB>
 __device__ __forceinline__ uint32_t pp_frag_off(int x0, int kbase, int lane, int h) {
   constexpr int CPR = RB / 16;
-  if constexpr (C::IN == IN_E4M3_LDS) {
+  if constexpr (pp_e8<C>) {
     if constexpr (KC) {
       const int r = x0 + lane % 16;
       const int kb = kbase + (lane / 16) * 8;  // bytes = elements
@@ -197,13 +228,15 @@ __device__ __forceinline__ uint32_t pp_frag_off(int x0, int kbase, int lane, int
   }
 }
 
-// 8 E4M3 values (bytes in K order) -> 8 bf16 values, exactly (every E4M3 number, subnormals
-// included, is a bf16 number), with the gfx950 packed conversion at unit scale.
-__device__ __forceinline__ bf16x8 pp_widen8(i32x2 v) {
-  const int w0 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, false));
-  const int w1 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, true));
-  const int w2 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, false));
-  const int w3 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, true));
+// 8 E4M3 values (bytes in K order) -> 8 bf16 values times `scale`, with the gfx950 packed
+// conversion: exact at unit scale (every E4M3 number, subnormals included, is a bf16
+// number), and with a block's power-of-two factor the same conversion as the other
+// block-scaled kernels.
+__device__ __forceinline__ bf16x8 pp_widen8(i32x2 v, float scale = 1.0f) {
+  const int w0 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], scale, false));
+  const int w1 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], scale, true));
+  const int w2 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], scale, false));
+  const int w3 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], scale, true));
   return __builtin_bit_cast(bf16x8, (i32x4){w0, w1, w2, w3});
 }
 
@@ -267,7 +300,6 @@ __device__ __forceinline__ void pp_store_tile_lds(const GemmArgs& a, const typen
   static_assert(C::MT == 16 && C::BN == 256 && C::THREADS == 512, "16x16 fragments, 256 columns, 8 waves");
   static_assert(C::WTM * C::BN * 4 <= PingPong<C>::LDS_BYTES, "one row of waves' fp32 image fits the LDS");
   constexpr int RB = C::BN * 4;  // bytes per staged row
-  constexpr int CPR = RB / 16;   // 16-byte chunks per staged row
   const float alpha = a.alpha, beta = a.beta;
   // every wave's copies have landed (the last ones, past K, write zeros into LDS)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -372,6 +404,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
   const int wn = wave & 3;
   const int wm = grp;
   const int nk = (a.K + C::BK - 1) / C::BK;
+  const int nkb = (a.K + 31) / 32;  // 32-element K blocks (block scales)
 
   // ---- this workgroup's work: K tiles [it, it_end) of the sequence that lays the K loops
   // of the stream-K tiles end to end (tile ts of that part holds [ts*nk, (ts+1)*nk)), or
@@ -458,6 +491,15 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
     bf16x8 fa[C::FM], fb[C::FN];
     // E4M3: the raw 8-byte A fragments, widened by the compute phase that uses them
     i32x2 ra8[P::E8 ? C::FM : 1];
+    // block scales: this K step's factors of the A fragments (rows xa0 + 16 i + lane % 16)
+    // and of the B fragments, read with the fragments
+    float sfa[P::MXS ? C::FM : 1], sfb[P::MXS ? C::FN : 1];
+    static_assert(!P::MXS || (C::FM == 8 && C::FN == 4 && C::WTM == 128 && C::WTN == 64),
+                  "a lane's A factors are 8 consecutive positions, its B factors 4");
+    // LDS address of this lane's factors in factor slot 0, K step 0 (the slot and the step
+    // add constants): A fragments 0-3 and 4-7 (positions 256 bytes apart), B fragments 0-3
+    const uint32_t scf_a = lds0 + P::SCF_OFF + (uint32_t)((wm * 128 + (lane & 15) * 4) * 4);
+    const uint32_t scf_b = lds0 + P::SCF_OFF + (uint32_t)((256 + wn * 64 + (lane & 15) * 4) * 4);
     auto rd = [&](uint32_t addr) -> u16x4 {
       return __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                            (__attribute__((address_space(3))) s16x4*)(uintptr_t)addr));
@@ -479,9 +521,25 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
         for (int i = 0; i < C::FM; ++i) ra8[i] = rd8(a_addr(u, kk, i, 0), !C::A_KC);
   #pragma unroll
         for (int j = 0; j < C::FN; ++j) rb8[j] = rd8(b_addr(u, kk, j, 0), !C::B_KC);
+        if constexpr (P::MXS) {
+          constexpr uint32_t o = (uint32_t)(u * P::SCF_BYTES + kk * (C::BM + C::BN) * 4);
+          const f32x4 a0 = *(__attribute__((address_space(3))) f32x4*)(uintptr_t)(scf_a + o);
+          const f32x4 a1 = *(__attribute__((address_space(3))) f32x4*)(uintptr_t)(scf_a + o + 256);
+          const f32x4 b0 = *(__attribute__((address_space(3))) f32x4*)(uintptr_t)(scf_b + o);
   #pragma unroll
-        for (int j = 0; j < C::FN; ++j) fb[j] = pp_widen8(rb8[j]);
-        fa[0] = pp_widen8(ra8[0]);
+          for (int e = 0; e < 4; ++e) {
+            sfa[e] = a0[e];
+            sfa[4 + e] = a1[e];
+            sfb[e] = b0[e];
+          }
+  #pragma unroll
+          for (int j = 0; j < C::FN; ++j) fb[j] = pp_widen8(rb8[j], sfb[j]);
+          fa[0] = pp_widen8(ra8[0], sfa[0]);
+        } else {
+  #pragma unroll
+          for (int j = 0; j < C::FN; ++j) fb[j] = pp_widen8(rb8[j]);
+          fa[0] = pp_widen8(ra8[0]);
+        }
         return;
       }
   #pragma unroll
@@ -515,7 +573,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
         constexpr int row = i / C::FN, col = i % C::FN;
         mma(acc[row][col], fb[col], fa[row]);
         if constexpr (P::E8 && row + 1 < C::FM) {
-          wpart[col] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ra8[row + 1][col >> 1], 1.0f,
+          const float sc = P::MXS ? sfa[P::MXS ? row + 1 : 0] : 1.0f;
+          wpart[col] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ra8[row + 1][col >> 1], sc,
                                                                                          (col & 1) != 0));
           if constexpr (col == 3)
             fa[row + 1] = __builtin_bit_cast(bf16x8, (i32x4){wpart[0], wpart[1], wpart[2], wpart[3]});
@@ -571,6 +630,43 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
     const uint32_t a_lim = C::A_KC || !SK ? a_total : min(a_total, (uint32_t)(kend * a.lda * C::ES));
     const uint32_t b_lim = C::B_KC || !SK ? b_total : min(b_total, (uint32_t)(kend * a.ldb * C::ES));
 
+    // ---- block scales.  Wave w copies positions [64 w, 64 w + 64) of a K tile's scale
+    // dwords (waves 0-3: rows of A, 4-7: rows of B); the dword of a row at K tile kt is its
+    // bytes [4 kt, 4 kt + 4), the scales of K blocks 4 kt .. 4 kt + 3 (whole dwords: scale
+    // rows are 4-byte aligned).  A row past M or N reads zeros.
+    uint32_t sc_goff = kOOB;
+    __amdgpu_buffer_rsrc_t sc_rsrc = make_rsrc(nullptr, 0u);
+    if constexpr (P::MXS) {
+      const int pos = (wave & 3) * 64 + lane;  // position within the operand's 256
+      if (wave < 4) {
+        const int r = (pos >> 7) * 128 + (((pos >> 6) & 1) * 4 + (pos & 3)) * 16 + ((pos >> 2) & 15);
+        sc_goff = m0 + r < a.M ? (uint32_t)((m0 + r) * a.ldsa) : kOOB;
+        sc_rsrc = make_rsrc(a.sa, (uint32_t)(a.M * a.ldsa));
+      } else {
+        const int r = (pos >> 6) * 64 + (pos & 3) * 16 + ((pos >> 2) & 15);
+        sc_goff = n0 + r < a.N ? (uint32_t)((n0 + r) * a.ldsb) : kOOB;
+        sc_rsrc = make_rsrc(a.sb, (uint32_t)(a.N * a.ldsb));
+      }
+    }
+    // the scale dwords of K tile kt into byte slot kt % 4
+    auto scale_copy = [&](int kt) {
+      const uint32_t l = lds0 + P::SCB_OFF + (uint32_t)((kt & (P::SCB_SLOTS - 1)) * P::SCB_BYTES + wave * 256);
+      pp_load_to_lds_dword(__builtin_amdgcn_readfirstlane(l), sc_goff + (uint32_t)kt * 4u, sc_rsrc);
+    };
+    // Thread t expands position t of K tile kt's scale bytes into its four fp32 factors in
+    // factor slot f: byte j is the factor of K block 4 kt + j, 2^(e - 127) with the
+    // UE8M0 code's special values; a block past K (its operands read zeros) gets 1.
+    auto scale_expand = [&](int kt, int f) {
+      const uint32_t w = *(__attribute__((address_space(3))) uint32_t*)(uintptr_t)(
+          lds0 + P::SCB_OFF + (uint32_t)((kt & (P::SCB_SLOTS - 1)) * P::SCB_BYTES + lane_t * 4));
+      const int nvalid = nkb - kt * 4;  // blocks of this tile inside K (uniform)
+      const uint32_t d = lds0 + P::SCF_OFF + (uint32_t)(f * P::SCF_BYTES + lane_t * 4);
+  #pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *(__attribute__((address_space(3))) float*)(uintptr_t)(d + (uint32_t)(j * (C::BM + C::BN) * 4)) =
+            j < nvalid ? ue8m0_value((w >> (8 * j)) & 0xFFu) : 1.0f;
+    };
+
     // Copies of K tile kt into slot u: A blocks first, then B.  Tiles past the segment are
     // still issued (all their chunks read zeros), so that every wave has the same number
     // of copies in flight at every barrier and the waits can count them.
@@ -603,6 +699,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
         pp_copies<P::A_IPW, true>(la, oa, rta);
         pp_copies<P::B_IPW, true>(lb, ob, rtb);
       }
+      if constexpr (P::MXS) scale_copy(kt + 1);  // the scales run one K tile ahead
     };
 
 #pragma unroll
@@ -610,9 +707,16 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) acc[i][j] = Acc{};
 
-    // ---- prologue: K tiles k0 .. k0+S-1 into slots 0 .. S-1; wait for the first
+    // ---- prologue: K tiles k0 .. k0+S-1 into slots 0 .. S-1; wait for the first.  With
+    // block scales, tile k0's scale bytes go first (the other tiles' ride with the copies of
+    // the tile before), and are expanded before anything is read.
+    if constexpr (P::MXS) scale_copy(k0);
     static_for<S>([&](auto uc) { copy_tile(decltype(uc)::value, k0 + decltype(uc)::value); });
     pp_wait_vm_barrier<(S - 1) * P::IPW>();
+    if constexpr (P::MXS) {
+      scale_expand(k0, 0);
+      pp_wait_lds_barrier();
+    }
 
     // ---- main loop over K steps h = (tile t, step kk), S tiles per iteration so that slots
     // are compile-time constants: tile t sits in slot (t - k0) % S.  Group 0 computes step h
@@ -645,6 +749,9 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
               if (!last || kt + 1 < k1)
                 read_step(std::integral_constant<int, last ? (u + 1) % S : u>{},
                           std::integral_constant<int, last ? 0 : kk + 1>{});
+              // block scales: the next tile's factors (its bytes landed before this tile's
+              // first barrier; its factor slot was last read before that barrier)
+              if constexpr (P::MXS && kk == 0) scale_expand(kt + 1, (u + 1) % S);
               if constexpr (last) copy_tile(u, kt + S);
               __builtin_amdgcn_sched_barrier(0);
               if (!last || kt + 1 < k1) pp_wait_lds_barrier();  // B(2h+2)
@@ -665,6 +772,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
               read_step(uc, kc);
               // the slot of tile t - 1, left by both groups at the last B(2h+1) of that tile
               if (kk == 0 && kt > k0) copy_tile((u + S - 1) % S, kt - 1 + S);
+              if constexpr (P::MXS && kk == 1) scale_expand(kt + 1, (u + 1) % S);
               __builtin_amdgcn_sched_barrier(0);
               if constexpr (last) {
                 pp_wait_vm_barrier<VM>();  // B(2h+1)
@@ -755,14 +863,24 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
 template <class C>
 hipError_t launch_pp(const GemmArgs& a, hipStream_t s) {
   if (a.splits != 1 || a.tri != TRI_NONE || a.kband != KBAND_NONE || a.dual) return hipErrorInvalidConfiguration;
-  if (a.sk_tiles > 0) {
-    // no stream-K form of the 128-deep E4M3 tile (the host never plans one: it would spill)
-    if constexpr (C::IN == IN_E4M3_LDS && C::BK > 64) return hipErrorInvalidConfiguration;
-    if (!a.ws || !a.flags || a.sk_grid < 1 || a.sk_iters < 1 || a.epoch == 0 ||
-        (int64_t)a.sk_grid * a.sk_iters < (int64_t)a.sk_tiles * ((a.K + C::BK - 1) / C::BK) ||
-        a.sk_dp + a.sk_tiles != a.tiles_m * a.tiles_n)
+  if constexpr (PingPong<C>::MXS) {
+    // scale rows of whole dwords, at least one byte per 32-element block of K
+    if (!a.mx || !a.sa || !a.sb || ((uintptr_t)a.sa & 3u) || ((uintptr_t)a.sb & 3u) || (a.ldsa & 3) ||
+        (a.ldsb & 3) || a.ldsa < (a.K + 31) / 32 || a.ldsb < (a.K + 31) / 32)
       return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gemm_pp_kernel<C, true>), dim3(a.sk_dp + a.sk_grid), dim3(C::THREADS), 0, s, a);
+  }
+  if (a.sk_tiles > 0) {
+    // no stream-K form of the 128-deep E4M3 tiles (the host never plans one: they would
+    // spill), so none is instantiated
+    if constexpr ((C::IN == IN_E4M3_LDS && C::BK > 64) || C::IN == IN_MX_LDS) {
+      return hipErrorInvalidConfiguration;
+    } else {
+      if (!a.ws || !a.flags || a.sk_grid < 1 || a.sk_iters < 1 || a.epoch == 0 ||
+          (int64_t)a.sk_grid * a.sk_iters < (int64_t)a.sk_tiles * ((a.K + C::BK - 1) / C::BK) ||
+          a.sk_dp + a.sk_tiles != a.tiles_m * a.tiles_n)
+        return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL((gemm_pp_kernel<C, true>), dim3(a.sk_dp + a.sk_grid), dim3(C::THREADS), 0, s, a);
+    }
   } else {
     hipLaunchKernelGGL((gemm_pp_kernel<C, false>), dim3(grid_tiles(a)), dim3(C::THREADS), 0, s, a);
   }
@@ -786,7 +904,8 @@ constexpr bool pp_pow2(int x) { return (x & (x - 1)) == 0; }
 hipError_t DBGEMM_PP_CAT(DBGEMM_DMA_TA, DBGEMM_DMA_TB)(const Policy& p, const GemmArgs& a, hipStream_t s) {
 #define DBGEMM_SIMT(name, eff)
 #define DBGEMM_MFMA(name_, pipe_, in_, bm_, bn_, bk_, wm_, wn_, mt_, st_, grp_, rn_, xcd_, sw_, eff_)        \
-  if constexpr (pipe_ == 2 && pp_pow2(DBGEMM_DMA_TA ? (bm_) : 16) && pp_pow2(DBGEMM_DMA_TB ? 16 : (bn_)))  \
+  if constexpr (pipe_ == 2 && pp_pow2(DBGEMM_DMA_TA ? (bm_) : 16) && pp_pow2(DBGEMM_DMA_TB ? 16 : (bn_)) &&  \
+                (in_ != IN_MX_LDS || (DBGEMM_DMA_TA == 0 && DBGEMM_DMA_TB == 1)))                           \
     if (p.BM == bm_ && p.BN == bn_ && p.BK == bk_ && p.WM == wm_ && p.WN == wn_ && p.MT == mt_ &&          \
         p.stages == st_ && p.in_mode == in_)                                                               \
       return launch_pp<Cfg<bm_, bn_, bk_, wm_, wn_, mt_, st_, in_, DBGEMM_DMA_TA != 0, DBGEMM_DMA_TB != 0>>(a, s);

@@ -91,8 +91,9 @@ __device__ inline void raster_tile(int L, const GemmArgs& a, int& tm, int& tn) {
 // operands with a UE8M0 scale per 32 along K, widened to bf16 times their scale);
 // IN_MX_NATIVE (the same operands on the scaled f8f6f4 MFMA, which applies the scales);
 // IN_E4M3_LDS (E4M3 operands kept as E4M3 bytes in LDS and widened exactly to bf16 in
-// registers after each fragment read, bf16 MFMA: the ping-pong kernel).
-enum { IN_BF16 = 0, IN_E4M3 = 1, IN_E4M3_NATIVE = 2, IN_MX = 3, IN_MX_NATIVE = 4, IN_E4M3_LDS = 5 };
+// registers after each fragment read, bf16 MFMA: the ping-pong kernel); IN_MX_LDS (the same
+// with a UE8M0 scale per 32 along K, applied by the widening: the ping-pong kernel).
+enum { IN_BF16 = 0, IN_E4M3 = 1, IN_E4M3_NATIVE = 2, IN_MX = 3, IN_MX_NATIVE = 4, IN_E4M3_LDS = 5, IN_MX_LDS = 6 };
 
 // READ_: 1 reads M/N-contiguous fragments with the transposing ds_read_b64_tr_*; 0 reads
 // them one element at a time (ds_read_u16), the plain-load rung of the read ablation.
@@ -108,7 +109,7 @@ struct Cfg {
   static constexpr bool FP8 = IN == IN_E4M3_NATIVE || MXN;  // fragments and MFMA are E4M3
   static constexpr int THREADS = WM * WN * 64;
   static constexpr int GES = IN == IN_BF16 ? 2 : 1;  // bytes per element in global memory
-  static constexpr int ES = (FP8 || IN == IN_E4M3_LDS) ? 1 : 2;  // bytes per element in LDS
+  static constexpr int ES = (FP8 || IN == IN_E4M3_LDS || IN == IN_MX_LDS) ? 1 : 2;  // bytes per element in LDS
   static constexpr int WIDEN = ES / GES;             // LDS chunks per global 16-byte chunk
   static constexpr int VEC = 16 / GES;               // elements per global 16-byte chunk
   static constexpr int WTM = BM / WM, WTN = BN / WN;

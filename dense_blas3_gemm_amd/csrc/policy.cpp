@@ -28,7 +28,7 @@ constexpr int kCount = sizeof(kTable) / sizeof(kTable[0]);
 // Resident workgroups per CU: bounded by LDS (160 KiB) and by the unified register
 // file (512 registers per lane per SIMD shared by the waves on that SIMD).
 int occupancy(const Policy& p) {
-  const int es = (p.in_mode == 2 || p.in_mode == 4 || p.in_mode == 5) ? 1 : 2;  // bytes per element in LDS
+  const int es = (p.in_mode == 2 || p.in_mode >= 4) ? 1 : 2;  // bytes per element in LDS
   const int lds = p.stages * (p.BM + p.BN) * p.BK * es;
   const int staging = p.pipe == 0 ? (p.BM + p.BN) * p.BK * (p.in_mode == 0 ? 2 : 1) / (p.WM * p.WN * 64) / 4 : 0;
   int occ_lds = (160 * 1024) / lds;
@@ -60,7 +60,7 @@ bool policy_serves(const Policy& p, const Problem& pr) {
   if (p.kind != KIND_MFMA || !pr.fast_ok) return false;
   if (p.k_contig_only && (pr.transA != 0 || pr.transB != 1)) return false;
   if (p.a_kc_only && pr.transA != 0) return false;
-  if (pr.mx) return p.in_mode == 3 || (p.in_mode == 4 && pr.mx_words);
+  if (pr.mx) return p.in_mode == 3 || ((p.in_mode == 4 || p.in_mode == 6) && pr.mx_words);
   if (pr.blas3)  // triangle, K band or dual product: the bf16 direct-to-LDS kernels
     return p.pipe == 1 && p.in_mode == 0 && !pr.in_fp8 && (!pr.square_tiles || p.BM == p.BN);
   return (p.in_mode < 3 || p.in_mode == 5) && (p.in_mode != 0) == (pr.in_fp8 != 0);

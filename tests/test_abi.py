@@ -137,13 +137,15 @@ def test_policy_selection_is_shape_driven_and_deterministic():
 
 def test_large_workload_choices():
     """The shape-driven choice for the large workloads: the 256 x 256 ping-pong tile (bf16)
-    and its 128-deep E4M3 form, never split and never stream-K (stream-K is named only)."""
+    and its 128-deep E4M3 and block-scaled E4M3 forms, never split and never stream-K
+    (stream-K is named only)."""
     q = lambda *a, **k: d.query_policy(*a, A_ptr=A, B_ptr=B, C_ptr=C, **k)
-    for M, N, K, tA, dt, prefix in [(4096, 4096, 4096, 0, d.BF16_BF16, "bf16_pp_m256n256k32"),
-                                    (2048, 5120, 5120, 0, d.BF16_BF16, "bf16_pp_m256n256k32"),
-                                    (5120, 5120, 2048, 1, d.BF16_BF16, "bf16_pp_m256n256k32"),
-                                    (16384, 5120, 5120, 0, d.E4M3_BF16, "e4m3_pp_m256n256k128")]:
-        name = q(M, N, K, transA=tA, dtype=dt)
+    for M, N, K, tA, tB, dt, prefix in [(4096, 4096, 4096, 0, 0, d.BF16_BF16, "bf16_pp_m256n256k32"),
+                                        (2048, 5120, 5120, 0, 0, d.BF16_BF16, "bf16_pp_m256n256k32"),
+                                        (5120, 5120, 2048, 1, 0, d.BF16_BF16, "bf16_pp_m256n256k32"),
+                                        (16384, 5120, 5120, 0, 0, d.E4M3_BF16, "e4m3_pp_m256n256k128"),
+                                        (16384, 5120, 5120, 0, 1, d.MXE4M3_BF16, "mxe4m3_pp_m256n256k128")]:
+        name = q(M, N, K, transA=tA, transB=tB, dtype=dt)
         assert name.startswith(prefix) and "+" not in name, (M, N, K, name)
 
 

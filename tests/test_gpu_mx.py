@@ -10,8 +10,10 @@ from gpu_util import sample_rows
 
 pytestmark = pytest.mark.gpu
 
-MX_POLICIES = ["mxe4m3_m256n256k64_w2x4_mt16_s2", "mxe4m3_m128n128k64_w2x4_mt16_s2",
-               "mxe4m3_m64n64k64_w2x2_mt16_s2", "simt_generic", None]
+MX_PP = "mxe4m3_pp_m256n256k128_w2x4_mt16_s2"
+MX_REG = "mxe4m3_m128n128k64_w2x4_mt16_s2"
+MX_POLICIES = ["mxe4m3_m256n256k64_w2x4_mt16_s2", MX_REG, "mxe4m3_m64n64k64_w2x2_mt16_s2", MX_PP,
+               "simt_generic", None]
 
 
 def _dev(bits, dtype=None):
@@ -281,6 +283,72 @@ def test_run_mx_native_needs_word_scales(gpu):
     d = gi.mx_operands(M, N, K, seeds=(1, 1, 2, 2))
     with pytest.raises(dbg.GemmError):
         _run_mx_padded(gpu, d, M, N, K, 33, "bf16", MX_NATIVE)
+    with pytest.raises(dbg.GemmError):
+        _run_mx_padded(gpu, d, M, N, K, 33, "bf16", MX_PP)
     got = _run_mx_padded(gpu, d, M, N, K, 33, "bf16", None)
     R, S = _oracle_mx(d, M, N, K, 1.0, 0.0, "bf16", None)
     assert tolerance.check(got, "bf16", R, S, K)["ok"]
+
+
+# ---- the ping-pong kernel with block scales in LDS
+
+
+def _special_scales(d, seed):
+    """A few valid blocks with the UE8M0 special codes: 0 (2^-127) and 255 (NaN)."""
+    rng = np.random.default_rng(seed)
+    for key in ("SA", "SB"):
+        s = d[key]
+        for code in (0, 255):
+            r = rng.integers(0, s.shape[0], 2)
+            c = rng.integers(0, s.shape[1], 2)
+            s[r, c] = code
+    return d
+
+
+@pytest.mark.parametrize("M,N,K", [(328, 296, 1040), (256, 256, 128), (520, 264, 2064), (40, 600, 4112),
+                                   (600, 40, 96), (264, 520, 16)])
+def test_run_mx_pp_matches_register_kernel(gpu, M, N, K):
+    """The ping-pong kernel and the register-staged kernel widen each element with the same
+    conversion and run the same 16x16x32 MFMAs in the same K order: identical bits, NaN
+    rows and columns of the 255 scale codes included.  Scale rows padded with NaN bytes past
+    ceil(K/32) (the ping-pong kernel copies whole 4-byte words and must not use them);
+    K = 1040, 2064, 4112, 96 and 16 end inside a 128-wide K tile, and 16 inside a block."""
+    d = _special_scales(gi.mx_operands(M, N, K, seeds=(M, N, K, 2)), K)
+    ld = -(-((K + 31) // 32) // 4) * 4
+    rng = np.random.default_rng(M + N)
+    C0 = gi.f32_bits(rng.standard_normal((M, N)).astype(np.float32))
+    got = _run_mx_padded(gpu, d, M, N, K, ld, "f32", MX_PP, 1.25, -0.5, C0)
+    want = _run_mx_padded(gpu, d, M, N, K, ld, "f32", MX_REG, 1.25, -0.5, C0)
+    assert np.array_equal(got, want)
+    nan = np.isnan(got.view(np.float32))
+    assert nan.any() and not nan.all()
+
+
+@pytest.mark.parametrize("c_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N,K", [(328, 296, 1040), (776, 520, 2000)])
+def test_run_mx_pp_parity(gpu, M, N, K, c_dtype):
+    """Against the oracle, with alpha and beta and NaN-padded scale rows."""
+    d = gi.mx_operands(M, N, K, seeds=(K, M, N, 3))
+    rng = np.random.default_rng(K + 1)
+    c = rng.standard_normal((M, N)).astype(np.float32)
+    C0 = gi.f32_to_bf16_bits(c) if c_dtype == "bf16" else gi.f32_bits(c)
+    ld = -(-((K + 31) // 32) // 4) * 4
+    got = _run_mx_padded(gpu, d, M, N, K, ld, c_dtype, MX_PP, 0.75, 0.5, C0)
+    R, S = _oracle_mx(d, M, N, K, 0.75, 0.5, c_dtype, C0)
+    res = tolerance.check(got, c_dtype, R, S, K)
+    assert res["ok"], res
+
+
+@pytest.mark.parametrize("c_dtype", ["bf16", "f32"])
+def test_run_mx_pp_integer_bitwise(gpu, c_dtype):
+    """Integer elements with scales 2^-2 .. 2^2: every product and partial sum is exact, so
+    the result is the oracle's rounded once, bit for bit (a factor applied to the wrong row,
+    block or K step cannot hide in rounding)."""
+    M, N, K = 520, 776, 1168
+    d = gi.mx_operands(M, N, K, seeds=(4, 3, 2, 1), kind="int8")
+    d["SA"] = gi.ue8m0_bytes(d["SA"].shape, 5, 125, 129)
+    d["SB"] = gi.ue8m0_bytes(d["SB"].shape, 6, 125, 129)
+    got = _run_mx_padded(gpu, d, M, N, K, 40, c_dtype, MX_PP)
+    R, _ = _oracle_mx(d, M, N, K, 1.0, 0.0, c_dtype, None)
+    want = oracle.round_bf16(R) if c_dtype == "bf16" else oracle.round_f32(R)
+    assert np.array_equal(got, want)
