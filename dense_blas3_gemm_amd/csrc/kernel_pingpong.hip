@@ -37,9 +37,10 @@
 //
 // E4M3 operands stay E4M3 bytes in LDS and are widened exactly to bf16 in registers after
 // each fragment read.  Block-scaled E4M3 (one UE8M0 byte per row and 32 elements of K)
-// adds a third stream: the scale bytes of each K tile are copied to LDS one tile ahead of
-// their operands, turned into fp32 factors in LDS by the waves during the tile before, and
-// each fragment is widened with its block's factor.
+// adds a third stream: the scale bytes are copied to LDS ahead of their operands, each
+// lane reads the scale words of its fragments' rows once per K tile, and each fragment is
+// widened with its block's scale code placed in the exponent field of the conversion's
+// scale operand.
 #include "mfma_common.h"
 
 namespace dbgemm {
@@ -138,8 +139,8 @@ struct PingPong {
                 "bf16 or E4M3 operands, LDS holds the global format");
   static_assert(!pp_e8<C> || C::MT == 16, "E4M3 tiles feed the 16x16x32 fragment map");
   static constexpr bool E8 = pp_e8<C>;
-  // block scales: per K tile, one dword per operand row (its four UE8M0 bytes) copied to
-  // LDS, then expanded there to four fp32 factors per row, one per K step
+  // block scales: per K tile, one dword per operand row (its four UE8M0 bytes, one per K
+  // step) copied to LDS
   static constexpr bool MXS = C::IN == IN_MX_LDS;
   static constexpr int NW = 8, S = C::STAGES;
   static_assert(!MXS || (C::A_KC && C::B_KC && C::BK == 128 && C::KT == 32 && C::BM == 256 && C::BN == 256 && S == 2),
@@ -149,29 +150,32 @@ struct PingPong {
                 "each wave copies whole 1 KiB blocks of both tiles");
   static constexpr int A_IPW = C::A_BYTES / 1024 / NW;  // copy instructions per wave per K tile
   static constexpr int B_IPW = C::B_BYTES / 1024 / NW;
-  static constexpr int SC_IPW = MXS ? 1 : 0;            // the scale dwords: 256 bytes per wave
-  static constexpr int IPW = A_IPW + B_IPW + SC_IPW;
+  static constexpr int DATA_IPW = A_IPW + B_IPW;
+  static constexpr int SC_IPW = MXS ? 1 : 0;  // the scale dwords of a K tile: 256 bytes per wave
+  static constexpr int IPW = DATA_IPW + SC_IPW;
   static_assert((S - 1) * IPW <= 63, "vmcnt range");
   static_assert((C::A_KC || (C::A_CPR & (C::A_CPR - 1)) == 0) && (C::B_KC || (C::B_CPR & (C::B_CPR - 1)) == 0),
                 "M/N-contiguous rows of a power of two of chunks (the XOR swizzle stays in the row)");
   static constexpr int NMF = C::FM * C::FN * C::KSTEPS;  // MFMAs per wave per K tile
   static_assert(NMF >= IPW, "one copy per MFMA at most");
-  // LDS: the A tiles of the S slots, then the B tiles; with block scales, four slots of
-  // scale bytes (a K tile's scales arrive one tile before its operands and are expanded
-  // during the tile before it) and S slots of fp32 factors.  Scale position p holds one
-  // row: bytes [p * 4, + 4) of a byte slot, and the fp32 factor of K step j at byte
-  // (j * 512 + p) * 4 of a factor slot.  Positions are ordered so that a lane's factors
-  // for one K step (its fragments' rows, 16 apart) are 16-byte runs, and the sixteen lanes
-  // of a row of a wave read sixteen consecutive runs (no bank conflicts): A rows
-  // wm * 128 + 16 i + l at p = wm * 128 + (i / 4) * 64 + 4 l + i % 4, B rows wn * 64 +
-  // 16 j + l at p = 256 + wn * 64 + 4 l + j.
+  // LDS: the A tiles of the S slots, then the B tiles; with block scales, 32 KiB of scale
+  // bytes.  Scale position p holds one row, and a K tile's scale words are read from
+  // [p * 4, + 4) of a 2 KiB table.  Scale rows aligned to 16 bytes are copied 16 bytes
+  // (four K tiles) at a time, with the copies of the K tile two before the first of the
+  // four, into two 8 KiB slots (position p at p * 16), and each thread later moves its
+  // position's four words into four tables (two sets of four, after the copy area).
+  // Otherwise a K tile's 4 bytes ride with the copies of the tile before it, straight into
+  // one of four tables in the copy area, the bytes of K tile kt in table kt % 4.  Positions are ordered so that the
+  // rows of a lane's fragments (16 apart) sit at consecutive positions, four at a time,
+  // and the sixteen lanes of a row of a wave read consecutive runs (no bank conflicts): A
+  // rows wm * 128 + 16 i + l at p = wm * 128 + (i / 4) * 64 + 4 l + i % 4, B rows wn * 64
+  // + 16 j + l at p = 256 + wn * 64 + 4 l + j.
   static constexpr int A_OFF = 0, B_OFF = S * C::A_BYTES;
-  static constexpr int SCB_SLOTS = 4;
-  static constexpr int SCB_BYTES = MXS ? (C::BM + C::BN) * 4 : 0;
-  static constexpr int SCF_BYTES = MXS ? C::KSTEPS * (C::BM + C::BN) * 4 : 0;
+  static constexpr int SC_TABLE = 4 * (C::BM + C::BN);              // one K tile's words
+  static constexpr int SCB_REGION = MXS ? 2 * 4 * SC_TABLE : 0;       // the copy area
   static constexpr int SCB_OFF = S * (C::A_BYTES + C::B_BYTES);
-  static constexpr int SCF_OFF = SCB_OFF + SCB_SLOTS * SCB_BYTES;
-  static constexpr int LDS_BYTES = SCF_OFF + S * SCF_BYTES;
+  static constexpr int SCR_OFF = SCB_OFF + SCB_REGION;               // the tables of 16-byte rows
+  static constexpr int LDS_BYTES = SCR_OFF + SCB_REGION;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
   // LDS reads per fragment (transposing bf16 reads take two 8-byte reads per fragment; an
   // E4M3 fragment is 8 bytes, one read either way)
@@ -230,8 +234,10 @@ __device__ __forceinline__ uint32_t pp_frag_off(int x0, int kbase, int lane, int
 
 // 8 E4M3 values (bytes in K order) -> 8 bf16 values times `scale`, with the gfx950 packed
 // conversion: exact at unit scale (every E4M3 number, subnormals included, is a bf16
-// number), and with a block's power-of-two factor the same conversion as the other
-// block-scaled kernels.
+// number).  The conversion takes its scale as a UE8M0 code: only the exponent field (bits
+// 23-30) of the operand counts, sign and mantissa are ignored, code 0 scales by 2^-127 and
+// code 255 gives NaN (measured on gfx950, and pinned by the block-scaled GPU tests, which
+// compare with a kernel that passes 2^(e - 127) as a float).
 __device__ __forceinline__ bf16x8 pp_widen8(i32x2 v, float scale = 1.0f) {
   const int w0 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], scale, false));
   const int w1 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], scale, true));
@@ -491,15 +497,94 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
     bf16x8 fa[C::FM], fb[C::FN];
     // E4M3: the raw 8-byte A fragments, widened by the compute phase that uses them
     i32x2 ra8[P::E8 ? C::FM : 1];
-    // block scales: this K step's factors of the A fragments (rows xa0 + 16 i + lane % 16)
-    // and of the B fragments, read with the fragments
-    float sfa[P::MXS ? C::FM : 1], sfb[P::MXS ? C::FN : 1];
+    // block scales: the scale words of a K tile for the rows of the A fragments (rows
+    // xa0 + 16 i + lane % 16) and of the B fragments, byte kk the code of K step kk; set b
+    // serves the tile in slot b, and is read during the tile before it (in the memory
+    // phase of its second K step, one of the lighter ones)
+    constexpr int NSW = P::MXS ? S : 1;
+    uint32_t swa[NSW][P::MXS ? C::FM : 1], swb[NSW][P::MXS ? C::FN : 1];
+    float soa[P::MXS ? C::FM : 1], sob[P::MXS ? C::FN : 1];  // one K step's scale operands
     static_assert(!P::MXS || (C::FM == 8 && C::FN == 4 && C::WTM == 128 && C::WTN == 64),
-                  "a lane's A factors are 8 consecutive positions, its B factors 4");
-    // LDS address of this lane's factors in factor slot 0, K step 0 (the slot and the step
-    // add constants): A fragments 0-3 and 4-7 (positions 256 bytes apart), B fragments 0-3
-    const uint32_t scf_a = lds0 + P::SCF_OFF + (uint32_t)((wm * 128 + (lane & 15) * 4) * 4);
-    const uint32_t scf_b = lds0 + P::SCF_OFF + (uint32_t)((256 + wn * 64 + (lane & 15) * 4) * 4);
+                  "a lane's A scale rows are 8 positions in two runs of 4, its B rows one run");
+    // the conversion's scale operand for K step kk: code kk of word w in the exponent field
+    // (the bits shifted in below and above it are ignored)
+    auto scale_op = [](uint32_t w, int kk) -> float {
+      return __builtin_bit_cast(float, kk == 3 ? w >> 1 : w << (23 - 8 * kk));
+    };
+    // ---- block scales.  Wave w copies positions [64 w, 64 w + 64) (waves 0-3: rows of A,
+    // 4-7: rows of B); the dword of a row at K tile kt is its bytes [4 kt, 4 kt + 4), the
+    // scales of K blocks 4 kt .. 4 kt + 3 (whole dwords: scale rows are 4-byte aligned),
+    // and its 16 bytes at 16 q those of K tiles 4 q .. 4 q + 3 (with 16-byte aligned rows,
+    // whose length covers them).  A row past M or N reads zeros.
+    const bool sc_quad = P::MXS && ((((uintptr_t)a.sa | (uintptr_t)a.sb) & 15u) | ((a.ldsa | a.ldsb) & 15)) == 0;
+    uint32_t sc_goff = kOOB;
+    __amdgpu_buffer_rsrc_t sc_rsrc = make_rsrc(nullptr, 0u);
+    if constexpr (P::MXS) {
+      const int pos = (wave & 3) * 64 + lane;  // position within the operand's 256
+      if (wave < 4) {
+        const int r = (pos >> 7) * 128 + (((pos >> 6) & 1) * 4 + (pos & 3)) * 16 + ((pos >> 2) & 15);
+        sc_goff = m0 + r < a.M ? (uint32_t)((m0 + r) * a.ldsa) : kOOB;
+        sc_rsrc = make_rsrc(a.sa, (uint32_t)(a.M * a.ldsa));
+      } else {
+        const int r = (pos >> 6) * 64 + (pos & 3) * 16 + ((pos >> 2) & 15);
+        sc_goff = n0 + r < a.N ? (uint32_t)((n0 + r) * a.ldsb) : kOOB;
+        sc_rsrc = make_rsrc(a.sb, (uint32_t)(a.N * a.ldsb));
+      }
+    }
+    // the scale bytes that ride with the copies of K tile kt: the next tile's dwords, or
+    // (16-byte rows) the 16 bytes of K tiles kt + 2 .. kt + 5 with every fourth tile
+    auto scale_copy = [&](int kt) {
+      if (sc_quad) {
+        if ((kt & 3) != 2) return;
+        const int q = (kt + 2) >> 2;
+        const uint32_t l = lds0 + P::SCB_OFF + (uint32_t)((q & 1) * 4 * P::SC_TABLE + wave * 1024);
+        const uint32_t o[1] = {sc_goff + (uint32_t)q * 16u};
+        pp_copies<1, false>(__builtin_amdgcn_readfirstlane(l), o, sc_rsrc);
+      } else {
+        const uint32_t l = lds0 + P::SCB_OFF + (uint32_t)(((kt + 1) & 3) * 2 * P::SC_TABLE + wave * 256);
+        pp_load_to_lds_dword(__builtin_amdgcn_readfirstlane(l), sc_goff + (uint32_t)(kt + 1) * 4u, sc_rsrc);
+      }
+    };
+    // This lane's scale words of K tile kt (its 8 A rows and 4 B rows) into set bc, with the
+    // codes of K blocks past K (whose operands read zeros) replaced by 127 (scale 1) in the
+    // last K tile: the bytes there may be row padding, and code 255 would give NaN even on
+    // zeros.
+    const int sc_l = lane & 15;
+    auto read_scales = [&](int kt, auto bc) {
+      constexpr int sb = P::MXS ? decltype(bc)::value : 0;
+      const uint32_t pa = (uint32_t)(wm * 128 + sc_l * 4), pb = (uint32_t)(256 + wn * 64 + sc_l * 4);
+      // K tile kt's table: four per 16-byte copy, or one per copy of 4 bytes
+      const uint32_t base = lds0 + (sc_quad ? (uint32_t)(P::SCR_OFF + (((kt >> 2) & 1) * 4 + (kt & 3)) * P::SC_TABLE)
+                                            : (uint32_t)(P::SCB_OFF + (kt & 3) * 2 * P::SC_TABLE));
+      const u32x4 a0 = *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(base + pa * 4);
+      const u32x4 a1 = *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(base + (pa + 64) * 4);
+      const u32x4 b0 = *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(base + pb * 4);
+  #pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        swa[sb][e] = a0[e];
+        swa[sb][4 + e] = a1[e];
+        swb[sb][P::MXS ? e : 0] = b0[e];
+      }
+      const int nvalid = nkb - kt * 4;  // blocks of this tile inside K (uniform)
+      if (nvalid < 4) {
+        const uint32_t keep = nvalid <= 0 ? 0u : (1u << (8 * nvalid)) - 1u;
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) swa[sb][i] = (swa[sb][i] & keep) | (0x7F7F7F7Fu & ~keep);
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) swb[sb][P::MXS ? j : 0] = (swb[sb][P::MXS ? j : 0] & keep) | (0x7F7F7F7Fu & ~keep);
+      }
+    };
+    // 16-byte scale rows: thread t moves position t of the copy of K tiles 4q .. 4q + 3
+    // into the four tables of set q % 2 (run during K tile 4q - 2, after that copy has
+    // landed and after the tables' previous K tiles, 4q - 8 .. 4q - 5, were read)
+    auto scale_spread = [&](int q) {
+      const u32x4 w = *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(
+          lds0 + P::SCB_OFF + (uint32_t)((q & 1) * 4 * P::SC_TABLE + lane_t * 16));
+      const uint32_t d = lds0 + P::SCR_OFF + (uint32_t)((q & 1) * 4 * P::SC_TABLE + lane_t * 4);
+  #pragma unroll
+      for (int e = 0; e < 4; ++e) *(__attribute__((address_space(3))) uint32_t*)(uintptr_t)(d + e * P::SC_TABLE) = w[e];
+    };
+
     auto rd = [&](uint32_t addr) -> u16x4 {
       return __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                            (__attribute__((address_space(3))) s16x4*)(uintptr_t)addr));
@@ -510,7 +595,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
     };
     // Memory phase: the fragments of K step kk of the tile in slot u (E4M3 tiles: all reads
     // first, then the widening, so that the reads are in flight together).
-    auto read_step = [&](auto uc, auto kc) {
+    auto read_step = [&](auto uc, auto kc, int rkt) {
       constexpr int u = decltype(uc)::value, kk = decltype(kc)::value;
       if constexpr (P::E8) {
         // B fragments and the first A fragment are widened here; the other A fragments in
@@ -522,19 +607,22 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
   #pragma unroll
         for (int j = 0; j < C::FN; ++j) rb8[j] = rd8(b_addr(u, kk, j, 0), !C::B_KC);
         if constexpr (P::MXS) {
-          constexpr uint32_t o = (uint32_t)(u * P::SCF_BYTES + kk * (C::BM + C::BN) * 4);
-          const f32x4 a0 = *(__attribute__((address_space(3))) f32x4*)(uintptr_t)(scf_a + o);
-          const f32x4 a1 = *(__attribute__((address_space(3))) f32x4*)(uintptr_t)(scf_a + o + 256);
-          const f32x4 b0 = *(__attribute__((address_space(3))) f32x4*)(uintptr_t)(scf_b + o);
+          // this step's scale operands, formed while the reads are in flight (a shift
+          // right before the conversion that reads it would stall it)
+          constexpr int sb = P::MXS ? u : 0;
+          __builtin_amdgcn_sched_barrier(0);
   #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sfa[e] = a0[e];
-            sfa[4 + e] = a1[e];
-            sfb[e] = b0[e];
-          }
+          for (int i = 0; i < C::FM; ++i) soa[P::MXS ? i : 0] = scale_op(swa[sb][P::MXS ? i : 0], kk);
   #pragma unroll
-          for (int j = 0; j < C::FN; ++j) fb[j] = pp_widen8(rb8[j], sfb[j]);
-          fa[0] = pp_widen8(ra8[0], sfa[0]);
+          for (int j = 0; j < C::FN; ++j) sob[P::MXS ? j : 0] = scale_op(swb[sb][P::MXS ? j : 0], kk);
+          __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+          for (int j = 0; j < C::FN; ++j) fb[j] = pp_widen8(rb8[j], sob[P::MXS ? j : 0]);
+          fa[0] = pp_widen8(ra8[0], soa[0]);
+          // the next tile's scale words (its bytes landed before this tile began)
+          if constexpr (kk == 1) read_scales(rkt + 1, std::integral_constant<int, (u + 1) % S>{});
+          if constexpr (kk == 2)
+            if (sc_quad && (rkt & 3) == 2) scale_spread((rkt + 2) >> 2);
         } else {
   #pragma unroll
           for (int j = 0; j < C::FN; ++j) fb[j] = pp_widen8(rb8[j]);
@@ -573,7 +661,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
         constexpr int row = i / C::FN, col = i % C::FN;
         mma(acc[row][col], fb[col], fa[row]);
         if constexpr (P::E8 && row + 1 < C::FM) {
-          const float sc = P::MXS ? sfa[P::MXS ? row + 1 : 0] : 1.0f;
+          const float sc = P::MXS ? soa[P::MXS ? row + 1 : 0] : 1.0f;
           wpart[col] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ra8[row + 1][col >> 1], sc,
                                                                                          (col & 1) != 0));
           if constexpr (col == 3)
@@ -630,43 +718,6 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
     const uint32_t a_lim = C::A_KC || !SK ? a_total : min(a_total, (uint32_t)(kend * a.lda * C::ES));
     const uint32_t b_lim = C::B_KC || !SK ? b_total : min(b_total, (uint32_t)(kend * a.ldb * C::ES));
 
-    // ---- block scales.  Wave w copies positions [64 w, 64 w + 64) of a K tile's scale
-    // dwords (waves 0-3: rows of A, 4-7: rows of B); the dword of a row at K tile kt is its
-    // bytes [4 kt, 4 kt + 4), the scales of K blocks 4 kt .. 4 kt + 3 (whole dwords: scale
-    // rows are 4-byte aligned).  A row past M or N reads zeros.
-    uint32_t sc_goff = kOOB;
-    __amdgpu_buffer_rsrc_t sc_rsrc = make_rsrc(nullptr, 0u);
-    if constexpr (P::MXS) {
-      const int pos = (wave & 3) * 64 + lane;  // position within the operand's 256
-      if (wave < 4) {
-        const int r = (pos >> 7) * 128 + (((pos >> 6) & 1) * 4 + (pos & 3)) * 16 + ((pos >> 2) & 15);
-        sc_goff = m0 + r < a.M ? (uint32_t)((m0 + r) * a.ldsa) : kOOB;
-        sc_rsrc = make_rsrc(a.sa, (uint32_t)(a.M * a.ldsa));
-      } else {
-        const int r = (pos >> 6) * 64 + (pos & 3) * 16 + ((pos >> 2) & 15);
-        sc_goff = n0 + r < a.N ? (uint32_t)((n0 + r) * a.ldsb) : kOOB;
-        sc_rsrc = make_rsrc(a.sb, (uint32_t)(a.N * a.ldsb));
-      }
-    }
-    // the scale dwords of K tile kt into byte slot kt % 4
-    auto scale_copy = [&](int kt) {
-      const uint32_t l = lds0 + P::SCB_OFF + (uint32_t)((kt & (P::SCB_SLOTS - 1)) * P::SCB_BYTES + wave * 256);
-      pp_load_to_lds_dword(__builtin_amdgcn_readfirstlane(l), sc_goff + (uint32_t)kt * 4u, sc_rsrc);
-    };
-    // Thread t expands position t of K tile kt's scale bytes into its four fp32 factors in
-    // factor slot f: byte j is the factor of K block 4 kt + j, 2^(e - 127) with the
-    // UE8M0 code's special values; a block past K (its operands read zeros) gets 1.
-    auto scale_expand = [&](int kt, int f) {
-      const uint32_t w = *(__attribute__((address_space(3))) uint32_t*)(uintptr_t)(
-          lds0 + P::SCB_OFF + (uint32_t)((kt & (P::SCB_SLOTS - 1)) * P::SCB_BYTES + lane_t * 4));
-      const int nvalid = nkb - kt * 4;  // blocks of this tile inside K (uniform)
-      const uint32_t d = lds0 + P::SCF_OFF + (uint32_t)(f * P::SCF_BYTES + lane_t * 4);
-  #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *(__attribute__((address_space(3))) float*)(uintptr_t)(d + (uint32_t)(j * (C::BM + C::BN) * 4)) =
-            j < nvalid ? ue8m0_value((w >> (8 * j)) & 0xFFu) : 1.0f;
-    };
-
     // Copies of K tile kt into slot u: A blocks first, then B.  Tiles past the segment are
     // still issued (all their chunks read zeros), so that every wave has the same number
     // of copies in flight at every barrier and the waits can count them.
@@ -699,7 +750,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
         pp_copies<P::A_IPW, true>(la, oa, rta);
         pp_copies<P::B_IPW, true>(lb, ob, rtb);
       }
-      if constexpr (P::MXS) scale_copy(kt + 1);  // the scales run one K tile ahead
+      if constexpr (P::MXS) scale_copy(kt);
     };
 
 #pragma unroll
@@ -708,14 +759,23 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
       for (int j = 0; j < C::FN; ++j) acc[i][j] = Acc{};
 
     // ---- prologue: K tiles k0 .. k0+S-1 into slots 0 .. S-1; wait for the first.  With
-    // block scales, tile k0's scale bytes go first (the other tiles' ride with the copies of
-    // the tile before), and are expanded before anything is read.
-    if constexpr (P::MXS) scale_copy(k0);
+    // block scales (one segment per workgroup: k0 = 0), the first scale bytes go first (the
+    // others ride with the copies of the tiles before them).  With 16-byte rows, tiles k0
+    // and k0 + 1 carry none, so the wait counts the data copies of tile k0 + 1 alone.
+    if constexpr (P::MXS) scale_copy(sc_quad ? k0 - 2 : k0 - 1);
     static_for<S>([&](auto uc) { copy_tile(decltype(uc)::value, k0 + decltype(uc)::value); });
-    pp_wait_vm_barrier<(S - 1) * P::IPW>();
     if constexpr (P::MXS) {
-      scale_expand(k0, 0);
-      pp_wait_lds_barrier();
+      if (sc_quad)
+        pp_wait_vm_barrier<(S - 1) * P::DATA_IPW>();
+      else
+        pp_wait_vm_barrier<(S - 1) * P::IPW>();
+      if (sc_quad) {
+        scale_spread(k0 >> 2);
+        pp_wait_lds_barrier();
+      }
+      read_scales(k0, std::integral_constant<int, 0>{});
+    } else {
+      pp_wait_vm_barrier<(S - 1) * P::IPW>();
     }
 
     // ---- main loop over K steps h = (tile t, step kk), S tiles per iteration so that slots
@@ -727,7 +787,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
     // barrier after which the first step of tile t + 1 is read, every wave waits for its
     // copies of tile t + 1.  Both groups run 2 (k1 - k0) KS barriers in all.
     if (grp == 0) {
-      read_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+      read_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, k0);
       __builtin_amdgcn_sched_barrier(0);
       pp_wait_lds_barrier();  // B0
       for (int kt0 = k0; kt0 < k1; kt0 += S) {
@@ -748,10 +808,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
               // full address queue)
               if (!last || kt + 1 < k1)
                 read_step(std::integral_constant<int, last ? (u + 1) % S : u>{},
-                          std::integral_constant<int, last ? 0 : kk + 1>{});
-              // block scales: the next tile's factors (its bytes landed before this tile's
-              // first barrier; its factor slot was last read before that barrier)
-              if constexpr (P::MXS && kk == 0) scale_expand(kt + 1, (u + 1) % S);
+                          std::integral_constant<int, last ? 0 : kk + 1>{}, last ? kt + 1 : kt);
               if constexpr (last) copy_tile(u, kt + S);
               __builtin_amdgcn_sched_barrier(0);
               if (!last || kt + 1 < k1) pp_wait_lds_barrier();  // B(2h+2)
@@ -769,10 +826,9 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
             static_for<KS>([&](auto kc) {
               constexpr int kk = decltype(kc)::value;
               constexpr bool last = kk == KS - 1;
-              read_step(uc, kc);
+              read_step(uc, kc, kt);
               // the slot of tile t - 1, left by both groups at the last B(2h+1) of that tile
               if (kk == 0 && kt > k0) copy_tile((u + S - 1) % S, kt - 1 + S);
-              if constexpr (P::MXS && kk == 1) scale_expand(kt + 1, (u + 1) % S);
               __builtin_amdgcn_sched_barrier(0);
               if constexpr (last) {
                 pp_wait_vm_barrier<VM>();  // B(2h+1)

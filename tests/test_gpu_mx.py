@@ -305,16 +305,19 @@ def _special_scales(d, seed):
     return d
 
 
+@pytest.mark.parametrize("align", [4, 16])
 @pytest.mark.parametrize("M,N,K", [(328, 296, 1040), (256, 256, 128), (520, 264, 2064), (40, 600, 4112),
-                                   (600, 40, 96), (264, 520, 16)])
-def test_run_mx_pp_matches_register_kernel(gpu, M, N, K):
+                                   (600, 40, 96), (264, 520, 16), (264, 264, 1664)])
+def test_run_mx_pp_matches_register_kernel(gpu, M, N, K, align):
     """The ping-pong kernel and the register-staged kernel widen each element with the same
     conversion and run the same 16x16x32 MFMAs in the same K order: identical bits, NaN
-    rows and columns of the 255 scale codes included.  Scale rows padded with NaN bytes past
-    ceil(K/32) (the ping-pong kernel copies whole 4-byte words and must not use them);
-    K = 1040, 2064, 4112, 96 and 16 end inside a 128-wide K tile, and 16 inside a block."""
+    rows and columns of the 255 scale codes included.  Scale rows padded to a multiple of
+    `align` bytes with NaN bytes past ceil(K/32) (the ping-pong kernel copies whole 4-byte
+    words, or with 16-byte rows 16 bytes at a time, and must not use them); K = 1040,
+    2064, 4112, 96 and 16 end inside a 128-wide K tile, and 16 inside a block; 1664 is 13
+    K tiles (the 16-byte copies of three full groups of four tiles and one more)."""
     d = _special_scales(gi.mx_operands(M, N, K, seeds=(M, N, K, 2)), K)
-    ld = -(-((K + 31) // 32) // 4) * 4
+    ld = -(-((K + 31) // 32) // align) * align
     rng = np.random.default_rng(M + N)
     C0 = gi.f32_bits(rng.standard_normal((M, N)).astype(np.float32))
     got = _run_mx_padded(gpu, d, M, N, K, ld, "f32", MX_PP, 1.25, -0.5, C0)
@@ -339,8 +342,9 @@ def test_run_mx_pp_parity(gpu, M, N, K, c_dtype):
     assert res["ok"], res
 
 
+@pytest.mark.parametrize("ld", [40, 48])
 @pytest.mark.parametrize("c_dtype", ["bf16", "f32"])
-def test_run_mx_pp_integer_bitwise(gpu, c_dtype):
+def test_run_mx_pp_integer_bitwise(gpu, c_dtype, ld):
     """Integer elements with scales 2^-2 .. 2^2: every product and partial sum is exact, so
     the result is the oracle's rounded once, bit for bit (a factor applied to the wrong row,
     block or K step cannot hide in rounding)."""
@@ -348,7 +352,7 @@ def test_run_mx_pp_integer_bitwise(gpu, c_dtype):
     d = gi.mx_operands(M, N, K, seeds=(4, 3, 2, 1), kind="int8")
     d["SA"] = gi.ue8m0_bytes(d["SA"].shape, 5, 125, 129)
     d["SB"] = gi.ue8m0_bytes(d["SB"].shape, 6, 125, 129)
-    got = _run_mx_padded(gpu, d, M, N, K, 40, c_dtype, MX_PP)
+    got = _run_mx_padded(gpu, d, M, N, K, ld, c_dtype, MX_PP)
     R, _ = _oracle_mx(d, M, N, K, 1.0, 0.0, c_dtype, None)
     want = oracle.round_bf16(R) if c_dtype == "bf16" else oracle.round_f32(R)
     assert np.array_equal(got, want)
