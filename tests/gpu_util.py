@@ -84,3 +84,14 @@ def compare(problem: gi.Gemm, data, C_bits, rows=None, accumulate="fp32"):
     R, S = oracle.gemm_problem(problem, data, rows=rows)
     got = C_bits if rows is None else C_bits[rows]
     return tolerance.check(got, problem.c_dtype, R, S, problem.K, accumulate=accumulate)
+
+
+def whole_tiles(M, count=8, tile=256):
+    """Every row of `count` 256-row tiles spread evenly from the first to the last (tiles
+    that cover different XCDs, raster positions and the ragged end)."""
+    n = (M + tile - 1) // tile
+    picks = sorted({round(i * (n - 1) / max(count - 1, 1)) for i in range(count)})
+    rows = []
+    for t in picks:
+        rows.extend(range(t * tile, min(M, (t + 1) * tile)))
+    return rows

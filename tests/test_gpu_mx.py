@@ -6,7 +6,7 @@ import pytest
 import gemm_inputs as gi
 import oracle
 import tolerance
-from gpu_util import sample_rows
+from gpu_util import sample_rows, whole_tiles
 
 pytestmark = pytest.mark.gpu
 
@@ -164,14 +164,14 @@ def test_run_mx_argument_errors(gpu):
 
 @pytest.mark.slow
 def test_mx_forward_full_size(gpu):
-    """16384 x 5120 x 5120 with bf16 C: sampled rows of every M tile against the oracle,
-    and the quantiser on sampled rows of a bf16 matrix of the same size."""
+    """16384 x 5120 x 5120 with bf16 C: four whole 256-row tiles against the oracle, and
+    the quantiser on sampled rows of a bf16 matrix of the same size."""
     import torch
     M, N, K = gi.MX_FWD_SHAPE
     d = gi.mx_operands(M, N, K, seeds=(0, 1, 2, 3))
     got = _run_mx(gpu, d, M, N, K)
     assert np.isfinite(tolerance.bf16_bits_to_f64(got)).all()
-    rows = sample_rows(M, per_tile=0, cap=16)
+    rows = whole_tiles(M, count=4)  # the block-scaled oracle is the slower one: 1024 rows
     R, S = _oracle_mx(d, M, N, K, 1.0, 0.0, "bf16", None, rows=rows)
     res = tolerance.check(got[rows], "bf16", R, S, K)
     assert res["ok"], res

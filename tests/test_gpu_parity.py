@@ -12,7 +12,7 @@ import pytest
 import gemm_inputs as gi
 import oracle
 import tolerance
-from gpu_util import compare, empty_c, run_gpu, sample_rows, to_device, to_host
+from gpu_util import compare, empty_c, run_gpu, sample_rows, to_device, to_host, whole_tiles
 
 pytestmark = pytest.mark.gpu
 
@@ -375,25 +375,15 @@ def test_projection_backward_beta_visible(gpu):
     assert not compare(p0, data, to_host(dW), rows=rows)["ok"]
 
 
-def _whole_tiles(M, tiles=(0, None, -1), tile=256):
-    """Every row of a few 256-row tiles: the first, one in the middle and the last."""
-    n = (M + tile - 1) // tile
-    rows = []
-    for t in tiles:
-        t = n // 2 if t is None else (t % n)
-        rows.extend(range(t * tile, min(M, (t + 1) * tile)))
-    return sorted(set(rows))
-
-
 @pytest.mark.slow
 def test_fp8_16384(gpu):
-    """Whole 256-row tiles (first, middle, last) of the E4M3 forward product, with bf16 and
-    with fp32 C; every other row is checked for finiteness."""
+    """Eight whole 256-row tiles of the E4M3 forward product (2048 of 16384 rows), with
+    bf16 and with fp32 C; every other row is checked for finiteness."""
     p = gi.FP8_FWD
     data = p.make()
     C = run_gpu(gpu, p, data)
     assert np.isfinite(tolerance.bf16_bits_to_f64(C)).all()
-    rows = _whole_tiles(p.M)
+    rows = whole_tiles(p.M)
     _assert_ok(compare(p, data, C, rows=rows), p.name)
     # the fp32 bound applies to the accumulation: same inputs with fp32 C
     p32 = dataclasses.replace(p, c_dtype="f32")
@@ -453,7 +443,7 @@ def test_fp8_16384_native(gpu):
     data = p.make()
     pol = "e4m3native_m256n256k128_w2x2_mt32_s2"
     C = run_gpu(gpu, p, data, policy=pol)
-    rows = _whole_tiles(p.M, tiles=(0, -1))
+    rows = whole_tiles(p.M)
     _assert_ok(compare(p, data, C, rows=rows, accumulate="e4m3_native"), "native")
     p32 = dataclasses.replace(p, c_dtype="f32")
     native = compare(p32, data, run_gpu(gpu, p32, data, policy=pol), rows=rows, accumulate="e4m3_native")
@@ -478,7 +468,7 @@ def test_full_size_integer_bitwise_shapes(gpu, name):
     p = _int_problem(gi.BY_NAME[name])
     data = p.make()
     C = run_gpu(gpu, p, data)
-    rows = _whole_tiles(p.M) if p.M > 8192 else None
+    rows = whole_tiles(p.M) if p.M > 8192 else None
     R, _ = oracle.gemm_problem(p, data, rows=rows, with_abs=False)
     assert np.abs(R).max() < 2 ** 24
     got = C if rows is None else C[rows]
