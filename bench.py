@@ -48,7 +48,7 @@ METRIC = "TFLOP/s and % of MI355X dense MFMA peak, 4096³ bf16 GEMM (1 GPU)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_4096_bf16.md")
 # the device code of the headline policy's kernel (the ping-pong kernel and its shared parts)
 KERNEL_SOURCES = [os.path.join(ROOT, "dense_blas3_gemm_amd", "csrc", f)
-                  for f in ("kernel_pingpong.hip", "mfma_common.h", "gemm_internal.h")]
+                  for f in ("kernel_pingpong.hip", "policies_pp.inc", "mfma_common.h", "gemm_internal.h")]
 
 
 def _dev(bits, kind):
@@ -61,11 +61,17 @@ def _dev(bits, kind):
 
 
 def kernel_hash() -> str:
+    """Hash of the headline kernel's sources with their // comments and blank lines removed
+    (a change of wording alone keeps counters taken on the code valid)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            for line in fh:
+                code = re.sub(r"//.*", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
@@ -435,6 +441,16 @@ def lds_probe_patterns():
         pats += [(f"A fragment, ds_read_b128, {tag}", 0, b128, 8),
                  (f"B fragment, ds_read_b64_tr_b16, {tag}", 1, tr, 4),
                  (f"B fragment, ds_read_u16 x8, {tag}", 2, u16, 1)]
+    # E4M3 K-contiguous fragments of a 128-byte-row tile (8 bytes per lane: row l % 16, K
+    # bytes 8 (l / 16) of the step's 32, chunk xor (r >> 1) & 7): one ds_read_b64 each, or
+    # two fragments 16 rows apart in one ds_read2st64_b64 (the pairing a compiler makes of
+    # such reads when it sees their constant distance)
+    def e8(r, kb):
+        return r * 128 + ((((kb >> 4) ^ ((r >> 1) & 7)) << 4) | (kb & 15))
+    b64 = [[e8(16 * j + l % 16, (l // 16) * 8) for l in range(64)] for j in range(8)]
+    pair = [[e8(32 * j + l % 16, (l // 16) * 8) for l in range(64)] for j in range(8)]
+    pats += [("E4M3 K-contiguous fragment, ds_read_b64", 3, b64, 8),
+             ("E4M3 K-contiguous fragments 16 rows apart, ds_read2st64_b64", 5, pair, 16)]
     return pats
 
 
@@ -461,8 +477,10 @@ def lds_probe(g, iters: int = 512, workgroups: int = 1024, reps: int = 5):
         us = float(np.median([a.elapsed_time(b) for a, b in ev[1:]])) * 1e3
         total_frags = workgroups * 4 * iters * frags
         ns_per_frag_cu = us * 1e3 * 256 / total_frags
-        rows.append((name, 8 // frags, us, ns_per_frag_cu))
-        print(f"| {name} | {8 // frags} | {us:.1f} | {ns_per_frag_cu:.2f} | {1024 / ns_per_frag_cu:.1f} |",
+        per_frag = 8 / frags
+        fbytes = 512 if kind in (3, 5) else 1024  # an E4M3 fragment is 64 lanes x 8 bytes
+        rows.append((name, per_frag, us, ns_per_frag_cu))
+        print(f"| {name} | {per_frag:g} | {us:.1f} | {ns_per_frag_cu:.2f} | {fbytes / ns_per_frag_cu:.1f} |",
               file=out)
     return rows
 

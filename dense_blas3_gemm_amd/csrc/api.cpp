@@ -361,7 +361,7 @@ gemm_status_t gemm_lds_probe(gemm_handle_t h, int kind, const uint32_t* offsets,
   for (int j = 0; j < 8; ++j)
     for (int l = 0; l < 64; ++l) {
       const uint32_t v = offsets[j * 64 + l];
-      if (v % (uint32_t)w != 0 || v > (uint32_t)(kLdsProbeBytes - w)) return GEMM_STATUS_INVALID_VALUE;
+      if (v % (uint32_t)w != 0 || v > (uint32_t)(kLdsProbeBytes - lds_probe_span(kind))) return GEMM_STATUS_INVALID_VALUE;
       o.off[j][l] = v;
     }
   const Handle* p = reinterpret_cast<const Handle*>(h);

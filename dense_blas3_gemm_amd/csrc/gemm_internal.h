@@ -143,7 +143,8 @@ struct LdsProbeOffsets {
   uint32_t off[8][64];
 };
 constexpr int kLdsProbeBytes = 65536;
-int lds_probe_width(int kind);  // bytes per lane of read kind 0..3, 0 for an unknown kind
+int lds_probe_width(int kind);  // bytes per lane of read kind 0..5, 0 for an unknown kind
+int lds_probe_span(int kind);   // bytes from a lane's offset to the end of what its read touches
 hipError_t launch_lds_probe(int kind, const LdsProbeOffsets& offs, int iters, int workgroups, hipStream_t s);
 
 // Hardware microbenchmarks (gemm_hw_probe): kind 0 / 1 the 16x16x32 / 32x32x16 bf16 MFMA

@@ -591,8 +591,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a) {
     };
     // (The plain 8-byte reads are volatile so that the compiler does not pair the reads of
     // two fragments 16 rows apart into one ds_read2st64_b64: the two addresses of a lane
-    // then fall in the same banks, measured at 1.8x the time of two ds_read_b64 with the
-    // bank-conflict counter at 131M cycles against 0.)
+    // then fall in the same banks; the LDS read probe's paired form, kind 5, runs 2.3x the
+    // time per fragment of single ds_read_b64, with bank conflicts where those have none.)
     auto rd8 = [&](uint32_t addr, bool tr) -> i32x2 {
       if (tr) return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(uintptr_t)addr);
       return *(volatile __attribute__((address_space(3))) i32x2*)(uintptr_t)addr;

@@ -230,10 +230,12 @@ gemm_status_t gemm_set_policy(gemm_handle_t h, const char* name);
  * fills a 64 KiB LDS array, then every lane repeats `iters` times: 8 reads of one kind
  * at LDS byte offsets offsets[j*64 + (lane % 64)], j = 0..7 (a host array of 512
  * values, copied at the call), then a wait for them.  kind: 0 ds_read_b128 (16 bytes),
- * 1 ds_read_b64_tr_b16 (8), 2 ds_read_u16 (2), 3 ds_read_b64 (8), 4 ds_read_b64_tr_b8 (8).
- * Each offset must be a
- * multiple of the width and at most 65536 - width, else INVALID_VALUE (nothing is
- * launched).  Time it with events around the call; it writes no memory. */
+ * 1 ds_read_b64_tr_b16 (8), 2 ds_read_u16 (2), 3 ds_read_b64 (8), 4 ds_read_b64_tr_b8 (8),
+ * 5 ds_read2st64_b64 (8 bytes at the offset and 8 at the offset + 2048: two fragments 16
+ * rows of 128 bytes apart in one instruction).  Each offset must be a multiple of the width
+ * and leave the read inside the 64 KiB (at most 65536 - width, 65536 - 2056 for kind 5),
+ * else INVALID_VALUE (nothing is launched).  Time it with events around the call; it writes
+ * no memory. */
 gemm_status_t gemm_lds_probe(gemm_handle_t h, int kind, const uint32_t* offsets, int iters,
                              int workgroups);
 

@@ -285,6 +285,12 @@ def test_lds_probe_runs(gpu):
     bad[3][5] = 65536 - 8  # past the end for 16-byte reads
     with pytest.raises(d.GemmError, match="INVALID"):
         gpu.lds_probe(0, bad, 4, 8)
+    bad[3][5] = 65536 - 2048  # the paired read's second address would pass the end
+    with pytest.raises(d.GemmError, match="INVALID"):
+        gpu.lds_probe(5, bad, 4, 8)
+    bad[3][5] = 65536 - 2056  # the last start the paired read allows
+    gpu.lds_probe(5, bad, 4, 8)
+    torch.cuda.synchronize()
 
 
 def test_hw_probes_run(gpu):
