@@ -192,14 +192,16 @@ def _padded_scales(s, ld, fill=255):
     return out
 
 
-def _run_mx_padded(gpu, d, M, N, K, ld, c_dtype, policy, alpha=1.0, beta=0.0, C0=None):
-    """As _run_mx, with the scales passed as views into padded rows of `ld` bytes."""
+def _run_mx_padded(gpu, d, M, N, K, ld, c_dtype, policy, alpha=1.0, beta=0.0, C0=None, start=0):
+    """As _run_mx, with the scales passed as views into padded rows of `ld` bytes, starting
+    `start` bytes into each row (the bytes before it NaN codes too)."""
     import torch
     nb = (K + 31) // 32
     A = _dev(d["A"], torch.float8_e4m3fn)
     B = _dev(d["B"], torch.float8_e4m3fn)
-    SA = _dev(_padded_scales(d["SA"], ld))[:, :nb]
-    SB = _dev(_padded_scales(d["SB"], ld))[:, :nb]
+    pad = lambda sc: np.concatenate([np.full((sc.shape[0], start), 255, np.uint8), sc], axis=1)
+    SA = _dev(_padded_scales(pad(d["SA"]), ld))[:, start:start + nb]
+    SB = _dev(_padded_scales(pad(d["SB"]), ld))[:, start:start + nb]
     dt = torch.float32 if c_dtype == "f32" else torch.bfloat16
     if C0 is not None:
         C = _dev(C0.view(np.int16) if c_dtype == "bf16" else C0.view(np.float32), dt if c_dtype == "bf16" else None)
@@ -305,23 +307,25 @@ def _special_scales(d, seed):
     return d
 
 
-@pytest.mark.parametrize("align", [4, 16])
+@pytest.mark.parametrize("align,start", [(4, 0), (16, 0), (16, 4)])
 @pytest.mark.parametrize("M,N,K", [(328, 296, 1040), (256, 256, 128), (520, 264, 2064), (40, 600, 4112),
                                    (600, 40, 96), (264, 520, 16), (264, 264, 1664)])
-def test_run_mx_pp_matches_register_kernel(gpu, M, N, K, align):
+def test_run_mx_pp_matches_register_kernel(gpu, M, N, K, align, start):
     """The ping-pong kernel and the register-staged kernel widen each element with the same
     conversion and run the same 16x16x32 MFMAs in the same K order: identical bits, NaN
     rows and columns of the 255 scale codes included.  Scale rows padded to a multiple of
     `align` bytes with NaN bytes past ceil(K/32) (the ping-pong kernel copies whole 4-byte
     words, or with 16-byte rows 16 bytes at a time, and must not use them); K = 1040,
     2064, 4112, 96 and 16 end inside a 128-wide K tile, and 16 inside a block; 1664 is 13
-    K tiles (the 16-byte copies of three full groups of four tiles and one more)."""
+    K tiles (the 16-byte copies of three full groups of four tiles and one more).  With
+    start = 4 the rows are 16-byte multiples but the arrays start 4 bytes into them: the
+    kernel must take the 4-byte copies."""
     d = _special_scales(gi.mx_operands(M, N, K, seeds=(M, N, K, 2)), K)
-    ld = -(-((K + 31) // 32) // align) * align
+    ld = -(-((K + 31) // 32 + start) // align) * align
     rng = np.random.default_rng(M + N)
     C0 = gi.f32_bits(rng.standard_normal((M, N)).astype(np.float32))
-    got = _run_mx_padded(gpu, d, M, N, K, ld, "f32", MX_PP, 1.25, -0.5, C0)
-    want = _run_mx_padded(gpu, d, M, N, K, ld, "f32", MX_REG, 1.25, -0.5, C0)
+    got = _run_mx_padded(gpu, d, M, N, K, ld, "f32", MX_PP, 1.25, -0.5, C0, start=start)
+    want = _run_mx_padded(gpu, d, M, N, K, ld, "f32", MX_REG, 1.25, -0.5, C0, start=start)
     assert np.array_equal(got, want)
     nan = np.isnan(got.view(np.float32))
     assert nan.any() and not nan.all()
