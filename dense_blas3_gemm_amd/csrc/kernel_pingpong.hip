@@ -151,7 +151,9 @@ struct PingPong {
   static constexpr int A_IPW = C::A_BYTES / 1024 / NW;  // copy instructions per wave per K tile
   static constexpr int B_IPW = C::B_BYTES / 1024 / NW;
   static constexpr int DATA_IPW = A_IPW + B_IPW;
-  static constexpr int SC_IPW = MXS ? 1 : 0;  // the scale dwords of a K tile: 256 bytes per wave
+  // the scale dwords of a K tile (4-byte scale rows): 256 bytes per wave; 16-byte rows take
+  // one 1 KiB copy per wave with every fourth K tile instead
+  static constexpr int SC_IPW = MXS ? 1 : 0;
   static constexpr int IPW = DATA_IPW + SC_IPW;
   static_assert((S - 1) * IPW <= 63, "vmcnt range");
   static_assert((C::A_KC || (C::A_CPR & (C::A_CPR - 1)) == 0) && (C::B_KC || (C::B_CPR & (C::B_CPR - 1)) == 0),
@@ -165,11 +167,11 @@ struct PingPong {
   // four, into two 8 KiB slots (position p at p * 16), and each thread later moves its
   // position's four words into four tables (two sets of four, after the copy area).
   // Otherwise a K tile's 4 bytes ride with the copies of the tile before it, straight into
-  // one of four tables in the copy area, the bytes of K tile kt in table kt % 4.  Positions are ordered so that the
-  // rows of a lane's fragments (16 apart) sit at consecutive positions, four at a time,
-  // and the sixteen lanes of a row of a wave read consecutive runs (no bank conflicts): A
-  // rows wm * 128 + 16 i + l at p = wm * 128 + (i / 4) * 64 + 4 l + i % 4, B rows wn * 64
-  // + 16 j + l at p = 256 + wn * 64 + 4 l + j.
+  // one of four tables in the copy area, the bytes of K tile kt in table kt % 4.  Positions
+  // are ordered so that the rows of a lane's fragments (16 apart) sit at consecutive
+  // positions, four at a time, and the sixteen lanes of a row of a wave read consecutive
+  // runs (no bank conflicts): A rows wm * 128 + 16 i + l at p = wm * 128 + (i / 4) * 64 +
+  // 4 l + i % 4, B rows wn * 64 + 16 j + l at p = 256 + wn * 64 + 4 l + j.
   static constexpr int A_OFF = 0, B_OFF = S * C::A_BYTES;
   static constexpr int SC_TABLE = 4 * (C::BM + C::BN);              // one K tile's words
   static constexpr int SCB_REGION = MXS ? 2 * 4 * SC_TABLE : 0;       // the copy area
