@@ -140,6 +140,41 @@ def test_odd_shapes_auto(gpu, M, N, K, tA, tB):
         _assert_ok(compare(p, data, C), f"{M}x{N}x{K} {tA}{tB} {c_dtype}")
 
 
+def _random_problems(n=24, seed=2026):
+    """Seeded mid-size problems for the shape-driven choice: M, N in [200, 3000], K in [8,
+    3000], each a multiple of 16 four times in five (the fast kernels' alignment) and any
+    value otherwise (the generic kernel), any transposes, bf16 or E4M3 operands, bf16 or
+    fp32 C, alpha and beta drawn (beta 0 half the time)."""
+    rng = np.random.default_rng(seed)
+    dim = lambda lo, hi: int(rng.integers(lo // 16, hi // 16 + 1)) * 16 if rng.random() < 0.8 else int(
+        rng.integers(lo, hi + 1))
+    out = []
+    for i in range(n):
+        M, N, K = dim(200, 3000), dim(200, 3000), dim(8, 3000)
+        tA, tB = (int(v) for v in rng.integers(0, 2, 2))
+        fp8 = rng.random() < 0.3
+        c_dtype = "f32" if rng.random() < 0.4 else "bf16"
+        alpha = float(rng.choice([1.0, -0.75, 2.0]))
+        beta = 0.0 if rng.random() < 0.5 else float(rng.choice([1.0, 0.5, -1.25]))
+        out.append(gi.Gemm(f"r{i}", M, N, K, transA=tA, transB=tB, in_dtype="e4m3" if fp8 else "bf16",
+                           c_dtype=c_dtype, alpha=alpha, beta=beta, dist="e4m3" if fp8 else "normal",
+                           c_dist="normal" if beta != 0.0 else None))
+    return out
+
+
+@pytest.mark.parametrize("p", _random_problems(), ids=lambda p: f"{p.name}-{p.M}x{p.N}x{p.K}-{p.transA}{p.transB}-"
+                         f"{p.in_dtype}-{p.c_dtype}")
+def test_random_midsize_shapes(gpu, p):
+    """Whatever policy the model picks (ping-pong, ring, register-staged or generic, split or
+    not), checked on rows spread over every M tile."""
+    import dense_blas3_gemm_amd as d
+    data = p.make(seeds=(p.M, p.N, p.K))
+    C = run_gpu(gpu, p, data)
+    rows = sample_rows(p.M, per_tile=1, cap=48, seed=p.K)
+    pol = gpu.query_policy(p.M, p.N, p.K, p.transA, p.transB, d.dtype_code(p.in_dtype, p.c_dtype))
+    _assert_ok(compare(p, data, C, rows=rows), f"{p.name} {pol}")
+
+
 def test_padded_leading_dimensions(gpu):
     """Row strides larger than the row length (aligned and unaligned)."""
     import torch
