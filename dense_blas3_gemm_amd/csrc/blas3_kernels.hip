@@ -26,35 +26,6 @@ __device__ inline uint16_t f2bf(float v) { return __builtin_bit_cast(uint16_t, s
 
 __device__ inline bool referenced(int i, int j, int uplo) { return uplo == 0 ? i >= j : i <= j; }
 
-// Items of the block inversion below: item it = s * (NB / G) + g is row group g of step s,
-// which updates rows r > k (lower) or r < k (upper) with k = s or NB - 1 - s.
-template <bool UPPER, int NB, int G>
-constexpr bool item_has_work(int it) {
-  const int s = it / (NB / G), g = it % (NB / G), k = UPPER ? NB - 1 - s : s;
-  return UPPER ? g * G < k : g * G + G - 1 > k;
-}
-template <bool UPPER, int NB, int G>
-constexpr int next_item(int it) {  // the next item with work after it, or -1
-  for (int j = it + 1; j < NB * (NB / G); ++j)
-    if (item_has_work<UPPER, NB, G>(j)) return j;
-  return -1;
-}
-template <bool UPPER, int NB, int G>
-constexpr int item_slot(int it) {  // register buffer of item it: alternates over the items with work
-  int n = 0;
-  for (int j = 0; j < it; ++j) n += item_has_work<UPPER, NB, G>(j) ? 1 : 0;
-  return n & 1;
-}
-
-// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), expanded at compile time
-template <int N, int I = 0, class F>
-__device__ __forceinline__ void cfor(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    cfor<N, I + 1>(f);
-  }
-}
-
 // dst[r][c] (r < rows, c < cols, leading dimension ldd) = T[r0 + r][c0 + c] of the n x n
 // triangular matrix T.  One thread per 8 consecutive columns of one row, written with one
 // 16-byte store; a group inside the stored triangle (and off a unit diagonal) is read with
@@ -219,101 +190,153 @@ __global__ __launch_bounds__(256) void expand_sym_kernel(const uint16_t* __restr
 
 // Inverse of each diagonal block T_bb (rows and columns [b*NB, b*NB + nb), nb = NB except
 // for a shorter last block) of the n x n triangular T, padded to NB x NB with the
-// identity.  Workgroup b, thread c computes column c of inv(T_bb) by column-oriented
-// substitution in fp32 with the whole column in registers: for each k in order
-// (ascending for a lower block, descending for an upper one), x_k = b_k / T_kk, then
-// b_r -= T_rk * x_k for the rows r still to come.  The updates of one step are
-// independent, so the loop is bound by FMA issue, not by latency; T is kept transposed in
-// LDS so that column k is one broadcast row.  The result, zeros outside the triangle, is
-// stored in fp32 at dst + b*NB*NB, [NB][NB]; blocks past n are the identity.
+// identity, in fp32, by recursive doubling: an upper block is handled as the transpose of
+// a lower one, L = T_bb^T, inv(T_bb) = inv(L)^T.  For a lower block [A 0; C D],
+//   inv = [inv(A) 0; -inv(D) (C inv(A))  inv(D)],
+// so the inverses of the four 32 x 32 diagonal blocks (one column per thread, by
+// substitution with the column in registers) give those of the two 64 x 64 blocks (two
+// products of 32 x 32 matrices each), which give the 128 x 128 inverse (two products of
+// 64 x 64 matrices).  The serial chain is 32 substitution steps plus four products,
+// against 128 steps for substitution over the whole block.  L is kept transposed in LDS
+// (column k one contiguous row); the inverse X is built in LDS, the products' first
+// factor W = C inv(A) parked in X's upper triangle (zero in the result, cleared after
+// use).  The result, zeros outside the triangle, is stored at dst + b*NB*NB, [NB][NB];
+// blocks past n are the identity.
 template <bool UPPER>
-__global__ __launch_bounds__(kTrsmNB) void invert_diag_kernel(const uint16_t* __restrict__ src, int64_t lds, int n,
-                                                              int unit, int vec, float* __restrict__ dst) {
-  constexpr int NB = kTrsmNB;
-  constexpr int LD = NB + 4;  // row stride of Tt: float4-aligned, 4-way bank spread on the transposing writes
-  __shared__ __attribute__((aligned(16))) float Tt[NB * LD];  // Tt[k * LD + r] = T[r][k]
-  __shared__ float dinv[NB];                                  // 1 / T[k][k]
+__global__ __launch_bounds__(256) void invert_diag_kernel(const uint16_t* __restrict__ src, int64_t lds, int n,
+                                                          int unit, int vec, float* __restrict__ dst) {
+  constexpr int NB = kTrsmNB, LD = NB + 4, SB = 32;  // row stride: float4-aligned rows
+  static_assert(NB == 128, "three doubling levels from 32");
+  __shared__ __attribute__((aligned(16))) float Lt[NB * LD];  // Lt[k * LD + r] = L[r][k]
+  __shared__ __attribute__((aligned(16))) float X[NB * LD];   // X[r * LD + c] = inv(L)[r][c]
+  __shared__ float dinv[NB];                                  // 1 / L[k][k]
   const int b = blockIdx.x, o = b * NB;
   const int nb = n - o < NB ? n - o : NB;
-  const int c = threadIdx.x;
-  // Thread c reads row c of the block: with `vec` (a full block, 16-byte aligned rows) as
-  // 16 independent 16-byte loads issued together, else element by element; it writes
-  // column c of Tt (consecutive threads, consecutive LDS words).
-  const int i = c;
-  uint16_t row[NB];
+  const int t = threadIdx.x;
+  // ---- L (lower: L[i][j] = T[o+i][o+j]; upper: T[o+j][o+i]), j <= i; the identity past
+  // nb and on a unit diagonal; zeros above the diagonal.  Element (p, q) of the stored
+  // block is L[i][j] with (i, j) = (p, q) for a lower block and (q, p) for an upper one.
+  auto put = [&](int p, int q, uint16_t bits) {
+    const int i = UPPER ? q : p, j = UPPER ? p : q;
+    float v = 0.f;
+    if (i == j && (unit || i >= nb)) v = 1.f;
+    else if (j <= i && i < nb && j < nb) v = bf16f(bits);
+    Lt[j * LD + i] = v;
+  };
   if (vec && nb == NB) {
-    const uint4* rp = (const uint4*)(src + (int64_t)(o + i) * lds + o);
-    uint4 w[NB / 8];
+    // a whole block with 16-byte aligned rows: thread t reads half t % 2 of row t / 2 as 8
+    // independent 16-byte loads issued together (the other triangle is read and dropped)
+    const int p = t >> 1, q0 = (t & 1) * (NB / 2);
+    const uint4* rp = (const uint4*)(src + (int64_t)(o + p) * lds + o + q0);
+    uint4 w[NB / 16];
 #pragma unroll
-    for (int q = 0; q < NB / 8; ++q) w[q] = rp[q];
+    for (int qq = 0; qq < NB / 16; ++qq) w[qq] = rp[qq];
 #pragma unroll
-    for (int q = 0; q < NB / 8; ++q) {
-      const uint32_t u[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
+    for (int qq = 0; qq < NB / 16; ++qq) {
+      const uint32_t u[4] = {w[qq].x, w[qq].y, w[qq].z, w[qq].w};
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        row[8 * q + 2 * h] = (uint16_t)u[h];
-        row[8 * q + 2 * h + 1] = (uint16_t)(u[h] >> 16);
+      for (int hh = 0; hh < 4; ++hh) {
+        put(p, q0 + 8 * qq + 2 * hh, (uint16_t)u[hh]);
+        put(p, q0 + 8 * qq + 2 * hh + 1, (uint16_t)(u[hh] >> 16));
       }
     }
   } else {
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-      row[j] = i < nb && j < nb && (UPPER ? i <= j : i >= j) ? src[(int64_t)(o + i) * lds + o + j] : (uint16_t)0;
+    // element by element, the referenced ones only (consecutive threads, consecutive
+    // elements of a row of T)
+    for (int e = t; e < NB * NB; e += 256) {
+      const int p = e / NB, q = e % NB;
+      const bool ref = (UPPER ? p <= q : q <= p) && p < nb && q < nb;
+      put(p, q, ref ? src[(int64_t)(o + p) * lds + o + q] : (uint16_t)0);
+    }
   }
+  for (int e = t; e < NB * NB; e += 256) X[(e / NB) * LD + e % NB] = 0.f;
+  __syncthreads();
+  if (t < NB) dinv[t] = 1.f / Lt[t * LD + t];
+  __syncthreads();
+  // ---- the four 32 x 32 diagonal inverses: thread t < 128 solves column t % 32 of block
+  // t / 32 (x_k = b_k / L_kk, then b_r -= L_rk x_k for r > k)
+  if (t < NB) {
+    const int s0 = (t / SB) * SB, c = t % SB;
+    float x[SB];
 #pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    float v = 0.f;
-    if (i == j && (unit || i >= nb)) v = 1.f;
-    else if (i < nb && j < nb && (UPPER ? i <= j : i >= j)) v = bf16f(row[j]);
-    Tt[j * LD + i] = v;
-    if (i == j) dinv[i] = 1.f / v;
+    for (int r = 0; r < SB; ++r) x[r] = r == c ? 1.f : 0.f;
+#pragma unroll
+    for (int k = 0; k < SB; ++k) {
+      x[k] *= dinv[s0 + k];
+      const float* col = Lt + (s0 + k) * LD + s0;  // L[s0 + r][s0 + k], r = 0 .. 31
+#pragma unroll
+      for (int r4 = (k + 1) / 4; r4 < SB / 4; ++r4) {
+        const float4 l = *(const float4*)(col + 4 * r4);
+        const float lv[4] = {l.x, l.y, l.z, l.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * r4 + e > k) x[4 * r4 + e] -= lv[e] * x[k];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < SB; ++r) X[(s0 + r) * LD + s0 + c] = x[r];
   }
   __syncthreads();
-  float x[NB];
+  // ---- doubling: for each block [A 0; C D] of edge 2h at offset o2, W = C inv(A) into
+  // X[o2 .. o2+h)[o2+h .. o2+2h), then the lower-left quadrant -inv(D) W, then W cleared.
+  // h = 32: two blocks, 128 threads each, 8 outputs per thread; h = 64: one block, 16.
+  auto level = [&](auto hc) {
+    constexpr int h = decltype(hc)::value, TPB = 256 / (NB / (2 * h));  // threads per block
+    constexpr int PER = h * h / TPB;                                      // outputs per thread
+    const int blk = t / TPB, lt = t % TPB, o2 = blk * 2 * h;
+    const int i = lt / (h / PER), j0 = (lt % (h / PER)) * PER;           // row i, columns j0 ..
+    float w[PER];
 #pragma unroll
-  for (int r = 0; r < NB; ++r) x[r] = r == c ? 1.f : 0.f;
-  // The updates of step s (k = s, or NB-1-s for an upper block) touch rows in 32-row
-  // groups; item (s, g) needs the 32 values T[32g .. 32g+31][k].  T never changes, so the
-  // values of the next item that has rows to update are read from LDS one item ahead (two
-  // register buffers) and the read latency hides behind the current item's FMAs.  Step s
-  // starts with x_k = b_k * (1 / T_kk): one multiply on the dependent chain instead of a
-  // division, with the reciprocal read one step ahead.  Every index is a compile-time
-  // constant, so x stays in registers.
-  constexpr int G = 32, NG = NB / G;
-  float4 buf[2][G / 4];
-  auto load = [&](auto item, float4* dstb) {
-    constexpr int s = decltype(item)::value / NG, g = decltype(item)::value % NG;
-    constexpr int k = UPPER ? NB - 1 - s : s;
-    const float4* col = (const float4*)(Tt + k * LD + g * G);
+    for (int e = 0; e < PER; ++e) w[e] = 0.f;
+    // (the loops are unrolled so that the LDS reads of several k are in flight together)
+#pragma unroll 8
+    for (int k = 0; k < h; ++k) {
+      const float cv = Lt[(o2 + k) * LD + o2 + h + i];  // C[i][k] = L[o2+h+i][o2+k]
+      const float* ar = X + (o2 + k) * LD + o2 + j0;    // inv(A)[k][j0 ..]
 #pragma unroll
-    for (int q = 0; q < G / 4; ++q) dstb[q] = col[q];
-  };
-  constexpr int first = next_item<UPPER, NB, G>(-1);
-  load(std::integral_constant<int, first>{}, buf[0]);
-  float dk = dinv[UPPER ? NB - 1 : 0];
-  cfor<NB>([&](auto sc) {
-    constexpr int s = decltype(sc)::value;
-    constexpr int k = UPPER ? NB - 1 - s : s;
-    x[k] = x[k] * dk;  // x_k, before the updates of its step
-    if constexpr (s + 1 < NB) dk = dinv[UPPER ? k - 1 : k + 1];
-    cfor<NG>([&](auto gc) {
-      constexpr int g = decltype(gc)::value, it = s * NG + g;
-      if constexpr (item_has_work<UPPER, NB, G>(it)) {
-        constexpr int nxt = next_item<UPPER, NB, G>(it);
-        constexpr int slot = item_slot<UPPER, NB, G>(it);
-        if constexpr (nxt >= 0) load(std::integral_constant<int, nxt>{}, buf[slot ^ 1]);
-        const float* v = (const float*)buf[slot];
-        cfor<G>([&](auto jc) {
-          constexpr int r = g * G + decltype(jc)::value;
-          if constexpr (UPPER ? r < k : r > k) x[r] -= v[decltype(jc)::value] * x[k];
-        });
-        __builtin_amdgcn_sched_barrier(0);
+      for (int e4 = 0; e4 < PER / 4; ++e4) {
+        const float4 a4 = *(const float4*)(ar + 4 * e4);
+        w[4 * e4] += cv * a4.x;
+        w[4 * e4 + 1] += cv * a4.y;
+        w[4 * e4 + 2] += cv * a4.z;
+        w[4 * e4 + 3] += cv * a4.w;
       }
-    });
-  });
-  float* out = dst + (int64_t)b * NB * NB;
+    }
+    float* wr = X + (o2 + i) * LD + o2 + h + j0;  // W[i][j0 ..], in the upper-right quadrant
 #pragma unroll
-  for (int r = 0; r < NB; ++r) out[r * NB + c] = x[r];
+    for (int e = 0; e < PER; ++e) wr[e] = w[e];
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < PER; ++e) w[e] = 0.f;
+#pragma unroll 4
+    for (int k = 0; k <= i; ++k) {
+      const float dv = X[(o2 + h + i) * LD + o2 + h + k];  // inv(D)[i][k], zero for k > i
+      const float* wk = X + (o2 + k) * LD + o2 + h + j0;    // W[k][j0 ..]
+#pragma unroll
+      for (int e4 = 0; e4 < PER / 4; ++e4) {
+        const float4 w4 = *(const float4*)(wk + 4 * e4);
+        w[4 * e4] -= dv * w4.x;
+        w[4 * e4 + 1] -= dv * w4.y;
+        w[4 * e4 + 2] -= dv * w4.z;
+        w[4 * e4 + 3] -= dv * w4.w;
+      }
+    }
+    float* qr = X + (o2 + h + i) * LD + o2 + j0;  // the lower-left quadrant
+#pragma unroll
+    for (int e = 0; e < PER; ++e) qr[e] = w[e];
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < PER; ++e) wr[e] = 0.f;
+    __syncthreads();
+  };
+  level(std::integral_constant<int, 32>{});
+  level(std::integral_constant<int, 64>{});
+  // ---- out: inv(T_bb) = X (lower) or X^T (upper), row-major, coalesced rows
+  float* out = dst + (int64_t)b * NB * NB;
+  for (int e = t; e < NB * NB; e += 256) {
+    const int r = e / NB, c = e % NB;
+    out[e] = UPPER ? X[c * LD + r] : X[r * LD + c];
+  }
 }
 
 // Inverse of each 2 x 2 block of the 128-block inverses: the 256 x 256 diagonal block
@@ -548,10 +571,10 @@ hipError_t launch_invert_diag(const void* src, int64_t lds, int n, int uplo, int
   // rows of T readable as 16-byte vectors
   const int vec = ((uintptr_t)src % 16 == 0) && lds % 8 == 0;
   if (uplo == 0)
-    hipLaunchKernelGGL(invert_diag_kernel<false>, dim3((unsigned)(2 * blocks)), dim3(kTrsmNB), 0, s,
+    hipLaunchKernelGGL(invert_diag_kernel<false>, dim3((unsigned)(2 * blocks)), dim3(256), 0, s,
                        (const uint16_t*)src, lds, n, unit, vec, inv128);
   else
-    hipLaunchKernelGGL(invert_diag_kernel<true>, dim3((unsigned)(2 * blocks)), dim3(kTrsmNB), 0, s,
+    hipLaunchKernelGGL(invert_diag_kernel<true>, dim3((unsigned)(2 * blocks)), dim3(256), 0, s,
                        (const uint16_t*)src, lds, n, unit, vec, inv128);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
