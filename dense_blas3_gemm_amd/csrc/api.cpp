@@ -436,9 +436,25 @@ static hipError_t enqueue_impl(int cu_count, hipStream_t stream, void* ws, int64
   a.B2 = x.B2;
   a.lda2 = x.lda2;
   a.ldb2 = x.ldb2;
-  const bool extras = x.tri != TRI_NONE || x.kband != KBAND_NONE || x.dual;
+  const bool batched = x.batch_y > 1 || x.batch_z > 1;
+  if (batched) {
+    a.batch_y = x.batch_y;
+    a.batch_z = x.batch_z;
+    for (int i = 0; i < 2; ++i) {
+      a.bsA[i] = x.bsA[i];
+      a.bsB[i] = x.bsB[i];
+      a.bsC[i] = x.bsC[i];
+    }
+  }
+  const bool extras = x.tri != TRI_NONE || x.kband != KBAND_NONE || x.dual || batched;
 
-  if (K == 0 || alpha == 0.f) return launch_scale(a, stream);
+  if (K == 0 || alpha == 0.f) {
+    if (batched) {  // the scaling kernel runs one product
+      *unsupported = true;
+      return hipSuccess;
+    }
+    return launch_scale(a, stream);
+  }
   Problem pr = make_problem(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, dtype, sa, ldsa, sb, ldsb);
   if (extras) {
     pr.blas3 = true;
@@ -456,6 +472,12 @@ static hipError_t enqueue_impl(int cu_count, hipStream_t stream, void* ws, int64
     return hipSuccess;
   }
   const Policy& pol = policy_at(idx);
+  // a batch runs only on the direct-to-LDS kernels, unsplit, with at most a K band (the
+  // same band in every product)
+  if (batched && (pol.pipe != 1 || sp > 1 || sk.tiles > 0 || x.tri != TRI_NONE || x.dual)) {
+    *unsupported = true;
+    return hipSuccess;
+  }
   if (pol.kind == KIND_SIMT) {
     if ((M + 63) / 64 > 65535) {
       *unsupported = true;
@@ -468,9 +490,12 @@ static hipError_t enqueue_impl(int cu_count, hipStream_t stream, void* ws, int64
   a.group = pol.group;
   a.raster_n = pol.raster_n;
   a.xcd = pol.xcd;
-  if (x.kband != KBAND_NONE) {
+  const int64_t batch = (int64_t)(x.batch_y > 1 ? x.batch_y : 1) * (x.batch_z > 1 ? x.batch_z : 1);
+  if (x.kband != KBAND_NONE && (int64_t)a.tiles_m * a.tiles_n * batch > cu_count) {
     // longest tiles first in dispatch order (tile_of): no per-XCD split of the order, and
-    // groups of tile rows (A bands) or columns (B bands) walked from the long end
+    // groups of tile rows (A bands) or columns (B bands) walked from the long end.  (In a
+    // single round every tile starts at once: the order does not matter there, and the
+    // per-XCD split keeps the operands' reuse in each L2.)
     a.xcd = 1;
     a.raster_n = (x.kband == KBAND_B_LOWER || x.kband == KBAND_B_UPPER) ? 1 : 0;
   }

@@ -91,6 +91,12 @@ int leaf_policy(int side) {
   return side == GEMM_SIDE_LEFT ? left : right;
 }
 
+// The policy of the batched products that double the diagonal inverses.
+int doubling_policy() {
+  static const int p = policy_find("bf16_dma_m64n64k64_w2x2_mt16_s4");
+  return p;
+}
+
 struct Trsm {
   HandleView hv;
   int side, transA;
@@ -100,7 +106,13 @@ struct Trsm {
   int64_t lda;
   void* B;
   int64_t ldb;
-  uint16_t* inv;      // inverted 256 x 256 diagonal blocks, [blocks][256][256]
+  // Inverses of T's lf x lf diagonal blocks, [ceil(n / lf)][lf][lf] (lf = 256, 512 or
+  // 1024).  With lf > 256 the whole lf-blocks (n / lf of them) start from the 128-block
+  // inverses on their diagonals and are completed by doubling (doubled()), and a leaf of lf
+  // rows (columns) is one product with the lf-block inverse; the rest of T (a trailing part
+  // shorter than lf) holds 256-block inverses and is solved with 256-leaves.
+  uint16_t* inv;
+  int64_t lf = kTrsmLeaf;
   uint16_t* scratch;  // one block row (column) of B, for leaves that cannot run in place
   // Out of place: every leaf writes its rows (columns) of X to X [M][ldx] in the workspace,
   // the updates read X from there, and one copy moves X into B at the end.  The leaves then
@@ -121,10 +133,60 @@ struct Trsm {
   const void* xsrc(int64_t row, int64_t col) const { return X ? off(X, row, col, ldx, 2) : off(B, row, col, ldb, 2); }
   int64_t xld() const { return X ? ldx : ldb; }
 
-  void leaf(int64_t o, int64_t nb, float alpha) {
-    constexpr int L = kTrsmLeaf;
-    const uint16_t* ib = inv + (o / L) * L * L;
+  // the inverse of the diagonal block that starts at o (a multiple of 256), leading dimension lf
+  const uint16_t* inv_at(int64_t o) const { return inv + (o / lf) * lf * lf + (o % lf) * (lf + 1); }
+  bool whole_lf(int64_t o, int64_t nb) const { return lf > kTrsmLeaf && nb == lf && o % lf == 0; }
+
+  // Completes the inverses of the whole lf-blocks: the inverse of a diagonal block
+  // [P 0; C R] (lower T) of edge 2h is [inv(P) 0; -inv(R) C inv(P)  inv(R)], and of
+  // [P C; 0 R] (upper) [inv(P)  -inv(P) C inv(R); 0 inv(R)].  For h = 128, 256, .. lf/2, two
+  // batched products over every 2h-block of every whole lf-block: W = C inv(P) (lower) or
+  // C inv(R) (upper) into the workspace, then the off-diagonal block -inv(R) W or
+  // -inv(P) W, each rounded to bf16.  The inverses are triangular: each product's K band
+  // skips the K tiles that meet only their zeros.
+  void doubled(int uplo, int64_t n, uint16_t* W) {
+    const int64_t whole = n / lf;
+    if (lf == kTrsmLeaf || whole == 0) return;
+    const bool lower = uplo == GEMM_LOWER;
     GemmExtras x;
+    x.policy = doubling_policy();
+    x.batch_z = (int)whole;
+    for (int64_t h = kTrsmNB; 2 * h <= lf; h *= 2) {
+      const int64_t per = lf / (2 * h);  // 2h-blocks per lf-block
+      x.batch_y = (int)per;
+      const void* Cb = lower ? off(A, h, 0, lda, 2) : off(A, 0, h, lda, 2);
+      const uint16_t* iP = inv;
+      const uint16_t* iR = inv + h * (lf + 1);
+      uint16_t* Q = lower ? inv + h * lf : inv + h;
+      const int64_t sT[2] = {2 * h * (lda + 1), lf * (lda + 1)};
+      const int64_t sI[2] = {2 * h * (lf + 1), lf * lf};
+      const int64_t sW[2] = {h * h, per * h * h};
+      for (int i = 0; i < 2; ++i) {
+        x.bsA[i] = sT[i];
+        x.bsB[i] = sI[i];
+        x.bsC[i] = sW[i];
+      }
+      x.kband = lower ? KBAND_B_LOWER : KBAND_B_UPPER;
+      keep(gemm_enqueue(hv, 0, 0, h, h, h, 1.f, Cb, lda, lower ? iP : iR, lf, 0.f, W, h, GEMM_BF16_BF16, x));
+      for (int i = 0; i < 2; ++i) {
+        x.bsA[i] = sI[i];
+        x.bsB[i] = sW[i];
+        x.bsC[i] = sI[i];
+      }
+      x.kband = lower ? KBAND_A_LOWER : KBAND_A_UPPER;
+      keep(gemm_enqueue(hv, 0, 0, h, h, h, -1.f, lower ? iR : iP, lf, W, h, 0.f, Q, lf, GEMM_BF16_BF16, x));
+    }
+  }
+
+  void leaf(int64_t o, int64_t nb, float alpha) {
+    const uint16_t* ib = inv_at(o);
+    const int64_t L = lf;
+    GemmExtras x;
+    // op(inv) is triangular like op(T): the K band skips the tiles of its zeros
+    if (side == GEMM_SIDE_LEFT)
+      x.kband = opT_lower ? KBAND_A_LOWER : KBAND_A_UPPER;
+    else
+      x.kband = opT_lower ? KBAND_B_LOWER : KBAND_B_UPPER;
     if (X) {  // out of place: any policy
       if (side == GEMM_SIDE_LEFT)
         keep(gemm_enqueue(hv, transA, 0, nb, N, nb, alpha, ib, L, off(B, o, 0, ldb, 2), ldb, 0.f, off(X, o, 0, ldx, 2),
@@ -151,16 +213,18 @@ struct Trsm {
         x.policy = pol;
         keep(gemm_enqueue(hv, 0, transA, M, nb, nb, alpha, Bb, ldb, ib, L, 0.f, Bb, ldb, GEMM_BF16_BF16, x));
       } else {
-        keep(gemm_enqueue(hv, 0, transA, M, nb, nb, alpha, Bb, ldb, ib, L, 0.f, scratch, L, GEMM_BF16_BF16, x));
-        keep(launch_copy2d(scratch, L, Bb, ldb, (int)M, (int)nb, hv.stream));
+        keep(gemm_enqueue(hv, 0, transA, M, nb, nb, alpha, Bb, ldb, ib, L, 0.f, scratch, kTrsmLeaf, GEMM_BF16_BF16,
+                          x));
+        keep(launch_copy2d(scratch, kTrsmLeaf, Bb, ldb, (int)M, (int)nb, hv.stream));
       }
     }
   }
 
   // Rows [r0, r0+m) of op(T) X = alpha * B (left side).
   void left(int64_t r0, int64_t m, float alpha) {
-    if (m <= kTrsmLeaf) return leaf(r0, m, alpha);
-    const int64_t m1 = ((m + 1) / 2 + kTrsmLeaf - 1) / kTrsmLeaf * kTrsmLeaf;
+    if (m <= kTrsmLeaf || whole_lf(r0, m)) return leaf(r0, m, alpha);
+    const int64_t g = m > lf ? lf : kTrsmLeaf;  // whole lf-blocks while they fit
+    const int64_t m1 = ((m + 1) / 2 + g - 1) / g * g;
     const GemmExtras x;
     if (opT_lower) {
       left(r0, m1, alpha);
@@ -177,8 +241,9 @@ struct Trsm {
 
   // Columns [c0, c0+n) of X op(T) = alpha * B (right side).
   void right(int64_t c0, int64_t n, float alpha) {
-    if (n <= kTrsmLeaf) return leaf(c0, n, alpha);
-    const int64_t n1 = ((n + 1) / 2 + kTrsmLeaf - 1) / kTrsmLeaf * kTrsmLeaf;
+    if (n <= kTrsmLeaf || whole_lf(c0, n)) return leaf(c0, n, alpha);
+    const int64_t g = n > lf ? lf : kTrsmLeaf;
+    const int64_t n1 = ((n + 1) / 2 + g - 1) / g * g;
     const GemmExtras x;
     if (!opT_lower) {  // X1 first: X2 op(T)22 = alpha*B2 - X1 op(T)12
       right(c0, n1, alpha);
@@ -383,14 +448,33 @@ gemm_status_t gemm_trsm(gemm_handle_t h, int side, int uplo, int transA, int dia
   if (!g.ok) return GEMM_STATUS_INTERNAL;
   if (alpha == 0.f)  // X = 0
     return status_of(gemm_enqueue(hv, 0, 0, M, N, 0, 0.f, nullptr, 1, nullptr, 1, 0.f, B, ldb, dtype, GemmExtras{}));
-  // workspace: the 256-block inverses (bf16), the fp32 128-block inverses they are made
-  // from, and one leaf's rows (columns) of B for leaves that cannot run in place
+  // workspace: the diagonal inverses (bf16), the fp32 128-block inverses they are made
+  // from, the doubling products' W, and X (out of place) or one leaf's rows (columns) of B
+  // for leaves that cannot run in place
   auto up256 = [](size_t v) { return (v + 255) / 256 * 256; };
   const int64_t blocks = (n + kTrsmLeaf - 1) / kTrsmLeaf;
-  const size_t inv_bytes = up256((size_t)blocks * kTrsmLeaf * kTrsmLeaf * 2);
+  auto inv_bytes_of = [&](int64_t e) { return up256((size_t)((n + e - 1) / e) * e * e * 2); };
+  auto w_bytes_of = [&](int64_t e) { return e > kTrsmLeaf ? up256((size_t)(n / e) * e * e / 2) : (size_t)0; };
   const size_t inv128_bytes = up256((size_t)2 * blocks * kTrsmNB * kTrsmNB * 4);
   const size_t scratch_bytes = side == GEMM_SIDE_LEFT ? (size_t)kTrsmLeaf * pad8(N) * 2 : (size_t)M * kTrsmLeaf * 2;
-  if (!hv.ws || inv_bytes + inv128_bytes + scratch_bytes > hv.ws_bytes) return GEMM_STATUS_NOT_SUPPORTED;
+  if (!hv.ws || inv_bytes_of(kTrsmLeaf) + inv128_bytes + scratch_bytes > hv.ws_bytes) return GEMM_STATUS_NOT_SUPPORTED;
+  // Out of place for large right-hand sides (from 2^20 elements of B), when X fits beside
+  // the inverses: its one copy back is cheaper than leaves limited to one tile per leaf.
+  // Out of place, the leaves are lf-blocks: the largest of 1024 and 512 that T holds twice,
+  // when T's rows can be read as 16-byte vectors (the batched doubling products) and
+  // everything fits; else 256.
+  const int64_t ldx = pad8(N);
+  const size_t x_bytes = (size_t)M * ldx * 2;
+  const bool out_of_place = M * N >= ((int64_t)1 << 20);
+  int64_t lf = kTrsmLeaf;
+  if (out_of_place && (uintptr_t)A % 16 == 0 && lda % 8 == 0 && doubling_policy() >= 0) {
+    for (int64_t e = 4 * kTrsmLeaf; e > kTrsmLeaf; e /= 2)
+      if (n >= 2 * e && inv_bytes_of(e) + inv128_bytes + w_bytes_of(e) + x_bytes <= hv.ws_bytes) {
+        lf = e;
+        break;
+      }
+  }
+  const size_t inv_bytes = inv_bytes_of(lf), w_bytes = w_bytes_of(lf);
   Trsm t;
   t.hv = hv;
   t.side = side;
@@ -403,17 +487,16 @@ gemm_status_t gemm_trsm(gemm_handle_t h, int side, int uplo, int transA, int dia
   t.B = B;
   t.ldb = ldb;
   t.inv = (uint16_t*)hv.ws;
+  t.lf = lf;
   float* inv128 = (float*)((char*)hv.ws + inv_bytes);
-  t.scratch = (uint16_t*)((char*)hv.ws + inv_bytes + inv128_bytes);
-  // Out of place for large right-hand sides (from 2^20 elements of B), when X fits beside
-  // the inverses: its one copy back is cheaper than leaves limited to one tile per leaf.
-  const int64_t ldx = pad8(N);
-  const size_t x_bytes = (size_t)M * ldx * 2;
-  if (M * N >= ((int64_t)1 << 20) && inv_bytes + inv128_bytes + x_bytes <= hv.ws_bytes) {
+  uint16_t* W = (uint16_t*)((char*)hv.ws + inv_bytes + inv128_bytes);
+  t.scratch = (uint16_t*)((char*)hv.ws + inv_bytes + inv128_bytes + w_bytes);
+  if (out_of_place && inv_bytes + inv128_bytes + w_bytes + x_bytes <= hv.ws_bytes) {
     t.X = t.scratch;
     t.ldx = ldx;
   }
-  t.keep(launch_invert_diag(A, lda, (int)n, uplo, diag, inv128, t.inv, hv.stream));
+  t.keep(launch_invert_diag(A, lda, (int)n, uplo, diag, inv128, t.inv, (int)lf, hv.stream));
+  if (t.err == hipSuccess) t.doubled(uplo, n, W);
   if (t.err == hipSuccess) {
     if (side == GEMM_SIDE_LEFT)
       t.left(0, M, alpha);

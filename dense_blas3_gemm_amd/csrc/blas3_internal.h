@@ -33,6 +33,9 @@ struct GemmExtras {
   const void* A2 = nullptr;
   const void* B2 = nullptr;
   int64_t lda2 = 0, ldb2 = 0;
+  // a batch of equal products (GemmArgs::batch_y ..; the direct-to-LDS kernels only)
+  int batch_y = 1, batch_z = 1;
+  int64_t bsA[2] = {0, 0}, bsB[2] = {0, 0}, bsC[2] = {0, 0};
   int policy = -1;
 };
 
@@ -55,10 +58,14 @@ hipError_t launch_expand_tri_trans(const void* src, int64_t lds, void* dst, int6
                                    int cols, int cols_pad, int n, int uplo, int unit, hipStream_t s);
 hipError_t launch_expand_sym(const void* src, int64_t lds, void* dst, int64_t ldd, int r0, int c0, int rows, int cols,
                              int cols_pad, int n, int uplo, hipStream_t s);
-// inv128: 2 * ceil(n / 256) fp32 [128][128] blocks (scratch); dst: ceil(n / 256) bf16
-// [256][256] blocks, the inverses of T's 256 x 256 diagonal blocks (identity past n).
+// inv128: 2 * ceil(n / 256) fp32 [128][128] blocks (scratch); dst: ceil(n / lf) bf16
+// [lf][lf] blocks (lf a multiple of 256).  With lf = 256, or past T's whole lf-blocks, the
+// inverses of T's 256 x 256 diagonal blocks (identity past n) on their diagonals, zeros in
+// their 256-blocks outside the triangle; in T's whole lf-blocks (lf > 256), the inverses of
+// the 128 x 128 diagonal blocks on the diagonals and zeros in the 128-blocks outside the
+// triangle, for the products that double them up to lf x lf.
 hipError_t launch_invert_diag(const void* src, int64_t lds, int n, int uplo, int unit, float* inv128, void* dst,
-                              hipStream_t s);
+                              int lf, hipStream_t s);
 // dst [cols][ldd] = src [rows][lds] transposed (bf16); dst rows zero-padded to a multiple of
 // 8 columns (ldd >= round_up(rows, 8)).
 hipError_t launch_transpose(const void* src, int64_t lds, void* dst, int64_t ldd, int rows, int cols, hipStream_t s);

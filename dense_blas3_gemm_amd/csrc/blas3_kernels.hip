@@ -201,10 +201,13 @@ __global__ __launch_bounds__(256) void expand_sym_kernel(const uint16_t* __restr
 // (column k one contiguous row); the inverse X is built in LDS, the products' first
 // factor W = C inv(A) parked in X's upper triangle (zero in the result, cleared after
 // use).  The result, zeros outside the triangle, is stored at dst + b*NB*NB, [NB][NB];
-// blocks past n are the identity.
+// blocks past n are the identity.  The first `whole` blocks (those of T's whole lf-blocks)
+// are stored instead rounded to bf16 on the diagonals of bdst, [n / lf][lf][lf], and the
+// lf-blocks' 128-blocks outside the triangle are zeroed: products double them up to lf x lf.
 template <bool UPPER>
 __global__ __launch_bounds__(256) void invert_diag_kernel(const uint16_t* __restrict__ src, int64_t lds, int n,
-                                                          int unit, int vec, float* __restrict__ dst) {
+                                                          int unit, int vec, float* __restrict__ dst,
+                                                          uint16_t* __restrict__ bdst, int lf, int whole) {
   constexpr int NB = kTrsmNB, LD = NB + 4, SB = 32;  // row stride: float4-aligned rows
   static_assert(NB == 128, "three doubling levels from 32");
   __shared__ __attribute__((aligned(16))) float Lt[NB * LD];  // Lt[k * LD + r] = L[r][k]
@@ -332,10 +335,33 @@ __global__ __launch_bounds__(256) void invert_diag_kernel(const uint16_t* __rest
   level(std::integral_constant<int, 32>{});
   level(std::integral_constant<int, 64>{});
   // ---- out: inv(T_bb) = X (lower) or X^T (upper), row-major, coalesced rows
-  float* out = dst + (int64_t)b * NB * NB;
-  for (int e = t; e < NB * NB; e += 256) {
-    const int r = e / NB, c = e % NB;
-    out[e] = UPPER ? X[c * LD + r] : X[r * LD + c];
+  if (b >= whole) {  // for the combination into 256-blocks
+    float* out = dst + (int64_t)b * NB * NB;
+    for (int e = t; e < NB * NB; e += 256) {
+      const int r = e / NB, c = e % NB;
+      out[e] = UPPER ? X[c * LD + r] : X[r * LD + c];
+    }
+  } else {
+    const int per = lf / NB, p = b % per;  // 128-blocks per lf-block; this one's position
+    uint16_t* base = bdst + (int64_t)(b / per) * lf * lf;
+    uint16_t* bo = base + (int64_t)p * NB * (lf + 1);
+    for (int e = t; e < NB * NB / 2; e += 256) {  // two elements per 4-byte store
+      const int r = e / (NB / 2), c = 2 * (e % (NB / 2));
+      const float v0 = UPPER ? X[c * LD + r] : X[r * LD + c];
+      const float v1 = UPPER ? X[(c + 1) * LD + r] : X[r * LD + c + 1];
+      *(uint32_t*)(bo + (int64_t)r * lf + c) = (uint32_t)f2bf(v0) | ((uint32_t)f2bf(v1) << 16);
+    }
+    // the per (per - 1) / 2 128-blocks of the lf-block outside the triangle, dealt out to its
+    // per workgroups in turn: zero block z is (row i, column j), i < j, j (j - 1) / 2 + i = z
+    // (lower; the transpose for upper).  16-byte stores: lf and the offsets are multiples of 8.
+    for (int zb = p; zb < per * (per - 1) / 2; zb += per) {
+      int j = 1;
+      while ((j + 1) * j / 2 <= zb) ++j;
+      const int i = zb - j * (j - 1) / 2;
+      uint16_t* z = base + (int64_t)(UPPER ? j : i) * NB * lf + (UPPER ? i : j) * NB;
+      for (int e = t; e < NB * NB / 8; e += 256)
+        *(uint4*)(z + (int64_t)(e / (NB / 8)) * lf + 8 * (e % (NB / 8))) = make_uint4(0, 0, 0, 0);
+    }
   }
 }
 
@@ -345,18 +371,22 @@ __global__ __launch_bounds__(256) void invert_diag_kernel(const uint16_t* __rest
 // i.e. Q = -P (C R) with (P, R) = (inv(D), inv(A)) or (inv(A), inv(D)).  Workgroup (b, s)
 // computes columns [32s, 32s + 32) of Q in fp32 (W = C R[:, cols], then Q = -P W, each
 // thread a 4 x 4 register tile) and writes columns 32s .. 32s + 31 of both halves of the
-// block, rounded once to bf16, at dst + b*256*256, [256][256].  inv holds the fp32 128-block
-// inverses, block 2b = inv(A), 2b + 1 = inv(D).
+// block, rounded once to bf16.  inv holds the fp32 128-block inverses, block 2b = inv(A),
+// 2b + 1 = inv(D).  dst holds the inverses of T's lf x lf diagonal blocks, [n / lf][lf][lf]
+// (lf a multiple of 256): the 256-block b sits on the diagonal of lf-block b / (lf / 256),
+// and the same workgroups write zeros in the 256-blocks of that lf-block outside its
+// triangle, in their slab of columns (the products that double the inverses up to lf x lf
+// fill the blocks inside the triangle).
 constexpr int CB = 2 * kTrsmNB;  // the combined block edge
 template <bool UPPER>
 __global__ __launch_bounds__(256) void combine_inverse_kernel(const uint16_t* __restrict__ src, int64_t lds, int n,
                                                               int vec, const float* __restrict__ inv,
-                                                              uint16_t* __restrict__ dst) {
+                                                              uint16_t* __restrict__ dst, int lf, int b0) {
   constexpr int NB = kTrsmNB, SW = 32, LD = NB + 4;
   __shared__ __attribute__((aligned(16))) float Xt[NB * LD];  // C^T, then P^T: Xt[k*LD + i] = X[i][k]
   __shared__ __attribute__((aligned(16))) float Rs[NB * SW];  // R[:, cols]
   __shared__ __attribute__((aligned(16))) float Ws[NB * SW];  // W = C R[:, cols]
-  const int b = blockIdx.x, s0 = blockIdx.y * SW, t = threadIdx.x;
+  const int b = b0 + (int)blockIdx.x, s0 = blockIdx.y * SW, t = threadIdx.x;
   const int o = b * CB;
   const float* Ai = inv + (int64_t)(2 * b) * NB * NB;
   const float* Di = Ai + NB * NB;
@@ -444,20 +474,32 @@ __global__ __launch_bounds__(256) void combine_inverse_kernel(const uint16_t* __
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) q[ii][jj] -= av[ii] * wv[jj];
   }
-  uint16_t* out = dst + (int64_t)b * CB * CB;
+  const int per = lf / CB, p = b % per;  // 256-blocks per lf-block; this one's position
+  uint16_t* out = dst + (int64_t)(b / per) * lf * lf + (int64_t)p * CB * (lf + 1);
   // Q's quadrant: rows 128.., columns s0.. (lower) or rows 0.., columns 128 + s0.. (upper)
   const int qr = UPPER ? 0 : NB, qc = UPPER ? NB + s0 : s0;
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) out[(qr + i0 + ii) * CB + qc + j0 + jj] = f2bf(q[ii][jj]);
+    for (int jj = 0; jj < 4; ++jj) out[(int64_t)(qr + i0 + ii) * lf + qc + j0 + jj] = f2bf(q[ii][jj]);
   // the other three quadrants' columns of this slab: inv(A) at (0, 0), inv(D) at (128, 128),
   // zeros in the quadrant opposite Q
   for (int e = t; e < NB * SW; e += 256) {
     const int i = e / SW, j = s0 + e % SW;
-    out[i * CB + j] = f2bf(Ai[i * NB + j]);
-    out[(NB + i) * CB + NB + j] = f2bf(Di[i * NB + j]);
-    out[(UPPER ? NB + i : i) * CB + (UPPER ? j : NB + j)] = 0;
+    out[(int64_t)i * lf + j] = f2bf(Ai[i * NB + j]);
+    out[(int64_t)(NB + i) * lf + NB + j] = f2bf(Di[i * NB + j]);
+    out[(int64_t)(UPPER ? NB + i : i) * lf + (UPPER ? j : NB + j)] = 0;
+  }
+  // the same two slabs of columns (s0 .., 128 + s0 ..) of the 256-blocks of this column
+  // outside the triangle: above the diagonal (lower), below it (upper)
+  const int q0 = UPPER ? p + 1 : 0, q1 = UPPER ? per : p;
+  for (int qb = q0; qb < q1; ++qb) {  // 16-byte stores: lf, s0 and the block offsets are multiples of 8
+    uint16_t* z = out + (int64_t)(qb - p) * CB * lf;
+    for (int e = t; e < CB * (SW / 8); e += 256) {
+      const int64_t r = (int64_t)(e / (SW / 8)) * lf + s0 + 8 * (e % (SW / 8));
+      *(uint4*)(z + r) = make_uint4(0, 0, 0, 0);
+      *(uint4*)(z + r + NB) = make_uint4(0, 0, 0, 0);
+    }
   }
 }
 
@@ -566,25 +608,29 @@ hipError_t launch_expand_sym(const void* src, int64_t lds, void* dst, int64_t ld
 }
 
 hipError_t launch_invert_diag(const void* src, int64_t lds, int n, int uplo, int unit, float* inv128, void* dst,
-                              hipStream_t s) {
+                              int lf, hipStream_t s) {
+  if (lf < kTrsmLeaf || lf % kTrsmLeaf != 0) return hipErrorInvalidValue;
   const int blocks = (n + kTrsmLeaf - 1) / kTrsmLeaf;  // 256-blocks; two 128-blocks each
+  // with lf > 256, the 128-blocks of T's whole lf-blocks go to dst in bf16 for the doubling
+  // products; the 256-blocks of the rest are combined here
+  const int whole256 = lf > kTrsmLeaf ? (n / lf) * (lf / kTrsmLeaf) : 0;
   // rows of T readable as 16-byte vectors
   const int vec = ((uintptr_t)src % 16 == 0) && lds % 8 == 0;
   if (uplo == 0)
     hipLaunchKernelGGL(invert_diag_kernel<false>, dim3((unsigned)(2 * blocks)), dim3(256), 0, s,
-                       (const uint16_t*)src, lds, n, unit, vec, inv128);
+                       (const uint16_t*)src, lds, n, unit, vec, inv128, (uint16_t*)dst, lf, 2 * whole256);
   else
     hipLaunchKernelGGL(invert_diag_kernel<true>, dim3((unsigned)(2 * blocks)), dim3(256), 0, s,
-                       (const uint16_t*)src, lds, n, unit, vec, inv128);
+                       (const uint16_t*)src, lds, n, unit, vec, inv128, (uint16_t*)dst, lf, 2 * whole256);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)blocks, kTrsmNB / 32);
+  if (e != hipSuccess || whole256 == blocks) return e;
+  const dim3 grid((unsigned)(blocks - whole256), kTrsmNB / 32);
   if (uplo == 0)
     hipLaunchKernelGGL(combine_inverse_kernel<false>, grid, dim3(256), 0, s, (const uint16_t*)src, lds, n, vec,
-                       (const float*)inv128, (uint16_t*)dst);
+                       (const float*)inv128, (uint16_t*)dst, lf, whole256);
   else
     hipLaunchKernelGGL(combine_inverse_kernel<true>, grid, dim3(256), 0, s, (const uint16_t*)src, lds, n, vec,
-                       (const float*)inv128, (uint16_t*)dst);
+                       (const float*)inv128, (uint16_t*)dst, lf, whole256);
   return hipGetLastError();
 }
 

@@ -73,6 +73,11 @@ struct GemmArgs {
   const void* A2;
   const void* B2;
   int64_t lda2, ldb2;
+  // A batch of equal products (direct-to-LDS kernels, unsplit, a K band at most): workgroup
+  // (x, y, z) runs tile x of the product whose A, B and C start y * bs?[0] + z * bs?[1]
+  // elements past the given ones.  batch_y, batch_z: the batch extents (0 or 1: none).
+  int batch_y, batch_z;
+  int64_t bsA[2], bsB[2], bsC[2];
 };
 enum { TRI_NONE = 0, TRI_LOWER = 1, TRI_UPPER = 2 };
 enum { KBAND_NONE = 0, KBAND_A_LOWER = 1, KBAND_A_UPPER = 2, KBAND_B_LOWER = 3, KBAND_B_UPPER = 4 };

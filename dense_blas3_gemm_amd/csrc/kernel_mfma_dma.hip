@@ -109,6 +109,13 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(GemmArgs a) {
   using Frag = typename FragOf<C::FP8>::T;
   using Acc = typename AccOf<C::MT>::T;
 
+  if (a.batch_y > 1 || a.batch_z > 1) {  // this workgroup's product of the batch
+    const int64_t y = blockIdx.y, z = blockIdx.z;
+    const int c_es = a.c_kind == C_F32 ? 4 : a.c_kind == C_BF16 ? 2 : 1;
+    a.A = (const char*)a.A + (y * a.bsA[0] + z * a.bsA[1]) * C::ES;
+    a.B = (const char*)a.B + (y * a.bsB[0] + z * a.bsB[1]) * C::ES;
+    a.C = (char*)a.C + (y * a.bsC[0] + z * a.bsC[1]) * c_es;
+  }
   int tm, tn, split;
   tile_of(blockIdx.x, a, tm, tn, split);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
@@ -408,7 +415,8 @@ __global__ __launch_bounds__(C::THREADS) void split_reduce_kernel(GemmArgs a) {
 template <class C>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   const int ntiles = a.tiles_m * a.tiles_n;
-  hipLaunchKernelGGL(gemm_dma_kernel<C>, dim3(grid_tiles(a)), dim3(C::THREADS), 0, s, a);
+  const unsigned by = a.batch_y > 1 ? (unsigned)a.batch_y : 1u, bz = a.batch_z > 1 ? (unsigned)a.batch_z : 1u;
+  hipLaunchKernelGGL(gemm_dma_kernel<C>, dim3(grid_tiles(a), by, bz), dim3(C::THREADS), 0, s, a);
   if (a.splits > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

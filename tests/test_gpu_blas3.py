@@ -376,6 +376,43 @@ def test_trsm_exact_integer_out_of_place(gpu, side, uplo, transA):
     assert np.array_equal(to_host(Bd), Xt)
 
 
+@pytest.mark.parametrize("n,m", [(1500, 700), (2300, 456), (2048, 512)])
+@pytest.mark.parametrize("side", [LEFT, RIGHT])
+@pytest.mark.parametrize("uplo", [LOWER, UPPER])
+@pytest.mark.parametrize("transA", [0, 1])
+def test_trsm_exact_integer_doubled_leaves(gpu, n, m, side, uplo, transA):
+    """From 2^20 elements of B the leaves are whole 512- or 1024-blocks of T whose inverses
+    are doubled up from the 256-block ones by batched products: n = 1500 (two 512-blocks and
+    a 476-row tail of 256-leaves), 2300 (two 1024-blocks and a 252 tail), 2048 (two
+    1024-blocks), bit for bit on exact integer systems."""
+    M, N = (n, m) if side == LEFT else (m, n)
+    A, Xt, Bb = _int_system(n, M, N, side, uplo, transA, 1, 50)
+    Bd = to_device(Bb, "bf16")
+    gpu.trsm(to_device(A, "bf16"), Bd, side=side, uplo=uplo, transA=transA, diag=1, alpha=1.0)
+    sync()
+    assert np.array_equal(to_host(Bd), Xt)
+
+
+@pytest.mark.parametrize("n,m", [(1500, 700), (2300, 456)])
+@pytest.mark.parametrize("side", [LEFT, RIGHT])
+@pytest.mark.parametrize("uplo", [LOWER, UPPER])
+def test_trsm_real_doubled_leaves(gpu, n, m, side, uplo):
+    """The doubled 512- and 1024-block inverses on real-valued systems, residual and forward
+    error within the bound."""
+    M, N = (n, m) if side == LEFT else (m, n)
+    A = gi.bf16_triangular(n, uplo, 60)
+    B = gi.bf16_uniform((M, N), 61)
+    Bd = to_device(B, "bf16")
+    gpu.trsm(to_device(A, "bf16"), Bd, side=side, uplo=uplo, transA=0, diag=0, alpha=0.75)
+    sync()
+    X = tolerance.bf16_bits_to_f64(to_host(Bd))
+    X_ref = blas3.trsm(side, uplo, 0, 0, M, N, 0.75, A, B)
+    T = blas3.triangular(A, n, uplo, 0)
+    res = tolerance.trsm_check(X, X_ref, T, 0.75 * tolerance.bf16_bits_to_f64(B), side, n)
+    _report(res)
+    assert res["ok"], res
+
+
 # ------------------------------------------------------------------ panels and strides
 
 @pytest.mark.parametrize("side", [LEFT, RIGHT])

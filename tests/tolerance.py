@@ -108,7 +108,9 @@ def trsm_check(X: np.ndarray, X_ref: np.ndarray, opT: np.ndarray, rhs: np.ndarra
     Error model of the blocked method: the inverted diagonal blocks, each leaf product and
     each GEMM update of B are rounded to bf16 once; a row of X passes through at most
     L = ceil(log2(n / leaf)) updates, one inverted block and one leaf rounding, g = L + 3
-    roundings in all.  Each is a relative perturbation of one bf16 rounding, of the same
+    roundings in all.  (Leaves of 2^d * leaf rows, whose inverses are doubled up d times with
+    two roundings each, run d update levels fewer: L + 3 + d roundings.  g stays L + 3, the
+    stricter count.)  Each is a relative perturbation of one bf16 rounding, of the same
     size as the last one, the rounding of the result itself.  So the measured floor is the
     exact solution X_ref rounded to bf16 once:
         eta_round = backward error of round_bf16(X_ref),  fwd_round = its forward error,
