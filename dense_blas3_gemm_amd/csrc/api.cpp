@@ -492,11 +492,12 @@ static hipError_t enqueue_impl(int cu_count, hipStream_t stream, void* ws, int64
   a.xcd = pol.xcd;
   const int64_t batch = (int64_t)(x.batch_y > 1 ? x.batch_y : 1) * (x.batch_z > 1 ? x.batch_z : 1);
   if (x.kband != KBAND_NONE && (int64_t)a.tiles_m * a.tiles_n * batch > cu_count) {
-    // longest tiles first in dispatch order (tile_of): no per-XCD split of the order, and
-    // groups of tile rows (A bands) or columns (B bands) walked from the long end.  (In a
-    // single round every tile starts at once: the order does not matter there, and the
-    // per-XCD split keeps the operands' reuse in each L2.)
-    a.xcd = 1;
+    // longest tiles first in dispatch order (tile_of): the XCDs take runs of four raster
+    // positions in turn instead of one contiguous part each, and groups of tile rows (A
+    // bands) or columns (B bands) are walked from the long end.  (In a single round every
+    // tile starts at once: the order does not matter there, and the per-XCD split keeps
+    // the operands' reuse in each L2.)
+    a.xcd = pol.xcd > 1 ? -pol.xcd : 1;
     a.raster_n = (x.kband == KBAND_B_LOWER || x.kband == KBAND_B_UPPER) ? 1 : 0;
   }
   a.swizzle = pol.swizzle;

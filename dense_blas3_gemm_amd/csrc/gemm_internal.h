@@ -26,7 +26,7 @@ struct GemmArgs {
   int tiles_m, tiles_n;
   int group;      // raster group width (tiles) along the grouped dimension
   int raster_n;   // 0: groups of `group` tile-rows walked along N; 1: the transpose
-  int xcd;        // number of XCDs to remap across (1 disables the remap)
+  int xcd;        // XCDs to remap across (1 disables the remap; below -1: runs of four in turn)
   int swizzle;    // 1: XOR-swizzled LDS layout, 0: plain row-major LDS tiles
   int krot;       // 1: each XCD starts its K loop at its own eighth of K (see the DMA kernel)
   // Split-K (direct-to-LDS kernels): `splits` workgroups share each output tile, split

@@ -38,10 +38,16 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 // maps are bijections, so every tile is computed exactly once.  With split-K the ids
 // cover tiles x splits; the splits of one tile are neighbours in the remapped order
 // (so they run on one XCD) and `split` is the id's position among them.
+// xcd < -1 (the K-banded grids, walked longest tile first): -xcd XCDs take runs of four
+// consecutive raster positions in turn, so each XCD's L2 serves runs of neighbouring tiles
+// while every XCD keeps to the same stretch of the longest-first order.
 __device__ inline int xcd_remap(int bid, int total, int xcd) {
   if (xcd > 1) {
     const int q = total / xcd;
     if (bid < q * xcd) return (bid % xcd) * q + bid / xcd;
+  } else if (xcd < -1) {
+    const int n = -xcd, chunk = 4 * n;
+    if (bid < total / chunk * chunk) return bid / chunk * chunk + (bid % n) * 4 + (bid / n) % 4;
   }
   return bid;
 }
