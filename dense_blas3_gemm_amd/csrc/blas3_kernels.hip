@@ -188,6 +188,57 @@ __global__ __launch_bounds__(256) void expand_sym_kernel(const uint16_t* __restr
   }
 }
 
+// The same expansion for a region of whole 64 x 64 blocks inside S (rows and columns 16-byte
+// aligned), one wave per block and no LDS: lane (p, q) builds the 8 x 8 sub-block at rows
+// 8q .., columns 8p .. of the output block, from eight 16-byte loads of the stored rows
+// (where the sub-block meets the stored triangle) and eight 16-byte loads of the mirrored
+// rows (where it meets the other one), those transposed in registers; a diagonal block
+// takes each element from the right source.  Loads and stores of a wave cover 8 rows x
+// 128 contiguous bytes each.
+__global__ __launch_bounds__(256) void expand_sym_blocks_kernel(const uint16_t* __restrict__ src, int64_t lds,
+                                                                uint16_t* __restrict__ dst, int64_t ldd, int r0,
+                                                                int c0, int bcols, int nblocks, int uplo) {
+  const int blk = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (blk >= nblocks) return;
+  const int by = blk / bcols, bx = blk % bcols;
+  const int p = lane / 8, q = lane % 8;
+  const int gi = r0 + by * SB + 8 * q, gj = c0 + bx * SB + 8 * p;  // S position of the sub-block
+  const bool lower = uplo == 0;
+  // sub-block rows gi .. gi+7, columns gj .. gj+7: stored where row >= column (lower)
+  const bool any_direct = lower ? gi + 7 >= gj : gi <= gj + 7;
+  const bool any_mirror = lower ? gi < gj + 7 : gi + 7 > gj;
+  uint4 d[8], m[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    d[k] = any_direct ? *(const uint4*)(src + (int64_t)(gi + k) * lds + gj) : make_uint4(0, 0, 0, 0);
+    m[k] = any_mirror ? *(const uint4*)(src + (int64_t)(gj + k) * lds + gi) : make_uint4(0, 0, 0, 0);
+  }
+  // S[gi + k][gj + e] = src[gj + e][gi + k] = element k of m[e] where mirrored
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t dw[4] = {d[k].x, d[k].y, d[k].z, d[k].w};
+    uint32_t w[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const uint4 a = m[2 * h], b = m[2 * h + 1];
+      const uint32_t ak = (k / 2 == 0 ? a.x : k / 2 == 1 ? a.y : k / 2 == 2 ? a.z : a.w);
+      const uint32_t bk = (k / 2 == 0 ? b.x : k / 2 == 1 ? b.y : k / 2 == 2 ? b.z : b.w);
+      const uint32_t mir = (k & 1) ? ((ak >> 16) | (bk & 0xFFFF0000u)) : ((ak & 0xFFFFu) | (bk << 16));
+      if (!any_mirror) {
+        w[h] = dw[h];
+      } else if (!any_direct) {
+        w[h] = mir;
+      } else {  // a diagonal sub-block: element by element
+        const int i = gi + k, j = gj + 2 * h;
+        const uint32_t lo = referenced(i, j, uplo) ? (dw[h] & 0xFFFFu) : (mir & 0xFFFFu);
+        const uint32_t hi = referenced(i, j + 1, uplo) ? (dw[h] & 0xFFFF0000u) : (mir & 0xFFFF0000u);
+        w[h] = lo | hi;
+      }
+    }
+    *(uint4*)(dst + (int64_t)(by * SB + 8 * q + k) * ldd + bx * SB + 8 * p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 // Inverse of each diagonal block T_bb (rows and columns [b*NB, b*NB + nb), nb = NB except
 // for a shorter last block) of the n x n triangular T, padded to NB x NB with the
 // identity, in fp32, by recursive doubling: an upper block is handled as the transpose of
@@ -601,6 +652,13 @@ hipError_t launch_expand_tri_trans(const void* src, int64_t lds, void* dst, int6
 hipError_t launch_expand_sym(const void* src, int64_t lds, void* dst, int64_t ldd, int r0, int c0, int rows, int cols,
                              int cols_pad, int n, int uplo, hipStream_t s) {
   const int vec = ((uintptr_t)src % 16 == 0) && lds % 8 == 0 && r0 % 8 == 0 && c0 % 8 == 0;
+  if (vec && (uintptr_t)dst % 16 == 0 && ldd % 8 == 0 && rows % SB == 0 && cols % SB == 0 && cols_pad == cols &&
+      r0 + rows <= n && c0 + cols <= n && rows > 0 && cols > 0) {
+    const int bcols = cols / SB, nblocks = (rows / SB) * bcols;
+    hipLaunchKernelGGL(expand_sym_blocks_kernel, dim3((unsigned)((nblocks + 3) / 4)), dim3(256), 0, s,
+                       (const uint16_t*)src, lds, (uint16_t*)dst, ldd, r0, c0, bcols, nblocks, uplo);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((cols_pad + SB - 1) / SB), (unsigned)((rows + SB - 1) / SB));
   hipLaunchKernelGGL(expand_sym_kernel, grid, dim3(256), 0, s, (const uint16_t*)src, lds, (uint16_t*)dst, ldd, r0, c0,
                      rows, cols, cols_pad, n, uplo, vec);

@@ -417,9 +417,10 @@ def test_trsm_real_doubled_leaves(gpu, n, m, side, uplo):
 
 @pytest.mark.parametrize("side", [LEFT, RIGHT])
 def test_symm_two_panels(gpu, side):
-    """n = 6144: the expanded symmetric matrix (6144 x 6144 bf16) exceeds the 64 MiB workspace,
-    so it is expanded and multiplied in two row panels (5376 + 768 rows)."""
-    n, other = 6144, 40
+    """n = 12288: the expanded symmetric matrix (12288 x 12288 bf16, 288 MiB) exceeds the 256 MiB
+    workspace, so it is expanded and multiplied in two row panels (10752 + 1536 rows; the
+    second panel's mirrored elements come from rows of the first)."""
+    n, other = 12288, 40
     M, N = (n, other) if side == LEFT else (other, n)
     A = gi.bf16_symmetric_stored(n, UPPER, 5)
     B = gi.bf16_uniform((M, N), 6)
