@@ -302,6 +302,8 @@ __device__ __forceinline__ void pp_add_partial(const float* slot, typename AccOf
 // wave's chunk reads spread over all banks), then all threads take 8 consecutive columns
 // each, 32 threads per 256-column row, add beta*C_old, round to C's type once and store
 // 16 bytes (bf16), 32 (fp32) or 8 (E4M3) per thread.  The same arithmetic as store_group.
+// The whole-vector stores are non-temporal: C is not read again by the kernel, and
+// streaming it past the caches cut 4096^2 at K = 256 from 18.0 to 16.0 us.
 template <class C>
 __device__ __forceinline__ void pp_store_tile_lds(const GemmArgs& a, const typename AccOf<C::MT>::T (&acc)[C::FM][C::FN],
                                                   int m0, int n0, int grp, int xb0, int lane, int t, uint32_t lds0) {
@@ -348,8 +350,8 @@ __device__ __forceinline__ void pp_store_tile_lds(const GemmArgs& a, const typen
               w[4 + e] += beta * o1[e];
             }
           }
-          cp[0] = (f32x4){w[0], w[1], w[2], w[3]};
-          cp[1] = (f32x4){w[4], w[5], w[6], w[7]};
+          __builtin_nontemporal_store((f32x4){w[0], w[1], w[2], w[3]}, cp);
+          __builtin_nontemporal_store((f32x4){w[4], w[5], w[6], w[7]}, cp + 1);
         } else if (a.c_kind == C_E4M3) {
           uint32_t* cp = (uint32_t*)((uint8_t*)a.C + base);
           if (beta != 0.f) {
@@ -360,7 +362,8 @@ __device__ __forceinline__ void pp_store_tile_lds(const GemmArgs& a, const typen
               w[4 + e] += beta * __builtin_amdgcn_cvt_f32_fp8((int)o1, e);
             });
           }
-          *(u32x2*)cp = (u32x2){e4m3x4_from_f32(w[0], w[1], w[2], w[3]), e4m3x4_from_f32(w[4], w[5], w[6], w[7])};
+          __builtin_nontemporal_store(
+              (u32x2){e4m3x4_from_f32(w[0], w[1], w[2], w[3]), e4m3x4_from_f32(w[4], w[5], w[6], w[7])}, (u32x2*)cp);
         } else {
           uint16_t* cp = (uint16_t*)a.C + base;
           if (beta != 0.f) {
@@ -371,7 +374,7 @@ __device__ __forceinline__ void pp_store_tile_lds(const GemmArgs& a, const typen
           u16x8 v;
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = f32_to_bf16_bits(w[e]);
-          *(u16x8*)cp = v;
+          __builtin_nontemporal_store(v, (u16x8*)cp);
         }
       } else {  // the last columns of C
 #pragma unroll
