@@ -376,19 +376,41 @@ def test_trsm_exact_integer_out_of_place(gpu, side, uplo, transA):
     assert np.array_equal(to_host(Bd), Xt)
 
 
-@pytest.mark.parametrize("n,m", [(1500, 700), (2300, 456), (2048, 512)])
+def _padded_t(A, n):
+    """T on the device with its rows padded to a multiple of 8 elements (16-byte aligned rows,
+    which the doubled leaves need), NaN in the padding."""
+    ld = (n + 7) // 8 * 8 + 8
+    full = np.full((n, ld), gi.BF16_NAN, dtype=np.uint16)
+    full[:, :n] = A
+    return to_device(full, "bf16")[:, :n]
+
+
+@pytest.mark.parametrize("n,m", [(1500, 700), (2300, 456), (2047, 520), (2048, 512)])
 @pytest.mark.parametrize("side", [LEFT, RIGHT])
 @pytest.mark.parametrize("uplo", [LOWER, UPPER])
 @pytest.mark.parametrize("transA", [0, 1])
 def test_trsm_exact_integer_doubled_leaves(gpu, n, m, side, uplo, transA):
-    """From 2^20 elements of B the leaves are whole 512- or 1024-blocks of T whose inverses
-    are doubled up from the 256-block ones by batched products: n = 1500 (two 512-blocks and
-    a 476-row tail of 256-leaves), 2300 (two 1024-blocks and a 252 tail), 2048 (two
+    """From 2^20 elements of B, with T's rows 16-byte aligned, the leaves are whole 512- or
+    1024-blocks of T whose inverses are doubled up from the 128-block ones by batched
+    products: n = 1500 (two 512-blocks and a 476-row tail of 256-leaves), 2300 (two
+    1024-blocks and a 252 tail), 2047 (three 512-blocks and a 511 tail), 2048 (two
     1024-blocks), bit for bit on exact integer systems."""
     M, N = (n, m) if side == LEFT else (m, n)
     A, Xt, Bb = _int_system(n, M, N, side, uplo, transA, 1, 50)
     Bd = to_device(Bb, "bf16")
-    gpu.trsm(to_device(A, "bf16"), Bd, side=side, uplo=uplo, transA=transA, diag=1, alpha=1.0)
+    gpu.trsm(_padded_t(A, n), Bd, side=side, uplo=uplo, transA=transA, diag=1, alpha=1.0)
+    sync()
+    assert np.array_equal(to_host(Bd), Xt)
+
+
+@pytest.mark.parametrize("side", [LEFT, RIGHT])
+def test_trsm_exact_integer_unaligned_t(gpu, side):
+    """T with rows that are not 16-byte aligned (n = 1500, lda = n): 256-leaves only."""
+    n, m = 1500, 700
+    M, N = (n, m) if side == LEFT else (m, n)
+    A, Xt, Bb = _int_system(n, M, N, side, LOWER, 0, 1, 51)
+    Bd = to_device(Bb, "bf16")
+    gpu.trsm(to_device(A, "bf16"), Bd, side=side, uplo=LOWER, transA=0, diag=1, alpha=1.0)
     sync()
     assert np.array_equal(to_host(Bd), Xt)
 
@@ -403,7 +425,7 @@ def test_trsm_real_doubled_leaves(gpu, n, m, side, uplo):
     A = gi.bf16_triangular(n, uplo, 60)
     B = gi.bf16_uniform((M, N), 61)
     Bd = to_device(B, "bf16")
-    gpu.trsm(to_device(A, "bf16"), Bd, side=side, uplo=uplo, transA=0, diag=0, alpha=0.75)
+    gpu.trsm(_padded_t(A, n), Bd, side=side, uplo=uplo, transA=0, diag=0, alpha=0.75)
     sync()
     X = tolerance.bf16_bits_to_f64(to_host(Bd))
     X_ref = blas3.trsm(side, uplo, 0, 0, M, N, 0.75, A, B)
