@@ -313,6 +313,42 @@ __device__ __forceinline__ void pp_store_tile_lds(const GemmArgs& a, const typen
   const float alpha = a.alpha, beta = a.beta;
   // every wave's copies have landed (the last ones, past K, write zeros into LDS)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (a.c_kind == C_BF16 && beta == 0.f) {
+    // beta = 0 into bf16: both groups stage alpha*acc already rounded to bf16 (the rounding
+    // the store makes), 16-byte chunks XOR-swizzled by row as above, then one pass of row
+    // stores
+    constexpr int RB2 = C::BN * 2;
+    static_assert(C::BM * RB2 <= PingPong<C>::LDS_BYTES, "the tile's bf16 image fits the LDS");
+    __syncthreads();  // the LDS is free: the K loop's reads are done
+    static_for<C::FM * C::FN>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      constexpr int i = p / C::FN, j = p % C::FN;
+      const int r = grp * C::WTM + i * 16 + lane % 16;
+      const int c = xb0 + j * 16 + 4 * (lane / 16);  // a multiple of 4: half a chunk
+      const int chunk = (c >> 3) ^ (r & 15);
+      const u16x4 v = {f32_to_bf16_bits(alpha * acc[i][j][0]), f32_to_bf16_bits(alpha * acc[i][j][1]),
+                       f32_to_bf16_bits(alpha * acc[i][j][2]), f32_to_bf16_bits(alpha * acc[i][j][3])};
+      *(__attribute__((address_space(3))) u16x4*)(uintptr_t)(lds0 + (uint32_t)(r * RB2 + chunk * 16 + (c & 7) * 2)) = v;
+    });
+    __syncthreads();
+    constexpr int RPS = C::THREADS / 32;  // rows per step: 32 threads of 8 columns per row
+#pragma unroll 2
+    for (int s = 0; s < C::BM / RPS; ++s) {
+      const int r = s * RPS + t / 32, ch = t % 32;
+      const int m = m0 + r, n = n0 + ch * 8;
+      if (m >= a.M || n >= a.N) continue;
+      const u16x8 v = *(__attribute__((address_space(3))) u16x8*)(uintptr_t)(lds0 + (uint32_t)(r * RB2 + (ch ^ (r & 15)) * 16));
+      uint16_t* cp = (uint16_t*)a.C + (int64_t)m * a.ldc + n;
+      if (n + 8 <= a.N) {
+        __builtin_nontemporal_store(v, (u16x8*)cp);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n + e < a.N) cp[e] = v[e];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     __syncthreads();  // the LDS is free: the K loop's reads, or the previous pass's
