@@ -70,6 +70,7 @@ __global__ __launch_bounds__(256) void expand_tri_kernel(const uint16_t* __restr
 }
 
 constexpr int SB = 64;  // block edge of the kernels that go through an LDS block
+constexpr int kInvThreads = 512;  // threads of a 128-block inversion
 
 // dst[r][c] = T^T[r0 + r][c0 + c] = T[c0 + c][r0 + r] of the n x n triangular T (stored
 // triangle, zeros elsewhere, ones on a unit diagonal): the transposed operand written out, so
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(256) void expand_sym_blocks_kernel(const uint16_t* 
 // are stored instead rounded to bf16 on the diagonals of bdst, [n / lf][lf][lf], and the
 // lf-blocks' 128-blocks outside the triangle are zeroed: products double them up to lf x lf.
 template <bool UPPER>
-__global__ __launch_bounds__(256) void invert_diag_kernel(const uint16_t* __restrict__ src, int64_t lds, int n,
+__global__ __launch_bounds__(kInvThreads) void invert_diag_kernel(const uint16_t* __restrict__ src, int64_t lds, int n,
                                                           int unit, int vec, float* __restrict__ dst,
                                                           uint16_t* __restrict__ bdst, int lf, int whole) {
   constexpr int NB = kTrsmNB, LD = NB + 4, SB = 32;  // row stride: float4-aligned rows
@@ -277,16 +278,17 @@ __global__ __launch_bounds__(256) void invert_diag_kernel(const uint16_t* __rest
     else if (j <= i && i < nb && j < nb) v = bf16f(bits);
     Lt[j * LD + i] = v;
   };
+  constexpr int TH = kInvThreads, PARTS = TH / NB;  // threads per row of the block
   if (vec && nb == NB) {
-    // a whole block with 16-byte aligned rows: thread t reads half t % 2 of row t / 2 as 8
-    // independent 16-byte loads issued together (the other triangle is read and dropped)
-    const int p = t >> 1, q0 = (t & 1) * (NB / 2);
+    // a whole block with 16-byte aligned rows: thread t reads part t % PARTS of row t / PARTS
+    // as independent 16-byte loads issued together (the other triangle is read and dropped)
+    const int p = t / PARTS, q0 = (t % PARTS) * (NB / PARTS);
     const uint4* rp = (const uint4*)(src + (int64_t)(o + p) * lds + o + q0);
-    uint4 w[NB / 16];
+    uint4 w[NB / PARTS / 8];
 #pragma unroll
-    for (int qq = 0; qq < NB / 16; ++qq) w[qq] = rp[qq];
+    for (int qq = 0; qq < NB / PARTS / 8; ++qq) w[qq] = rp[qq];
 #pragma unroll
-    for (int qq = 0; qq < NB / 16; ++qq) {
+    for (int qq = 0; qq < NB / PARTS / 8; ++qq) {
       const uint32_t u[4] = {w[qq].x, w[qq].y, w[qq].z, w[qq].w};
 #pragma unroll
       for (int hh = 0; hh < 4; ++hh) {
@@ -297,13 +299,13 @@ __global__ __launch_bounds__(256) void invert_diag_kernel(const uint16_t* __rest
   } else {
     // element by element, the referenced ones only (consecutive threads, consecutive
     // elements of a row of T)
-    for (int e = t; e < NB * NB; e += 256) {
+    for (int e = t; e < NB * NB; e += TH) {
       const int p = e / NB, q = e % NB;
       const bool ref = (UPPER ? p <= q : q <= p) && p < nb && q < nb;
       put(p, q, ref ? src[(int64_t)(o + p) * lds + o + q] : (uint16_t)0);
     }
   }
-  for (int e = t; e < NB * NB; e += 256) X[(e / NB) * LD + e % NB] = 0.f;
+  for (int e = t; e < NB * NB; e += TH) X[(e / NB) * LD + e % NB] = 0.f;
   __syncthreads();
   if (t < NB) dinv[t] = 1.f / Lt[t * LD + t];
   __syncthreads();
@@ -333,9 +335,9 @@ __global__ __launch_bounds__(256) void invert_diag_kernel(const uint16_t* __rest
   __syncthreads();
   // ---- doubling: for each block [A 0; C D] of edge 2h at offset o2, W = C inv(A) into
   // X[o2 .. o2+h)[o2+h .. o2+2h), then the lower-left quadrant -inv(D) W, then W cleared.
-  // h = 32: two blocks, 128 threads each, 8 outputs per thread; h = 64: one block, 16.
+  // h = 32: two blocks, 256 threads each, 4 outputs per thread; h = 64: one block, 8.
   auto level = [&](auto hc) {
-    constexpr int h = decltype(hc)::value, TPB = 256 / (NB / (2 * h));  // threads per block
+    constexpr int h = decltype(hc)::value, TPB = TH / (NB / (2 * h));  // threads per block
     constexpr int PER = h * h / TPB;                                      // outputs per thread
     const int blk = t / TPB, lt = t % TPB, o2 = blk * 2 * h;
     const int i = lt / (h / PER), j0 = (lt % (h / PER)) * PER;           // row i, columns j0 ..
@@ -388,7 +390,7 @@ __global__ __launch_bounds__(256) void invert_diag_kernel(const uint16_t* __rest
   // ---- out: inv(T_bb) = X (lower) or X^T (upper), row-major, coalesced rows
   if (b >= whole) {  // for the combination into 256-blocks
     float* out = dst + (int64_t)b * NB * NB;
-    for (int e = t; e < NB * NB; e += 256) {
+    for (int e = t; e < NB * NB; e += TH) {
       const int r = e / NB, c = e % NB;
       out[e] = UPPER ? X[c * LD + r] : X[r * LD + c];
     }
@@ -396,7 +398,7 @@ __global__ __launch_bounds__(256) void invert_diag_kernel(const uint16_t* __rest
     const int per = lf / NB, p = b % per;  // 128-blocks per lf-block; this one's position
     uint16_t* base = bdst + (int64_t)(b / per) * lf * lf;
     uint16_t* bo = base + (int64_t)p * NB * (lf + 1);
-    for (int e = t; e < NB * NB / 2; e += 256) {  // two elements per 4-byte store
+    for (int e = t; e < NB * NB / 2; e += TH) {  // two elements per 4-byte store
       const int r = e / (NB / 2), c = 2 * (e % (NB / 2));
       const float v0 = UPPER ? X[c * LD + r] : X[r * LD + c];
       const float v1 = UPPER ? X[(c + 1) * LD + r] : X[r * LD + c + 1];
@@ -410,7 +412,7 @@ __global__ __launch_bounds__(256) void invert_diag_kernel(const uint16_t* __rest
       while ((j + 1) * j / 2 <= zb) ++j;
       const int i = zb - j * (j - 1) / 2;
       uint16_t* z = base + (int64_t)(UPPER ? j : i) * NB * lf + (UPPER ? i : j) * NB;
-      for (int e = t; e < NB * NB / 8; e += 256)
+      for (int e = t; e < NB * NB / 8; e += TH)
         *(uint4*)(z + (int64_t)(e / (NB / 8)) * lf + 8 * (e % (NB / 8))) = make_uint4(0, 0, 0, 0);
     }
   }
@@ -675,10 +677,10 @@ hipError_t launch_invert_diag(const void* src, int64_t lds, int n, int uplo, int
   // rows of T readable as 16-byte vectors
   const int vec = ((uintptr_t)src % 16 == 0) && lds % 8 == 0;
   if (uplo == 0)
-    hipLaunchKernelGGL(invert_diag_kernel<false>, dim3((unsigned)(2 * blocks)), dim3(256), 0, s,
+    hipLaunchKernelGGL(invert_diag_kernel<false>, dim3((unsigned)(2 * blocks)), dim3(kInvThreads), 0, s,
                        (const uint16_t*)src, lds, n, unit, vec, inv128, (uint16_t*)dst, lf, 2 * whole256);
   else
-    hipLaunchKernelGGL(invert_diag_kernel<true>, dim3((unsigned)(2 * blocks)), dim3(256), 0, s,
+    hipLaunchKernelGGL(invert_diag_kernel<true>, dim3((unsigned)(2 * blocks)), dim3(kInvThreads), 0, s,
                        (const uint16_t*)src, lds, n, unit, vec, inv128, (uint16_t*)dst, lf, 2 * whole256);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || whole256 == blocks) return e;
