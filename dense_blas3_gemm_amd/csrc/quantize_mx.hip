@@ -38,15 +38,14 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(int64_t rows, int64_t 
   const int64_t nb = (cols + 31) / 32;
   const int64_t per_row = 4 * nb;  // 8-element chunks per row, whole groups
   // x: chunks of a row (a multiple of 4 per block: a group's lanes enter and leave together);
-  // y: rows, grid-strided
+  // y: rows, grid-strided, two per iteration
   const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (k >= per_row) return;
   const int64_t b = k / 4;
   const int64_t c0 = b * 32 + (k % 4) * 8;
-  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
-    const int n = cols - c0 >= 8 ? 8 : (cols > c0 ? (int)(cols - c0) : 0);
+  const int n = cols - c0 >= 8 ? 8 : (cols > c0 ? (int)(cols - c0) : 0);
+  auto load = [&](int64_t r, float* v) {
     const uint16_t* s = src + r * ld_src + c0;
-    float v[8];
     if (n == 8 && ((uintptr_t)s & 15u) == 0) {
       const u32x4 w = *(const u32x4*)s;
 #pragma unroll
@@ -58,6 +57,8 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(int64_t rows, int64_t 
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = j < n ? bf16f(s[j]) : 0.0f;
     }
+  };
+  auto finish = [&](int64_t r, const float* v) {
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));  // NaN does not set it
@@ -77,6 +78,15 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(int64_t rows, int64_t 
       for (int j = 0; j < 8; ++j)
         if (j < n) d[j] = (uint8_t)e4m3_from_f32(v[j] * inv);
     }
+  };
+  // two rows per iteration, both loads issued before either is used
+  for (int64_t r = blockIdx.y; r < rows; r += 2 * (int64_t)gridDim.y) {
+    const int64_t r2 = r + gridDim.y;
+    float v[8], v2[8];
+    load(r, v);
+    if (r2 < rows) load(r2, v2);
+    finish(r, v);
+    if (r2 < rows) finish(r2, v2);
   }
 }
 
@@ -87,7 +97,8 @@ hipError_t launch_quantize_mx(int64_t rows, int64_t cols, const void* src, int64
   const int64_t per_row = 4 * ((cols + 31) / 32);
   const int64_t bx = (per_row + 255) / 256;
   if (bx > 65535) return hipErrorInvalidConfiguration;  // rows past kQuantizeMaxCols (the host checks)
-  const int64_t by = rows < 65535 ? rows : 65535;
+  const int64_t half = (rows + 1) / 2;  // two rows per workgroup and iteration
+  const int64_t by = half < 65535 ? half : 65535;
   hipLaunchKernelGGL(quantize_mx_kernel, dim3((unsigned)bx, (unsigned)(by > 0 ? by : 1)), dim3(256), 0, s, rows, cols,
                      (const uint16_t*)src, ld_src, (uint8_t*)dst, ld_dst, scales, ld_scales);
   return hipGetLastError();

@@ -43,8 +43,10 @@ def _quantize_gpu(gpu, bits):
 
 
 @pytest.mark.parametrize("rows,cols", [(1, 1), (3, 31), (7, 33), (64, 70), (129, 256), (40, 1000),
-                                       (3, 96), (17, 512), (5, 5120)])
+                                       (3, 96), (17, 512), (5, 5120), (1531, 3000), (2048, 5120)])
 def test_quantize_mx_bit_exact(gpu, rows, cols):
+    """Up to 2048 x 5120: more 8-element chunks than one pass of the grid (each thread takes
+    several, two at a time), with ragged rows and a ragged last pass."""
     bits = _bf16_input(rows, cols, rows * 1000 + cols)
     codes, scales = _quantize_gpu(gpu, bits)
     want_c, want_s = oracle.quantize_mx(oracle.decode(bits, "bf16"))
