@@ -147,11 +147,9 @@ int policy_select(const Problem& pr, int cu_count, int64_t ws_floats, int* split
       // workgroups sharing a CU at a time: the occupancy, or fewer on a small grid
       const double per_cu = (double)(int64_t)((wgs + cu_count - 1) / cu_count);
       const double conc = per_cu < occ ? per_cu : occ;
-      // a ping-pong ring of more than two slots takes longer to fill: measured at 4096^2,
-      // the four 32-deep slots lose to two 64-deep ones up to K = 512 (20.8 against 18.8 us
-      // at K = 256) and win from K = 1024 on
-      const double fill = p.pipe == 2 ? 16.0 * (p.stages - 2) : 0.0;
-      double t = rounds * conc * (double)p.BM * p.BN * (k_eff + K0 + fill) / p.efficiency;
+      // (the four-slot ping-pong ring, measured at 4096^2 against the two-slot 64-deep one,
+      // is as fast or faster from K = 256 up: 14.8-15.7 against 15.6-16.4 us at K = 256)
+      double t = rounds * conc * (double)p.BM * p.BN * (k_eff + K0) / p.efficiency;
       // a K band, tiles walked from the longest K to the shortest: round r of R holds
       // tiles of about K (1 - r/R), so the rounds add up to (R + 1) / 2 full-K rounds
       if (pr.kband) t *= (rounds + 1.0) / (2.0 * rounds);

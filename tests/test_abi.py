@@ -150,13 +150,12 @@ def test_large_workload_choices():
 
 
 def test_small_k_choices():
-    """At 4096^2 the two-slot 64-deep ping-pong tile up to K = 512 (its ring fills sooner),
-    the four-slot 32-deep one from K = 1024 (measured: 18.8 against 20.8 us at K = 256,
-    35.2 against 36.1 at K = 1024)."""
+    """At 4096^2 the four-slot 32-deep ping-pong tile at every K from 256 (measured against the
+    two-slot 64-deep one: 14.8-15.7 against 15.6-16.4 us at K = 256, 20.7-22.6 against
+    21.2-22.5 at K = 512, 31.9-33.6 against 32.2-34.5 at K = 1024)."""
     q = lambda *a, **k: d.query_policy(*a, A_ptr=A, B_ptr=B, C_ptr=C, **k)
-    for K, want in [(256, "bf16_pp_m256n256k64_w2x4_mt16_s2"), (512, "bf16_pp_m256n256k64_w2x4_mt16_s2"),
-                    (1024, "bf16_pp_m256n256k32_w2x4_mt16_s4"), (2048, "bf16_pp_m256n256k32_w2x4_mt16_s4")]:
-        assert q(4096, 4096, K, dtype=d.BF16_BF16) == want, K
+    for K in (256, 512, 1024, 2048):
+        assert q(4096, 4096, K, dtype=d.BF16_BF16) == "bf16_pp_m256n256k32_w2x4_mt16_s4", K
 
 
 def test_lds_probe_rejects_bad_arguments():
